@@ -1,0 +1,326 @@
+"""Float64 CPU oracle of decode attention over a paged KV cache.
+
+TEST INFRASTRUCTURE ONLY: imported by tests, the smoke check and the bench's
+CPU baseline, never by the product path.
+
+Pages cited (titles as the pages give them):
+  [FDE]  "Forward Deployed Engineering Interview", Ch.2 "Batching and the KV
+         Cache": section 6 (bytes per token), section 8 (paging, the
+         block_manager.py teaching model).
+  [API]  "Anthropic Interview: Design an LLM Inference API with GPU Batching":
+         Key concepts (Paged KV memory), 4. Data model (4.1, 4.2).
+  [QA]   "MLSys Engineer - Inference Systems Q&A": Q1 (PagedAttention, the
+         kernel rewrite), Q3 (pool size, layout for coalesced access), Q4
+         (online softmax, fp32 accumulation).
+  [WB]   "LLM inference and serving" workbook: The equations (KV-cache size,
+         roofline balance point, decode throughput ceiling), Code from memory
+         (naive incremental decoding, the step() function).
+  [SRV]  "Ch.29 Building a Production LLM Serving Stack": 29.1.2 (block
+         accounting worked example), 29.2.1 (attention intensity).
+
+What the oracle computes is the plain definition: decode attention over a
+paged cache equals ordinary softmax attention of one query over its
+sequence's de-paged, contiguous K/V ([WB] step(): append the new row, then
+softmax(K q / sqrt(d)) V over all rows; [QA] Q1: the paged kernel differs from
+the contiguous one only in addressing).  Nothing is blocked, fused or reordered.
+
+Readings taken where the pages are silent (each listed in the design notes):
+  * context_len counts the token written this step ([WB] step() appends before
+    attending; its printed check counts prompt + decoded rows).
+  * query head h reads KV head h // (H / H_kv) (contiguous groups).
+  * the in-block layout of the pool (the pages fix only the block-table
+    mapping; [QA] Q1's address formula omits the token and head strides) is
+    the one the C ABI documents, restated here independently:
+        K element (p, h, t, x) at (((p*H_kv + h)*(d/X) + x//X)*16 + t)*X + x%X
+        V element (p, h, t, x) at ((p*H_kv + h)*d + x)*16 + t
+    with X = 16 bytes / element size (8 for bf16, 4 for fp32).
+  * ctx <= 0 gives an all-zero output (no token to attend to).
+  * split-KV partitions are logical token ranges [k*P, (k+1)*P).
+
+Parity status: every function below is pinned by tests/test_oracle_pins.py
+against printed page values, closed forms, library routines or invariants.
+"""
+from __future__ import annotations
+
+import math
+from typing import Tuple
+
+import numpy as np
+
+__all__ = [
+    "BLOCK",
+    "bits_to_f64",
+    "chunk_elems",
+    "k_offset",
+    "v_offset",
+    "blocks_needed",
+    "slot_mapping",
+    "reshape_and_cache",
+    "gather_sequence",
+    "decode",
+    "decode_sequence",
+    "partials",
+    "reduce",
+    "kv_bytes",
+    "kv_bytes_per_token",
+    "kv_bytes_per_token_mla",
+    "ridge_intensity",
+    "decode_tokens_per_s_ceiling",
+    "decode_step_floor_s",
+]
+
+BLOCK = 16  # tokens per physical block ([QA] Q1: "typically 16 tokens")
+
+
+# --------------------------------------------------------------------------
+# element encodings
+# --------------------------------------------------------------------------
+def bits_to_f64(bits: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact widening of stored bit patterns to float64.
+
+    bf16 is the top half of a float32, so shifting its 16 bits up by 16 gives
+    that float32 exactly; float32 widens to float64 exactly.
+    """
+    bits = np.asarray(bits)
+    if dtype == "bf16":
+        return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    if dtype == "f32":
+        return bits.astype(np.uint32).view(np.float32).astype(np.float64)
+    raise ValueError(dtype)
+
+
+def chunk_elems(dtype: str) -> int:
+    """Elements per 16-byte chunk of the K layout."""
+    return {"bf16": 8, "f32": 4}[dtype]
+
+
+# --------------------------------------------------------------------------
+# the pool layout, restated from the documented formula
+# --------------------------------------------------------------------------
+def k_offset(p, h, t, x, H_kv: int, d: int, dtype: str):
+    """Element offset of K[block p, kv head h, in-block token t, dim x]."""
+    X = chunk_elems(dtype)
+    p = np.asarray(p, dtype=np.int64)
+    tile = (p * H_kv + h) * (d // X)
+    return ((tile + np.asarray(x) // X) * BLOCK + np.asarray(t)) * X + np.asarray(x) % X
+
+
+def v_offset(p, h, t, x, H_kv: int, d: int, dtype: str):
+    """Element offset of V[block p, kv head h, in-block token t, dim x]."""
+    p = np.asarray(p, dtype=np.int64)
+    return ((p * H_kv + h) * d + np.asarray(x)) * BLOCK + np.asarray(t)
+
+
+# --------------------------------------------------------------------------
+# block bookkeeping arithmetic
+# --------------------------------------------------------------------------
+def blocks_needed(tokens: int, block_size: int = BLOCK) -> int:
+    """Blocks a sequence of `tokens` tokens occupies: ceil(tokens / block).
+
+    [SRV] 29.1.2 worked example sizes requests this way (5,000 tokens -> 313
+    blocks); [QA] Q1 bounds the waste by one partial block.
+    """
+    return -(-int(tokens) // block_size)
+
+
+def slot_mapping(block_tables: np.ndarray, context_lens: np.ndarray) -> np.ndarray:
+    """Physical slot of each sequence's newest token (position ctx - 1).
+
+    [QA] Q1: logical position i lives in block block_table[i // block_size] at
+    offset i % block_size; the slot number is block * 16 + offset.  A sequence
+    with ctx <= 0 has no new token: slot -1 (skipped by the cache write).
+    """
+    tables = np.asarray(block_tables)
+    ctx = np.asarray(context_lens, dtype=np.int64)
+    out = np.full(ctx.shape[0], -1, dtype=np.int64)
+    for b in range(ctx.shape[0]):
+        n = int(ctx[b])
+        if n <= 0:
+            continue
+        pos = n - 1
+        out[b] = int(tables[b, pos // BLOCK]) * BLOCK + pos % BLOCK
+    return out
+
+
+# --------------------------------------------------------------------------
+# the cache write
+# --------------------------------------------------------------------------
+def reshape_and_cache(k_pool: np.ndarray, v_pool: np.ndarray, key: np.ndarray,
+                      value: np.ndarray, slots: np.ndarray, H_kv: int, d: int,
+                      dtype: str, num_blocks: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Write each token's K and V rows into its slot; return new pools.
+
+    [WB] step(): the cache append, K and V grow by one row per token and old
+    rows are never recomputed; [FDE] section 8 append(): the token goes into the
+    last block of the table.  A bit copy: -0.0 and NaN payloads survive.  A
+    negative slot is skipped.  Two tokens naming one slot in one call would race
+    on a GPU, so the oracle refuses them, as it refuses slots past the pool.
+    """
+    k_pool = np.array(k_pool, copy=True)
+    v_pool = np.array(v_pool, copy=True)
+    key = np.asarray(key).reshape(-1, H_kv, d)
+    value = np.asarray(value).reshape(-1, H_kv, d)
+    slots = np.asarray(slots, dtype=np.int64)
+    live = [int(s) for s in slots if s >= 0]
+    if len(set(live)) != len(live):
+        raise ValueError("duplicate slot in one cache write")
+    for i, s in enumerate(slots):
+        s = int(s)
+        if s < 0:
+            continue
+        if s >= num_blocks * BLOCK:
+            raise ValueError(f"slot {s} outside a pool of {num_blocks} blocks")
+        blk, off = divmod(s, BLOCK)
+        for h in range(H_kv):
+            xs = np.arange(d)
+            k_pool[k_offset(blk, h, off, xs, H_kv, d, dtype)] = key[i, h]
+            v_pool[v_offset(blk, h, off, xs, H_kv, d, dtype)] = value[i, h]
+    return k_pool, v_pool
+
+
+# --------------------------------------------------------------------------
+# de-paging and attention
+# --------------------------------------------------------------------------
+def gather_sequence(k_pool: np.ndarray, v_pool: np.ndarray, table_row: np.ndarray,
+                    ctx: int, kvh: int, H_kv: int, d: int, dtype: str
+                    ) -> Tuple[np.ndarray, np.ndarray]:
+    """Contiguous float64 K, V [ctx, d] of one sequence and KV head.
+
+    Token t is read from block table_row[t // 16], slot t % 16 ([QA] Q1).  Only
+    the first ceil(ctx / 16) table entries and the first ctx tokens are read.
+    """
+    t = np.arange(int(ctx), dtype=np.int64)
+    if t.size == 0:
+        return np.zeros((0, d)), np.zeros((0, d))
+    blocks = np.asarray(table_row, dtype=np.int64)[t // BLOCK]
+    xs = np.arange(d, dtype=np.int64)
+    ko = k_offset(blocks[:, None], kvh, (t % BLOCK)[:, None], xs[None, :], H_kv, d, dtype)
+    vo = v_offset(blocks[:, None], kvh, (t % BLOCK)[:, None], xs[None, :], H_kv, d, dtype)
+    return bits_to_f64(k_pool[ko], dtype), bits_to_f64(v_pool[vo], dtype)
+
+
+def decode_sequence(k_pool, v_pool, q_b: np.ndarray, table_row, ctx: int,
+                    H: int, H_kv: int, d: int, dtype: str, scale: float) -> np.ndarray:
+    """Output [H, d] of one sequence: softmax(scale * K q_h) V per query head.
+
+    [WB] step(): attn = softmax(K @ q / sqrt(d)); ctx = attn @ V, over every
+    cached row including the new one.  Max-subtracted softmax in float64.
+    """
+    g = H // H_kv
+    out = np.zeros((H, d))
+    if ctx <= 0:
+        return out
+    q = bits_to_f64(q_b, dtype).reshape(H, d)
+    for kvh in range(H_kv):
+        K, V = gather_sequence(k_pool, v_pool, table_row, ctx, kvh, H_kv, d, dtype)
+        for h in range(kvh * g, (kvh + 1) * g):
+            s = scale * (K @ q[h])
+            p = np.exp(s - s.max())
+            out[h] = (p @ V) / p.sum()
+    return out
+
+
+def decode(k_pool, v_pool, q: np.ndarray, block_tables: np.ndarray,
+           context_lens: np.ndarray, H: int, H_kv: int, d: int, dtype: str,
+           scale: float) -> np.ndarray:
+    """Float64 decode-attention output [B, H, d] for a whole batch."""
+    B = len(context_lens)
+    out = np.zeros((B, H, d))
+    for b in range(B):
+        out[b] = decode_sequence(k_pool, v_pool, q[b], block_tables[b],
+                                 int(context_lens[b]), H, H_kv, d, dtype, scale)
+    return out
+
+
+def partials(k_pool, v_pool, q, block_tables, context_lens, H: int, H_kv: int,
+             d: int, dtype: str, scale: float, partition_size: int):
+    """Per-partition (o, m, l) of split-KV decode.
+
+    Partition k of a sequence covers logical tokens [k*P, min((k+1)*P, ctx)).
+    For its scores s: m_k = max s, l_k = sum exp(s - m_k), and
+    o_k = sum exp(s - m_k) v / l_k.  These are the running max and denominator
+    of [QA] Q4's online softmax, taken over one partition.
+    Returns (o [B,H,Pmax,d], m [B,H,Pmax], l [B,H,Pmax], counts [B]).
+    """
+    P = int(partition_size)
+    if P <= 0 or P % BLOCK:
+        raise ValueError("partition size must be a positive multiple of 16")
+    B = len(context_lens)
+    g = H // H_kv
+    counts = np.array([-(-max(int(c), 0) // P) for c in context_lens], dtype=np.int64)
+    Pmax = max(int(counts.max()) if B else 0, 1)
+    o = np.zeros((B, H, Pmax, d))
+    m = np.full((B, H, Pmax), -np.inf)
+    l = np.zeros((B, H, Pmax))
+    for b in range(B):
+        n = int(context_lens[b])
+        if n <= 0:
+            continue
+        qb = bits_to_f64(q[b], dtype).reshape(H, d)
+        for kvh in range(H_kv):
+            K, V = gather_sequence(k_pool, v_pool, block_tables[b], n, kvh, H_kv, d, dtype)
+            for h in range(kvh * g, (kvh + 1) * g):
+                s = scale * (K @ qb[h])
+                for k in range(int(counts[b])):
+                    sk = s[k * P:(k + 1) * P]
+                    mk = sk.max()
+                    e = np.exp(sk - mk)
+                    m[b, h, k] = mk
+                    l[b, h, k] = e.sum()
+                    o[b, h, k] = (e @ V[k * P:(k + 1) * P]) / e.sum()
+    return o, m, l, counts
+
+
+def reduce(o: np.ndarray, m: np.ndarray, l: np.ndarray, counts: np.ndarray) -> np.ndarray:
+    """Merge split partials by log-sum-exp.
+
+    With M = max_k m_k and w_k = l_k exp(m_k - M): out = sum w_k o_k / sum w_k.
+    This is [QA] Q4's rescale rule (multiply by exp(m_old - m_new) when the
+    max rises) applied to whole partitions.  A sequence with no partition
+    gives zeros.
+    """
+    B, H, _, d = o.shape
+    out = np.zeros((B, H, d))
+    for b in range(B):
+        n = int(counts[b])
+        if n == 0:
+            continue
+        for h in range(H):
+            M = m[b, h, :n].max()
+            w = l[b, h, :n] * np.exp(m[b, h, :n] - M)
+            out[b, h] = (w @ o[b, h, :n]) / w.sum()
+    return out
+
+
+# --------------------------------------------------------------------------
+# byte and roofline arithmetic
+# --------------------------------------------------------------------------
+def kv_bytes(L: int, H_kv: int, d: int, b: int, S: int, B: int) -> int:
+    """KV-cache bytes = 2 * L * H_kv * d * b * S * B ([WB] KV-cache size)."""
+    return 2 * L * H_kv * d * b * S * B
+
+
+def kv_bytes_per_token(layers: int, kv_heads: int, head_dim: int, b: int = 2) -> int:
+    """Bytes per token = 2 * L * H_kv * d_head * b ([FDE] section 6)."""
+    return kv_bytes(layers, kv_heads, head_dim, b, 1, 1)
+
+
+def kv_bytes_per_token_mla(r_kv: int, d_rope: int, layers: int, b: int = 2) -> int:
+    """Latent-attention bytes per token = (r_kv + d_rope) * L * b ([FDE] section 6)."""
+    return (r_kv + d_rope) * layers * b
+
+
+def ridge_intensity(peak_flops: float, bandwidth: float) -> float:
+    """I* = peak FLOP/s / peak bandwidth ([WB] roofline balance point)."""
+    return peak_flops / bandwidth
+
+
+def decode_tokens_per_s_ceiling(bandwidth: float, n_params: float,
+                                bytes_per_weight: float) -> float:
+    """tokens/s <= bandwidth / (N * bytes per weight) ([WB] decode ceiling)."""
+    return bandwidth / (n_params * bytes_per_weight)
+
+
+def decode_step_floor_s(bytes_per_step: float, bandwidth: float) -> float:
+    """Bytes read per step divided by bandwidth ([FDE] section 1 decode floor)."""
+    return bytes_per_step / bandwidth

@@ -1,0 +1,265 @@
+"""The five seeded workloads and a generic recipe for smaller test shapes.
+
+Draw order inside one workload (one numpy PCG64 stream per seed):
+context lengths -> physical block permutation -> q -> pool K -> pool V ->
+new k, v.  Nothing here knows how a token is laid out inside a cache block:
+the pools are returned as flat arrays of independent N(0,1) values, one per
+element, so any layout reads the same distribution.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from typing import List, Optional, Sequence
+
+import numpy as np
+
+BLOCK_SIZE = 16
+# Block-table entries past a sequence's used blocks hold this value: an index no
+# pool ever has, so a kernel that read one would fault or fail a check.
+TABLE_SENTINEL = np.int32(0x7FFFFFFF)
+
+CONFIG_NAMES = {
+    1: "tiny-fp32-mha",
+    2: "7b-shape-b64-bf16",
+    3: "gqa-b256-bf16",
+    4: "long-context-split-bf16",
+    5: "shared-prefix-50-step-bf16",
+}
+
+
+def bits_dtype(dtype: str):
+    """numpy container type for one element's bit pattern."""
+    if dtype == "bf16":
+        return np.uint16
+    if dtype == "f32":
+        return np.uint32
+    raise ValueError(f"unsupported dtype {dtype!r}")
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bf16 (round to nearest, ties to even); return bits.
+
+    Inputs here are finite N(0,1) draws, so no NaN/Inf handling is needed.
+    """
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    lsb = (u >> np.uint32(16)) & np.uint32(1)
+    r = (u + np.uint32(0x7FFF) + lsb) >> np.uint32(16)
+    return r.astype(np.uint16)
+
+
+def _normal_bits(rng: np.random.Generator, n: int, dtype: str,
+                 chunk: int = 1 << 24) -> np.ndarray:
+    """n independent N(0,1) values as bit patterns, drawn in fixed-size chunks."""
+    out = np.empty(n, dtype=bits_dtype(dtype))
+    buf = np.empty(min(chunk, max(n, 1)), dtype=np.float32)
+    pos = 0
+    while pos < n:
+        m = min(chunk, n - pos)
+        rng.standard_normal(out=buf[:m], dtype=np.float32)
+        if dtype == "bf16":
+            out[pos:pos + m] = f32_to_bf16_bits(buf[:m])
+        else:
+            out[pos:pos + m] = buf[:m].view(np.uint32)
+        pos += m
+    return out
+
+
+@dataclass
+class DecodeStep:
+    """Inputs of one decode step: one new token per sequence.
+
+    context_lens[b] counts every cached token of sequence b *including* the one
+    this step writes, so the new token sits at position context_lens[b] - 1.
+    """
+    context_lens: np.ndarray      # int32 [B]
+    q: np.ndarray                 # bits [B, H, d]
+    new_k: np.ndarray             # bits [B, H_kv, d]
+    new_v: np.ndarray             # bits [B, H_kv, d]
+
+
+@dataclass
+class Workload:
+    name: str
+    dtype: str                    # "f32" | "bf16"
+    B: int
+    H: int
+    H_kv: int
+    d: int
+    num_blocks: int
+    max_nb: int                   # columns of the block table
+    scale: float
+    partition_size: int           # 0 = single pass, else tokens per split
+    block_tables: np.ndarray      # int32 [B, max_nb]; unused entries = TABLE_SENTINEL
+    k_pool: np.ndarray            # bits, flat, num_blocks*H_kv*16*d elements
+    v_pool: np.ndarray
+    steps: List[DecodeStep] = field(default_factory=list)
+    block_size: int = BLOCK_SIZE
+    seed: int = 0
+
+    @property
+    def elem_bytes(self) -> int:
+        return 2 if self.dtype == "bf16" else 4
+
+    @property
+    def group(self) -> int:
+        return self.H // self.H_kv
+
+    @property
+    def pool_elems(self) -> int:
+        return self.num_blocks * self.H_kv * self.block_size * self.d
+
+    @property
+    def max_context_len(self) -> int:
+        return int(max(int(s.context_lens.max()) for s in self.steps))
+
+
+def _blocks_for(n_tokens: int) -> int:
+    return -(-int(n_tokens) // BLOCK_SIZE)
+
+
+def scattered_workload(name: str, dtype: str, B: int, H: int, H_kv: int, d: int,
+                       context_lens: Sequence[int], seed: int, rng=None,
+                       pool_factor: float = 1.25, max_nb: Optional[int] = None,
+                       partition_size: int = 0, num_blocks: Optional[int] = None,
+                       ) -> Workload:
+    """One decode step over sequences whose blocks are scattered at random.
+
+    The pool holds ceil(pool_factor * total blocks) blocks (or num_blocks); the
+    physical blocks are the first sum(nb) entries of a seeded permutation of the
+    pool, dealt to the sequences in order.
+    """
+    rng = rng if rng is not None else np.random.Generator(np.random.PCG64(seed))
+    ctx = np.asarray(context_lens, dtype=np.int64)
+    if ctx.shape != (B,):
+        raise ValueError("need one context length per sequence")
+    nb = [_blocks_for(c) for c in ctx]
+    total = int(sum(nb))
+    if num_blocks is None:
+        num_blocks = max(int(math.ceil(pool_factor * total)), 1)
+    if num_blocks < total:
+        raise ValueError("pool smaller than the blocks the sequences need")
+    if max_nb is None:
+        max_nb = max(max(nb), 1)
+    perm = rng.permutation(num_blocks).astype(np.int32)
+    tables = np.full((B, max_nb), TABLE_SENTINEL, dtype=np.int32)
+    pos = 0
+    for b in range(B):
+        tables[b, :nb[b]] = perm[pos:pos + nb[b]]
+        pos += nb[b]
+    q = _normal_bits(rng, B * H * d, dtype).reshape(B, H, d)
+    n_pool = num_blocks * H_kv * BLOCK_SIZE * d
+    k_pool = _normal_bits(rng, n_pool, dtype)
+    v_pool = _normal_bits(rng, n_pool, dtype)
+    new_k = _normal_bits(rng, B * H_kv * d, dtype).reshape(B, H_kv, d)
+    new_v = _normal_bits(rng, B * H_kv * d, dtype).reshape(B, H_kv, d)
+    step = DecodeStep(context_lens=ctx.astype(np.int32), q=q, new_k=new_k, new_v=new_v)
+    return Workload(name=name, dtype=dtype, B=B, H=H, H_kv=H_kv, d=d,
+                    num_blocks=num_blocks, max_nb=max_nb, scale=1.0 / math.sqrt(d),
+                    partition_size=partition_size, block_tables=tables,
+                    k_pool=k_pool, v_pool=v_pool, steps=[step], seed=seed)
+
+
+def _config1(seed: int) -> Workload:
+    # Tiny fp32 MHA: 2 sequences of 17 and 33 tokens (the new token opens a
+    # fresh block in both), pool of 16 blocks, tables drawn from a permutation.
+    rng = np.random.Generator(np.random.PCG64(seed))
+    ctx = [17, 33]
+    return scattered_workload(CONFIG_NAMES[1], "f32", B=2, H=2, H_kv=2, d=64,
+                              context_lens=ctx, seed=seed, rng=rng, num_blocks=16)
+
+
+def _config2(seed: int) -> Workload:
+    rng = np.random.Generator(np.random.PCG64(seed))
+    ctx = rng.integers(512, 2048, size=64, endpoint=True)
+    return scattered_workload(CONFIG_NAMES[2], "bf16", B=64, H=32, H_kv=32, d=128,
+                              context_lens=ctx, seed=seed, rng=rng, max_nb=128)
+
+
+def _config3(seed: int) -> Workload:
+    rng = np.random.Generator(np.random.PCG64(seed))
+    draw = rng.lognormal(mean=math.log(1800.0), sigma=1.0, size=256)
+    ctx = np.clip(np.rint(draw), 64, 8192).astype(np.int64)
+    return scattered_workload(CONFIG_NAMES[3], "bf16", B=256, H=64, H_kv=8, d=128,
+                              context_lens=ctx, seed=seed, rng=rng, max_nb=512)
+
+
+def _config4(seed: int) -> Workload:
+    rng = np.random.Generator(np.random.PCG64(seed))
+    ctx = [100000, 65536, 32768, 4096, 2048, 1024, 300, 17]
+    return scattered_workload(CONFIG_NAMES[4], "bf16", B=8, H=32, H_kv=8, d=128,
+                              context_lens=ctx, seed=seed, rng=rng, max_nb=6250,
+                              partition_size=512)
+
+
+SHARED_PREFIX_BLOCKS = 64
+SHARED_PREFIX_STEPS = 50
+
+
+def shared_prefix_workload(seed: int, B: int = 128, H: int = 32, H_kv: int = 8,
+                           d: int = 128, steps: int = SHARED_PREFIX_STEPS,
+                           prefix_blocks: int = SHARED_PREFIX_BLOCKS,
+                           private_range=(16, 300), name: Optional[str] = None,
+                           ) -> Workload:
+    """Continuous decode over a shared prefix.
+
+    Every sequence's table starts with the same `prefix_blocks` physical blocks,
+    then private blocks for its own tokens. Each step appends one token per
+    sequence; a sequence takes the next block of a seeded free list whenever its
+    new token opens a block. The returned block table is the one after the last
+    step; entries a step does not reach are never read by that step.
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    private = rng.integers(private_range[0], private_range[1], size=B, endpoint=True)
+    prefix_tokens = prefix_blocks * BLOCK_SIZE
+    final_private_blocks = [_blocks_for(int(p) + steps) for p in private]
+    num_blocks = prefix_blocks + int(math.ceil(1.25 * sum(final_private_blocks)))
+    perm = rng.permutation(num_blocks).astype(np.int32)
+    prefix = perm[:prefix_blocks]
+    free = list(perm[prefix_blocks:])
+    max_nb = _blocks_for(prefix_tokens + int(private.max()) + steps)
+    tables = np.full((B, max_nb), TABLE_SENTINEL, dtype=np.int32)
+    tables[:, :prefix_blocks] = prefix[None, :]
+    for b in range(B):
+        n = _blocks_for(int(private[b]))
+        for j in range(n):
+            tables[b, prefix_blocks + j] = free.pop(0)
+    ctx_per_step = []
+    for s in range(steps):
+        ctx_s = np.empty(B, dtype=np.int32)
+        for b in range(B):
+            pos = prefix_tokens + int(private[b]) + s       # the new token's position
+            if pos % BLOCK_SIZE == 0:                        # it opens a fresh block
+                tables[b, pos // BLOCK_SIZE] = free.pop(0)
+            ctx_s[b] = pos + 1
+        ctx_per_step.append(ctx_s)
+    dtype = "bf16"
+    n_pool = num_blocks * H_kv * BLOCK_SIZE * d
+    qs = [_normal_bits(rng, B * H * d, dtype).reshape(B, H, d) for _ in range(steps)]
+    k_pool = _normal_bits(rng, n_pool, dtype)
+    v_pool = _normal_bits(rng, n_pool, dtype)
+    step_list = []
+    for s in range(steps):
+        nk = _normal_bits(rng, B * H_kv * d, dtype).reshape(B, H_kv, d)
+        nv = _normal_bits(rng, B * H_kv * d, dtype).reshape(B, H_kv, d)
+        step_list.append(DecodeStep(context_lens=ctx_per_step[s], q=qs[s], new_k=nk, new_v=nv))
+    return Workload(name=name or CONFIG_NAMES[5], dtype=dtype, B=B, H=H, H_kv=H_kv, d=d,
+                    num_blocks=num_blocks, max_nb=max_nb, scale=1.0 / math.sqrt(d),
+                    partition_size=0, block_tables=tables, k_pool=k_pool, v_pool=v_pool,
+                    steps=step_list, seed=seed)
+
+
+def make_workload(config: int, seed: Optional[int] = None) -> Workload:
+    """Build workload `config` (1..5) with its default seed (= config number)."""
+    seed = config if seed is None else seed
+    if config == 1:
+        return _config1(seed)
+    if config == 2:
+        return _config2(seed)
+    if config == 3:
+        return _config3(seed)
+    if config == 4:
+        return _config4(seed)
+    if config == 5:
+        return shared_prefix_workload(seed)
+    raise ValueError(f"no workload {config}")
