@@ -1,0 +1,178 @@
+/*
+ * pagedkv.h - C ABI of libpagedkv: decode attention over a paged KV cache on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation (pages cited by title and section):
+ *   - "MLSys Engineer - Inference Systems Q&A", Q1 (How does PagedAttention
+ *     work?): the cache is split into fixed blocks of 16 tokens; each sequence
+ *     has a block table mapping logical token position i to physical block
+ *     block_table[i / 16], slot i % 16; the attention kernel reads K and V
+ *     through that table instead of a contiguous buffer.
+ *   - "LLM inference and serving" workbook, Code from memory (naive
+ *     incremental decoding): each decode step appends the new token's K and V
+ *     rows, then attends with softmax(K q / sqrt(d)) V over every cached row,
+ *     the new one included.
+ *   - same Q&A page, Q4 (fused attention kernel): scores never leave the chip;
+ *     a running max m and denominator l are rescaled by exp(m_old - m_new)
+ *     whenever the max rises (online softmax); accumulation is in fp32.
+ *   - "Anthropic Interview: Design an LLM Inference API with GPU Batching",
+ *     4.1/4.2 Data model: a sequence owns a block_table of block ids; blocks
+ *     come from a free stack kept by the host.
+ *
+ * Conventions shared by every call:
+ *   - Ownership: the caller allocates and owns every buffer (pool, query,
+ *     output, tables, lengths, slots, workspace).  The library never allocates
+ *     or frees device memory and never synchronises a stream.
+ *   - Streams: `stream` is a hipStream_t (NULL = the default stream).  Every
+ *     call enqueues its kernels there and returns at once; ordering between
+ *     calls is stream order.
+ *   - Errors: every argument the host can check (null pointers, sizes,
+ *     dtypes, head counts, workspace size) is checked before anything is
+ *     enqueued; a failed check returns a negative kv_status and leaves a
+ *     message for kv_last_error().  Device-resident values (table entries,
+ *     lengths, slots) are checked by the kernels themselves: a bad value never
+ *     makes a kernel read or write outside the buffers; it is reported as NaN
+ *     in the affected output rows (decode) or as a skipped write (cache write).
+ *   - Threading: all calls are re-entrant; a kv_pool is immutable after
+ *     creation and may be shared by threads.
+ *
+ * Pool layout in HBM (one K cache and one V cache, each num_blocks *
+ * num_kv_heads * 16 * head_dim elements).  Every (block p, kv head h) tile is
+ * 16 * head_dim contiguous elements starting at element (p*H_kv + h)*16*d.
+ * Inside a tile, with X = 16 / sizeof(element) (8 for bf16, 4 for fp32):
+ *   K[p][h][t][x] at (((p*H_kv + h)*(d/X) + x/X)*16 + t)*X + x%X
+ *       i.e. the tile is [d/X][16 tokens][X]: the 16 bytes holding dims
+ *       x..x+X-1 of one token are contiguous, and the 16 tokens' copies of one
+ *       such chunk follow one another;
+ *   V[p][h][t][x] at ((p*H_kv + h)*d + x)*16 + t
+ *       i.e. the tile is [d][16 tokens]: one dim's 16 tokens are contiguous.
+ * These are the operand layouts of the gfx950 matrix-core instructions the
+ * grouped-query kernel feeds straight from memory (K as the row operand of
+ * S = K Q^T, V^T as the row operand of O^T = V^T P^T); the same layout keeps
+ * every load of the VALU kernel a coalesced 16-byte access.
+ *
+ * Query and output: [B][H][d], contiguous, same dtype as the pool.  Query head
+ * h reads KV head h / (H / H_kv) (contiguous groups).
+ */
+#ifndef PAGEDKV_H_
+#define PAGEDKV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KV_OK = 0,
+  KV_ERR_INVALID_ARG = -1,  /* null pointer, negative or inconsistent size   */
+  KV_ERR_UNSUPPORTED = -2,  /* a dtype / head_dim / block size not built      */
+  KV_ERR_WORKSPACE = -3,    /* workspace missing or smaller than required     */
+  KV_ERR_HIP = -4           /* a HIP runtime call failed (message has detail) */
+} kv_status;
+
+typedef enum { KV_F32 = 0, KV_BF16 = 1 } kv_dtype;
+
+typedef struct {
+  int32_t num_blocks;    /* physical blocks in the pool, >= 1              */
+  int32_t block_size;    /* tokens per block; only 16 is supported          */
+  int32_t num_kv_heads;  /* H_kv, >= 1                                      */
+  int32_t head_dim;      /* d: 64 or 128                                    */
+  kv_dtype dtype;        /* element type of K, V, query and output          */
+} kv_pool_desc;
+
+typedef struct kv_pool kv_pool; /* opaque host object; borrows the two caches */
+
+/* Bytes of ONE cache (K or V) for this geometry; 0 if the descriptor is
+ * invalid.  The pool is num_blocks*H_kv*16*d elements (the KV-cache size
+ * formula of the workbook's "The equations" with L = 1, per cache). */
+size_t kv_pool_bytes(const kv_pool_desc* desc);
+
+/* Wrap two caller-owned device buffers (each kv_pool_bytes(desc) bytes, 16-byte
+ * aligned) as a pool.  Host metadata only; nothing is copied or cleared.
+ * Returns KV_OK and *out on success. */
+kv_status kv_pool_create(const kv_pool_desc* desc, void* k_cache, void* v_cache,
+                         kv_pool** out);
+
+/* Free the host object (never the caller's buffers).  NULL is ignored. */
+void kv_pool_destroy(kv_pool* pool);
+
+/* Slot of each sequence's newest token: for b < B with n = context_lens[b],
+ *   slot_mapping[b] = block_tables[b*max_nb + (n-1)/16] * 16 + (n-1) % 16,
+ * the block-table mapping of the Q&A page's Q1 applied to position n - 1
+ * (context_lens count the token being written).  n <= 0, n > max_nb*16 or a
+ * negative table entry give -1 (the cache write skips it).
+ * block_tables: device int32 [B][max_nb]; context_lens: device int32 [B];
+ * slot_mapping: device int64 [B] (written). */
+kv_status kv_slot_mapping(const int32_t* block_tables, int32_t max_nb,
+                          const int32_t* context_lens, int32_t B,
+                          int64_t* slot_mapping, void* stream);
+
+/* Cache write: copy token i's K and V rows (key/value: device [N][H_kv][d],
+ * pool dtype) into slot s = slot_mapping[i] (device int64 [N]): block s / 16,
+ * in-block token s % 16, using the pool layout above.  The workbook's decode
+ * step appends the new row before attending; the Q&A page's Q7 stores all K/V
+ * of a batch in one pass.  A bit copy: every bit pattern, NaN payloads and
+ * -0.0 included, lands unchanged.  s < 0 and s >= num_blocks*16 are skipped.
+ * Two tokens naming one slot in one call race (undefined result). */
+kv_status reshape_and_cache(const kv_pool* pool, const void* key, const void* value,
+                            const int64_t* slot_mapping, int32_t N, void* stream);
+
+/* Workspace bytes paged_attention_decode needs in split mode: with
+ * P = ceil(max_context_len / partition_size) partitions per sequence,
+ *   o: float [B][H][P][d], then m: float [B][H][P], then l: float [B][H][P]
+ * (each region 256-byte aligned).  0 when partition_size == 0. */
+size_t paged_attention_workspace_bytes(int32_t B, int32_t H, int32_t head_dim,
+                                       int32_t max_context_len, int32_t partition_size);
+
+/* Decode attention for one new query token per sequence.
+ *   out[b][h][:] = softmax_t(scale * q[b][h] . K_b[t]) V_b[t], t < ctx_b,
+ * where K_b[t], V_b[t] are read from block block_tables[b*max_nb + t/16],
+ * slot t % 16 (ctx_b = context_lens[b], which includes the token written this
+ * step).  fp32 accumulation; bf16 outputs are rounded to nearest-even.
+ * query: device [B][H][d]; out: device [B][H][d]; block_tables: device int32
+ * [B][max_nb] (entries past ceil(ctx_b/16) are never read); context_lens:
+ * device int32 [B]; max_context_len: a host upper bound on every ctx_b.
+ * ctx_b <= 0 gives zeros.  ctx_b > max_nb*16, ctx_b > max_context_len (split
+ * mode) or a table entry outside the pool gives NaN for that sequence.
+ * partition_size == 0: single pass, writes out.  partition_size = 16*k > 0:
+ * split-KV; each partition of partition_size tokens writes (o, m, l) into the
+ * workspace (m, l in base-2 units: m = max of scale*log2(e)*q.k, l = sum of
+ * 2^(that - m), o = normalised partial output); sequences with a single
+ * partition write out directly.  Follow with paged_attention_reduce.
+ * H must be a multiple of H_kv.  Kernel choice: H_kv < H with bf16 uses the
+ * matrix-core kernel; otherwise the vector-ALU kernel. */
+kv_status paged_attention_decode(const kv_pool* pool, void* out, const void* query,
+                                 const int32_t* block_tables, int32_t max_nb,
+                                 const int32_t* context_lens, int32_t B, int32_t H,
+                                 int32_t max_context_len, float scale,
+                                 int32_t partition_size, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
+/* Merge split partials (the workspace paged_attention_decode wrote with the
+ * same B, H, head_dim, max_context_len and partition_size) by log-sum-exp:
+ * with M = max_k m_k and w_k = l_k * 2^(m_k - M),
+ *   out[b][h] = sum_k w_k o_k / sum_k w_k   over the ceil(ctx_b/partition_size)
+ * partitions of sequence b; this is Q4's rescale rule applied to whole
+ * partitions.  Sequences with one partition are left as the decode wrote
+ * them; ctx_b <= 0 gives zeros; ctx_b > max_context_len gives NaN.
+ * out: device [B][H][head_dim] of out_dtype. */
+kv_status paged_attention_reduce(void* out, const void* workspace,
+                                 const int32_t* context_lens, int32_t B, int32_t H,
+                                 int32_t head_dim, int32_t max_context_len,
+                                 int32_t partition_size, kv_dtype out_dtype,
+                                 void* stream);
+
+/* Which decode kernel paged_attention_decode launches for this pool and H:
+ * 0 = vector-ALU kernel, 1 = matrix-core (MFMA) kernel, < 0 = unsupported. */
+int32_t kv_decode_kernel_kind(const kv_pool* pool, int32_t H);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* kv_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H_ */

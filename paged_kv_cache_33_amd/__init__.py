@@ -1,0 +1,225 @@
+"""Paged KV-cache decode attention for AMD MI355X (gfx950).
+
+A thin Python binding over libpagedkv's C ABI (include/pagedkv.h), with the
+same names.  It only marshals arguments: it checks that each torch tensor is a
+contiguous device buffer of the size the C call documents, then passes raw
+pointers and the stream.  Every step of the computation runs in the HIP
+kernels; if the library is missing, every call raises.
+
+PyTorch is used for device memory and streams only.
+"""
+from __future__ import annotations
+
+import ctypes as C
+from typing import Optional, Union
+
+import torch
+
+from . import _lib
+from ._lib import KVPoolDesc, PagedKVError  # noqa: F401
+
+__all__ = [
+    "KVPool",
+    "PagedKVError",
+    "kv_pool_bytes",
+    "kv_pool_create",
+    "kv_slot_mapping",
+    "reshape_and_cache",
+    "paged_attention_workspace_bytes",
+    "paged_attention_decode",
+    "paged_attention_reduce",
+    "kv_decode_kernel_kind",
+    "library_path",
+]
+
+BLOCK_SIZE = 16
+
+
+def library_path() -> str:
+    return _lib.LIB_PATH
+
+
+def _dtype_code(dtype) -> int:
+    if dtype in ("bf16", torch.bfloat16, _lib.KV_BF16):
+        return _lib.KV_BF16
+    if dtype in ("f32", torch.float32, _lib.KV_F32):
+        return _lib.KV_F32
+    raise ValueError(f"unsupported dtype {dtype!r}")
+
+
+def _elem_size(code: int) -> int:
+    return 2 if code == _lib.KV_BF16 else 4
+
+
+def _stream_handle(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _buf(t: torch.Tensor, name: str, nbytes: Optional[int] = None,
+         elem_size: Optional[int] = None, dtype: Optional[torch.dtype] = None) -> int:
+    """Pointer of a contiguous device tensor, after checking what the C call reads."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must live on the GPU (got {t.device})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} (got {t.dtype})")
+    if elem_size is not None and t.element_size() != elem_size:
+        raise ValueError(f"{name} must have {elem_size}-byte elements (got {t.element_size()})")
+    have = t.numel() * t.element_size()
+    if nbytes is not None and have != nbytes:
+        raise ValueError(f"{name} holds {have} bytes, the call reads/writes {nbytes}")
+    return t.data_ptr()
+
+
+def kv_pool_bytes(num_blocks: int, num_kv_heads: int, head_dim: int, dtype) -> int:
+    """Bytes of ONE cache (K or V) of this geometry (0 if unsupported)."""
+    desc = KVPoolDesc(num_blocks, BLOCK_SIZE, num_kv_heads, head_dim, _dtype_code(dtype))
+    return int(_lib.load().kv_pool_bytes(C.byref(desc)))
+
+
+class KVPool:
+    """A K cache and a V cache in the documented block layout, owned by torch."""
+
+    def __init__(self, k_cache: torch.Tensor, v_cache: torch.Tensor, num_blocks: int,
+                 num_kv_heads: int, head_dim: int, dtype):
+        lib = _lib.load()
+        self.dtype_code = _dtype_code(dtype)
+        self.num_blocks = int(num_blocks)
+        self.num_kv_heads = int(num_kv_heads)
+        self.head_dim = int(head_dim)
+        self.desc = KVPoolDesc(self.num_blocks, BLOCK_SIZE, self.num_kv_heads, self.head_dim,
+                               self.dtype_code)
+        need = int(lib.kv_pool_bytes(C.byref(self.desc)))
+        if need == 0:
+            _lib.check(lib.kv_pool_create(C.byref(self.desc), None, None, C.byref(C.c_void_p())))
+        kp = _buf(k_cache, "k_cache", need)
+        vp = _buf(v_cache, "v_cache", need)
+        handle = C.c_void_p()
+        _lib.check(lib.kv_pool_create(C.byref(self.desc), kp, vp, C.byref(handle)))
+        self.k_cache = k_cache
+        self.v_cache = v_cache
+        self._handle = handle
+
+    @classmethod
+    def allocate(cls, num_blocks: int, num_kv_heads: int, head_dim: int, dtype,
+                 device="cuda") -> "KVPool":
+        code = _dtype_code(dtype)
+        tdt = torch.bfloat16 if code == _lib.KV_BF16 else torch.float32
+        n = num_blocks * num_kv_heads * BLOCK_SIZE * head_dim
+        k = torch.empty(n, dtype=tdt, device=device)
+        v = torch.empty(n, dtype=tdt, device=device)
+        return cls(k, v, num_blocks, num_kv_heads, head_dim, dtype)
+
+    @property
+    def handle(self) -> C.c_void_p:
+        if self._handle is None:
+            raise RuntimeError("pool is closed")
+        return self._handle
+
+    @property
+    def elem_size(self) -> int:
+        return _elem_size(self.dtype_code)
+
+    def close(self) -> None:
+        if getattr(self, "_handle", None) is not None:
+            _lib.load().kv_pool_destroy(self._handle)
+            self._handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def kv_pool_create(k_cache, v_cache, num_blocks, num_kv_heads, head_dim, dtype) -> KVPool:
+    return KVPool(k_cache, v_cache, num_blocks, num_kv_heads, head_dim, dtype)
+
+
+def kv_slot_mapping(block_tables: torch.Tensor, context_lens: torch.Tensor,
+                    slot_mapping: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Slot of each sequence's newest token, computed on the GPU (int64 [B])."""
+    if block_tables.dim() != 2:
+        raise ValueError("block_tables must be [B, max_nb]")
+    B, max_nb = block_tables.shape
+    tp = _buf(block_tables, "block_tables", dtype=torch.int32)
+    cp = _buf(context_lens, "context_lens", 4 * B, dtype=torch.int32)
+    if slot_mapping is None:
+        slot_mapping = torch.empty(B, dtype=torch.int64, device=block_tables.device)
+    sp = _buf(slot_mapping, "slot_mapping", 8 * B, dtype=torch.int64)
+    _lib.check(_lib.load().kv_slot_mapping(tp, max_nb, cp, B, sp, _stream_handle(stream)))
+    return slot_mapping
+
+
+def reshape_and_cache(pool: KVPool, key: torch.Tensor, value: torch.Tensor,
+                      slot_mapping: torch.Tensor, stream=None) -> None:
+    """Write token i's K/V rows ([N, H_kv, d]) into slot slot_mapping[i]."""
+    N = int(slot_mapping.numel())
+    row = pool.num_kv_heads * pool.head_dim * pool.elem_size
+    kp = _buf(key, "key", N * row, elem_size=pool.elem_size)
+    vp = _buf(value, "value", N * row, elem_size=pool.elem_size)
+    sp = _buf(slot_mapping, "slot_mapping", 8 * N, dtype=torch.int64)
+    _lib.check(_lib.load().reshape_and_cache(pool.handle, kp, vp, sp, N, _stream_handle(stream)))
+
+
+def paged_attention_workspace_bytes(B: int, H: int, head_dim: int, max_context_len: int,
+                                    partition_size: int) -> int:
+    return int(_lib.load().paged_attention_workspace_bytes(B, H, head_dim, max_context_len,
+                                                           partition_size))
+
+
+def paged_attention_decode(pool: KVPool, out: torch.Tensor, query: torch.Tensor,
+                           block_tables: torch.Tensor, context_lens: torch.Tensor,
+                           max_context_len: int, scale: float, partition_size: int = 0,
+                           workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Decode attention for one new query per sequence; see pagedkv.h."""
+    if query.dim() != 3 or query.shape[2] != pool.head_dim:
+        raise ValueError("query must be [B, H, head_dim]")
+    B, H, d = query.shape
+    if block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be [B, max_nb]")
+    max_nb = int(block_tables.shape[1])
+    es = pool.elem_size
+    qp = _buf(query, "query", B * H * d * es, elem_size=es)
+    op = _buf(out, "out", B * H * d * es, elem_size=es)
+    tp = _buf(block_tables, "block_tables", dtype=torch.int32)
+    cp = _buf(context_lens, "context_lens", 4 * B, dtype=torch.int32)
+    wp, wbytes = None, 0
+    if partition_size:
+        if workspace is None:
+            raise ValueError("split mode (partition_size > 0) needs a workspace")
+        wp = _buf(workspace, "workspace")
+        wbytes = workspace.numel() * workspace.element_size()
+    _lib.check(_lib.load().paged_attention_decode(
+        pool.handle, op, qp, tp, max_nb, cp, B, H, int(max_context_len), float(scale),
+        int(partition_size), wp, wbytes, _stream_handle(stream)))
+
+
+def paged_attention_reduce(out: torch.Tensor, workspace: torch.Tensor, context_lens: torch.Tensor,
+                           max_context_len: int, partition_size: int, dtype, stream=None) -> None:
+    """Merge the split partials of paged_attention_decode into out [B, H, d]."""
+    if out.dim() != 3:
+        raise ValueError("out must be [B, H, head_dim]")
+    B, H, d = out.shape
+    code = _dtype_code(dtype)
+    op = _buf(out, "out", B * H * d * _elem_size(code), elem_size=_elem_size(code))
+    need = paged_attention_workspace_bytes(B, H, d, max_context_len, partition_size)
+    wp = _buf(workspace, "workspace")
+    if workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace must hold at least {need} bytes")
+    cp = _buf(context_lens, "context_lens", 4 * B, dtype=torch.int32)
+    _lib.check(_lib.load().paged_attention_reduce(
+        op, wp, cp, B, H, d, int(max_context_len), int(partition_size), code,
+        _stream_handle(stream)))
+
+
+def kv_decode_kernel_kind(pool: KVPool, H: int) -> int:
+    """0 = vector-ALU decode kernel, 1 = matrix-core kernel, < 0 unsupported."""
+    return int(_lib.load().kv_decode_kernel_kind(pool.handle, H))

@@ -1,0 +1,254 @@
+// C ABI of libpagedkv: argument checks, kernel choice and launches.
+// The operation and every convention are documented in include/pagedkv.h.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <new>
+#include <string>
+
+#include "../../include/pagedkv.h"
+#include "launch.h"
+
+struct kv_pool {
+  kv_pool_desc desc;
+  void* k_cache;
+  void* v_cache;
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+kv_status fail(kv_status code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+kv_status ok() {
+  g_last_error.clear();
+  return KV_OK;
+}
+
+kv_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(KV_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+size_t elem_bytes(kv_dtype t) { return t == KV_BF16 ? 2 : 4; }
+
+// Longest split supported: the reduce keeps one weight per partition in LDS.
+constexpr int64_t kMaxPartitions = 8192;
+
+kv_status check_desc(const kv_pool_desc* d) {
+  if (!d) return fail(KV_ERR_INVALID_ARG, "pool descriptor is NULL");
+  if (d->dtype != KV_F32 && d->dtype != KV_BF16)
+    return fail(KV_ERR_UNSUPPORTED, "dtype %d is not supported (f32=0, bf16=1)", int(d->dtype));
+  if (d->block_size != 16)
+    return fail(KV_ERR_UNSUPPORTED, "block_size %d is not supported (16 only)", d->block_size);
+  if (d->head_dim != 64 && d->head_dim != 128)
+    return fail(KV_ERR_UNSUPPORTED, "head_dim %d is not supported (64 or 128)", d->head_dim);
+  if (d->num_blocks < 1) return fail(KV_ERR_INVALID_ARG, "num_blocks must be >= 1");
+  if (d->num_kv_heads < 1) return fail(KV_ERR_INVALID_ARG, "num_kv_heads must be >= 1");
+  return KV_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int64_t num_partitions(int32_t max_context_len, int32_t partition_size) {
+  if (partition_size <= 0) return 1;
+  const int64_t n = (int64_t(max_context_len) + partition_size - 1) / partition_size;
+  return n < 1 ? 1 : n;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+struct WorkspaceView {
+  float* o;
+  float* m;
+  float* l;
+  size_t bytes;
+};
+
+WorkspaceView workspace_view(void* ws, int32_t B, int32_t H, int32_t d, int64_t P) {
+  const size_t n = size_t(B) * size_t(H) * size_t(P);
+  const size_t o_bytes = align256(n * size_t(d) * sizeof(float));
+  const size_t ml_bytes = align256(n * sizeof(float));
+  char* base = static_cast<char*>(ws);
+  WorkspaceView v;
+  v.o = reinterpret_cast<float*>(base);
+  v.m = reinterpret_cast<float*>(base + o_bytes);
+  v.l = reinterpret_cast<float*>(base + o_bytes + ml_bytes);
+  v.bytes = o_bytes + 2 * ml_bytes;
+  return v;
+}
+
+kv_status check_partition(int32_t max_context_len, int32_t partition_size) {
+  if (max_context_len < 0) return fail(KV_ERR_INVALID_ARG, "max_context_len must be >= 0");
+  if (partition_size < 0 || partition_size % 16 != 0)
+    return fail(KV_ERR_INVALID_ARG,
+                "partition_size %d must be 0 (single pass) or a positive multiple of 16",
+                partition_size);
+  if (num_partitions(max_context_len, partition_size) > kMaxPartitions)
+    return fail(KV_ERR_INVALID_ARG, "more than %lld partitions per sequence",
+                static_cast<long long>(kMaxPartitions));
+  return KV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t kv_pool_bytes(const kv_pool_desc* desc) {
+  if (check_desc(desc) != KV_OK) return 0;
+  return size_t(desc->num_blocks) * size_t(desc->num_kv_heads) * 16u * size_t(desc->head_dim) *
+         elem_bytes(desc->dtype);
+}
+
+kv_status kv_pool_create(const kv_pool_desc* desc, void* k_cache, void* v_cache, kv_pool** out) {
+  if (!out) return fail(KV_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  if (kv_status s = check_desc(desc); s != KV_OK) return s;
+  if (!k_cache || !v_cache) return fail(KV_ERR_INVALID_ARG, "k_cache and v_cache must be non-NULL");
+  if (!aligned16(k_cache) || !aligned16(v_cache))
+    return fail(KV_ERR_INVALID_ARG, "k_cache and v_cache must be 16-byte aligned");
+  kv_pool* p = new (std::nothrow) kv_pool;
+  if (!p) return fail(KV_ERR_INVALID_ARG, "out of host memory");
+  p->desc = *desc;
+  p->k_cache = k_cache;
+  p->v_cache = v_cache;
+  *out = p;
+  return ok();
+}
+
+void kv_pool_destroy(kv_pool* pool) { delete pool; }
+
+kv_status kv_slot_mapping(const int32_t* block_tables, int32_t max_nb, const int32_t* context_lens,
+                          int32_t B, int64_t* slot_mapping, void* stream) {
+  if (B < 0) return fail(KV_ERR_INVALID_ARG, "B must be >= 0");
+  if (max_nb < 1) return fail(KV_ERR_INVALID_ARG, "max_nb must be >= 1");
+  if (B > 0 && (!block_tables || !context_lens || !slot_mapping))
+    return fail(KV_ERR_INVALID_ARG, "block_tables, context_lens and slot_mapping must be non-NULL");
+  pagedkv::SlotMappingArgs a{block_tables, max_nb, context_lens, B, slot_mapping};
+  return hip_status(pagedkv::launch_slot_mapping(a, static_cast<hipStream_t>(stream)),
+                    "slot mapping launch");
+}
+
+kv_status reshape_and_cache(const kv_pool* pool, const void* key, const void* value,
+                            const int64_t* slot_mapping, int32_t N, void* stream) {
+  if (!pool) return fail(KV_ERR_INVALID_ARG, "pool is NULL");
+  if (N < 0) return fail(KV_ERR_INVALID_ARG, "N must be >= 0");
+  if (N == 0) return ok();
+  if (!key || !value || !slot_mapping)
+    return fail(KV_ERR_INVALID_ARG, "key, value and slot_mapping must be non-NULL");
+  if (!aligned16(key) || !aligned16(value))
+    return fail(KV_ERR_INVALID_ARG, "key and value must be 16-byte aligned");
+  const kv_pool_desc& d = pool->desc;
+  pagedkv::CacheWriteArgs a{pool->k_cache, pool->v_cache, d.num_blocks, d.num_kv_heads,
+                            d.head_dim, key, value, slot_mapping, N};
+  return hip_status(pagedkv::launch_cache_write(a, d.dtype == KV_BF16,
+                                                static_cast<hipStream_t>(stream)),
+                    "cache write launch");
+}
+
+size_t paged_attention_workspace_bytes(int32_t B, int32_t H, int32_t head_dim,
+                                       int32_t max_context_len, int32_t partition_size) {
+  if (partition_size <= 0 || B <= 0 || H <= 0 || head_dim <= 0 || max_context_len < 0) return 0;
+  const int64_t P = num_partitions(max_context_len, partition_size);
+  return workspace_view(nullptr, B, H, head_dim, P).bytes;
+}
+
+int32_t kv_decode_kernel_kind(const kv_pool* pool, int32_t H) {
+  if (!pool || H < 1 || H % pool->desc.num_kv_heads != 0) return -1;
+  return (pool->desc.dtype == KV_BF16 && H > pool->desc.num_kv_heads) ? 1 : 0;
+}
+
+kv_status paged_attention_decode(const kv_pool* pool, void* out, const void* query,
+                                 const int32_t* block_tables, int32_t max_nb,
+                                 const int32_t* context_lens, int32_t B, int32_t H,
+                                 int32_t max_context_len, float scale, int32_t partition_size,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  if (!pool) return fail(KV_ERR_INVALID_ARG, "pool is NULL");
+  const kv_pool_desc& d = pool->desc;
+  if (B < 0) return fail(KV_ERR_INVALID_ARG, "B must be >= 0");
+  if (H < 1 || H % d.num_kv_heads != 0)
+    return fail(KV_ERR_INVALID_ARG, "H (%d) must be a positive multiple of num_kv_heads (%d)", H,
+                d.num_kv_heads);
+  if (max_nb < 1) return fail(KV_ERR_INVALID_ARG, "max_nb must be >= 1");
+  if (kv_status s = check_partition(max_context_len, partition_size); s != KV_OK) return s;
+  if (!(scale == scale)) return fail(KV_ERR_INVALID_ARG, "scale is NaN");
+  if (B == 0) return ok();
+  if (!out || !query || !block_tables || !context_lens)
+    return fail(KV_ERR_INVALID_ARG, "out, query, block_tables and context_lens must be non-NULL");
+  if (!aligned16(query) || !aligned16(out))
+    return fail(KV_ERR_INVALID_ARG, "query and out must be 16-byte aligned");
+  const int64_t P = num_partitions(max_context_len, partition_size);
+  WorkspaceView ws{nullptr, nullptr, nullptr, 0};
+  if (partition_size > 0) {
+    ws = workspace_view(workspace, B, H, d.head_dim, P);
+    if (!workspace || workspace_bytes < ws.bytes)
+      return fail(KV_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", ws.bytes,
+                  workspace ? workspace_bytes : size_t(0));
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+      return fail(KV_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  }
+  pagedkv::DecodeArgs a{};
+  a.k_cache = pool->k_cache;
+  a.v_cache = pool->v_cache;
+  a.num_blocks = d.num_blocks;
+  a.num_kv_heads = d.num_kv_heads;
+  a.query = query;
+  a.out = out;
+  a.block_tables = block_tables;
+  a.max_nb = max_nb;
+  a.context_lens = context_lens;
+  a.B = B;
+  a.H = H;
+  a.max_context_len = max_context_len;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.partition_size = partition_size;
+  a.num_partitions = static_cast<int32_t>(P);
+  a.ws_o = ws.o;
+  a.ws_m = ws.m;
+  a.ws_l = ws.l;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool bf16 = d.dtype == KV_BF16;
+  hipError_t e;
+  if (kv_decode_kernel_kind(pool, H) == 1)
+    e = pagedkv::launch_decode_mfma(a, d.head_dim, s);
+  else
+    e = pagedkv::launch_decode_valu(a, bf16, d.head_dim, s);
+  return hip_status(e, "decode launch");
+}
+
+kv_status paged_attention_reduce(void* out, const void* workspace, const int32_t* context_lens,
+                                 int32_t B, int32_t H, int32_t head_dim, int32_t max_context_len,
+                                 int32_t partition_size, kv_dtype out_dtype, void* stream) {
+  if (B < 0 || H < 1) return fail(KV_ERR_INVALID_ARG, "B must be >= 0 and H >= 1");
+  if (head_dim != 64 && head_dim != 128)
+    return fail(KV_ERR_UNSUPPORTED, "head_dim %d is not supported (64 or 128)", head_dim);
+  if (out_dtype != KV_F32 && out_dtype != KV_BF16)
+    return fail(KV_ERR_UNSUPPORTED, "dtype %d is not supported", int(out_dtype));
+  if (partition_size <= 0)
+    return fail(KV_ERR_INVALID_ARG, "reduce needs the split partition_size (> 0)");
+  if (kv_status s = check_partition(max_context_len, partition_size); s != KV_OK) return s;
+  if (B == 0) return ok();
+  if (!out || !workspace || !context_lens)
+    return fail(KV_ERR_INVALID_ARG, "out, workspace and context_lens must be non-NULL");
+  const int64_t P = num_partitions(max_context_len, partition_size);
+  WorkspaceView ws = workspace_view(const_cast<void*>(workspace), B, H, head_dim, P);
+  pagedkv::ReduceArgs a{out, ws.o, ws.m, ws.l, context_lens, B, H, head_dim,
+                        static_cast<int32_t>(P), partition_size};
+  return hip_status(
+      pagedkv::launch_reduce(a, out_dtype == KV_BF16, static_cast<hipStream_t>(stream)),
+      "reduce launch");
+}
+
+const char* kv_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

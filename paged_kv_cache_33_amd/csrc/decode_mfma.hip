@@ -1,0 +1,293 @@
+// Paged decode attention for grouped-query heads on the gfx950 matrix cores.
+//
+// With g = H / H_kv query heads sharing one KV head, each K/V tile read from
+// HBM serves g queries ("MLSys Engineer - Inference Systems Q&A", Q4: the win
+// is queries per loaded K/V tile; Q7 of the "LLM inference and serving"
+// workbook: GQA heads share one KV head).  Per 16-token block the work is two
+// small dense products, done as MFMA tiles with fp32 accumulation:
+//   S  [16 tokens x 16 heads] = K [16 x d] . Q^T [d x 16]      (d/32 x 16x16x32)
+//   O^T [d x 16 heads]       += V^T [d x 16 tokens] . P^T [16 x 16] (d/16 x 16x16x16)
+// Query heads beyond g in the 16-wide tile are zero columns and are never
+// written out.  Softmax is online per head column, as in the VALU kernel.
+//
+// Operand layouts (wave64, lane l, q = l / 16, n = l % 16):
+//   16x16x32 bf16: A row n, k = 8q..8q+7; B column n, k = 8q..8q+7;
+//   16x16x16 bf16: A row n, k = 4q..4q+3; B column n, k = 4q..4q+3;
+//   accumulator: register j holds row 4q + j, column n.
+// K's [d/8][16][8] tile puts the 8 dims of chunk 4i + q of token n in one
+// 16-byte load (a coalesced 1 KiB per wave); the contraction runs over dims in
+// that chunk order, and Q's operand is loaded in the same order.  V's [d][16]
+// tile puts tokens 4q..4q+3 of dim 16mc + n in one 8-byte load (a coalesced
+// 512 B per wave).  The S accumulator (tokens 4q+j of head n) is already the
+// P^T operand of the second product, so no data moves between lanes.
+#include "device_common.h"
+#include "launch.h"
+
+namespace pagedkv {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kHeadsPerTile = 16;
+
+typedef __bf16 bf16x8_t __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef short short4_t __attribute__((__vector_size__(4 * sizeof(short))));
+typedef float floatx4_t __attribute__((__vector_size__(4 * sizeof(float))));
+
+template <int D>
+struct MfmaShape {
+  static constexpr int KI = D / 32;  // QK products per block (= 16-byte K loads per lane)
+  static constexpr int MC = D / 16;  // PV products per block (= 8-byte V loads per lane)
+};
+
+template <int D>
+struct MfmaFrag {
+  uint4 k[MfmaShape<D>::KI];
+  uint2 v[MfmaShape<D>::MC];
+};
+
+template <int D>
+__device__ __forceinline__ void load_block(MfmaFrag<D>& f, const uint16_t* kt, const uint16_t* vt,
+                                           int lane) {
+#pragma unroll
+  for (int i = 0; i < MfmaShape<D>::KI; ++i)
+    f.k[i] = *reinterpret_cast<const uint4*>(kt + (i * kWave + lane) * 8);
+  const int n = lane & 15, q = lane >> 4;
+#pragma unroll
+  for (int mc = 0; mc < MfmaShape<D>::MC; ++mc)
+    f.v[mc] = *reinterpret_cast<const uint2*>(vt + (16 * mc + n) * kBlockTokens + 4 * q);
+}
+
+template <int D>
+struct MfmaState {
+  floatx4_t o[MfmaShape<D>::MC];  // O^T[16mc + 4q + j][head n]
+  float m;                        // running max of head n (base 2)
+  float l;                        // denominator share of head n over tokens 4q..4q+3
+};
+
+__device__ __forceinline__ uint32_t zero_masked_pair(uint32_t w, bool keep_lo, bool keep_hi) {
+  return (keep_lo ? (w & 0x0000ffffu) : 0u) | (keep_hi ? (w & 0xffff0000u) : 0u);
+}
+
+template <int D, bool kTail>
+__device__ __forceinline__ void compute_block(const MfmaFrag<D>& f,
+                                              const bf16x8_t (&qop)[MfmaShape<D>::KI],
+                                              MfmaState<D>& st, int nvalid, float scale_log2,
+                                              int lane) {
+  const int q = lane >> 4;
+  floatx4_t s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < MfmaShape<D>::KI; ++i)
+    s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, f.k[i]), qop[i], s,
+                                                0, 0, 0);
+  float sc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    sc[j] = s[j] * scale_log2;
+    if (kTail && 4 * q + j >= nvalid) sc[j] = -INFINITY;  // select: the slot may hold NaN
+  }
+  float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+  mx = wave_xor_max(mx, 16);
+  mx = wave_xor_max(mx, 32);
+  const float m_new = fmaxf(st.m, mx);
+  const float alpha = fast_exp2(st.m - m_new);
+  st.m = m_new;
+  uint16_t pb[4];
+  float psum = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    pb[j] = f32_to_bf16_rne(fast_exp2(sc[j] - m_new));
+    psum += bf16_to_f32(pb[j]);  // the denominator sums the same rounded weights
+  }
+  st.l = fmaf(st.l, alpha, psum);
+  short4_t pop;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) pop[j] = static_cast<short>(pb[j]);
+#pragma unroll
+  for (int mc = 0; mc < MfmaShape<D>::MC; ++mc) {
+    uint2 v = f.v[mc];
+    if (kTail) {  // tokens past the range get weight 0; their V must be 0, not NaN
+      v.x = zero_masked_pair(v.x, 4 * q + 0 < nvalid, 4 * q + 1 < nvalid);
+      v.y = zero_masked_pair(v.y, 4 * q + 2 < nvalid, 4 * q + 3 < nvalid);
+    }
+    st.o[mc] *= alpha;
+    st.o[mc] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(short4_t, v), pop,
+                                                        st.o[mc], 0, 0, 0);
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kWaves * kWave) void decode_mfma_kernel(DecodeArgs a) {
+  constexpr int KI = MfmaShape<D>::KI;
+  constexpr int MC = MfmaShape<D>::MC;
+  constexpr int kRow = D + 4;  // padded LDS row (floats)
+
+  __shared__ __attribute__((aligned(16))) float sm_o[kWaves][kHeadsPerTile][kRow];
+  __shared__ float sm_m[kWaves][kHeadsPerTile];
+  __shared__ float sm_l[kWaves][kHeadsPerTile];
+  __shared__ int sm_bad[kWaves];
+
+  const int g = a.H / a.num_kv_heads;
+  const int ngroups = (g + kHeadsPerTile - 1) / kHeadsPerTile;
+  const int part = blockIdx.x;
+  const int kvh = blockIdx.y / ngroups;
+  const int hg = blockIdx.y % ngroups;
+  const int b = blockIdx.z;
+  const int head0 = kvh * g + hg * kHeadsPerTile;
+  const int nh = min(kHeadsPerTile, g - hg * kHeadsPerTile);
+  const int lane = threadIdx.x % kWave;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int n = lane & 15, q = lane >> 4;
+
+  const int ctx = a.context_lens[b];
+  const bool split = a.partition_size > 0;
+  const int nparts = split ? (ctx > 0 ? (ctx + a.partition_size - 1) / a.partition_size : 0) : 1;
+  const bool bad_len = ctx > a.max_nb * kBlockTokens || (split && nparts > a.num_partitions);
+  uint16_t* out = static_cast<uint16_t*>(a.out);
+  auto out_at = [&](int hh, int x) -> uint16_t& {
+    return out[(size_t(b) * a.H + head0 + hh) * D + x];
+  };
+  auto prow = [&](int hh) -> size_t {
+    return (size_t(b) * a.H + head0 + hh) * a.num_partitions + part;
+  };
+
+  if (!split && (ctx <= 0 || bad_len)) {
+    const uint16_t fill = ctx <= 0 ? uint16_t(0) : uint16_t(0x7fc0);
+    for (int idx = threadIdx.x; idx < nh * D; idx += blockDim.x) out_at(idx / D, idx % D) = fill;
+    return;
+  }
+  if (split && bad_len) {
+    if (part >= nparts) return;
+    for (int idx = threadIdx.x; idx < nh * D; idx += blockDim.x) {
+      const int hh = idx / D, x = idx % D;
+      if (nparts == 1) {
+        out_at(hh, x) = 0x7fc0;
+      } else {
+        a.ws_o[prow(hh) * D + x] = __int_as_float(0x7fc00000);
+        if (x == 0) { a.ws_m[prow(hh)] = 0.f; a.ws_l[prow(hh)] = 1.f; }
+      }
+    }
+    return;
+  }
+  if (split && part >= nparts) return;
+
+  const int tb = split ? part * a.partition_size : 0;
+  const int te = split ? min(tb + a.partition_size, ctx) : ctx;
+  const int jb = tb / kBlockTokens;
+  const int je = (te + kBlockTokens - 1) / kBlockTokens;
+
+  // Q^T operand: head n of this tile, dims of chunk 4i + q; zero past the group.
+  bf16x8_t qop[KI];
+  {
+    const uint16_t* qrow =
+        static_cast<const uint16_t*>(a.query) + (size_t(b) * a.H + head0 + min(n, nh - 1)) * D;
+#pragma unroll
+    for (int i = 0; i < KI; ++i) {
+      uint4 raw = *reinterpret_cast<const uint4*>(qrow + (4 * i + q) * 8);
+      if (n >= nh) raw = make_uint4(0u, 0u, 0u, 0u);
+      qop[i] = __builtin_bit_cast(bf16x8_t, raw);
+    }
+  }
+
+  const uint16_t* kc = static_cast<const uint16_t*>(a.k_cache);
+  const uint16_t* vc = static_cast<const uint16_t*>(a.v_cache);
+  const int32_t* table = a.block_tables + int64_t(b) * a.max_nb;
+  const int64_t tile_elems = int64_t(kBlockTokens) * D;
+
+  MfmaState<D> st;
+#pragma unroll
+  for (int mc = 0; mc < MC; ++mc) st.o[mc] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+  st.m = -INFINITY;
+  st.l = 0.f;
+  int bad_blk = 0;
+
+  auto fetch = [&](int j, MfmaFrag<D>& f) -> bool {
+    const int p = __builtin_amdgcn_readfirstlane(table[j]);
+    if (p < 0 || p >= a.num_blocks) return false;
+    const int64_t tile = (int64_t(p) * a.num_kv_heads + kvh) * tile_elems;
+    load_block<D>(f, kc + tile, vc + tile, lane);
+    return true;
+  };
+  auto consume = [&](int j, bool ok, const MfmaFrag<D>& f) {
+    if (!ok) { bad_blk = 1; return; }
+    const int nvalid = te - j * kBlockTokens;
+    if (nvalid >= kBlockTokens)
+      compute_block<D, false>(f, qop, st, nvalid, a.scale_log2, lane);
+    else
+      compute_block<D, true>(f, qop, st, nvalid, a.scale_log2, lane);
+  };
+
+  MfmaFrag<D> fa, fb;
+  int j = jb + w;
+  bool ok_a = false, ok_b = false;
+  if (j < je) ok_a = fetch(j, fa);
+  while (j < je) {
+    const int j1 = j + kWaves;
+    if (j1 < je) ok_b = fetch(j1, fb);
+    consume(j, ok_a, fa);
+    if (j1 >= je) break;
+    const int j2 = j1 + kWaves;
+    if (j2 < je) ok_a = fetch(j2, fa);
+    consume(j1, ok_b, fb);
+    j = j2;
+  }
+
+  float lsum = st.l;
+  lsum = wave_xor_add(lsum, 16);
+  lsum = wave_xor_add(lsum, 32);
+  if (q == 0) {
+    sm_m[w][n] = st.m;
+    sm_l[w][n] = lsum;
+  }
+  if (lane == 0) sm_bad[w] = bad_blk;
+#pragma unroll
+  for (int mc = 0; mc < MC; ++mc)
+    *reinterpret_cast<floatx4_t*>(&sm_o[w][n][16 * mc + 4 * q]) = st.o[mc];
+  __syncthreads();
+
+  int bad = 0;
+#pragma unroll
+  for (int ww = 0; ww < kWaves; ++ww) bad |= sm_bad[ww];
+  for (int idx = threadIdx.x; idx < nh * D; idx += blockDim.x) {
+    const int hh = idx / D, x = idx % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, sm_m[ww][hh]);
+    float L = 0.f, acc = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww) {
+      if (sm_m[ww][hh] == -INFINITY) continue;
+      const float sc = fast_exp2(sm_m[ww][hh] - M);
+      L = fmaf(sm_l[ww][hh], sc, L);
+      acc = fmaf(sm_o[ww][hh][x], sc, acc);
+    }
+    float res = acc / L;
+    if (bad) res = __int_as_float(0x7fc00000);
+    if (!split || nparts == 1) {
+      out_at(hh, x) = f32_to_bf16_rne(res);
+    } else {
+      a.ws_o[prow(hh) * D + x] = res;
+      if (x == 0) {
+        a.ws_m[prow(hh)] = bad ? 0.f : M;
+        a.ws_l[prow(hh)] = bad ? 1.f : L;
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_decode_mfma(const DecodeArgs& a, int head_dim, hipStream_t s) {
+  const int g = a.H / a.num_kv_heads;
+  const int ngroups = (g + kHeadsPerTile - 1) / kHeadsPerTile;
+  const dim3 grid(a.num_partitions, a.num_kv_heads * ngroups, a.B);
+  const dim3 block(kWaves * kWave);
+  if (head_dim == 128)
+    hipLaunchKernelGGL(decode_mfma_kernel<128>, grid, block, 0, s, a);
+  else if (head_dim == 64)
+    hipLaunchKernelGGL(decode_mfma_kernel<64>, grid, block, 0, s, a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace pagedkv

@@ -1,0 +1,285 @@
+// Paged decode attention on the vector ALUs: one query head per work-group.
+//
+// What it computes ("MLSys Engineer - Inference Systems Q&A", Q1 and Q4; the
+// "LLM inference and serving" workbook's incremental decoder): for query head h
+// of sequence b, out = softmax_t(scale * q . K[t]) V[t] over the ctx tokens of
+// the sequence, K[t] and V[t] read through the block table.  Scores stay in
+// registers; a running max and denominator are rescaled whenever the max
+// rises (online softmax); everything accumulates in fp32.
+//
+// Work decomposition: a work-group of 4 wavefronts takes one (partition, query
+// head, sequence); wave w walks the partition's blocks w, w+4, w+8, ...
+// keeping its own (m, l, O), and the four are merged through LDS at the end.
+// The next block's K and V are loaded while the current one is computed.
+//
+// Lane mapping for one 16-token block (see the pool layout in pagedkv.h):
+//   K tile [d/X][16][X]: load i gives lane l the 16-byte chunk 4i + l/16 of
+//     token l%16; each lane forms a partial dot over its chunks, and two
+//     cross-row shuffles complete the score of token l%16 in every row.
+//   V tile [d][16]: lane l owns dims l and l+64; each 16-byte load gives it X
+//     consecutive tokens of one dim, and the tokens are the same for every lane,
+//     so the 16 probabilities are broadcast once per block (readlane) and
+//     each lane does plain fp32 FMAs.
+#include "device_common.h"
+#include "launch.h"
+
+namespace pagedkv {
+namespace {
+
+constexpr int kWaves = 4;
+
+template <typename Tr, int D>
+struct ValuShape {
+  static constexpr int X = Tr::kChunk;  // elements per 16-byte chunk
+  static constexpr int C = D / X;       // chunks per token row
+  static constexpr int KL = C / 4;      // K loads per lane per block
+  static constexpr int XK = D / 64;     // output dims per lane
+  static constexpr int R = 16 / X;      // 16-byte pieces per V row (16 tokens)
+  static constexpr int VL = XK * R;     // V loads per lane per block
+};
+
+template <typename Tr, int D>
+struct BlockFrag {
+  uint4 k[ValuShape<Tr, D>::KL];
+  uint4 v[ValuShape<Tr, D>::VL];
+};
+
+template <typename Tr, int D>
+__device__ __forceinline__ void load_block(BlockFrag<Tr, D>& f, const typename Tr::storage* kt,
+                                           const typename Tr::storage* vt, int lane) {
+  using Sh = ValuShape<Tr, D>;
+#pragma unroll
+  for (int i = 0; i < Sh::KL; ++i)
+    f.k[i] = *reinterpret_cast<const uint4*>(kt + (i * kWave + lane) * Sh::X);
+#pragma unroll
+  for (int xk = 0; xk < Sh::XK; ++xk)
+#pragma unroll
+    for (int th = 0; th < Sh::R; ++th)
+      f.v[xk * Sh::R + th] =
+          *reinterpret_cast<const uint4*>(vt + ((xk * kWave + lane) * kBlockTokens + th * Sh::X));
+}
+
+struct WaveState {
+  float m;    // running max (base-2 units), uniform across the wave
+  float l;    // this lane's share of the denominator (token lane%16)
+};
+
+// One block of 16 tokens; `nvalid` (uniform) tokens of it are inside the range.
+template <typename Tr, int D, bool kTail>
+__device__ __forceinline__ void compute_block(const BlockFrag<Tr, D>& f,
+                                              const float (&qf)[ValuShape<Tr, D>::KL][Tr::kChunk],
+                                              float (&o)[ValuShape<Tr, D>::XK], WaveState& st,
+                                              int nvalid, float scale_log2, int lane) {
+  using Sh = ValuShape<Tr, D>;
+  constexpr int X = Sh::X;
+  float dot = 0.f;
+#pragma unroll
+  for (int i = 0; i < Sh::KL; ++i) {
+    float kf[X];
+    unpack_chunk(f.k[i], kf, Tr{});
+#pragma unroll
+    for (int e = 0; e < X; ++e) dot = fmaf(qf[i][e], kf[e], dot);
+  }
+  dot = wave_xor_add(dot, 16);
+  dot = wave_xor_add(dot, 32);
+  const int t = lane & 15;
+  float s = dot * scale_log2;
+  if (kTail && t >= nvalid) s = -INFINITY;  // select, never multiply: slot may hold NaN
+  float mb = s;
+  mb = wave_xor_max(mb, 1);
+  mb = wave_xor_max(mb, 2);
+  mb = wave_xor_max(mb, 4);
+  mb = wave_xor_max(mb, 8);
+  const float m_new = fmaxf(st.m, mb);
+  const float alpha = fast_exp2(st.m - m_new);
+  const float p = fast_exp2(s - m_new);
+  st.l = fmaf(st.l, alpha, p);
+  st.m = m_new;
+#pragma unroll
+  for (int xk = 0; xk < Sh::XK; ++xk) o[xk] *= alpha;
+  float ps[kBlockTokens];
+#pragma unroll
+  for (int tt = 0; tt < kBlockTokens; ++tt)
+    ps[tt] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(p), tt));
+#pragma unroll
+  for (int xk = 0; xk < Sh::XK; ++xk) {
+#pragma unroll
+    for (int th = 0; th < Sh::R; ++th) {
+      float vf[X];
+      unpack_chunk(f.v[xk * Sh::R + th], vf, Tr{});
+#pragma unroll
+      for (int e = 0; e < X; ++e) {
+        const int tt = th * X + e;
+        if (!kTail || tt < nvalid) o[xk] = fmaf(ps[tt], vf[e], o[xk]);
+      }
+    }
+  }
+}
+
+template <typename Tr, int D>
+__global__ __launch_bounds__(kWaves * kWave) void decode_valu_kernel(DecodeArgs a) {
+  using S = typename Tr::storage;
+  using Sh = ValuShape<Tr, D>;
+  constexpr int X = Sh::X;
+
+  __shared__ float sm_o[kWaves][D];
+  __shared__ float sm_m[kWaves];
+  __shared__ float sm_l[kWaves];
+  __shared__ int sm_bad[kWaves];
+
+  const int part = blockIdx.x;
+  const int h = blockIdx.y;
+  const int b = blockIdx.z;
+  const int lane = threadIdx.x % kWave;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int kvh = h / (a.H / a.num_kv_heads);
+  const int ctx = a.context_lens[b];
+  const bool split = a.partition_size > 0;
+  const int nparts = split ? (ctx > 0 ? (ctx + a.partition_size - 1) / a.partition_size : 0) : 1;
+  const bool bad_len = ctx > a.max_nb * kBlockTokens || (split && nparts > a.num_partitions);
+  const size_t row = (size_t(b) * a.H + h) * D;
+  S* out = static_cast<S*>(a.out) + row;
+  const size_t prow = (size_t(b) * a.H + h) * a.num_partitions + part;
+
+  if (!split && (ctx <= 0 || bad_len)) {
+    const float fill = ctx <= 0 ? 0.f : __int_as_float(0x7fc00000);
+    for (int x = threadIdx.x; x < D; x += blockDim.x) out[x] = Tr::from_f32(fill);
+    return;
+  }
+  if (split && bad_len) {
+    if (part >= nparts) return;
+    const float nan = __int_as_float(0x7fc00000);
+    if (nparts == 1) {
+      for (int x = threadIdx.x; x < D; x += blockDim.x) out[x] = Tr::from_f32(nan);
+    } else {
+      for (int x = threadIdx.x; x < D; x += blockDim.x) a.ws_o[prow * D + x] = nan;
+      if (threadIdx.x == 0) { a.ws_m[prow] = 0.f; a.ws_l[prow] = 1.f; }
+    }
+    return;
+  }
+  if (split && part >= nparts) return;
+
+  const int tb = split ? part * a.partition_size : 0;
+  const int te = split ? min(tb + a.partition_size, ctx) : ctx;
+  const int jb = tb / kBlockTokens;
+  const int je = (te + kBlockTokens - 1) / kBlockTokens;
+
+  // This lane's slice of the query: chunks 4i + lane/16, as fp32.
+  float qf[Sh::KL][X];
+  {
+    const S* qrow = static_cast<const S*>(a.query) + row;
+#pragma unroll
+    for (int i = 0; i < Sh::KL; ++i) {
+      const uint4 raw = *reinterpret_cast<const uint4*>(qrow + (4 * i + lane / 16) * X);
+      unpack_chunk(raw, qf[i], Tr{});
+    }
+  }
+
+  const S* kc = static_cast<const S*>(a.k_cache);
+  const S* vc = static_cast<const S*>(a.v_cache);
+  const int32_t* table = a.block_tables + int64_t(b) * a.max_nb;
+  const int64_t tile_elems = int64_t(kBlockTokens) * D;
+
+  WaveState st{-INFINITY, 0.f};
+  float o[Sh::XK];
+#pragma unroll
+  for (int xk = 0; xk < Sh::XK; ++xk) o[xk] = 0.f;
+  int bad_blk = 0;
+
+  // Returns false (and loads nothing) for a table entry outside the pool.
+  auto fetch = [&](int j, BlockFrag<Tr, D>& f) -> bool {
+    const int p = __builtin_amdgcn_readfirstlane(table[j]);
+    if (p < 0 || p >= a.num_blocks) return false;
+    const int64_t tile = (int64_t(p) * a.num_kv_heads + kvh) * tile_elems;
+    load_block<Tr, D>(f, kc + tile, vc + tile, lane);
+    return true;
+  };
+  auto consume = [&](int j, bool ok, const BlockFrag<Tr, D>& f) {
+    if (!ok) { bad_blk = 1; return; }
+    const int nvalid = te - j * kBlockTokens;
+    if (nvalid >= kBlockTokens)
+      compute_block<Tr, D, false>(f, qf, o, st, nvalid, a.scale_log2, lane);
+    else
+      compute_block<Tr, D, true>(f, qf, o, st, nvalid, a.scale_log2, lane);
+  };
+
+  // Ping-pong over two register buffers: block j+4 is in flight while j computes.
+  BlockFrag<Tr, D> fa, fb;
+  int j = jb + w;
+  bool ok_a = false, ok_b = false;
+  if (j < je) ok_a = fetch(j, fa);
+  while (j < je) {
+    const int j1 = j + kWaves;
+    if (j1 < je) ok_b = fetch(j1, fb);
+    consume(j, ok_a, fa);
+    if (j1 >= je) break;
+    const int j2 = j1 + kWaves;
+    if (j2 < je) ok_a = fetch(j2, fa);
+    consume(j1, ok_b, fb);
+    j = j2;
+  }
+
+  // Wave totals: the denominator is spread over the 16 token lanes of a row.
+  float lsum = st.l;
+  lsum = wave_xor_add(lsum, 1);
+  lsum = wave_xor_add(lsum, 2);
+  lsum = wave_xor_add(lsum, 4);
+  lsum = wave_xor_add(lsum, 8);
+  if (lane == 0) {
+    sm_m[w] = st.m;
+    sm_l[w] = lsum;
+    sm_bad[w] = bad_blk;
+  }
+#pragma unroll
+  for (int xk = 0; xk < Sh::XK; ++xk) sm_o[w][xk * kWave + lane] = o[xk];
+  __syncthreads();
+
+  for (int x = threadIdx.x; x < D; x += blockDim.x) {
+    float M = -INFINITY;
+    int bad = 0;
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww) {
+      M = fmaxf(M, sm_m[ww]);
+      bad |= sm_bad[ww];
+    }
+    float L = 0.f, acc = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww) {
+      if (sm_m[ww] == -INFINITY) continue;  // a wave that saw no block
+      const float sc = fast_exp2(sm_m[ww] - M);
+      L = fmaf(sm_l[ww], sc, L);
+      acc = fmaf(sm_o[ww][x], sc, acc);
+    }
+    float res = acc / L;
+    if (bad) res = __int_as_float(0x7fc00000);
+    if (!split || nparts == 1) {
+      out[x] = Tr::from_f32(res);
+    } else {
+      a.ws_o[prow * D + x] = res;
+      if (x == 0) {
+        a.ws_m[prow] = bad ? 0.f : M;
+        a.ws_l[prow] = bad ? 1.f : L;
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_decode_valu(const DecodeArgs& a, bool bf16, int head_dim, hipStream_t s) {
+  const dim3 grid(a.num_partitions, a.H, a.B);
+  const dim3 block(kWaves * kWave);
+  if (bf16 && head_dim == 128)
+    hipLaunchKernelGGL((decode_valu_kernel<Bf16, 128>), grid, block, 0, s, a);
+  else if (bf16 && head_dim == 64)
+    hipLaunchKernelGGL((decode_valu_kernel<Bf16, 64>), grid, block, 0, s, a);
+  else if (!bf16 && head_dim == 128)
+    hipLaunchKernelGGL((decode_valu_kernel<F32, 128>), grid, block, 0, s, a);
+  else if (!bf16 && head_dim == 64)
+    hipLaunchKernelGGL((decode_valu_kernel<F32, 64>), grid, block, 0, s, a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace pagedkv

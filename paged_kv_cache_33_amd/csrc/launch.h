@@ -1,0 +1,71 @@
+// Internal launch interface between the C ABI (api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pagedkv {
+
+// Everything a decode kernel needs; passed by value as the kernel argument.
+struct DecodeArgs {
+  const void* k_cache;
+  const void* v_cache;
+  int32_t num_blocks;
+  int32_t num_kv_heads;
+  const void* query;           // [B][H][d]
+  void* out;                   // [B][H][d]
+  const int32_t* block_tables; // [B][max_nb]
+  int32_t max_nb;
+  const int32_t* context_lens; // [B]
+  int32_t B;
+  int32_t H;
+  int32_t max_context_len;
+  float scale_log2;            // scale * log2(e): scores are kept in base 2
+  int32_t partition_size;      // tokens per partition; 0 = whole sequence
+  int32_t num_partitions;      // partitions per sequence in the grid (1 if single pass)
+  float* ws_o;                 // [B][H][P][d]   (split mode only)
+  float* ws_m;                 // [B][H][P]
+  float* ws_l;                 // [B][H][P]
+};
+
+struct ReduceArgs {
+  void* out;
+  const float* ws_o;
+  const float* ws_m;
+  const float* ws_l;
+  const int32_t* context_lens;
+  int32_t B;
+  int32_t H;
+  int32_t head_dim;
+  int32_t num_partitions;
+  int32_t partition_size;
+};
+
+struct CacheWriteArgs {
+  void* k_cache;
+  void* v_cache;
+  int32_t num_blocks;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  const void* key;              // [N][H_kv][d]
+  const void* value;
+  const int64_t* slot_mapping;  // [N]
+  int32_t N;
+};
+
+struct SlotMappingArgs {
+  const int32_t* block_tables;
+  int32_t max_nb;
+  const int32_t* context_lens;
+  int32_t B;
+  int64_t* slot_mapping;
+};
+
+// Launchers: return the hipError_t of the launch.
+hipError_t launch_slot_mapping(const SlotMappingArgs& a, hipStream_t s);
+hipError_t launch_cache_write(const CacheWriteArgs& a, bool bf16, hipStream_t s);
+hipError_t launch_decode_valu(const DecodeArgs& a, bool bf16, int head_dim, hipStream_t s);
+hipError_t launch_decode_mfma(const DecodeArgs& a, int head_dim, hipStream_t s);
+hipError_t launch_reduce(const ReduceArgs& a, bool bf16_out, hipStream_t s);
+
+}  // namespace pagedkv

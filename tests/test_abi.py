@@ -1,0 +1,183 @@
+"""The C ABI without a GPU: the library loads, exports every declared symbol,
+and rejects bad arguments synchronously, before anything is enqueued.
+
+No call here reaches a kernel launch: each one fails validation first or has
+nothing to launch (B = 0, N = 0).  Device pointers passed to kv_pool_create
+are never dereferenced on the host.
+"""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from paged_kv_cache_33_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pagedkv.h")
+
+FAKE_K = 0x10000  # aligned, never dereferenced by host code
+FAKE_V = 0x20000
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    text = "\n".join(l for l in text.splitlines() if not l.strip().startswith("#"))
+    text = text.replace('extern "C" {', " ")
+    names = []
+    for stmt in text.split(";"):
+        if "{" in stmt or "}" in stmt and "(" not in stmt or "typedef" in stmt:
+            continue
+        m = re.search(r"(\w+)\s*\(([^()]*)\)\s*$", stmt.strip().rstrip("}").strip())
+        if m:
+            names.append(m.group(1))
+    return names
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def desc(num_blocks=8, block_size=16, H_kv=2, d=128, dtype=_lib.KV_BF16):
+    return _lib.KVPoolDesc(num_blocks, block_size, H_kv, d, dtype)
+
+
+def test_header_declares_the_expected_calls():
+    names = declared_functions()
+    assert set(names) == set(_lib.EXPORTED), names
+    for required in ("kv_pool_create", "reshape_and_cache", "paged_attention_decode",
+                     "paged_attention_reduce"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_pool_bytes(lib):
+    assert lib.kv_pool_bytes(C.byref(desc(8, 16, 2, 128, _lib.KV_BF16))) == 8 * 2 * 16 * 128 * 2
+    assert lib.kv_pool_bytes(C.byref(desc(3, 16, 1, 64, _lib.KV_F32))) == 3 * 16 * 64 * 4
+    assert lib.kv_pool_bytes(C.byref(desc(8, 32, 2, 128))) == 0
+    assert lib.kv_pool_bytes(C.byref(desc(8, 16, 2, 96))) == 0
+    assert lib.kv_pool_bytes(None) == 0
+
+
+def _create(lib, d, k=FAKE_K, v=FAKE_V):
+    h = C.c_void_p()
+    st = lib.kv_pool_create(C.byref(d) if d is not None else None, k, v, C.byref(h))
+    return st, h
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(dtype=7), _lib.KV_ERR_UNSUPPORTED),
+    (dict(block_size=32), _lib.KV_ERR_UNSUPPORTED),
+    (dict(d=96), _lib.KV_ERR_UNSUPPORTED),
+    (dict(num_blocks=0), _lib.KV_ERR_INVALID_ARG),
+    (dict(H_kv=0), _lib.KV_ERR_INVALID_ARG),
+])
+def test_pool_create_rejects_bad_descriptors(lib, bad, code):
+    st, h = _create(lib, desc(**bad))
+    assert st == code
+    assert h.value is None
+    assert lib.kv_last_error()
+
+
+def test_pool_create_rejects_null_and_misaligned(lib):
+    assert _create(lib, None)[0] == _lib.KV_ERR_INVALID_ARG
+    assert _create(lib, desc(), k=0)[0] == _lib.KV_ERR_INVALID_ARG
+    assert _create(lib, desc(), v=FAKE_V + 2)[0] == _lib.KV_ERR_INVALID_ARG
+    assert b"aligned" in lib.kv_last_error()
+
+
+@pytest.fixture
+def pool(lib):
+    st, h = _create(lib, desc(8, 16, 2, 128, _lib.KV_BF16))
+    assert st == _lib.KV_OK and h.value
+    assert lib.kv_last_error() == b""
+    yield h
+    lib.kv_pool_destroy(h)
+
+
+def test_kernel_kind(lib, pool):
+    assert lib.kv_decode_kernel_kind(pool, 2) == 0      # MHA: vector ALU
+    assert lib.kv_decode_kernel_kind(pool, 16) == 1     # GQA bf16: matrix cores
+    assert lib.kv_decode_kernel_kind(pool, 3) == -1     # not a multiple of H_kv
+    st, hf = _create(lib, desc(8, 16, 2, 64, _lib.KV_F32))
+    assert lib.kv_decode_kernel_kind(hf, 8) == 0        # fp32: vector ALU
+    lib.kv_pool_destroy(hf)
+
+
+def test_cache_write_argument_errors(lib, pool):
+    assert lib.reshape_and_cache(None, FAKE_K, FAKE_V, FAKE_K, 1, None) == _lib.KV_ERR_INVALID_ARG
+    assert lib.reshape_and_cache(pool, FAKE_K, FAKE_V, FAKE_K, -1, None) == _lib.KV_ERR_INVALID_ARG
+    assert lib.reshape_and_cache(pool, None, FAKE_V, FAKE_K, 1, None) == _lib.KV_ERR_INVALID_ARG
+    assert lib.reshape_and_cache(pool, FAKE_K + 4, FAKE_V, FAKE_K, 1, None) == _lib.KV_ERR_INVALID_ARG
+    assert lib.reshape_and_cache(pool, None, None, None, 0, None) == _lib.KV_OK  # nothing to do
+
+
+def test_slot_mapping_argument_errors(lib):
+    assert lib.kv_slot_mapping(None, 4, None, -1, None, None) == _lib.KV_ERR_INVALID_ARG
+    assert lib.kv_slot_mapping(FAKE_K, 0, FAKE_K, 1, FAKE_V, None) == _lib.KV_ERR_INVALID_ARG
+    assert lib.kv_slot_mapping(None, 4, FAKE_K, 1, FAKE_V, None) == _lib.KV_ERR_INVALID_ARG
+
+
+def _decode(lib, pool, B=2, H=4, max_nb=4, max_ctx=64, scale=0.1, P=0, ws=None, ws_bytes=0,
+            out=FAKE_K, q=FAKE_V):
+    return lib.paged_attention_decode(pool, out, q, FAKE_K, max_nb, FAKE_V, B, H, max_ctx, scale,
+                                      P, ws, ws_bytes, None)
+
+
+def test_decode_argument_errors(lib, pool):
+    assert _decode(lib, None) == _lib.KV_ERR_INVALID_ARG
+    assert _decode(lib, pool, H=3) == _lib.KV_ERR_INVALID_ARG
+    assert _decode(lib, pool, B=-1) == _lib.KV_ERR_INVALID_ARG
+    assert _decode(lib, pool, max_nb=0) == _lib.KV_ERR_INVALID_ARG
+    assert _decode(lib, pool, P=24) == _lib.KV_ERR_INVALID_ARG
+    assert _decode(lib, pool, P=-16) == _lib.KV_ERR_INVALID_ARG
+    assert _decode(lib, pool, scale=float("nan")) == _lib.KV_ERR_INVALID_ARG
+    assert _decode(lib, pool, out=None) == _lib.KV_ERR_INVALID_ARG
+    assert _decode(lib, pool, q=FAKE_V + 8) == _lib.KV_ERR_INVALID_ARG
+    assert _decode(lib, pool, P=16, ws=None) == _lib.KV_ERR_WORKSPACE
+    need = lib.paged_attention_workspace_bytes(2, 4, 128, 64, 16)
+    assert _decode(lib, pool, P=16, ws=FAKE_K, ws_bytes=need - 1) == _lib.KV_ERR_WORKSPACE
+    assert b"workspace" in lib.kv_last_error()
+    assert _decode(lib, pool, P=16, ws=FAKE_K + 16, ws_bytes=need) == _lib.KV_ERR_WORKSPACE
+    assert _decode(lib, pool, max_ctx=16 * 8193, P=16, ws=FAKE_K, ws_bytes=1 << 40) \
+        == _lib.KV_ERR_INVALID_ARG
+    assert _decode(lib, pool, B=0) == _lib.KV_OK  # nothing to launch
+
+
+def test_workspace_size_formula(lib):
+    def al(x):
+        return (x + 255) // 256 * 256
+    for B, H, d, L, P in [(8, 32, 128, 100000, 512), (2, 2, 64, 33, 16), (1, 1, 128, 1, 512)]:
+        n = B * H * -(-L // P)
+        assert lib.paged_attention_workspace_bytes(B, H, d, L, P) == al(n * d * 4) + 2 * al(n * 4)
+    assert lib.paged_attention_workspace_bytes(8, 32, 128, 1000, 0) == 0
+
+
+def test_reduce_argument_errors(lib):
+    r = lib.paged_attention_reduce
+    assert r(FAKE_K, FAKE_V, FAKE_K, 2, 4, 128, 64, 0, _lib.KV_BF16, None) == _lib.KV_ERR_INVALID_ARG
+    assert r(FAKE_K, FAKE_V, FAKE_K, 2, 4, 96, 64, 16, _lib.KV_BF16, None) == _lib.KV_ERR_UNSUPPORTED
+    assert r(FAKE_K, FAKE_V, FAKE_K, 2, 4, 128, 64, 16, 5, None) == _lib.KV_ERR_UNSUPPORTED
+    assert r(None, FAKE_V, FAKE_K, 2, 4, 128, 64, 16, _lib.KV_BF16, None) == _lib.KV_ERR_INVALID_ARG
+    assert r(FAKE_K, FAKE_V, FAKE_K, 0, 4, 128, 64, 16, _lib.KV_BF16, None) == _lib.KV_OK
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    import paged_kv_cache_33_amd as P
+    with pytest.raises((ValueError, TypeError)):
+        P.kv_slot_mapping(torch.zeros((2, 3), dtype=torch.int32), torch.zeros(2, dtype=torch.int32))
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="no fallback"):
+        _lib.load()

@@ -1,0 +1,206 @@
+"""GPU parity at sizes the oracle finishes in seconds: slot mapping and cache
+writes bit-exact, decode outputs within the stated tolerances, and the
+bitwise invariances the pages imply (block permutation, shared prefix, batch
+composition).  Every call goes through the C ABI via the thin binding.
+
+Tolerances: fp32 max-abs <= 1e-5; bf16 relative-L2 <= 5e-3 and max-abs <= 1e-2
+against the float64 oracle.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import paged_kv_cache_33_amd as P
+from workloads import configs as W
+
+from _harness import (assert_close, from_dev, gpu_step, log, oracle_step, poison,
+                      single_step_case, upload)
+
+pytestmark = pytest.mark.gpu
+
+# lengths spanning: 1 token, exactly one block, one past a block, several
+# blocks with a ragged tail, and more than one 512-token partition
+LENS_SHORT = [1, 16, 17, 45, 130]
+LENS_LONG = [1, 15, 16, 17, 250, 700, 1100]
+
+
+def test_native_library_is_the_one_loaded():
+    lib = P._lib.load()
+    assert P.library_path().endswith("libpagedkv.so")
+    assert lib._name == P.library_path()
+    assert torch.cuda.is_available()
+
+
+def test_config1_tiny_fp32():
+    w = W.make_workload(1)
+    single_step_case(w, 0, label="config1")
+    single_step_case(w, 16, label="config1-split16")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("P_", [0, 16, 32, 512])
+def test_mha_bf16(d, P_):
+    w = W.scattered_workload("mha", "bf16", B=len(LENS_LONG), H=4, H_kv=4, d=d,
+                             context_lens=LENS_LONG, seed=21 + d)
+    single_step_case(w, P_, label=f"mha-bf16-d{d}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("H,H_kv", [(4, 2), (16, 2), (8, 1), (32, 2), (64, 2), (6, 2)])
+@pytest.mark.parametrize("P_", [0, 32, 512])
+def test_gqa_bf16_matrix_cores(d, H, H_kv, P_):
+    w = W.scattered_workload("gqa", "bf16", B=len(LENS_LONG), H=H, H_kv=H_kv, d=d,
+                             context_lens=LENS_LONG, seed=31 + H + d)
+    assert P.kv_decode_kernel_kind(upload(w, w.k_pool, w.v_pool).pool, H) == 1
+    single_step_case(w, P_, label=f"gqa-bf16-d{d}-g{H // H_kv}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("H,H_kv", [(2, 2), (8, 2)])
+@pytest.mark.parametrize("P_", [0, 16])
+def test_fp32_vector_alu(d, H, H_kv, P_):
+    w = W.scattered_workload("f32", "f32", B=len(LENS_SHORT), H=H, H_kv=H_kv, d=d,
+                             context_lens=LENS_SHORT, seed=41 + d + H)
+    single_step_case(w, P_, label=f"f32-d{d}-H{H}")
+
+
+@pytest.mark.parametrize("H,H_kv", [(4, 4), (8, 2)])
+@pytest.mark.parametrize("P_", [0, 16])
+def test_empty_context_gives_zeros(H, H_kv, P_):
+    lens = [0, 20, 0, 33]
+    w = W.scattered_workload("empty", "bf16", B=4, H=H, H_kv=H_kv, d=128, context_lens=lens,
+                             seed=51)
+    step = w.steps[0]
+    kp, vp = poison(w, np.maximum(step.context_lens.astype(np.int64) - 1, 0))
+    dw = upload(w, kp, vp)
+    slots, out = gpu_step(dw, step, P_)
+    got = from_dev(out, "bf16")
+    assert list(slots.cpu().numpy()[[0, 2]]) == [-1, -1]
+    assert np.all(got[[0, 2]] == 0)
+    _, _, _, ref = oracle_step(w, kp, vp, step, seqs=[1, 3])
+    assert_close(got, ref, "bf16", "empty-ctx")
+
+
+def test_empty_batch_is_a_no_op():
+    w = W.scattered_workload("e", "bf16", B=1, H=4, H_kv=4, d=128, context_lens=[5], seed=52)
+    dw = upload(w, w.k_pool, w.v_pool)
+    q = torch.empty((0, 4, 128), dtype=torch.int16, device="cuda")
+    out = torch.empty_like(q)
+    t = torch.empty((0, 1), dtype=torch.int32, device="cuda")
+    c = torch.empty((0,), dtype=torch.int32, device="cuda")
+    P.paged_attention_decode(dw.pool, out, q, t, c, 16, 0.1)
+    torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------- invariances
+def _outputs(w, kp, vp, P_=0):
+    dw = upload(w, kp, vp)
+    _, out = gpu_step(dw, w.steps[0], P_, write=False)
+    return from_dev(out, w.dtype)
+
+
+@pytest.mark.parametrize("H,H_kv", [(4, 4), (16, 2)])
+@pytest.mark.parametrize("P_", [0, 32])
+def test_block_permutation_is_bitwise_invariant(H, H_kv, P_):
+    w = W.scattered_workload("perm", "bf16", B=len(LENS_LONG), H=H, H_kv=H_kv, d=128,
+                             context_lens=LENS_LONG, seed=61)
+    kp, vp = poison(w, w.steps[0].context_lens.astype(np.int64))
+    base = _outputs(w, kp, vp, P_)
+    pi = np.random.default_rng(5).permutation(w.num_blocks)
+    tile = w.H_kv * 16 * w.d
+    kp2, vp2 = np.empty_like(kp), np.empty_like(vp)
+    for p in range(w.num_blocks):
+        kp2[pi[p] * tile:(pi[p] + 1) * tile] = kp[p * tile:(p + 1) * tile]
+        vp2[pi[p] * tile:(pi[p] + 1) * tile] = vp[p * tile:(p + 1) * tile]
+    used = w.block_tables != W.TABLE_SENTINEL
+    w.block_tables[used] = pi[w.block_tables[used]]
+    moved = _outputs(w, kp2, vp2, P_)
+    np.testing.assert_array_equal(base, moved)
+
+
+@pytest.mark.parametrize("H,H_kv", [(4, 4), (32, 8)])
+def test_shared_prefix_equals_private_copies_bitwise(H, H_kv):
+    w = W.shared_prefix_workload(7, B=6, H=H, H_kv=H_kv, d=128, steps=1, prefix_blocks=4,
+                                 private_range=(1, 40))
+    kp, vp = poison(w, w.steps[0].context_lens.astype(np.int64))
+    shared = _outputs(w, kp, vp)
+    # give every sequence its own copy of the prefix blocks
+    tile = w.H_kv * 16 * w.d
+    extra = w.B * 4
+    kp2 = np.concatenate([kp, np.empty(extra * tile, kp.dtype)])
+    vp2 = np.concatenate([vp, np.empty(extra * tile, vp.dtype)])
+    t2 = w.block_tables.copy()
+    nxt = w.num_blocks
+    for b in range(w.B):
+        for j in range(4):
+            src = int(w.block_tables[b, j])
+            kp2[nxt * tile:(nxt + 1) * tile] = kp[src * tile:(src + 1) * tile]
+            vp2[nxt * tile:(nxt + 1) * tile] = vp[src * tile:(src + 1) * tile]
+            t2[b, j] = nxt
+            nxt += 1
+    w.num_blocks += extra
+    w.block_tables = t2
+    private = _outputs(w, kp2, vp2)
+    np.testing.assert_array_equal(shared, private)
+
+
+@pytest.mark.parametrize("H,H_kv", [(4, 4), (16, 2)])
+def test_batch_composition_is_bitwise_invariant(H, H_kv):
+    w = W.scattered_workload("batch", "bf16", B=len(LENS_LONG), H=H, H_kv=H_kv, d=128,
+                             context_lens=LENS_LONG, seed=71)
+    kp, vp = poison(w, w.steps[0].context_lens.astype(np.int64))
+    full = _outputs(w, kp, vp)
+    again = _outputs(w, kp, vp)
+    np.testing.assert_array_equal(full, again)                 # repeatable
+    for b in (0, 5, 6):
+        one = W.Workload(**{**w.__dict__, "B": 1, "block_tables": w.block_tables[b:b + 1].copy(),
+                            "steps": [W.DecodeStep(w.steps[0].context_lens[b:b + 1],
+                                                   w.steps[0].q[b:b + 1], w.steps[0].new_k[b:b + 1],
+                                                   w.steps[0].new_v[b:b + 1])]})
+        alone = _outputs(one, kp, vp)
+        np.testing.assert_array_equal(alone[0], full[b])
+
+
+@pytest.mark.parametrize("H,H_kv", [(4, 4), (16, 2)])
+def test_single_token_context_returns_value_row_exactly(H, H_kv):
+    w = W.scattered_workload("one", "bf16", B=3, H=H, H_kv=H_kv, d=128, context_lens=[1, 1, 1],
+                             seed=81)
+    step = w.steps[0]
+    kp, vp = poison(w, np.zeros(3, np.int64))
+    dw = upload(w, kp, vp)
+    _, out = gpu_step(dw, step, 0)
+    got = from_dev(out, "bf16")
+    g = H // H_kv
+    for b in range(3):
+        for h in range(H):
+            np.testing.assert_array_equal(got[b, h], step.new_v[b, h // g])
+
+
+@pytest.mark.parametrize("H,H_kv", [(4, 4), (16, 2)])
+@pytest.mark.parametrize("P_", [0, 32])
+def test_split_matches_single_pass(H, H_kv, P_):
+    w = W.scattered_workload("split", "bf16", B=len(LENS_LONG), H=H, H_kv=H_kv, d=128,
+                             context_lens=LENS_LONG, seed=91)
+    kp, vp = poison(w, w.steps[0].context_lens.astype(np.int64))
+    a = O.bits_to_f64(_outputs(w, kp, vp, 0), "bf16")
+    b = O.bits_to_f64(_outputs(w, kp, vp, P_ or 16), "bf16")
+    assert np.linalg.norm(a - b) / np.linalg.norm(a) <= 5e-3
+    assert np.abs(a - b).max() <= 1e-2
+
+
+@pytest.mark.parametrize("H,H_kv", [(4, 4), (32, 8)])
+def test_value_outliers_keep_tolerance(H, H_kv):
+    """V with 20x amplitude on a few channels (fp32 accumulation must hold)."""
+    w = W.scattered_workload("outlier", "bf16", B=len(LENS_LONG), H=H, H_kv=H_kv, d=128,
+                             context_lens=LENS_LONG, seed=101)
+    v = O.bits_to_f64(w.v_pool, "bf16").reshape(w.num_blocks, w.H_kv, 128, 16)
+    v[:, :, [3, 77, 120], :] *= 20.0                       # channels are dims in V's [d][16] tile
+    w.v_pool = W.f32_to_bf16_bits(v.reshape(-1).astype(np.float32))
+    nv = O.bits_to_f64(w.steps[0].new_v, "bf16")
+    nv[..., [3, 77, 120]] *= 20.0
+    w.steps[0].new_v = W.f32_to_bf16_bits(nv.astype(np.float32))
+    # rel-L2 keeps its bound; max-abs scales with the 20x amplitude of the
+    # outlier channels, whose outputs reach tens where one bf16 ulp is ~0.1
+    single_step_case(w, 0, label="outliers", amplitude=20.0)
+    single_step_case(w, 32, label="outliers-split", amplitude=20.0)

@@ -1,6 +1,7 @@
 """The five seeded workloads and a generic recipe for smaller test shapes.
 
-Draw order inside one workload (one numpy PCG64 stream per seed):
+Draw order inside one workload (a numpy PCG64 stream per seed; the two pool
+fills come from their own keyed streams, see _pool_bits):
 context lengths -> physical block permutation -> q -> pool K -> pool V ->
 new k, v.  Nothing here knows how a token is laid out inside a cache block:
 the pools are returned as flat arrays of independent N(0,1) values, one per
@@ -9,6 +10,8 @@ element, so any layout reads the same distribution.
 from __future__ import annotations
 
 import math
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
 from typing import List, Optional, Sequence
 
@@ -43,25 +46,54 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     Inputs here are finite N(0,1) draws, so no NaN/Inf handling is needed.
     """
     u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
-    lsb = (u >> np.uint32(16)) & np.uint32(1)
-    r = (u + np.uint32(0x7FFF) + lsb) >> np.uint32(16)
+    r = u >> np.uint32(16)
+    r &= np.uint32(1)            # the bit that breaks ties towards even
+    r += np.uint32(0x7FFF)
+    r += u
+    r >>= np.uint32(16)
     return r.astype(np.uint16)
 
 
 def _normal_bits(rng: np.random.Generator, n: int, dtype: str,
                  chunk: int = 1 << 24) -> np.ndarray:
-    """n independent N(0,1) values as bit patterns, drawn in fixed-size chunks."""
+    """n independent N(0,1) values as bit patterns, drawn from `rng` in order."""
     out = np.empty(n, dtype=bits_dtype(dtype))
     buf = np.empty(min(chunk, max(n, 1)), dtype=np.float32)
     pos = 0
     while pos < n:
         m = min(chunk, n - pos)
         rng.standard_normal(out=buf[:m], dtype=np.float32)
-        if dtype == "bf16":
-            out[pos:pos + m] = f32_to_bf16_bits(buf[:m])
-        else:
-            out[pos:pos + m] = buf[:m].view(np.uint32)
+        out[pos:pos + m] = f32_to_bf16_bits(buf[:m]) if dtype == "bf16" else buf[:m].view(np.uint32)
         pos += m
+    return out
+
+
+POOL_CHUNK = 1 << 22  # elements per independently keyed stream of a pool fill
+
+
+def _pool_bits(seed: int, tag: int, n: int, dtype: str, threads: int = 0) -> np.ndarray:
+    """A pool's n N(0,1) values, drawn in fixed chunks of POOL_CHUNK elements.
+
+    Chunk i comes from its own PCG64 stream keyed by SeedSequence([seed, tag, i]),
+    so the values do not depend on how many threads fill them.
+    """
+    out = np.empty(n, dtype=bits_dtype(dtype))
+    nchunks = -(-n // POOL_CHUNK)
+
+    def fill(i: int) -> None:
+        lo = i * POOL_CHUNK
+        m = min(POOL_CHUNK, n - lo)
+        rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, tag, i])))
+        buf = rng.standard_normal(m, dtype=np.float32)
+        out[lo:lo + m] = f32_to_bf16_bits(buf) if dtype == "bf16" else buf.view(np.uint32)
+
+    threads = threads or min(16, os.cpu_count() or 1)
+    if nchunks <= 1 or threads <= 1:
+        for i in range(nchunks):
+            fill(i)
+    else:
+        with ThreadPoolExecutor(max_workers=threads) as ex:
+            list(ex.map(fill, range(nchunks)))
     return out
 
 
@@ -149,8 +181,8 @@ def scattered_workload(name: str, dtype: str, B: int, H: int, H_kv: int, d: int,
         pos += nb[b]
     q = _normal_bits(rng, B * H * d, dtype).reshape(B, H, d)
     n_pool = num_blocks * H_kv * BLOCK_SIZE * d
-    k_pool = _normal_bits(rng, n_pool, dtype)
-    v_pool = _normal_bits(rng, n_pool, dtype)
+    k_pool = _pool_bits(seed, 1, n_pool, dtype)
+    v_pool = _pool_bits(seed, 2, n_pool, dtype)
     new_k = _normal_bits(rng, B * H_kv * d, dtype).reshape(B, H_kv, d)
     new_v = _normal_bits(rng, B * H_kv * d, dtype).reshape(B, H_kv, d)
     step = DecodeStep(context_lens=ctx.astype(np.int32), q=q, new_k=new_k, new_v=new_v)
@@ -236,8 +268,8 @@ def shared_prefix_workload(seed: int, B: int = 128, H: int = 32, H_kv: int = 8,
     dtype = "bf16"
     n_pool = num_blocks * H_kv * BLOCK_SIZE * d
     qs = [_normal_bits(rng, B * H * d, dtype).reshape(B, H, d) for _ in range(steps)]
-    k_pool = _normal_bits(rng, n_pool, dtype)
-    v_pool = _normal_bits(rng, n_pool, dtype)
+    k_pool = _pool_bits(seed, 1, n_pool, dtype)
+    v_pool = _pool_bits(seed, 2, n_pool, dtype)
     step_list = []
     for s in range(steps):
         nk = _normal_bits(rng, B * H_kv * d, dtype).reshape(B, H_kv, d)
