@@ -7,7 +7,7 @@
 #include <new>
 #include <string>
 
-#include "../../include/pagedkv.h"
+#include "pagedkv.h"
 #include "launch.h"
 
 struct kv_pool {

@@ -26,7 +26,7 @@
 namespace pagedkv {
 namespace {
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
 constexpr int kHeadsPerTile = 16;
 
 typedef __bf16 bf16x8_t __attribute__((__vector_size__(8 * sizeof(__bf16))));
@@ -50,11 +50,11 @@ __device__ __forceinline__ void load_block(MfmaFrag<D>& f, const uint16_t* kt, c
                                            int lane) {
 #pragma unroll
   for (int i = 0; i < MfmaShape<D>::KI; ++i)
-    f.k[i] = *reinterpret_cast<const uint4*>(kt + (i * kWave + lane) * 8);
+    f.k[i] = load_tile16(kt + (i * kWave + lane) * 8);
   const int n = lane & 15, q = lane >> 4;
 #pragma unroll
   for (int mc = 0; mc < MfmaShape<D>::MC; ++mc)
-    f.v[mc] = *reinterpret_cast<const uint2*>(vt + (16 * mc + n) * kBlockTokens + 4 * q);
+    f.v[mc] = load_tile8(vt + (16 * mc + n) * kBlockTokens + 4 * q);
 }
 
 template <int D>
@@ -85,23 +85,18 @@ __device__ __forceinline__ void compute_block(const MfmaFrag<D>& f,
     sc[j] = s[j] * scale_log2;
     if (kTail && 4 * q + j >= nvalid) sc[j] = -INFINITY;  // select: the slot may hold NaN
   }
-  float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-  mx = wave_xor_max(mx, 16);
-  mx = wave_xor_max(mx, 32);
+  const float mx = cross_row_max(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
   const float m_new = fmaxf(st.m, mx);
   const float alpha = fast_exp2(st.m - m_new);
   st.m = m_new;
-  uint16_t pb[4];
-  float psum = 0.f;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    pb[j] = f32_to_bf16_rne(fast_exp2(sc[j] - m_new));
-    psum += bf16_to_f32(pb[j]);  // the denominator sums the same rounded weights
-  }
+  // weights rounded to bf16 for the matrix core; the denominator sums the
+  // same rounded values
+  const uint32_t p01 = pack_bf16x2(fast_exp2(sc[0] - m_new), fast_exp2(sc[1] - m_new));
+  const uint32_t p23 = pack_bf16x2(fast_exp2(sc[2] - m_new), fast_exp2(sc[3] - m_new));
+  const float psum = (__uint_as_float(p01 << 16) + __uint_as_float(p01 & 0xffff0000u)) +
+                     (__uint_as_float(p23 << 16) + __uint_as_float(p23 & 0xffff0000u));
   st.l = fmaf(st.l, alpha, psum);
-  short4_t pop;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) pop[j] = static_cast<short>(pb[j]);
+  const short4_t pop = __builtin_bit_cast(short4_t, make_uint2(p01, p23));
 #pragma unroll
   for (int mc = 0; mc < MfmaShape<D>::MC; ++mc) {
     uint2 v = f.v[mc];
@@ -200,8 +195,18 @@ __global__ __launch_bounds__(kWaves * kWave) void decode_mfma_kernel(DecodeArgs 
   st.l = 0.f;
   int bad_blk = 0;
 
-  auto fetch = [&](int j, MfmaFrag<D>& f) -> bool {
-    const int p = __builtin_amdgcn_readfirstlane(table[j]);
+  // The wave's blocks are j = jb + w + 4n; their table entries are read 64 at
+  // a time into one register (lane i holds entry n0 + i).
+  int win = -1;
+  auto table_entry = [&](int nn) -> int {
+    if ((nn & 63) == 0) {
+      const int jj = jb + w + kWaves * (nn + lane);
+      win = jj < je ? table[jj] : -1;
+    }
+    return __builtin_amdgcn_readlane(win, nn & 63);
+  };
+  auto fetch = [&](int nn, MfmaFrag<D>& f) -> bool {
+    const int p = table_entry(nn);
     if (p < 0 || p >= a.num_blocks) return false;
     const int64_t tile = (int64_t(p) * a.num_kv_heads + kvh) * tile_elems;
     load_block<D>(f, kc + tile, vc + tile, lane);
@@ -216,24 +221,19 @@ __global__ __launch_bounds__(kWaves * kWave) void decode_mfma_kernel(DecodeArgs 
       compute_block<D, true>(f, qop, st, nvalid, a.scale_log2, lane);
   };
 
+  const int nblk = je - jb - w > 0 ? (je - jb - w + kWaves - 1) / kWaves : 0;
   MfmaFrag<D> fa, fb;
-  int j = jb + w;
   bool ok_a = false, ok_b = false;
-  if (j < je) ok_a = fetch(j, fa);
-  while (j < je) {
-    const int j1 = j + kWaves;
-    if (j1 < je) ok_b = fetch(j1, fb);
-    consume(j, ok_a, fa);
-    if (j1 >= je) break;
-    const int j2 = j1 + kWaves;
-    if (j2 < je) ok_a = fetch(j2, fa);
-    consume(j1, ok_b, fb);
-    j = j2;
+  if (nblk > 0) ok_a = fetch(0, fa);
+  for (int nn = 0; nn < nblk; nn += 2) {
+    if (nn + 1 < nblk) ok_b = fetch(nn + 1, fb);
+    consume(jb + w + kWaves * nn, ok_a, fa);
+    if (nn + 1 >= nblk) break;
+    if (nn + 2 < nblk) ok_a = fetch(nn + 2, fa);
+    consume(jb + w + kWaves * (nn + 1), ok_b, fb);
   }
 
-  float lsum = st.l;
-  lsum = wave_xor_add(lsum, 16);
-  lsum = wave_xor_add(lsum, 32);
+  const float lsum = cross_row_sum(st.l);
   if (q == 0) {
     sm_m[w][n] = st.m;
     sm_l[w][n] = lsum;

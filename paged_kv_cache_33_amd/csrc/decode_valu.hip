@@ -7,9 +7,9 @@
 // registers; a running max and denominator are rescaled whenever the max
 // rises (online softmax); everything accumulates in fp32.
 //
-// Work decomposition: a work-group of 4 wavefronts takes one (partition, query
-// head, sequence); wave w walks the partition's blocks w, w+4, w+8, ...
-// keeping its own (m, l, O), and the four are merged through LDS at the end.
+// Work decomposition: a work-group of 8 wavefronts takes one (partition, query
+// head, sequence); wave w walks the partition's blocks w, w+8, w+16, ...
+// keeping its own (m, l, O), and the eight are merged through LDS at the end.
 // The next block's K and V are loaded while the current one is computed.
 //
 // Lane mapping for one 16-token block (see the pool layout in pagedkv.h):
@@ -26,7 +26,7 @@
 namespace pagedkv {
 namespace {
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
 
 template <typename Tr, int D>
 struct ValuShape {
@@ -50,13 +50,13 @@ __device__ __forceinline__ void load_block(BlockFrag<Tr, D>& f, const typename T
   using Sh = ValuShape<Tr, D>;
 #pragma unroll
   for (int i = 0; i < Sh::KL; ++i)
-    f.k[i] = *reinterpret_cast<const uint4*>(kt + (i * kWave + lane) * Sh::X);
+    f.k[i] = load_tile16(kt + (i * kWave + lane) * Sh::X);
 #pragma unroll
   for (int xk = 0; xk < Sh::XK; ++xk)
 #pragma unroll
     for (int th = 0; th < Sh::R; ++th)
       f.v[xk * Sh::R + th] =
-          *reinterpret_cast<const uint4*>(vt + ((xk * kWave + lane) * kBlockTokens + th * Sh::X));
+          load_tile16(vt + ((xk * kWave + lane) * kBlockTokens + th * Sh::X));
 }
 
 struct WaveState {
@@ -64,53 +64,99 @@ struct WaveState {
   float l;    // this lane's share of the denominator (token lane%16)
 };
 
+// The query slice a lane contracts with: chunks 4i + lane/16 of the head row.
+// bf16 keeps the stored pairs (the dot2 instruction takes them as they are);
+// fp32 keeps floats.
+template <typename Tr, int D>
+struct QueryFrag {
+  uint4 c[ValuShape<Tr, D>::KL];
+};
+
+// Zero the bf16 V values of tokens >= nvalid inside one 16-byte piece holding
+// tokens first..first+7 of one dim (the same tokens in every lane).
+__device__ __forceinline__ uint4 mask_tail_tokens(uint4 v, int first, int nvalid) {
+  uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int t0 = first + 2 * c;
+    w[c] = t0 + 1 < nvalid ? w[c] : (t0 < nvalid ? (w[c] & 0x0000ffffu) : 0u);
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
 // One block of 16 tokens; `nvalid` (uniform) tokens of it are inside the range.
 template <typename Tr, int D, bool kTail>
-__device__ __forceinline__ void compute_block(const BlockFrag<Tr, D>& f,
-                                              const float (&qf)[ValuShape<Tr, D>::KL][Tr::kChunk],
+__device__ __forceinline__ void compute_block(const BlockFrag<Tr, D>& f, const QueryFrag<Tr, D>& qf,
                                               float (&o)[ValuShape<Tr, D>::XK], WaveState& st,
                                               int nvalid, float scale_log2, int lane) {
   using Sh = ValuShape<Tr, D>;
-  constexpr int X = Sh::X;
+  constexpr bool kBf16 = Tr::kChunk == 8;
+  // ---- scores: this lane's chunks of token lane%16, then the 4 rows combined
   float dot = 0.f;
 #pragma unroll
   for (int i = 0; i < Sh::KL; ++i) {
-    float kf[X];
-    unpack_chunk(f.k[i], kf, Tr{});
-#pragma unroll
-    for (int e = 0; e < X; ++e) dot = fmaf(qf[i][e], kf[e], dot);
+    if constexpr (kBf16) {
+      dot = dot2_bf16(f.k[i].x, qf.c[i].x, dot);
+      dot = dot2_bf16(f.k[i].y, qf.c[i].y, dot);
+      dot = dot2_bf16(f.k[i].z, qf.c[i].z, dot);
+      dot = dot2_bf16(f.k[i].w, qf.c[i].w, dot);
+    } else {
+      dot = fmaf(__uint_as_float(f.k[i].x), __uint_as_float(qf.c[i].x), dot);
+      dot = fmaf(__uint_as_float(f.k[i].y), __uint_as_float(qf.c[i].y), dot);
+      dot = fmaf(__uint_as_float(f.k[i].z), __uint_as_float(qf.c[i].z), dot);
+      dot = fmaf(__uint_as_float(f.k[i].w), __uint_as_float(qf.c[i].w), dot);
+    }
   }
-  dot = wave_xor_add(dot, 16);
-  dot = wave_xor_add(dot, 32);
+  dot = cross_row_sum(dot);
   const int t = lane & 15;
   float s = dot * scale_log2;
   if (kTail && t >= nvalid) s = -INFINITY;  // select, never multiply: slot may hold NaN
-  float mb = s;
-  mb = wave_xor_max(mb, 1);
-  mb = wave_xor_max(mb, 2);
-  mb = wave_xor_max(mb, 4);
-  mb = wave_xor_max(mb, 8);
-  const float m_new = fmaxf(st.m, mb);
+  // ---- online softmax over the block's 16 tokens (one per lane of a row)
+  const float m_new = fmaxf(st.m, row16_max(s));
   const float alpha = fast_exp2(st.m - m_new);
   const float p = fast_exp2(s - m_new);
-  st.l = fmaf(st.l, alpha, p);
   st.m = m_new;
 #pragma unroll
   for (int xk = 0; xk < Sh::XK; ++xk) o[xk] *= alpha;
-  float ps[kBlockTokens];
+  if constexpr (kBf16) {
+    // weights rounded to bf16 pairs (tokens 2k, 2k+1); the denominator sums
+    // the same rounded values
+    const uint32_t packed = pack_bf16x2(p, dpp_mov<kDppQuadXor1>(p));
+    st.l = fmaf(st.l, alpha, __uint_as_float(packed << 16));
+    uint32_t pp[kBlockTokens / 2];
 #pragma unroll
-  for (int tt = 0; tt < kBlockTokens; ++tt)
-    ps[tt] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(p), tt));
+    for (int k = 0; k < kBlockTokens / 2; ++k)
+      pp[k] = __builtin_amdgcn_readlane(packed, 2 * k);
 #pragma unroll
-  for (int xk = 0; xk < Sh::XK; ++xk) {
+    for (int xk = 0; xk < Sh::XK; ++xk) {
 #pragma unroll
-    for (int th = 0; th < Sh::R; ++th) {
-      float vf[X];
-      unpack_chunk(f.v[xk * Sh::R + th], vf, Tr{});
+      for (int th = 0; th < Sh::R; ++th) {
+        uint4 v = f.v[xk * Sh::R + th];
+        if (kTail) v = mask_tail_tokens(v, th * 8, nvalid);
+        o[xk] = dot2_bf16(v.x, pp[th * 4 + 0], o[xk]);
+        o[xk] = dot2_bf16(v.y, pp[th * 4 + 1], o[xk]);
+        o[xk] = dot2_bf16(v.z, pp[th * 4 + 2], o[xk]);
+        o[xk] = dot2_bf16(v.w, pp[th * 4 + 3], o[xk]);
+      }
+    }
+  } else {
+    st.l = fmaf(st.l, alpha, p);
+    float ps[kBlockTokens];
 #pragma unroll
-      for (int e = 0; e < X; ++e) {
-        const int tt = th * X + e;
-        if (!kTail || tt < nvalid) o[xk] = fmaf(ps[tt], vf[e], o[xk]);
+    for (int tt = 0; tt < kBlockTokens; ++tt)
+      ps[tt] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(p), tt));
+#pragma unroll
+    for (int xk = 0; xk < Sh::XK; ++xk) {
+#pragma unroll
+      for (int th = 0; th < Sh::R; ++th) {
+        const uint4 v = f.v[xk * Sh::R + th];
+        const float vf[4] = {__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z),
+                             __uint_as_float(v.w)};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int tt = th * 4 + e;
+          if (!kTail || tt < nvalid) o[xk] = fmaf(ps[tt], vf[e], o[xk]);
+        }
       }
     }
   }
@@ -164,15 +210,13 @@ __global__ __launch_bounds__(kWaves * kWave) void decode_valu_kernel(DecodeArgs 
   const int jb = tb / kBlockTokens;
   const int je = (te + kBlockTokens - 1) / kBlockTokens;
 
-  // This lane's slice of the query: chunks 4i + lane/16, as fp32.
-  float qf[Sh::KL][X];
+  // This lane's slice of the query: chunks 4i + lane/16.
+  QueryFrag<Tr, D> qf;
   {
     const S* qrow = static_cast<const S*>(a.query) + row;
 #pragma unroll
-    for (int i = 0; i < Sh::KL; ++i) {
-      const uint4 raw = *reinterpret_cast<const uint4*>(qrow + (4 * i + lane / 16) * X);
-      unpack_chunk(raw, qf[i], Tr{});
-    }
+    for (int i = 0; i < Sh::KL; ++i)
+      qf.c[i] = *reinterpret_cast<const uint4*>(qrow + (4 * i + lane / 16) * X);
   }
 
   const S* kc = static_cast<const S*>(a.k_cache);
@@ -186,9 +230,20 @@ __global__ __launch_bounds__(kWaves * kWave) void decode_valu_kernel(DecodeArgs 
   for (int xk = 0; xk < Sh::XK; ++xk) o[xk] = 0.f;
   int bad_blk = 0;
 
+  // The wave's blocks are j = jb + w + 4n, n = 0, 1, ...  Their table entries
+  // are read 64 at a time into one register (lane i holds entry n0 + i) so
+  // that a tile's address never waits on a dependent load.
+  int win = -1;
+  auto table_entry = [&](int n) -> int {
+    if ((n & 63) == 0) {
+      const int jj = jb + w + kWaves * (n + lane);
+      win = jj < je ? table[jj] : -1;
+    }
+    return __builtin_amdgcn_readlane(win, n & 63);
+  };
   // Returns false (and loads nothing) for a table entry outside the pool.
-  auto fetch = [&](int j, BlockFrag<Tr, D>& f) -> bool {
-    const int p = __builtin_amdgcn_readfirstlane(table[j]);
+  auto fetch = [&](int n, BlockFrag<Tr, D>& f) -> bool {
+    const int p = table_entry(n);
     if (p < 0 || p >= a.num_blocks) return false;
     const int64_t tile = (int64_t(p) * a.num_kv_heads + kvh) * tile_elems;
     load_block<Tr, D>(f, kc + tile, vc + tile, lane);
@@ -203,28 +258,21 @@ __global__ __launch_bounds__(kWaves * kWave) void decode_valu_kernel(DecodeArgs 
       compute_block<Tr, D, true>(f, qf, o, st, nvalid, a.scale_log2, lane);
   };
 
-  // Ping-pong over two register buffers: block j+4 is in flight while j computes.
+  // Ping-pong over two register buffers: block n+1 is in flight while n computes.
+  const int nblk = je - jb - w > 0 ? (je - jb - w + kWaves - 1) / kWaves : 0;
   BlockFrag<Tr, D> fa, fb;
-  int j = jb + w;
   bool ok_a = false, ok_b = false;
-  if (j < je) ok_a = fetch(j, fa);
-  while (j < je) {
-    const int j1 = j + kWaves;
-    if (j1 < je) ok_b = fetch(j1, fb);
-    consume(j, ok_a, fa);
-    if (j1 >= je) break;
-    const int j2 = j1 + kWaves;
-    if (j2 < je) ok_a = fetch(j2, fa);
-    consume(j1, ok_b, fb);
-    j = j2;
+  if (nblk > 0) ok_a = fetch(0, fa);
+  for (int n = 0; n < nblk; n += 2) {
+    if (n + 1 < nblk) ok_b = fetch(n + 1, fb);
+    consume(jb + w + kWaves * n, ok_a, fa);
+    if (n + 1 >= nblk) break;
+    if (n + 2 < nblk) ok_a = fetch(n + 2, fa);
+    consume(jb + w + kWaves * (n + 1), ok_b, fb);
   }
 
   // Wave totals: the denominator is spread over the 16 token lanes of a row.
-  float lsum = st.l;
-  lsum = wave_xor_add(lsum, 1);
-  lsum = wave_xor_add(lsum, 2);
-  lsum = wave_xor_add(lsum, 4);
-  lsum = wave_xor_add(lsum, 8);
+  const float lsum = row16_sum(st.l);
   if (lane == 0) {
     sm_m[w] = st.m;
     sm_l[w] = lsum;

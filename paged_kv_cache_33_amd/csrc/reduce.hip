@@ -7,25 +7,52 @@
 // applied to whole partitions:
 //   w_k = l_k * 2^(m_k - M),   out = sum_k w_k o_k / sum_k w_k.
 // One work-group per (query head, sequence); the weights are computed once into
-// LDS, then each thread owns one or more output dims.
+// LDS, then the threads split the partitions and each output dim.
 #include "device_common.h"
 #include "launch.h"
 
 namespace pagedkv {
 namespace {
 
-constexpr int kReduceThreads = 128;
+constexpr int kReduceThreads = 256;
 
-template <typename Tr>
+// Block-wide max / sum of one value per thread (256 threads = 4 waves).
+__device__ __forceinline__ float block_max(float v, float* scratch) {
+  v = cross_row_max(row16_max(v));
+  const int w = threadIdx.x / kWave;
+  __syncthreads();
+  if (threadIdx.x % kWave == 0) scratch[w] = v;
+  __syncthreads();
+  float r = scratch[0];
+#pragma unroll
+  for (int i = 1; i < kReduceThreads / kWave; ++i) r = fmaxf(r, scratch[i]);
+  return r;
+}
+__device__ __forceinline__ float block_sum(float v, float* scratch) {
+  v = cross_row_sum(row16_sum(v));
+  const int w = threadIdx.x / kWave;
+  __syncthreads();
+  if (threadIdx.x % kWave == 0) scratch[w] = v;
+  __syncthreads();
+  float r = 0.f;
+#pragma unroll
+  for (int i = 0; i < kReduceThreads / kWave; ++i) r += scratch[i];
+  return r;
+}
+
+// Thread t owns output dim t % D and partitions k = t / D, t / D + G, ... with
+// G = 256 / D groups; four independent accumulators keep four partial rows in
+// flight, and the G group sums meet in LDS.
+template <typename Tr, int D>
 __global__ __launch_bounds__(kReduceThreads) void lse_reduce_kernel(ReduceArgs a) {
+  constexpr int G = kReduceThreads / D;
   extern __shared__ float sm_w[];  // [num_partitions] weights
   __shared__ float sm_red[kReduceThreads / kWave];
-  __shared__ float sm_total;
+  __shared__ float sm_part[G][D];
   using S = typename Tr::storage;
 
   const int h = blockIdx.x;
   const int b = blockIdx.y;
-  const int D = a.head_dim;
   const int ctx = a.context_lens[b];
   const int nparts = ctx > 0 ? (ctx + a.partition_size - 1) / a.partition_size : 0;
   S* out = static_cast<S*>(a.out) + (size_t(b) * a.H + h) * D;
@@ -40,40 +67,36 @@ __global__ __launch_bounds__(kReduceThreads) void lse_reduce_kernel(ReduceArgs a
   const float* m = a.ws_m + base;
   const float* l = a.ws_l + base;
   const float* o = a.ws_o + base * D;
-  const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
 
-  // M = max_k m_k
   float mx = -INFINITY;
-  for (int k = threadIdx.x; k < nparts; k += blockDim.x) mx = fmaxf(mx, m[k]);
-  for (int off = 32; off >= 1; off >>= 1) mx = wave_xor_max(mx, off);
-  if (lane == 0) sm_red[w] = mx;
-  __syncthreads();
-  float M = -INFINITY;
-  for (int i = 0; i < kReduceThreads / kWave; ++i) M = fmaxf(M, sm_red[i]);
-  __syncthreads();
+  for (int k = threadIdx.x; k < nparts; k += kReduceThreads) mx = fmaxf(mx, m[k]);
+  const float M = block_max(mx, sm_red);
 
-  // w_k and their sum
   float tot = 0.f;
-  for (int k = threadIdx.x; k < nparts; k += blockDim.x) {
+  for (int k = threadIdx.x; k < nparts; k += kReduceThreads) {
     const float wk = l[k] * fast_exp2(m[k] - M);
     sm_w[k] = wk;
     tot += wk;
   }
-  for (int off = 32; off >= 1; off >>= 1) tot = wave_xor_add(tot, off);
-  if (lane == 0) sm_red[w] = tot;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    float t = 0.f;
-    for (int i = 0; i < kReduceThreads / kWave; ++i) t += sm_red[i];
-    sm_total = t;
-  }
-  __syncthreads();
-  const float inv = 1.f / sm_total;
+  const float total = block_sum(tot, sm_red);  // its barriers also publish sm_w
 
-  for (int x = threadIdx.x; x < D; x += blockDim.x) {
-    float acc = 0.f;
-    for (int k = 0; k < nparts; ++k) acc = fmaf(sm_w[k], o[size_t(k) * D + x], acc);
-    out[x] = Tr::from_f32(acc * inv);
+  const int x = threadIdx.x % D;
+  const int kg = threadIdx.x / D;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  int k = kg;
+  for (; k + 3 * G < nparts; k += 4 * G) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      acc[u] = fmaf(sm_w[k + u * G], o[size_t(k + u * G) * D + x], acc[u]);
+  }
+  for (; k < nparts; k += G) acc[0] = fmaf(sm_w[k], o[size_t(k) * D + x], acc[0]);
+  sm_part[kg][x] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+  __syncthreads();
+  if (kg == 0) {
+    float r = 0.f;
+#pragma unroll
+    for (int g = 0; g < G; ++g) r += sm_part[g][x];
+    out[x] = Tr::from_f32(r / total);
   }
 }
 
@@ -82,11 +105,18 @@ __global__ __launch_bounds__(kReduceThreads) void lse_reduce_kernel(ReduceArgs a
 hipError_t launch_reduce(const ReduceArgs& a, bool bf16_out, hipStream_t s) {
   if (a.B == 0 || a.H == 0) return hipSuccess;
   const dim3 grid(a.H, a.B);
+  const dim3 block(kReduceThreads);
   const size_t shmem = size_t(a.num_partitions) * sizeof(float);
-  if (bf16_out)
-    hipLaunchKernelGGL(lse_reduce_kernel<Bf16>, grid, dim3(kReduceThreads), shmem, s, a);
+  if (bf16_out && a.head_dim == 128)
+    hipLaunchKernelGGL((lse_reduce_kernel<Bf16, 128>), grid, block, shmem, s, a);
+  else if (bf16_out && a.head_dim == 64)
+    hipLaunchKernelGGL((lse_reduce_kernel<Bf16, 64>), grid, block, shmem, s, a);
+  else if (!bf16_out && a.head_dim == 128)
+    hipLaunchKernelGGL((lse_reduce_kernel<F32, 128>), grid, block, shmem, s, a);
+  else if (!bf16_out && a.head_dim == 64)
+    hipLaunchKernelGGL((lse_reduce_kernel<F32, 64>), grid, block, shmem, s, a);
   else
-    hipLaunchKernelGGL(lse_reduce_kernel<F32>, grid, dim3(kReduceThreads), shmem, s, a);
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
