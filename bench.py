@@ -50,6 +50,9 @@ def parse_args(argv=None):
                     help="only run a plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--decode-only", action="store_true",
                     help="launch only the decode kernel repeatedly (for counter runs)")
+    ap.add_argument("--unfused", action="store_true",
+                    help="run the step as three calls (slot map, cache write, decode) instead "
+                         "of kv_cache_append + decode")
     return ap.parse_args(argv)
 
 
@@ -149,8 +152,11 @@ def main(argv=None) -> int:
 
     def run_step(i, ev=None):
         s = steps_dev[i % len(steps_dev)]
-        P.kv_slot_mapping(tables, s["ctx"], s["slots"], stream)
-        P.reshape_and_cache(pool, s["k"], s["v"], s["slots"], stream)
+        if args.unfused:
+            P.kv_slot_mapping(tables, s["ctx"], s["slots"], stream)
+            P.reshape_and_cache(pool, s["k"], s["v"], s["slots"], stream)
+        else:
+            P.kv_cache_append(pool, s["k"], s["v"], tables, s["ctx"], s["slots"], stream)
         if ev is not None:
             ev[0].record(stream)
         P.paged_attention_decode(pool, out, s["q"], tables, s["ctx"], L_max, w.scale, part, ws,
@@ -225,6 +231,8 @@ def main(argv=None) -> int:
             "max_context_tokens": L_max,
             "partition_size": part,
             "seed": w.seed,
+            "step": ("kv_slot_mapping + reshape_and_cache" if args.unfused else "kv_cache_append")
+                    + " + paged_attention_decode" + (" + paged_attention_reduce" if part else ""),
         },
         "decode_steps_per_sec": round(1000.0 / ms_step, 1),
         "pct_of_peak": round(100.0 * gbs / PEAK_HBM_GBS, 2),

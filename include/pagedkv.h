@@ -119,6 +119,22 @@ kv_status kv_slot_mapping(const int32_t* block_tables, int32_t max_nb,
 kv_status reshape_and_cache(const kv_pool* pool, const void* key, const void* value,
                             const int64_t* slot_mapping, int32_t N, void* stream);
 
+/* Append one new token per sequence: the slot mapping and the cache write in
+ * one launch.  For b < B with n = context_lens[b], the new token sits at
+ * position n - 1 (context_lens count it, as the workbook's decoder appends the
+ * row before attending); its K and V rows (key/value: device [B][H_kv][d],
+ * pool dtype) are copied bit for bit into block block_tables[b*max_nb +
+ * (n-1)/16], in-block slot (n-1) % 16.  The same result as kv_slot_mapping
+ * followed by reshape_and_cache.  slot_mapping: optional device int64 [B]
+ * (NULL = not wanted) receiving each slot, or -1 where nothing was written:
+ * n <= 0, n > max_nb*16, or a table entry outside the pool.  The block must not
+ * be shared with another sequence of the same call (the host block manager
+ * copies a shared last block before appending). */
+kv_status kv_cache_append(const kv_pool* pool, const void* key, const void* value,
+                          const int32_t* block_tables, int32_t max_nb,
+                          const int32_t* context_lens, int32_t B, int64_t* slot_mapping,
+                          void* stream);
+
 /* Workspace bytes paged_attention_decode needs in split mode: with
  * P = ceil(max_context_len / partition_size) partitions per sequence,
  *   o: float [B][H][P][d], then m: float [B][H][P], then l: float [B][H][P]

@@ -25,6 +25,7 @@ __all__ = [
     "kv_pool_create",
     "kv_slot_mapping",
     "reshape_and_cache",
+    "kv_cache_append",
     "paged_attention_workspace_bytes",
     "paged_attention_decode",
     "paged_attention_reduce",
@@ -167,6 +168,25 @@ def reshape_and_cache(pool: KVPool, key: torch.Tensor, value: torch.Tensor,
     vp = _buf(value, "value", N * row, elem_size=pool.elem_size)
     sp = _buf(slot_mapping, "slot_mapping", 8 * N, dtype=torch.int64)
     _lib.check(_lib.load().reshape_and_cache(pool.handle, kp, vp, sp, N, _stream_handle(stream)))
+
+
+def kv_cache_append(pool: KVPool, key: torch.Tensor, value: torch.Tensor,
+                    block_tables: torch.Tensor, context_lens: torch.Tensor,
+                    slot_mapping: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Append one token per sequence (rows [B, H_kv, d]) at position ctx - 1:
+    slot mapping and cache write in one launch; see pagedkv.h."""
+    if block_tables.dim() != 2:
+        raise ValueError("block_tables must be [B, max_nb]")
+    B, max_nb = block_tables.shape
+    row = B * pool.num_kv_heads * pool.head_dim * pool.elem_size
+    kp = _buf(key, "key", row, elem_size=pool.elem_size)
+    vp = _buf(value, "value", row, elem_size=pool.elem_size)
+    tp = _buf(block_tables, "block_tables", dtype=torch.int32)
+    cp = _buf(context_lens, "context_lens", 4 * B, dtype=torch.int32)
+    sp = None if slot_mapping is None else _buf(slot_mapping, "slot_mapping", 8 * B,
+                                                dtype=torch.int64)
+    _lib.check(_lib.load().kv_cache_append(pool.handle, kp, vp, tp, max_nb, cp, B, sp,
+                                           _stream_handle(stream)))
 
 
 def paged_attention_workspace_bytes(B: int, H: int, head_dim: int, max_context_len: int,

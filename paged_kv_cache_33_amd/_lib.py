@@ -32,6 +32,7 @@ EXPORTED = (
     "kv_pool_destroy",
     "kv_slot_mapping",
     "reshape_and_cache",
+    "kv_cache_append",
     "paged_attention_workspace_bytes",
     "paged_attention_decode",
     "paged_attention_reduce",
@@ -80,6 +81,7 @@ def load() -> C.CDLL:
         "paged_attention_workspace_bytes": (sz, [i32, i32, i32, i32, i32]),
         "paged_attention_decode": (C.c_int, [vp, vp, vp, i32p, i32, i32p, i32, i32, i32,
                                              C.c_float, i32, vp, sz, vp]),
+        "kv_cache_append": (C.c_int, [vp, vp, vp, i32p, i32, i32p, i32, vp, vp]),
         "paged_attention_reduce": (C.c_int, [vp, vp, i32p, i32, i32, i32, i32, i32, C.c_int, vp]),
         "kv_decode_kernel_kind": (C.c_int32, [vp, i32]),
         "kv_last_error": (C.c_char_p, []),

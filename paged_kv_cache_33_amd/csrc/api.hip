@@ -4,8 +4,10 @@
 
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <new>
 #include <string>
+#include <unordered_map>
 
 #include "pagedkv.h"
 #include "launch.h"
@@ -15,6 +17,36 @@ struct kv_pool {
   void* k_cache;
   void* v_cache;
 };
+
+namespace pagedkv {
+
+int resident_workers(const void* kernel, int threads, int tiles) {
+  static std::mutex mu;
+  static std::unordered_map<const void*, int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  int total = 0;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = cache[dev].find(kernel);
+    if (it != cache[dev].end()) {
+      total = it->second;
+    } else {
+      int cus = 0, per_cu = 0;
+      if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        cus = 256;
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess ||
+          per_cu < 1)
+        per_cu = 1;
+      total = cus * per_cu;
+      cache[dev][kernel] = total;
+    }
+  }
+  const int per_tile = total / (tiles > 0 ? tiles : 1);
+  return per_tile > 0 ? per_tile : 1;
+}
+
+}  // namespace pagedkv
 
 namespace {
 
@@ -168,11 +200,15 @@ int32_t kv_decode_kernel_kind(const kv_pool* pool, int32_t H) {
   return (pool->desc.dtype == KV_BF16 && H > pool->desc.num_kv_heads) ? 1 : 0;
 }
 
-kv_status paged_attention_decode(const kv_pool* pool, void* out, const void* query,
-                                 const int32_t* block_tables, int32_t max_nb,
-                                 const int32_t* context_lens, int32_t B, int32_t H,
-                                 int32_t max_context_len, float scale, int32_t partition_size,
-                                 void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+kv_status decode_impl(const kv_pool* pool, void* out, const void* query,
+                      const int32_t* block_tables, int32_t max_nb, const int32_t* context_lens,
+                      int32_t B, int32_t H, int32_t max_context_len, float scale,
+                      int32_t partition_size, void* workspace, size_t workspace_bytes,
+                      void* stream) {
   if (!pool) return fail(KV_ERR_INVALID_ARG, "pool is NULL");
   const kv_pool_desc& d = pool->desc;
   if (B < 0) return fail(KV_ERR_INVALID_ARG, "B must be >= 0");
@@ -183,6 +219,9 @@ kv_status paged_attention_decode(const kv_pool* pool, void* out, const void* que
   if (kv_status s = check_partition(max_context_len, partition_size); s != KV_OK) return s;
   if (!(scale == scale)) return fail(KV_ERR_INVALID_ARG, "scale is NaN");
   if (B == 0) return ok();
+  if (partition_size > 0 && B > pagedkv::kMaxSplitSeqs)
+    return fail(KV_ERR_UNSUPPORTED, "split mode holds at most %d sequences per call (got %d)",
+                pagedkv::kMaxSplitSeqs, B);
   if (!out || !query || !block_tables || !context_lens)
     return fail(KV_ERR_INVALID_ARG, "out, query, block_tables and context_lens must be non-NULL");
   if (!aligned16(query) || !aligned16(out))
@@ -224,6 +263,38 @@ kv_status paged_attention_decode(const kv_pool* pool, void* out, const void* que
   else
     e = pagedkv::launch_decode_valu(a, bf16, d.head_dim, s);
   return hip_status(e, "decode launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+kv_status paged_attention_decode(const kv_pool* pool, void* out, const void* query,
+                                 const int32_t* block_tables, int32_t max_nb,
+                                 const int32_t* context_lens, int32_t B, int32_t H,
+                                 int32_t max_context_len, float scale, int32_t partition_size,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl(pool, out, query, block_tables, max_nb, context_lens, B, H, max_context_len,
+                     scale, partition_size, workspace, workspace_bytes, stream);
+}
+
+kv_status kv_cache_append(const kv_pool* pool, const void* key, const void* value,
+                          const int32_t* block_tables, int32_t max_nb,
+                          const int32_t* context_lens, int32_t B, int64_t* slot_mapping,
+                          void* stream) {
+  if (!pool) return fail(KV_ERR_INVALID_ARG, "pool is NULL");
+  if (B < 0) return fail(KV_ERR_INVALID_ARG, "B must be >= 0");
+  if (max_nb < 1) return fail(KV_ERR_INVALID_ARG, "max_nb must be >= 1");
+  if (B == 0) return ok();
+  if (!key || !value || !block_tables || !context_lens)
+    return fail(KV_ERR_INVALID_ARG, "key, value, block_tables and context_lens must be non-NULL");
+  if (!aligned16(key) || !aligned16(value))
+    return fail(KV_ERR_INVALID_ARG, "key and value must be 16-byte aligned");
+  const kv_pool_desc& d = pool->desc;
+  pagedkv::AppendArgs a{pool->k_cache, pool->v_cache, d.num_blocks, d.num_kv_heads, d.head_dim,
+                        key, value, block_tables, max_nb, context_lens, B, slot_mapping};
+  return hip_status(pagedkv::launch_append(a, d.dtype == KV_BF16, static_cast<hipStream_t>(stream)),
+                    "append launch");
 }
 
 kv_status paged_attention_reduce(void* out, const void* workspace, const int32_t* context_lens,

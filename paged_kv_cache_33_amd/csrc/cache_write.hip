@@ -1,10 +1,16 @@
-// Slot mapping and the cache write (reshape_and_cache).
+// Slot mapping and the cache write (reshape_and_cache, kv_cache_append).
 //
 // The block-table mapping is the one "MLSys Engineer - Inference Systems Q&A",
 // Q1 gives: logical position i lives in block table[i / 16] at slot i % 16.  The
 // write is the append step of the "LLM inference and serving" workbook's
 // incremental decoder (K and V grow by one row per token), done for a whole
 // batch in one launch.
+//
+// Stores are non-temporal.  A decode step writes a few bytes into many cache
+// lines (one token of each K chunk row and of each V dim row); left dirty in the
+// caches, those lines would be evicted one by one in the middle of the next
+// decode's read stream and cost it far more than their size.  Streamed out
+// here, they are gone before the decode starts.
 #include "device_common.h"
 #include "launch.h"
 
@@ -22,6 +28,28 @@ __global__ __launch_bounds__(256) void slot_mapping_kernel(SlotMappingArgs a) {
     if (blk >= 0) slot = int64_t(blk) * kBlockTokens + pos % kBlockTokens;
   }
   a.slot_mapping[b] = slot;
+}
+
+// Write chunk c (X elements) of one token's K and V rows into in-block slot t of
+// tile `tile`: one 16-byte store for K ([d/X][16][X] tile), X element stores
+// for V ([d][16] tile).  Pure bit moves: no value is converted.
+template <typename Tr>
+__device__ __forceinline__ void write_token_chunk(void* k_cache, void* v_cache, int64_t tile, int C,
+                                                  int head_dim, int c, int t,
+                                                  const typename Tr::storage* ksrc,
+                                                  const typename Tr::storage* vsrc) {
+  using S = typename Tr::storage;
+  constexpr int X = Tr::kChunk;
+  const uint4 kc = *reinterpret_cast<const uint4*>(ksrc);
+  const uint4 vc = *reinterpret_cast<const uint4*>(vsrc);
+  S* kdst = static_cast<S*>(k_cache) + ((tile * C + c) * kBlockTokens + t) * X;
+  const u32x4_t ku = {kc.x, kc.y, kc.z, kc.w};
+  __builtin_nontemporal_store(ku, reinterpret_cast<u32x4_t*>(kdst));
+  S ve[X];
+  __builtin_memcpy(ve, &vc, sizeof(vc));
+  S* vdst = static_cast<S*>(v_cache) + (tile * head_dim + int64_t(c) * X) * kBlockTokens + t;
+#pragma unroll
+  for (int e = 0; e < X; ++e) __builtin_nontemporal_store(ve[e], vdst + e * kBlockTokens);
 }
 
 // One thread per (token, kv head, 16-byte chunk of the head's row).  K chunks
@@ -45,16 +73,38 @@ __global__ __launch_bounds__(256) void cache_write_kernel(CacheWriteArgs a) {
   const int64_t src = (i * a.num_kv_heads + h) * a.head_dim + int64_t(c) * X;
   const int64_t tile = p * a.num_kv_heads + h;
 
-  const uint4 kc = *reinterpret_cast<const uint4*>(static_cast<const S*>(a.key) + src);
-  S* kdst = static_cast<S*>(a.k_cache) + ((tile * C + c) * kBlockTokens + t) * X;
-  *reinterpret_cast<uint4*>(kdst) = kc;
+  write_token_chunk<Tr>(a.k_cache, a.v_cache, tile, C, a.head_dim, c, t,
+                        static_cast<const S*>(a.key) + src, static_cast<const S*>(a.value) + src);
+}
 
-  const uint4 vc = *reinterpret_cast<const uint4*>(static_cast<const S*>(a.value) + src);
-  S ve[X];
-  __builtin_memcpy(ve, &vc, sizeof(vc));
-  S* vdst = static_cast<S*>(a.v_cache) + (tile * a.head_dim + int64_t(c) * X) * kBlockTokens + t;
-#pragma unroll
-  for (int e = 0; e < X; ++e) vdst[e * kBlockTokens] = ve[e];
+// One new token per sequence, slot mapping and write in one launch: one thread
+// per (sequence, kv head, 16-byte chunk).  The slot is that of position
+// ctx - 1; -1 (nothing written) for ctx <= 0, ctx > max_nb*16 or a table entry
+// outside the pool.
+template <typename Tr>
+__global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
+  using S = typename Tr::storage;
+  constexpr int X = Tr::kChunk;
+  const int C = a.head_dim / X;
+  const int64_t total = int64_t(a.B) * a.num_kv_heads * C;
+  const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx >= total) return;
+  const int c = int(idx % C);
+  const int h = int((idx / C) % a.num_kv_heads);
+  const int b = int(idx / (int64_t(C) * a.num_kv_heads));
+  const int32_t n = a.context_lens[b];
+  int64_t slot = -1;
+  if (n > 0 && n <= a.max_nb * kBlockTokens) {
+    const int32_t pos = n - 1;
+    const int32_t blk = a.block_tables[int64_t(b) * a.max_nb + pos / kBlockTokens];
+    if (blk >= 0 && blk < a.num_blocks) slot = int64_t(blk) * kBlockTokens + pos % kBlockTokens;
+  }
+  if (a.slot_mapping && h == 0 && c == 0) a.slot_mapping[b] = slot;
+  if (slot < 0) return;
+  const int64_t src = (int64_t(b) * a.num_kv_heads + h) * a.head_dim + int64_t(c) * X;
+  const int64_t tile = (slot / kBlockTokens) * a.num_kv_heads + h;
+  write_token_chunk<Tr>(a.k_cache, a.v_cache, tile, C, a.head_dim, c, int(slot % kBlockTokens),
+                        static_cast<const S*>(a.key) + src, static_cast<const S*>(a.value) + src);
 }
 
 hipError_t launch_slot_mapping(const SlotMappingArgs& a, hipStream_t s) {
@@ -75,6 +125,19 @@ hipError_t launch_cache_write(const CacheWriteArgs& a, bool bf16, hipStream_t s)
     hipLaunchKernelGGL(cache_write_kernel<Bf16>, dim3(blocks), dim3(threads), 0, s, a);
   else
     hipLaunchKernelGGL(cache_write_kernel<F32>, dim3(blocks), dim3(threads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_append(const AppendArgs& a, bool bf16, hipStream_t s) {
+  const int X = bf16 ? Bf16::kChunk : F32::kChunk;
+  const int64_t total = int64_t(a.B) * a.num_kv_heads * (a.head_dim / X);
+  if (total == 0) return hipSuccess;
+  const int threads = 256;
+  const unsigned blocks = unsigned((total + threads - 1) / threads);
+  if (bf16)
+    hipLaunchKernelGGL(append_kernel<Bf16>, dim3(blocks), dim3(threads), 0, s, a);
+  else
+    hipLaunchKernelGGL(append_kernel<F32>, dim3(blocks), dim3(threads), 0, s, a);
   return hipGetLastError();
 }
 

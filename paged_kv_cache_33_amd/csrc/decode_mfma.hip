@@ -22,6 +22,7 @@
 // P^T operand of the second product, so no data moves between lanes.
 #include "device_common.h"
 #include "launch.h"
+#include "work_list.h"
 
 namespace pagedkv {
 namespace {
@@ -110,8 +111,11 @@ __device__ __forceinline__ void compute_block(const MfmaFrag<D>& f,
   }
 }
 
+// One work item: partition `part` of sequence b, head tile `tile_y` (a KV
+// head and a group of up to 16 of its query heads).
 template <int D>
-__global__ __launch_bounds__(kWaves * kWave) void decode_mfma_kernel(DecodeArgs a) {
+__device__ __forceinline__ void mfma_item(const DecodeArgs& a, const int part, const int tile_y,
+                                          const int b) {
   constexpr int KI = MfmaShape<D>::KI;
   constexpr int MC = MfmaShape<D>::MC;
   constexpr int kRow = D + 4;  // padded LDS row (floats)
@@ -123,10 +127,8 @@ __global__ __launch_bounds__(kWaves * kWave) void decode_mfma_kernel(DecodeArgs 
 
   const int g = a.H / a.num_kv_heads;
   const int ngroups = (g + kHeadsPerTile - 1) / kHeadsPerTile;
-  const int part = blockIdx.x;
-  const int kvh = blockIdx.y / ngroups;
-  const int hg = blockIdx.y % ngroups;
-  const int b = blockIdx.z;
+  const int kvh = tile_y / ngroups;
+  const int hg = tile_y % ngroups;
   const int head0 = kvh * g + hg * kHeadsPerTile;
   const int nh = min(kHeadsPerTile, g - hg * kHeadsPerTile);
   const int lane = threadIdx.x % kWave;
@@ -170,6 +172,17 @@ __global__ __launch_bounds__(kWaves * kWave) void decode_mfma_kernel(DecodeArgs 
   const int jb = tb / kBlockTokens;
   const int je = (te + kBlockTokens - 1) / kBlockTokens;
 
+  // The wave's blocks are j = jb + w + 8n, n = 0, 1, ...  Their table
+  // entries are read 64 at a time into one register (lane i holds entry n0 + i)
+  // so that a tile's address never waits on a dependent load.  The first window
+  // is requested before anything else: the first tile loads wait only for it.
+  const int32_t* table = a.block_tables + int64_t(b) * a.max_nb;
+  int win;
+  {
+    const int jj = jb + w + kWaves * lane;
+    win = jj < je ? table[jj] : -1;
+  }
+
   // Q^T operand: head n of this tile, dims of chunk 4i + q; zero past the group.
   bf16x8_t qop[KI];
   {
@@ -185,7 +198,6 @@ __global__ __launch_bounds__(kWaves * kWave) void decode_mfma_kernel(DecodeArgs 
 
   const uint16_t* kc = static_cast<const uint16_t*>(a.k_cache);
   const uint16_t* vc = static_cast<const uint16_t*>(a.v_cache);
-  const int32_t* table = a.block_tables + int64_t(b) * a.max_nb;
   const int64_t tile_elems = int64_t(kBlockTokens) * D;
 
   MfmaState<D> st;
@@ -195,42 +207,39 @@ __global__ __launch_bounds__(kWaves * kWave) void decode_mfma_kernel(DecodeArgs 
   st.l = 0.f;
   int bad_blk = 0;
 
-  // The wave's blocks are j = jb + w + 4n; their table entries are read 64 at
-  // a time into one register (lane i holds entry n0 + i).
-  int win = -1;
   auto table_entry = [&](int nn) -> int {
-    if ((nn & 63) == 0) {
+    if (nn > 0 && (nn & 63) == 0) {
       const int jj = jb + w + kWaves * (nn + lane);
       win = jj < je ? table[jj] : -1;
     }
     return __builtin_amdgcn_readlane(win, nn & 63);
   };
-  auto fetch = [&](int nn, MfmaFrag<D>& f) -> bool {
+  auto fetch = [&](int nn, MfmaFrag<D>& f) -> int64_t {
     const int p = table_entry(nn);
-    if (p < 0 || p >= a.num_blocks) return false;
+    if (p < 0 || p >= a.num_blocks) return -1;
     const int64_t tile = (int64_t(p) * a.num_kv_heads + kvh) * tile_elems;
     load_block<D>(f, kc + tile, vc + tile, lane);
-    return true;
+    return tile;
   };
-  auto consume = [&](int j, bool ok, const MfmaFrag<D>& f) {
-    if (!ok) { bad_blk = 1; return; }
+  auto consume = [&](int j, int64_t tile, const MfmaFrag<D>& f) {
+    if (tile < 0) { bad_blk = 1; return; }
     const int nvalid = te - j * kBlockTokens;
     if (nvalid >= kBlockTokens)
       compute_block<D, false>(f, qop, st, nvalid, a.scale_log2, lane);
     else
       compute_block<D, true>(f, qop, st, nvalid, a.scale_log2, lane);
   };
-
+  // Ping-pong over two register buffers: block n+1 is in flight while n computes.
   const int nblk = je - jb - w > 0 ? (je - jb - w + kWaves - 1) / kWaves : 0;
   MfmaFrag<D> fa, fb;
-  bool ok_a = false, ok_b = false;
-  if (nblk > 0) ok_a = fetch(0, fa);
+  int64_t tile_a = -1, tile_b = -1;
+  if (nblk > 0) tile_a = fetch(0, fa);
   for (int nn = 0; nn < nblk; nn += 2) {
-    if (nn + 1 < nblk) ok_b = fetch(nn + 1, fb);
-    consume(jb + w + kWaves * nn, ok_a, fa);
+    if (nn + 1 < nblk) tile_b = fetch(nn + 1, fb);
+    consume(jb + w + kWaves * nn, tile_a, fa);
     if (nn + 1 >= nblk) break;
-    if (nn + 2 < nblk) ok_a = fetch(nn + 2, fa);
-    consume(jb + w + kWaves * (nn + 1), ok_b, fb);
+    if (nn + 2 < nblk) tile_a = fetch(nn + 2, fa);
+    consume(jb + w + kWaves * (nn + 1), tile_b, fb);
   }
 
   const float lsum = cross_row_sum(st.l);
@@ -274,19 +283,47 @@ __global__ __launch_bounds__(kWaves * kWave) void decode_mfma_kernel(DecodeArgs 
   }
 }
 
+// Single pass (kSplit = false): grid (1, head tiles, B), one work-group per
+// sequence and head tile.  Split (kSplit = true): grid (resident workers, head
+// tiles, 1) walking the work list.  Two instantiations keep each one's
+// register allocation that of a single inlined item.
+template <int D, bool kSplit>
+__global__ __launch_bounds__(kWaves * kWave) void decode_mfma_kernel(DecodeArgs a) {
+  if constexpr (!kSplit) {
+    mfma_item<D>(a, 0, blockIdx.y, blockIdx.z);
+  } else {
+    __shared__ int sm_starts[kMaxSplitSeqs + 1];
+    const int n_items = build_work_list(a, sm_starts);
+    for (int i = blockIdx.x; i < n_items; i += gridDim.x) {
+      int b, part;
+      locate_item(sm_starts, a.B, i, b, part);
+      mfma_item<D>(a, part, blockIdx.y, b);
+      __syncthreads();  // the next item reuses the merge buffers
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_decode_mfma(const DecodeArgs& a, int head_dim, hipStream_t s) {
-  const int g = a.H / a.num_kv_heads;
-  const int ngroups = (g + kHeadsPerTile - 1) / kHeadsPerTile;
-  const dim3 grid(a.num_partitions, a.num_kv_heads * ngroups, a.B);
-  const dim3 block(kWaves * kWave);
+  const bool split = a.partition_size > 0;
+  void (*kern)(DecodeArgs) = nullptr;
   if (head_dim == 128)
-    hipLaunchKernelGGL(decode_mfma_kernel<128>, grid, block, 0, s, a);
+    kern = split ? decode_mfma_kernel<128, true> : decode_mfma_kernel<128, false>;
   else if (head_dim == 64)
-    hipLaunchKernelGGL(decode_mfma_kernel<64>, grid, block, 0, s, a);
+    kern = split ? decode_mfma_kernel<64, true> : decode_mfma_kernel<64, false>;
   else
     return hipErrorInvalidValue;
+  const int g = a.H / a.num_kv_heads;
+  const int tiles = a.num_kv_heads * ((g + kHeadsPerTile - 1) / kHeadsPerTile);
+  const dim3 block(kWaves * kWave);
+  dim3 grid(1, tiles, a.B);
+  if (a.partition_size > 0) {
+    const int64_t most = int64_t(a.B) * a.num_partitions;
+    const int workers = resident_workers(reinterpret_cast<const void*>(kern), block.x, tiles);
+    grid = dim3(unsigned(most < workers ? most : workers), tiles, 1);
+  }
+  hipLaunchKernelGGL(kern, grid, block, 0, s, a);
   return hipGetLastError();
 }
 

@@ -22,6 +22,7 @@
 //     each lane does plain fp32 FMAs.
 #include "device_common.h"
 #include "launch.h"
+#include "work_list.h"
 
 namespace pagedkv {
 namespace {
@@ -162,8 +163,10 @@ __device__ __forceinline__ void compute_block(const BlockFrag<Tr, D>& f, const Q
   }
 }
 
+// One work item: partition `part` of sequence b, query head h.
 template <typename Tr, int D>
-__global__ __launch_bounds__(kWaves * kWave) void decode_valu_kernel(DecodeArgs a) {
+__device__ __forceinline__ void valu_item(const DecodeArgs& a, const int part, const int h,
+                                          const int b) {
   using S = typename Tr::storage;
   using Sh = ValuShape<Tr, D>;
   constexpr int X = Sh::X;
@@ -173,9 +176,6 @@ __global__ __launch_bounds__(kWaves * kWave) void decode_valu_kernel(DecodeArgs 
   __shared__ float sm_l[kWaves];
   __shared__ int sm_bad[kWaves];
 
-  const int part = blockIdx.x;
-  const int h = blockIdx.y;
-  const int b = blockIdx.z;
   const int lane = threadIdx.x % kWave;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int kvh = h / (a.H / a.num_kv_heads);
@@ -210,6 +210,17 @@ __global__ __launch_bounds__(kWaves * kWave) void decode_valu_kernel(DecodeArgs 
   const int jb = tb / kBlockTokens;
   const int je = (te + kBlockTokens - 1) / kBlockTokens;
 
+  // The wave's blocks are j = jb + w + 8n, n = 0, 1, ...  Their table
+  // entries are read 64 at a time into one register (lane i holds entry n0 + i)
+  // so that a tile's address never waits on a dependent load.  The first window
+  // is requested before anything else: the first tile loads wait only for it.
+  const int32_t* table = a.block_tables + int64_t(b) * a.max_nb;
+  int win;
+  {
+    const int jj = jb + w + kWaves * lane;
+    win = jj < je ? table[jj] : -1;
+  }
+
   // This lane's slice of the query: chunks 4i + lane/16.
   QueryFrag<Tr, D> qf;
   {
@@ -221,7 +232,6 @@ __global__ __launch_bounds__(kWaves * kWave) void decode_valu_kernel(DecodeArgs 
 
   const S* kc = static_cast<const S*>(a.k_cache);
   const S* vc = static_cast<const S*>(a.v_cache);
-  const int32_t* table = a.block_tables + int64_t(b) * a.max_nb;
   const int64_t tile_elems = int64_t(kBlockTokens) * D;
 
   WaveState st{-INFINITY, 0.f};
@@ -230,45 +240,41 @@ __global__ __launch_bounds__(kWaves * kWave) void decode_valu_kernel(DecodeArgs 
   for (int xk = 0; xk < Sh::XK; ++xk) o[xk] = 0.f;
   int bad_blk = 0;
 
-  // The wave's blocks are j = jb + w + 4n, n = 0, 1, ...  Their table entries
-  // are read 64 at a time into one register (lane i holds entry n0 + i) so
-  // that a tile's address never waits on a dependent load.
-  int win = -1;
   auto table_entry = [&](int n) -> int {
-    if ((n & 63) == 0) {
+    if (n > 0 && (n & 63) == 0) {
       const int jj = jb + w + kWaves * (n + lane);
       win = jj < je ? table[jj] : -1;
     }
     return __builtin_amdgcn_readlane(win, n & 63);
   };
-  // Returns false (and loads nothing) for a table entry outside the pool.
-  auto fetch = [&](int n, BlockFrag<Tr, D>& f) -> bool {
+  // Returns the tile's element offset, or -1 (and loads nothing) for a table
+  // entry outside the pool.
+  auto fetch = [&](int n, BlockFrag<Tr, D>& f) -> int64_t {
     const int p = table_entry(n);
-    if (p < 0 || p >= a.num_blocks) return false;
+    if (p < 0 || p >= a.num_blocks) return -1;
     const int64_t tile = (int64_t(p) * a.num_kv_heads + kvh) * tile_elems;
     load_block<Tr, D>(f, kc + tile, vc + tile, lane);
-    return true;
+    return tile;
   };
-  auto consume = [&](int j, bool ok, const BlockFrag<Tr, D>& f) {
-    if (!ok) { bad_blk = 1; return; }
+  auto consume = [&](int j, int64_t tile, const BlockFrag<Tr, D>& f) {
+    if (tile < 0) { bad_blk = 1; return; }
     const int nvalid = te - j * kBlockTokens;
     if (nvalid >= kBlockTokens)
       compute_block<Tr, D, false>(f, qf, o, st, nvalid, a.scale_log2, lane);
     else
       compute_block<Tr, D, true>(f, qf, o, st, nvalid, a.scale_log2, lane);
   };
-
   // Ping-pong over two register buffers: block n+1 is in flight while n computes.
   const int nblk = je - jb - w > 0 ? (je - jb - w + kWaves - 1) / kWaves : 0;
   BlockFrag<Tr, D> fa, fb;
-  bool ok_a = false, ok_b = false;
-  if (nblk > 0) ok_a = fetch(0, fa);
+  int64_t tile_a = -1, tile_b = -1;
+  if (nblk > 0) tile_a = fetch(0, fa);
   for (int n = 0; n < nblk; n += 2) {
-    if (n + 1 < nblk) ok_b = fetch(n + 1, fb);
-    consume(jb + w + kWaves * n, ok_a, fa);
+    if (n + 1 < nblk) tile_b = fetch(n + 1, fb);
+    consume(jb + w + kWaves * n, tile_a, fa);
     if (n + 1 >= nblk) break;
-    if (n + 2 < nblk) ok_a = fetch(n + 2, fa);
-    consume(jb + w + kWaves * (n + 1), ok_b, fb);
+    if (n + 2 < nblk) tile_a = fetch(n + 2, fa);
+    consume(jb + w + kWaves * (n + 1), tile_b, fb);
   }
 
   // Wave totals: the denominator is spread over the 16 token lanes of a row.
@@ -312,21 +318,49 @@ __global__ __launch_bounds__(kWaves * kWave) void decode_valu_kernel(DecodeArgs 
   }
 }
 
+// Single pass (kSplit = false): grid (1, head tiles, B), one work-group per
+// sequence and head tile.  Split (kSplit = true): grid (resident workers, head
+// tiles, 1) walking the work list.  Two instantiations keep each one's
+// register allocation that of a single inlined item.
+template <typename Tr, int D, bool kSplit>
+__global__ __launch_bounds__(kWaves * kWave) void decode_valu_kernel(DecodeArgs a) {
+  if constexpr (!kSplit) {
+    valu_item<Tr, D>(a, 0, blockIdx.y, blockIdx.z);
+  } else {
+    __shared__ int sm_starts[kMaxSplitSeqs + 1];
+    const int n_items = build_work_list(a, sm_starts);
+    for (int i = blockIdx.x; i < n_items; i += gridDim.x) {
+      int b, part;
+      locate_item(sm_starts, a.B, i, b, part);
+      valu_item<Tr, D>(a, part, blockIdx.y, b);
+      __syncthreads();  // the next item reuses the merge buffers
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_decode_valu(const DecodeArgs& a, bool bf16, int head_dim, hipStream_t s) {
-  const dim3 grid(a.num_partitions, a.H, a.B);
-  const dim3 block(kWaves * kWave);
+  const bool split = a.partition_size > 0;
+  void (*kern)(DecodeArgs) = nullptr;
   if (bf16 && head_dim == 128)
-    hipLaunchKernelGGL((decode_valu_kernel<Bf16, 128>), grid, block, 0, s, a);
+    kern = split ? decode_valu_kernel<Bf16, 128, true> : decode_valu_kernel<Bf16, 128, false>;
   else if (bf16 && head_dim == 64)
-    hipLaunchKernelGGL((decode_valu_kernel<Bf16, 64>), grid, block, 0, s, a);
+    kern = split ? decode_valu_kernel<Bf16, 64, true> : decode_valu_kernel<Bf16, 64, false>;
   else if (!bf16 && head_dim == 128)
-    hipLaunchKernelGGL((decode_valu_kernel<F32, 128>), grid, block, 0, s, a);
+    kern = split ? decode_valu_kernel<F32, 128, true> : decode_valu_kernel<F32, 128, false>;
   else if (!bf16 && head_dim == 64)
-    hipLaunchKernelGGL((decode_valu_kernel<F32, 64>), grid, block, 0, s, a);
+    kern = split ? decode_valu_kernel<F32, 64, true> : decode_valu_kernel<F32, 64, false>;
   else
     return hipErrorInvalidValue;
+  const dim3 block(kWaves * kWave);
+  dim3 grid(1, a.H, a.B);
+  if (a.partition_size > 0) {
+    const int64_t most = int64_t(a.B) * a.num_partitions;
+    const int workers = resident_workers(reinterpret_cast<const void*>(kern), block.x, a.H);
+    grid = dim3(unsigned(most < workers ? most : workers), a.H, 1);
+  }
+  hipLaunchKernelGGL(kern, grid, block, 0, s, a);
   return hipGetLastError();
 }
 

@@ -6,6 +6,14 @@
 
 namespace pagedkv {
 
+// Sequences one split-KV call may hold: the kernels keep one prefix-sum entry
+// per sequence in LDS.
+constexpr int kMaxSplitSeqs = 4096;
+
+// Work-groups of `kernel` (block size `threads`) the current GPU keeps
+// resident at once, divided among `tiles` head tiles (at least 1 each).
+int resident_workers(const void* kernel, int threads, int tiles);
+
 // Everything a decode kernel needs; passed by value as the kernel argument.
 struct DecodeArgs {
   const void* k_cache;
@@ -53,6 +61,22 @@ struct CacheWriteArgs {
   int32_t N;
 };
 
+// One new token per sequence: slot mapping and cache write in one launch.
+struct AppendArgs {
+  void* k_cache;
+  void* v_cache;
+  int32_t num_blocks;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  const void* key;              // [B][H_kv][d]
+  const void* value;
+  const int32_t* block_tables;  // [B][max_nb]
+  int32_t max_nb;
+  const int32_t* context_lens;  // [B]
+  int32_t B;
+  int64_t* slot_mapping;        // optional [B] out
+};
+
 struct SlotMappingArgs {
   const int32_t* block_tables;
   int32_t max_nb;
@@ -64,6 +88,7 @@ struct SlotMappingArgs {
 // Launchers: return the hipError_t of the launch.
 hipError_t launch_slot_mapping(const SlotMappingArgs& a, hipStream_t s);
 hipError_t launch_cache_write(const CacheWriteArgs& a, bool bf16, hipStream_t s);
+hipError_t launch_append(const AppendArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_decode_valu(const DecodeArgs& a, bool bf16, int head_dim, hipStream_t s);
 hipError_t launch_decode_mfma(const DecodeArgs& a, int head_dim, hipStream_t s);
 hipError_t launch_reduce(const ReduceArgs& a, bool bf16_out, hipStream_t s);

@@ -83,21 +83,26 @@ def upload(w: W.Workload, k_pool: np.ndarray, v_pool: np.ndarray) -> DevWorkload
 
 
 def gpu_step(dw: DevWorkload, step: W.DecodeStep, partition_size: int = 0,
-             max_context_len: Optional[int] = None, write: bool = True):
-    """One decode step on the GPU: slot mapping, cache write, decode (+ reduce).
+             max_context_len: Optional[int] = None, write: bool = True, fused: bool = False):
+    """One decode step on the GPU: slot mapping, cache write, decode (+ reduce);
+    the first two as separate calls or (fused) as one kv_cache_append.
     Returns (slots, out) as device tensors."""
     w = dw.w
     ctx = torch.from_numpy(step.context_lens).cuda()
     q = to_dev(step.q)
-    slots = P.kv_slot_mapping(dw.tables, ctx)
-    if write:
-        P.reshape_and_cache(dw.pool, to_dev(step.new_k), to_dev(step.new_v), slots)
     out = torch.empty_like(q)
-    L = int(step.context_lens.max()) if max_context_len is None else max_context_len
+    L = int(max(step.context_lens.max(), 1)) if max_context_len is None else max_context_len
     ws = None
     if partition_size:
         n = P.paged_attention_workspace_bytes(w.B, w.H, w.d, L, partition_size)
         ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    if fused:
+        slots = torch.full((w.B,), -7, dtype=torch.int64, device="cuda")
+        P.kv_cache_append(dw.pool, to_dev(step.new_k), to_dev(step.new_v), dw.tables, ctx, slots)
+    else:
+        slots = P.kv_slot_mapping(dw.tables, ctx)
+        if write:
+            P.reshape_and_cache(dw.pool, to_dev(step.new_k), to_dev(step.new_v), slots)
     P.paged_attention_decode(dw.pool, out, q, dw.tables, ctx, L, w.scale, partition_size, ws)
     if partition_size:
         P.paged_attention_reduce(out, ws, ctx, L, partition_size, w.dtype)
@@ -136,14 +141,15 @@ def assert_close(got_bits: np.ndarray, ref: dict, dtype: str, label: str = "",
 
 
 def single_step_case(w: W.Workload, partition_size: int = 0, seqs=None, label: str = "",
-                     amplitude: float = 1.0):
+                     amplitude: float = 1.0, fused: bool = False):
     """Full parity check of one step: slots and pool bit-exact, outputs in tolerance."""
     step = w.steps[0]
     first_unwritten = step.context_lens.astype(np.int64) - 1
     kp0, vp0 = poison(w, np.maximum(first_unwritten, 0))
     dw = upload(w, kp0, vp0)
-    log(f"[gpu] {label} B={w.B} H={w.H} H_kv={w.H_kv} d={w.d} {w.dtype} P={partition_size}")
-    slots, out = gpu_step(dw, step, partition_size)
+    log(f"[gpu] {label} B={w.B} H={w.H} H_kv={w.H_kv} d={w.d} {w.dtype} P={partition_size}"
+        f"{' fused' if fused else ''}")
+    slots, out = gpu_step(dw, step, partition_size, fused=fused)
     torch.cuda.synchronize()
     oslots, kp, vp, ref = oracle_step(w, kp0, vp0, step, seqs)
     np.testing.assert_array_equal(slots.cpu().numpy(), oslots, err_msg=f"{label}: slots")

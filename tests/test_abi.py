@@ -119,6 +119,16 @@ def test_cache_write_argument_errors(lib, pool):
     assert lib.reshape_and_cache(pool, None, None, None, 0, None) == _lib.KV_OK  # nothing to do
 
 
+def test_append_argument_errors(lib, pool):
+    f = lib.kv_cache_append
+    assert f(None, FAKE_K, FAKE_V, FAKE_K, 4, FAKE_V, 2, None, None) == _lib.KV_ERR_INVALID_ARG
+    assert f(pool, FAKE_K, FAKE_V, FAKE_K, 4, FAKE_V, -1, None, None) == _lib.KV_ERR_INVALID_ARG
+    assert f(pool, FAKE_K, FAKE_V, FAKE_K, 0, FAKE_V, 2, None, None) == _lib.KV_ERR_INVALID_ARG
+    assert f(pool, None, FAKE_V, FAKE_K, 4, FAKE_V, 2, None, None) == _lib.KV_ERR_INVALID_ARG
+    assert f(pool, FAKE_K + 2, FAKE_V, FAKE_K, 4, FAKE_V, 2, None, None) == _lib.KV_ERR_INVALID_ARG
+    assert f(pool, None, None, None, 4, None, 0, None, None) == _lib.KV_OK   # nothing to do
+
+
 def test_slot_mapping_argument_errors(lib):
     assert lib.kv_slot_mapping(None, 4, None, -1, None, None) == _lib.KV_ERR_INVALID_ARG
     assert lib.kv_slot_mapping(FAKE_K, 0, FAKE_K, 1, FAKE_V, None) == _lib.KV_ERR_INVALID_ARG

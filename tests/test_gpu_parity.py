@@ -16,6 +16,7 @@ from workloads import configs as W
 
 from _harness import (assert_close, from_dev, gpu_step, log, oracle_step, poison,
                       single_step_case, upload)
+from _harness import to_dev as _harness_to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -204,3 +205,47 @@ def test_value_outliers_keep_tolerance(H, H_kv):
     # outlier channels, whose outputs reach tens where one bf16 ulp is ~0.1
     single_step_case(w, 0, label="outliers", amplitude=20.0)
     single_step_case(w, 32, label="outliers-split", amplitude=20.0)
+
+
+# ---------------------------------------------------------------- fused append
+@pytest.mark.parametrize("dtype,d,H,H_kv", [("bf16", 128, 4, 4), ("bf16", 64, 4, 4),
+                                            ("bf16", 128, 16, 2), ("bf16", 128, 64, 2),
+                                            ("f32", 64, 2, 2), ("f32", 128, 8, 2)])
+@pytest.mark.parametrize("P_", [0, 512])
+def test_append_then_decode_matches_oracle(dtype, d, H, H_kv, P_):
+    lens = [1, 15, 16, 17, 33, 250, 700]
+    w = W.scattered_workload("append", dtype, B=len(lens), H=H, H_kv=H_kv, d=d, context_lens=lens,
+                             seed=111 + d + H)
+    single_step_case(w, P_, label=f"append-{dtype}-d{d}-H{H}", fused=True)
+
+
+@pytest.mark.parametrize("dtype,d,H_kv", [("bf16", 128, 4), ("bf16", 64, 2), ("f32", 64, 3),
+                                          ("f32", 128, 1)])
+def test_append_equals_slot_mapping_plus_cache_write(dtype, d, H_kv):
+    """kv_cache_append == kv_slot_mapping + reshape_and_cache, bit for bit, including the
+    -1 slots of an empty sequence, a length past the table and a table entry
+    outside the pool."""
+    lens = [0, 1, 16, 17, 47, 200, 31]
+    w = W.scattered_workload("append-eq", dtype, B=len(lens), H=H_kv, H_kv=H_kv, d=d,
+                             context_lens=lens, seed=131 + d)
+    step = w.steps[0]
+    kp, vp = poison(w, np.maximum(step.context_lens.astype(np.int64) - 1, 0))
+    w.block_tables[6, 1] = w.num_blocks + 5           # position 30 lies in a block outside the pool
+    ctx = step.context_lens.copy()
+    ctx[3] = w.max_nb * 16 + 1                          # past the table
+    a = upload(w, kp, vp)
+    b = upload(w, kp, vp)
+    tctx = torch.from_numpy(ctx).cuda()
+    sa = P.kv_slot_mapping(a.tables, tctx)
+    P.reshape_and_cache(a.pool, _harness_to_dev(step.new_k), _harness_to_dev(step.new_v), sa)
+    sb = torch.full((w.B,), -7, dtype=torch.int64, device="cuda")
+    P.kv_cache_append(b.pool, _harness_to_dev(step.new_k), _harness_to_dev(step.new_v), b.tables,
+                      tctx, sb)
+    torch.cuda.synchronize()
+    got = sb.cpu().numpy()
+    ref = sa.cpu().numpy()
+    ref[ref >= w.num_blocks * 16] = -1                  # the fused call reports these as -1
+    np.testing.assert_array_equal(got, ref)
+    assert got[0] == -1 and got[3] == -1 and got[6] == -1
+    assert np.array_equal(from_dev(a.pool.k_cache, dtype), from_dev(b.pool.k_cache, dtype))
+    assert np.array_equal(from_dev(a.pool.v_cache, dtype), from_dev(b.pool.v_cache, dtype))
