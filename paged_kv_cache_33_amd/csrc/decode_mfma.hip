@@ -207,19 +207,18 @@ __device__ __forceinline__ void mfma_item(const DecodeArgs& a, const int part, c
   st.l = 0.f;
   int bad_blk = 0;
 
-  auto table_entry = [&](int nn) -> int {
-    if (nn > 0 && (nn & 63) == 0) {
-      const int jj = jb + w + kWaves * (nn + lane);
-      win = jj < je ? table[jj] : -1;
-    }
-    return __builtin_amdgcn_readlane(win, nn & 63);
-  };
-  auto fetch = [&](int nn, MfmaFrag<D>& f) -> int64_t {
-    const int p = table_entry(nn);
-    if (p < 0 || p >= a.num_blocks) return -1;
-    const int64_t tile = (int64_t(p) * a.num_kv_heads + kvh) * tile_elems;
+  // Block n of this wave's walk, from the current window of table entries
+  // (lane i of `win` holds entry n0 + i).  No branch around the loads: an entry
+  // outside the pool loads tile 0 instead (always valid memory) and is
+  // reported as -1, so every load in the loop below is unconditional and the
+  // compiler can keep the next block's loads in flight while one computes.
+  int n0 = 0;
+  auto fetch = [&](int n, MfmaFrag<D>& f) -> int64_t {
+    const int p = __builtin_amdgcn_readlane(win, n - n0);
+    const bool ok = p >= 0 && p < a.num_blocks;
+    const int64_t tile = (int64_t(ok ? p : 0) * a.num_kv_heads + kvh) * tile_elems;
     load_block<D>(f, kc + tile, vc + tile, lane);
-    return tile;
+    return ok ? tile : -1;
   };
   auto consume = [&](int j, int64_t tile, const MfmaFrag<D>& f) {
     if (tile < 0) { bad_blk = 1; return; }
@@ -229,17 +228,32 @@ __device__ __forceinline__ void mfma_item(const DecodeArgs& a, const int part, c
     else
       compute_block<D, true>(f, qop, st, nvalid, a.scale_log2, lane);
   };
-  // Ping-pong over two register buffers: block n+1 is in flight while n computes.
+  // Ping-pong over two register buffers: block n+1 is in flight while n
+  // computes.  Windows of 64 blocks; inside one, every iteration has a next
+  // block to fetch (the last one or two are peeled off).
   const int nblk = je - jb - w > 0 ? (je - jb - w + kWaves - 1) / kWaves : 0;
   MfmaFrag<D> fa, fb;
-  int64_t tile_a = -1, tile_b = -1;
-  if (nblk > 0) tile_a = fetch(0, fa);
-  for (int nn = 0; nn < nblk; nn += 2) {
-    if (nn + 1 < nblk) tile_b = fetch(nn + 1, fb);
-    consume(jb + w + kWaves * nn, tile_a, fa);
-    if (nn + 1 >= nblk) break;
-    if (nn + 2 < nblk) tile_a = fetch(nn + 2, fa);
-    consume(jb + w + kWaves * (nn + 1), tile_b, fb);
+  for (; n0 < nblk; n0 += kWave) {
+    const int cnt = min(kWave, nblk - n0);
+    if (n0 > 0) {
+      const int jj = jb + w + kWaves * (n0 + lane);
+      win = lane < cnt ? table[jj] : -1;
+    }
+    int64_t tile_a = fetch(n0, fa), tile_b;
+    int n = 0;
+    for (; n + 2 < cnt; n += 2) {
+      tile_b = fetch(n0 + n + 1, fb);
+      consume(jb + w + kWaves * (n0 + n), tile_a, fa);
+      tile_a = fetch(n0 + n + 2, fa);
+      consume(jb + w + kWaves * (n0 + n + 1), tile_b, fb);
+    }
+    if (n + 1 < cnt) {
+      tile_b = fetch(n0 + n + 1, fb);
+      consume(jb + w + kWaves * (n0 + n), tile_a, fa);
+      consume(jb + w + kWaves * (n0 + n + 1), tile_b, fb);
+    } else {
+      consume(jb + w + kWaves * (n0 + n), tile_a, fa);
+    }
   }
 
   const float lsum = cross_row_sum(st.l);

@@ -240,21 +240,18 @@ __device__ __forceinline__ void valu_item(const DecodeArgs& a, const int part, c
   for (int xk = 0; xk < Sh::XK; ++xk) o[xk] = 0.f;
   int bad_blk = 0;
 
-  auto table_entry = [&](int n) -> int {
-    if (n > 0 && (n & 63) == 0) {
-      const int jj = jb + w + kWaves * (n + lane);
-      win = jj < je ? table[jj] : -1;
-    }
-    return __builtin_amdgcn_readlane(win, n & 63);
-  };
-  // Returns the tile's element offset, or -1 (and loads nothing) for a table
-  // entry outside the pool.
+  // Block n of this wave's walk, from the current window of table entries
+  // (lane i of `win` holds entry n0 + i).  No branch around the loads: an entry
+  // outside the pool loads tile 0 instead (always valid memory) and is
+  // reported as -1, so every load in the loop below is unconditional and the
+  // compiler can keep the next block's loads in flight while one computes.
+  int n0 = 0;
   auto fetch = [&](int n, BlockFrag<Tr, D>& f) -> int64_t {
-    const int p = table_entry(n);
-    if (p < 0 || p >= a.num_blocks) return -1;
-    const int64_t tile = (int64_t(p) * a.num_kv_heads + kvh) * tile_elems;
+    const int p = __builtin_amdgcn_readlane(win, n - n0);
+    const bool ok = p >= 0 && p < a.num_blocks;
+    const int64_t tile = (int64_t(ok ? p : 0) * a.num_kv_heads + kvh) * tile_elems;
     load_block<Tr, D>(f, kc + tile, vc + tile, lane);
-    return tile;
+    return ok ? tile : -1;
   };
   auto consume = [&](int j, int64_t tile, const BlockFrag<Tr, D>& f) {
     if (tile < 0) { bad_blk = 1; return; }
@@ -264,17 +261,32 @@ __device__ __forceinline__ void valu_item(const DecodeArgs& a, const int part, c
     else
       compute_block<Tr, D, true>(f, qf, o, st, nvalid, a.scale_log2, lane);
   };
-  // Ping-pong over two register buffers: block n+1 is in flight while n computes.
+  // Ping-pong over two register buffers: block n+1 is in flight while n
+  // computes.  Windows of 64 blocks; inside one, every iteration has a next
+  // block to fetch (the last one or two are peeled off).
   const int nblk = je - jb - w > 0 ? (je - jb - w + kWaves - 1) / kWaves : 0;
   BlockFrag<Tr, D> fa, fb;
-  int64_t tile_a = -1, tile_b = -1;
-  if (nblk > 0) tile_a = fetch(0, fa);
-  for (int n = 0; n < nblk; n += 2) {
-    if (n + 1 < nblk) tile_b = fetch(n + 1, fb);
-    consume(jb + w + kWaves * n, tile_a, fa);
-    if (n + 1 >= nblk) break;
-    if (n + 2 < nblk) tile_a = fetch(n + 2, fa);
-    consume(jb + w + kWaves * (n + 1), tile_b, fb);
+  for (; n0 < nblk; n0 += kWave) {
+    const int cnt = min(kWave, nblk - n0);
+    if (n0 > 0) {
+      const int jj = jb + w + kWaves * (n0 + lane);
+      win = lane < cnt ? table[jj] : -1;
+    }
+    int64_t tile_a = fetch(n0, fa), tile_b;
+    int n = 0;
+    for (; n + 2 < cnt; n += 2) {
+      tile_b = fetch(n0 + n + 1, fb);
+      consume(jb + w + kWaves * (n0 + n), tile_a, fa);
+      tile_a = fetch(n0 + n + 2, fa);
+      consume(jb + w + kWaves * (n0 + n + 1), tile_b, fb);
+    }
+    if (n + 1 < cnt) {
+      tile_b = fetch(n0 + n + 1, fb);
+      consume(jb + w + kWaves * (n0 + n), tile_a, fa);
+      consume(jb + w + kWaves * (n0 + n + 1), tile_b, fb);
+    } else {
+      consume(jb + w + kWaves * (n0 + n), tile_a, fa);
+    }
   }
 
   // Wave totals: the denominator is spread over the 16 token lanes of a row.
