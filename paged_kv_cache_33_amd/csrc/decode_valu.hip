@@ -331,13 +331,17 @@ __device__ __forceinline__ void valu_item(const DecodeArgs& a, const int part, c
 }
 
 // Single pass (kSplit = false): grid (1, head tiles, B), one work-group per
-// sequence and head tile.  Split (kSplit = true): grid (resident workers, head
+// sequence and head tile, sequences taken longest first.  Split (kSplit = true): grid (resident workers, head
 // tiles, 1) walking the work list.  Two instantiations keep each one's
 // register allocation that of a single inlined item.
 template <typename Tr, int D, bool kSplit>
 __global__ __launch_bounds__(kWaves * kWave) void decode_valu_kernel(DecodeArgs a) {
   if constexpr (!kSplit) {
-    valu_item<Tr, D>(a, 0, blockIdx.y, blockIdx.z);
+    __shared__ int sm_order[kOrderBuckets + kWaves + 1];
+    const int b = a.B <= kMaxOrderedSeqs
+        ? sequence_of_rank<kWaves * kWave>(a.context_lens, a.B, a.max_nb, blockIdx.z, sm_order)
+        : int(blockIdx.z);
+    valu_item<Tr, D>(a, 0, blockIdx.y, b);
   } else {
     __shared__ int sm_starts[kMaxSplitSeqs + 1];
     const int n_items = build_work_list(a, sm_starts);

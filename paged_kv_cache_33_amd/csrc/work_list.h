@@ -59,4 +59,85 @@ __device__ __forceinline__ void locate_item(const int* starts, int B, int i, int
   part = i - starts[lo];
 }
 
+
+// Single-pass decode takes sequences longest first.  Work-groups are dispatched
+// in index order, so when work-group z takes the z-th longest sequence the
+// dispatcher itself deals the work longest-processing-time first: the long
+// sequences start at once and the short ones fill the gaps at the end, where a
+// long sequence drawn late would otherwise run alone on a draining GPU.  Every
+// work-group derives the same order from context_lens: sequences are bucketed
+// by block count (kOrderBuckets equal-width buckets over [0, max_nb]), longer
+// buckets first, index order inside a bucket.  Any order is correct (each
+// sequence is still taken by exactly one work-group); this one balances load.
+constexpr int kOrderBuckets = 32;
+constexpr int kMaxOrderedSeqs = 4096;
+
+// Sequence of rank r (0 <= r < B <= kMaxOrderedSeqs) in that order.  sh: LDS of
+// kOrderBuckets + kThreads / 64 + 1 ints.  Called by every thread of the
+// work-group (it synchronises).
+template <int kThreads>
+__device__ __forceinline__ int sequence_of_rank(const int32_t* __restrict__ context_lens, int B,
+                                                int max_nb, int r, int* sh) {
+  constexpr int kW = kThreads / kWave;
+  constexpr int kMaxIters = kMaxOrderedSeqs / kThreads;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
+  int* total = sh;                      // [kOrderBuckets] members per bucket
+  int* wave_cnt = sh + kOrderBuckets;   // [kW] members of the wanted bucket per wave
+  int* result = wave_cnt + kW;
+  for (int k = tid; k < kOrderBuckets; k += kThreads) total[k] = 0;
+  if (tid == 0) *result = r;  // always a valid index
+  // Wave w owns sequences [w * per_wave, (w + 1) * per_wave), 64 per iteration.
+  const int iters = (B + kThreads - 1) / kThreads;
+  const int per_wave = iters * kWave;
+  int key[kMaxIters];
+#pragma unroll
+  for (int it = 0; it < kMaxIters; ++it) {
+    key[it] = -1;
+    const int j = w * per_wave + it * kWave + lane;
+    if (it < iters && j < B) {
+      const int n = context_lens[j];
+      const int64_t nb = n > 0 ? min((int64_t(n) + kBlockTokens - 1) / kBlockTokens, int64_t(max_nb)) : 0;
+      key[it] = int(nb * kOrderBuckets / (int64_t(max_nb) + 1));
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int it = 0; it < kMaxIters; ++it)
+    if (key[it] >= 0) atomicAdd(&total[key[it]], 1);
+  __syncthreads();
+  // Bucket holding rank r, from the longest bucket down, and r's index in it.
+  int want_key = 0, before = 0;
+  for (int k = kOrderBuckets - 1; k >= 0; --k) {
+    const int t = total[k];
+    if (r < before + t) { want_key = k; break; }
+    before += t;
+  }
+  const int want = r - before;
+  int cnt = 0;
+#pragma unroll
+  for (int it = 0; it < kMaxIters; ++it)
+    cnt += __popcll(__ballot(key[it] == want_key));
+  if (lane == 0) wave_cnt[w] = cnt;
+  __syncthreads();
+  int base = 0;
+  for (int ww = 0; ww < w; ++ww) base += wave_cnt[ww];
+  if (want >= base && want < base + cnt) {
+    int seen = base;
+#pragma unroll
+    for (int it = 0; it < kMaxIters; ++it) {
+      const uint64_t m = __ballot(key[it] == want_key);
+      const int c = __popcll(m);
+      if (want < seen + c) {
+        const bool mine = (m >> lane) & 1;
+        if (mine && __popcll(m & ((uint64_t(1) << lane) - 1)) == want - seen)
+          *result = w * per_wave + it * kWave + lane;
+        break;
+      }
+      seen += c;
+    }
+  }
+  __syncthreads();
+  return *result;
+}
+
 }  // namespace pagedkv
