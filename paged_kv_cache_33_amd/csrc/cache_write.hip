@@ -30,18 +30,16 @@ __global__ __launch_bounds__(256) void slot_mapping_kernel(SlotMappingArgs a) {
   a.slot_mapping[b] = slot;
 }
 
-// Write chunk c (X elements) of one token's K and V rows into in-block slot t of
-// tile `tile`: one 16-byte store for K ([d/X][16][X] tile), X element stores
-// for V ([d][16] tile).  Pure bit moves: no value is converted.
+// Write chunk c (X elements) of one token's K and V rows, already loaded as
+// kc and vc, into in-block slot t of tile `tile`: one 16-byte store for K
+// ([d/X][16][X] tile), X element stores for V ([d][16] tile).  Pure bit moves:
+// no value is converted.
 template <typename Tr>
 __device__ __forceinline__ void write_token_chunk(void* k_cache, void* v_cache, int64_t tile, int C,
-                                                  int head_dim, int c, int t,
-                                                  const typename Tr::storage* ksrc,
-                                                  const typename Tr::storage* vsrc) {
+                                                  int head_dim, int c, int t, const uint4 kc,
+                                                  const uint4 vc) {
   using S = typename Tr::storage;
   constexpr int X = Tr::kChunk;
-  const uint4 kc = *reinterpret_cast<const uint4*>(ksrc);
-  const uint4 vc = *reinterpret_cast<const uint4*>(vsrc);
   S* kdst = static_cast<S*>(k_cache) + ((tile * C + c) * kBlockTokens + t) * X;
   const u32x4_t ku = {kc.x, kc.y, kc.z, kc.w};
   __builtin_nontemporal_store(ku, reinterpret_cast<u32x4_t*>(kdst));
@@ -52,12 +50,17 @@ __device__ __forceinline__ void write_token_chunk(void* k_cache, void* v_cache, 
   for (int e = 0; e < X; ++e) __builtin_nontemporal_store(ve[e], vdst + e * kBlockTokens);
 }
 
+// The 16-byte chunk of a source row (key or value) at element offset src.
+template <typename Tr>
+__device__ __forceinline__ uint4 load_chunk(const void* base, int64_t src) {
+  return *reinterpret_cast<const uint4*>(static_cast<const typename Tr::storage*>(base) + src);
+}
+
 // One thread per (token, kv head, 16-byte chunk of the head's row).  K chunks
 // land as one 16-byte store ([d/X][16][X] tile); V elements land one by one in
 // the token-minor [d][16] tile.  Pure bit moves: no value is converted.
 template <typename Tr>
 __global__ __launch_bounds__(256) void cache_write_kernel(CacheWriteArgs a) {
-  using S = typename Tr::storage;
   constexpr int X = Tr::kChunk;
   const int C = a.head_dim / X;
   const int64_t total = int64_t(a.N) * a.num_kv_heads * C;
@@ -66,15 +69,17 @@ __global__ __launch_bounds__(256) void cache_write_kernel(CacheWriteArgs a) {
   const int c = int(idx % C);
   const int h = int((idx / C) % a.num_kv_heads);
   const int64_t i = idx / (int64_t(C) * a.num_kv_heads);
+  // The source chunk does not depend on the slot: load it first, so its
+  // latency overlaps that of the slot load.
+  const int64_t src = (i * a.num_kv_heads + h) * a.head_dim + int64_t(c) * X;
+  const uint4 kc = load_chunk<Tr>(a.key, src);
+  const uint4 vc = load_chunk<Tr>(a.value, src);
   const int64_t slot = a.slot_mapping[i];
   if (slot < 0 || slot >= int64_t(a.num_blocks) * kBlockTokens) return;
   const int64_t p = slot / kBlockTokens;
   const int t = int(slot % kBlockTokens);
-  const int64_t src = (i * a.num_kv_heads + h) * a.head_dim + int64_t(c) * X;
   const int64_t tile = p * a.num_kv_heads + h;
-
-  write_token_chunk<Tr>(a.k_cache, a.v_cache, tile, C, a.head_dim, c, t,
-                        static_cast<const S*>(a.key) + src, static_cast<const S*>(a.value) + src);
+  write_token_chunk<Tr>(a.k_cache, a.v_cache, tile, C, a.head_dim, c, t, kc, vc);
 }
 
 // One new token per sequence, slot mapping and write in one launch: one thread
@@ -83,7 +88,6 @@ __global__ __launch_bounds__(256) void cache_write_kernel(CacheWriteArgs a) {
 // outside the pool.
 template <typename Tr>
 __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
-  using S = typename Tr::storage;
   constexpr int X = Tr::kChunk;
   const int C = a.head_dim / X;
   const int64_t total = int64_t(a.B) * a.num_kv_heads * C;
@@ -92,6 +96,10 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   const int c = int(idx % C);
   const int h = int((idx / C) % a.num_kv_heads);
   const int b = int(idx / (int64_t(C) * a.num_kv_heads));
+  // Source chunk first: it overlaps the dependent length -> table loads.
+  const int64_t src = (int64_t(b) * a.num_kv_heads + h) * a.head_dim + int64_t(c) * X;
+  const uint4 kc = load_chunk<Tr>(a.key, src);
+  const uint4 vc = load_chunk<Tr>(a.value, src);
   const int32_t n = a.context_lens[b];
   int64_t slot = -1;
   if (n > 0 && n <= a.max_nb * kBlockTokens) {
@@ -101,10 +109,9 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   }
   if (a.slot_mapping && h == 0 && c == 0) a.slot_mapping[b] = slot;
   if (slot < 0) return;
-  const int64_t src = (int64_t(b) * a.num_kv_heads + h) * a.head_dim + int64_t(c) * X;
   const int64_t tile = (slot / kBlockTokens) * a.num_kv_heads + h;
-  write_token_chunk<Tr>(a.k_cache, a.v_cache, tile, C, a.head_dim, c, int(slot % kBlockTokens),
-                        static_cast<const S*>(a.key) + src, static_cast<const S*>(a.value) + src);
+  write_token_chunk<Tr>(a.k_cache, a.v_cache, tile, C, a.head_dim, c, int(slot % kBlockTokens), kc,
+                        vc);
 }
 
 hipError_t launch_slot_mapping(const SlotMappingArgs& a, hipStream_t s) {

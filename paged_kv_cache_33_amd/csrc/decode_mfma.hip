@@ -27,7 +27,12 @@
 namespace pagedkv {
 namespace {
 
-constexpr int kWaves = 8;
+// Waves per work-group.  Single pass: 4, so that three work-groups share a CU
+// (168 VGPRs leave room for 3 waves per SIMD) and a finishing work-group's
+// successor fetches its first blocks while two others stream.  Split: 8, as its
+// work-list loop does not fit 3 waves per SIMD without spilling.
+template <bool kSplit>
+constexpr int kWavesOf = kSplit ? 8 : 4;
 constexpr int kHeadsPerTile = 16;
 
 typedef __bf16 bf16x8_t __attribute__((__vector_size__(8 * sizeof(__bf16))));
@@ -113,7 +118,7 @@ __device__ __forceinline__ void compute_block(const MfmaFrag<D>& f,
 
 // One work item: partition `part` of sequence b, head tile `tile_y` (a KV
 // head and a group of up to 16 of its query heads).
-template <int D>
+template <int D, int kWaves>
 __device__ __forceinline__ void mfma_item(const DecodeArgs& a, const int part, const int tile_y,
                                           const int b) {
   constexpr int KI = MfmaShape<D>::KI;
@@ -298,24 +303,26 @@ __device__ __forceinline__ void mfma_item(const DecodeArgs& a, const int part, c
 }
 
 // Single pass (kSplit = false): grid (1, head tiles, B), one work-group per
-// sequence and head tile, sequences taken longest first.  Split (kSplit = true): grid (resident workers, head
-// tiles, 1) walking the work list.  Two instantiations keep each one's
+// sequence and head tile, sequences taken longest first.  Split (kSplit =
+// true): grid (resident workers, head tiles, 1) walking the work list.  Two instantiations keep each one's
 // register allocation that of a single inlined item.
 template <int D, bool kSplit>
-__global__ __launch_bounds__(kWaves * kWave) void decode_mfma_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kWavesOf<kSplit> * kWave, kSplit ? 1 : 3) void decode_mfma_kernel(
+    DecodeArgs a) {
+  constexpr int kWaves = kWavesOf<kSplit>;
   if constexpr (!kSplit) {
     __shared__ int sm_order[kOrderBuckets + kWaves + 1];
     const int b = a.B <= kMaxOrderedSeqs
         ? sequence_of_rank<kWaves * kWave>(a.context_lens, a.B, a.max_nb, blockIdx.z, sm_order)
         : int(blockIdx.z);
-    mfma_item<D>(a, 0, blockIdx.y, b);
+    mfma_item<D, kWaves>(a, 0, blockIdx.y, b);
   } else {
     __shared__ int sm_starts[kMaxSplitSeqs + 1];
     const int n_items = build_work_list(a, sm_starts);
     for (int i = blockIdx.x; i < n_items; i += gridDim.x) {
       int b, part;
       locate_item(sm_starts, a.B, i, b, part);
-      mfma_item<D>(a, part, blockIdx.y, b);
+      mfma_item<D, kWaves>(a, part, blockIdx.y, b);
       __syncthreads();  // the next item reuses the merge buffers
     }
   }
@@ -334,7 +341,7 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, int head_dim, hipStream_t s) 
     return hipErrorInvalidValue;
   const int g = a.H / a.num_kv_heads;
   const int tiles = a.num_kv_heads * ((g + kHeadsPerTile - 1) / kHeadsPerTile);
-  const dim3 block(kWaves * kWave);
+  const dim3 block((split ? kWavesOf<true> : kWavesOf<false>) * kWave);
   dim3 grid(1, tiles, a.B);
   if (a.partition_size > 0) {
     const int64_t most = int64_t(a.B) * a.num_partitions;
