@@ -7,7 +7,7 @@
 // applied to whole partitions:
 //   w_k = l_k * 2^(m_k - M),   out = sum_k w_k o_k / sum_k w_k.
 // One work-group per (query head, sequence); the weights are computed once into
-// LDS, then the threads split the partitions and each output dim.
+// LDS, then the threads split the partitions and the output dims.
 #include "device_common.h"
 #include "launch.h"
 
@@ -40,15 +40,17 @@ __device__ __forceinline__ float block_sum(float v, float* scratch) {
   return r;
 }
 
-// Thread t owns output dim t % D and partitions k = t / D, t / D + G, ... with
-// G = 256 / D groups; four independent accumulators keep four partial rows in
-// flight, and the G group sums meet in LDS.
+// Thread t owns the four output dims 4*(t % R) .. +3 (one 16-byte load per
+// partition row, R = D / 4 threads per row) and partitions k = t / R,
+// t / R + G, ... with G = 256 / R groups; four independent accumulators keep
+// four partition rows in flight per thread, and the G group sums meet in LDS.
 template <typename Tr, int D>
 __global__ __launch_bounds__(kReduceThreads) void lse_reduce_kernel(ReduceArgs a) {
-  constexpr int G = kReduceThreads / D;
+  constexpr int R = D / 4;
+  constexpr int G = kReduceThreads / R;
   extern __shared__ float sm_w[];  // [num_partitions] weights
   __shared__ float sm_red[kReduceThreads / kWave];
-  __shared__ float sm_part[G][D];
+  __shared__ __attribute__((aligned(16))) float sm_part[G][D];
   using S = typename Tr::storage;
 
   const int h = blockIdx.x;
@@ -66,7 +68,7 @@ __global__ __launch_bounds__(kReduceThreads) void lse_reduce_kernel(ReduceArgs a
   const size_t base = (size_t(b) * a.H + h) * a.num_partitions;
   const float* m = a.ws_m + base;
   const float* l = a.ws_l + base;
-  const float* o = a.ws_o + base * D;
+  const float4* o = reinterpret_cast<const float4*>(a.ws_o + base * D);
 
   float mx = -INFINITY;
   for (int k = threadIdx.x; k < nparts; k += kReduceThreads) mx = fmaxf(mx, m[k]);
@@ -80,23 +82,38 @@ __global__ __launch_bounds__(kReduceThreads) void lse_reduce_kernel(ReduceArgs a
   }
   const float total = block_sum(tot, sm_red);  // its barriers also publish sm_w
 
-  const int x = threadIdx.x % D;
-  const int kg = threadIdx.x / D;
-  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  const int xv = threadIdx.x % R;
+  const int kg = threadIdx.x / R;
+  float4 acc[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) acc[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+  auto fma4 = [](float w, const float4 v, float4& c) {
+    c.x = fmaf(w, v.x, c.x);
+    c.y = fmaf(w, v.y, c.y);
+    c.z = fmaf(w, v.z, c.z);
+    c.w = fmaf(w, v.w, c.w);
+  };
   int k = kg;
   for (; k + 3 * G < nparts; k += 4 * G) {
+    float4 v[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-      acc[u] = fmaf(sm_w[k + u * G], o[size_t(k + u * G) * D + x], acc[u]);
+    for (int u = 0; u < 4; ++u) v[u] = o[size_t(k + u * G) * R + xv];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) fma4(sm_w[k + u * G], v[u], acc[u]);
   }
-  for (; k < nparts; k += G) acc[0] = fmaf(sm_w[k], o[size_t(k) * D + x], acc[0]);
-  sm_part[kg][x] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+  for (; k < nparts; k += G) fma4(sm_w[k], o[size_t(k) * R + xv], acc[0]);
+  float4 r;
+  r.x = (acc[0].x + acc[1].x) + (acc[2].x + acc[3].x);
+  r.y = (acc[0].y + acc[1].y) + (acc[2].y + acc[3].y);
+  r.z = (acc[0].z + acc[1].z) + (acc[2].z + acc[3].z);
+  r.w = (acc[0].w + acc[1].w) + (acc[2].w + acc[3].w);
+  *reinterpret_cast<float4*>(&sm_part[kg][4 * xv]) = r;
   __syncthreads();
-  if (kg == 0) {
-    float r = 0.f;
+  for (int x = threadIdx.x; x < D; x += kReduceThreads) {
+    float sum = 0.f;
 #pragma unroll
-    for (int g = 0; g < G; ++g) r += sm_part[g][x];
-    out[x] = Tr::from_f32(r / total);
+    for (int g = 0; g < G; ++g) sum += sm_part[g][x];
+    out[x] = Tr::from_f32(sum / total);
   }
 }
 
