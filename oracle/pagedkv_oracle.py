@@ -17,6 +17,11 @@ Pages cited (titles as the pages give them):
          (naive incremental decoding, the step() function).
   [SRV]  "Ch.29 Building a Production LLM Serving Stack": 29.1.2 (block
          accounting worked example), 29.2.1 (attention intensity).
+  [FDE9] "Forward Deployed Engineering Interview", Ch.2 section 9 (shrinking
+         the cache: an fp8_e4m3 cache, available on ROCm, halves every row;
+         scales are per tensor) and the annotated serving configuration of the
+         same chapter (--kv-cache-dtype fp8: every scale is 1.0 without
+         calibration).
 
 What the oracle computes is the plain definition: decode attention over a
 paged cache equals ordinary softmax attention of one query over its
@@ -33,9 +38,15 @@ Readings taken where the pages are silent (each listed in the design notes):
     the one the C ABI documents, restated here independently:
         K element (p, h, t, x) at (((p*H_kv + h)*(d/X) + x//X)*16 + t)*X + x%X
         V element (p, h, t, x) at ((p*H_kv + h)*d + x)*16 + t
-    with X = 16 bytes / element size (8 for bf16, 4 for fp32).
+    with X = 16 bytes / element size (8 for bf16, 4 for fp32, 16 for fp8).
   * ctx <= 0 gives an all-zero output (no token to attend to).
   * split-KV partitions are logical token ranges [k*P, (k+1)*P).
+  * fp8 cache ([FDE9]): elements are OCP E4M3 codes (the format ROCm's
+    fp8_e4m3 names); a cached value is code value * per-tensor scale.  The
+    write stores the nearest E4M3 value of x / scale, the division done in
+    float32, ties to the even code; magnitudes beyond 448 (the largest finite
+    E4M3 value; the format has no infinities) store +-448, and NaN stores
+    sign | 0x7F.  Queries and outputs stay bf16.
 
 Parity status: every function below is pinned by tests/test_oracle_pins.py
 against printed page values, closed forms, library routines or invariants.
@@ -50,7 +61,12 @@ import numpy as np
 __all__ = [
     "BLOCK",
     "bits_to_f64",
+    "act_dtype",
     "chunk_elems",
+    "E4M3_MAX",
+    "e4m3_value",
+    "e4m3_encode",
+    "e4m3_quantize",
     "k_offset",
     "v_offset",
     "blocks_needed",
@@ -82,16 +98,77 @@ def bits_to_f64(bits: np.ndarray, dtype: str) -> np.ndarray:
     that float32 exactly; float32 widens to float64 exactly.
     """
     bits = np.asarray(bits)
-    if dtype == "bf16":
-        return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
-    if dtype == "f32":
-        return bits.astype(np.uint32).view(np.float32).astype(np.float64)
+    with np.errstate(invalid="ignore"):  # NaN patterns widen to NaN
+        if dtype == "bf16":
+            return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+        if dtype == "f32":
+            return bits.astype(np.uint32).view(np.float32).astype(np.float64)
+    if dtype == "fp8":
+        return e4m3_value(bits)
     raise ValueError(dtype)
+
+
+def act_dtype(dtype: str) -> str:
+    """Element type of query, output and the rows handed to the cache write
+    for a cache of element type `dtype` (an fp8 cache serves bf16 activations)."""
+    return "bf16" if dtype == "fp8" else dtype
 
 
 def chunk_elems(dtype: str) -> int:
     """Elements per 16-byte chunk of the K layout."""
-    return {"bf16": 8, "f32": 4}[dtype]
+    return {"bf16": 8, "f32": 4, "fp8": 16}[dtype]
+
+
+# --------------------------------------------------------------------------
+# fp8 (E4M3) cache elements, [FDE9]
+# --------------------------------------------------------------------------
+E4M3_MAX = 448.0  # largest finite E4M3 magnitude: (1 + 6/8) * 2**8
+
+
+def e4m3_value(codes) -> np.ndarray:
+    """Float64 value of E4M3 codes.
+
+    The format: one sign bit, four exponent bits with bias 7, three mantissa
+    bits.  Exponent field 0 is subnormal, value m/8 * 2**-6; otherwise the value
+    is (1 + m/8) * 2**(e - 7).  Exponent 15 with mantissa 7 is NaN (no
+    infinities), so the largest finite magnitude is 448.
+    """
+    c = np.asarray(codes).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    mag = np.where((e == 15) & (c & 0x7 == 7), np.nan, mag)
+    return sign * mag
+
+
+def e4m3_encode(x) -> np.ndarray:
+    """E4M3 codes of float32 values: the nearest finite E4M3 value, a tie going
+    to the code whose mantissa is even; magnitudes beyond 448 give +-448; NaN
+    gives sign | 0x7F; the sign of -0.0 is kept."""
+    with np.errstate(invalid="ignore", over="ignore"):
+        x = np.asarray(x, dtype=np.float32).astype(np.float64)
+    nan = np.isnan(x)
+    a = np.where(nan, 0.0, np.minimum(np.abs(x), E4M3_MAX))
+    table = e4m3_value(np.arange(0x7F))       # codes 0..126: 0 .. 448, increasing
+    hi = np.minimum(np.searchsorted(table, a, side="left"), 0x7E)
+    lo = np.maximum(hi - 1, 0)
+    d_lo = a - table[lo]
+    d_hi = table[hi] - a
+    code = np.where((d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0)), hi, lo)
+    neg = np.signbit(x)
+    code = np.where(neg, code | 0x80, code)
+    code = np.where(nan, np.where(neg, 0xFF, 0x7F), code)
+    return code.astype(np.uint8)
+
+
+def e4m3_quantize(bits: np.ndarray, dtype: str, scale: float) -> np.ndarray:
+    """Codes of stored activation values (bit patterns of `dtype`) under a
+    per-tensor scale: e4m3_encode(x / scale), the division in float32."""
+    x = bits_to_f64(bits, dtype).astype(np.float32)   # exact: bf16/f32 values
+    with np.errstate(invalid="ignore", divide="ignore", over="ignore"):
+        q = x / np.float32(scale)
+    return e4m3_encode(q)
 
 
 # --------------------------------------------------------------------------
@@ -147,19 +224,25 @@ def slot_mapping(block_tables: np.ndarray, context_lens: np.ndarray) -> np.ndarr
 # --------------------------------------------------------------------------
 def reshape_and_cache(k_pool: np.ndarray, v_pool: np.ndarray, key: np.ndarray,
                       value: np.ndarray, slots: np.ndarray, H_kv: int, d: int,
-                      dtype: str, num_blocks: int) -> Tuple[np.ndarray, np.ndarray]:
+                      dtype: str, num_blocks: int, k_scale: float = 1.0,
+                      v_scale: float = 1.0) -> Tuple[np.ndarray, np.ndarray]:
     """Write each token's K and V rows into its slot; return new pools.
 
     [WB] step(): the cache append, K and V grow by one row per token and old
     rows are never recomputed; [FDE] section 8 append(): the token goes into the
-    last block of the table.  A bit copy: -0.0 and NaN payloads survive.  A
-    negative slot is skipped.  Two tokens naming one slot in one call would race
-    on a GPU, so the oracle refuses them, as it refuses slots past the pool.
+    last block of the table.  For bf16/fp32 caches a bit copy: -0.0 and NaN
+    payloads survive.  For an fp8 cache the rows are bf16 and each element is
+    stored as e4m3_quantize(x, k_scale or v_scale) ([FDE9]).  A negative slot is
+    skipped.  Two tokens naming one slot in one call would race on a GPU, so the
+    oracle refuses them, as it refuses slots past the pool.
     """
     k_pool = np.array(k_pool, copy=True)
     v_pool = np.array(v_pool, copy=True)
     key = np.asarray(key).reshape(-1, H_kv, d)
     value = np.asarray(value).reshape(-1, H_kv, d)
+    if dtype == "fp8":
+        key = e4m3_quantize(key, act_dtype(dtype), k_scale)
+        value = e4m3_quantize(value, act_dtype(dtype), v_scale)
     slots = np.asarray(slots, dtype=np.int64)
     live = [int(s) for s in slots if s >= 0]
     if len(set(live)) != len(live):
@@ -182,12 +265,14 @@ def reshape_and_cache(k_pool: np.ndarray, v_pool: np.ndarray, key: np.ndarray,
 # de-paging and attention
 # --------------------------------------------------------------------------
 def gather_sequence(k_pool: np.ndarray, v_pool: np.ndarray, table_row: np.ndarray,
-                    ctx: int, kvh: int, H_kv: int, d: int, dtype: str
+                    ctx: int, kvh: int, H_kv: int, d: int, dtype: str,
+                    k_scale: float = 1.0, v_scale: float = 1.0
                     ) -> Tuple[np.ndarray, np.ndarray]:
     """Contiguous float64 K, V [ctx, d] of one sequence and KV head.
 
     Token t is read from block table_row[t // 16], slot t % 16 ([QA] Q1).  Only
     the first ceil(ctx / 16) table entries and the first ctx tokens are read.
+    An fp8 cache's values are code value * scale ([FDE9]; exact in float64).
     """
     t = np.arange(int(ctx), dtype=np.int64)
     if t.size == 0:
@@ -196,11 +281,17 @@ def gather_sequence(k_pool: np.ndarray, v_pool: np.ndarray, table_row: np.ndarra
     xs = np.arange(d, dtype=np.int64)
     ko = k_offset(blocks[:, None], kvh, (t % BLOCK)[:, None], xs[None, :], H_kv, d, dtype)
     vo = v_offset(blocks[:, None], kvh, (t % BLOCK)[:, None], xs[None, :], H_kv, d, dtype)
-    return bits_to_f64(k_pool[ko], dtype), bits_to_f64(v_pool[vo], dtype)
+    K = bits_to_f64(k_pool[ko], dtype)
+    V = bits_to_f64(v_pool[vo], dtype)
+    if dtype == "fp8":
+        K = K * float(np.float32(k_scale))
+        V = V * float(np.float32(v_scale))
+    return K, V
 
 
 def decode_sequence(k_pool, v_pool, q_b: np.ndarray, table_row, ctx: int,
-                    H: int, H_kv: int, d: int, dtype: str, scale: float) -> np.ndarray:
+                    H: int, H_kv: int, d: int, dtype: str, scale: float,
+                    k_scale: float = 1.0, v_scale: float = 1.0) -> np.ndarray:
     """Output [H, d] of one sequence: softmax(scale * K q_h) V per query head.
 
     [WB] step(): attn = softmax(K @ q / sqrt(d)); ctx = attn @ V, over every
@@ -210,9 +301,10 @@ def decode_sequence(k_pool, v_pool, q_b: np.ndarray, table_row, ctx: int,
     out = np.zeros((H, d))
     if ctx <= 0:
         return out
-    q = bits_to_f64(q_b, dtype).reshape(H, d)
+    q = bits_to_f64(q_b, act_dtype(dtype)).reshape(H, d)
     for kvh in range(H_kv):
-        K, V = gather_sequence(k_pool, v_pool, table_row, ctx, kvh, H_kv, d, dtype)
+        K, V = gather_sequence(k_pool, v_pool, table_row, ctx, kvh, H_kv, d, dtype,
+                               k_scale, v_scale)
         for h in range(kvh * g, (kvh + 1) * g):
             s = scale * (K @ q[h])
             p = np.exp(s - s.max())
@@ -222,18 +314,20 @@ def decode_sequence(k_pool, v_pool, q_b: np.ndarray, table_row, ctx: int,
 
 def decode(k_pool, v_pool, q: np.ndarray, block_tables: np.ndarray,
            context_lens: np.ndarray, H: int, H_kv: int, d: int, dtype: str,
-           scale: float) -> np.ndarray:
+           scale: float, k_scale: float = 1.0, v_scale: float = 1.0) -> np.ndarray:
     """Float64 decode-attention output [B, H, d] for a whole batch."""
     B = len(context_lens)
     out = np.zeros((B, H, d))
     for b in range(B):
         out[b] = decode_sequence(k_pool, v_pool, q[b], block_tables[b],
-                                 int(context_lens[b]), H, H_kv, d, dtype, scale)
+                                 int(context_lens[b]), H, H_kv, d, dtype, scale,
+                                 k_scale, v_scale)
     return out
 
 
 def partials(k_pool, v_pool, q, block_tables, context_lens, H: int, H_kv: int,
-             d: int, dtype: str, scale: float, partition_size: int):
+             d: int, dtype: str, scale: float, partition_size: int,
+             k_scale: float = 1.0, v_scale: float = 1.0):
     """Per-partition (o, m, l) of split-KV decode.
 
     Partition k of a sequence covers logical tokens [k*P, min((k+1)*P, ctx)).
@@ -256,9 +350,10 @@ def partials(k_pool, v_pool, q, block_tables, context_lens, H: int, H_kv: int,
         n = int(context_lens[b])
         if n <= 0:
             continue
-        qb = bits_to_f64(q[b], dtype).reshape(H, d)
+        qb = bits_to_f64(q[b], act_dtype(dtype)).reshape(H, d)
         for kvh in range(H_kv):
-            K, V = gather_sequence(k_pool, v_pool, block_tables[b], n, kvh, H_kv, d, dtype)
+            K, V = gather_sequence(k_pool, v_pool, block_tables[b], n, kvh, H_kv, d, dtype,
+                                   k_scale, v_scale)
             for h in range(kvh * g, (kvh + 1) * g):
                 s = scale * (K @ qb[h])
                 for k in range(int(counts[b])):

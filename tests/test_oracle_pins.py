@@ -419,14 +419,14 @@ def test_planted_mistakes_are_caught(monkeypatch):
     real_gather = O.pagedkv_oracle.gather_sequence
 
     # (1) drop the newest token (context length read as exclusive)
-    def short(kp, vp, row, ctx, kvh, H_kv, d, dt):
-        return real_gather(kp, vp, row, ctx - 1, kvh, H_kv, d, dt)
+    def short(kp, vp, row, ctx, kvh, H_kv, d, dt, *scales):
+        return real_gather(kp, vp, row, ctx - 1, kvh, H_kv, d, dt, *scales)
     monkeypatch.setattr(O.pagedkv_oracle, "gather_sequence", short)
     assert not np.allclose(run(), ref, rtol=1e-6)
     # (2) wrong KV head for a query head (h % H_kv instead of h // g)
     monkeypatch.setattr(O.pagedkv_oracle, "gather_sequence",
-                        lambda kp, vp, row, ctx, kvh, H_kv, d, dt:
-                        real_gather(kp, vp, row, ctx, (kvh + 1) % H_kv, H_kv, d, dt))
+                        lambda kp, vp, row, ctx, kvh, H_kv, d, dt, *scales:
+                        real_gather(kp, vp, row, ctx, (kvh + 1) % H_kv, H_kv, d, dt, *scales))
     assert not np.allclose(run(), ref, rtol=1e-6)
     monkeypatch.setattr(O.pagedkv_oracle, "gather_sequence", real_gather)
     # (3) transposed K/V layout

@@ -54,3 +54,22 @@ def test_shared_prefix_recipe():
     private = w.block_tables[:, 64:][w.block_tables[:, 64:] != W.TABLE_SENTINEL]
     assert len(set(private.tolist())) == len(private)      # private blocks not shared
     assert used.max() < w.num_blocks
+
+
+def test_fp8_workload_shares_shapes_and_draws_valid_codes():
+    w8 = W.make_workload(4, kv_dtype="fp8")
+    w = W.make_workload(4)
+    assert w8.kv_dtype == "fp8" and w8.dtype == "bf16" and w8.name.endswith("-fp8kv")
+    assert w8.k_pool.dtype == np.uint8 and w8.kv_elem_bytes == 1
+    # same lengths, tables and activations as the bf16 workload
+    np.testing.assert_array_equal(w8.block_tables, w.block_tables)
+    np.testing.assert_array_equal(w8.steps[0].context_lens, w.steps[0].context_lens)
+    np.testing.assert_array_equal(w8.steps[0].q, w.steps[0].q)
+    np.testing.assert_array_equal(w8.steps[0].new_k, w.steps[0].new_k)
+    # the byte recipe: magnitude codes 0x00..0x3F with either sign, never NaN
+    mag = w8.k_pool & 0x7F
+    assert int(mag.max()) == W.FP8_MAG_CODES - 1
+    assert set(np.unique(w8.v_pool & 0x80).tolist()) == {0, 0x80}
+    assert w8.k_scale == 1.0 and w8.v_scale == 1.0
+    with pytest.raises(ValueError):
+        W.make_workload(1, kv_dtype="fp8")

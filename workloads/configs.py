@@ -37,6 +37,8 @@ def bits_dtype(dtype: str):
         return np.uint16
     if dtype == "f32":
         return np.uint32
+    if dtype == "fp8":
+        return np.uint8
     raise ValueError(f"unsupported dtype {dtype!r}")
 
 
@@ -71,9 +73,15 @@ def _normal_bits(rng: np.random.Generator, n: int, dtype: str,
 POOL_CHUNK = 1 << 22  # elements per independently keyed stream of a pool fill
 
 
-def _pool_bits(seed: int, tag: int, n: int, dtype: str, threads: int = 0) -> np.ndarray:
-    """A pool's n N(0,1) values, drawn in fixed chunks of POOL_CHUNK elements.
+FP8_MAG_CODES = 0x40  # fp8 pool bytes: magnitude codes 0x00..0x3F
 
+
+def _pool_bits(seed: int, tag: int, n: int, dtype: str, threads: int = 0) -> np.ndarray:
+    """A pool's n values, drawn in fixed chunks of POOL_CHUNK elements.
+
+    bf16 / f32: N(0,1) values.  fp8: bytes with a random sign bit and a
+    magnitude code drawn uniformly from 0x00..0x3F (in the E4M3 format those
+    are the values 0 to 1.875, spaced logarithmically; no NaN code is drawn).
     Chunk i comes from its own PCG64 stream keyed by SeedSequence([seed, tag, i]),
     so the values do not depend on how many threads fill them.
     """
@@ -84,6 +92,10 @@ def _pool_bits(seed: int, tag: int, n: int, dtype: str, threads: int = 0) -> np.
         lo = i * POOL_CHUNK
         m = min(POOL_CHUNK, n - lo)
         rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, tag, i])))
+        if dtype == "fp8":
+            r = rng.integers(0, 2 * FP8_MAG_CODES, size=m, dtype=np.uint8)
+            out[lo:lo + m] = (r & np.uint8(FP8_MAG_CODES - 1)) | ((r & np.uint8(FP8_MAG_CODES)) << np.uint8(1))
+            return
         buf = rng.standard_normal(m, dtype=np.float32)
         out[lo:lo + m] = f32_to_bf16_bits(buf) if dtype == "bf16" else buf.view(np.uint32)
 
@@ -113,7 +125,7 @@ class DecodeStep:
 @dataclass
 class Workload:
     name: str
-    dtype: str                    # "f32" | "bf16"
+    dtype: str                    # activations (q, out, new rows): "f32" | "bf16"
     B: int
     H: int
     H_kv: int
@@ -128,10 +140,21 @@ class Workload:
     steps: List[DecodeStep] = field(default_factory=list)
     block_size: int = BLOCK_SIZE
     seed: int = 0
+    kv_dtype: Optional[str] = None  # cache elements: as dtype, or "fp8" (E4M3 codes)
+    k_scale: float = 1.0            # per-tensor scales of an fp8 cache
+    v_scale: float = 1.0
+
+    def __post_init__(self):
+        if self.kv_dtype is None:
+            self.kv_dtype = self.dtype
 
     @property
     def elem_bytes(self) -> int:
         return 2 if self.dtype == "bf16" else 4
+
+    @property
+    def kv_elem_bytes(self) -> int:
+        return 1 if self.kv_dtype == "fp8" else self.elem_bytes
 
     @property
     def group(self) -> int:
@@ -154,7 +177,8 @@ def scattered_workload(name: str, dtype: str, B: int, H: int, H_kv: int, d: int,
                        context_lens: Sequence[int], seed: int, rng=None,
                        pool_factor: float = 1.25, max_nb: Optional[int] = None,
                        partition_size: int = 0, num_blocks: Optional[int] = None,
-                       ) -> Workload:
+                       kv_dtype: Optional[str] = None, k_scale: float = 1.0,
+                       v_scale: float = 1.0) -> Workload:
     """One decode step over sequences whose blocks are scattered at random.
 
     The pool holds ceil(pool_factor * total blocks) blocks (or num_blocks); the
@@ -181,15 +205,23 @@ def scattered_workload(name: str, dtype: str, B: int, H: int, H_kv: int, d: int,
         pos += nb[b]
     q = _normal_bits(rng, B * H * d, dtype).reshape(B, H, d)
     n_pool = num_blocks * H_kv * BLOCK_SIZE * d
-    k_pool = _pool_bits(seed, 1, n_pool, dtype)
-    v_pool = _pool_bits(seed, 2, n_pool, dtype)
+    kv_dtype = kv_dtype or dtype
+    k_pool = _pool_bits(seed, 1, n_pool, kv_dtype)
+    v_pool = _pool_bits(seed, 2, n_pool, kv_dtype)
     new_k = _normal_bits(rng, B * H_kv * d, dtype).reshape(B, H_kv, d)
     new_v = _normal_bits(rng, B * H_kv * d, dtype).reshape(B, H_kv, d)
     step = DecodeStep(context_lens=ctx.astype(np.int32), q=q, new_k=new_k, new_v=new_v)
     return Workload(name=name, dtype=dtype, B=B, H=H, H_kv=H_kv, d=d,
                     num_blocks=num_blocks, max_nb=max_nb, scale=1.0 / math.sqrt(d),
                     partition_size=partition_size, block_tables=tables,
-                    k_pool=k_pool, v_pool=v_pool, steps=[step], seed=seed)
+                    k_pool=k_pool, v_pool=v_pool, steps=[step], seed=seed,
+                    kv_dtype=kv_dtype, k_scale=k_scale, v_scale=v_scale)
+
+
+def _name(config: int, kv_dtype: str) -> str:
+    """Workload name; an fp8-cache variant of a bf16 workload says so."""
+    base = CONFIG_NAMES[config]
+    return base if kv_dtype != "fp8" else base.replace("-bf16", "") + "-fp8kv"
 
 
 def _config1(seed: int) -> Workload:
@@ -201,27 +233,29 @@ def _config1(seed: int) -> Workload:
                               context_lens=ctx, seed=seed, rng=rng, num_blocks=16)
 
 
-def _config2(seed: int) -> Workload:
+def _config2(seed: int, kv_dtype: str = "bf16") -> Workload:
     rng = np.random.Generator(np.random.PCG64(seed))
     ctx = rng.integers(512, 2048, size=64, endpoint=True)
-    return scattered_workload(CONFIG_NAMES[2], "bf16", B=64, H=32, H_kv=32, d=128,
-                              context_lens=ctx, seed=seed, rng=rng, max_nb=128)
+    return scattered_workload(_name(2, kv_dtype), "bf16", B=64, H=32, H_kv=32, d=128,
+                              context_lens=ctx, seed=seed, rng=rng, max_nb=128,
+                              kv_dtype=kv_dtype)
 
 
-def _config3(seed: int) -> Workload:
+def _config3(seed: int, kv_dtype: str = "bf16") -> Workload:
     rng = np.random.Generator(np.random.PCG64(seed))
     draw = rng.lognormal(mean=math.log(1800.0), sigma=1.0, size=256)
     ctx = np.clip(np.rint(draw), 64, 8192).astype(np.int64)
-    return scattered_workload(CONFIG_NAMES[3], "bf16", B=256, H=64, H_kv=8, d=128,
-                              context_lens=ctx, seed=seed, rng=rng, max_nb=512)
+    return scattered_workload(_name(3, kv_dtype), "bf16", B=256, H=64, H_kv=8, d=128,
+                              context_lens=ctx, seed=seed, rng=rng, max_nb=512,
+                              kv_dtype=kv_dtype)
 
 
-def _config4(seed: int) -> Workload:
+def _config4(seed: int, kv_dtype: str = "bf16") -> Workload:
     rng = np.random.Generator(np.random.PCG64(seed))
     ctx = [100000, 65536, 32768, 4096, 2048, 1024, 300, 17]
-    return scattered_workload(CONFIG_NAMES[4], "bf16", B=8, H=32, H_kv=8, d=128,
+    return scattered_workload(_name(4, kv_dtype), "bf16", B=8, H=32, H_kv=8, d=128,
                               context_lens=ctx, seed=seed, rng=rng, max_nb=6250,
-                              partition_size=512)
+                              partition_size=512, kv_dtype=kv_dtype)
 
 
 SHARED_PREFIX_BLOCKS = 64
@@ -232,7 +266,7 @@ def shared_prefix_workload(seed: int, B: int = 128, H: int = 32, H_kv: int = 8,
                            d: int = 128, steps: int = SHARED_PREFIX_STEPS,
                            prefix_blocks: int = SHARED_PREFIX_BLOCKS,
                            private_range=(16, 300), name: Optional[str] = None,
-                           ) -> Workload:
+                           kv_dtype: str = "bf16") -> Workload:
     """Continuous decode over a shared prefix.
 
     Every sequence's table starts with the same `prefix_blocks` physical blocks,
@@ -268,30 +302,40 @@ def shared_prefix_workload(seed: int, B: int = 128, H: int = 32, H_kv: int = 8,
     dtype = "bf16"
     n_pool = num_blocks * H_kv * BLOCK_SIZE * d
     qs = [_normal_bits(rng, B * H * d, dtype).reshape(B, H, d) for _ in range(steps)]
-    k_pool = _pool_bits(seed, 1, n_pool, dtype)
-    v_pool = _pool_bits(seed, 2, n_pool, dtype)
+    k_pool = _pool_bits(seed, 1, n_pool, kv_dtype)
+    v_pool = _pool_bits(seed, 2, n_pool, kv_dtype)
     step_list = []
     for s in range(steps):
         nk = _normal_bits(rng, B * H_kv * d, dtype).reshape(B, H_kv, d)
         nv = _normal_bits(rng, B * H_kv * d, dtype).reshape(B, H_kv, d)
         step_list.append(DecodeStep(context_lens=ctx_per_step[s], q=qs[s], new_k=nk, new_v=nv))
-    return Workload(name=name or CONFIG_NAMES[5], dtype=dtype, B=B, H=H, H_kv=H_kv, d=d,
+    return Workload(name=name or _name(5, kv_dtype), dtype=dtype, B=B, H=H, H_kv=H_kv, d=d,
                     num_blocks=num_blocks, max_nb=max_nb, scale=1.0 / math.sqrt(d),
                     partition_size=0, block_tables=tables, k_pool=k_pool, v_pool=v_pool,
-                    steps=step_list, seed=seed)
+                    steps=step_list, seed=seed, kv_dtype=kv_dtype)
 
 
-def make_workload(config: int, seed: Optional[int] = None) -> Workload:
-    """Build workload `config` (1..5) with its default seed (= config number)."""
+def make_workload(config: int, seed: Optional[int] = None, kv_dtype: str = "") -> Workload:
+    """Build workload `config` (1..5) with its default seed (= config number).
+
+    kv_dtype "fp8" gives the same shapes, lengths, tables and activations with an
+    fp8 cache (configs 2..5; its pool bytes follow the fp8 recipe of _pool_bits,
+    scales 1.0).
+    """
     seed = config if seed is None else seed
+    if kv_dtype and kv_dtype not in ("fp8", "bf16", "f32"):
+        raise ValueError(f"unsupported kv_dtype {kv_dtype!r}")
     if config == 1:
+        if kv_dtype == "fp8":
+            raise ValueError("workload 1 is float32; an fp8 cache serves bf16 activations")
         return _config1(seed)
+    kv = "fp8" if kv_dtype == "fp8" else "bf16"
     if config == 2:
-        return _config2(seed)
+        return _config2(seed, kv)
     if config == 3:
-        return _config3(seed)
+        return _config3(seed, kv)
     if config == 4:
-        return _config4(seed)
+        return _config4(seed, kv)
     if config == 5:
-        return shared_prefix_workload(seed)
+        return shared_prefix_workload(seed, kv_dtype=kv)
     raise ValueError(f"no workload {config}")
