@@ -60,6 +60,9 @@ def parse_args(argv=None):
     ap.add_argument("--config", type=int, default=2, help="workload 1..5 (default 2: the headline)")
     ap.add_argument("--partition", type=int, default=None,
                     help="split-KV partition size in tokens (0 = single pass)")
+    ap.add_argument("--kv-dtype", default="bf16", choices=["bf16", "fp8"],
+                    help="cache element type: bf16 (the workloads as configured) or fp8 "
+                         "(E4M3 codes, scales 1.0, bf16 activations)")
     ap.add_argument("--cold", action="store_true",
                     help="evict the caches before every step and time steps one by one")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -87,14 +90,15 @@ def kernel_source_hash() -> str:
 
 def step_bytes(w, step) -> dict:
     """Algorithmic bytes of one step (each byte the method must move, once)."""
-    e = w.elem_bytes
+    e = w.elem_bytes            # query, output, rows handed to the write
+    ec = w.kv_elem_bytes        # cache elements
     ctx = step.context_lens.astype(np.int64)
     ctx = np.maximum(ctx, 0)
     nb = (ctx + 15) // 16
-    kv = int(ctx.sum()) * w.H_kv * w.d * 2 * e
+    kv = int(ctx.sum()) * w.H_kv * w.d * 2 * ec
     qo = 2 * w.B * w.H * w.d * e
     decode = kv + qo + 4 * int(nb.sum()) + 4 * w.B
-    write = 2 * (2 * w.B * w.H_kv * w.d * e)               # K,V rows in and out
+    write = 2 * w.B * w.H_kv * w.d * (e + ec)              # K,V rows in, cache elements out
     slots = 4 * w.B + 4 * w.B + 8 * w.B                    # lengths, table entries, slots out
     return {"decode": decode, "kv": kv, "step": decode + write + slots}
 
@@ -135,7 +139,7 @@ def _cpu_prepare(w):
     step = w.steps[0]
     slots = O.slot_mapping(w.block_tables, step.context_lens)
     kp, vp = O.reshape_and_cache(w.k_pool, w.v_pool, step.new_k, step.new_v, slots, w.H_kv, w.d,
-                                 w.dtype, w.num_blocks)
+                                 w.kv_dtype, w.num_blocks, w.k_scale, w.v_scale)
     _CPU.update(w=w, kp=kp, vp=vp)
 
 
@@ -144,7 +148,8 @@ def _cpu_one(b: int) -> np.ndarray:
     w = _CPU["w"]
     step = w.steps[0]
     return O.decode_sequence(_CPU["kp"], _CPU["vp"], step.q[b], w.block_tables[b],
-                             int(step.context_lens[b]), w.H, w.H_kv, w.d, w.dtype, w.scale)
+                             int(step.context_lens[b]), w.H, w.H_kv, w.d, w.kv_dtype, w.scale,
+                             w.k_scale, w.v_scale)
 
 
 def _cpu_worker(args):
@@ -278,9 +283,9 @@ def main(argv=None) -> int:
 
     from workloads import configs as W
     t0 = time.time()
-    w = W.make_workload(args.config)
+    w = W.make_workload(args.config, kv_dtype=args.kv_dtype if args.kv_dtype != "bf16" else "")
     part = DEFAULT_PARTITION[args.config] if args.partition is None else args.partition
-    print(f"[bench] workload {w.name}: B={w.B} H={w.H} H_kv={w.H_kv} d={w.d} pool={w.num_blocks} "
+    print(f"[bench] workload {w.name} ({w.kv_dtype} cache): B={w.B} H={w.H} H_kv={w.H_kv} d={w.d} pool={w.num_blocks} "
           f"blocks, generated in {time.time() - t0:.1f}s; partition={part}", file=sys.stderr,
           flush=True)
 
@@ -298,12 +303,14 @@ def main(argv=None) -> int:
 
     import paged_kv_cache_33_amd as P
 
-    view = np.int16 if w.dtype == "bf16" else np.int32
+    views = {np.dtype(np.uint16): np.int16, np.dtype(np.uint32): np.int32}
 
     def dev(a):
-        return torch.from_numpy(np.ascontiguousarray(a).view(view)).cuda()
+        a = np.ascontiguousarray(a)
+        return torch.from_numpy(a.view(views.get(a.dtype, a.dtype))).cuda()
 
-    pool = P.KVPool(dev(w.k_pool), dev(w.v_pool), w.num_blocks, w.H_kv, w.d, w.dtype)
+    pool = P.KVPool(dev(w.k_pool), dev(w.v_pool), w.num_blocks, w.H_kv, w.d, w.kv_dtype,
+                    w.k_scale, w.v_scale)
     tables = torch.from_numpy(w.block_tables).cuda()
     steps_dev = []
     for st in w.steps:
@@ -412,7 +419,7 @@ def main(argv=None) -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": w.dtype,
+        "dtype": w.dtype if w.kv_dtype == w.dtype else f"{w.kv_dtype} cache, {w.dtype} activations",
         "data": "synthetic",
         "config": {
             "workload": w.name,
@@ -425,6 +432,7 @@ def main(argv=None) -> int:
             "max_context_tokens": L_max,
             "partition_size": part,
             "seed": w.seed,
+            "kv_cache": w.kv_dtype,
             "step": ("kv_slot_mapping + reshape_and_cache" if args.unfused else "kv_cache_append")
                     + " + paged_attention_decode" + (" + paged_attention_reduce" if part else ""),
             "caches": "evicted before every step" if args.cold else "warm (steps back to back)",

@@ -18,6 +18,9 @@
  *   - "Anthropic Interview: Design an LLM Inference API with GPU Batching",
  *     4.1/4.2 Data model: a sequence owns a block_table of block ids; blocks
  *     come from a free stack kept by the host.
+ *   - "Forward Deployed Engineering Interview", Ch.2 section 9 (shrinking the
+ *     cache) and its annotated serving configuration: an fp8_e4m3 cache, with
+ *     per-tensor scales (1.0 when uncalibrated), halves the bytes per token.
  *
  * Conventions shared by every call:
  *   - Ownership: the caller allocates and owns every buffer (pool, query,
@@ -39,7 +42,8 @@
  * Pool layout in HBM (one K cache and one V cache, each num_blocks *
  * num_kv_heads * 16 * head_dim elements).  Every (block p, kv head h) tile is
  * 16 * head_dim contiguous elements starting at element (p*H_kv + h)*16*d.
- * Inside a tile, with X = 16 / sizeof(element) (8 for bf16, 4 for fp32):
+ * Inside a tile, with X = 16 / sizeof(element) (8 for bf16, 4 for fp32, 16 for
+ * fp8):
  *   K[p][h][t][x] at (((p*H_kv + h)*(d/X) + x/X)*16 + t)*X + x%X
  *       i.e. the tile is [d/X][16 tokens][X]: the 16 bytes holding dims
  *       x..x+X-1 of one token are contiguous, and the 16 tokens' copies of one
@@ -51,8 +55,18 @@
  * S = K Q^T, V^T as the row operand of O^T = V^T P^T); the same layout keeps
  * every load of the VALU kernel a coalesced 16-byte access.
  *
- * Query and output: [B][H][d], contiguous, same dtype as the pool.  Query head
- * h reads KV head h / (H / H_kv) (contiguous groups).
+ * Query and output: [B][H][d], contiguous, of the pool's activation type: the
+ * pool dtype for KV_F32 / KV_BF16, bf16 for KV_FP8_E4M3.  Query head h reads
+ * KV head h / (H / H_kv) (contiguous groups).
+ *
+ * fp8 pools (KV_FP8_E4M3).  Each cached element is an OCP E4M3 code (1 sign, 4
+ * exponent bits with bias 7, 3 mantissa bits; exponent 15 with mantissa 7 is
+ * NaN; largest finite value 448); the value it stands for is code value * the
+ * pool's k_scale (K) or v_scale (V).  The cache write stores, for a bf16 input
+ * x, the nearest E4M3 value of x / scale (the division in fp32), ties to the
+ * code with an even mantissa; magnitudes beyond 448 store +-448 and NaN stores
+ * sign | 0x7F.  The decode converts codes to bf16 exactly and applies the
+ * scales in fp32.
  */
 #ifndef PAGEDKV_H_
 #define PAGEDKV_H_
@@ -72,21 +86,28 @@ typedef enum {
   KV_ERR_HIP = -4           /* a HIP runtime call failed (message has detail) */
 } kv_status;
 
-typedef enum { KV_F32 = 0, KV_BF16 = 1 } kv_dtype;
+typedef enum {
+  KV_F32 = 0,      /* fp32 cache, fp32 activations                          */
+  KV_BF16 = 1,     /* bf16 cache, bf16 activations                          */
+  KV_FP8_E4M3 = 2  /* E4M3 cache codes with per-tensor scales, bf16 activations */
+} kv_dtype;
 
 typedef struct {
   int32_t num_blocks;    /* physical blocks in the pool, >= 1              */
   int32_t block_size;    /* tokens per block; only 16 is supported          */
   int32_t num_kv_heads;  /* H_kv, >= 1                                      */
   int32_t head_dim;      /* d: 64 or 128                                    */
-  kv_dtype dtype;        /* element type of K, V, query and output          */
+  kv_dtype dtype;        /* cache element type (activations: see above)     */
+  float k_scale;         /* KV_FP8_E4M3: scale of K codes, finite and > 0;  */
+  float v_scale;         /*   of V codes.  Ignored for the other dtypes.    */
 } kv_pool_desc;
 
 typedef struct kv_pool kv_pool; /* opaque host object; borrows the two caches */
 
 /* Bytes of ONE cache (K or V) for this geometry; 0 if the descriptor is
  * invalid.  The pool is num_blocks*H_kv*16*d elements (the KV-cache size
- * formula of the workbook's "The equations" with L = 1, per cache). */
+ * formula of the workbook's "The equations" with L = 1, per cache) of 4, 2 or
+ * 1 byte. */
 size_t kv_pool_bytes(const kv_pool_desc* desc);
 
 /* Wrap two caller-owned device buffers (each kv_pool_bytes(desc) bytes, 16-byte
@@ -109,23 +130,25 @@ kv_status kv_slot_mapping(const int32_t* block_tables, int32_t max_nb,
                           const int32_t* context_lens, int32_t B,
                           int64_t* slot_mapping, void* stream);
 
-/* Cache write: copy token i's K and V rows (key/value: device [N][H_kv][d],
- * pool dtype) into slot s = slot_mapping[i] (device int64 [N]): block s / 16,
- * in-block token s % 16, using the pool layout above.  The workbook's decode
- * step appends the new row before attending; the Q&A page's Q7 stores all K/V
- * of a batch in one pass.  A bit copy: every bit pattern, NaN payloads and
- * -0.0 included, lands unchanged.  s < 0 and s >= num_blocks*16 are skipped.
- * Two tokens naming one slot in one call race (undefined result). */
+/* Cache write: store token i's K and V rows (key/value: device [N][H_kv][d]
+ * of the activation type) into slot s = slot_mapping[i] (device int64 [N]):
+ * block s / 16, in-block token s % 16, using the pool layout above.  The
+ * workbook's decode step appends the new row before attending; the Q&A page's
+ * Q7 stores all K/V of a batch in one pass.  KV_F32 / KV_BF16: a bit copy,
+ * every bit pattern, NaN payloads and -0.0 included, lands unchanged.
+ * KV_FP8_E4M3: each element is stored as its E4M3 code (see above).  s < 0 and
+ * s >= num_blocks*16 are skipped.  Two tokens naming one slot in one call race
+ * (undefined result). */
 kv_status reshape_and_cache(const kv_pool* pool, const void* key, const void* value,
                             const int64_t* slot_mapping, int32_t N, void* stream);
 
 /* Append one new token per sequence: the slot mapping and the cache write in
  * one launch.  For b < B with n = context_lens[b], the new token sits at
  * position n - 1 (context_lens count it, as the workbook's decoder appends the
- * row before attending); its K and V rows (key/value: device [B][H_kv][d],
- * pool dtype) are copied bit for bit into block block_tables[b*max_nb +
- * (n-1)/16], in-block slot (n-1) % 16.  The same result as kv_slot_mapping
- * followed by reshape_and_cache.  slot_mapping: optional device int64 [B]
+ * row before attending); its K and V rows (key/value: device [B][H_kv][d] of
+ * the activation type) are stored, as reshape_and_cache stores them, into block
+ * block_tables[b*max_nb + (n-1)/16], in-block slot (n-1) % 16.  The same result
+ * as kv_slot_mapping followed by reshape_and_cache.  slot_mapping: optional device int64 [B]
  * (NULL = not wanted) receiving each slot, or -1 where nothing was written:
  * n <= 0, n > max_nb*16, or a table entry outside the pool.  The block must not
  * be shared with another sequence of the same call (the host block manager
@@ -146,8 +169,9 @@ size_t paged_attention_workspace_bytes(int32_t B, int32_t H, int32_t head_dim,
  *   out[b][h][:] = softmax_t(scale * q[b][h] . K_b[t]) V_b[t], t < ctx_b,
  * where K_b[t], V_b[t] are read from block block_tables[b*max_nb + t/16],
  * slot t % 16 (ctx_b = context_lens[b], which includes the token written this
- * step).  fp32 accumulation; bf16 outputs are rounded to nearest-even.
- * query: device [B][H][d]; out: device [B][H][d]; block_tables: device int32
+ * step; for an fp8 pool K_b[t] and V_b[t] are code values times the pool's
+ * scales).  fp32 accumulation; bf16 outputs are rounded to nearest-even.
+ * query, out: device [B][H][d] of the activation type; block_tables: device int32
  * [B][max_nb] (entries past ceil(ctx_b/16) are never read); context_lens:
  * device int32 [B]; max_context_len: a host upper bound on every ctx_b.
  * ctx_b <= 0 gives zeros.  ctx_b > max_nb*16, ctx_b > max_context_len (split
@@ -157,8 +181,8 @@ size_t paged_attention_workspace_bytes(int32_t B, int32_t H, int32_t head_dim,
  * workspace (m, l in base-2 units: m = max of scale*log2(e)*q.k, l = sum of
  * 2^(that - m), o = normalised partial output); sequences with a single
  * partition write out directly.  Follow with paged_attention_reduce.
- * H must be a multiple of H_kv.  Kernel choice: H_kv < H with bf16 uses the
- * matrix-core kernel; otherwise the vector-ALU kernel. */
+ * H must be a multiple of H_kv.  Kernel choice: H_kv < H with a bf16 or fp8
+ * pool uses the matrix-core kernel; otherwise the vector-ALU kernel. */
 kv_status paged_attention_decode(const kv_pool* pool, void* out, const void* query,
                                  const int32_t* block_tables, int32_t max_nb,
                                  const int32_t* context_lens, int32_t B, int32_t H,
@@ -173,7 +197,8 @@ kv_status paged_attention_decode(const kv_pool* pool, void* out, const void* que
  * partitions of sequence b; this is Q4's rescale rule applied to whole
  * partitions.  Sequences with one partition are left as the decode wrote
  * them; ctx_b <= 0 gives zeros; ctx_b > max_context_len gives NaN.
- * out: device [B][H][head_dim] of out_dtype. */
+ * out: device [B][H][head_dim] of out_dtype, the pool's activation type
+ * (KV_BF16 for an fp8 pool; KV_FP8_E4M3 is refused). */
 kv_status paged_attention_reduce(void* out, const void* workspace,
                                  const int32_t* context_lens, int32_t B, int32_t H,
                                  int32_t head_dim, int32_t max_context_len,

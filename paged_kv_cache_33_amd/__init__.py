@@ -45,11 +45,19 @@ def _dtype_code(dtype) -> int:
         return _lib.KV_BF16
     if dtype in ("f32", torch.float32, _lib.KV_F32):
         return _lib.KV_F32
+    if dtype in ("fp8", "fp8_e4m3", torch.float8_e4m3fn, _lib.KV_FP8_E4M3):
+        return _lib.KV_FP8_E4M3
     raise ValueError(f"unsupported dtype {dtype!r}")
 
 
 def _elem_size(code: int) -> int:
-    return 2 if code == _lib.KV_BF16 else 4
+    """Bytes of one cache element."""
+    return {_lib.KV_BF16: 2, _lib.KV_F32: 4, _lib.KV_FP8_E4M3: 1}[code]
+
+
+def _act_code(code: int) -> int:
+    """Element type of query, output and cache-write rows for a cache type."""
+    return _lib.KV_BF16 if code == _lib.KV_FP8_E4M3 else code
 
 
 def _stream_handle(stream) -> int:
@@ -81,22 +89,28 @@ def _buf(t: torch.Tensor, name: str, nbytes: Optional[int] = None,
 
 def kv_pool_bytes(num_blocks: int, num_kv_heads: int, head_dim: int, dtype) -> int:
     """Bytes of ONE cache (K or V) of this geometry (0 if unsupported)."""
-    desc = KVPoolDesc(num_blocks, BLOCK_SIZE, num_kv_heads, head_dim, _dtype_code(dtype))
+    desc = KVPoolDesc(num_blocks, BLOCK_SIZE, num_kv_heads, head_dim, _dtype_code(dtype), 1.0, 1.0)
     return int(_lib.load().kv_pool_bytes(C.byref(desc)))
 
 
 class KVPool:
-    """A K cache and a V cache in the documented block layout, owned by torch."""
+    """A K cache and a V cache in the documented block layout, owned by torch.
+
+    dtype "fp8" holds E4M3 codes; k_scale / v_scale are its per-tensor scales
+    (ignored for bf16 / f32 pools)."""
 
     def __init__(self, k_cache: torch.Tensor, v_cache: torch.Tensor, num_blocks: int,
-                 num_kv_heads: int, head_dim: int, dtype):
+                 num_kv_heads: int, head_dim: int, dtype, k_scale: float = 1.0,
+                 v_scale: float = 1.0):
         lib = _lib.load()
         self.dtype_code = _dtype_code(dtype)
         self.num_blocks = int(num_blocks)
         self.num_kv_heads = int(num_kv_heads)
         self.head_dim = int(head_dim)
+        self.k_scale = float(k_scale)
+        self.v_scale = float(v_scale)
         self.desc = KVPoolDesc(self.num_blocks, BLOCK_SIZE, self.num_kv_heads, self.head_dim,
-                               self.dtype_code)
+                               self.dtype_code, self.k_scale, self.v_scale)
         need = int(lib.kv_pool_bytes(C.byref(self.desc)))
         if need == 0:
             _lib.check(lib.kv_pool_create(C.byref(self.desc), None, None, C.byref(C.c_void_p())))
@@ -110,13 +124,14 @@ class KVPool:
 
     @classmethod
     def allocate(cls, num_blocks: int, num_kv_heads: int, head_dim: int, dtype,
-                 device="cuda") -> "KVPool":
+                 device="cuda", k_scale: float = 1.0, v_scale: float = 1.0) -> "KVPool":
         code = _dtype_code(dtype)
-        tdt = torch.bfloat16 if code == _lib.KV_BF16 else torch.float32
+        tdt = {_lib.KV_BF16: torch.bfloat16, _lib.KV_F32: torch.float32,
+               _lib.KV_FP8_E4M3: torch.uint8}[code]
         n = num_blocks * num_kv_heads * BLOCK_SIZE * head_dim
         k = torch.empty(n, dtype=tdt, device=device)
         v = torch.empty(n, dtype=tdt, device=device)
-        return cls(k, v, num_blocks, num_kv_heads, head_dim, dtype)
+        return cls(k, v, num_blocks, num_kv_heads, head_dim, dtype, k_scale, v_scale)
 
     @property
     def handle(self) -> C.c_void_p:
@@ -126,7 +141,17 @@ class KVPool:
 
     @property
     def elem_size(self) -> int:
+        """Bytes of one cache element."""
         return _elem_size(self.dtype_code)
+
+    @property
+    def act_code(self) -> int:
+        return _act_code(self.dtype_code)
+
+    @property
+    def act_size(self) -> int:
+        """Bytes of one query / output / cache-write row element."""
+        return _elem_size(self.act_code)
 
     def close(self) -> None:
         if getattr(self, "_handle", None) is not None:
@@ -140,8 +165,9 @@ class KVPool:
             pass
 
 
-def kv_pool_create(k_cache, v_cache, num_blocks, num_kv_heads, head_dim, dtype) -> KVPool:
-    return KVPool(k_cache, v_cache, num_blocks, num_kv_heads, head_dim, dtype)
+def kv_pool_create(k_cache, v_cache, num_blocks, num_kv_heads, head_dim, dtype,
+                   k_scale: float = 1.0, v_scale: float = 1.0) -> KVPool:
+    return KVPool(k_cache, v_cache, num_blocks, num_kv_heads, head_dim, dtype, k_scale, v_scale)
 
 
 def kv_slot_mapping(block_tables: torch.Tensor, context_lens: torch.Tensor,
@@ -163,9 +189,9 @@ def reshape_and_cache(pool: KVPool, key: torch.Tensor, value: torch.Tensor,
                       slot_mapping: torch.Tensor, stream=None) -> None:
     """Write token i's K/V rows ([N, H_kv, d]) into slot slot_mapping[i]."""
     N = int(slot_mapping.numel())
-    row = pool.num_kv_heads * pool.head_dim * pool.elem_size
-    kp = _buf(key, "key", N * row, elem_size=pool.elem_size)
-    vp = _buf(value, "value", N * row, elem_size=pool.elem_size)
+    row = pool.num_kv_heads * pool.head_dim * pool.act_size
+    kp = _buf(key, "key", N * row, elem_size=pool.act_size)
+    vp = _buf(value, "value", N * row, elem_size=pool.act_size)
     sp = _buf(slot_mapping, "slot_mapping", 8 * N, dtype=torch.int64)
     _lib.check(_lib.load().reshape_and_cache(pool.handle, kp, vp, sp, N, _stream_handle(stream)))
 
@@ -178,9 +204,9 @@ def kv_cache_append(pool: KVPool, key: torch.Tensor, value: torch.Tensor,
     if block_tables.dim() != 2:
         raise ValueError("block_tables must be [B, max_nb]")
     B, max_nb = block_tables.shape
-    row = B * pool.num_kv_heads * pool.head_dim * pool.elem_size
-    kp = _buf(key, "key", row, elem_size=pool.elem_size)
-    vp = _buf(value, "value", row, elem_size=pool.elem_size)
+    row = B * pool.num_kv_heads * pool.head_dim * pool.act_size
+    kp = _buf(key, "key", row, elem_size=pool.act_size)
+    vp = _buf(value, "value", row, elem_size=pool.act_size)
     tp = _buf(block_tables, "block_tables", dtype=torch.int32)
     cp = _buf(context_lens, "context_lens", 4 * B, dtype=torch.int32)
     sp = None if slot_mapping is None else _buf(slot_mapping, "slot_mapping", 8 * B,
@@ -206,7 +232,7 @@ def paged_attention_decode(pool: KVPool, out: torch.Tensor, query: torch.Tensor,
     if block_tables.dim() != 2 or block_tables.shape[0] != B:
         raise ValueError("block_tables must be [B, max_nb]")
     max_nb = int(block_tables.shape[1])
-    es = pool.elem_size
+    es = pool.act_size
     qp = _buf(query, "query", B * H * d * es, elem_size=es)
     op = _buf(out, "out", B * H * d * es, elem_size=es)
     tp = _buf(block_tables, "block_tables", dtype=torch.int32)
@@ -224,11 +250,13 @@ def paged_attention_decode(pool: KVPool, out: torch.Tensor, query: torch.Tensor,
 
 def paged_attention_reduce(out: torch.Tensor, workspace: torch.Tensor, context_lens: torch.Tensor,
                            max_context_len: int, partition_size: int, dtype, stream=None) -> None:
-    """Merge the split partials of paged_attention_decode into out [B, H, d]."""
+    """Merge the split partials of paged_attention_decode into out [B, H, d];
+    dtype is the output's (an fp8 pool's activation type, bf16, is accepted as
+    "fp8" too)."""
     if out.dim() != 3:
         raise ValueError("out must be [B, H, head_dim]")
     B, H, d = out.shape
-    code = _dtype_code(dtype)
+    code = _act_code(_dtype_code(dtype))
     op = _buf(out, "out", B * H * d * _elem_size(code), elem_size=_elem_size(code))
     need = paged_attention_workspace_bytes(B, H, d, max_context_len, partition_size)
     wp = _buf(workspace, "workspace")

@@ -16,6 +16,7 @@ KV_ERR_WORKSPACE = -3
 KV_ERR_HIP = -4
 KV_F32 = 0
 KV_BF16 = 1
+KV_FP8_E4M3 = 2
 
 STATUS_NAMES = {
     KV_OK: "KV_OK",
@@ -48,6 +49,8 @@ class KVPoolDesc(C.Structure):
         ("num_kv_heads", C.c_int32),
         ("head_dim", C.c_int32),
         ("dtype", C.c_int),
+        ("k_scale", C.c_float),
+        ("v_scale", C.c_float),
     ]
 
 

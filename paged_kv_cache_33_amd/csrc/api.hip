@@ -72,15 +72,27 @@ kv_status hip_status(hipError_t e, const char* what) {
   return fail(KV_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-size_t elem_bytes(kv_dtype t) { return t == KV_BF16 ? 2 : 4; }
+size_t elem_bytes(kv_dtype t) { return t == KV_FP8_E4M3 ? 1 : t == KV_BF16 ? 2 : 4; }
+
+pagedkv::Kind kind_of(kv_dtype t) {
+  return t == KV_FP8_E4M3 ? pagedkv::Kind::kFp8
+         : t == KV_BF16   ? pagedkv::Kind::kBf16
+                          : pagedkv::Kind::kF32;
+}
+
+bool positive_finite(float x) { return x > 0.f && x <= 3.4028234663852886e38f; }
 
 // Longest split supported: the reduce keeps one weight per partition in LDS.
 constexpr int64_t kMaxPartitions = 8192;
 
 kv_status check_desc(const kv_pool_desc* d) {
   if (!d) return fail(KV_ERR_INVALID_ARG, "pool descriptor is NULL");
-  if (d->dtype != KV_F32 && d->dtype != KV_BF16)
-    return fail(KV_ERR_UNSUPPORTED, "dtype %d is not supported (f32=0, bf16=1)", int(d->dtype));
+  if (d->dtype != KV_F32 && d->dtype != KV_BF16 && d->dtype != KV_FP8_E4M3)
+    return fail(KV_ERR_UNSUPPORTED, "dtype %d is not supported (f32=0, bf16=1, fp8_e4m3=2)",
+                int(d->dtype));
+  if (d->dtype == KV_FP8_E4M3 && (!positive_finite(d->k_scale) || !positive_finite(d->v_scale)))
+    return fail(KV_ERR_INVALID_ARG, "fp8 pool scales must be finite and > 0 (k %g, v %g)",
+                double(d->k_scale), double(d->v_scale));
   if (d->block_size != 16)
     return fail(KV_ERR_UNSUPPORTED, "block_size %d is not supported (16 only)", d->block_size);
   if (d->head_dim != 64 && d->head_dim != 128)
@@ -182,8 +194,8 @@ kv_status reshape_and_cache(const kv_pool* pool, const void* key, const void* va
     return fail(KV_ERR_INVALID_ARG, "key and value must be 16-byte aligned");
   const kv_pool_desc& d = pool->desc;
   pagedkv::CacheWriteArgs a{pool->k_cache, pool->v_cache, d.num_blocks, d.num_kv_heads,
-                            d.head_dim, key, value, slot_mapping, N};
-  return hip_status(pagedkv::launch_cache_write(a, d.dtype == KV_BF16,
+                            d.head_dim, key, value, slot_mapping, N, d.k_scale, d.v_scale};
+  return hip_status(pagedkv::launch_cache_write(a, kind_of(d.dtype),
                                                 static_cast<hipStream_t>(stream)),
                     "cache write launch");
 }
@@ -197,7 +209,8 @@ size_t paged_attention_workspace_bytes(int32_t B, int32_t H, int32_t head_dim,
 
 int32_t kv_decode_kernel_kind(const kv_pool* pool, int32_t H) {
   if (!pool || H < 1 || H % pool->desc.num_kv_heads != 0) return -1;
-  return (pool->desc.dtype == KV_BF16 && H > pool->desc.num_kv_heads) ? 1 : 0;
+  const bool packed = pool->desc.dtype == KV_BF16 || pool->desc.dtype == KV_FP8_E4M3;
+  return (packed && H > pool->desc.num_kv_heads) ? 1 : 0;
 }
 
 }  // extern "C"
@@ -249,19 +262,22 @@ kv_status decode_impl(const kv_pool* pool, void* out, const void* query,
   a.B = B;
   a.H = H;
   a.max_context_len = max_context_len;
-  a.scale_log2 = scale * 1.4426950408889634f;
+  const bool fp8 = d.dtype == KV_FP8_E4M3;
+  // an fp8 key is code * k_scale, so its score is (q . code) * k_scale: the
+  // factor joins the softmax scale; V's factor multiplies the output
+  a.scale_log2 = scale * 1.4426950408889634f * (fp8 ? d.k_scale : 1.f);
+  a.v_scale = fp8 ? d.v_scale : 1.f;
   a.partition_size = partition_size;
   a.num_partitions = static_cast<int32_t>(P);
   a.ws_o = ws.o;
   a.ws_m = ws.m;
   a.ws_l = ws.l;
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  const bool bf16 = d.dtype == KV_BF16;
   hipError_t e;
   if (kv_decode_kernel_kind(pool, H) == 1)
-    e = pagedkv::launch_decode_mfma(a, d.head_dim, s);
+    e = pagedkv::launch_decode_mfma(a, kind_of(d.dtype), d.head_dim, s);
   else
-    e = pagedkv::launch_decode_valu(a, bf16, d.head_dim, s);
+    e = pagedkv::launch_decode_valu(a, kind_of(d.dtype), d.head_dim, s);
   return hip_status(e, "decode launch");
 }
 
@@ -292,8 +308,9 @@ kv_status kv_cache_append(const kv_pool* pool, const void* key, const void* valu
     return fail(KV_ERR_INVALID_ARG, "key and value must be 16-byte aligned");
   const kv_pool_desc& d = pool->desc;
   pagedkv::AppendArgs a{pool->k_cache, pool->v_cache, d.num_blocks, d.num_kv_heads, d.head_dim,
-                        key, value, block_tables, max_nb, context_lens, B, slot_mapping};
-  return hip_status(pagedkv::launch_append(a, d.dtype == KV_BF16, static_cast<hipStream_t>(stream)),
+                        key,           value,          block_tables, max_nb,     context_lens,
+                        B,             slot_mapping,   d.k_scale,    d.v_scale};
+  return hip_status(pagedkv::launch_append(a, kind_of(d.dtype), static_cast<hipStream_t>(stream)),
                     "append launch");
 }
 

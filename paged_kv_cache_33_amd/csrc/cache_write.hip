@@ -6,6 +6,9 @@
 // incremental decoder (K and V grow by one row per token), done for a whole
 // batch in one launch.
 //
+// An fp8 pool stores each element as an E4M3 code of x / scale (see
+// source_chunk); bf16 and fp32 pools store the bits unchanged.
+//
 // Stores are non-temporal.  A decode step writes a few bytes into many cache
 // lines (one token of each K chunk row and of each V dim row); left dirty in the
 // caches, those lines would be evicted one by one in the middle of the next
@@ -30,10 +33,9 @@ __global__ __launch_bounds__(256) void slot_mapping_kernel(SlotMappingArgs a) {
   a.slot_mapping[b] = slot;
 }
 
-// Write chunk c (X elements) of one token's K and V rows, already loaded as
-// kc and vc, into in-block slot t of tile `tile`: one 16-byte store for K
-// ([d/X][16][X] tile), X element stores for V ([d][16] tile).  Pure bit moves:
-// no value is converted.
+// Write chunk c (X elements) of one token's K and V rows, already in cache
+// storage as kc and vc, into in-block slot t of tile `tile`: one 16-byte store
+// for K ([d/X][16][X] tile), X element stores for V ([d][16] tile).
 template <typename Tr>
 __device__ __forceinline__ void write_token_chunk(void* k_cache, void* v_cache, int64_t tile, int C,
                                                   int head_dim, int c, int t, const uint4 kc,
@@ -50,15 +52,32 @@ __device__ __forceinline__ void write_token_chunk(void* k_cache, void* v_cache, 
   for (int e = 0; e < X; ++e) __builtin_nontemporal_store(ve[e], vdst + e * kBlockTokens);
 }
 
-// The 16-byte chunk of a source row (key or value) at element offset src.
+// Chunk c of a source row (key or value), whose first element is at element
+// offset src, in cache storage.  bf16 / fp32: the row's own 16 bytes.  fp8: the
+// row's 16 bf16 values (32 bytes), each stored as e4m3_code(x / scale), the
+// division in fp32 (correctly rounded) - "Forward Deployed Engineering
+// Interview", Ch.2 section 9: a per-tensor scale, 1.0 when uncalibrated.
 template <typename Tr>
-__device__ __forceinline__ uint4 load_chunk(const void* base, int64_t src) {
-  return *reinterpret_cast<const uint4*>(static_cast<const typename Tr::storage*>(base) + src);
+__device__ __forceinline__ uint4 source_chunk(const void* base, int64_t src, float scale) {
+  if constexpr (Tr::kKind == Kind::kFp8) {
+    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + src);
+    const uint4 lo = p[0], hi = p[1];
+    const uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    uint32_t c[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      c[k] = e4m3_code(bf16_lo(w[2 * k]) / scale) | e4m3_code(bf16_hi(w[2 * k]) / scale) << 8 |
+             e4m3_code(bf16_lo(w[2 * k + 1]) / scale) << 16 |
+             e4m3_code(bf16_hi(w[2 * k + 1]) / scale) << 24;
+    return make_uint4(c[0], c[1], c[2], c[3]);
+  } else {
+    return *reinterpret_cast<const uint4*>(static_cast<const typename Tr::storage*>(base) + src);
+  }
 }
 
-// One thread per (token, kv head, 16-byte chunk of the head's row).  K chunks
-// land as one 16-byte store ([d/X][16][X] tile); V elements land one by one in
-// the token-minor [d][16] tile.  Pure bit moves: no value is converted.
+// One thread per (token, kv head, 16-byte chunk of the head's cached row).  K
+// chunks land as one 16-byte store ([d/X][16][X] tile); V elements land one by
+// one in the token-minor [d][16] tile.  bf16 / fp32: pure bit moves.
 template <typename Tr>
 __global__ __launch_bounds__(256) void cache_write_kernel(CacheWriteArgs a) {
   constexpr int X = Tr::kChunk;
@@ -72,8 +91,8 @@ __global__ __launch_bounds__(256) void cache_write_kernel(CacheWriteArgs a) {
   // The source chunk does not depend on the slot: load it first, so its
   // latency overlaps that of the slot load.
   const int64_t src = (i * a.num_kv_heads + h) * a.head_dim + int64_t(c) * X;
-  const uint4 kc = load_chunk<Tr>(a.key, src);
-  const uint4 vc = load_chunk<Tr>(a.value, src);
+  const uint4 kc = source_chunk<Tr>(a.key, src, a.k_scale);
+  const uint4 vc = source_chunk<Tr>(a.value, src, a.v_scale);
   const int64_t slot = a.slot_mapping[i];
   if (slot < 0 || slot >= int64_t(a.num_blocks) * kBlockTokens) return;
   const int64_t p = slot / kBlockTokens;
@@ -98,8 +117,8 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   const int b = int(idx / (int64_t(C) * a.num_kv_heads));
   // Source chunk first: it overlaps the dependent length -> table loads.
   const int64_t src = (int64_t(b) * a.num_kv_heads + h) * a.head_dim + int64_t(c) * X;
-  const uint4 kc = load_chunk<Tr>(a.key, src);
-  const uint4 vc = load_chunk<Tr>(a.value, src);
+  const uint4 kc = source_chunk<Tr>(a.key, src, a.k_scale);
+  const uint4 vc = source_chunk<Tr>(a.value, src, a.v_scale);
   const int32_t n = a.context_lens[b];
   int64_t slot = -1;
   if (n > 0 && n <= a.max_nb * kBlockTokens) {
@@ -122,29 +141,45 @@ hipError_t launch_slot_mapping(const SlotMappingArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_cache_write(const CacheWriteArgs& a, bool bf16, hipStream_t s) {
-  const int X = bf16 ? Bf16::kChunk : F32::kChunk;
-  const int64_t total = int64_t(a.N) * a.num_kv_heads * (a.head_dim / X);
+static int chunk_elems(Kind kind) {
+  return kind == Kind::kFp8 ? Fp8::kChunk : kind == Kind::kBf16 ? Bf16::kChunk : F32::kChunk;
+}
+
+hipError_t launch_cache_write(const CacheWriteArgs& a, Kind kind, hipStream_t s) {
+  const int64_t total = int64_t(a.N) * a.num_kv_heads * (a.head_dim / chunk_elems(kind));
   if (total == 0) return hipSuccess;
   const int threads = 256;
   const unsigned blocks = unsigned((total + threads - 1) / threads);
-  if (bf16)
-    hipLaunchKernelGGL(cache_write_kernel<Bf16>, dim3(blocks), dim3(threads), 0, s, a);
-  else
-    hipLaunchKernelGGL(cache_write_kernel<F32>, dim3(blocks), dim3(threads), 0, s, a);
+  switch (kind) {
+    case Kind::kBf16:
+      hipLaunchKernelGGL(cache_write_kernel<Bf16>, dim3(blocks), dim3(threads), 0, s, a);
+      break;
+    case Kind::kF32:
+      hipLaunchKernelGGL(cache_write_kernel<F32>, dim3(blocks), dim3(threads), 0, s, a);
+      break;
+    case Kind::kFp8:
+      hipLaunchKernelGGL(cache_write_kernel<Fp8>, dim3(blocks), dim3(threads), 0, s, a);
+      break;
+  }
   return hipGetLastError();
 }
 
-hipError_t launch_append(const AppendArgs& a, bool bf16, hipStream_t s) {
-  const int X = bf16 ? Bf16::kChunk : F32::kChunk;
-  const int64_t total = int64_t(a.B) * a.num_kv_heads * (a.head_dim / X);
+hipError_t launch_append(const AppendArgs& a, Kind kind, hipStream_t s) {
+  const int64_t total = int64_t(a.B) * a.num_kv_heads * (a.head_dim / chunk_elems(kind));
   if (total == 0) return hipSuccess;
   const int threads = 256;
   const unsigned blocks = unsigned((total + threads - 1) / threads);
-  if (bf16)
-    hipLaunchKernelGGL(append_kernel<Bf16>, dim3(blocks), dim3(threads), 0, s, a);
-  else
-    hipLaunchKernelGGL(append_kernel<F32>, dim3(blocks), dim3(threads), 0, s, a);
+  switch (kind) {
+    case Kind::kBf16:
+      hipLaunchKernelGGL(append_kernel<Bf16>, dim3(blocks), dim3(threads), 0, s, a);
+      break;
+    case Kind::kF32:
+      hipLaunchKernelGGL(append_kernel<F32>, dim3(blocks), dim3(threads), 0, s, a);
+      break;
+    case Kind::kFp8:
+      hipLaunchKernelGGL(append_kernel<Fp8>, dim3(blocks), dim3(threads), 0, s, a);
+      break;
+  }
   return hipGetLastError();
 }
 

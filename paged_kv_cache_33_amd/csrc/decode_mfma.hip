@@ -20,6 +20,8 @@
 // tile puts tokens 4q..4q+3 of dim 16mc + n in one 8-byte load (a coalesced
 // 512 B per wave).  The S accumulator (tokens 4q+j of head n) is already the
 // P^T operand of the second product, so no data moves between lanes.
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 #include "work_list.h"
@@ -45,22 +47,67 @@ struct MfmaShape {
   static constexpr int MC = D / 16;  // PV products per block (= 8-byte V loads per lane)
 };
 
-template <int D>
+// One block's K and V as loaded by one lane.  bf16: 16-byte K chunk 4i + q of
+// token n is operand i of S = K Q^T as stored; 8 bytes of V (tokens 4q..4q+3
+// of dim 16mc + n) are operand mc of O^T = V^T P^T.  fp8 (E4M3 codes): one
+// 16-byte load holds chunk q + 4j (16 dims) and becomes operands 2j, 2j+1
+// (dims 8 and 8 more); 4 bytes of V become operand mc.  The codes convert to
+// bf16 exactly, so both caches feed the same bf16 products.
+template <typename E, int D>
 struct MfmaFrag {
-  uint4 k[MfmaShape<D>::KI];
-  uint2 v[MfmaShape<D>::MC];
+  static constexpr bool kFp8 = E::kKind == Kind::kFp8;
+  static constexpr int KL = kFp8 ? D / 64 : D / 32;  // 16-byte K loads per lane
+  using VPiece = std::conditional_t<kFp8, uint32_t, uint2>;
+  uint4 k[KL];
+  VPiece v[MfmaShape<D>::MC];
 };
 
-template <int D>
-__device__ __forceinline__ void load_block(MfmaFrag<D>& f, const uint16_t* kt, const uint16_t* vt,
-                                           int lane) {
+template <typename E, int D>
+__device__ __forceinline__ void load_block(MfmaFrag<E, D>& f, const typename E::storage* kt,
+                                           const typename E::storage* vt, int lane) {
+  constexpr int X = E::kChunk;
 #pragma unroll
-  for (int i = 0; i < MfmaShape<D>::KI; ++i)
-    f.k[i] = load_tile16(kt + (i * kWave + lane) * 8);
+  for (int i = 0; i < MfmaFrag<E, D>::KL; ++i)
+    f.k[i] = load_tile16(kt + (i * kWave + lane) * X);
   const int n = lane & 15, q = lane >> 4;
 #pragma unroll
-  for (int mc = 0; mc < MfmaShape<D>::MC; ++mc)
-    f.v[mc] = load_tile8(vt + (16 * mc + n) * kBlockTokens + 4 * q);
+  for (int mc = 0; mc < MfmaShape<D>::MC; ++mc) {
+    if constexpr (MfmaFrag<E, D>::kFp8)
+      f.v[mc] = load_tile4(vt + (16 * mc + n) * kBlockTokens + 4 * q);
+    else
+      f.v[mc] = load_tile8(vt + (16 * mc + n) * kBlockTokens + 4 * q);
+  }
+}
+
+// Operand i of S = K Q^T and operand mc of O^T = V^T P^T, as bf16.
+template <typename E, int D>
+__device__ __forceinline__ bf16x8_t k_operand(const MfmaFrag<E, D>& f, int i) {
+  if constexpr (MfmaFrag<E, D>::kFp8) {
+    const uint4 c = f.k[i >> 1];
+    const uint32_t w0 = (i & 1) ? c.z : c.x, w1 = (i & 1) ? c.w : c.y;
+    return __builtin_bit_cast(bf16x8_t, make_uint4(e4m3x2_to_bf16x2<false>(w0),
+                                                   e4m3x2_to_bf16x2<true>(w0),
+                                                   e4m3x2_to_bf16x2<false>(w1),
+                                                   e4m3x2_to_bf16x2<true>(w1)));
+  } else {
+    return __builtin_bit_cast(bf16x8_t, f.k[i]);
+  }
+}
+template <typename E, int D>
+__device__ __forceinline__ uint2 v_operand(const MfmaFrag<E, D>& f, int mc) {
+  if constexpr (MfmaFrag<E, D>::kFp8)
+    return make_uint2(e4m3x2_to_bf16x2<false>(f.v[mc]), e4m3x2_to_bf16x2<true>(f.v[mc]));
+  else
+    return f.v[mc];
+}
+
+// First query dim of the 8 that pair with K operand i in lane quarter q.
+template <typename E>
+__device__ __forceinline__ int query_dim0(int i, int q) {
+  if constexpr (E::kKind == Kind::kFp8)
+    return (q + 4 * (i >> 1)) * 16 + (i & 1) * 8;
+  else
+    return (4 * i + q) * 8;
 }
 
 template <int D>
@@ -74,8 +121,8 @@ __device__ __forceinline__ uint32_t zero_masked_pair(uint32_t w, bool keep_lo, b
   return (keep_lo ? (w & 0x0000ffffu) : 0u) | (keep_hi ? (w & 0xffff0000u) : 0u);
 }
 
-template <int D, bool kTail>
-__device__ __forceinline__ void compute_block(const MfmaFrag<D>& f,
+template <typename E, int D, bool kTail>
+__device__ __forceinline__ void compute_block(const MfmaFrag<E, D>& f,
                                               const bf16x8_t (&qop)[MfmaShape<D>::KI],
                                               MfmaState<D>& st, int nvalid, float scale_log2,
                                               int lane) {
@@ -83,8 +130,7 @@ __device__ __forceinline__ void compute_block(const MfmaFrag<D>& f,
   floatx4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int i = 0; i < MfmaShape<D>::KI; ++i)
-    s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, f.k[i]), qop[i], s,
-                                                0, 0, 0);
+    s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand<E, D>(f, i), qop[i], s, 0, 0, 0);
   float sc[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -105,7 +151,7 @@ __device__ __forceinline__ void compute_block(const MfmaFrag<D>& f,
   const short4_t pop = __builtin_bit_cast(short4_t, make_uint2(p01, p23));
 #pragma unroll
   for (int mc = 0; mc < MfmaShape<D>::MC; ++mc) {
-    uint2 v = f.v[mc];
+    uint2 v = v_operand<E, D>(f, mc);
     if (kTail) {  // tokens past the range get weight 0; their V must be 0, not NaN
       v.x = zero_masked_pair(v.x, 4 * q + 0 < nvalid, 4 * q + 1 < nvalid);
       v.y = zero_masked_pair(v.y, 4 * q + 2 < nvalid, 4 * q + 3 < nvalid);
@@ -118,9 +164,10 @@ __device__ __forceinline__ void compute_block(const MfmaFrag<D>& f,
 
 // One work item: partition `part` of sequence b, head tile `tile_y` (a KV
 // head and a group of up to 16 of its query heads).
-template <int D, int kWaves>
+template <typename E, int D, int kWaves>
 __device__ __forceinline__ void mfma_item(const DecodeArgs& a, const int part, const int tile_y,
                                           const int b) {
+  using S = typename E::storage;
   constexpr int KI = MfmaShape<D>::KI;
   constexpr int MC = MfmaShape<D>::MC;
   constexpr int kRow = D + 4;  // padded LDS row (floats)
@@ -195,14 +242,14 @@ __device__ __forceinline__ void mfma_item(const DecodeArgs& a, const int part, c
         static_cast<const uint16_t*>(a.query) + (size_t(b) * a.H + head0 + min(n, nh - 1)) * D;
 #pragma unroll
     for (int i = 0; i < KI; ++i) {
-      uint4 raw = *reinterpret_cast<const uint4*>(qrow + (4 * i + q) * 8);
+      uint4 raw = *reinterpret_cast<const uint4*>(qrow + query_dim0<E>(i, q));
       if (n >= nh) raw = make_uint4(0u, 0u, 0u, 0u);
       qop[i] = __builtin_bit_cast(bf16x8_t, raw);
     }
   }
 
-  const uint16_t* kc = static_cast<const uint16_t*>(a.k_cache);
-  const uint16_t* vc = static_cast<const uint16_t*>(a.v_cache);
+  const S* kc = static_cast<const S*>(a.k_cache);
+  const S* vc = static_cast<const S*>(a.v_cache);
   const int64_t tile_elems = int64_t(kBlockTokens) * D;
 
   MfmaState<D> st;
@@ -218,26 +265,26 @@ __device__ __forceinline__ void mfma_item(const DecodeArgs& a, const int part, c
   // reported as -1, so every load in the loop below is unconditional and the
   // compiler can keep the next block's loads in flight while one computes.
   int n0 = 0;
-  auto fetch = [&](int n, MfmaFrag<D>& f) -> int64_t {
+  auto fetch = [&](int n, MfmaFrag<E, D>& f) -> int64_t {
     const int p = __builtin_amdgcn_readlane(win, n - n0);
     const bool ok = p >= 0 && p < a.num_blocks;
     const int64_t tile = (int64_t(ok ? p : 0) * a.num_kv_heads + kvh) * tile_elems;
-    load_block<D>(f, kc + tile, vc + tile, lane);
+    load_block<E, D>(f, kc + tile, vc + tile, lane);
     return ok ? tile : -1;
   };
-  auto consume = [&](int j, int64_t tile, const MfmaFrag<D>& f) {
+  auto consume = [&](int j, int64_t tile, const MfmaFrag<E, D>& f) {
     if (tile < 0) { bad_blk = 1; return; }
     const int nvalid = te - j * kBlockTokens;
     if (nvalid >= kBlockTokens)
-      compute_block<D, false>(f, qop, st, nvalid, a.scale_log2, lane);
+      compute_block<E, D, false>(f, qop, st, nvalid, a.scale_log2, lane);
     else
-      compute_block<D, true>(f, qop, st, nvalid, a.scale_log2, lane);
+      compute_block<E, D, true>(f, qop, st, nvalid, a.scale_log2, lane);
   };
   // Ping-pong over two register buffers: block n+1 is in flight while n
   // computes.  Windows of 64 blocks; inside one, every iteration has a next
   // block to fetch (the last one or two are peeled off).
   const int nblk = je - jb - w > 0 ? (je - jb - w + kWaves - 1) / kWaves : 0;
-  MfmaFrag<D> fa, fb;
+  MfmaFrag<E, D> fa, fb;
   for (; n0 < nblk; n0 += kWave) {
     const int cnt = min(kWave, nblk - n0);
     if (n0 > 0) {
@@ -288,7 +335,7 @@ __device__ __forceinline__ void mfma_item(const DecodeArgs& a, const int part, c
       L = fmaf(sm_l[ww][hh], sc, L);
       acc = fmaf(sm_o[ww][hh][x], sc, acc);
     }
-    float res = acc / L;
+    float res = acc / L * a.v_scale;
     if (bad) res = __int_as_float(0x7fc00000);
     if (!split || nparts == 1) {
       out_at(hh, x) = f32_to_bf16_rne(res);
@@ -306,7 +353,7 @@ __device__ __forceinline__ void mfma_item(const DecodeArgs& a, const int part, c
 // sequence and head tile, sequences taken longest first.  Split (kSplit =
 // true): grid (resident workers, head tiles, 1) walking the work list.  Two instantiations keep each one's
 // register allocation that of a single inlined item.
-template <int D, bool kSplit>
+template <typename E, int D, bool kSplit>
 __global__ __launch_bounds__(kWavesOf<kSplit> * kWave, kSplit ? 1 : 3) void decode_mfma_kernel(
     DecodeArgs a) {
   constexpr int kWaves = kWavesOf<kSplit>;
@@ -315,14 +362,14 @@ __global__ __launch_bounds__(kWavesOf<kSplit> * kWave, kSplit ? 1 : 3) void deco
     const int b = a.B <= kMaxOrderedSeqs
         ? sequence_of_rank<kWaves * kWave>(a.context_lens, a.B, a.max_nb, blockIdx.z, sm_order)
         : int(blockIdx.z);
-    mfma_item<D, kWaves>(a, 0, blockIdx.y, b);
+    mfma_item<E, D, kWaves>(a, 0, blockIdx.y, b);
   } else {
     __shared__ int sm_starts[kMaxSplitSeqs + 1];
     const int n_items = build_work_list(a, sm_starts);
     for (int i = blockIdx.x; i < n_items; i += gridDim.x) {
       int b, part;
       locate_item(sm_starts, a.B, i, b, part);
-      mfma_item<D, kWaves>(a, part, blockIdx.y, b);
+      mfma_item<E, D, kWaves>(a, part, blockIdx.y, b);
       __syncthreads();  // the next item reuses the merge buffers
     }
   }
@@ -330,15 +377,21 @@ __global__ __launch_bounds__(kWavesOf<kSplit> * kWave, kSplit ? 1 : 3) void deco
 
 }  // namespace
 
-hipError_t launch_decode_mfma(const DecodeArgs& a, int head_dim, hipStream_t s) {
-  const bool split = a.partition_size > 0;
-  void (*kern)(DecodeArgs) = nullptr;
+template <typename E>
+void (*mfma_kernel(int head_dim, bool split))(DecodeArgs) {
   if (head_dim == 128)
-    kern = split ? decode_mfma_kernel<128, true> : decode_mfma_kernel<128, false>;
-  else if (head_dim == 64)
-    kern = split ? decode_mfma_kernel<64, true> : decode_mfma_kernel<64, false>;
-  else
-    return hipErrorInvalidValue;
+    return split ? decode_mfma_kernel<E, 128, true> : decode_mfma_kernel<E, 128, false>;
+  if (head_dim == 64)
+    return split ? decode_mfma_kernel<E, 64, true> : decode_mfma_kernel<E, 64, false>;
+  return nullptr;
+}
+
+hipError_t launch_decode_mfma(const DecodeArgs& a, Kind kind, int head_dim, hipStream_t s) {
+  const bool split = a.partition_size > 0;
+  void (*kern)(DecodeArgs) = kind == Kind::kBf16  ? mfma_kernel<Bf16>(head_dim, split)
+                             : kind == Kind::kFp8 ? mfma_kernel<Fp8>(head_dim, split)
+                                                  : nullptr;
+  if (!kern) return hipErrorInvalidValue;
   const int g = a.H / a.num_kv_heads;
   const int tiles = a.num_kv_heads * ((g + kHeadsPerTile - 1) / kHeadsPerTile);
   const dim3 block((split ? kWavesOf<true> : kWavesOf<false>) * kWave);

@@ -65,13 +65,24 @@ struct WaveState {
   float l;    // this lane's share of the denominator (token lane%16)
 };
 
-// The query slice a lane contracts with: chunks 4i + lane/16 of the head row.
-// bf16 keeps the stored pairs (the dot2 instruction takes them as they are);
-// fp32 keeps floats.
+// The query slice a lane contracts with: the dims of K chunks 4i + lane/16 of
+// the head row.  bf16 keeps the stored pairs (the dot2 instruction takes them
+// as they are); fp32 keeps floats; an fp8 cache's 16-element chunk pairs with
+// 16 bf16 query values, two 16-byte pieces.
 template <typename Tr, int D>
 struct QueryFrag {
-  uint4 c[ValuShape<Tr, D>::KL];
+  static constexpr int kPieces = Tr::kKind == Kind::kFp8 ? 2 : 1;
+  uint4 c[ValuShape<Tr, D>::KL][kPieces];
 };
+
+// One 16-byte piece of 16 E4M3 codes as 8 bf16 pairs (lo: codes 0..7, hi:
+// codes 8..15), exact.
+__device__ __forceinline__ void e4m3x16_to_bf16(const uint4& v, uint4& lo, uint4& hi) {
+  lo = make_uint4(e4m3x2_to_bf16x2<false>(v.x), e4m3x2_to_bf16x2<true>(v.x),
+                  e4m3x2_to_bf16x2<false>(v.y), e4m3x2_to_bf16x2<true>(v.y));
+  hi = make_uint4(e4m3x2_to_bf16x2<false>(v.z), e4m3x2_to_bf16x2<true>(v.z),
+                  e4m3x2_to_bf16x2<false>(v.w), e4m3x2_to_bf16x2<true>(v.w));
+}
 
 // Zero the bf16 V values of tokens >= nvalid inside one 16-byte piece holding
 // tokens first..first+7 of one dim (the same tokens in every lane).
@@ -91,21 +102,33 @@ __device__ __forceinline__ void compute_block(const BlockFrag<Tr, D>& f, const Q
                                               float (&o)[ValuShape<Tr, D>::XK], WaveState& st,
                                               int nvalid, float scale_log2, int lane) {
   using Sh = ValuShape<Tr, D>;
-  constexpr bool kBf16 = Tr::kChunk == 8;
+  constexpr bool kFp8 = Tr::kKind == Kind::kFp8;
+  constexpr bool kPacked = Tr::kKind != Kind::kF32;  // bf16 pairs into dot2
   // ---- scores: this lane's chunks of token lane%16, then the 4 rows combined
   float dot = 0.f;
 #pragma unroll
   for (int i = 0; i < Sh::KL; ++i) {
-    if constexpr (kBf16) {
-      dot = dot2_bf16(f.k[i].x, qf.c[i].x, dot);
-      dot = dot2_bf16(f.k[i].y, qf.c[i].y, dot);
-      dot = dot2_bf16(f.k[i].z, qf.c[i].z, dot);
-      dot = dot2_bf16(f.k[i].w, qf.c[i].w, dot);
+    if constexpr (kFp8) {
+      uint4 klo, khi;
+      e4m3x16_to_bf16(f.k[i], klo, khi);
+      dot = dot2_bf16(klo.x, qf.c[i][0].x, dot);
+      dot = dot2_bf16(klo.y, qf.c[i][0].y, dot);
+      dot = dot2_bf16(klo.z, qf.c[i][0].z, dot);
+      dot = dot2_bf16(klo.w, qf.c[i][0].w, dot);
+      dot = dot2_bf16(khi.x, qf.c[i][1].x, dot);
+      dot = dot2_bf16(khi.y, qf.c[i][1].y, dot);
+      dot = dot2_bf16(khi.z, qf.c[i][1].z, dot);
+      dot = dot2_bf16(khi.w, qf.c[i][1].w, dot);
+    } else if constexpr (kPacked) {
+      dot = dot2_bf16(f.k[i].x, qf.c[i][0].x, dot);
+      dot = dot2_bf16(f.k[i].y, qf.c[i][0].y, dot);
+      dot = dot2_bf16(f.k[i].z, qf.c[i][0].z, dot);
+      dot = dot2_bf16(f.k[i].w, qf.c[i][0].w, dot);
     } else {
-      dot = fmaf(__uint_as_float(f.k[i].x), __uint_as_float(qf.c[i].x), dot);
-      dot = fmaf(__uint_as_float(f.k[i].y), __uint_as_float(qf.c[i].y), dot);
-      dot = fmaf(__uint_as_float(f.k[i].z), __uint_as_float(qf.c[i].z), dot);
-      dot = fmaf(__uint_as_float(f.k[i].w), __uint_as_float(qf.c[i].w), dot);
+      dot = fmaf(__uint_as_float(f.k[i].x), __uint_as_float(qf.c[i][0].x), dot);
+      dot = fmaf(__uint_as_float(f.k[i].y), __uint_as_float(qf.c[i][0].y), dot);
+      dot = fmaf(__uint_as_float(f.k[i].z), __uint_as_float(qf.c[i][0].z), dot);
+      dot = fmaf(__uint_as_float(f.k[i].w), __uint_as_float(qf.c[i][0].w), dot);
     }
   }
   dot = cross_row_sum(dot);
@@ -119,7 +142,7 @@ __device__ __forceinline__ void compute_block(const BlockFrag<Tr, D>& f, const Q
   st.m = m_new;
 #pragma unroll
   for (int xk = 0; xk < Sh::XK; ++xk) o[xk] *= alpha;
-  if constexpr (kBf16) {
+  if constexpr (kPacked) {
     // weights rounded to bf16 pairs (tokens 2k, 2k+1); the denominator sums
     // the same rounded values
     const uint32_t packed = pack_bf16x2(p, dpp_mov<kDppQuadXor1>(p));
@@ -128,16 +151,23 @@ __device__ __forceinline__ void compute_block(const BlockFrag<Tr, D>& f, const Q
 #pragma unroll
     for (int k = 0; k < kBlockTokens / 2; ++k)
       pp[k] = __builtin_amdgcn_readlane(packed, 2 * k);
+    auto accumulate = [&](uint4 v, int th, float& acc) {  // tokens 8th .. 8th+7
+      if (kTail) v = mask_tail_tokens(v, th * 8, nvalid);
+      acc = dot2_bf16(v.x, pp[th * 4 + 0], acc);
+      acc = dot2_bf16(v.y, pp[th * 4 + 1], acc);
+      acc = dot2_bf16(v.z, pp[th * 4 + 2], acc);
+      acc = dot2_bf16(v.w, pp[th * 4 + 3], acc);
+    };
 #pragma unroll
     for (int xk = 0; xk < Sh::XK; ++xk) {
+      if constexpr (kFp8) {
+        uint4 vlo, vhi;
+        e4m3x16_to_bf16(f.v[xk], vlo, vhi);
+        accumulate(vlo, 0, o[xk]);
+        accumulate(vhi, 1, o[xk]);
+      } else {
 #pragma unroll
-      for (int th = 0; th < Sh::R; ++th) {
-        uint4 v = f.v[xk * Sh::R + th];
-        if (kTail) v = mask_tail_tokens(v, th * 8, nvalid);
-        o[xk] = dot2_bf16(v.x, pp[th * 4 + 0], o[xk]);
-        o[xk] = dot2_bf16(v.y, pp[th * 4 + 1], o[xk]);
-        o[xk] = dot2_bf16(v.z, pp[th * 4 + 2], o[xk]);
-        o[xk] = dot2_bf16(v.w, pp[th * 4 + 3], o[xk]);
+        for (int th = 0; th < Sh::R; ++th) accumulate(f.v[xk * Sh::R + th], th, o[xk]);
       }
     }
   } else {
@@ -168,6 +198,7 @@ template <typename Tr, int D>
 __device__ __forceinline__ void valu_item(const DecodeArgs& a, const int part, const int h,
                                           const int b) {
   using S = typename Tr::storage;
+  using A = typename Tr::act;
   using Sh = ValuShape<Tr, D>;
   constexpr int X = Sh::X;
 
@@ -184,7 +215,7 @@ __device__ __forceinline__ void valu_item(const DecodeArgs& a, const int part, c
   const int nparts = split ? (ctx > 0 ? (ctx + a.partition_size - 1) / a.partition_size : 0) : 1;
   const bool bad_len = ctx > a.max_nb * kBlockTokens || (split && nparts > a.num_partitions);
   const size_t row = (size_t(b) * a.H + h) * D;
-  S* out = static_cast<S*>(a.out) + row;
+  A* out = static_cast<A*>(a.out) + row;
   const size_t prow = (size_t(b) * a.H + h) * a.num_partitions + part;
 
   if (!split && (ctx <= 0 || bad_len)) {
@@ -221,13 +252,15 @@ __device__ __forceinline__ void valu_item(const DecodeArgs& a, const int part, c
     win = jj < je ? table[jj] : -1;
   }
 
-  // This lane's slice of the query: chunks 4i + lane/16.
+  // This lane's slice of the query: the dims of chunks 4i + lane/16.
   QueryFrag<Tr, D> qf;
   {
-    const S* qrow = static_cast<const S*>(a.query) + row;
+    const A* qrow = static_cast<const A*>(a.query) + row;
 #pragma unroll
     for (int i = 0; i < Sh::KL; ++i)
-      qf.c[i] = *reinterpret_cast<const uint4*>(qrow + (4 * i + lane / 16) * X);
+#pragma unroll
+      for (int pc = 0; pc < QueryFrag<Tr, D>::kPieces; ++pc)
+        qf.c[i][pc] = *reinterpret_cast<const uint4*>(qrow + (4 * i + lane / 16) * X + pc * 8);
   }
 
   const S* kc = static_cast<const S*>(a.k_cache);
@@ -316,7 +349,7 @@ __device__ __forceinline__ void valu_item(const DecodeArgs& a, const int part, c
       L = fmaf(sm_l[ww], sc, L);
       acc = fmaf(sm_o[ww][x], sc, acc);
     }
-    float res = acc / L;
+    float res = acc / L * a.v_scale;
     if (bad) res = __int_as_float(0x7fc00000);
     if (!split || nparts == 1) {
       out[x] = Tr::from_f32(res);
@@ -356,19 +389,21 @@ __global__ __launch_bounds__(kWaves * kWave) void decode_valu_kernel(DecodeArgs 
 
 }  // namespace
 
-hipError_t launch_decode_valu(const DecodeArgs& a, bool bf16, int head_dim, hipStream_t s) {
+template <typename Tr>
+void (*valu_kernel(int head_dim, bool split))(DecodeArgs) {
+  if (head_dim == 128)
+    return split ? decode_valu_kernel<Tr, 128, true> : decode_valu_kernel<Tr, 128, false>;
+  if (head_dim == 64)
+    return split ? decode_valu_kernel<Tr, 64, true> : decode_valu_kernel<Tr, 64, false>;
+  return nullptr;
+}
+
+hipError_t launch_decode_valu(const DecodeArgs& a, Kind kind, int head_dim, hipStream_t s) {
   const bool split = a.partition_size > 0;
-  void (*kern)(DecodeArgs) = nullptr;
-  if (bf16 && head_dim == 128)
-    kern = split ? decode_valu_kernel<Bf16, 128, true> : decode_valu_kernel<Bf16, 128, false>;
-  else if (bf16 && head_dim == 64)
-    kern = split ? decode_valu_kernel<Bf16, 64, true> : decode_valu_kernel<Bf16, 64, false>;
-  else if (!bf16 && head_dim == 128)
-    kern = split ? decode_valu_kernel<F32, 128, true> : decode_valu_kernel<F32, 128, false>;
-  else if (!bf16 && head_dim == 64)
-    kern = split ? decode_valu_kernel<F32, 64, true> : decode_valu_kernel<F32, 64, false>;
-  else
-    return hipErrorInvalidValue;
+  void (*kern)(DecodeArgs) = kind == Kind::kBf16  ? valu_kernel<Bf16>(head_dim, split)
+                             : kind == Kind::kF32 ? valu_kernel<F32>(head_dim, split)
+                                                  : valu_kernel<Fp8>(head_dim, split);
+  if (!kern) return hipErrorInvalidValue;
   const dim3 block(kWaves * kWave);
   dim3 grid(1, a.H, a.B);
   if (a.partition_size > 0) {

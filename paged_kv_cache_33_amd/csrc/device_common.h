@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "launch.h"
+
 namespace pagedkv {
 
 constexpr int kBlockTokens = 16;  // tokens per physical block
@@ -105,31 +107,53 @@ __device__ __forceinline__ uint2 load_tile8(const void* p) {
   const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
   return make_uint2(v.x, v.y);
 }
+__device__ __forceinline__ uint32_t load_tile4(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+}
 
-// Element-type traits: storage type and elements per 16-byte chunk.
+// Element-type traits.  storage: one cache element; act: one element of the
+// query, the output and the rows handed to the cache write; kChunk: cache
+// elements per 16-byte chunk of the K layout.
 struct Bf16 {
   using storage = uint16_t;
+  using act = uint16_t;
+  static constexpr Kind kKind = Kind::kBf16;
   static constexpr int kChunk = 8;
-  __device__ __forceinline__ static float to_f32(storage s) { return bf16_to_f32(s); }
-  __device__ __forceinline__ static storage from_f32(float f) { return f32_to_bf16_rne(f); }
+  __device__ __forceinline__ static act from_f32(float f) { return f32_to_bf16_rne(f); }
 };
 struct F32 {
   using storage = float;
+  using act = float;
+  static constexpr Kind kKind = Kind::kF32;
   static constexpr int kChunk = 4;
-  __device__ __forceinline__ static float to_f32(storage s) { return s; }
-  __device__ __forceinline__ static storage from_f32(float f) { return f; }
+  __device__ __forceinline__ static act from_f32(float f) { return f; }
+};
+// fp8 cache ("Forward Deployed Engineering Interview", Ch.2 section 9): OCP
+// E4M3 codes with per-tensor scales; bf16 activations.
+struct Fp8 {
+  using storage = uint8_t;
+  using act = uint16_t;
+  static constexpr Kind kKind = Kind::kFp8;
+  static constexpr int kChunk = 16;
+  __device__ __forceinline__ static act from_f32(float f) { return f32_to_bf16_rne(f); }
 };
 
-// Unpack one 16-byte chunk (4 dwords) into kChunk floats.
-__device__ __forceinline__ void unpack_chunk(const uint4& c, float (&f)[8], Bf16) {
-  f[0] = bf16_lo(c.x); f[1] = bf16_hi(c.x);
-  f[2] = bf16_lo(c.y); f[3] = bf16_hi(c.y);
-  f[4] = bf16_lo(c.z); f[5] = bf16_hi(c.z);
-  f[6] = bf16_lo(c.w); f[7] = bf16_hi(c.w);
+// Two E4M3 codes (bytes 0, 1 of `w`, or bytes 2, 3 when `hi`) as a bf16 pair:
+// exact, since every E4M3 value is a bf16 value.
+template <bool kHi>
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, kHi));
 }
-__device__ __forceinline__ void unpack_chunk(const uint4& c, float (&f)[4], F32) {
-  f[0] = __uint_as_float(c.x); f[1] = __uint_as_float(c.y);
-  f[2] = __uint_as_float(c.z); f[3] = __uint_as_float(c.w);
+
+// E4M3 code of x: the nearest value, ties to the even code (the hardware
+// conversion), after clamping to +-448 so that an overflow stores the largest
+// finite value rather than the NaN code; NaN stores sign | 0x7F.
+__device__ __forceinline__ uint32_t e4m3_code(float x) {
+  const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
+  if (x != x) return sign | 0x7Fu;
+  const float c = fminf(fmaxf(x, -448.f), 448.f);
+  return uint32_t(__builtin_amdgcn_cvt_pk_fp8_f32(c, c, 0, false)) & 0xFFu;
 }
 
 }  // namespace pagedkv

@@ -10,6 +10,9 @@ namespace pagedkv {
 // per sequence in LDS.
 constexpr int kMaxSplitSeqs = 4096;
 
+// Cache element type of a pool (see the traits in device_common.h).
+enum class Kind { kF32, kBf16, kFp8 };
+
 // Work-groups of `kernel` (block size `threads`) the current GPU keeps
 // resident at once, divided among `tiles` head tiles (at least 1 each).
 int resident_workers(const void* kernel, int threads, int tiles);
@@ -28,7 +31,8 @@ struct DecodeArgs {
   int32_t B;
   int32_t H;
   int32_t max_context_len;
-  float scale_log2;            // scale * log2(e): scores are kept in base 2
+  float scale_log2;            // scale * log2(e) (* k_scale for fp8): scores in base 2
+  float v_scale;               // output multiplier (fp8: the V scale; else 1)
   int32_t partition_size;      // tokens per partition; 0 = whole sequence
   int32_t num_partitions;      // partitions per sequence in the grid (1 if single pass)
   float* ws_o;                 // [B][H][P][d]   (split mode only)
@@ -59,6 +63,8 @@ struct CacheWriteArgs {
   const void* value;
   const int64_t* slot_mapping;  // [N]
   int32_t N;
+  float k_scale;                // fp8: stored code = e4m3(x / scale)
+  float v_scale;
 };
 
 // One new token per sequence: slot mapping and cache write in one launch.
@@ -75,6 +81,8 @@ struct AppendArgs {
   const int32_t* context_lens;  // [B]
   int32_t B;
   int64_t* slot_mapping;        // optional [B] out
+  float k_scale;                // fp8: stored code = e4m3(x / scale)
+  float v_scale;
 };
 
 struct SlotMappingArgs {
@@ -87,10 +95,10 @@ struct SlotMappingArgs {
 
 // Launchers: return the hipError_t of the launch.
 hipError_t launch_slot_mapping(const SlotMappingArgs& a, hipStream_t s);
-hipError_t launch_cache_write(const CacheWriteArgs& a, bool bf16, hipStream_t s);
-hipError_t launch_append(const AppendArgs& a, bool bf16, hipStream_t s);
-hipError_t launch_decode_valu(const DecodeArgs& a, bool bf16, int head_dim, hipStream_t s);
-hipError_t launch_decode_mfma(const DecodeArgs& a, int head_dim, hipStream_t s);
+hipError_t launch_cache_write(const CacheWriteArgs& a, Kind kind, hipStream_t s);
+hipError_t launch_append(const AppendArgs& a, Kind kind, hipStream_t s);
+hipError_t launch_decode_valu(const DecodeArgs& a, Kind kind, int head_dim, hipStream_t s);
+hipError_t launch_decode_mfma(const DecodeArgs& a, Kind kind, int head_dim, hipStream_t s);
 hipError_t launch_reduce(const ReduceArgs& a, bool bf16_out, hipStream_t s);
 
 }  // namespace pagedkv

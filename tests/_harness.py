@@ -1,11 +1,14 @@
 """Shared helpers of the GPU parity tests: move a seeded workload to the GPU,
 run one decode step through the C ABI, and compute the oracle's answer.
 
-Poisoning: every slot a step must not read holds a quiet NaN (bf16 0x7FC0,
-fp32 0x7FC00000): the tail of each sequence's last block, every block no
+Poisoning: every slot a step must not read holds a NaN (bf16 0x7FC0, fp32
+0x7FC00000, E4M3 0x7F): the tail of each sequence's last block, every block no
 table uses, and the slot each step's new token is written to (so a decode
 that ran before the write would read NaN).  Table entries past a sequence's
 blocks already hold an index outside the pool.
+
+A workload's pool holds w.kv_dtype elements (bf16, f32 or fp8 codes); its
+queries, outputs and new rows hold w.dtype (bf16 for an fp8 pool).
 """
 from __future__ import annotations
 
@@ -20,7 +23,7 @@ import oracle as O
 import paged_kv_cache_33_amd as P
 from workloads import configs as W
 
-NAN_BITS = {"bf16": np.uint16(0x7FC0), "f32": np.uint32(0x7FC00000)}
+NAN_BITS = {"bf16": np.uint16(0x7FC0), "f32": np.uint32(0x7FC00000), "fp8": np.uint8(0x7F)}
 BF16_REL_L2 = 5e-3
 BF16_MAX_ABS = 1e-2
 F32_MAX_ABS = 1e-5
@@ -35,7 +38,7 @@ def poison(w: W.Workload, first_unwritten: np.ndarray):
     of each sequence's blocks and in every block no sequence uses."""
     kp = w.k_pool.copy()
     vp = w.v_pool.copy()
-    nan = NAN_BITS[w.dtype]
+    nan = NAN_BITS[w.kv_dtype]
     tile = w.H_kv * 16 * w.d
     used = np.zeros(w.num_blocks, dtype=bool)
     xs = np.arange(w.d)
@@ -46,8 +49,8 @@ def poison(w: W.Workload, first_unwritten: np.ndarray):
         for pos in range(int(first_unwritten[b]), nb_final * 16):
             blk = int(row[pos // 16])
             for h in range(w.H_kv):
-                kp[O.k_offset(blk, h, pos % 16, xs, w.H_kv, w.d, w.dtype)] = nan
-                vp[O.v_offset(blk, h, pos % 16, xs, w.H_kv, w.d, w.dtype)] = nan
+                kp[O.k_offset(blk, h, pos % 16, xs, w.H_kv, w.d, w.kv_dtype)] = nan
+                vp[O.v_offset(blk, h, pos % 16, xs, w.H_kv, w.d, w.kv_dtype)] = nan
     for blk in np.flatnonzero(~used):
         kp[blk * tile:(blk + 1) * tile] = nan
         vp[blk * tile:(blk + 1) * tile] = nan
@@ -66,6 +69,8 @@ def from_dev(t: torch.Tensor, dtype: str) -> np.ndarray:
     a = t.detach().cpu().contiguous()
     if dtype == "bf16":
         return a.view(torch.int16).numpy().view(np.uint16)
+    if dtype == "fp8":
+        return a.view(torch.uint8).numpy()
     return a.view(torch.int32).numpy().view(np.uint32)
 
 
@@ -77,7 +82,8 @@ class DevWorkload:
 
 
 def upload(w: W.Workload, k_pool: np.ndarray, v_pool: np.ndarray) -> DevWorkload:
-    pool = P.KVPool(to_dev(k_pool), to_dev(v_pool), w.num_blocks, w.H_kv, w.d, w.dtype)
+    pool = P.KVPool(to_dev(k_pool), to_dev(v_pool), w.num_blocks, w.H_kv, w.d, w.kv_dtype,
+                    w.k_scale, w.v_scale)
     tables = torch.from_numpy(w.block_tables).cuda()
     return DevWorkload(w=w, pool=pool, tables=tables)
 
@@ -113,10 +119,11 @@ def oracle_step(w: W.Workload, k_pool, v_pool, step: W.DecodeStep, seqs=None):
     """Oracle slot mapping, cache write and decode (optionally for some sequences)."""
     slots = O.slot_mapping(w.block_tables, step.context_lens)
     kp, vp = O.reshape_and_cache(k_pool, v_pool, step.new_k, step.new_v, slots, w.H_kv, w.d,
-                                 w.dtype, w.num_blocks)
+                                 w.kv_dtype, w.num_blocks, w.k_scale, w.v_scale)
     seqs = range(w.B) if seqs is None else seqs
     ref = {b: O.decode_sequence(kp, vp, step.q[b], w.block_tables[b], int(step.context_lens[b]),
-                                w.H, w.H_kv, w.d, w.dtype, w.scale) for b in seqs}
+                                w.H, w.H_kv, w.d, w.kv_dtype, w.scale, w.k_scale, w.v_scale)
+           for b in seqs}
     return slots, kp, vp, ref
 
 
@@ -147,14 +154,14 @@ def single_step_case(w: W.Workload, partition_size: int = 0, seqs=None, label: s
     first_unwritten = step.context_lens.astype(np.int64) - 1
     kp0, vp0 = poison(w, np.maximum(first_unwritten, 0))
     dw = upload(w, kp0, vp0)
-    log(f"[gpu] {label} B={w.B} H={w.H} H_kv={w.H_kv} d={w.d} {w.dtype} P={partition_size}"
+    log(f"[gpu] {label} B={w.B} H={w.H} H_kv={w.H_kv} d={w.d} {w.kv_dtype} P={partition_size}"
         f"{' fused' if fused else ''}")
     slots, out = gpu_step(dw, step, partition_size, fused=fused)
     torch.cuda.synchronize()
     oslots, kp, vp, ref = oracle_step(w, kp0, vp0, step, seqs)
     np.testing.assert_array_equal(slots.cpu().numpy(), oslots, err_msg=f"{label}: slots")
-    assert np.array_equal(from_dev(dw.pool.k_cache, w.dtype), kp), f"{label}: K pool bits"
-    assert np.array_equal(from_dev(dw.pool.v_cache, w.dtype), vp), f"{label}: V pool bits"
+    assert np.array_equal(from_dev(dw.pool.k_cache, w.kv_dtype), kp), f"{label}: K pool bits"
+    assert np.array_equal(from_dev(dw.pool.v_cache, w.kv_dtype), vp), f"{label}: V pool bits"
     return assert_close(from_dev(out, w.dtype), ref, w.dtype, label, amplitude)
 
 

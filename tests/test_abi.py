@@ -41,8 +41,9 @@ def lib():
     return _lib.load()
 
 
-def desc(num_blocks=8, block_size=16, H_kv=2, d=128, dtype=_lib.KV_BF16):
-    return _lib.KVPoolDesc(num_blocks, block_size, H_kv, d, dtype)
+def desc(num_blocks=8, block_size=16, H_kv=2, d=128, dtype=_lib.KV_BF16, k_scale=1.0,
+         v_scale=1.0):
+    return _lib.KVPoolDesc(num_blocks, block_size, H_kv, d, dtype, k_scale, v_scale)
 
 
 def test_header_declares_the_expected_calls():
@@ -61,6 +62,7 @@ def test_library_exports_every_declared_symbol(lib):
 def test_pool_bytes(lib):
     assert lib.kv_pool_bytes(C.byref(desc(8, 16, 2, 128, _lib.KV_BF16))) == 8 * 2 * 16 * 128 * 2
     assert lib.kv_pool_bytes(C.byref(desc(3, 16, 1, 64, _lib.KV_F32))) == 3 * 16 * 64 * 4
+    assert lib.kv_pool_bytes(C.byref(desc(5, 16, 4, 128, _lib.KV_FP8_E4M3))) == 5 * 4 * 16 * 128
     assert lib.kv_pool_bytes(C.byref(desc(8, 32, 2, 128))) == 0
     assert lib.kv_pool_bytes(C.byref(desc(8, 16, 2, 96))) == 0
     assert lib.kv_pool_bytes(None) == 0
@@ -78,6 +80,10 @@ def _create(lib, d, k=FAKE_K, v=FAKE_V):
     (dict(d=96), _lib.KV_ERR_UNSUPPORTED),
     (dict(num_blocks=0), _lib.KV_ERR_INVALID_ARG),
     (dict(H_kv=0), _lib.KV_ERR_INVALID_ARG),
+    (dict(dtype=_lib.KV_FP8_E4M3, k_scale=0.0), _lib.KV_ERR_INVALID_ARG),
+    (dict(dtype=_lib.KV_FP8_E4M3, v_scale=-1.0), _lib.KV_ERR_INVALID_ARG),
+    (dict(dtype=_lib.KV_FP8_E4M3, k_scale=float("nan")), _lib.KV_ERR_INVALID_ARG),
+    (dict(dtype=_lib.KV_FP8_E4M3, v_scale=float("inf")), _lib.KV_ERR_INVALID_ARG),
 ])
 def test_pool_create_rejects_bad_descriptors(lib, bad, code):
     st, h = _create(lib, desc(**bad))
@@ -109,6 +115,15 @@ def test_kernel_kind(lib, pool):
     st, hf = _create(lib, desc(8, 16, 2, 64, _lib.KV_F32))
     assert lib.kv_decode_kernel_kind(hf, 8) == 0        # fp32: vector ALU
     lib.kv_pool_destroy(hf)
+    st, h8 = _create(lib, desc(8, 16, 2, 128, _lib.KV_FP8_E4M3, 0.5, 2.0))
+    assert st == _lib.KV_OK
+    assert lib.kv_decode_kernel_kind(h8, 2) == 0        # fp8 MHA: vector ALU
+    assert lib.kv_decode_kernel_kind(h8, 8) == 1        # fp8 GQA: matrix cores
+    lib.kv_pool_destroy(h8)
+    # scales are ignored (not checked) for the other dtypes
+    st, hb = _create(lib, desc(8, 16, 2, 128, _lib.KV_BF16, 0.0, float("nan")))
+    assert st == _lib.KV_OK
+    lib.kv_pool_destroy(hb)
 
 
 def test_cache_write_argument_errors(lib, pool):
@@ -175,6 +190,9 @@ def test_reduce_argument_errors(lib):
     assert r(FAKE_K, FAKE_V, FAKE_K, 2, 4, 128, 64, 0, _lib.KV_BF16, None) == _lib.KV_ERR_INVALID_ARG
     assert r(FAKE_K, FAKE_V, FAKE_K, 2, 4, 96, 64, 16, _lib.KV_BF16, None) == _lib.KV_ERR_UNSUPPORTED
     assert r(FAKE_K, FAKE_V, FAKE_K, 2, 4, 128, 64, 16, 5, None) == _lib.KV_ERR_UNSUPPORTED
+    # outputs are activations: an fp8 output type is refused
+    assert r(FAKE_K, FAKE_V, FAKE_K, 2, 4, 128, 64, 16, _lib.KV_FP8_E4M3, None) == \
+        _lib.KV_ERR_UNSUPPORTED
     assert r(None, FAKE_V, FAKE_K, 2, 4, 128, 64, 16, _lib.KV_BF16, None) == _lib.KV_ERR_INVALID_ARG
     assert r(FAKE_K, FAKE_V, FAKE_K, 0, 4, 128, 64, 16, _lib.KV_BF16, None) == _lib.KV_OK
 
