@@ -178,9 +178,10 @@ size_t paged_attention_workspace_bytes(int32_t B, int32_t H, int32_t head_dim,
  * mode) or a table entry outside the pool gives NaN for that sequence.
  * partition_size == 0: single pass, writes out.  partition_size = 16*k > 0:
  * split-KV; each partition of partition_size tokens writes (o, m, l) into the
- * workspace (m, l in base-2 units: m = max of scale*log2(e)*q.k, l = sum of
- * 2^(that - m), o = normalised partial output); sequences with a single
- * partition write out directly.  Follow with paged_attention_reduce.
+ * workspace (base-2 units: with s = scale*log2(e)*q.k over the partition, m is
+ * a reference value with max(s) - 8 <= m <= max(s), l = sum of 2^(s - m), o =
+ * normalised partial output); sequences with a single partition write out
+ * directly.  Follow with paged_attention_reduce.
  * H must be a multiple of H_kv.  Kernel choice: H_kv < H with a bf16 or fp8
  * pool uses the matrix-core kernel; otherwise the vector-ALU kernel. */
 kv_status paged_attention_decode(const kv_pool* pool, void* out, const void* query,

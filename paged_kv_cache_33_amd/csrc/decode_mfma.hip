@@ -36,6 +36,7 @@ namespace {
 template <bool kSplit>
 constexpr int kWavesOf = kSplit ? 8 : 4;
 constexpr int kHeadsPerTile = 16;
+constexpr float kRescaleSlack = 8.f;  // see compute_block
 
 typedef __bf16 bf16x8_t __attribute__((__vector_size__(8 * sizeof(__bf16))));
 typedef short short4_t __attribute__((__vector_size__(4 * sizeof(short))));
@@ -113,7 +114,7 @@ __device__ __forceinline__ int query_dim0(int i, int q) {
 template <int D>
 struct MfmaState {
   floatx4_t o[MfmaShape<D>::MC];  // O^T[16mc + 4q + j][head n]
-  float m;                        // running max of head n (base 2)
+  float m;                        // reference max of head n (base 2): within 8 of the max
   float l;                        // denominator share of head n over tokens 4q..4q+3
 };
 
@@ -138,16 +139,26 @@ __device__ __forceinline__ void compute_block(const MfmaFrag<E, D>& f,
     if (kTail && 4 * q + j >= nvalid) sc[j] = -INFINITY;  // select: the slot may hold NaN
   }
   const float mx = cross_row_max(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
-  const float m_new = fmaxf(st.m, mx);
-  const float alpha = fast_exp2(st.m - m_new);
-  st.m = m_new;
+  // The reference max st.m moves only when a head's block max exceeds it by
+  // more than kRescaleSlack (base-2 units), so weights 2^(s - m) stay below 2^8
+  // and most blocks skip rescaling O (32 multiplies at d = 128).  Softmax does
+  // not depend on the reference, so only rounding changes.
+  const bool grow = mx > st.m + kRescaleSlack;
+  if (__builtin_amdgcn_ballot_w64(grow) != 0) {  // wave-uniform branch
+    const float m_new = grow ? mx : st.m;
+    const float alpha = fast_exp2(st.m - m_new);
+    st.l *= alpha;
+#pragma unroll
+    for (int mc = 0; mc < MfmaShape<D>::MC; ++mc) st.o[mc] *= alpha;
+    st.m = m_new;
+  }
   // weights rounded to bf16 for the matrix core; the denominator sums the
   // same rounded values
-  const uint32_t p01 = pack_bf16x2(fast_exp2(sc[0] - m_new), fast_exp2(sc[1] - m_new));
-  const uint32_t p23 = pack_bf16x2(fast_exp2(sc[2] - m_new), fast_exp2(sc[3] - m_new));
+  const uint32_t p01 = pack_bf16x2(fast_exp2(sc[0] - st.m), fast_exp2(sc[1] - st.m));
+  const uint32_t p23 = pack_bf16x2(fast_exp2(sc[2] - st.m), fast_exp2(sc[3] - st.m));
   const float psum = (__uint_as_float(p01 << 16) + __uint_as_float(p01 & 0xffff0000u)) +
                      (__uint_as_float(p23 << 16) + __uint_as_float(p23 & 0xffff0000u));
-  st.l = fmaf(st.l, alpha, psum);
+  st.l += psum;
   const short4_t pop = __builtin_bit_cast(short4_t, make_uint2(p01, p23));
 #pragma unroll
   for (int mc = 0; mc < MfmaShape<D>::MC; ++mc) {
@@ -156,7 +167,6 @@ __device__ __forceinline__ void compute_block(const MfmaFrag<E, D>& f,
       v.x = zero_masked_pair(v.x, 4 * q + 0 < nvalid, 4 * q + 1 < nvalid);
       v.y = zero_masked_pair(v.y, 4 * q + 2 < nvalid, 4 * q + 3 < nvalid);
     }
-    st.o[mc] *= alpha;
     st.o[mc] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(short4_t, v), pop,
                                                         st.o[mc], 0, 0, 0);
   }
