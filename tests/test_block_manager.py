@@ -1,0 +1,115 @@
+"""Pins of the block-manager oracle (CPU): the page's demo and bookkeeping
+invariants over seeded random operation sequences."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+from oracle.block_manager import BLOCK, BlockManagerModel, NoBlocks
+
+from block_manager_cases import load_demo, random_ops, replay_demo
+
+
+def test_demo_prints_the_page_values():
+    d = load_demo()
+    want = [st["print"] for st in d["steps"] if "print" in st]
+    assert want == [0, 32, 59, 0, 0, 32]
+    assert replay_demo(BlockManagerModel(d["num_blocks"])) == want
+
+
+def _check_invariants(m: BlockManagerModel, history):
+    refs = np.zeros(len(m.blocks), dtype=int)
+    for seq, (table, _) in m.seqs.items():
+        for b in table:
+            refs[b.id] += 1
+        # the table holds exactly the sequence's tokens, in order
+        toks = [t for b in table for t in b.tokens]
+        assert toks == history[seq], seq
+        # every block but the last is full
+        assert all(len(b.tokens) == BLOCK for b in table[:-1])
+    assert refs.tolist() == m.refs()                 # counts = table references
+    free = m.free_order()
+    assert len(set(free)) == len(free)
+    assert sorted(free) == [i for i, r in enumerate(refs) if r == 0]
+    for key, b in m.cache.items():                   # cache entries point at full blocks
+        assert b.key == key and len(b.tokens) == BLOCK
+
+
+@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("num_blocks", [12, 40])
+def test_random_operations_keep_the_bookkeeping_consistent(seed, num_blocks):
+    m = BlockManagerModel(num_blocks)
+    history = {}
+    for op in random_ops(seed, 300):
+        kind = op[0]
+        if kind == "admit" and op[1] not in m.seqs:
+            before = (m.free_order(), m.refs())
+            try:
+                hits = m.admit(op[1], op[2], op[3])
+            except NoBlocks:
+                assert (m.free_order(), m.refs()) == before   # nothing changed
+                continue
+            assert hits % BLOCK == 0 and hits <= len(op[2])
+            history[op[1]] = list(op[2])
+        elif kind == "append" and op[1] in m.seqs:
+            last = m.seqs[op[1]][0][-1] if m.seqs[op[1]][0] else None
+            shared = last is not None and last.refs > 1 and len(last.tokens) < BLOCK
+            before = (m.free_order(), m.refs())
+            try:
+                slot, copy = m.append(op[1], op[2])
+            except NoBlocks:
+                assert (m.free_order(), m.refs()) == before
+                continue
+            history[op[1]].append(op[2])
+            # copy-on-write exactly when the partial last block was shared;
+            # the token's slot lies in a block only this sequence holds
+            assert (copy is not None) == shared
+            assert m.refs()[slot // BLOCK] == 1
+            assert m.table(op[1])[-1] == slot // BLOCK
+            if copy:
+                assert copy[1] == slot // BLOCK
+        elif kind == "fork" and op[1] in m.seqs and op[2] not in m.seqs:
+            m.fork(op[1], op[2])
+            history[op[2]] = list(history[op[1]])
+        elif kind == "release" and op[1] in m.seqs:
+            m.release(op[1])
+            history.pop(op[1])
+        _check_invariants(m, history)
+
+
+def test_released_prefix_is_found_until_its_block_is_reused():
+    m = BlockManagerModel(3)
+    p = list(range(32))
+    assert m.admit(1, p) == 0                   # blocks 0, 1
+    m.release(1)                                # free queue: 2, 1, 0 (last block first)
+    assert m.admit(2, p) == 32                  # both blocks still hold the prefix
+    m.release(2)                                # free queue: 2, 1, 0
+    m.admit(3, list(range(100, 116)))           # takes block 2
+    m.admit(4, list(range(200, 216)))           # takes block 1: the prefix's second block
+    m.release(3)
+    m.release(4)
+    assert m.admit(5, p) == 16                  # only the first block still holds it
+
+
+def test_an_operation_without_enough_blocks_changes_nothing():
+    m = BlockManagerModel(3)
+    m.admit(1, list(range(40)))                 # 3 blocks, the last one partial
+    state = (m.free_order(), m.refs(), m.table(1))
+    with pytest.raises(NoBlocks):
+        m.admit(2, list(range(200, 220)))
+    assert (m.free_order(), m.refs(), m.table(1)) == state
+    for t in range(8):                          # fills the last block: no block needed
+        m.append(1, t)
+    with pytest.raises(NoBlocks):
+        m.append(1, 99)                         # needs a fresh block
+    m.fork(1, 2)
+    assert m.num_free() == 0 and m.refs() == [2, 2, 2]
+    assert m.num_tokens(1) == 48
+
+
+def test_salt_separates_identical_prompts():
+    m = BlockManagerModel(16)
+    p = list(range(48))
+    m.admit(1, p, "x")
+    assert m.admit(2, p, "y") == 0
+    assert m.admit(3, p, "x") == 48
