@@ -83,7 +83,8 @@ typedef enum {
   KV_ERR_INVALID_ARG = -1,  /* null pointer, negative or inconsistent size   */
   KV_ERR_UNSUPPORTED = -2,  /* a dtype / head_dim / block size not built      */
   KV_ERR_WORKSPACE = -3,    /* workspace missing or smaller than required     */
-  KV_ERR_HIP = -4           /* a HIP runtime call failed (message has detail) */
+  KV_ERR_HIP = -4,          /* a HIP runtime call failed (message has detail) */
+  KV_ERR_NO_BLOCKS = -5     /* block manager: not enough free blocks; nothing changed */
 } kv_status;
 
 typedef enum {
@@ -205,6 +206,76 @@ kv_status paged_attention_reduce(void* out, const void* workspace,
                                  int32_t head_dim, int32_t max_context_len,
                                  int32_t partition_size, kv_dtype out_dtype,
                                  void* stream);
+
+/* Copy whole blocks on the GPU: for i < n, block src[i] of both caches (all KV
+ * heads, all 16 slots, K and V) is copied to block dst[i].  This is the data
+ * half of copy-on-write: the block manager below names the pair when a token
+ * is appended to a shared last block, and the copy must run (stream order)
+ * before that token is written.  src, dst: device int32 [n]; a pair with an
+ * index outside the pool, or src == dst, is skipped.  No block may be a
+ * destination twice, or both a source and a destination, in one call. */
+kv_status kv_copy_blocks(const kv_pool* pool, const int32_t* src, const int32_t* dst, int32_t n,
+                         void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Host block manager ("Forward Deployed Engineering Interview", Ch.2 section 8,
+ * the block-manager teaching model; "Anthropic Interview: Design an LLM
+ * Inference API with GPU Batching", 4.1/4.2 data model): block tables,
+ * reference counts, a free queue and a prefix cache for a pool of num_blocks
+ * blocks of 16 token slots.  Host memory only; it never touches the GPU.
+ *   - The key of a full block covers its parent's key (the block before it in
+ *     the table; the sequence's salt for a first block) and its 16 token ids.
+ *   - admit reuses the cached blocks of the unbroken run of full blocks at the
+ *     start of a prompt (a released block still holding its prefix is taken
+ *     back from the free queue) and takes fresh blocks for the rest.
+ *   - A fresh block is the front of the free queue (least recently freed); it
+ *     loses the cache entry it still carried.
+ *   - append opens a fresh block when the last one is full, and copies the
+ *     last block first when it is shared (copy-on-write).
+ *   - fork gives a child the parent's table, every block shared.
+ *   - release drops one reference per block, last block first; unreferenced
+ *     blocks join the back of the free queue and stay cached until reused.
+ * An operation that needs more free blocks than exist returns KV_ERR_NO_BLOCKS
+ * and changes nothing (the caller preempts a sequence and retries).  Sequence
+ * ids are the caller's.  Calls on one manager are serialised by a lock. */
+typedef struct kv_block_manager kv_block_manager;
+
+kv_status kv_bm_create(int32_t num_blocks, kv_block_manager** out);
+void kv_bm_destroy(kv_block_manager* bm);
+
+/* Build sequence seq's table for a prompt of n token ids (host int32), salt
+ * (salt_len bytes, may be 0).  *hits = prompt tokens found in cached blocks (a
+ * multiple of 16): their K/V rows are already in the pool; the caller writes
+ * the rest at slots table[i/16]*16 + i%16, i >= *hits. */
+kv_status kv_bm_admit(kv_block_manager* bm, int64_t seq, const int32_t* tokens, int32_t n,
+                      const char* salt, int32_t salt_len, int32_t* hits);
+
+/* Append one token to seq.  *slot = its slot (block*16 + offset).  When the
+ * last block was shared, *copy_src / *copy_dst name the block to copy first
+ * (kv_copy_blocks); otherwise both are -1. */
+kv_status kv_bm_append(kv_block_manager* bm, int64_t seq, int32_t token, int64_t* slot,
+                       int32_t* copy_src, int32_t* copy_dst);
+
+/* Child shares every block of seq (parallel sampling, beam search). */
+kv_status kv_bm_fork(kv_block_manager* bm, int64_t seq, int64_t child);
+
+/* Drop seq and its references. */
+kv_status kv_bm_release(kv_block_manager* bm, int64_t seq);
+
+/* Free blocks (-1 for a NULL manager). */
+int32_t kv_bm_num_free(kv_block_manager* bm);
+
+/* seq's block ids (host int32, capacity entries; NULL to ask only for the
+ * counts), number of blocks and of tokens. */
+kv_status kv_bm_table(kv_block_manager* bm, int64_t seq, int32_t* blocks, int32_t capacity,
+                      int32_t* num_blocks, int32_t* num_tokens);
+
+/* Decode inputs for a batch: row b of tables (host int32 [B][max_nb]) gets
+ * seqs[b]'s block ids, then -1; context_lens[b] (host int32 [B]) its token
+ * count.  Fails, writing nothing, if a sequence is unknown or has more than
+ * max_nb blocks. */
+kv_status kv_bm_batch_tables(kv_block_manager* bm, const int64_t* seqs, int32_t B, int32_t max_nb,
+                             int32_t* tables, int32_t* context_lens);
 
 /* Which decode kernel paged_attention_decode launches for this pool and H:
  * 0 = vector-ALU kernel, 1 = matrix-core (MFMA) kernel, < 0 = unsupported. */

@@ -15,8 +15,10 @@ from typing import Optional, Union
 
 import torch
 
+import numpy as np
+
 from . import _lib
-from ._lib import KVPoolDesc, PagedKVError  # noqa: F401
+from ._lib import KVPoolDesc, NoBlocks, PagedKVError  # noqa: F401
 
 __all__ = [
     "KVPool",
@@ -30,6 +32,9 @@ __all__ = [
     "paged_attention_decode",
     "paged_attention_reduce",
     "kv_decode_kernel_kind",
+    "kv_copy_blocks",
+    "BlockManager",
+    "NoBlocks",
     "library_path",
 ]
 
@@ -271,3 +276,83 @@ def paged_attention_reduce(out: torch.Tensor, workspace: torch.Tensor, context_l
 def kv_decode_kernel_kind(pool: KVPool, H: int) -> int:
     """0 = vector-ALU decode kernel, 1 = matrix-core kernel, < 0 unsupported."""
     return int(_lib.load().kv_decode_kernel_kind(pool.handle, H))
+
+
+def kv_copy_blocks(pool: KVPool, src: torch.Tensor, dst: torch.Tensor, stream=None) -> None:
+    """Copy whole blocks src[i] -> dst[i] of both caches on the GPU (device int32 [n])."""
+    n = int(src.numel())
+    sp = _buf(src, "src", 4 * n, dtype=torch.int32)
+    dp = _buf(dst, "dst", 4 * n, dtype=torch.int32)
+    _lib.check(_lib.load().kv_copy_blocks(pool.handle, sp, dp, n, _stream_handle(stream)))
+
+
+class BlockManager:
+    """The C ABI's host block manager (kv_bm_*): tables, counts, free queue,
+    prefix cache, fork and copy-on-write for a pool of num_blocks blocks."""
+
+    def __init__(self, num_blocks: int):
+        lib = _lib.load()
+        h = C.c_void_p()
+        _lib.check(lib.kv_bm_create(int(num_blocks), C.byref(h)))
+        self._h = h
+        self.num_blocks = int(num_blocks)
+
+    def close(self) -> None:
+        if getattr(self, "_h", None) is not None:
+            _lib.load().kv_bm_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def admit(self, seq: int, prompt, salt: str = "") -> int:
+        """Build seq's table for a prompt (token ids); return the tokens found cached."""
+        toks = np.ascontiguousarray(np.asarray(prompt, dtype=np.int32))
+        sb = salt.encode("utf-8")
+        hits = C.c_int32()
+        _lib.check(_lib.load().kv_bm_admit(self._h, int(seq), toks.ctypes.data if toks.size else None,
+                                           int(toks.size), sb, len(sb), C.byref(hits)))
+        return int(hits.value)
+
+    def append(self, seq: int, token: int):
+        """Write one token; return (slot, (src, dst) of a copy-on-write or None)."""
+        slot, cs, cd = C.c_int64(), C.c_int32(), C.c_int32()
+        _lib.check(_lib.load().kv_bm_append(self._h, int(seq), int(token), C.byref(slot),
+                                            C.byref(cs), C.byref(cd)))
+        return int(slot.value), (None if cs.value < 0 else (int(cs.value), int(cd.value)))
+
+    def fork(self, seq: int, child: int) -> None:
+        _lib.check(_lib.load().kv_bm_fork(self._h, int(seq), int(child)))
+
+    def release(self, seq: int) -> None:
+        _lib.check(_lib.load().kv_bm_release(self._h, int(seq)))
+
+    def num_free(self) -> int:
+        return int(_lib.load().kv_bm_num_free(self._h))
+
+    def table(self, seq: int):
+        nb, nt = C.c_int32(), C.c_int32()
+        lib = _lib.load()
+        _lib.check(lib.kv_bm_table(self._h, int(seq), None, 0, C.byref(nb), C.byref(nt)))
+        out = np.zeros(max(nb.value, 1), dtype=np.int32)
+        _lib.check(lib.kv_bm_table(self._h, int(seq), out.ctypes.data, out.size, C.byref(nb),
+                                   C.byref(nt)))
+        return out[:nb.value].tolist()
+
+    def num_tokens(self, seq: int) -> int:
+        nb, nt = C.c_int32(), C.c_int32()
+        _lib.check(_lib.load().kv_bm_table(self._h, int(seq), None, 0, C.byref(nb), C.byref(nt)))
+        return int(nt.value)
+
+    def batch_tables(self, seqs, max_nb: int):
+        """Host int32 tables [B, max_nb] (-1 past each table) and lengths [B]."""
+        ids = np.ascontiguousarray(np.asarray(seqs, dtype=np.int64))
+        B = ids.size
+        tables = np.empty((B, max_nb), dtype=np.int32)
+        lens = np.empty(B, dtype=np.int32)
+        _lib.check(_lib.load().kv_bm_batch_tables(self._h, ids.ctypes.data, B, int(max_nb),
+                                                  tables.ctypes.data, lens.ctypes.data))
+        return tables, lens

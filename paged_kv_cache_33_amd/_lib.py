@@ -14,6 +14,7 @@ KV_ERR_INVALID_ARG = -1
 KV_ERR_UNSUPPORTED = -2
 KV_ERR_WORKSPACE = -3
 KV_ERR_HIP = -4
+KV_ERR_NO_BLOCKS = -5
 KV_F32 = 0
 KV_BF16 = 1
 KV_FP8_E4M3 = 2
@@ -24,6 +25,7 @@ STATUS_NAMES = {
     KV_ERR_UNSUPPORTED: "KV_ERR_UNSUPPORTED",
     KV_ERR_WORKSPACE: "KV_ERR_WORKSPACE",
     KV_ERR_HIP: "KV_ERR_HIP",
+    KV_ERR_NO_BLOCKS: "KV_ERR_NO_BLOCKS",
 }
 
 # Every symbol include/pagedkv.h declares, in declaration order.
@@ -37,6 +39,16 @@ EXPORTED = (
     "paged_attention_workspace_bytes",
     "paged_attention_decode",
     "paged_attention_reduce",
+    "kv_copy_blocks",
+    "kv_bm_create",
+    "kv_bm_destroy",
+    "kv_bm_admit",
+    "kv_bm_append",
+    "kv_bm_fork",
+    "kv_bm_release",
+    "kv_bm_num_free",
+    "kv_bm_table",
+    "kv_bm_batch_tables",
     "kv_decode_kernel_kind",
     "kv_last_error",
 )
@@ -58,6 +70,10 @@ class PagedKVError(RuntimeError):
     def __init__(self, status: int, message: str):
         super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
         self.status = status
+
+
+class NoBlocks(PagedKVError):
+    """The block manager had too few free blocks; nothing was changed."""
 
 
 _lib = None
@@ -86,6 +102,18 @@ def load() -> C.CDLL:
                                              C.c_float, i32, vp, sz, vp]),
         "kv_cache_append": (C.c_int, [vp, vp, vp, i32p, i32, i32p, i32, vp, vp]),
         "paged_attention_reduce": (C.c_int, [vp, vp, i32p, i32, i32, i32, i32, i32, C.c_int, vp]),
+        "kv_copy_blocks": (C.c_int, [vp, i32p, i32p, i32, vp]),
+        "kv_bm_create": (C.c_int, [i32, C.POINTER(vp)]),
+        "kv_bm_destroy": (None, [vp]),
+        "kv_bm_admit": (C.c_int, [vp, C.c_int64, vp, i32, C.c_char_p, i32, C.POINTER(C.c_int32)]),
+        "kv_bm_append": (C.c_int, [vp, C.c_int64, i32, i64p, C.POINTER(C.c_int32),
+                                   C.POINTER(C.c_int32)]),
+        "kv_bm_fork": (C.c_int, [vp, C.c_int64, C.c_int64]),
+        "kv_bm_release": (C.c_int, [vp, C.c_int64]),
+        "kv_bm_num_free": (C.c_int32, [vp]),
+        "kv_bm_table": (C.c_int, [vp, C.c_int64, vp, i32, C.POINTER(C.c_int32),
+                                  C.POINTER(C.c_int32)]),
+        "kv_bm_batch_tables": (C.c_int, [vp, vp, i32, i32, vp, vp]),
         "kv_decode_kernel_kind": (C.c_int32, [vp, i32]),
         "kv_last_error": (C.c_char_p, []),
     }
@@ -93,7 +121,6 @@ def load() -> C.CDLL:
         fn = getattr(lib, name)
         fn.restype = res
         fn.argtypes = args
-    del i64p
     _lib = lib
     return lib
 
@@ -101,4 +128,4 @@ def load() -> C.CDLL:
 def check(status: int) -> None:
     if status != KV_OK:
         msg = load().kv_last_error().decode(errors="replace")
-        raise PagedKVError(status, msg)
+        raise (NoBlocks if status == KV_ERR_NO_BLOCKS else PagedKVError)(status, msg)

@@ -23,6 +23,7 @@ BUILD = os.path.join(ROOT, "_build", "pagedkv")
 LIB = os.path.join(PKG, "libpagedkv.so")
 
 SOURCES = ["api.hip", "cache_write.hip", "decode_valu.hip", "decode_mfma.hip", "reduce.hip"]
+HOST_SOURCES = ["block_manager.cpp"]  # host-only C++ (the block manager)
 ARCH = "gfx950"
 
 # Packed-fp32 instructions are kept out of every kernel: the compiler may not
@@ -38,6 +39,9 @@ CFLAGS = [
     f"-I{INCLUDE}",
     f"-I{CSRC}",
 ]
+
+
+HOST_CFLAGS = ["-x", "c++", "-O3", "-std=c++17", "-fPIC", "-Wall", f"-I{INCLUDE}", f"-I{CSRC}"]
 
 
 def hipcc() -> str:
@@ -70,6 +74,10 @@ def build(jobs: int = 0, verbose: bool = False) -> str:
         obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
         objs.append(obj)
         cmds.append([cc, *CFLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+    for src in HOST_SOURCES:
+        obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+        objs.append(obj)
+        cmds.append([cc, *HOST_CFLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
     jobs = jobs or min(len(cmds), os.cpu_count() or 1, 8)
     with ThreadPoolExecutor(max_workers=jobs) as ex:
         for out in ex.map(lambda c: _run(c, verbose), cmds):

@@ -9,8 +9,9 @@
 #include <string>
 #include <unordered_map>
 
-#include "pagedkv.h"
+#include "errors.h"
 #include "launch.h"
+#include "pagedkv.h"
 
 struct kv_pool {
   kv_pool_desc desc;
@@ -49,10 +50,12 @@ int resident_workers(const void* kernel, int threads, int tiles) {
 }  // namespace pagedkv
 
 namespace {
-
 thread_local std::string g_last_error;
+}  // namespace
 
-kv_status fail(kv_status code, const char* fmt, ...) {
+namespace pagedkv {
+
+kv_status report(kv_status code, const char* fmt, ...) {
   char buf[512];
   va_list ap;
   va_start(ap, fmt);
@@ -62,10 +65,18 @@ kv_status fail(kv_status code, const char* fmt, ...) {
   return code;
 }
 
-kv_status ok() {
+kv_status report_ok() {
   g_last_error.clear();
   return KV_OK;
 }
+
+}  // namespace pagedkv
+
+namespace {
+
+using pagedkv::report;
+constexpr auto fail = report;
+kv_status ok() { return pagedkv::report_ok(); }
 
 kv_status hip_status(hipError_t e, const char* what) {
   if (e == hipSuccess) return ok();
@@ -312,6 +323,21 @@ kv_status kv_cache_append(const kv_pool* pool, const void* key, const void* valu
                         B,             slot_mapping,   d.k_scale,    d.v_scale};
   return hip_status(pagedkv::launch_append(a, kind_of(d.dtype), static_cast<hipStream_t>(stream)),
                     "append launch");
+}
+
+kv_status kv_copy_blocks(const kv_pool* pool, const int32_t* src, const int32_t* dst, int32_t n,
+                         void* stream) {
+  if (!pool) return fail(KV_ERR_INVALID_ARG, "pool is NULL");
+  if (n < 0) return fail(KV_ERR_INVALID_ARG, "n must be >= 0");
+  if (n == 0) return ok();
+  if (!src || !dst) return fail(KV_ERR_INVALID_ARG, "src and dst must be non-NULL");
+  const kv_pool_desc& d = pool->desc;
+  pagedkv::CopyBlocksArgs a{pool->k_cache, pool->v_cache, d.num_blocks,
+                            int64_t(d.num_kv_heads) * 16 * d.head_dim *
+                                int64_t(elem_bytes(d.dtype)),
+                            src, dst, n};
+  return hip_status(pagedkv::launch_copy_blocks(a, static_cast<hipStream_t>(stream)),
+                    "copy_blocks launch");
 }
 
 kv_status paged_attention_reduce(void* out, const void* workspace, const int32_t* context_lens,

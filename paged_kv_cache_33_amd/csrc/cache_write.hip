@@ -141,6 +141,28 @@ hipError_t launch_slot_mapping(const SlotMappingArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Copy-on-write data copy: work-group (i, c) copies block src[i] of cache c
+// (0 = K, 1 = V) to block dst[i], 16 bytes per thread and step.  Both sides
+// stream (non-temporal): the source is not reread, and the destination's next
+// reader is a later decode, which should not meet dirty lines in the caches.
+__global__ __launch_bounds__(256) void copy_blocks_kernel(CopyBlocksArgs a) {
+  const int i = blockIdx.x;
+  const int32_t s = a.src[i], d = a.dst[i];
+  if (s < 0 || s >= a.num_blocks || d < 0 || d >= a.num_blocks || s == d) return;
+  char* base = static_cast<char*>(blockIdx.y == 0 ? a.k_cache : a.v_cache);
+  const u32x4_t* from = reinterpret_cast<const u32x4_t*>(base + int64_t(s) * a.block_bytes);
+  u32x4_t* to = reinterpret_cast<u32x4_t*>(base + int64_t(d) * a.block_bytes);
+  const int64_t n16 = a.block_bytes / 16;
+  for (int64_t k = threadIdx.x; k < n16; k += blockDim.x)
+    __builtin_nontemporal_store(__builtin_nontemporal_load(from + k), to + k);
+}
+
+hipError_t launch_copy_blocks(const CopyBlocksArgs& a, hipStream_t s) {
+  if (a.n == 0) return hipSuccess;
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3(unsigned(a.n), 2), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 static int chunk_elems(Kind kind) {
   return kind == Kind::kFp8 ? Fp8::kChunk : kind == Kind::kBf16 ? Bf16::kChunk : F32::kChunk;
 }

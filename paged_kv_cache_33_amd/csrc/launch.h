@@ -85,6 +85,17 @@ struct AppendArgs {
   float v_scale;
 };
 
+// Whole-block copies (copy-on-write): block src[i] -> dst[i] in both caches.
+struct CopyBlocksArgs {
+  void* k_cache;
+  void* v_cache;
+  int32_t num_blocks;
+  int64_t block_bytes;          // bytes of one block in one cache (a multiple of 16)
+  const int32_t* src;
+  const int32_t* dst;
+  int32_t n;
+};
+
 struct SlotMappingArgs {
   const int32_t* block_tables;
   int32_t max_nb;
@@ -97,6 +108,7 @@ struct SlotMappingArgs {
 hipError_t launch_slot_mapping(const SlotMappingArgs& a, hipStream_t s);
 hipError_t launch_cache_write(const CacheWriteArgs& a, Kind kind, hipStream_t s);
 hipError_t launch_append(const AppendArgs& a, Kind kind, hipStream_t s);
+hipError_t launch_copy_blocks(const CopyBlocksArgs& a, hipStream_t s);
 hipError_t launch_decode_valu(const DecodeArgs& a, Kind kind, int head_dim, hipStream_t s);
 hipError_t launch_decode_mfma(const DecodeArgs& a, Kind kind, int head_dim, hipStream_t s);
 hipError_t launch_reduce(const ReduceArgs& a, bool bf16_out, hipStream_t s);
