@@ -74,6 +74,10 @@ def parse_args(argv=None):
                     help="only run a plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--decode-only", action="store_true",
                     help="launch only the decode kernel repeatedly (for counter runs)")
+    ap.add_argument("--serve", action="store_true",
+                    help="a serving loop driven by the native block manager (prefix-cached "
+                         "admission, forked samples, copy-on-write appends) at the 7B shape; "
+                         "prints its own JSON line")
     ap.add_argument("--unfused", action="store_true",
                     help="run the step's cache write as two calls (kv_slot_mapping + "
                          "reshape_and_cache) instead of kv_cache_append")
@@ -266,6 +270,110 @@ def parity_vs_refs(w, gpu_out_bits: np.ndarray, refs: dict) -> dict:
 
 
 # --------------------------------------------------------------------------
+# Serving loop on the native block manager
+
+def serve(args) -> int:
+    """B sequences share a 1,024-token system prompt (found in the prefix cache
+    after the first admission) plus 16..300 private tokens; every fourth
+    sequence is forked once (a second sample).  Each step appends one token to
+    every sequence (one kv_bm_append_batch call), copies the shared last blocks
+    that the appends name (one kv_copy_blocks), writes the new rows at the
+    manager's slots, uploads the batch tables and decodes; every eighth step
+    four samples are released and forked again, so copies on write keep
+    happening.  Step time covers all of it, host included."""
+    import torch
+    import paged_kv_cache_33_amd as P
+    torch.cuda.set_device(0)
+    H = H_kv = 32
+    d, B0, system_len = 128, 48, 1024
+    rng = np.random.default_rng(5)
+    system = rng.integers(0, 32000, size=system_len).tolist()
+    private = rng.integers(16, 301, size=B0)
+    num_blocks = 8192
+    elem = 2
+    n = num_blocks * H_kv * 16 * d
+    kc = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    vc = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    kc.normal_()
+    vc.normal_()
+    pool = P.KVPool(kc, vc, num_blocks, H_kv, d, "bf16")
+    bm = P.BlockManager(num_blocks)
+    seqs, hits_total = [], 0
+    for b in range(B0):
+        prompt = system + rng.integers(0, 32000, size=int(private[b])).tolist()
+        hits_total += bm.admit(b, prompt)
+        seqs.append(b)
+    for b in range(0, B0, 4):
+        bm.fork(b, 1000 + b)
+        seqs.append(1000 + b)
+    B = len(seqs)
+    max_nb = 128
+    q = torch.randn(B, H, d, device="cuda").to(torch.bfloat16)
+    out = torch.empty_like(q)
+    rows = torch.randn(B, H_kv, d, device="cuda").to(torch.bfloat16)
+    stream = torch.cuda.current_stream()
+    scale = 1.0 / math.sqrt(d)
+
+    parents = list(range(0, B0, 4))
+    children = {p: 1000 + p for p in parents}
+    next_child = 2000
+    state = {"i": 0}
+
+    def step():
+        nonlocal next_child
+        t0 = time.perf_counter()
+        if state["i"] % 8 == 7:                # re-sample: four forks replace their children
+            for p in parents[:4]:
+                old = children[p]
+                bm.release(old)
+                bm.fork(p, next_child)
+                seqs[seqs.index(old)] = next_child
+                children[p] = next_child
+                next_child += 1
+            for _ in range(4):                 # the next four parents go next time
+                parents.append(parents.pop(0))
+        state["i"] += 1
+        slots, copies = bm.append_batch(seqs, rng.integers(0, 32000, size=B))
+        tables, lens = bm.batch_tables(seqs, max_nb)
+        host = time.perf_counter() - t0
+        if len(copies):
+            cp = torch.from_numpy(np.ascontiguousarray(copies.T)).cuda(non_blocking=True)
+            P.kv_copy_blocks(pool, cp[0], cp[1], stream)
+        P.reshape_and_cache(pool, rows, rows, torch.from_numpy(slots).cuda(non_blocking=True),
+                            stream)
+        tt = torch.from_numpy(tables).cuda(non_blocking=True)
+        cl = torch.from_numpy(lens).cuda(non_blocking=True)
+        P.paged_attention_decode(pool, out, q, tt, cl, int(lens.max()), scale, 0, None, stream)
+        return host, len(copies), int(lens.sum())
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    host_s, copies, ctx_tokens = 0.0, 0, 0
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        h, c, ct = step()
+        host_s += h
+        copies += c
+        ctx_tokens += ct
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = wall / args.steps * 1e3
+    kv = ctx_tokens / args.steps * H_kv * d * 2 * elem
+    print(json.dumps({
+        "metric": "serving step on the native block manager, 7B shape",
+        "value": round(1000.0 / ms, 1), "unit": "steps/s", "ms_per_step": round(ms, 4),
+        "steps": args.steps, "warmup": args.warmup, "batch": B,
+        "forked_samples": B - B0, "prefix_tokens_found_at_admission": hits_total,
+        "host_block_manager_us_per_step": round(host_s / args.steps * 1e6, 1),
+        "copy_on_write_blocks_per_step": round(copies / args.steps, 2),
+        "kv_GBs": round(kv / (ms * 1e-3) / 1e9, 1),
+        "dtype": "bf16", "data": "synthetic",
+        "step": "kv_bm_append_batch + kv_bm_batch_tables + kv_copy_blocks + reshape_and_cache "
+                "+ table upload + paged_attention_decode",
+    }), flush=True)
+    return 0
+
 
 def main(argv=None) -> int:
     args = parse_args(argv)
@@ -280,6 +388,8 @@ def main(argv=None) -> int:
         torch.cuda.set_device(0)
         calib_copy(args.calib_copy_mib)
         return 0
+    if args.serve:
+        return serve(args)
 
     from workloads import configs as W
     t0 = time.time()

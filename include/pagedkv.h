@@ -256,6 +256,15 @@ kv_status kv_bm_admit(kv_block_manager* bm, int64_t seq, const int32_t* tokens, 
 kv_status kv_bm_append(kv_block_manager* bm, int64_t seq, int32_t token, int64_t* slot,
                        int32_t* copy_src, int32_t* copy_dst);
 
+/* kv_bm_append for seqs[0..B) in order (one token each, host arrays):
+ * slots[b] receives each slot; the copies to make first are written to
+ * copy_src / copy_dst (host int32, room for B) and counted in *n_copies.  On a
+ * failure the sequences before the failing one stay appended: *done (may be
+ * NULL) counts them, and the status is returned. */
+kv_status kv_bm_append_batch(kv_block_manager* bm, const int64_t* seqs, const int32_t* tokens,
+                             int32_t B, int64_t* slots, int32_t* copy_src, int32_t* copy_dst,
+                             int32_t* n_copies, int32_t* done);
+
 /* Child shares every block of seq (parallel sampling, beam search). */
 kv_status kv_bm_fork(kv_block_manager* bm, int64_t seq, int64_t child);
 

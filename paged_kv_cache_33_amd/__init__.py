@@ -324,6 +324,23 @@ class BlockManager:
                                             C.byref(cs), C.byref(cd)))
         return int(slot.value), (None if cs.value < 0 else (int(cs.value), int(cd.value)))
 
+    def append_batch(self, seqs, tokens):
+        """Append tokens[b] to seqs[b] in order; return (slots int64 [B], copy
+        pairs int32 [n, 2] to make first)."""
+        ids = np.ascontiguousarray(np.asarray(seqs, dtype=np.int64))
+        toks = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32))
+        if ids.shape != toks.shape:
+            raise ValueError("one token per sequence")
+        B = ids.size
+        slots = np.empty(B, dtype=np.int64)
+        cs = np.empty(max(B, 1), dtype=np.int32)
+        cd = np.empty(max(B, 1), dtype=np.int32)
+        n, done = C.c_int32(), C.c_int32()
+        _lib.check(_lib.load().kv_bm_append_batch(self._h, ids.ctypes.data, toks.ctypes.data, B,
+                                                  slots.ctypes.data, cs.ctypes.data,
+                                                  cd.ctypes.data, C.byref(n), C.byref(done)))
+        return slots, np.stack([cs[:n.value], cd[:n.value]], axis=1)
+
     def fork(self, seq: int, child: int) -> None:
         _lib.check(_lib.load().kv_bm_fork(self._h, int(seq), int(child)))
 

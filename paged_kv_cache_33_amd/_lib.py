@@ -44,6 +44,7 @@ EXPORTED = (
     "kv_bm_destroy",
     "kv_bm_admit",
     "kv_bm_append",
+    "kv_bm_append_batch",
     "kv_bm_fork",
     "kv_bm_release",
     "kv_bm_num_free",
@@ -108,6 +109,8 @@ def load() -> C.CDLL:
         "kv_bm_admit": (C.c_int, [vp, C.c_int64, vp, i32, C.c_char_p, i32, C.POINTER(C.c_int32)]),
         "kv_bm_append": (C.c_int, [vp, C.c_int64, i32, i64p, C.POINTER(C.c_int32),
                                    C.POINTER(C.c_int32)]),
+        "kv_bm_append_batch": (C.c_int, [vp, vp, vp, i32, vp, vp, vp, C.POINTER(C.c_int32),
+                                         C.POINTER(C.c_int32)]),
         "kv_bm_fork": (C.c_int, [vp, C.c_int64, C.c_int64]),
         "kv_bm_release": (C.c_int, [vp, C.c_int64]),
         "kv_bm_num_free": (C.c_int32, [vp]),

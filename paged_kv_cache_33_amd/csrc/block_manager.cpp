@@ -384,6 +384,28 @@ kv_status kv_bm_append(kv_block_manager* bm, int64_t seq, int32_t token, int64_t
   return check(bm->impl.append(seq, token, slot, copy_src, copy_dst), "append", seq);
 }
 
+kv_status kv_bm_append_batch(kv_block_manager* bm, const int64_t* seqs, const int32_t* tokens,
+                             int32_t B, int64_t* slots, int32_t* copy_src, int32_t* copy_dst,
+                             int32_t* n_copies, int32_t* done) {
+  if (done) *done = 0;
+  if (!bm || B < 0 || !n_copies || (B > 0 && (!seqs || !tokens || !slots || !copy_src || !copy_dst)))
+    return pagedkv::report(KV_ERR_INVALID_ARG, "append_batch: bad argument");
+  std::lock_guard<std::mutex> lock(bm->impl.mu);
+  *n_copies = 0;
+  for (int32_t b = 0; b < B; ++b) {
+    int32_t cs = -1, cd = -1;
+    const kv_status s = bm->impl.append(seqs[b], tokens[b], &slots[b], &cs, &cd);
+    if (s != KV_OK) return check(s, "append_batch", seqs[b]);
+    if (cs >= 0) {
+      copy_src[*n_copies] = cs;
+      copy_dst[*n_copies] = cd;
+      ++*n_copies;
+    }
+    if (done) *done = b + 1;
+  }
+  return pagedkv::report_ok();
+}
+
 kv_status kv_bm_fork(kv_block_manager* bm, int64_t seq, int64_t child) {
   if (!bm) return pagedkv::report(KV_ERR_INVALID_ARG, "fork: manager is NULL");
   std::lock_guard<std::mutex> lock(bm->impl.mu);

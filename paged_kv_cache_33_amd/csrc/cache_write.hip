@@ -141,25 +141,43 @@ hipError_t launch_slot_mapping(const SlotMappingArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Copy-on-write data copy: work-group (i, c) copies block src[i] of cache c
-// (0 = K, 1 = V) to block dst[i], 16 bytes per thread and step.  Both sides
-// stream (non-temporal): the source is not reread, and the destination's next
-// reader is a later decode, which should not meet dirty lines in the caches.
-__global__ __launch_bounds__(256) void copy_blocks_kernel(CopyBlocksArgs a) {
+// Copy-on-write data copy: work-group (i, c, z) copies slice z (kCopySlice
+// bytes) of block src[i] of cache c (0 = K, 1 = V) to block dst[i], four
+// 16-byte loads in flight per thread.  A lone copy thus still spreads over
+// many work-groups.  Both sides stream (non-temporal): the source is not
+// reread, and the destination's next reader is a later decode, which should
+// not meet dirty lines in the caches.
+constexpr int kCopyThreads = 256;
+constexpr int64_t kCopySlice = int64_t(kCopyThreads) * 16 * 4;
+
+__global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(CopyBlocksArgs a) {
   const int i = blockIdx.x;
   const int32_t s = a.src[i], d = a.dst[i];
   if (s < 0 || s >= a.num_blocks || d < 0 || d >= a.num_blocks || s == d) return;
   char* base = static_cast<char*>(blockIdx.y == 0 ? a.k_cache : a.v_cache);
-  const u32x4_t* from = reinterpret_cast<const u32x4_t*>(base + int64_t(s) * a.block_bytes);
-  u32x4_t* to = reinterpret_cast<u32x4_t*>(base + int64_t(d) * a.block_bytes);
-  const int64_t n16 = a.block_bytes / 16;
-  for (int64_t k = threadIdx.x; k < n16; k += blockDim.x)
-    __builtin_nontemporal_store(__builtin_nontemporal_load(from + k), to + k);
+  const int64_t lo = int64_t(blockIdx.z) * kCopySlice;
+  const int64_t hi = min(lo + kCopySlice, a.block_bytes);
+  const u32x4_t* from = reinterpret_cast<const u32x4_t*>(base + int64_t(s) * a.block_bytes + lo);
+  u32x4_t* to = reinterpret_cast<u32x4_t*>(base + int64_t(d) * a.block_bytes + lo);
+  const int n16 = int((hi - lo) / 16);
+  u32x4_t v[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int k = threadIdx.x + u * kCopyThreads;
+    if (k < n16) v[u] = __builtin_nontemporal_load(from + k);
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int k = threadIdx.x + u * kCopyThreads;
+    if (k < n16) __builtin_nontemporal_store(v[u], to + k);
+  }
 }
 
 hipError_t launch_copy_blocks(const CopyBlocksArgs& a, hipStream_t s) {
   if (a.n == 0) return hipSuccess;
-  hipLaunchKernelGGL(copy_blocks_kernel, dim3(unsigned(a.n), 2), dim3(256), 0, s, a);
+  const unsigned slices = unsigned((a.block_bytes + kCopySlice - 1) / kCopySlice);
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3(unsigned(a.n), 2, slices), dim3(kCopyThreads), 0, s,
+                     a);
   return hipGetLastError();
 }
 

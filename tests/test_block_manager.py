@@ -160,3 +160,27 @@ def test_native_manager_argument_errors():
     lib = P._lib.load()
     assert lib.kv_bm_num_free(None) == -1
     assert lib.kv_copy_blocks(None, None, None, 1, None) == P._lib.KV_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_batched_append_equals_appends_one_by_one(seed):
+    rng = np.random.default_rng(seed)
+    a, b, m = P.BlockManager(64), P.BlockManager(64), BlockManagerModel(64)
+    for mgr in (a, b, m):
+        mgr.admit(1, list(range(40)))
+        mgr.admit(2, list(range(40)) + [5])
+        mgr.fork(2, 3)
+        mgr.fork(1, 4)
+    seqs = [1, 2, 3, 4]
+    for _ in range(30):
+        toks = rng.integers(0, 9, size=4).tolist()
+        slots, copies = a.append_batch(seqs, toks)
+        one = [b.append(s, t) for s, t in zip(seqs, toks)]
+        mod = [m.append(s, t) for s, t in zip(seqs, toks)]
+        assert one == mod
+        assert slots.tolist() == [x[0] for x in one]
+        assert [tuple(c) for c in copies.tolist()] == [x[1] for x in one if x[1] is not None]
+    assert [a.table(s) for s in seqs] == [m.table(s) for s in seqs]
+    with pytest.raises(P.PagedKVError):
+        a.append_batch([1, 99], [0, 0])             # unknown second sequence: first stays appended
+    assert a.num_tokens(1) == m.num_tokens(1) + 1
