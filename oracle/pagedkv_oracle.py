@@ -71,10 +71,12 @@ __all__ = [
     "v_offset",
     "blocks_needed",
     "slot_mapping",
+    "chunk_slots",
     "reshape_and_cache",
     "gather_sequence",
     "decode",
     "decode_sequence",
+    "decode_multi",
     "partials",
     "reduce",
     "kv_bytes",
@@ -219,6 +221,23 @@ def slot_mapping(block_tables: np.ndarray, context_lens: np.ndarray) -> np.ndarr
     return out
 
 
+def chunk_slots(block_tables: np.ndarray, context_lens: np.ndarray,
+                query_start: np.ndarray) -> np.ndarray:
+    """Slots of the n_b newest tokens of each sequence (positions ctx_b - n_b ..
+    ctx_b - 1), n_b = query_start[b+1] - query_start[b]: the [QA] Q1 mapping per
+    position.  -1 where a position is negative (n_b > ctx_b)."""
+    tables = np.asarray(block_tables)
+    qs = np.asarray(query_start, dtype=np.int64)
+    out = np.full(int(qs[-1]), -1, dtype=np.int64)
+    for b in range(len(context_lens)):
+        n = int(qs[b + 1] - qs[b])
+        for j in range(n):
+            pos = int(context_lens[b]) - n + j
+            if pos >= 0:
+                out[qs[b] + j] = int(tables[b, pos // BLOCK]) * BLOCK + pos % BLOCK
+    return out
+
+
 # --------------------------------------------------------------------------
 # the cache write
 # --------------------------------------------------------------------------
@@ -309,6 +328,41 @@ def decode_sequence(k_pool, v_pool, q_b: np.ndarray, table_row, ctx: int,
             s = scale * (K @ q[h])
             p = np.exp(s - s.max())
             out[h] = (p @ V) / p.sum()
+    return out
+
+
+def decode_multi(k_pool, v_pool, q_rows: np.ndarray, query_start, block_tables,
+                 context_lens, H: int, H_kv: int, d: int, dtype: str, scale: float,
+                 k_scale: float = 1.0, v_scale: float = 1.0, seqs=None) -> dict:
+    """Attention of several new query tokens per sequence, causal within them.
+
+    [API] (chunked prefill: a prompt enters in chunks, e.g. of 512 tokens,
+    alongside decode steps), [QA] and [WB] (speculative decoding: the target
+    verifies K draft tokens in one pass).  Sequence b's n_b = query_start[b+1]
+    - query_start[b] query rows (q_rows [T, H, d] bits) are the tokens at
+    positions ctx_b - n_b .. ctx_b - 1, whose K/V rows are already in the cache
+    (context_lens count them); the token at position p attends to positions
+    0..p: the [WB] step() attention with the rows appended one at a time.
+    Returns {b: float64 [n_b, H, d]}.
+    """
+    g = H // H_kv
+    qs = np.asarray(query_start, dtype=np.int64)
+    out = {}
+    for b in (range(len(context_lens)) if seqs is None else seqs):
+        n = int(qs[b + 1] - qs[b])
+        ctx = int(context_lens[b])
+        rows = np.zeros((n, H, d))
+        q = bits_to_f64(q_rows[qs[b]:qs[b + 1]], act_dtype(dtype)).reshape(n, H, d)
+        for kvh in range(H_kv):
+            K, V = gather_sequence(k_pool, v_pool, block_tables[b], ctx, kvh, H_kv, d, dtype,
+                                   k_scale, v_scale)
+            for j in range(n):
+                p = ctx - n + j
+                for h in range(kvh * g, (kvh + 1) * g):
+                    sc = scale * (K[:p + 1] @ q[j, h])
+                    w = np.exp(sc - sc.max())
+                    rows[j, h] = (w @ V[:p + 1]) / w.sum()
+        out[b] = rows
     return out
 
 

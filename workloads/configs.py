@@ -123,6 +123,19 @@ class DecodeStep:
 
 
 @dataclass
+class MultiStep:
+    """Inputs of one step with several new tokens per sequence (a prefill chunk
+    or a block of draft tokens to verify): sequence b's rows are
+    query_start[b] .. query_start[b+1]-1, the tokens at positions
+    context_lens[b] - n_b .. context_lens[b] - 1 (context_lens count them)."""
+    context_lens: np.ndarray      # int32 [B]
+    query_start: np.ndarray       # int32 [B + 1]
+    q: np.ndarray                 # bits [T, H, d]
+    new_k: np.ndarray             # bits [T, H_kv, d]
+    new_v: np.ndarray             # bits [T, H_kv, d]
+
+
+@dataclass
 class Workload:
     name: str
     dtype: str                    # activations (q, out, new rows): "f32" | "bf16"
@@ -140,6 +153,7 @@ class Workload:
     steps: List[DecodeStep] = field(default_factory=list)
     block_size: int = BLOCK_SIZE
     seed: int = 0
+    multi: Optional[MultiStep] = None  # a several-token step, if the workload has one
     kv_dtype: Optional[str] = None  # cache elements: as dtype, or "fp8" (E4M3 codes)
     k_scale: float = 1.0            # per-tensor scales of an fp8 cache
     v_scale: float = 1.0
@@ -216,6 +230,28 @@ def scattered_workload(name: str, dtype: str, B: int, H: int, H_kv: int, d: int,
                     partition_size=partition_size, block_tables=tables,
                     k_pool=k_pool, v_pool=v_pool, steps=[step], seed=seed,
                     kv_dtype=kv_dtype, k_scale=k_scale, v_scale=v_scale)
+
+
+def multi_token_workload(name: str, dtype: str, B: int, H: int, H_kv: int, d: int,
+                         context_lens: Sequence[int], query_lens: Sequence[int], seed: int,
+                         kv_dtype: Optional[str] = None, k_scale: float = 1.0,
+                         v_scale: float = 1.0, max_nb: Optional[int] = None) -> Workload:
+    """A scattered pool as scattered_workload, plus a step of query_lens[b] new
+    tokens per sequence (the last query_lens[b] of its context_lens[b])."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    w = scattered_workload(name, dtype, B, H, H_kv, d, context_lens, seed, rng=rng,
+                           kv_dtype=kv_dtype, k_scale=k_scale, v_scale=v_scale, max_nb=max_nb)
+    qlen = np.asarray(query_lens, dtype=np.int64)
+    if qlen.shape != (B,):
+        raise ValueError("need one query length per sequence")
+    qs = np.zeros(B + 1, dtype=np.int32)
+    qs[1:] = np.cumsum(qlen)
+    T = int(qs[-1])
+    w.multi = MultiStep(context_lens=np.asarray(context_lens, dtype=np.int32), query_start=qs,
+                        q=_normal_bits(rng, T * H * d, dtype).reshape(T, H, d),
+                        new_k=_normal_bits(rng, T * H_kv * d, dtype).reshape(T, H_kv, d),
+                        new_v=_normal_bits(rng, T * H_kv * d, dtype).reshape(T, H_kv, d))
+    return w
 
 
 def _name(config: int, kv_dtype: str) -> str:
