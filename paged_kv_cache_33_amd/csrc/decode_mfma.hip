@@ -9,21 +9,10 @@
 //   O^T [d x 16 heads]       += V^T [d x 16 tokens] . P^T [16 x 16] (d/16 x 16x16x16)
 // Query heads beyond g in the 16-wide tile are zero columns and are never
 // written out.  Softmax is online per head column, as in the VALU kernel.
-//
-// Operand layouts (wave64, lane l, q = l / 16, n = l % 16):
-//   16x16x32 bf16: A row n, k = 8q..8q+7; B column n, k = 8q..8q+7;
-//   16x16x16 bf16: A row n, k = 4q..4q+3; B column n, k = 4q..4q+3;
-//   accumulator: register j holds row 4q + j, column n.
-// K's [d/8][16][8] tile puts the 8 dims of chunk 4i + q of token n in one
-// 16-byte load (a coalesced 1 KiB per wave); the contraction runs over dims in
-// that chunk order, and Q's operand is loaded in the same order.  V's [d][16]
-// tile puts tokens 4q..4q+3 of dim 16mc + n in one 8-byte load (a coalesced
-// 512 B per wave).  The S accumulator (tokens 4q+j of head n) is already the
-// P^T operand of the second product, so no data moves between lanes.
-#include <type_traits>
-
+// The tile code (operands, online softmax per block) is in mfma_tile.h.
 #include "device_common.h"
 #include "launch.h"
+#include "mfma_tile.h"
 #include "work_list.h"
 
 namespace pagedkv {
@@ -35,143 +24,6 @@ namespace {
 // work-list loop does not fit 3 waves per SIMD without spilling.
 template <bool kSplit>
 constexpr int kWavesOf = kSplit ? 8 : 4;
-constexpr int kHeadsPerTile = 16;
-constexpr float kRescaleSlack = 8.f;  // see compute_block
-
-typedef __bf16 bf16x8_t __attribute__((__vector_size__(8 * sizeof(__bf16))));
-typedef short short4_t __attribute__((__vector_size__(4 * sizeof(short))));
-typedef float floatx4_t __attribute__((__vector_size__(4 * sizeof(float))));
-
-template <int D>
-struct MfmaShape {
-  static constexpr int KI = D / 32;  // QK products per block (= 16-byte K loads per lane)
-  static constexpr int MC = D / 16;  // PV products per block (= 8-byte V loads per lane)
-};
-
-// One block's K and V as loaded by one lane.  bf16: 16-byte K chunk 4i + q of
-// token n is operand i of S = K Q^T as stored; 8 bytes of V (tokens 4q..4q+3
-// of dim 16mc + n) are operand mc of O^T = V^T P^T.  fp8 (E4M3 codes): one
-// 16-byte load holds chunk q + 4j (16 dims) and becomes operands 2j, 2j+1
-// (dims 8 and 8 more); 4 bytes of V become operand mc.  The codes convert to
-// bf16 exactly, so both caches feed the same bf16 products.
-template <typename E, int D>
-struct MfmaFrag {
-  static constexpr bool kFp8 = E::kKind == Kind::kFp8;
-  static constexpr int KL = kFp8 ? D / 64 : D / 32;  // 16-byte K loads per lane
-  using VPiece = std::conditional_t<kFp8, uint32_t, uint2>;
-  uint4 k[KL];
-  VPiece v[MfmaShape<D>::MC];
-};
-
-template <typename E, int D>
-__device__ __forceinline__ void load_block(MfmaFrag<E, D>& f, const typename E::storage* kt,
-                                           const typename E::storage* vt, int lane) {
-  constexpr int X = E::kChunk;
-#pragma unroll
-  for (int i = 0; i < MfmaFrag<E, D>::KL; ++i)
-    f.k[i] = load_tile16(kt + (i * kWave + lane) * X);
-  const int n = lane & 15, q = lane >> 4;
-#pragma unroll
-  for (int mc = 0; mc < MfmaShape<D>::MC; ++mc) {
-    if constexpr (MfmaFrag<E, D>::kFp8)
-      f.v[mc] = load_tile4(vt + (16 * mc + n) * kBlockTokens + 4 * q);
-    else
-      f.v[mc] = load_tile8(vt + (16 * mc + n) * kBlockTokens + 4 * q);
-  }
-}
-
-// Operand i of S = K Q^T and operand mc of O^T = V^T P^T, as bf16.
-template <typename E, int D>
-__device__ __forceinline__ bf16x8_t k_operand(const MfmaFrag<E, D>& f, int i) {
-  if constexpr (MfmaFrag<E, D>::kFp8) {
-    const uint4 c = f.k[i >> 1];
-    const uint32_t w0 = (i & 1) ? c.z : c.x, w1 = (i & 1) ? c.w : c.y;
-    return __builtin_bit_cast(bf16x8_t, make_uint4(e4m3x2_to_bf16x2<false>(w0),
-                                                   e4m3x2_to_bf16x2<true>(w0),
-                                                   e4m3x2_to_bf16x2<false>(w1),
-                                                   e4m3x2_to_bf16x2<true>(w1)));
-  } else {
-    return __builtin_bit_cast(bf16x8_t, f.k[i]);
-  }
-}
-template <typename E, int D>
-__device__ __forceinline__ uint2 v_operand(const MfmaFrag<E, D>& f, int mc) {
-  if constexpr (MfmaFrag<E, D>::kFp8)
-    return make_uint2(e4m3x2_to_bf16x2<false>(f.v[mc]), e4m3x2_to_bf16x2<true>(f.v[mc]));
-  else
-    return f.v[mc];
-}
-
-// First query dim of the 8 that pair with K operand i in lane quarter q.
-template <typename E>
-__device__ __forceinline__ int query_dim0(int i, int q) {
-  if constexpr (E::kKind == Kind::kFp8)
-    return (q + 4 * (i >> 1)) * 16 + (i & 1) * 8;
-  else
-    return (4 * i + q) * 8;
-}
-
-template <int D>
-struct MfmaState {
-  floatx4_t o[MfmaShape<D>::MC];  // O^T[16mc + 4q + j][head n]
-  float m;                        // reference max of head n (base 2): within 8 of the max
-  float l;                        // denominator share of head n over tokens 4q..4q+3
-};
-
-__device__ __forceinline__ uint32_t zero_masked_pair(uint32_t w, bool keep_lo, bool keep_hi) {
-  return (keep_lo ? (w & 0x0000ffffu) : 0u) | (keep_hi ? (w & 0xffff0000u) : 0u);
-}
-
-template <typename E, int D, bool kTail>
-__device__ __forceinline__ void compute_block(const MfmaFrag<E, D>& f,
-                                              const bf16x8_t (&qop)[MfmaShape<D>::KI],
-                                              MfmaState<D>& st, int nvalid, float scale_log2,
-                                              int lane) {
-  const int q = lane >> 4;
-  floatx4_t s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int i = 0; i < MfmaShape<D>::KI; ++i)
-    s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand<E, D>(f, i), qop[i], s, 0, 0, 0);
-  float sc[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    sc[j] = s[j] * scale_log2;
-    if (kTail && 4 * q + j >= nvalid) sc[j] = -INFINITY;  // select: the slot may hold NaN
-  }
-  const float mx = cross_row_max(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
-  // The reference max st.m moves only when a head's block max exceeds it by
-  // more than kRescaleSlack (base-2 units), so weights 2^(s - m) stay below 2^8
-  // and most blocks skip rescaling O (32 multiplies at d = 128).  Softmax does
-  // not depend on the reference, so only rounding changes.
-  const bool grow = mx > st.m + kRescaleSlack;
-  if (__builtin_amdgcn_ballot_w64(grow) != 0) {  // wave-uniform branch
-    const float m_new = grow ? mx : st.m;
-    const float alpha = fast_exp2(st.m - m_new);
-    st.l *= alpha;
-#pragma unroll
-    for (int mc = 0; mc < MfmaShape<D>::MC; ++mc) st.o[mc] *= alpha;
-    st.m = m_new;
-  }
-  // weights rounded to bf16 for the matrix core; the denominator sums the
-  // same rounded values
-  const uint32_t p01 = pack_bf16x2(fast_exp2(sc[0] - st.m), fast_exp2(sc[1] - st.m));
-  const uint32_t p23 = pack_bf16x2(fast_exp2(sc[2] - st.m), fast_exp2(sc[3] - st.m));
-  const float psum = (__uint_as_float(p01 << 16) + __uint_as_float(p01 & 0xffff0000u)) +
-                     (__uint_as_float(p23 << 16) + __uint_as_float(p23 & 0xffff0000u));
-  st.l += psum;
-  const short4_t pop = __builtin_bit_cast(short4_t, make_uint2(p01, p23));
-#pragma unroll
-  for (int mc = 0; mc < MfmaShape<D>::MC; ++mc) {
-    uint2 v = v_operand<E, D>(f, mc);
-    if (kTail) {  // tokens past the range get weight 0; their V must be 0, not NaN
-      v.x = zero_masked_pair(v.x, 4 * q + 0 < nvalid, 4 * q + 1 < nvalid);
-      v.y = zero_masked_pair(v.y, 4 * q + 2 < nvalid, 4 * q + 3 < nvalid);
-    }
-    st.o[mc] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(short4_t, v), pop,
-                                                        st.o[mc], 0, 0, 0);
-  }
-}
-
 // One work item: partition `part` of sequence b, head tile `tile_y` (a KV
 // head and a group of up to 16 of its query heads).
 template <typename E, int D, int kWaves>

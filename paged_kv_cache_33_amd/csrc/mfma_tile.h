@@ -1,0 +1,210 @@
+// MFMA tile code shared by the decode kernel (decode_mfma.hip) and the
+// multi-token kernel (multi_mfma.hip): per 16-token block, S = K Q^T and
+// O^T += V^T P^T as gfx950 matrix-core tiles with the online softmax between.
+//
+// Operand layouts (wave64, lane l, q = l / 16, n = l % 16):
+//   16x16x32 bf16: A row n, k = 8q..8q+7; B column n, k = 8q..8q+7;
+//   16x16x16 bf16: A row n, k = 4q..4q+3; B column n, k = 4q..4q+3;
+//   accumulator: register j holds row 4q + j, column n.
+// K's [d/8][16][8] tile puts the 8 dims of chunk 4i + q of token n in one
+// 16-byte load (a coalesced 1 KiB per wave); the contraction runs over dims in
+// that chunk order, and Q's operand is loaded in the same order.  V's [d][16]
+// tile puts tokens 4q..4q+3 of dim 16mc + n in one 8-byte load (a coalesced
+// 512 B per wave).  The S accumulator (tokens 4q+j of head n) is already the
+// P^T operand of the second product, so no data moves between lanes.
+#pragma once
+
+#include <type_traits>
+
+#include "device_common.h"
+
+namespace pagedkv {
+namespace {
+
+constexpr int kHeadsPerTile = 16;
+constexpr float kRescaleSlack = 8.f;  // see compute_block
+
+typedef __bf16 bf16x8_t __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef short short4_t __attribute__((__vector_size__(4 * sizeof(short))));
+typedef float floatx4_t __attribute__((__vector_size__(4 * sizeof(float))));
+
+template <int D>
+struct MfmaShape {
+  static constexpr int KI = D / 32;  // QK products per block (= 16-byte K loads per lane)
+  static constexpr int MC = D / 16;  // PV products per block (= 8-byte V loads per lane)
+};
+
+// One block's K and V as loaded by one lane.  bf16: 16-byte K chunk 4i + q of
+// token n is operand i of S = K Q^T as stored; 8 bytes of V (tokens 4q..4q+3
+// of dim 16mc + n) are operand mc of O^T = V^T P^T.  fp8 (E4M3 codes): one
+// 16-byte load holds chunk q + 4j (16 dims) and becomes operands 2j, 2j+1
+// (dims 8 and 8 more); 4 bytes of V become operand mc.  The codes convert to
+// bf16 exactly, so both caches feed the same bf16 products.
+template <typename E, int D>
+struct MfmaFrag {
+  static constexpr bool kFp8 = E::kKind == Kind::kFp8;
+  static constexpr int KL = kFp8 ? D / 64 : D / 32;  // 16-byte K loads per lane
+  using VPiece = std::conditional_t<kFp8, uint32_t, uint2>;
+  uint4 k[KL];
+  VPiece v[MfmaShape<D>::MC];
+};
+
+template <typename E, int D>
+__device__ __forceinline__ void load_block(MfmaFrag<E, D>& f, const typename E::storage* kt,
+                                           const typename E::storage* vt, int lane) {
+  constexpr int X = E::kChunk;
+#pragma unroll
+  for (int i = 0; i < MfmaFrag<E, D>::KL; ++i)
+    f.k[i] = load_tile16(kt + (i * kWave + lane) * X);
+  const int n = lane & 15, q = lane >> 4;
+#pragma unroll
+  for (int mc = 0; mc < MfmaShape<D>::MC; ++mc) {
+    if constexpr (MfmaFrag<E, D>::kFp8)
+      f.v[mc] = load_tile4(vt + (16 * mc + n) * kBlockTokens + 4 * q);
+    else
+      f.v[mc] = load_tile8(vt + (16 * mc + n) * kBlockTokens + 4 * q);
+  }
+}
+
+// Operand i of S = K Q^T and operand mc of O^T = V^T P^T, as bf16.
+template <typename E, int D>
+__device__ __forceinline__ bf16x8_t k_operand(const MfmaFrag<E, D>& f, int i) {
+  if constexpr (MfmaFrag<E, D>::kFp8) {
+    const uint4 c = f.k[i >> 1];
+    const uint32_t w0 = (i & 1) ? c.z : c.x, w1 = (i & 1) ? c.w : c.y;
+    return __builtin_bit_cast(bf16x8_t, make_uint4(e4m3x2_to_bf16x2<false>(w0),
+                                                   e4m3x2_to_bf16x2<true>(w0),
+                                                   e4m3x2_to_bf16x2<false>(w1),
+                                                   e4m3x2_to_bf16x2<true>(w1)));
+  } else {
+    return __builtin_bit_cast(bf16x8_t, f.k[i]);
+  }
+}
+template <typename E, int D>
+__device__ __forceinline__ uint2 v_operand(const MfmaFrag<E, D>& f, int mc) {
+  if constexpr (MfmaFrag<E, D>::kFp8)
+    return make_uint2(e4m3x2_to_bf16x2<false>(f.v[mc]), e4m3x2_to_bf16x2<true>(f.v[mc]));
+  else
+    return f.v[mc];
+}
+
+// First query dim of the 8 that pair with K operand i in lane quarter q.
+template <typename E>
+__device__ __forceinline__ int query_dim0(int i, int q) {
+  if constexpr (E::kKind == Kind::kFp8)
+    return (q + 4 * (i >> 1)) * 16 + (i & 1) * 8;
+  else
+    return (4 * i + q) * 8;
+}
+
+template <int D>
+struct MfmaState {
+  floatx4_t o[MfmaShape<D>::MC];  // O^T[16mc + 4q + j][head n]
+  float m;                        // reference max of head n (base 2): within 8 of the max
+  float l;                        // denominator share of head n over tokens 4q..4q+3
+};
+
+__device__ __forceinline__ uint32_t zero_masked_pair(uint32_t w, bool keep_lo, bool keep_hi) {
+  return (keep_lo ? (w & 0x0000ffffu) : 0u) | (keep_hi ? (w & 0xffff0000u) : 0u);
+}
+
+// One 16-token block: S = K Q^T, the online softmax per column, O^T += V^T P^T.
+// nvalid (uniform): tokens of the block inside the range; with kTail the rest
+// get no weight and their V is zeroed (their slots may hold NaN).  kCausal: the
+// block's first token is at key position key0 and this lane's column may see
+// positions <= limit only.
+template <typename E, int D, bool kTail, bool kCausal = false>
+__device__ __forceinline__ void compute_block(const MfmaFrag<E, D>& f,
+                                              const bf16x8_t (&qop)[MfmaShape<D>::KI],
+                                              MfmaState<D>& st, int nvalid, float scale_log2,
+                                              int lane, int key0 = 0, int limit = 0) {
+  const int q = lane >> 4;
+  floatx4_t s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < MfmaShape<D>::KI; ++i)
+    s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand<E, D>(f, i), qop[i], s, 0, 0, 0);
+  float sc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    sc[j] = s[j] * scale_log2;
+    if (kTail && 4 * q + j >= nvalid) sc[j] = -INFINITY;  // select: the slot may hold NaN
+    if (kCausal && key0 + 4 * q + j > limit) sc[j] = -INFINITY;
+  }
+  const float mx = cross_row_max(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
+  // The reference max st.m moves only when a head's block max exceeds it by
+  // more than kRescaleSlack (base-2 units), so weights 2^(s - m) stay below 2^8
+  // and most blocks skip rescaling O (32 multiplies at d = 128).  Softmax does
+  // not depend on the reference, so only rounding changes.
+  const bool grow = mx > st.m + kRescaleSlack;
+  if (__builtin_amdgcn_ballot_w64(grow) != 0) {  // wave-uniform branch
+    const float m_new = grow ? mx : st.m;
+    const float alpha = fast_exp2(st.m - m_new);
+    st.l *= alpha;
+#pragma unroll
+    for (int mc = 0; mc < MfmaShape<D>::MC; ++mc) st.o[mc] *= alpha;
+    st.m = m_new;
+  }
+  // weights rounded to bf16 for the matrix core; the denominator sums the
+  // same rounded values.  Causal: a column that has seen no position yet
+  // (every score -inf) takes weight 0, not 2^(-inf - -inf).
+  const float mref = (kCausal && st.m == -INFINITY) ? 0.f : st.m;
+  const uint32_t p01 = pack_bf16x2(fast_exp2(sc[0] - mref), fast_exp2(sc[1] - mref));
+  const uint32_t p23 = pack_bf16x2(fast_exp2(sc[2] - mref), fast_exp2(sc[3] - mref));
+  const float psum = (__uint_as_float(p01 << 16) + __uint_as_float(p01 & 0xffff0000u)) +
+                     (__uint_as_float(p23 << 16) + __uint_as_float(p23 & 0xffff0000u));
+  st.l += psum;
+  const short4_t pop = __builtin_bit_cast(short4_t, make_uint2(p01, p23));
+#pragma unroll
+  for (int mc = 0; mc < MfmaShape<D>::MC; ++mc) {
+    uint2 v = v_operand<E, D>(f, mc);
+    if (kTail) {  // tokens past the range get weight 0; their V must be 0, not NaN
+      v.x = zero_masked_pair(v.x, 4 * q + 0 < nvalid, 4 * q + 1 < nvalid);
+      v.y = zero_masked_pair(v.y, 4 * q + 2 < nvalid, 4 * q + 3 < nvalid);
+    }
+    st.o[mc] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(short4_t, v), pop,
+                                                        st.o[mc], 0, 0, 0);
+  }
+}
+
+
+// Walk a wave's blocks j = jb + w, jb + w + kWaves, ... < je.  Table entries
+// are read 64 at a time into one register (lane i holds the entry of the
+// wave's block n0 + i) so no tile load waits on a dependent table load; win
+// holds the first window on entry.  fetch(entry, frag) loads a block's tiles
+// (unconditionally: an entry outside the pool loads tile 0 and is reported as
+// -1) and returns its tile offset or -1; consume(j, tile, frag) computes it.
+// Two register buffers ping-pong, and inside a window every iteration has a
+// next block to fetch (the last one or two are peeled off), so the loads of
+// block n+1 stay in flight while block n computes.
+template <int kWaves, typename Frag, typename Fetch, typename Consume>
+__device__ __forceinline__ void walk_blocks(int jb, int je, int w, int lane,
+                                            const int32_t* table, int win, Fetch&& fetch,
+                                            Consume&& consume) {
+  const int nblk = je - jb - w > 0 ? (je - jb - w + kWaves - 1) / kWaves : 0;
+  Frag fa, fb;
+  for (int n0 = 0; n0 < nblk; n0 += kWave) {
+    const int cnt = min(kWave, nblk - n0);
+    if (n0 > 0) {
+      const int jj = jb + w + kWaves * (n0 + lane);
+      win = lane < cnt ? table[jj] : -1;
+    }
+    int64_t tile_a = fetch(__builtin_amdgcn_readlane(win, 0), fa), tile_b;
+    int n = 0;
+    for (; n + 2 < cnt; n += 2) {
+      tile_b = fetch(__builtin_amdgcn_readlane(win, n + 1), fb);
+      consume(jb + w + kWaves * (n0 + n), tile_a, fa);
+      tile_a = fetch(__builtin_amdgcn_readlane(win, n + 2), fa);
+      consume(jb + w + kWaves * (n0 + n + 1), tile_b, fb);
+    }
+    if (n + 1 < cnt) {
+      tile_b = fetch(__builtin_amdgcn_readlane(win, n + 1), fb);
+      consume(jb + w + kWaves * (n0 + n), tile_a, fa);
+      consume(jb + w + kWaves * (n0 + n + 1), tile_b, fb);
+    } else {
+      consume(jb + w + kWaves * (n0 + n), tile_a, fa);
+    }
+  }
+}
+
+}  // namespace
+}  // namespace pagedkv
