@@ -159,6 +159,27 @@ kv_status kv_cache_append(const kv_pool* pool, const void* key, const void* valu
                           const int32_t* context_lens, int32_t B, int64_t* slot_mapping,
                           void* stream);
 
+/* Append several new tokens per sequence (a prefill chunk, or draft tokens to
+ * verify) in one launch: sequence b's n_b = query_start[b+1] - query_start[b]
+ * rows, key/value rows query_start[b] .. query_start[b+1]-1 (device
+ * [num_rows][H_kv][d] of the activation type), are the tokens at positions
+ * ctx_b - n_b .. ctx_b - 1 (context_lens count them, as for kv_cache_append);
+ * row j is stored, as reshape_and_cache stores it, into block
+ * block_tables[b*max_nb + p/16], slot p % 16, p = ctx_b - n_b + j.  This is
+ * the workbook's append step for the n_b rows of one pass, as chunked prefill
+ * ("Anthropic Interview: Design an LLM Inference API with GPU Batching",
+ * scheduling) and speculative verification (the Q&A page) feed them.
+ * query_start: device int32 [B+1]; max_query_len: a host bound on every n_b
+ * (rows j >= max_query_len are not written).  slot_mapping: optional device
+ * int64 [num_rows] receiving each row's slot, or -1 where nothing was written:
+ * p < 0, p >= max_nb*16 or a table entry outside the pool.  A sequence whose
+ * rows do not lie inside [0, num_rows) is skipped whole. */
+kv_status kv_cache_append_chunk(const kv_pool* pool, const void* key, const void* value,
+                                int32_t num_rows, const int32_t* query_start,
+                                int32_t max_query_len, const int32_t* block_tables,
+                                int32_t max_nb, const int32_t* context_lens, int32_t B,
+                                int64_t* slot_mapping, void* stream);
+
 /* Workspace bytes paged_attention_decode needs in split mode: with
  * P = ceil(max_context_len / partition_size) partitions per sequence,
  *   o: float [B][H][P][d], then m: float [B][H][P], then l: float [B][H][P]
@@ -206,6 +227,31 @@ kv_status paged_attention_reduce(void* out, const void* workspace,
                                  int32_t head_dim, int32_t max_context_len,
                                  int32_t partition_size, kv_dtype out_dtype,
                                  void* stream);
+
+/* Attention of several new query tokens per sequence, causal within them: the
+ * workbook's incremental decoder with the rows appended one at a time,
+ * evaluated for all of them in one pass (a prefill chunk; the K draft tokens
+ * speculative decoding verifies, the Q&A page and the workbook).  Sequence b
+ * has n_b = query_start[b+1] - query_start[b] query rows, rows query_start[b]
+ * .. query_start[b+1]-1 of query (device [num_rows][H][d], bf16), the tokens
+ * at positions ctx_b - n_b .. ctx_b - 1 whose K/V rows are already cached
+ * (context_lens count them; write them first with kv_cache_append_chunk).
+ * The row at position p gets
+ *   out[row][h][:] = softmax_t(scale * q[row][h] . K_b[t]) V_b[t], t <= p,
+ * with K_b, V_b read through the block table as in paged_attention_decode;
+ * out: device [num_rows][H][d], bf16 (rounded to nearest-even).  n_b = 1 is
+ * the decode step.  Matrix-core kernel for every H / H_kv, bf16 or fp8 pools
+ * (KV_F32 is refused).  max_query_len: a host bound on every n_b.  Rows of a
+ * sequence with n_b > ctx_b, n_b > max_query_len or ctx_b > max_nb*16 are NaN
+ * (those below max_query_len; nothing is written past it).  A table entry
+ * outside the pool that a row's range reaches makes that row NaN (and may make
+ * other rows of its sequence NaN).  n_b <= 0 writes nothing, and a sequence
+ * whose rows do not lie inside [0, num_rows) is skipped whole. */
+kv_status paged_attention_multi(const kv_pool* pool, void* out, const void* query,
+                                int32_t num_rows, const int32_t* query_start,
+                                int32_t max_query_len, const int32_t* block_tables,
+                                int32_t max_nb, const int32_t* context_lens, int32_t B, int32_t H,
+                                float scale, void* stream);
 
 /* Copy whole blocks on the GPU: for i < n, block src[i] of both caches (all KV
  * heads, all 16 slots, K and V) is copied to block dst[i].  This is the data

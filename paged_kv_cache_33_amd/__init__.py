@@ -28,9 +28,11 @@ __all__ = [
     "kv_slot_mapping",
     "reshape_and_cache",
     "kv_cache_append",
+    "kv_cache_append_chunk",
     "paged_attention_workspace_bytes",
     "paged_attention_decode",
     "paged_attention_reduce",
+    "paged_attention_multi",
     "kv_decode_kernel_kind",
     "kv_copy_blocks",
     "BlockManager",
@@ -218,6 +220,53 @@ def kv_cache_append(pool: KVPool, key: torch.Tensor, value: torch.Tensor,
                                                 dtype=torch.int64)
     _lib.check(_lib.load().kv_cache_append(pool.handle, kp, vp, tp, max_nb, cp, B, sp,
                                            _stream_handle(stream)))
+
+
+def kv_cache_append_chunk(pool: KVPool, key: torch.Tensor, value: torch.Tensor,
+                          query_start: torch.Tensor, max_query_len: int,
+                          block_tables: torch.Tensor, context_lens: torch.Tensor,
+                          slot_mapping: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Append the n_b = query_start[b+1] - query_start[b] newest tokens of each
+    sequence (rows [num_rows, H_kv, d]) at positions ctx - n_b .. ctx - 1; see
+    pagedkv.h."""
+    if block_tables.dim() != 2:
+        raise ValueError("block_tables must be [B, max_nb]")
+    B, max_nb = block_tables.shape
+    if key.dim() != 3:
+        raise ValueError("key must be [num_rows, H_kv, head_dim]")
+    T = int(key.shape[0])
+    row = T * pool.num_kv_heads * pool.head_dim * pool.act_size
+    kp = _buf(key, "key", row, elem_size=pool.act_size)
+    vp = _buf(value, "value", row, elem_size=pool.act_size)
+    qsp = _buf(query_start, "query_start", 4 * (B + 1), dtype=torch.int32)
+    tp = _buf(block_tables, "block_tables", dtype=torch.int32)
+    cp = _buf(context_lens, "context_lens", 4 * B, dtype=torch.int32)
+    sp = None if slot_mapping is None else _buf(slot_mapping, "slot_mapping", 8 * T,
+                                                dtype=torch.int64)
+    _lib.check(_lib.load().kv_cache_append_chunk(pool.handle, kp, vp, T, qsp, int(max_query_len),
+                                                 tp, max_nb, cp, B, sp, _stream_handle(stream)))
+
+
+def paged_attention_multi(pool: KVPool, out: torch.Tensor, query: torch.Tensor,
+                          query_start: torch.Tensor, max_query_len: int,
+                          block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
+                          stream=None) -> None:
+    """Attention of several new query rows per sequence ([num_rows, H, d], bf16),
+    causal within each sequence's rows; see pagedkv.h."""
+    if query.dim() != 3 or query.shape[2] != pool.head_dim:
+        raise ValueError("query must be [num_rows, H, head_dim]")
+    T, H, d = query.shape
+    if block_tables.dim() != 2:
+        raise ValueError("block_tables must be [B, max_nb]")
+    B, max_nb = block_tables.shape
+    qp = _buf(query, "query", T * H * d * 2, elem_size=2)
+    op = _buf(out, "out", T * H * d * 2, elem_size=2)
+    qsp = _buf(query_start, "query_start", 4 * (B + 1), dtype=torch.int32)
+    tp = _buf(block_tables, "block_tables", dtype=torch.int32)
+    cp = _buf(context_lens, "context_lens", 4 * B, dtype=torch.int32)
+    _lib.check(_lib.load().paged_attention_multi(
+        pool.handle, op, qp, T, qsp, int(max_query_len), tp, max_nb, cp, B, H, float(scale),
+        _stream_handle(stream)))
 
 
 def paged_attention_workspace_bytes(B: int, H: int, head_dim: int, max_context_len: int,

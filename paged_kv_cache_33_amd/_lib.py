@@ -36,9 +36,11 @@ EXPORTED = (
     "kv_slot_mapping",
     "reshape_and_cache",
     "kv_cache_append",
+    "kv_cache_append_chunk",
     "paged_attention_workspace_bytes",
     "paged_attention_decode",
     "paged_attention_reduce",
+    "paged_attention_multi",
     "kv_copy_blocks",
     "kv_bm_create",
     "kv_bm_destroy",
@@ -103,6 +105,10 @@ def load() -> C.CDLL:
                                              C.c_float, i32, vp, sz, vp]),
         "kv_cache_append": (C.c_int, [vp, vp, vp, i32p, i32, i32p, i32, vp, vp]),
         "paged_attention_reduce": (C.c_int, [vp, vp, i32p, i32, i32, i32, i32, i32, C.c_int, vp]),
+        "kv_cache_append_chunk": (C.c_int, [vp, vp, vp, i32, i32p, i32, i32p, i32, i32p, i32,
+                                            vp, vp]),
+        "paged_attention_multi": (C.c_int, [vp, vp, vp, i32, i32p, i32, i32p, i32, i32p, i32,
+                                            i32, C.c_float, vp]),
         "kv_copy_blocks": (C.c_int, [vp, i32p, i32p, i32, vp]),
         "kv_bm_create": (C.c_int, [i32, C.POINTER(vp)]),
         "kv_bm_destroy": (None, [vp]),

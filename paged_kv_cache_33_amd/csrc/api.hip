@@ -325,6 +325,95 @@ kv_status kv_cache_append(const kv_pool* pool, const void* key, const void* valu
                     "append launch");
 }
 
+kv_status kv_cache_append_chunk(const kv_pool* pool, const void* key, const void* value,
+                                int32_t num_rows, const int32_t* query_start,
+                                int32_t max_query_len, const int32_t* block_tables,
+                                int32_t max_nb, const int32_t* context_lens, int32_t B,
+                                int64_t* slot_mapping, void* stream) {
+  if (!pool) return fail(KV_ERR_INVALID_ARG, "pool is NULL");
+  if (B < 0 || num_rows < 0 || max_query_len < 0)
+    return fail(KV_ERR_INVALID_ARG, "B, num_rows and max_query_len must be >= 0");
+  if (max_nb < 1) return fail(KV_ERR_INVALID_ARG, "max_nb must be >= 1");
+  if (B == 0 || num_rows == 0 || max_query_len == 0) return ok();
+  if (!key || !value || !query_start || !block_tables || !context_lens)
+    return fail(KV_ERR_INVALID_ARG,
+                "key, value, query_start, block_tables and context_lens must be non-NULL");
+  if (!aligned16(key) || !aligned16(value))
+    return fail(KV_ERR_INVALID_ARG, "key and value must be 16-byte aligned");
+  const kv_pool_desc& d = pool->desc;
+  pagedkv::AppendArgs a{};
+  a.k_cache = pool->k_cache;
+  a.v_cache = pool->v_cache;
+  a.num_blocks = d.num_blocks;
+  a.num_kv_heads = d.num_kv_heads;
+  a.head_dim = d.head_dim;
+  a.key = key;
+  a.value = value;
+  a.block_tables = block_tables;
+  a.max_nb = max_nb;
+  a.context_lens = context_lens;
+  a.B = B;
+  a.slot_mapping = slot_mapping;
+  a.k_scale = d.k_scale;
+  a.v_scale = d.v_scale;
+  a.query_start = query_start;
+  a.max_query_len = max_query_len;
+  a.num_rows = num_rows;
+  return hip_status(pagedkv::launch_append(a, kind_of(d.dtype), static_cast<hipStream_t>(stream)),
+                    "chunk append launch");
+}
+
+kv_status paged_attention_multi(const kv_pool* pool, void* out, const void* query,
+                                int32_t num_rows, const int32_t* query_start,
+                                int32_t max_query_len, const int32_t* block_tables,
+                                int32_t max_nb, const int32_t* context_lens, int32_t B, int32_t H,
+                                float scale, void* stream) {
+  if (!pool) return fail(KV_ERR_INVALID_ARG, "pool is NULL");
+  const kv_pool_desc& d = pool->desc;
+  if (d.dtype != KV_BF16 && d.dtype != KV_FP8_E4M3)
+    return fail(KV_ERR_UNSUPPORTED, "multi-token attention needs a bf16 or fp8 pool (dtype %d)",
+                int(d.dtype));
+  if (B < 0 || num_rows < 0 || max_query_len < 0)
+    return fail(KV_ERR_INVALID_ARG, "B, num_rows and max_query_len must be >= 0");
+  if (H < 1 || H % d.num_kv_heads != 0)
+    return fail(KV_ERR_INVALID_ARG, "H (%d) must be a positive multiple of num_kv_heads (%d)", H,
+                d.num_kv_heads);
+  if (max_nb < 1) return fail(KV_ERR_INVALID_ARG, "max_nb must be >= 1");
+  if (!(scale == scale)) return fail(KV_ERR_INVALID_ARG, "scale is NaN");
+  if (B > 65535) return fail(KV_ERR_UNSUPPORTED, "at most 65535 sequences per call (got %d)", B);
+  const int64_t tiles = (int64_t(max_query_len) * (H / d.num_kv_heads) + 15) / 16;
+  if (tiles > (int64_t(1) << 30))
+    return fail(KV_ERR_INVALID_ARG, "max_query_len * H / H_kv is too large");
+  if (B == 0 || num_rows == 0 || max_query_len == 0) return ok();
+  if (!out || !query || !query_start || !block_tables || !context_lens)
+    return fail(KV_ERR_INVALID_ARG,
+                "out, query, query_start, block_tables and context_lens must be non-NULL");
+  if (!aligned16(query) || !aligned16(out))
+    return fail(KV_ERR_INVALID_ARG, "query and out must be 16-byte aligned");
+  pagedkv::MultiArgs a{};
+  a.k_cache = pool->k_cache;
+  a.v_cache = pool->v_cache;
+  a.num_blocks = d.num_blocks;
+  a.num_kv_heads = d.num_kv_heads;
+  a.query = query;
+  a.out = out;
+  a.num_rows = num_rows;
+  a.query_start = query_start;
+  a.max_query_len = max_query_len;
+  a.block_tables = block_tables;
+  a.max_nb = max_nb;
+  a.context_lens = context_lens;
+  a.B = B;
+  a.H = H;
+  const bool fp8 = d.dtype == KV_FP8_E4M3;
+  a.scale_log2 = scale * 1.4426950408889634f * (fp8 ? d.k_scale : 1.f);
+  a.v_scale = fp8 ? d.v_scale : 1.f;
+  a.tiles_per_group = static_cast<int32_t>(tiles < 4 ? tiles : 4);
+  return hip_status(pagedkv::launch_multi_mfma(a, kind_of(d.dtype), d.head_dim,
+                                               static_cast<hipStream_t>(stream)),
+                    "multi-token attention launch");
+}
+
 kv_status kv_copy_blocks(const kv_pool* pool, const int32_t* src, const int32_t* dst, int32_t n,
                          void* stream) {
   if (!pool) return fail(KV_ERR_INVALID_ARG, "pool is NULL");

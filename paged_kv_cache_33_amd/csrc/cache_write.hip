@@ -1,4 +1,5 @@
-// Slot mapping and the cache write (reshape_and_cache, kv_cache_append).
+// Slot mapping and the cache write (reshape_and_cache, kv_cache_append,
+// kv_cache_append_chunk).
 //
 // The block-table mapping is the one "MLSys Engineer - Inference Systems Q&A",
 // Q1 gives: logical position i lives in block table[i / 16] at slot i % 16.  The
@@ -133,6 +134,45 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
                         vc);
 }
 
+// Several new tokens per sequence (a prefill chunk, draft tokens): one thread
+// per (row j of sequence b, kv head, 16-byte chunk), over j < max_query_len.
+// Row query_start[b] + j sits at position ctx - n + j (n = query_start[b+1] -
+// query_start[b]); its slot follows the table as for one token.  A sequence
+// whose rows are not inside [0, num_rows) is skipped whole; a row whose
+// position is negative or past the table, or whose entry is outside the pool,
+// gets slot -1 and no write.
+template <typename Tr>
+__global__ __launch_bounds__(256) void append_chunk_kernel(AppendArgs a) {
+  constexpr int X = Tr::kChunk;
+  const int C = a.head_dim / X;
+  const int64_t per_row = int64_t(a.num_kv_heads) * C;
+  const int64_t total = int64_t(a.max_query_len) * a.B * per_row;
+  const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx >= total) return;
+  const int c = int(idx % C);
+  const int h = int((idx / C) % a.num_kv_heads);
+  const int64_t rb = idx / per_row;  // j * B + b: neighbouring threads share j
+  const int b = int(rb % a.B);
+  const int j = int(rb / a.B);
+  const int32_t q0 = a.query_start[b], q1 = a.query_start[b + 1];
+  if (q0 < 0 || q1 > a.num_rows || j >= q1 - q0) return;
+  const int64_t row = int64_t(q0) + j;
+  const int64_t src = (row * a.num_kv_heads + h) * a.head_dim + int64_t(c) * X;
+  const uint4 kc = source_chunk<Tr>(a.key, src, a.k_scale);
+  const uint4 vc = source_chunk<Tr>(a.value, src, a.v_scale);
+  const int64_t pos = int64_t(a.context_lens[b]) - (q1 - q0) + j;
+  int64_t slot = -1;
+  if (pos >= 0 && pos < int64_t(a.max_nb) * kBlockTokens) {
+    const int32_t blk = a.block_tables[int64_t(b) * a.max_nb + pos / kBlockTokens];
+    if (blk >= 0 && blk < a.num_blocks) slot = int64_t(blk) * kBlockTokens + pos % kBlockTokens;
+  }
+  if (a.slot_mapping && h == 0 && c == 0) a.slot_mapping[row] = slot;
+  if (slot < 0) return;
+  const int64_t tile = (slot / kBlockTokens) * a.num_kv_heads + h;
+  write_token_chunk<Tr>(a.k_cache, a.v_cache, tile, C, a.head_dim, c, int(slot % kBlockTokens), kc,
+                        vc);
+}
+
 hipError_t launch_slot_mapping(const SlotMappingArgs& a, hipStream_t s) {
   if (a.B == 0) return hipSuccess;
   const int threads = 256;
@@ -204,22 +244,22 @@ hipError_t launch_cache_write(const CacheWriteArgs& a, Kind kind, hipStream_t s)
   return hipGetLastError();
 }
 
+template <typename Tr>
+static void (*append_kernel_for(bool chunk))(AppendArgs) {
+  return chunk ? append_chunk_kernel<Tr> : append_kernel<Tr>;
+}
+
 hipError_t launch_append(const AppendArgs& a, Kind kind, hipStream_t s) {
-  const int64_t total = int64_t(a.B) * a.num_kv_heads * (a.head_dim / chunk_elems(kind));
+  const bool chunk = a.query_start != nullptr;
+  const int64_t rows = chunk ? int64_t(a.max_query_len) * a.B : a.B;
+  const int64_t total = rows * a.num_kv_heads * (a.head_dim / chunk_elems(kind));
   if (total == 0) return hipSuccess;
   const int threads = 256;
   const unsigned blocks = unsigned((total + threads - 1) / threads);
-  switch (kind) {
-    case Kind::kBf16:
-      hipLaunchKernelGGL(append_kernel<Bf16>, dim3(blocks), dim3(threads), 0, s, a);
-      break;
-    case Kind::kF32:
-      hipLaunchKernelGGL(append_kernel<F32>, dim3(blocks), dim3(threads), 0, s, a);
-      break;
-    case Kind::kFp8:
-      hipLaunchKernelGGL(append_kernel<Fp8>, dim3(blocks), dim3(threads), 0, s, a);
-      break;
-  }
+  void (*kern)(AppendArgs) = kind == Kind::kBf16  ? append_kernel_for<Bf16>(chunk)
+                             : kind == Kind::kFp8 ? append_kernel_for<Fp8>(chunk)
+                                                  : append_kernel_for<F32>(chunk);
+  hipLaunchKernelGGL(kern, dim3(blocks), dim3(threads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -40,6 +40,29 @@ struct DecodeArgs {
   float* ws_l;                 // [B][H][P]
 };
 
+// Several new query tokens per sequence (a prefill chunk or draft tokens to
+// verify), causal within them.  Sequence b's rows are query_start[b] ..
+// query_start[b+1]-1, at positions ctx_b - n_b .. ctx_b - 1.
+struct MultiArgs {
+  const void* k_cache;
+  const void* v_cache;
+  int32_t num_blocks;
+  int32_t num_kv_heads;
+  const void* query;            // [num_rows][H][d]
+  void* out;                    // [num_rows][H][d]
+  int32_t num_rows;
+  const int32_t* query_start;   // [B+1]
+  int32_t max_query_len;
+  const int32_t* block_tables;  // [B][max_nb]
+  int32_t max_nb;
+  const int32_t* context_lens;  // [B]
+  int32_t B;
+  int32_t H;
+  float scale_log2;             // as DecodeArgs
+  float v_scale;
+  int32_t tiles_per_group;      // 16-column tiles one work-group takes (1..4)
+};
+
 struct ReduceArgs {
   void* out;
   const float* ws_o;
@@ -80,9 +103,15 @@ struct AppendArgs {
   int32_t max_nb;
   const int32_t* context_lens;  // [B]
   int32_t B;
-  int64_t* slot_mapping;        // optional [B] out
+  int64_t* slot_mapping;        // optional [B] out ([num_rows] with query_start)
   float k_scale;                // fp8: stored code = e4m3(x / scale)
   float v_scale;
+  // Several rows per sequence: with query_start non-NULL, key/value are
+  // [num_rows][H_kv][d] and sequence b's rows query_start[b] .. [b+1]-1 sit at
+  // positions ctx_b - n_b .. ctx_b - 1 (n_b <= max_query_len).
+  const int32_t* query_start;
+  int32_t max_query_len;
+  int32_t num_rows;
 };
 
 // Whole-block copies (copy-on-write): block src[i] -> dst[i] in both caches.
@@ -111,6 +140,7 @@ hipError_t launch_append(const AppendArgs& a, Kind kind, hipStream_t s);
 hipError_t launch_copy_blocks(const CopyBlocksArgs& a, hipStream_t s);
 hipError_t launch_decode_valu(const DecodeArgs& a, Kind kind, int head_dim, hipStream_t s);
 hipError_t launch_decode_mfma(const DecodeArgs& a, Kind kind, int head_dim, hipStream_t s);
+hipError_t launch_multi_mfma(const MultiArgs& a, Kind kind, int head_dim, hipStream_t s);
 hipError_t launch_reduce(const ReduceArgs& a, bool bf16_out, hipStream_t s);
 
 }  // namespace pagedkv

@@ -167,41 +167,39 @@ __device__ __forceinline__ void compute_block(const MfmaFrag<E, D>& f,
 }
 
 
-// Walk a wave's blocks j = jb + w, jb + w + kWaves, ... < je.  Table entries
-// are read 64 at a time into one register (lane i holds the entry of the
-// wave's block n0 + i) so no tile load waits on a dependent table load; win
-// holds the first window on entry.  fetch(entry, frag) loads a block's tiles
-// (unconditionally: an entry outside the pool loads tile 0 and is reported as
-// -1) and returns its tile offset or -1; consume(j, tile, frag) computes it.
-// Two register buffers ping-pong, and inside a window every iteration has a
-// next block to fetch (the last one or two are peeled off), so the loads of
-// block n+1 stay in flight while block n computes.
-template <int kWaves, typename Frag, typename Fetch, typename Consume>
-__device__ __forceinline__ void walk_blocks(int jb, int je, int w, int lane,
-                                            const int32_t* table, int win, Fetch&& fetch,
+// Walk a wave's blocks j = first, first + stride, ... < je.  Table entries are
+// read 64 at a time into one register (lane i holds the entry of the wave's
+// block n0 + i) so no tile load waits on a dependent table load.
+// fetch(entry, frag) loads a block's tiles (unconditionally: an entry outside
+// the pool loads tile 0 and is reported as -1) and returns its tile offset or
+// -1; consume(j, tile, frag) computes it.  Two register buffers ping-pong, and
+// inside a window every iteration has a next block to fetch (the last one or
+// two are peeled off), so the loads of block n+1 stay in flight while block n
+// computes.
+template <typename Frag, typename Fetch, typename Consume>
+__device__ __forceinline__ void walk_blocks(int first, int stride, int je, int lane,
+                                            const int32_t* table, Fetch&& fetch,
                                             Consume&& consume) {
-  const int nblk = je - jb - w > 0 ? (je - jb - w + kWaves - 1) / kWaves : 0;
+  const int nblk = je > first ? (je - first + stride - 1) / stride : 0;
   Frag fa, fb;
   for (int n0 = 0; n0 < nblk; n0 += kWave) {
     const int cnt = min(kWave, nblk - n0);
-    if (n0 > 0) {
-      const int jj = jb + w + kWaves * (n0 + lane);
-      win = lane < cnt ? table[jj] : -1;
-    }
+    const int win = lane < cnt ? table[first + stride * (n0 + lane)] : -1;
+    const int j0 = first + stride * n0;
     int64_t tile_a = fetch(__builtin_amdgcn_readlane(win, 0), fa), tile_b;
     int n = 0;
     for (; n + 2 < cnt; n += 2) {
       tile_b = fetch(__builtin_amdgcn_readlane(win, n + 1), fb);
-      consume(jb + w + kWaves * (n0 + n), tile_a, fa);
+      consume(j0 + stride * n, tile_a, fa);
       tile_a = fetch(__builtin_amdgcn_readlane(win, n + 2), fa);
-      consume(jb + w + kWaves * (n0 + n + 1), tile_b, fb);
+      consume(j0 + stride * (n + 1), tile_b, fb);
     }
     if (n + 1 < cnt) {
       tile_b = fetch(__builtin_amdgcn_readlane(win, n + 1), fb);
-      consume(jb + w + kWaves * (n0 + n), tile_a, fa);
-      consume(jb + w + kWaves * (n0 + n + 1), tile_b, fb);
+      consume(j0 + stride * n, tile_a, fa);
+      consume(j0 + stride * (n + 1), tile_b, fb);
     } else {
-      consume(jb + w + kWaves * (n0 + n), tile_a, fa);
+      consume(j0 + stride * n, tile_a, fa);
     }
   }
 }

@@ -1,0 +1,205 @@
+// Attention of several new query tokens per sequence over a paged KV cache,
+// causal within them, on the gfx950 matrix cores.
+//
+// A sequence's n new tokens sit at positions ctx - n .. ctx - 1 and their K/V
+// rows are already cached; the token at position p attends to positions 0..p.
+// That is the incremental decoder of the "LLM inference and serving" workbook
+// (Code from memory) with the rows appended one at a time, evaluated for all n
+// rows in one pass: a prompt chunk of chunked prefill ("Anthropic Interview:
+// Design an LLM Inference API with GPU Batching", scheduling: a long prompt
+// enters in chunks alongside decode steps), or the K draft tokens the target
+// model verifies in one pass under speculative decoding ("MLSys Engineer -
+// Inference Systems Q&A" and the workbook's speculative-decoding questions).
+//
+// The 16 columns of an MFMA tile are (token, query head) pairs of one KV head:
+// column c is token c / g, head c % g (g = H / H_kv), so each K/V tile read
+// from HBM serves every head of the group for up to 16/g tokens at once (or 16
+// heads of one token when g > 16).  The per-block arithmetic is the decode
+// kernel's (mfma_tile.h) with one more mask: lane column c may see keys up to
+// its own position.  Blocks wholly visible to every column of the tile take
+// the unmasked path.
+//
+// A work-group (4 waves) takes up to 4 consecutive column tiles of one
+// sequence and KV head.  With t tiles in hand (rounded up to 1, 2 or 4), 4 / t
+// waves share each tile and split its blocks round-robin; their partial
+// (m, l, O) merge in LDS as in the decode kernel.  One tile (a decode-like
+// step, or g * n <= 16) keeps all four waves streaming the sequence; four
+// tiles (a long prefill chunk) give each wave its own columns, and the four
+// waves read the same K/V blocks at nearly the same time, so three of the four
+// reads hit in the CU's cache.
+#include "device_common.h"
+#include "launch.h"
+#include "mfma_tile.h"
+
+namespace pagedkv {
+namespace {
+
+constexpr int kMultiWaves = 4;
+constexpr int kMaxTilesPerGroup = 4;
+
+template <typename E, int D>
+__global__ __launch_bounds__(kMultiWaves* kWave, 3) void multi_mfma_kernel(MultiArgs a) {
+  using S = typename E::storage;
+  constexpr int KI = MfmaShape<D>::KI;
+  constexpr int MC = MfmaShape<D>::MC;
+  constexpr int kRow = D + 4;  // padded LDS row (floats)
+
+  __shared__ __attribute__((aligned(16))) float sm_o[kMultiWaves][kHeadsPerTile][kRow];
+  __shared__ float sm_m[kMultiWaves][kHeadsPerTile];
+  __shared__ float sm_l[kMultiWaves][kHeadsPerTile];
+  __shared__ int sm_bad[kMultiWaves];
+
+  const int b = blockIdx.z;
+  const int kvh = blockIdx.y;
+  const int lane = threadIdx.x % kWave;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int n = lane & 15, q = lane >> 4;
+  const int g = a.H / a.num_kv_heads;
+
+  const int32_t q0 = a.query_start[b], q1 = a.query_start[b + 1];
+  // rows outside the buffers: nothing can be read or written for b
+  if (q0 < 0 || q1 > a.num_rows || q1 <= q0) return;
+  const int nq = q1 - q0;
+  const int ctx = a.context_lens[b];
+  const int ncols = min(nq, a.max_query_len) * g;  // columns the grid covers
+  const int tiles = (ncols + kHeadsPerTile - 1) / kHeadsPerTile;
+  const int t0 = blockIdx.x * a.tiles_per_group;
+  if (t0 >= tiles) return;
+  const int ct = min(a.tiles_per_group, tiles - t0);  // 1..4 tiles in hand
+  const int wpt = ct == 1 ? kMultiWaves : ct == 2 ? kMultiWaves / 2 : 1;  // waves per tile
+  const int my = w / wpt;  // this wave's tile in the group
+  const int phase = w % wpt;
+
+  uint16_t* out = static_cast<uint16_t*>(a.out);
+  // Output element (column c, dim x) of this sequence and KV head.
+  auto out_at = [&](int c, int x) -> uint16_t& {
+    return out[((int64_t(q0) + c / g) * a.H + kvh * g + c % g) * D + x];
+  };
+  const int cbeg = t0 * kHeadsPerTile;
+  const int cend = min(cbeg + ct * kHeadsPerTile, ncols);
+
+  if (nq > ctx || nq > a.max_query_len || ctx > a.max_nb * kBlockTokens) {
+    for (int idx = threadIdx.x; idx < (cend - cbeg) * D; idx += blockDim.x)
+      out_at(cbeg + idx / D, idx % D) = 0x7fc0;
+    return;
+  }
+
+  // This wave's columns: [tb, te_col) of tile t0 + my (none past the group).
+  const bool active = my < ct;
+  const int tcb = (t0 + my) * kHeadsPerTile;
+  const int tce = active ? min(tcb + kHeadsPerTile, ncols) : tcb;
+  const int pos0 = ctx - nq;  // position of the sequence's first new token
+  // Keys every column of the tile may see (<= kmin) and that some column may
+  // see (< kend).
+  const int kmin = pos0 + tcb / g;
+  const int kend = active ? pos0 + (tce - 1) / g + 1 : 0;
+  const int je = (kend + kBlockTokens - 1) / kBlockTokens;
+
+  // Lane column c = tcb + n: token c / g (limit: its own position), head c % g.
+  // Columns past the tile's end take zero queries and see up to kend - 1.
+  const int c = tcb + n;
+  const bool col_ok = c < tce;
+  const int limit = col_ok ? pos0 + c / g : kend - 1;
+
+  bf16x8_t qop[KI];
+  {
+    const int cc = col_ok ? c : tcb;
+    const uint16_t* qrow = static_cast<const uint16_t*>(a.query) +
+                           ((int64_t(q0) + cc / g) * a.H + kvh * g + cc % g) * D;
+#pragma unroll
+    for (int i = 0; i < KI; ++i) {
+      uint4 raw = active ? *reinterpret_cast<const uint4*>(qrow + query_dim0<E>(i, q))
+                         : make_uint4(0u, 0u, 0u, 0u);
+      if (!col_ok) raw = make_uint4(0u, 0u, 0u, 0u);
+      qop[i] = __builtin_bit_cast(bf16x8_t, raw);
+    }
+  }
+
+  const int32_t* table = a.block_tables + int64_t(b) * a.max_nb;
+  const S* kc = static_cast<const S*>(a.k_cache);
+  const S* vc = static_cast<const S*>(a.v_cache);
+  const int64_t tile_elems = int64_t(kBlockTokens) * D;
+
+  MfmaState<D> st;
+#pragma unroll
+  for (int mc = 0; mc < MC; ++mc) st.o[mc] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+  st.m = -INFINITY;
+  st.l = 0.f;
+  int bad_blk = 0;
+
+  auto fetch = [&](int p, MfmaFrag<E, D>& f) -> int64_t {
+    const bool ok = p >= 0 && p < a.num_blocks;
+    const int64_t tile = (int64_t(ok ? p : 0) * a.num_kv_heads + kvh) * tile_elems;
+    load_block<E, D>(f, kc + tile, vc + tile, lane);
+    return ok ? tile : -1;
+  };
+  auto consume = [&](int j, int64_t tile, const MfmaFrag<E, D>& f) {
+    if (tile < 0) { bad_blk = 1; return; }
+    const int key0 = j * kBlockTokens;
+    const int nvalid = kend - key0;
+    if (nvalid >= kBlockTokens && key0 + kBlockTokens - 1 <= kmin)
+      compute_block<E, D, false>(f, qop, st, nvalid, a.scale_log2, lane);
+    else
+      compute_block<E, D, true, true>(f, qop, st, nvalid, a.scale_log2, lane, key0, limit);
+  };
+  walk_blocks<MfmaFrag<E, D>>(phase, wpt, je, lane, table, fetch, consume);
+
+  const float lsum = cross_row_sum(st.l);
+  if (q == 0) {
+    sm_m[w][n] = st.m;
+    sm_l[w][n] = lsum;
+  }
+  if (lane == 0) sm_bad[w] = bad_blk;
+#pragma unroll
+  for (int mc = 0; mc < MC; ++mc)
+    *reinterpret_cast<floatx4_t*>(&sm_o[w][n][16 * mc + 4 * q]) = st.o[mc];
+  __syncthreads();
+
+  // Merge the waves of each tile: column cbeg + idx / D, dim idx % D.
+  for (int idx = threadIdx.x; idx < (cend - cbeg) * D; idx += blockDim.x) {
+    const int cl = idx / D, x = idx % D;
+    const int w0 = (cl / kHeadsPerTile) * wpt, col = cl % kHeadsPerTile;
+    float M = -INFINITY;
+    int bad = 0;
+    for (int ww = w0; ww < w0 + wpt; ++ww) {
+      M = fmaxf(M, sm_m[ww][col]);
+      bad |= sm_bad[ww];
+    }
+    float L = 0.f, acc = 0.f;
+    for (int ww = w0; ww < w0 + wpt; ++ww) {
+      if (sm_m[ww][col] == -INFINITY) continue;
+      const float sc = fast_exp2(sm_m[ww][col] - M);
+      L = fmaf(sm_l[ww][col], sc, L);
+      acc = fmaf(sm_o[ww][col][x], sc, acc);
+    }
+    float res = acc / L * a.v_scale;
+    if (bad) res = __int_as_float(0x7fc00000);
+    out_at(cbeg + cl, x) = f32_to_bf16_rne(res);
+  }
+}
+
+template <typename E>
+void (*multi_kernel(int head_dim))(MultiArgs) {
+  if (head_dim == 128) return multi_mfma_kernel<E, 128>;
+  if (head_dim == 64) return multi_mfma_kernel<E, 64>;
+  return nullptr;
+}
+
+}  // namespace
+
+hipError_t launch_multi_mfma(const MultiArgs& a, Kind kind, int head_dim, hipStream_t s) {
+  void (*kern)(MultiArgs) = kind == Kind::kBf16  ? multi_kernel<Bf16>(head_dim)
+                            : kind == Kind::kFp8 ? multi_kernel<Fp8>(head_dim)
+                                                 : nullptr;
+  if (!kern || a.tiles_per_group < 1 || a.tiles_per_group > kMaxTilesPerGroup)
+    return hipErrorInvalidValue;
+  if (a.B == 0 || a.max_query_len == 0) return hipSuccess;
+  const int g = a.H / a.num_kv_heads;
+  const int64_t tiles = (int64_t(a.max_query_len) * g + kHeadsPerTile - 1) / kHeadsPerTile;
+  const int64_t groups = (tiles + a.tiles_per_group - 1) / a.tiles_per_group;
+  hipLaunchKernelGGL(kern, dim3(unsigned(groups), unsigned(a.num_kv_heads), unsigned(a.B)),
+                     dim3(kMultiWaves * kWave), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace pagedkv

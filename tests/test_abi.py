@@ -176,6 +176,49 @@ def test_decode_argument_errors(lib, pool):
     assert _decode(lib, pool, B=0) == _lib.KV_OK  # nothing to launch
 
 
+def _multi(lib, pool, B=2, H=4, T=6, mq=4, max_nb=4, scale=0.1, out=FAKE_K, q=FAKE_V,
+           qs=FAKE_K):
+    return lib.paged_attention_multi(pool, out, q, T, qs, mq, FAKE_K, max_nb, FAKE_V, B, H, scale,
+                                     None)
+
+
+def test_multi_argument_errors(lib, pool):
+    assert _multi(lib, None) == _lib.KV_ERR_INVALID_ARG
+    assert _multi(lib, pool, H=3) == _lib.KV_ERR_INVALID_ARG
+    assert _multi(lib, pool, B=-1) == _lib.KV_ERR_INVALID_ARG
+    assert _multi(lib, pool, T=-1) == _lib.KV_ERR_INVALID_ARG
+    assert _multi(lib, pool, mq=-1) == _lib.KV_ERR_INVALID_ARG
+    assert _multi(lib, pool, max_nb=0) == _lib.KV_ERR_INVALID_ARG
+    assert _multi(lib, pool, scale=float("nan")) == _lib.KV_ERR_INVALID_ARG
+    assert _multi(lib, pool, qs=None) == _lib.KV_ERR_INVALID_ARG
+    assert _multi(lib, pool, out=None) == _lib.KV_ERR_INVALID_ARG
+    assert _multi(lib, pool, q=FAKE_V + 8) == _lib.KV_ERR_INVALID_ARG
+    assert _multi(lib, pool, B=70000) == _lib.KV_ERR_UNSUPPORTED
+    assert _multi(lib, pool, mq=1 << 30, H=64) == _lib.KV_ERR_INVALID_ARG   # grid too large
+    for nothing in (dict(B=0), dict(T=0), dict(mq=0)):
+        assert _multi(lib, pool, out=None, **nothing) == _lib.KV_OK        # nothing to launch
+    st, hf = _create(lib, desc(8, 16, 2, 64, _lib.KV_F32))
+    assert _multi(lib, hf) == _lib.KV_ERR_UNSUPPORTED                       # no fp32 kernel
+    assert b"bf16 or fp8" in lib.kv_last_error()
+    lib.kv_pool_destroy(hf)
+
+
+def test_append_chunk_argument_errors(lib, pool):
+    def f(pool=pool, key=FAKE_K, value=FAKE_V, T=6, qs=FAKE_K, mq=4, max_nb=4, B=2):
+        return lib.kv_cache_append_chunk(pool, key, value, T, qs, mq, FAKE_K, max_nb, FAKE_V, B,
+                                         None, None)
+    assert f(pool=None) == _lib.KV_ERR_INVALID_ARG
+    assert f(B=-1) == _lib.KV_ERR_INVALID_ARG
+    assert f(T=-1) == _lib.KV_ERR_INVALID_ARG
+    assert f(mq=-1) == _lib.KV_ERR_INVALID_ARG
+    assert f(max_nb=0) == _lib.KV_ERR_INVALID_ARG
+    assert f(qs=None) == _lib.KV_ERR_INVALID_ARG
+    assert f(key=None) == _lib.KV_ERR_INVALID_ARG
+    assert f(value=FAKE_V + 2) == _lib.KV_ERR_INVALID_ARG
+    for nothing in (dict(B=0), dict(T=0), dict(mq=0)):
+        assert f(key=None, **nothing) == _lib.KV_OK
+
+
 def test_workspace_size_formula(lib):
     def al(x):
         return (x + 255) // 256 * 256

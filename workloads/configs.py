@@ -232,6 +232,25 @@ def scattered_workload(name: str, dtype: str, B: int, H: int, H_kv: int, d: int,
                     kv_dtype=kv_dtype, k_scale=k_scale, v_scale=v_scale)
 
 
+def add_multi_step(w: Workload, query_lens: Sequence[int], rng=None, seed: int = 0) -> Workload:
+    """Give w a step of query_lens[b] new tokens per sequence: the last
+    query_lens[b] of its first step's context (q [T, H, d], new K/V rows
+    [T, H_kv, d] drawn in that order from rng, or from a PCG64 stream of seed)."""
+    rng = rng if rng is not None else np.random.Generator(np.random.PCG64(seed))
+    ctx = np.asarray(w.steps[0].context_lens, dtype=np.int32)
+    qlen = np.asarray(query_lens, dtype=np.int64)
+    if qlen.shape != (w.B,):
+        raise ValueError("need one query length per sequence")
+    qs = np.zeros(w.B + 1, dtype=np.int32)
+    qs[1:] = np.cumsum(qlen)
+    T = int(qs[-1])
+    w.multi = MultiStep(context_lens=ctx, query_start=qs,
+                        q=_normal_bits(rng, T * w.H * w.d, w.dtype).reshape(T, w.H, w.d),
+                        new_k=_normal_bits(rng, T * w.H_kv * w.d, w.dtype).reshape(T, w.H_kv, w.d),
+                        new_v=_normal_bits(rng, T * w.H_kv * w.d, w.dtype).reshape(T, w.H_kv, w.d))
+    return w
+
+
 def multi_token_workload(name: str, dtype: str, B: int, H: int, H_kv: int, d: int,
                          context_lens: Sequence[int], query_lens: Sequence[int], seed: int,
                          kv_dtype: Optional[str] = None, k_scale: float = 1.0,
@@ -241,17 +260,7 @@ def multi_token_workload(name: str, dtype: str, B: int, H: int, H_kv: int, d: in
     rng = np.random.Generator(np.random.PCG64(seed))
     w = scattered_workload(name, dtype, B, H, H_kv, d, context_lens, seed, rng=rng,
                            kv_dtype=kv_dtype, k_scale=k_scale, v_scale=v_scale, max_nb=max_nb)
-    qlen = np.asarray(query_lens, dtype=np.int64)
-    if qlen.shape != (B,):
-        raise ValueError("need one query length per sequence")
-    qs = np.zeros(B + 1, dtype=np.int32)
-    qs[1:] = np.cumsum(qlen)
-    T = int(qs[-1])
-    w.multi = MultiStep(context_lens=np.asarray(context_lens, dtype=np.int32), query_start=qs,
-                        q=_normal_bits(rng, T * H * d, dtype).reshape(T, H, d),
-                        new_k=_normal_bits(rng, T * H_kv * d, dtype).reshape(T, H_kv, d),
-                        new_v=_normal_bits(rng, T * H_kv * d, dtype).reshape(T, H_kv, d))
-    return w
+    return add_multi_step(w, query_lens, rng=rng)
 
 
 def _name(config: int, kv_dtype: str) -> str:
