@@ -78,6 +78,13 @@ def parse_args(argv=None):
                     help="a serving loop driven by the native block manager (prefix-cached "
                          "admission, forked samples, copy-on-write appends) at the 7B shape; "
                          "prints its own JSON line")
+    ap.add_argument("--verify", type=int, default=0, metavar="K",
+                    help="draft verification: K new tokens per sequence of --config (2 or 3), "
+                         "written with kv_cache_append_chunk and attended with "
+                         "paged_attention_multi; prints its own JSON line")
+    ap.add_argument("--prefill", action="store_true",
+                    help="chunked prefill: a 512-token chunk for each of 16 sequences "
+                         "(64 query heads over 8 KV heads); prints its own JSON line")
     ap.add_argument("--unfused", action="store_true",
                     help="run the step's cache write as two calls (kv_slot_mapping + "
                          "reshape_and_cache) instead of kv_cache_append")
@@ -375,6 +382,178 @@ def serve(args) -> int:
     return 0
 
 
+# --------------------------------------------------------------------------
+# Several new tokens per sequence: draft verification and chunked prefill
+
+PEAK_MFMA_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak
+PREFILL_CHUNK = 512
+
+
+def multi_workload(args):
+    from workloads import configs as W
+    kv = args.kv_dtype if args.kv_dtype != "bf16" else ""
+    if args.prefill:
+        # chunk k of a prompt: the chunk is the last 512 of 512..4096 context tokens
+        rng = np.random.default_rng(2024)
+        ctx = rng.integers(PREFILL_CHUNK, 4097, size=16)
+        w = W.multi_token_workload(f"prefill-chunk{PREFILL_CHUNK}-b16-gqa64x8", "bf16", 16, 64, 8,
+                                   128, ctx, [PREFILL_CHUNK] * 16, seed=2024,
+                                   kv_dtype=kv or None)
+        return w
+    if args.config not in (2, 3):
+        raise SystemExit("--verify runs on --config 2 or 3")
+    w = W.make_workload(args.config, kv_dtype=kv)
+    W.add_multi_step(w, [args.verify] * w.B, seed=900 + args.config)
+    w.name = f"{w.name}-verify{args.verify}"
+    return w
+
+
+def multi_bytes_flops(w) -> dict:
+    """Algorithmic bytes and flops of one multi-token step."""
+    m = w.multi
+    ctx = m.context_lens.astype(np.int64)
+    n = np.diff(m.query_start).astype(np.int64)
+    T = int(n.sum())
+    e, ec = w.elem_bytes, w.kv_elem_bytes
+    kv = int(ctx.sum()) * w.H_kv * w.d * 2 * ec          # every cached K/V row once
+    nb = (ctx + 15) // 16
+    attn = kv + 2 * T * w.H * w.d * e + 4 * int(nb.sum()) + 4 * (2 * w.B + 1)
+    write = 2 * T * w.H_kv * w.d * (e + ec) + 8 * T
+    # row at position p: q.k and p.v over p + 1 keys, per query head
+    seen = sum(int(((c - k + 1) + c) * k // 2) for c, k in zip(ctx, n))
+    flops = 4 * w.H * w.d * seen
+    return {"attn": attn, "kv": kv, "write": write, "step": attn + write, "flops": flops,
+            "rows": T}
+
+
+def multi(args) -> int:
+    """Time the multi-token step (chunk write + causal multi-row attention) and,
+    on the same pool, the one-token decode step of the same sequences."""
+    import torch
+    import oracle as O
+    import paged_kv_cache_33_amd as P
+    w = multi_workload(args)
+    m = w.multi
+    print(f"[bench] {w.name} ({w.kv_dtype} cache): B={w.B} H={w.H} H_kv={w.H_kv} rows="
+          f"{int(m.query_start[-1])}", file=sys.stderr, flush=True)
+    torch.cuda.set_device(0)
+    views = {np.dtype(np.uint16): np.int16, np.dtype(np.uint32): np.int32}
+
+    def dev(a):
+        a = np.ascontiguousarray(a)
+        return torch.from_numpy(a.view(views.get(a.dtype, a.dtype))).cuda()
+
+    pool = P.KVPool(dev(w.k_pool), dev(w.v_pool), w.num_blocks, w.H_kv, w.d, w.kv_dtype,
+                    w.k_scale, w.v_scale)
+    tables = torch.from_numpy(w.block_tables).cuda()
+    ctx = torch.from_numpy(m.context_lens).cuda()
+    qs = torch.from_numpy(m.query_start).cuda()
+    mq = int(np.diff(m.query_start).max())
+    q, nk, nv = dev(m.q), dev(m.new_k), dev(m.new_v)
+    out = torch.empty_like(q)
+    slots = torch.empty(q.shape[0], dtype=torch.int64, device="cuda")
+    stream = torch.cuda.current_stream()
+    st = w.steps[0]
+    dq, dk, dv = dev(st.q), dev(st.new_k), dev(st.new_v)
+    dout = torch.empty_like(dq)
+    L = int(m.context_lens.max())
+
+    def run(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        P.kv_cache_append_chunk(pool, nk, nv, qs, mq, tables, ctx, slots, stream)
+        if ev is not None:
+            ev[1].record(stream)
+        P.paged_attention_multi(pool, out, q, qs, mq, tables, ctx, w.scale, stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    def run_decode():
+        P.kv_cache_append(pool, dk, dv, tables, ctx, None, stream)
+        P.paged_attention_decode(pool, dout, dq, tables, ctx, L, w.scale, 0, None, stream)
+
+    # parity of three sequences' rows against the oracle
+    run()
+    torch.cuda.synchronize()
+    sl = O.chunk_slots(w.block_tables, m.context_lens, m.query_start)
+    kp, vp = O.reshape_and_cache(w.k_pool, w.v_pool, m.new_k, m.new_v, sl, w.H_kv, w.d,
+                                 w.kv_dtype, w.num_blocks, w.k_scale, w.v_scale)
+    seqs = [int(np.argmin(m.context_lens)), int(np.argmax(m.context_lens)), w.B // 2]
+    ref = O.decode_multi(kp, vp, m.q, m.query_start, w.block_tables, m.context_lens, w.H, w.H_kv,
+                         w.d, w.kv_dtype, w.scale, w.k_scale, w.v_scale, seqs=seqs)
+    got = out.cpu().numpy().view(np.uint16)
+    worst, num, den = 0.0, 0.0, 0.0
+    for b, r in ref.items():
+        g = O.bits_to_f64(got[m.query_start[b]:m.query_start[b + 1]], "bf16")
+        amp = np.maximum(1.0, np.abs(r).reshape(len(r), -1).max(axis=1))
+        worst = max(worst, float((np.abs(g - r).reshape(len(r), -1).max(axis=1) / amp).max()))
+        num += float(((g - r) ** 2).sum())
+        den += float((r ** 2).sum())
+    rel = math.sqrt(num / den)
+    parity = {"sequences": seqs, "max_abs_over_row_scale": worst, "rel_l2": rel,
+              "ok": bool(worst <= 1e-2 and rel <= 5e-3)}
+
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    a, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(args.steps):
+        run()
+    b_.record(stream)
+    torch.cuda.synchronize()
+    ms_step = a.elapsed_time(b_) / args.steps
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3))
+           for _ in range(args.steps)]
+    for i in range(args.steps):
+        run(evs[i])
+    torch.cuda.synchronize()
+    attn_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    write_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    for _ in range(args.warmup):
+        run_decode()
+    a.record(stream)
+    for _ in range(args.steps):
+        run_decode()
+    b_.record(stream)
+    torch.cuda.synchronize()
+    dec_ms = a.elapsed_time(b_) / args.steps
+
+    bf = multi_bytes_flops(w)
+    attn_avg = float(attn_ms.mean())
+    if args.prefill:
+        achieved = bf["flops"] / (attn_avg * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_MFMA_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_MFMA_BF16_TFLOPS, 4)}
+    else:
+        achieved = bf["attn"] / (attn_avg * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4)}
+    roof.update({"kernel": "multi_mfma", "traffic": None, "bytes_per_launch": bf["attn"],
+                 "flops_per_launch": bf["flops"], "avg_launch_ms": round(attn_avg, 5)})
+    rows = bf["rows"]
+    print(json.dumps({
+        "metric": ("chunked-prefill attention over a paged KV cache" if args.prefill else
+                   "draft verification over a paged KV cache (K new tokens per sequence)"),
+        "value": round(rows / (ms_step * 1e-3), 1), "unit": "query tokens/s",
+        "ms_per_step": round(ms_step, 5), "steps": args.steps, "warmup": args.warmup,
+        "higher_is_better": True, "n_gpus": 1,
+        "dtype": "bf16" if w.kv_dtype == "bf16" else f"{w.kv_dtype} cache, bf16 activations",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.B, "query_heads": w.H, "kv_heads": w.H_kv,
+                   "head_dim": w.d, "rows": rows,
+                   "sum_context_tokens": int(m.context_lens.astype(np.int64).sum()),
+                   "step": "kv_cache_append_chunk + paged_attention_multi"},
+        "step_GBs": round(bf["step"] / (ms_step * 1e-3) / 1e9, 1),
+        "write_ms_avg": round(float(write_ms.mean()), 5),
+        "decode_step_ms_same_pool": round(dec_ms, 5),
+        "step_over_decode_step": round(ms_step / dec_ms, 3),
+        "roofline": roof,
+        "parity": parity,
+    }), flush=True)
+    return 0 if parity["ok"] else 3
+
+
 def main(argv=None) -> int:
     args = parse_args(argv)
     if args.gpus != 1:
@@ -390,6 +569,8 @@ def main(argv=None) -> int:
         return 0
     if args.serve:
         return serve(args)
+    if args.verify or args.prefill:
+        return multi(args)
 
     from workloads import configs as W
     t0 = time.time()

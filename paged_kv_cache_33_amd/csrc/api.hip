@@ -408,7 +408,11 @@ kv_status paged_attention_multi(const kv_pool* pool, void* out, const void* quer
   const bool fp8 = d.dtype == KV_FP8_E4M3;
   a.scale_log2 = scale * 1.4426950408889634f * (fp8 ? d.k_scale : 1.f);
   a.v_scale = fp8 ? d.v_scale : 1.f;
-  a.tiles_per_group = static_cast<int32_t>(tiles < 4 ? tiles : 4);
+  // one tile per wave when one tile holds every column; else two per wave,
+  // and up to four such sets per work-group
+  a.tiles_per_set = tiles > 1 ? 2 : 1;
+  const int64_t sets = (tiles + a.tiles_per_set - 1) / a.tiles_per_set;
+  a.sets_per_group = static_cast<int32_t>(sets < 4 ? sets : 4);
   return hip_status(pagedkv::launch_multi_mfma(a, kind_of(d.dtype), d.head_dim,
                                                static_cast<hipStream_t>(stream)),
                     "multi-token attention launch");

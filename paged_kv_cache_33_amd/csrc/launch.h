@@ -60,7 +60,8 @@ struct MultiArgs {
   int32_t H;
   float scale_log2;             // as DecodeArgs
   float v_scale;
-  int32_t tiles_per_group;      // 16-column tiles one work-group takes (1..4)
+  int32_t tiles_per_set;        // 16-column tiles one wave carries (1 or 2)
+  int32_t sets_per_group;       // column sets one work-group takes (1..4)
 };
 
 struct ReduceArgs {

@@ -19,37 +19,53 @@
 // its own position.  Blocks wholly visible to every column of the tile take
 // the unmasked path.
 //
-// A work-group (4 waves) takes up to 4 consecutive column tiles of one
-// sequence and KV head.  With t tiles in hand (rounded up to 1, 2 or 4), 4 / t
-// waves share each tile and split its blocks round-robin; their partial
-// (m, l, O) merge in LDS as in the decode kernel.  One tile (a decode-like
-// step, or g * n <= 16) keeps all four waves streaming the sequence; four
-// tiles (a long prefill chunk) give each wave its own columns, and the four
-// waves read the same K/V blocks at nearly the same time, so three of the four
-// reads hit in the CU's cache.
+// A wave carries one or two column tiles (a column set): the tiles' query
+// operands and running states sit side by side in its registers and every
+// K/V block it loads feeds all of them, so K/V bytes are loaded once per 16 or
+// 32 columns.  A work-group (4 waves) takes up to 4 consecutive column sets of
+// one sequence and KV head.  With s sets in hand (rounded up to 1, 2 or 4),
+// 4 / s waves share each set and split its blocks round-robin; their partial
+// (m, l, O) merge in LDS as in the decode kernel.  One set (a decode step, or
+// draft verification with g * n <= 32) keeps all four waves streaming the
+// sequence once; four sets (a long prefill chunk) give each wave its own
+// columns, and the four waves read the same K/V blocks at nearly the same
+// time, so most of those reads hit in the CU's cache.
 #include "device_common.h"
 #include "launch.h"
 #include "mfma_tile.h"
+#include "work_list.h"
 
 namespace pagedkv {
 namespace {
 
 constexpr int kMultiWaves = 4;
-constexpr int kMaxTilesPerGroup = 4;
+constexpr int kMaxSetsPerGroup = 4;
 
-template <typename E, int D>
-__global__ __launch_bounds__(kMultiWaves* kWave, 3) void multi_mfma_kernel(MultiArgs a) {
+// kTiles (1 or 2): 16-column tiles one wave carries.  A wave holds the query
+// operands and running state of each of its tiles and feeds them all from
+// the same K/V registers, so a block is loaded once for 16 * kTiles columns.
+// Two tiles take 2 waves per SIMD instead of 3 (the second state costs 48
+// VGPRs at d = 128).
+template <typename E, int D, int kTiles>
+__global__ __launch_bounds__(kMultiWaves* kWave, kTiles == 1 ? 3 : 2) void multi_mfma_kernel(
+    MultiArgs a) {
   using S = typename E::storage;
   constexpr int KI = MfmaShape<D>::KI;
   constexpr int MC = MfmaShape<D>::MC;
   constexpr int kRow = D + 4;  // padded LDS row (floats)
+  constexpr int kSetCols = kHeadsPerTile * kTiles;
 
-  __shared__ __attribute__((aligned(16))) float sm_o[kMultiWaves][kHeadsPerTile][kRow];
-  __shared__ float sm_m[kMultiWaves][kHeadsPerTile];
-  __shared__ float sm_l[kMultiWaves][kHeadsPerTile];
+  __shared__ __attribute__((aligned(16))) float sm_o[kMultiWaves][kSetCols][kRow];
+  __shared__ float sm_m[kMultiWaves][kSetCols];
+  __shared__ float sm_l[kMultiWaves][kSetCols];
   __shared__ int sm_bad[kMultiWaves];
 
-  const int b = blockIdx.z;
+  // sequences longest first, as in the decode kernel: work-group z takes the
+  // z-th longest context
+  __shared__ int sm_order[kOrderBuckets + kMultiWaves + 1];
+  const int b = a.B <= kMaxOrderedSeqs ? sequence_of_rank<kMultiWaves * kWave>(
+                                             a.context_lens, a.B, a.max_nb, blockIdx.z, sm_order)
+                                       : int(blockIdx.z);
   const int kvh = blockIdx.y;
   const int lane = threadIdx.x % kWave;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -62,21 +78,21 @@ __global__ __launch_bounds__(kMultiWaves* kWave, 3) void multi_mfma_kernel(Multi
   const int nq = q1 - q0;
   const int ctx = a.context_lens[b];
   const int ncols = min(nq, a.max_query_len) * g;  // columns the grid covers
-  const int tiles = (ncols + kHeadsPerTile - 1) / kHeadsPerTile;
-  const int t0 = blockIdx.x * a.tiles_per_group;
-  if (t0 >= tiles) return;
-  const int ct = min(a.tiles_per_group, tiles - t0);  // 1..4 tiles in hand
-  const int wpt = ct == 1 ? kMultiWaves : ct == 2 ? kMultiWaves / 2 : 1;  // waves per tile
-  const int my = w / wpt;  // this wave's tile in the group
-  const int phase = w % wpt;
+  const int nsets = (ncols + kSetCols - 1) / kSetCols;
+  const int s0 = blockIdx.x * a.sets_per_group;
+  if (s0 >= nsets) return;
+  const int cs = min(a.sets_per_group, nsets - s0);  // 1..4 column sets in hand
+  const int wps = cs == 1 ? kMultiWaves : cs == 2 ? kMultiWaves / 2 : 1;  // waves per set
+  const int my = w / wps;  // this wave's set in the group
+  const int phase = w % wps;
 
   uint16_t* out = static_cast<uint16_t*>(a.out);
   // Output element (column c, dim x) of this sequence and KV head.
   auto out_at = [&](int c, int x) -> uint16_t& {
     return out[((int64_t(q0) + c / g) * a.H + kvh * g + c % g) * D + x];
   };
-  const int cbeg = t0 * kHeadsPerTile;
-  const int cend = min(cbeg + ct * kHeadsPerTile, ncols);
+  const int cbeg = s0 * kSetCols;
+  const int cend = min(cbeg + cs * kSetCols, ncols);
 
   if (nq > ctx || nq > a.max_query_len || ctx > a.max_nb * kBlockTokens) {
     for (int idx = threadIdx.x; idx < (cend - cbeg) * D; idx += blockDim.x)
@@ -84,34 +100,37 @@ __global__ __launch_bounds__(kMultiWaves* kWave, 3) void multi_mfma_kernel(Multi
     return;
   }
 
-  // This wave's columns: [tb, te_col) of tile t0 + my (none past the group).
-  const bool active = my < ct;
-  const int tcb = (t0 + my) * kHeadsPerTile;
-  const int tce = active ? min(tcb + kHeadsPerTile, ncols) : tcb;
+  // This wave's columns: [scb, sce) of set s0 + my (none past the group).
+  const bool active = my < cs;
+  const int scb = (s0 + my) * kSetCols;
+  const int sce = active ? min(scb + kSetCols, ncols) : scb;
   const int pos0 = ctx - nq;  // position of the sequence's first new token
-  // Keys every column of the tile may see (<= kmin) and that some column may
+  // Keys every column of the set may see (<= kmin) and that some column may
   // see (< kend).
-  const int kmin = pos0 + tcb / g;
-  const int kend = active ? pos0 + (tce - 1) / g + 1 : 0;
+  const int kmin = pos0 + scb / g;
+  const int kend = active ? pos0 + (sce - 1) / g + 1 : 0;
   const int je = (kend + kBlockTokens - 1) / kBlockTokens;
+  // Tiles of the set that hold columns (uniform): the second may be empty.
+  const int ntiles = active ? (sce - scb + kHeadsPerTile - 1) / kHeadsPerTile : 0;
 
-  // Lane column c = tcb + n: token c / g (limit: its own position), head c % g.
-  // Columns past the tile's end take zero queries and see up to kend - 1.
-  const int c = tcb + n;
-  const bool col_ok = c < tce;
-  const int limit = col_ok ? pos0 + c / g : kend - 1;
-
-  bf16x8_t qop[KI];
-  {
-    const int cc = col_ok ? c : tcb;
+  // Lane column c = scb + 16 tt + n of tile tt: token c / g (limit: its own
+  // position), head c % g.  Columns past the set's end take zero queries and
+  // see up to kend - 1.
+  int limit[kTiles];
+  bf16x8_t qop[kTiles][KI];
+#pragma unroll
+  for (int tt = 0; tt < kTiles; ++tt) {
+    const int c = scb + tt * kHeadsPerTile + n;
+    const bool col_ok = c < sce;
+    limit[tt] = col_ok ? pos0 + c / g : kend - 1;
+    const int cc = col_ok ? c : scb;
     const uint16_t* qrow = static_cast<const uint16_t*>(a.query) +
                            ((int64_t(q0) + cc / g) * a.H + kvh * g + cc % g) * D;
 #pragma unroll
     for (int i = 0; i < KI; ++i) {
-      uint4 raw = active ? *reinterpret_cast<const uint4*>(qrow + query_dim0<E>(i, q))
-                         : make_uint4(0u, 0u, 0u, 0u);
-      if (!col_ok) raw = make_uint4(0u, 0u, 0u, 0u);
-      qop[i] = __builtin_bit_cast(bf16x8_t, raw);
+      uint4 raw = make_uint4(0u, 0u, 0u, 0u);
+      if (col_ok) raw = *reinterpret_cast<const uint4*>(qrow + query_dim0<E>(i, q));
+      qop[tt][i] = __builtin_bit_cast(bf16x8_t, raw);
     }
   }
 
@@ -120,11 +139,14 @@ __global__ __launch_bounds__(kMultiWaves* kWave, 3) void multi_mfma_kernel(Multi
   const S* vc = static_cast<const S*>(a.v_cache);
   const int64_t tile_elems = int64_t(kBlockTokens) * D;
 
-  MfmaState<D> st;
+  MfmaState<D> st[kTiles];
 #pragma unroll
-  for (int mc = 0; mc < MC; ++mc) st.o[mc] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-  st.m = -INFINITY;
-  st.l = 0.f;
+  for (int tt = 0; tt < kTiles; ++tt) {
+#pragma unroll
+    for (int mc = 0; mc < MC; ++mc) st[tt].o[mc] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    st[tt].m = -INFINITY;
+    st[tt].l = 0.f;
+  }
   int bad_blk = 0;
 
   auto fetch = [&](int p, MfmaFrag<E, D>& f) -> int64_t {
@@ -137,36 +159,46 @@ __global__ __launch_bounds__(kMultiWaves* kWave, 3) void multi_mfma_kernel(Multi
     if (tile < 0) { bad_blk = 1; return; }
     const int key0 = j * kBlockTokens;
     const int nvalid = kend - key0;
-    if (nvalid >= kBlockTokens && key0 + kBlockTokens - 1 <= kmin)
-      compute_block<E, D, false>(f, qop, st, nvalid, a.scale_log2, lane);
-    else
-      compute_block<E, D, true, true>(f, qop, st, nvalid, a.scale_log2, lane, key0, limit);
+    const bool open = nvalid >= kBlockTokens && key0 + kBlockTokens - 1 <= kmin;
+#pragma unroll
+    for (int tt = 0; tt < kTiles; ++tt) {
+      if (tt > 0 && tt >= ntiles) break;  // uniform: an empty second tile
+      if (open)
+        compute_block<E, D, false>(f, qop[tt], st[tt], nvalid, a.scale_log2, lane);
+      else
+        compute_block<E, D, true, true>(f, qop[tt], st[tt], nvalid, a.scale_log2, lane, key0,
+                                        limit[tt]);
+    }
   };
-  walk_blocks<MfmaFrag<E, D>>(phase, wpt, je, lane, table, fetch, consume);
+  walk_blocks<MfmaFrag<E, D>>(phase, wps, je, lane, table, fetch, consume);
 
-  const float lsum = cross_row_sum(st.l);
-  if (q == 0) {
-    sm_m[w][n] = st.m;
-    sm_l[w][n] = lsum;
+#pragma unroll
+  for (int tt = 0; tt < kTiles; ++tt) {
+    const float lsum = cross_row_sum(st[tt].l);
+    const int col = tt * kHeadsPerTile + n;
+    if (q == 0) {
+      sm_m[w][col] = st[tt].m;
+      sm_l[w][col] = lsum;
+    }
+#pragma unroll
+    for (int mc = 0; mc < MC; ++mc)
+      *reinterpret_cast<floatx4_t*>(&sm_o[w][col][16 * mc + 4 * q]) = st[tt].o[mc];
   }
   if (lane == 0) sm_bad[w] = bad_blk;
-#pragma unroll
-  for (int mc = 0; mc < MC; ++mc)
-    *reinterpret_cast<floatx4_t*>(&sm_o[w][n][16 * mc + 4 * q]) = st.o[mc];
   __syncthreads();
 
-  // Merge the waves of each tile: column cbeg + idx / D, dim idx % D.
+  // Merge the waves of each set: column cbeg + idx / D, dim idx % D.
   for (int idx = threadIdx.x; idx < (cend - cbeg) * D; idx += blockDim.x) {
     const int cl = idx / D, x = idx % D;
-    const int w0 = (cl / kHeadsPerTile) * wpt, col = cl % kHeadsPerTile;
+    const int w0 = (cl / kSetCols) * wps, col = cl % kSetCols;
     float M = -INFINITY;
     int bad = 0;
-    for (int ww = w0; ww < w0 + wpt; ++ww) {
+    for (int ww = w0; ww < w0 + wps; ++ww) {
       M = fmaxf(M, sm_m[ww][col]);
       bad |= sm_bad[ww];
     }
     float L = 0.f, acc = 0.f;
-    for (int ww = w0; ww < w0 + wpt; ++ww) {
+    for (int ww = w0; ww < w0 + wps; ++ww) {
       if (sm_m[ww][col] == -INFINITY) continue;
       const float sc = fast_exp2(sm_m[ww][col] - M);
       L = fmaf(sm_l[ww][col], sc, L);
@@ -178,25 +210,33 @@ __global__ __launch_bounds__(kMultiWaves* kWave, 3) void multi_mfma_kernel(Multi
   }
 }
 
-template <typename E>
+template <typename E, int kTiles>
 void (*multi_kernel(int head_dim))(MultiArgs) {
-  if (head_dim == 128) return multi_mfma_kernel<E, 128>;
-  if (head_dim == 64) return multi_mfma_kernel<E, 64>;
+  if (head_dim == 128) return multi_mfma_kernel<E, 128, kTiles>;
+  if (head_dim == 64) return multi_mfma_kernel<E, 64, kTiles>;
   return nullptr;
+}
+
+template <typename E>
+void (*multi_kernel(int head_dim, int tiles))(MultiArgs) {
+  return tiles == 1 ? multi_kernel<E, 1>(head_dim) : multi_kernel<E, 2>(head_dim);
 }
 
 }  // namespace
 
 hipError_t launch_multi_mfma(const MultiArgs& a, Kind kind, int head_dim, hipStream_t s) {
-  void (*kern)(MultiArgs) = kind == Kind::kBf16  ? multi_kernel<Bf16>(head_dim)
-                            : kind == Kind::kFp8 ? multi_kernel<Fp8>(head_dim)
-                                                 : nullptr;
-  if (!kern || a.tiles_per_group < 1 || a.tiles_per_group > kMaxTilesPerGroup)
+  if (a.tiles_per_set < 1 || a.tiles_per_set > 2 || a.sets_per_group < 1 ||
+      a.sets_per_group > kMaxSetsPerGroup)
     return hipErrorInvalidValue;
+  void (*kern)(MultiArgs) = kind == Kind::kBf16  ? multi_kernel<Bf16>(head_dim, a.tiles_per_set)
+                            : kind == Kind::kFp8 ? multi_kernel<Fp8>(head_dim, a.tiles_per_set)
+                                                 : nullptr;
+  if (!kern) return hipErrorInvalidValue;
   if (a.B == 0 || a.max_query_len == 0) return hipSuccess;
   const int g = a.H / a.num_kv_heads;
-  const int64_t tiles = (int64_t(a.max_query_len) * g + kHeadsPerTile - 1) / kHeadsPerTile;
-  const int64_t groups = (tiles + a.tiles_per_group - 1) / a.tiles_per_group;
+  const int64_t set_cols = int64_t(kHeadsPerTile) * a.tiles_per_set;
+  const int64_t sets = (int64_t(a.max_query_len) * g + set_cols - 1) / set_cols;
+  const int64_t groups = (sets + a.sets_per_group - 1) / a.sets_per_group;
   hipLaunchKernelGGL(kern, dim3(unsigned(groups), unsigned(a.num_kv_heads), unsigned(a.B)),
                      dim3(kMultiWaves * kWave), 0, s, a);
   return hipGetLastError();
