@@ -19,9 +19,14 @@ Pages cited (titles as the pages give them):
          accounting worked example), 29.2.1 (attention intensity).
   [FDE9] "Forward Deployed Engineering Interview", Ch.2 section 9 (shrinking
          the cache: an fp8_e4m3 cache, available on ROCm, halves every row;
-         scales are per tensor) and the annotated serving configuration of the
-         same chapter (--kv-cache-dtype fp8: every scale is 1.0 without
+         scales are per tensor; windowed layers such as gpt-oss's 128-token
+         band cap what a layer keeps) and the annotated serving configuration
+         of the same chapter (--kv-cache-dtype fp8: every scale is 1.0 without
          calibration).
+  [QA3]  same Q&A page, Q3 item 4 (local-attention layers need only the last
+         W tokens) and Q4 (sliding-window attention: the first K tile a query
+         at position q_pos needs starts at q_pos + 1 - W, rounded down to the
+         tile; tiles wholly before it are skipped).
 
 What the oracle computes is the plain definition: decode attention over a
 paged cache equals ordinary softmax attention of one query over its
@@ -41,6 +46,12 @@ Readings taken where the pages are silent (each listed in the design notes):
     with X = 16 bytes / element size (8 for bf16, 4 for fp32, 16 for fp8).
   * ctx <= 0 gives an all-zero output (no token to attend to).
   * split-KV partitions are logical token ranges [k*P, (k+1)*P).
+  * sliding window ([QA3]): with window W > 0 a query at position p attends to
+    positions max(0, p - W + 1) .. p, i.e. its own position and the W - 1
+    before it; W = 0 means the whole context.  In split mode the partitions of
+    a windowed query start at the block holding its first visible position:
+    partition k covers [r + k*P, r + (k+1)*P) with r = 16 * floor(first / 16),
+    positions before `first` getting no weight.
   * fp8 cache ([FDE9]): elements are OCP E4M3 codes (the format ROCm's
     fp8_e4m3 names); a cached value is code value * per-tensor scale.  The
     write stores the nearest E4M3 value of x / scale, the division done in
@@ -71,6 +82,7 @@ __all__ = [
     "v_offset",
     "blocks_needed",
     "slot_mapping",
+    "window_first",
     "chunk_slots",
     "reshape_and_cache",
     "gather_sequence",
@@ -308,22 +320,32 @@ def gather_sequence(k_pool: np.ndarray, v_pool: np.ndarray, table_row: np.ndarra
     return K, V
 
 
+def window_first(pos: int, window: int) -> int:
+    """First position a query at position pos sees ([QA3]): pos - W + 1, not
+    below 0; 0 for W = 0 (the whole context)."""
+    return max(0, int(pos) - int(window) + 1) if window > 0 else 0
+
+
 def decode_sequence(k_pool, v_pool, q_b: np.ndarray, table_row, ctx: int,
                     H: int, H_kv: int, d: int, dtype: str, scale: float,
-                    k_scale: float = 1.0, v_scale: float = 1.0) -> np.ndarray:
+                    k_scale: float = 1.0, v_scale: float = 1.0, window: int = 0) -> np.ndarray:
     """Output [H, d] of one sequence: softmax(scale * K q_h) V per query head.
 
     [WB] step(): attn = softmax(K @ q / sqrt(d)); ctx = attn @ V, over every
-    cached row including the new one.  Max-subtracted softmax in float64.
+    cached row including the new one; with a window W > 0, over the rows of
+    positions window_first(ctx - 1, W) .. ctx - 1 only ([QA3]).
+    Max-subtracted softmax in float64.
     """
     g = H // H_kv
     out = np.zeros((H, d))
     if ctx <= 0:
         return out
+    first = window_first(ctx - 1, window)
     q = bits_to_f64(q_b, act_dtype(dtype)).reshape(H, d)
     for kvh in range(H_kv):
         K, V = gather_sequence(k_pool, v_pool, table_row, ctx, kvh, H_kv, d, dtype,
                                k_scale, v_scale)
+        K, V = K[first:], V[first:]
         for h in range(kvh * g, (kvh + 1) * g):
             s = scale * (K @ q[h])
             p = np.exp(s - s.max())
@@ -333,7 +355,8 @@ def decode_sequence(k_pool, v_pool, q_b: np.ndarray, table_row, ctx: int,
 
 def decode_multi(k_pool, v_pool, q_rows: np.ndarray, query_start, block_tables,
                  context_lens, H: int, H_kv: int, d: int, dtype: str, scale: float,
-                 k_scale: float = 1.0, v_scale: float = 1.0, seqs=None) -> dict:
+                 k_scale: float = 1.0, v_scale: float = 1.0, seqs=None,
+                 window: int = 0) -> dict:
     """Attention of several new query tokens per sequence, causal within them.
 
     [API] (chunked prefill: a prompt enters in chunks, e.g. of 512 tokens,
@@ -342,7 +365,8 @@ def decode_multi(k_pool, v_pool, q_rows: np.ndarray, query_start, block_tables,
     - query_start[b] query rows (q_rows [T, H, d] bits) are the tokens at
     positions ctx_b - n_b .. ctx_b - 1, whose K/V rows are already in the cache
     (context_lens count them); the token at position p attends to positions
-    0..p: the [WB] step() attention with the rows appended one at a time.
+    0..p: the [WB] step() attention with the rows appended one at a time
+    (with a window W > 0: positions window_first(p, W) .. p, [QA3]).
     Returns {b: float64 [n_b, H, d]}.
     """
     g = H // H_kv
@@ -358,44 +382,51 @@ def decode_multi(k_pool, v_pool, q_rows: np.ndarray, query_start, block_tables,
                                    k_scale, v_scale)
             for j in range(n):
                 p = ctx - n + j
+                f = window_first(p, window)
                 for h in range(kvh * g, (kvh + 1) * g):
-                    sc = scale * (K[:p + 1] @ q[j, h])
+                    sc = scale * (K[f:p + 1] @ q[j, h])
                     w = np.exp(sc - sc.max())
-                    rows[j, h] = (w @ V[:p + 1]) / w.sum()
+                    rows[j, h] = (w @ V[f:p + 1]) / w.sum()
         out[b] = rows
     return out
 
 
 def decode(k_pool, v_pool, q: np.ndarray, block_tables: np.ndarray,
            context_lens: np.ndarray, H: int, H_kv: int, d: int, dtype: str,
-           scale: float, k_scale: float = 1.0, v_scale: float = 1.0) -> np.ndarray:
+           scale: float, k_scale: float = 1.0, v_scale: float = 1.0,
+           window: int = 0) -> np.ndarray:
     """Float64 decode-attention output [B, H, d] for a whole batch."""
     B = len(context_lens)
     out = np.zeros((B, H, d))
     for b in range(B):
         out[b] = decode_sequence(k_pool, v_pool, q[b], block_tables[b],
                                  int(context_lens[b]), H, H_kv, d, dtype, scale,
-                                 k_scale, v_scale)
+                                 k_scale, v_scale, window)
     return out
 
 
 def partials(k_pool, v_pool, q, block_tables, context_lens, H: int, H_kv: int,
              d: int, dtype: str, scale: float, partition_size: int,
-             k_scale: float = 1.0, v_scale: float = 1.0):
+             k_scale: float = 1.0, v_scale: float = 1.0, window: int = 0):
     """Per-partition (o, m, l) of split-KV decode.
 
-    Partition k of a sequence covers logical tokens [k*P, min((k+1)*P, ctx)).
-    For its scores s: m_k = max s, l_k = sum exp(s - m_k), and
-    o_k = sum exp(s - m_k) v / l_k.  These are the running max and denominator
-    of [QA] Q4's online softmax, taken over one partition.
-    Returns (o [B,H,Pmax,d], m [B,H,Pmax], l [B,H,Pmax], counts [B]).
+    Partition k of a sequence covers logical tokens [r + k*P, min(r + (k+1)*P,
+    ctx)), r = 0 without a window; with a window W, r is the start of the block
+    holding the first visible position f = window_first(ctx - 1, W), and
+    positions before f get no weight.  For a partition's scores s: m_k = max s,
+    l_k = sum exp(s - m_k), and o_k = sum exp(s - m_k) v / l_k.  These are the
+    running max and denominator of [QA] Q4's online softmax, taken over one
+    partition.  Returns (o [B,H,Pmax,d], m [B,H,Pmax], l [B,H,Pmax], counts [B]).
     """
     P = int(partition_size)
     if P <= 0 or P % BLOCK:
         raise ValueError("partition size must be a positive multiple of 16")
     B = len(context_lens)
     g = H // H_kv
-    counts = np.array([-(-max(int(c), 0) // P) for c in context_lens], dtype=np.int64)
+    first = [window_first(int(c) - 1, window) if int(c) > 0 else 0 for c in context_lens]
+    r0 = [f // BLOCK * BLOCK for f in first]
+    counts = np.array([-(-(max(int(c), 0) - r) // P) if int(c) > 0 else 0
+                       for c, r in zip(context_lens, r0)], dtype=np.int64)
     Pmax = max(int(counts.max()) if B else 0, 1)
     o = np.zeros((B, H, Pmax, d))
     m = np.full((B, H, Pmax), -np.inf)
@@ -411,12 +442,14 @@ def partials(k_pool, v_pool, q, block_tables, context_lens, H: int, H_kv: int,
             for h in range(kvh * g, (kvh + 1) * g):
                 s = scale * (K @ qb[h])
                 for k in range(int(counts[b])):
-                    sk = s[k * P:(k + 1) * P]
+                    lo = max(r0[b] + k * P, first[b])
+                    hi = min(r0[b] + (k + 1) * P, n)
+                    sk = s[lo:hi]
                     mk = sk.max()
                     e = np.exp(sk - mk)
                     m[b, h, k] = mk
                     l[b, h, k] = e.sum()
-                    o[b, h, k] = (e @ V[k * P:(k + 1) * P]) / e.sum()
+                    o[b, h, k] = (e @ V[lo:hi]) / e.sum()
     return o, m, l, counts
 
 
