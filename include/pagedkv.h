@@ -213,6 +213,26 @@ kv_status paged_attention_decode(const kv_pool* pool, void* out, const void* que
                                  int32_t partition_size, void* workspace,
                                  size_t workspace_bytes, void* stream);
 
+/* paged_attention_decode with a sliding window ("MLSys Engineer - Inference
+ * Systems Q&A", Q3 item 4: a local-attention layer needs only the last W
+ * tokens; Q4: tiles wholly before the window are never loaded): the query of
+ * sequence b (position ctx_b - 1) attends to positions
+ * max(0, ctx_b - window) .. ctx_b - 1 only, the last `window` tokens; window
+ * = 0 is paged_attention_decode.  Blocks wholly before the window are not
+ * read (their table entries may be anything).  Split mode lays the partitions
+ * out from the start of the block holding the first visible position:
+ * partition k covers [r + k*partition_size, r + (k+1)*partition_size), r =
+ * 16 * floor(max(0, ctx_b - window) / 16), so a sequence has
+ * ceil((ctx_b - r) / partition_size) partitions; merge them with
+ * paged_attention_reduce_window and the same window.  window < 0 is
+ * KV_ERR_INVALID_ARG. */
+kv_status paged_attention_decode_window(const kv_pool* pool, void* out, const void* query,
+                                        const int32_t* block_tables, int32_t max_nb,
+                                        const int32_t* context_lens, int32_t B, int32_t H,
+                                        int32_t max_context_len, float scale, int32_t window,
+                                        int32_t partition_size, void* workspace,
+                                        size_t workspace_bytes, void* stream);
+
 /* Merge split partials (the workspace paged_attention_decode wrote with the
  * same B, H, head_dim, max_context_len and partition_size) by log-sum-exp:
  * with M = max_k m_k and w_k = l_k * 2^(m_k - M),
@@ -227,6 +247,14 @@ kv_status paged_attention_reduce(void* out, const void* workspace,
                                  int32_t head_dim, int32_t max_context_len,
                                  int32_t partition_size, kv_dtype out_dtype,
                                  void* stream);
+
+/* paged_attention_reduce for partials paged_attention_decode_window wrote
+ * (the partition layout above); window = 0 is paged_attention_reduce. */
+kv_status paged_attention_reduce_window(void* out, const void* workspace,
+                                        const int32_t* context_lens, int32_t B, int32_t H,
+                                        int32_t head_dim, int32_t max_context_len,
+                                        int32_t window, int32_t partition_size,
+                                        kv_dtype out_dtype, void* stream);
 
 /* Attention of several new query tokens per sequence, causal within them: the
  * workbook's incremental decoder with the rows appended one at a time,
@@ -246,12 +274,14 @@ kv_status paged_attention_reduce(void* out, const void* workspace,
  * (those below max_query_len; nothing is written past it).  A table entry
  * outside the pool that a row's range reaches makes that row NaN (and may make
  * other rows of its sequence NaN).  n_b <= 0 writes nothing, and a sequence
- * whose rows do not lie inside [0, num_rows) is skipped whole. */
+ * whose rows do not lie inside [0, num_rows) is skipped whole.  window > 0: a
+ * sliding window as in paged_attention_decode_window, per row (the row at
+ * position p sees max(0, p - window + 1) .. p); 0 = the whole context. */
 kv_status paged_attention_multi(const kv_pool* pool, void* out, const void* query,
                                 int32_t num_rows, const int32_t* query_start,
                                 int32_t max_query_len, const int32_t* block_tables,
                                 int32_t max_nb, const int32_t* context_lens, int32_t B, int32_t H,
-                                float scale, void* stream);
+                                float scale, int32_t window, void* stream);
 
 /* Copy whole blocks on the GPU: for i < n, block src[i] of both caches (all KV
  * heads, all 16 slots, K and V) is copied to block dst[i].  This is the data

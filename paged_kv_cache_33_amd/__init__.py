@@ -250,9 +250,10 @@ def kv_cache_append_chunk(pool: KVPool, key: torch.Tensor, value: torch.Tensor,
 def paged_attention_multi(pool: KVPool, out: torch.Tensor, query: torch.Tensor,
                           query_start: torch.Tensor, max_query_len: int,
                           block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
-                          stream=None) -> None:
+                          stream=None, window: int = 0) -> None:
     """Attention of several new query rows per sequence ([num_rows, H, d], bf16),
-    causal within each sequence's rows; see pagedkv.h."""
+    causal within each sequence's rows (and within a sliding window of `window`
+    positions when > 0); see pagedkv.h."""
     if query.dim() != 3 or query.shape[2] != pool.head_dim:
         raise ValueError("query must be [num_rows, H, head_dim]")
     T, H, d = query.shape
@@ -266,7 +267,7 @@ def paged_attention_multi(pool: KVPool, out: torch.Tensor, query: torch.Tensor,
     cp = _buf(context_lens, "context_lens", 4 * B, dtype=torch.int32)
     _lib.check(_lib.load().paged_attention_multi(
         pool.handle, op, qp, T, qsp, int(max_query_len), tp, max_nb, cp, B, H, float(scale),
-        _stream_handle(stream)))
+        int(window), _stream_handle(stream)))
 
 
 def paged_attention_workspace_bytes(B: int, H: int, head_dim: int, max_context_len: int,
@@ -278,8 +279,10 @@ def paged_attention_workspace_bytes(B: int, H: int, head_dim: int, max_context_l
 def paged_attention_decode(pool: KVPool, out: torch.Tensor, query: torch.Tensor,
                            block_tables: torch.Tensor, context_lens: torch.Tensor,
                            max_context_len: int, scale: float, partition_size: int = 0,
-                           workspace: Optional[torch.Tensor] = None, stream=None) -> None:
-    """Decode attention for one new query per sequence; see pagedkv.h."""
+                           workspace: Optional[torch.Tensor] = None, stream=None,
+                           window: int = 0) -> None:
+    """Decode attention for one new query per sequence; see pagedkv.h.  window
+    > 0 calls paged_attention_decode_window (the last `window` tokens only)."""
     if query.dim() != 3 or query.shape[2] != pool.head_dim:
         raise ValueError("query must be [B, H, head_dim]")
     B, H, d = query.shape
@@ -297,13 +300,20 @@ def paged_attention_decode(pool: KVPool, out: torch.Tensor, query: torch.Tensor,
             raise ValueError("split mode (partition_size > 0) needs a workspace")
         wp = _buf(workspace, "workspace")
         wbytes = workspace.numel() * workspace.element_size()
-    _lib.check(_lib.load().paged_attention_decode(
-        pool.handle, op, qp, tp, max_nb, cp, B, H, int(max_context_len), float(scale),
-        int(partition_size), wp, wbytes, _stream_handle(stream)))
+    lib = _lib.load()
+    if window:
+        _lib.check(lib.paged_attention_decode_window(
+            pool.handle, op, qp, tp, max_nb, cp, B, H, int(max_context_len), float(scale),
+            int(window), int(partition_size), wp, wbytes, _stream_handle(stream)))
+    else:
+        _lib.check(lib.paged_attention_decode(
+            pool.handle, op, qp, tp, max_nb, cp, B, H, int(max_context_len), float(scale),
+            int(partition_size), wp, wbytes, _stream_handle(stream)))
 
 
 def paged_attention_reduce(out: torch.Tensor, workspace: torch.Tensor, context_lens: torch.Tensor,
-                           max_context_len: int, partition_size: int, dtype, stream=None) -> None:
+                           max_context_len: int, partition_size: int, dtype, stream=None,
+                           window: int = 0) -> None:
     """Merge the split partials of paged_attention_decode into out [B, H, d];
     dtype is the output's (an fp8 pool's activation type, bf16, is accepted as
     "fp8" too)."""
@@ -317,9 +327,15 @@ def paged_attention_reduce(out: torch.Tensor, workspace: torch.Tensor, context_l
     if workspace.numel() * workspace.element_size() < need:
         raise ValueError(f"workspace must hold at least {need} bytes")
     cp = _buf(context_lens, "context_lens", 4 * B, dtype=torch.int32)
-    _lib.check(_lib.load().paged_attention_reduce(
-        op, wp, cp, B, H, d, int(max_context_len), int(partition_size), code,
-        _stream_handle(stream)))
+    lib = _lib.load()
+    if window:
+        _lib.check(lib.paged_attention_reduce_window(
+            op, wp, cp, B, H, d, int(max_context_len), int(window), int(partition_size), code,
+            _stream_handle(stream)))
+    else:
+        _lib.check(lib.paged_attention_reduce(
+            op, wp, cp, B, H, d, int(max_context_len), int(partition_size), code,
+            _stream_handle(stream)))
 
 
 def kv_decode_kernel_kind(pool: KVPool, H: int) -> int:

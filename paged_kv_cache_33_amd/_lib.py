@@ -39,7 +39,9 @@ EXPORTED = (
     "kv_cache_append_chunk",
     "paged_attention_workspace_bytes",
     "paged_attention_decode",
+    "paged_attention_decode_window",
     "paged_attention_reduce",
+    "paged_attention_reduce_window",
     "paged_attention_multi",
     "kv_copy_blocks",
     "kv_bm_create",
@@ -108,7 +110,11 @@ def load() -> C.CDLL:
         "kv_cache_append_chunk": (C.c_int, [vp, vp, vp, i32, i32p, i32, i32p, i32, i32p, i32,
                                             vp, vp]),
         "paged_attention_multi": (C.c_int, [vp, vp, vp, i32, i32p, i32, i32p, i32, i32p, i32,
-                                            i32, C.c_float, vp]),
+                                            i32, C.c_float, i32, vp]),
+        "paged_attention_decode_window": (C.c_int, [vp, vp, vp, i32p, i32, i32p, i32, i32, i32,
+                                                    C.c_float, i32, i32, vp, sz, vp]),
+        "paged_attention_reduce_window": (C.c_int, [vp, vp, i32p, i32, i32, i32, i32, i32, i32,
+                                                    C.c_int, vp]),
         "kv_copy_blocks": (C.c_int, [vp, i32p, i32p, i32, vp]),
         "kv_bm_create": (C.c_int, [i32, C.POINTER(vp)]),
         "kv_bm_destroy": (None, [vp]),

@@ -230,10 +230,11 @@ namespace {
 
 kv_status decode_impl(const kv_pool* pool, void* out, const void* query,
                       const int32_t* block_tables, int32_t max_nb, const int32_t* context_lens,
-                      int32_t B, int32_t H, int32_t max_context_len, float scale,
+                      int32_t B, int32_t H, int32_t max_context_len, float scale, int32_t window,
                       int32_t partition_size, void* workspace, size_t workspace_bytes,
                       void* stream) {
   if (!pool) return fail(KV_ERR_INVALID_ARG, "pool is NULL");
+  if (window < 0) return fail(KV_ERR_INVALID_ARG, "window must be >= 0 (0 = whole context)");
   const kv_pool_desc& d = pool->desc;
   if (B < 0) return fail(KV_ERR_INVALID_ARG, "B must be >= 0");
   if (H < 1 || H % d.num_kv_heads != 0)
@@ -278,6 +279,7 @@ kv_status decode_impl(const kv_pool* pool, void* out, const void* query,
   // factor joins the softmax scale; V's factor multiplies the output
   a.scale_log2 = scale * 1.4426950408889634f * (fp8 ? d.k_scale : 1.f);
   a.v_scale = fp8 ? d.v_scale : 1.f;
+  a.window = window;
   a.partition_size = partition_size;
   a.num_partitions = static_cast<int32_t>(P);
   a.ws_o = ws.o;
@@ -302,7 +304,17 @@ kv_status paged_attention_decode(const kv_pool* pool, void* out, const void* que
                                  int32_t max_context_len, float scale, int32_t partition_size,
                                  void* workspace, size_t workspace_bytes, void* stream) {
   return decode_impl(pool, out, query, block_tables, max_nb, context_lens, B, H, max_context_len,
-                     scale, partition_size, workspace, workspace_bytes, stream);
+                     scale, 0, partition_size, workspace, workspace_bytes, stream);
+}
+
+kv_status paged_attention_decode_window(const kv_pool* pool, void* out, const void* query,
+                                        const int32_t* block_tables, int32_t max_nb,
+                                        const int32_t* context_lens, int32_t B, int32_t H,
+                                        int32_t max_context_len, float scale, int32_t window,
+                                        int32_t partition_size, void* workspace,
+                                        size_t workspace_bytes, void* stream) {
+  return decode_impl(pool, out, query, block_tables, max_nb, context_lens, B, H, max_context_len,
+                     scale, window, partition_size, workspace, workspace_bytes, stream);
 }
 
 kv_status kv_cache_append(const kv_pool* pool, const void* key, const void* value,
@@ -367,8 +379,9 @@ kv_status paged_attention_multi(const kv_pool* pool, void* out, const void* quer
                                 int32_t num_rows, const int32_t* query_start,
                                 int32_t max_query_len, const int32_t* block_tables,
                                 int32_t max_nb, const int32_t* context_lens, int32_t B, int32_t H,
-                                float scale, void* stream) {
+                                float scale, int32_t window, void* stream) {
   if (!pool) return fail(KV_ERR_INVALID_ARG, "pool is NULL");
+  if (window < 0) return fail(KV_ERR_INVALID_ARG, "window must be >= 0 (0 = whole context)");
   const kv_pool_desc& d = pool->desc;
   if (d.dtype != KV_BF16 && d.dtype != KV_FP8_E4M3)
     return fail(KV_ERR_UNSUPPORTED, "multi-token attention needs a bf16 or fp8 pool (dtype %d)",
@@ -408,6 +421,7 @@ kv_status paged_attention_multi(const kv_pool* pool, void* out, const void* quer
   const bool fp8 = d.dtype == KV_FP8_E4M3;
   a.scale_log2 = scale * 1.4426950408889634f * (fp8 ? d.k_scale : 1.f);
   a.v_scale = fp8 ? d.v_scale : 1.f;
+  a.window = window;
   // one tile per wave when one tile holds every column; else two per wave,
   // and up to four such sets per work-group
   a.tiles_per_set = tiles > 1 ? 2 : 1;
@@ -433,10 +447,12 @@ kv_status kv_copy_blocks(const kv_pool* pool, const int32_t* src, const int32_t*
                     "copy_blocks launch");
 }
 
-kv_status paged_attention_reduce(void* out, const void* workspace, const int32_t* context_lens,
-                                 int32_t B, int32_t H, int32_t head_dim, int32_t max_context_len,
-                                 int32_t partition_size, kv_dtype out_dtype, void* stream) {
+static kv_status reduce_impl(void* out, const void* workspace, const int32_t* context_lens,
+                             int32_t B, int32_t H, int32_t head_dim, int32_t max_context_len,
+                             int32_t window, int32_t partition_size, kv_dtype out_dtype,
+                             void* stream) {
   if (B < 0 || H < 1) return fail(KV_ERR_INVALID_ARG, "B must be >= 0 and H >= 1");
+  if (window < 0) return fail(KV_ERR_INVALID_ARG, "window must be >= 0 (0 = whole context)");
   if (head_dim != 64 && head_dim != 128)
     return fail(KV_ERR_UNSUPPORTED, "head_dim %d is not supported (64 or 128)", head_dim);
   if (out_dtype != KV_F32 && out_dtype != KV_BF16)
@@ -450,10 +466,26 @@ kv_status paged_attention_reduce(void* out, const void* workspace, const int32_t
   const int64_t P = num_partitions(max_context_len, partition_size);
   WorkspaceView ws = workspace_view(const_cast<void*>(workspace), B, H, head_dim, P);
   pagedkv::ReduceArgs a{out, ws.o, ws.m, ws.l, context_lens, B, H, head_dim,
-                        static_cast<int32_t>(P), partition_size};
+                        static_cast<int32_t>(P), partition_size, window};
   return hip_status(
       pagedkv::launch_reduce(a, out_dtype == KV_BF16, static_cast<hipStream_t>(stream)),
       "reduce launch");
+}
+
+kv_status paged_attention_reduce(void* out, const void* workspace, const int32_t* context_lens,
+                                 int32_t B, int32_t H, int32_t head_dim, int32_t max_context_len,
+                                 int32_t partition_size, kv_dtype out_dtype, void* stream) {
+  return reduce_impl(out, workspace, context_lens, B, H, head_dim, max_context_len, 0,
+                     partition_size, out_dtype, stream);
+}
+
+kv_status paged_attention_reduce_window(void* out, const void* workspace,
+                                        const int32_t* context_lens, int32_t B, int32_t H,
+                                        int32_t head_dim, int32_t max_context_len,
+                                        int32_t window, int32_t partition_size,
+                                        kv_dtype out_dtype, void* stream) {
+  return reduce_impl(out, workspace, context_lens, B, H, head_dim, max_context_len, window,
+                     partition_size, out_dtype, stream);
 }
 
 const char* kv_last_error(void) { return g_last_error.c_str(); }

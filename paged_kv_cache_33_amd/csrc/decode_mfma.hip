@@ -51,7 +51,9 @@ __device__ __forceinline__ void mfma_item(const DecodeArgs& a, const int part, c
 
   const int ctx = a.context_lens[b];
   const bool split = a.partition_size > 0;
-  const int nparts = split ? (ctx > 0 ? (ctx + a.partition_size - 1) / a.partition_size : 0) : 1;
+  const int first = ctx > 0 ? window_first(ctx - 1, a.window) : 0;  // first visible token
+  const int rs = range_start(ctx, a.window);
+  const int nparts = split ? (ctx > 0 ? (ctx - rs + a.partition_size - 1) / a.partition_size : 0) : 1;
   const bool bad_len = ctx > a.max_nb * kBlockTokens || (split && nparts > a.num_partitions);
   uint16_t* out = static_cast<uint16_t*>(a.out);
   auto out_at = [&](int hh, int x) -> uint16_t& {
@@ -81,7 +83,7 @@ __device__ __forceinline__ void mfma_item(const DecodeArgs& a, const int part, c
   }
   if (split && part >= nparts) return;
 
-  const int tb = split ? part * a.partition_size : 0;
+  const int tb = rs + (split ? part * a.partition_size : 0);
   const int te = split ? min(tb + a.partition_size, ctx) : ctx;
   const int jb = tb / kBlockTokens;
   const int je = (te + kBlockTokens - 1) / kBlockTokens;
@@ -137,10 +139,11 @@ __device__ __forceinline__ void mfma_item(const DecodeArgs& a, const int part, c
   auto consume = [&](int j, int64_t tile, const MfmaFrag<E, D>& f) {
     if (tile < 0) { bad_blk = 1; return; }
     const int nvalid = te - j * kBlockTokens;
-    if (nvalid >= kBlockTokens)
-      compute_block<E, D, false>(f, qop, st, nvalid, a.scale_log2, lane);
+    const int nfirst = first - j * kBlockTokens;  // > 0 only where a window starts
+    if (nvalid >= kBlockTokens && nfirst <= 0)
+      compute_block<E, D, false>(f, qop, st, 0, nvalid, a.scale_log2, lane);
     else
-      compute_block<E, D, true>(f, qop, st, nvalid, a.scale_log2, lane);
+      compute_block<E, D, true>(f, qop, st, nfirst, nvalid, a.scale_log2, lane);
   };
   // Ping-pong over two register buffers: block n+1 is in flight while n
   // computes.  Windows of 64 blocks; inside one, every iteration has a next

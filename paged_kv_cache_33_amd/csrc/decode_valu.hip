@@ -84,23 +84,28 @@ __device__ __forceinline__ void e4m3x16_to_bf16(const uint4& v, uint4& lo, uint4
                   e4m3x2_to_bf16x2<false>(v.w), e4m3x2_to_bf16x2<true>(v.w));
 }
 
-// Zero the bf16 V values of tokens >= nvalid inside one 16-byte piece holding
-// tokens first..first+7 of one dim (the same tokens in every lane).
-__device__ __forceinline__ uint4 mask_tail_tokens(uint4 v, int first, int nvalid) {
+// Zero the bf16 V values of tokens outside [nfirst, nvalid) inside one 16-byte
+// piece holding tokens first..first+7 of one dim (the same tokens in every
+// lane).
+__device__ __forceinline__ uint4 mask_tokens(uint4 v, int first, int nfirst, int nvalid) {
   uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     const int t0 = first + 2 * c;
-    w[c] = t0 + 1 < nvalid ? w[c] : (t0 < nvalid ? (w[c] & 0x0000ffffu) : 0u);
+    const bool keep_lo = t0 >= nfirst && t0 < nvalid;
+    const bool keep_hi = t0 + 1 >= nfirst && t0 + 1 < nvalid;
+    w[c] = (keep_lo ? (w[c] & 0x0000ffffu) : 0u) | (keep_hi ? (w[c] & 0xffff0000u) : 0u);
   }
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
-// One block of 16 tokens; `nvalid` (uniform) tokens of it are inside the range.
+// One block of 16 tokens.  With kTail only tokens nfirst .. nvalid-1 (uniform
+// bounds) are inside the range: the block holding the end of the range, or the
+// first position of a sliding window.
 template <typename Tr, int D, bool kTail>
 __device__ __forceinline__ void compute_block(const BlockFrag<Tr, D>& f, const QueryFrag<Tr, D>& qf,
                                               float (&o)[ValuShape<Tr, D>::XK], WaveState& st,
-                                              int nvalid, float scale_log2, int lane) {
+                                              int nfirst, int nvalid, float scale_log2, int lane) {
   using Sh = ValuShape<Tr, D>;
   constexpr bool kFp8 = Tr::kKind == Kind::kFp8;
   constexpr bool kPacked = Tr::kKind != Kind::kF32;  // bf16 pairs into dot2
@@ -134,7 +139,7 @@ __device__ __forceinline__ void compute_block(const BlockFrag<Tr, D>& f, const Q
   dot = cross_row_sum(dot);
   const int t = lane & 15;
   float s = dot * scale_log2;
-  if (kTail && t >= nvalid) s = -INFINITY;  // select, never multiply: slot may hold NaN
+  if (kTail && (t >= nvalid || t < nfirst)) s = -INFINITY;  // select: the slot may hold NaN
   // ---- online softmax over the block's 16 tokens (one per lane of a row)
   const float m_new = fmaxf(st.m, row16_max(s));
   const float alpha = fast_exp2(st.m - m_new);
@@ -152,7 +157,7 @@ __device__ __forceinline__ void compute_block(const BlockFrag<Tr, D>& f, const Q
     for (int k = 0; k < kBlockTokens / 2; ++k)
       pp[k] = __builtin_amdgcn_readlane(packed, 2 * k);
     auto accumulate = [&](uint4 v, int th, float& acc) {  // tokens 8th .. 8th+7
-      if (kTail) v = mask_tail_tokens(v, th * 8, nvalid);
+      if (kTail) v = mask_tokens(v, th * 8, nfirst, nvalid);
       acc = dot2_bf16(v.x, pp[th * 4 + 0], acc);
       acc = dot2_bf16(v.y, pp[th * 4 + 1], acc);
       acc = dot2_bf16(v.z, pp[th * 4 + 2], acc);
@@ -186,7 +191,7 @@ __device__ __forceinline__ void compute_block(const BlockFrag<Tr, D>& f, const Q
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int tt = th * 4 + e;
-          if (!kTail || tt < nvalid) o[xk] = fmaf(ps[tt], vf[e], o[xk]);
+          if (!kTail || (tt < nvalid && tt >= nfirst)) o[xk] = fmaf(ps[tt], vf[e], o[xk]);
         }
       }
     }
@@ -212,7 +217,9 @@ __device__ __forceinline__ void valu_item(const DecodeArgs& a, const int part, c
   const int kvh = h / (a.H / a.num_kv_heads);
   const int ctx = a.context_lens[b];
   const bool split = a.partition_size > 0;
-  const int nparts = split ? (ctx > 0 ? (ctx + a.partition_size - 1) / a.partition_size : 0) : 1;
+  const int first = ctx > 0 ? window_first(ctx - 1, a.window) : 0;  // first visible token
+  const int rs = range_start(ctx, a.window);
+  const int nparts = split ? (ctx > 0 ? (ctx - rs + a.partition_size - 1) / a.partition_size : 0) : 1;
   const bool bad_len = ctx > a.max_nb * kBlockTokens || (split && nparts > a.num_partitions);
   const size_t row = (size_t(b) * a.H + h) * D;
   A* out = static_cast<A*>(a.out) + row;
@@ -236,7 +243,7 @@ __device__ __forceinline__ void valu_item(const DecodeArgs& a, const int part, c
   }
   if (split && part >= nparts) return;
 
-  const int tb = split ? part * a.partition_size : 0;
+  const int tb = rs + (split ? part * a.partition_size : 0);
   const int te = split ? min(tb + a.partition_size, ctx) : ctx;
   const int jb = tb / kBlockTokens;
   const int je = (te + kBlockTokens - 1) / kBlockTokens;
@@ -289,10 +296,11 @@ __device__ __forceinline__ void valu_item(const DecodeArgs& a, const int part, c
   auto consume = [&](int j, int64_t tile, const BlockFrag<Tr, D>& f) {
     if (tile < 0) { bad_blk = 1; return; }
     const int nvalid = te - j * kBlockTokens;
-    if (nvalid >= kBlockTokens)
-      compute_block<Tr, D, false>(f, qf, o, st, nvalid, a.scale_log2, lane);
+    const int nfirst = first - j * kBlockTokens;  // > 0 only where a window starts
+    if (nvalid >= kBlockTokens && nfirst <= 0)
+      compute_block<Tr, D, false>(f, qf, o, st, 0, nvalid, a.scale_log2, lane);
     else
-      compute_block<Tr, D, true>(f, qf, o, st, nvalid, a.scale_log2, lane);
+      compute_block<Tr, D, true>(f, qf, o, st, nfirst, nvalid, a.scale_log2, lane);
   };
   // Ping-pong over two register buffers: block n+1 is in flight while n
   // computes.  Windows of 64 blocks; inside one, every iteration has a next

@@ -27,6 +27,19 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 
 // 2^x on the hardware's transcendental unit (v_exp_f32).  Arguments here are
 // always <= 0 or -inf, where it returns values in [0, 1] and exactly 1 at 0.
+// Sliding window ("MLSys Engineer - Inference Systems Q&A", Q3 item 4 and
+// Q4): a query at position pos sees positions pos - window + 1 .. pos, not
+// below 0; window = 0 means the whole context.
+__device__ __forceinline__ int window_first(int pos, int window) {
+  return window > 0 && pos >= window ? pos - window + 1 : 0;
+}
+// First token of the range a decode query (position ctx - 1) walks: the start
+// of the block holding its first visible position.  Split partitions are laid
+// out from here, so none lies wholly before the window.
+__device__ __forceinline__ int range_start(int ctx, int window) {
+  return ctx > 0 ? window_first(ctx - 1, window) / kBlockTokens * kBlockTokens : 0;
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ float wave_xor_max(float v, int lane_mask) {

@@ -33,6 +33,7 @@ struct DecodeArgs {
   int32_t max_context_len;
   float scale_log2;            // scale * log2(e) (* k_scale for fp8): scores in base 2
   float v_scale;               // output multiplier (fp8: the V scale; else 1)
+  int32_t window;              // sliding window in tokens; 0 = whole context
   int32_t partition_size;      // tokens per partition; 0 = whole sequence
   int32_t num_partitions;      // partitions per sequence in the grid (1 if single pass)
   float* ws_o;                 // [B][H][P][d]   (split mode only)
@@ -60,6 +61,7 @@ struct MultiArgs {
   int32_t H;
   float scale_log2;             // as DecodeArgs
   float v_scale;
+  int32_t window;               // sliding window per row; 0 = whole context
   int32_t tiles_per_set;        // 16-column tiles one wave carries (1 or 2)
   int32_t sets_per_group;       // column sets one work-group takes (1..4)
 };
@@ -75,6 +77,7 @@ struct ReduceArgs {
   int32_t head_dim;
   int32_t num_partitions;
   int32_t partition_size;
+  int32_t window;               // as DecodeArgs: partitions start at range_start
 };
 
 struct CacheWriteArgs {

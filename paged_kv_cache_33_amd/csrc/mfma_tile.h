@@ -109,15 +109,16 @@ __device__ __forceinline__ uint32_t zero_masked_pair(uint32_t w, bool keep_lo, b
 }
 
 // One 16-token block: S = K Q^T, the online softmax per column, O^T += V^T P^T.
-// nvalid (uniform): tokens of the block inside the range; with kTail the rest
-// get no weight and their V is zeroed (their slots may hold NaN).  kCausal: the
-// block's first token is at key position key0 and this lane's column may see
-// positions <= limit only.
+// With kTail only tokens nfirst .. nvalid-1 of the block (uniform bounds) are
+// inside the range; the rest get no weight and their V is zeroed (their slots
+// may hold NaN).  kCausal: the block's first token is at key position key0 and
+// this lane's column may see positions lo .. limit only.
 template <typename E, int D, bool kTail, bool kCausal = false>
 __device__ __forceinline__ void compute_block(const MfmaFrag<E, D>& f,
                                               const bf16x8_t (&qop)[MfmaShape<D>::KI],
-                                              MfmaState<D>& st, int nvalid, float scale_log2,
-                                              int lane, int key0 = 0, int limit = 0) {
+                                              MfmaState<D>& st, int nfirst, int nvalid,
+                                              float scale_log2, int lane, int key0 = 0,
+                                              int lo = 0, int limit = 0) {
   const int q = lane >> 4;
   floatx4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -127,8 +128,9 @@ __device__ __forceinline__ void compute_block(const MfmaFrag<E, D>& f,
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     sc[j] = s[j] * scale_log2;
-    if (kTail && 4 * q + j >= nvalid) sc[j] = -INFINITY;  // select: the slot may hold NaN
-    if (kCausal && key0 + 4 * q + j > limit) sc[j] = -INFINITY;
+    if (kTail && (4 * q + j >= nvalid || 4 * q + j < nfirst))
+      sc[j] = -INFINITY;  // select: the slot may hold NaN
+    if (kCausal && (key0 + 4 * q + j > limit || key0 + 4 * q + j < lo)) sc[j] = -INFINITY;
   }
   const float mx = cross_row_max(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
   // The reference max st.m moves only when a head's block max exceeds it by
@@ -137,12 +139,14 @@ __device__ __forceinline__ void compute_block(const MfmaFrag<E, D>& f,
   // not depend on the reference, so only rounding changes.
   const bool grow = mx > st.m + kRescaleSlack;
   if (__builtin_amdgcn_ballot_w64(grow) != 0) {  // wave-uniform branch
-    const float m_new = grow ? mx : st.m;
-    const float alpha = fast_exp2(st.m - m_new);
+    // Only growing columns rescale.  The others keep factor 1: a column that
+    // has seen no key yet (m = -inf, possible under causal and window masks)
+    // would otherwise get 2^(-inf - -inf) = NaN.
+    const float alpha = grow ? fast_exp2(st.m - mx) : 1.f;
     st.l *= alpha;
 #pragma unroll
     for (int mc = 0; mc < MfmaShape<D>::MC; ++mc) st.o[mc] *= alpha;
-    st.m = m_new;
+    st.m = grow ? mx : st.m;
   }
   // weights rounded to bf16 for the matrix core; the denominator sums the
   // same rounded values.  Causal: a column that has seen no position yet
@@ -157,9 +161,11 @@ __device__ __forceinline__ void compute_block(const MfmaFrag<E, D>& f,
 #pragma unroll
   for (int mc = 0; mc < MfmaShape<D>::MC; ++mc) {
     uint2 v = v_operand<E, D>(f, mc);
-    if (kTail) {  // tokens past the range get weight 0; their V must be 0, not NaN
-      v.x = zero_masked_pair(v.x, 4 * q + 0 < nvalid, 4 * q + 1 < nvalid);
-      v.y = zero_masked_pair(v.y, 4 * q + 2 < nvalid, 4 * q + 3 < nvalid);
+    if (kTail) {  // tokens outside the range get weight 0; their V must be 0, not NaN
+      const int t = 4 * q;
+      v.x = zero_masked_pair(v.x, t >= nfirst && t < nvalid, t + 1 >= nfirst && t + 1 < nvalid);
+      v.y = zero_masked_pair(v.y, t + 2 >= nfirst && t + 2 < nvalid,
+                             t + 3 >= nfirst && t + 3 < nvalid);
     }
     st.o[mc] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(short4_t, v), pop,
                                                         st.o[mc], 0, 0, 0);

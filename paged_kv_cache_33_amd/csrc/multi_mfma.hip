@@ -16,8 +16,9 @@
 // from HBM serves every head of the group for up to 16/g tokens at once (or 16
 // heads of one token when g > 16).  The per-block arithmetic is the decode
 // kernel's (mfma_tile.h) with one more mask: lane column c may see keys up to
-// its own position.  Blocks wholly visible to every column of the tile take
-// the unmasked path.
+// its own position (and, with a sliding window, none before its position
+// minus window - 1).  Blocks wholly visible to every column of the tile take
+// the unmasked path; blocks wholly before every column's window are skipped.
 //
 // A wave carries one or two column tiles (a column set): the tiles' query
 // operands and running states sit side by side in its registers and every
@@ -44,10 +45,11 @@ constexpr int kMaxSetsPerGroup = 4;
 // kTiles (1 or 2): 16-column tiles one wave carries.  A wave holds the query
 // operands and running state of each of its tiles and feeds them all from
 // the same K/V registers, so a block is loaded once for 16 * kTiles columns.
-// Two tiles take 2 waves per SIMD instead of 3 (the second state costs 48
-// VGPRs at d = 128).
+// Both variants run 2 waves per SIMD: the second state costs 48 VGPRs at
+// d = 128, and even one tile with its per-column causal and window bounds
+// spills at 3 (measured: 3 per SIMD with spills was 8% slower).
 template <typename E, int D, int kTiles>
-__global__ __launch_bounds__(kMultiWaves* kWave, kTiles == 1 ? 3 : 2) void multi_mfma_kernel(
+__global__ __launch_bounds__(kMultiWaves* kWave, 2) void multi_mfma_kernel(
     MultiArgs a) {
   using S = typename E::storage;
   constexpr int KI = MfmaShape<D>::KI;
@@ -105,24 +107,29 @@ __global__ __launch_bounds__(kMultiWaves* kWave, kTiles == 1 ? 3 : 2) void multi
   const int scb = (s0 + my) * kSetCols;
   const int sce = active ? min(scb + kSetCols, ncols) : scb;
   const int pos0 = ctx - nq;  // position of the sequence's first new token
-  // Keys every column of the set may see (<= kmin) and that some column may
-  // see (< kend).
+  // Keys every column of the set may see (klo_max .. kmin) and that some
+  // column may see (klo .. kend - 1): the first column has the lowest position,
+  // the last the highest (with a sliding window both bounds move with it).
   const int kmin = pos0 + scb / g;
   const int kend = active ? pos0 + (sce - 1) / g + 1 : 0;
+  const int klo = window_first(kmin, a.window);
+  const int klo_max = active ? window_first(kend - 1, a.window) : 0;
+  const int jb = klo / kBlockTokens;
   const int je = (kend + kBlockTokens - 1) / kBlockTokens;
   // Tiles of the set that hold columns (uniform): the second may be empty.
   const int ntiles = active ? (sce - scb + kHeadsPerTile - 1) / kHeadsPerTile : 0;
 
-  // Lane column c = scb + 16 tt + n of tile tt: token c / g (limit: its own
-  // position), head c % g.  Columns past the set's end take zero queries and
-  // see up to kend - 1.
-  int limit[kTiles];
+  // Lane column c = scb + 16 tt + n of tile tt: token c / g (it sees lo ..
+  // limit, limit its own position), head c % g.  Columns past the set's end
+  // take zero queries and see what the last column sees.
+  int limit[kTiles], lo[kTiles];
   bf16x8_t qop[kTiles][KI];
 #pragma unroll
   for (int tt = 0; tt < kTiles; ++tt) {
     const int c = scb + tt * kHeadsPerTile + n;
     const bool col_ok = c < sce;
     limit[tt] = col_ok ? pos0 + c / g : kend - 1;
+    lo[tt] = window_first(limit[tt], a.window);
     const int cc = col_ok ? c : scb;
     const uint16_t* qrow = static_cast<const uint16_t*>(a.query) +
                            ((int64_t(q0) + cc / g) * a.H + kvh * g + cc % g) * D;
@@ -159,18 +166,20 @@ __global__ __launch_bounds__(kMultiWaves* kWave, kTiles == 1 ? 3 : 2) void multi
     if (tile < 0) { bad_blk = 1; return; }
     const int key0 = j * kBlockTokens;
     const int nvalid = kend - key0;
-    const bool open = nvalid >= kBlockTokens && key0 + kBlockTokens - 1 <= kmin;
+    const int nfirst = klo - key0;  // tokens below klo: masked for every column
+    const bool open =
+        nvalid >= kBlockTokens && key0 + kBlockTokens - 1 <= kmin && key0 >= klo_max;
 #pragma unroll
     for (int tt = 0; tt < kTiles; ++tt) {
       if (tt > 0 && tt >= ntiles) break;  // uniform: an empty second tile
       if (open)
-        compute_block<E, D, false>(f, qop[tt], st[tt], nvalid, a.scale_log2, lane);
+        compute_block<E, D, false>(f, qop[tt], st[tt], 0, nvalid, a.scale_log2, lane);
       else
-        compute_block<E, D, true, true>(f, qop[tt], st[tt], nvalid, a.scale_log2, lane, key0,
-                                        limit[tt]);
+        compute_block<E, D, true, true>(f, qop[tt], st[tt], nfirst, nvalid, a.scale_log2, lane,
+                                        key0, lo[tt], limit[tt]);
     }
   };
-  walk_blocks<MfmaFrag<E, D>>(phase, wps, je, lane, table, fetch, consume);
+  walk_blocks<MfmaFrag<E, D>>(jb + phase, wps, je, lane, table, fetch, consume);
 
 #pragma unroll
   for (int tt = 0; tt < kTiles; ++tt) {

@@ -56,7 +56,8 @@ __global__ __launch_bounds__(kReduceThreads) void lse_reduce_kernel(ReduceArgs a
   const int h = blockIdx.x;
   const int b = blockIdx.y;
   const int ctx = a.context_lens[b];
-  const int nparts = ctx > 0 ? (ctx + a.partition_size - 1) / a.partition_size : 0;
+  const int nparts =
+      ctx > 0 ? (ctx - range_start(ctx, a.window) + a.partition_size - 1) / a.partition_size : 0;
   S* out = static_cast<S*>(a.out) + (size_t(b) * a.H + h) * D;
 
   if (nparts == 1) return;  // the decode kernel wrote this row itself

@@ -1,6 +1,7 @@
 // Work list of split-KV decode: the (sequence, partition) items that exist.
 //
-// A sequence of ctx tokens has ceil(ctx / P) partitions of P tokens.  Sizing a
+// A sequence of ctx tokens has ceil((ctx - r) / P) partitions of P tokens, r
+// the start of its range (0 without a sliding window).  Sizing a
 // grid by the longest sequence would launch mostly empty work-groups when
 // lengths differ (100,000 and 17 tokens in one batch); instead every
 // work-group builds the prefix sum of the per-sequence partition counts in LDS
@@ -15,14 +16,14 @@
 namespace pagedkv {
 
 // Fills starts[0..B] with the exclusive prefix sum of the per-sequence item
-// counts (min(ceil(ctx/P), P_max); 0 for ctx <= 0) and returns the total.
+// counts (min(ceil((ctx - r)/P), P_max); 0 for ctx <= 0) and returns the total.
 // Must be called by every thread of the work-group.
 __device__ __forceinline__ int build_work_list(const DecodeArgs& a, int* starts) {
   const int B = a.B;
   const int P = a.partition_size;
   for (int t = threadIdx.x; t < B; t += blockDim.x) {
     const int ctx = a.context_lens[t];
-    const int np = ctx > 0 ? (ctx + P - 1) / P : 0;
+    const int np = ctx > 0 ? (ctx - range_start(ctx, a.window) + P - 1) / P : 0;
     starts[t + 1] = min(np, a.num_partitions);
   }
   __syncthreads();

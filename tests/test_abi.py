@@ -177,9 +177,9 @@ def test_decode_argument_errors(lib, pool):
 
 
 def _multi(lib, pool, B=2, H=4, T=6, mq=4, max_nb=4, scale=0.1, out=FAKE_K, q=FAKE_V,
-           qs=FAKE_K):
+           qs=FAKE_K, window=0):
     return lib.paged_attention_multi(pool, out, q, T, qs, mq, FAKE_K, max_nb, FAKE_V, B, H, scale,
-                                     None)
+                                     window, None)
 
 
 def test_multi_argument_errors(lib, pool):
@@ -190,6 +190,7 @@ def test_multi_argument_errors(lib, pool):
     assert _multi(lib, pool, mq=-1) == _lib.KV_ERR_INVALID_ARG
     assert _multi(lib, pool, max_nb=0) == _lib.KV_ERR_INVALID_ARG
     assert _multi(lib, pool, scale=float("nan")) == _lib.KV_ERR_INVALID_ARG
+    assert _multi(lib, pool, window=-1) == _lib.KV_ERR_INVALID_ARG
     assert _multi(lib, pool, qs=None) == _lib.KV_ERR_INVALID_ARG
     assert _multi(lib, pool, out=None) == _lib.KV_ERR_INVALID_ARG
     assert _multi(lib, pool, q=FAKE_V + 8) == _lib.KV_ERR_INVALID_ARG
@@ -217,6 +218,24 @@ def test_append_chunk_argument_errors(lib, pool):
     assert f(value=FAKE_V + 2) == _lib.KV_ERR_INVALID_ARG
     for nothing in (dict(B=0), dict(T=0), dict(mq=0)):
         assert f(key=None, **nothing) == _lib.KV_OK
+
+
+def test_window_argument_errors(lib, pool):
+    f = lib.paged_attention_decode_window
+    assert f(pool, FAKE_K, FAKE_V, FAKE_K, 4, FAKE_V, 2, 4, 64, 0.1, -1, 0, None, 0, None) \
+        == _lib.KV_ERR_INVALID_ARG
+    assert b"window" in lib.kv_last_error()
+    assert f(None, FAKE_K, FAKE_V, FAKE_K, 4, FAKE_V, 2, 4, 64, 0.1, 8, 0, None, 0, None) \
+        == _lib.KV_ERR_INVALID_ARG
+    assert f(pool, FAKE_K, FAKE_V, FAKE_K, 4, FAKE_V, 2, 4, 64, 0.1, 8, 16, None, 0, None) \
+        == _lib.KV_ERR_WORKSPACE
+    assert f(pool, None, None, None, 4, None, 0, 4, 64, 0.1, 8, 0, None, 0, None) == _lib.KV_OK
+    r = lib.paged_attention_reduce_window
+    assert r(FAKE_K, FAKE_V, FAKE_K, 2, 4, 128, 64, -3, 16, _lib.KV_BF16, None) \
+        == _lib.KV_ERR_INVALID_ARG
+    assert r(FAKE_K, FAKE_V, FAKE_K, 2, 4, 128, 64, 8, 0, _lib.KV_BF16, None) \
+        == _lib.KV_ERR_INVALID_ARG
+    assert r(None, None, None, 0, 4, 128, 64, 8, 16, _lib.KV_BF16, None) == _lib.KV_OK
 
 
 def test_workspace_size_formula(lib):
