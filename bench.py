@@ -63,6 +63,9 @@ def parse_args(argv=None):
     ap.add_argument("--kv-dtype", default="bf16", choices=["bf16", "fp8"],
                     help="cache element type: bf16 (the workloads as configured) or fp8 "
                          "(E4M3 codes, scales 1.0, bf16 activations)")
+    ap.add_argument("--window", type=int, default=0,
+                    help="sliding window in tokens (0 = whole context): each decode query "
+                         "attends to its last W positions (paged_attention_decode_window)")
     ap.add_argument("--cold", action="store_true",
                     help="evict the caches before every step and time steps one by one")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -99,13 +102,17 @@ def kernel_source_hash() -> str:
     return h.hexdigest()
 
 
-def step_bytes(w, step) -> dict:
-    """Algorithmic bytes of one step (each byte the method must move, once)."""
+def step_bytes(w, step, window: int = 0) -> dict:
+    """Algorithmic bytes of one step (each byte the method must move, once).
+    With a sliding window only the visible positions' K/V count (and the
+    table entries of their blocks)."""
     e = w.elem_bytes            # query, output, rows handed to the write
     ec = w.kv_elem_bytes        # cache elements
     ctx = step.context_lens.astype(np.int64)
     ctx = np.maximum(ctx, 0)
-    nb = (ctx + 15) // 16
+    first = np.maximum(ctx - window, 0) if window > 0 else np.zeros_like(ctx)
+    nb = (ctx + 15) // 16 - first // 16
+    ctx = ctx - first
     kv = int(ctx.sum()) * w.H_kv * w.d * 2 * ec
     qo = 2 * w.B * w.H * w.d * e
     decode = kv + qo + 4 * int(nb.sum()) + 4 * w.B
@@ -145,13 +152,13 @@ def calib_copy(mib: int, iters: int = 5) -> None:
 _CPU = {}  # state the forked workers read (shared copy-on-write)
 
 
-def _cpu_prepare(w):
+def _cpu_prepare(w, window: int = 0):
     import oracle as O
     step = w.steps[0]
     slots = O.slot_mapping(w.block_tables, step.context_lens)
     kp, vp = O.reshape_and_cache(w.k_pool, w.v_pool, step.new_k, step.new_v, slots, w.H_kv, w.d,
                                  w.kv_dtype, w.num_blocks, w.k_scale, w.v_scale)
-    _CPU.update(w=w, kp=kp, vp=vp)
+    _CPU.update(w=w, kp=kp, vp=vp, window=window)
 
 
 def _cpu_one(b: int) -> np.ndarray:
@@ -160,7 +167,13 @@ def _cpu_one(b: int) -> np.ndarray:
     step = w.steps[0]
     return O.decode_sequence(_CPU["kp"], _CPU["vp"], step.q[b], w.block_tables[b],
                              int(step.context_lens[b]), w.H, w.H_kv, w.d, w.kv_dtype, w.scale,
-                             w.k_scale, w.v_scale)
+                             w.k_scale, w.v_scale, window=_CPU["window"])
+
+
+def _visible(ctx, window: int) -> int:
+    """Context tokens a decode query attends to."""
+    c = max(int(ctx), 0)
+    return min(c, window) if window > 0 else c
 
 
 def _cpu_worker(args):
@@ -174,7 +187,7 @@ def _cpu_worker(args):
         while True:
             for b in seqs:
                 _cpu_one(int(b))
-                tokens += int(_CPU["w"].steps[0].context_lens[b])
+                tokens += _visible(_CPU["w"].steps[0].context_lens[b], _CPU["window"])
                 if time.perf_counter() - t0 >= budget_s:
                     return tokens, time.perf_counter() - t0
 
@@ -192,12 +205,12 @@ def _host_info() -> dict:
     return {"cpu_model": model, "affinity_cores": len(os.sched_getaffinity(0))}
 
 
-def cpu_baseline(w, budget_s: float, par_budget_s: float):
+def cpu_baseline(w, budget_s: float, par_budget_s: float, window: int = 0):
     """Oracle throughput on a bounded sample of the first step.  Returns the
     record and {sequence: float64 output [H, d]} of the one-thread sample."""
     import multiprocessing as mp
     from threadpoolctl import threadpool_limits
-    _cpu_prepare(w)
+    _cpu_prepare(w, window)
     step = w.steps[0]
     order = np.random.default_rng(1234).permutation(w.B)
     # one thread: the sampled sequences' outputs are the parity reference; once
@@ -210,11 +223,11 @@ def cpu_baseline(w, budget_s: float, par_budget_s: float):
                 ref = _cpu_one(int(b))
                 elapsed += time.perf_counter() - t
                 refs.setdefault(int(b), ref)
-                tokens += int(step.context_lens[b])
+                tokens += _visible(step.context_lens[b], window)
                 if elapsed >= budget_s:
                     break
-    total_tokens = int(np.maximum(step.context_lens, 0).sum())
-    dec_bytes = step_bytes(w, step)["decode"]
+    total_tokens = sum(_visible(c, window) for c in step.context_lens)
+    dec_bytes = step_bytes(w, step, window)["decode"]
     one_step_s = elapsed / max(tokens, 1) * total_tokens
 
     host = _host_info()
@@ -583,7 +596,7 @@ def main(argv=None) -> int:
     cpu_rec, refs = None, None
     if not (args.no_cpu_baseline or args.decode_only):
         t0 = time.time()
-        cpu_rec, refs = cpu_baseline(w, args.cpu_seconds, args.cpu_parallel_seconds)
+        cpu_rec, refs = cpu_baseline(w, args.cpu_seconds, args.cpu_parallel_seconds, args.window)
         print(f"[bench] cpu baseline done in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
 
     import torch
@@ -631,11 +644,12 @@ def main(argv=None) -> int:
         if ev is not None:
             ev[1].record(stream)
         P.paged_attention_decode(pool, out, s["q"], tables, s["ctx"], L_max, w.scale, part, ws,
-                                 stream)
+                                 stream, window=args.window)
         if ev is not None:
             ev[2].record(stream)
         if part:
-            P.paged_attention_reduce(out, ws, s["ctx"], L_max, part, w.dtype, stream)
+            P.paged_attention_reduce(out, ws, s["ctx"], L_max, part, w.dtype, stream,
+                                     window=args.window)
         if ev is not None:
             ev[3].record(stream)
 
@@ -643,7 +657,7 @@ def main(argv=None) -> int:
         s = steps_dev[0]
         for _ in range(args.warmup + args.steps):
             P.paged_attention_decode(pool, out, s["q"], tables, s["ctx"], L_max, w.scale, part,
-                                     ws, stream)
+                                     ws, stream, window=args.window)
         torch.cuda.synchronize()
         print(json.dumps({"decode_only_launches": args.warmup + args.steps}), flush=True)
         return 0
@@ -688,13 +702,14 @@ def main(argv=None) -> int:
         ms_step = float(step_ms.mean())
     dec_avg = float(dec_ms.mean())
 
-    by = [step_bytes(w, st) for st in w.steps]
+    by = [step_bytes(w, st, args.window) for st in w.steps]
     used = [by[i % len(by)] for i in range(args.steps)]
     step_b = float(np.mean([u["step"] for u in used]))
     dec_b = float(np.mean([u["decode"] for u in used]))
     gbs = step_b / (ms_step * 1e-3) / 1e9
     dec_gbs = dec_b / (dec_avg * 1e-3) / 1e9
-    traffic = traffic_from_profile(kernel, w.name)
+    wname = w.name + (f"-window{args.window}" if args.window else "")
+    traffic = traffic_from_profile(kernel, wname)
 
     def pct(a, q):
         return round(float(np.percentile(a, q)), 5)
@@ -713,7 +728,7 @@ def main(argv=None) -> int:
         "dtype": w.dtype if w.kv_dtype == w.dtype else f"{w.kv_dtype} cache, {w.dtype} activations",
         "data": "synthetic",
         "config": {
-            "workload": w.name,
+            "workload": wname,
             "batch": w.B,
             "query_heads": w.H,
             "kv_heads": w.H_kv,
@@ -722,10 +737,14 @@ def main(argv=None) -> int:
             "sum_context_tokens": int(w.steps[0].context_lens.astype(np.int64).sum()),
             "max_context_tokens": L_max,
             "partition_size": part,
+            "window": args.window,
             "seed": w.seed,
             "kv_cache": w.kv_dtype,
             "step": ("kv_slot_mapping + reshape_and_cache" if args.unfused else "kv_cache_append")
-                    + " + paged_attention_decode" + (" + paged_attention_reduce" if part else ""),
+                    + (" + paged_attention_decode_window" if args.window else
+                       " + paged_attention_decode")
+                    + ((" + paged_attention_reduce_window" if args.window else
+                        " + paged_attention_reduce") if part else ""),
             "caches": "evicted before every step" if args.cold else "warm (steps back to back)",
         },
         "decode_steps_per_sec": round(1000.0 / ms_step, 1),
