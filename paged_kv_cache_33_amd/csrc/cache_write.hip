@@ -15,6 +15,8 @@
 // caches, those lines would be evicted one by one in the middle of the next
 // decode's read stream and cost it far more than their size.  Streamed out
 // here, they are gone before the decode starts.
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -134,43 +136,104 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
                         vc);
 }
 
-// Several new tokens per sequence (a prefill chunk, draft tokens): one thread
-// per (row j of sequence b, kv head, 16-byte chunk), over j < max_query_len.
-// Row query_start[b] + j sits at position ctx - n + j (n = query_start[b+1] -
-// query_start[b]); its slot follows the table as for one token.  A sequence
-// whose rows are not inside [0, num_rows) is skipped whole; a row whose
-// position is negative or past the table, or whose entry is outside the pool,
-// gets slot -1 and no write.
+// Several new tokens per sequence (a prefill chunk, draft tokens).  Row
+// query_start[b] + j sits at position ctx - n + j (n = query_start[b+1] -
+// query_start[b], j < max_query_len); its slot follows the table as for one
+// token.  One work-group per (block kb touched by the rows, KV head, sequence)
+// writes that block's tile at once:
+//   K: thread (chunk c, slot s) stores the 16-byte chunk; the 16 slots of one
+//      chunk are contiguous in the [d/X][16][X] tile, so a wave's stores are;
+//   V: the rows' values pass through LDS (slot-major, padded) and thread
+//      (dim x, piece) stores the 16 bytes of the dim's [16]-slot row that the
+//      piece covers.  A piece the rows cover only in part is read, merged and
+//      written back: this work-group is the only writer of the tile in the call
+//      (blocks are not shared between the sequences of one call), and the
+//      slots it keeps are written back bit for bit.
+// A sequence whose rows are not inside [0, num_rows) is skipped whole; a row
+// whose position is negative or past the table, or whose block entry is
+// outside the pool, gets slot -1 and no write.
+constexpr int kChunkThreads = 256;
+
 template <typename Tr>
-__global__ __launch_bounds__(256) void append_chunk_kernel(AppendArgs a) {
-  constexpr int X = Tr::kChunk;
-  const int C = a.head_dim / X;
-  const int64_t per_row = int64_t(a.num_kv_heads) * C;
-  const int64_t total = int64_t(a.max_query_len) * a.B * per_row;
-  const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (idx >= total) return;
-  const int c = int(idx % C);
-  const int h = int((idx / C) % a.num_kv_heads);
-  const int64_t rb = idx / per_row;  // j * B + b: neighbouring threads share j
-  const int b = int(rb % a.B);
-  const int j = int(rb / a.B);
+__global__ __launch_bounds__(kChunkThreads) void append_chunk_kernel(AppendArgs a) {
+  using S = typename Tr::storage;
+  constexpr int X = Tr::kChunk;                 // elements per 16 bytes
+  constexpr int kMaxRowU4 = 128 * 4 / 16 + 1;   // a padded LDS row of the widest case
+  __shared__ uint4 sv[kBlockTokens][kMaxRowU4];
+
+  const int b = blockIdx.z, h = blockIdx.y;
   const int32_t q0 = a.query_start[b], q1 = a.query_start[b + 1];
-  if (q0 < 0 || q1 > a.num_rows || j >= q1 - q0) return;
-  const int64_t row = int64_t(q0) + j;
-  const int64_t src = (row * a.num_kv_heads + h) * a.head_dim + int64_t(c) * X;
-  const uint4 kc = source_chunk<Tr>(a.key, src, a.k_scale);
-  const uint4 vc = source_chunk<Tr>(a.value, src, a.v_scale);
-  const int64_t pos = int64_t(a.context_lens[b]) - (q1 - q0) + j;
-  int64_t slot = -1;
-  if (pos >= 0 && pos < int64_t(a.max_nb) * kBlockTokens) {
-    const int32_t blk = a.block_tables[int64_t(b) * a.max_nb + pos / kBlockTokens];
-    if (blk >= 0 && blk < a.num_blocks) slot = int64_t(blk) * kBlockTokens + pos % kBlockTokens;
+  if (q0 < 0 || q1 > a.num_rows || q1 <= q0) return;
+  const int n = q1 - q0;
+  const int nrows = min(n, a.max_query_len);
+  const int64_t pos0 = int64_t(a.context_lens[b]) - n;  // position of row 0
+  const int64_t cap = int64_t(a.max_nb) * kBlockTokens;
+  const int64_t p_lo = max(pos0, int64_t(0));
+  const int64_t p_hi = min(pos0 + nrows, cap);
+  // rows with no position in the table: slot -1 (one work-group reports them)
+  if (a.slot_mapping && blockIdx.x == 0 && h == 0) {
+    for (int j = threadIdx.x; j < nrows; j += blockDim.x) {
+      const int64_t pos = pos0 + j;
+      if (pos < 0 || pos >= cap) a.slot_mapping[int64_t(q0) + j] = -1;
+    }
   }
-  if (a.slot_mapping && h == 0 && c == 0) a.slot_mapping[row] = slot;
-  if (slot < 0) return;
-  const int64_t tile = (slot / kBlockTokens) * a.num_kv_heads + h;
-  write_token_chunk<Tr>(a.k_cache, a.v_cache, tile, C, a.head_dim, c, int(slot % kBlockTokens), kc,
-                        vc);
+  if (p_lo >= p_hi) return;
+  const int64_t kb = p_lo / kBlockTokens + blockIdx.x;
+  if (kb * kBlockTokens >= p_hi) return;
+  const int s_lo = int(max(p_lo, kb * kBlockTokens) - kb * kBlockTokens);  // slots [s_lo, s_hi)
+  const int s_hi = int(min(p_hi, kb * kBlockTokens + kBlockTokens) - kb * kBlockTokens);
+  const int32_t blk = a.block_tables[int64_t(b) * a.max_nb + kb];
+  const bool ok = blk >= 0 && blk < a.num_blocks;
+  // row of slot s: q0 + (kb*16 + s - pos0)
+  const int64_t row0 = int64_t(q0) + kb * kBlockTokens - pos0;
+  if (a.slot_mapping && h == 0) {
+    for (int s = s_lo + int(threadIdx.x); s < s_hi; s += blockDim.x)
+      a.slot_mapping[row0 + s] = ok ? int64_t(blk) * kBlockTokens + s : -1;
+  }
+  if (!ok) return;
+
+  const int D = a.head_dim;
+  const int C = D / X;                       // 16-byte chunks per row
+  const int64_t tile = int64_t(blk) * a.num_kv_heads + h;
+  S* kt = static_cast<S*>(a.k_cache) + tile * int64_t(kBlockTokens) * D;
+  S* vt = static_cast<S*>(a.v_cache) + tile * int64_t(kBlockTokens) * D;
+
+  // K straight to the tile; V chunks into LDS
+  for (int idx = threadIdx.x; idx < C * kBlockTokens; idx += blockDim.x) {
+    const int c = idx / kBlockTokens, s = idx % kBlockTokens;
+    if (s < s_lo || s >= s_hi) continue;
+    const int64_t src = ((row0 + s) * a.num_kv_heads + h) * D + int64_t(c) * X;
+    const uint4 kc = source_chunk<Tr>(a.key, src, a.k_scale);
+    const u32x4_t ku = {kc.x, kc.y, kc.z, kc.w};
+    __builtin_nontemporal_store(ku, reinterpret_cast<u32x4_t*>(kt + (int64_t(c) * kBlockTokens + s) * X));
+    sv[s][c] = source_chunk<Tr>(a.value, src, a.v_scale);
+  }
+  __syncthreads();
+
+  // V rows: dim x, piece pc of X slots (16 bytes); elements move as integers
+  using U = std::conditional_t<sizeof(S) == 4, uint32_t,
+                               std::conditional_t<sizeof(S) == 2, uint16_t, uint8_t>>;
+  constexpr int kPieces = kBlockTokens / X;
+  const U* lds = reinterpret_cast<const U*>(&sv[0][0]);
+  const int row_elems = kMaxRowU4 * X;       // LDS row stride in elements
+  const bool full = s_lo == 0 && s_hi == kBlockTokens;
+  for (int idx = threadIdx.x; idx < D * kPieces; idx += blockDim.x) {
+    const int x = idx / kPieces, pc = idx % kPieces;
+    const int f = pc * X;                    // first slot of the piece
+    if (f + X <= s_lo || f >= s_hi) continue;
+    u32x4_t* dst = reinterpret_cast<u32x4_t*>(vt + int64_t(x) * kBlockTokens + f);
+    U e[X];
+    if (!full && (f < s_lo || f + X > s_hi)) {
+      const u32x4_t old = *dst;              // slots the rows do not cover stay as they are
+      __builtin_memcpy(e, &old, sizeof(old));
+    }
+#pragma unroll
+    for (int k = 0; k < X; ++k)
+      if (f + k >= s_lo && f + k < s_hi) e[k] = lds[(f + k) * row_elems + x];
+    u32x4_t v;
+    __builtin_memcpy(&v, e, sizeof(v));
+    __builtin_nontemporal_store(v, dst);
+  }
 }
 
 hipError_t launch_slot_mapping(const SlotMappingArgs& a, hipStream_t s) {
@@ -251,14 +314,21 @@ static void (*append_kernel_for(bool chunk))(AppendArgs) {
 
 hipError_t launch_append(const AppendArgs& a, Kind kind, hipStream_t s) {
   const bool chunk = a.query_start != nullptr;
-  const int64_t rows = chunk ? int64_t(a.max_query_len) * a.B : a.B;
-  const int64_t total = rows * a.num_kv_heads * (a.head_dim / chunk_elems(kind));
-  if (total == 0) return hipSuccess;
-  const int threads = 256;
-  const unsigned blocks = unsigned((total + threads - 1) / threads);
   void (*kern)(AppendArgs) = kind == Kind::kBf16  ? append_kernel_for<Bf16>(chunk)
                              : kind == Kind::kFp8 ? append_kernel_for<Fp8>(chunk)
                                                   : append_kernel_for<F32>(chunk);
+  if (chunk) {
+    // blocks the rows of one sequence may touch: ceil(max_query_len / 16) + 1
+    if (a.B == 0 || a.max_query_len == 0) return hipSuccess;
+    const int64_t nbk = (int64_t(a.max_query_len) + kBlockTokens - 1) / kBlockTokens + 1;
+    hipLaunchKernelGGL(kern, dim3(unsigned(nbk), unsigned(a.num_kv_heads), unsigned(a.B)),
+                       dim3(kChunkThreads), 0, s, a);
+    return hipGetLastError();
+  }
+  const int64_t total = int64_t(a.B) * a.num_kv_heads * (a.head_dim / chunk_elems(kind));
+  if (total == 0) return hipSuccess;
+  const int threads = 256;
+  const unsigned blocks = unsigned((total + threads - 1) / threads);
   hipLaunchKernelGGL(kern, dim3(blocks), dim3(threads), 0, s, a);
   return hipGetLastError();
 }

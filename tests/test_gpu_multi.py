@@ -216,3 +216,41 @@ def test_full_size_draft_verification(config, K, kv_dtype):
     seqs = sorted({int(ctx.argmin()), int(ctx.argmax()),
                    *rng.choice(w.B, size=10, replace=False).tolist()})
     multi_case(w, f"config{config}-K{K}-{w.kv_dtype}", seqs=seqs)
+
+
+@pytest.mark.parametrize("kv", ["f32", "bf16", "fp8"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_chunk_write_alone_is_bit_exact(kv, d):
+    """kv_cache_append_chunk for every pool dtype: chunks that start and end
+    inside blocks, fill whole blocks, cross several, a first chunk, one row, a
+    sequence with no row, one with more rows than context (its first rows get
+    slot -1) and one with more rows than max_query_len (rows past it are not
+    written).  Slots and both pools equal the oracle's bit for bit; the slots
+    the chunk does not cover keep their bits (NaN payloads included)."""
+    ctx = [40, 16, 100, 7, 33, 5, 60]
+    n = [13, 16, 70, 1, 0, 9, 44]
+    act = "f32" if kv == "f32" else "bf16"
+    w = W.multi_token_workload("cw", act, len(ctx), 8, 2, d, ctx, n, seed=61 + d, kv_dtype=kv,
+                               k_scale=0.5 if kv == "fp8" else 1.0,
+                               v_scale=1.5 if kv == "fp8" else 1.0)
+    m = w.multi
+    mq = 40                                   # sequences 2 (70 rows) and 6 (44) exceed it
+    kp0, vp0 = poison(w, np.zeros(w.B, dtype=np.int64))   # every slot NaN before the write
+    dw = upload(w, kp0, vp0)
+    log(f"[gpu] chunk write {kv} d={d}")
+    T = int(m.query_start[-1])
+    slots = torch.full((T,), -7, dtype=torch.int64, device="cuda")
+    P.kv_cache_append_chunk(dw.pool, to_dev(m.new_k), to_dev(m.new_v),
+                            torch.from_numpy(m.query_start).cuda(), mq, dw.tables,
+                            torch.from_numpy(m.context_lens).cuda(), slots)
+    torch.cuda.synchronize()
+    want = O.chunk_slots(w.block_tables, m.context_lens, m.query_start)
+    for b in range(w.B):                      # rows at or past max_query_len: untouched
+        for j in range(mq, int(m.query_start[b + 1] - m.query_start[b])):
+            want[m.query_start[b] + j] = -7
+    np.testing.assert_array_equal(slots.cpu().numpy(), want)
+    written = np.where(want >= 0, want, -1)
+    kp, vp = O.reshape_and_cache(kp0, vp0, m.new_k, m.new_v, written, w.H_kv, w.d, kv,
+                                 w.num_blocks, w.k_scale, w.v_scale)
+    assert np.array_equal(from_dev(dw.pool.k_cache, kv), kp)
+    assert np.array_equal(from_dev(dw.pool.v_cache, kv), vp)
