@@ -66,6 +66,21 @@ __device__ __forceinline__ void load_block(MfmaFrag<E, D>& f, const typename E::
   }
 }
 
+// load_block from a copy of the two tiles in LDS (same layouts).
+template <typename E, int D>
+__device__ __forceinline__ void load_block_lds(MfmaFrag<E, D>& f, const typename E::storage* kt,
+                                               const typename E::storage* vt, int lane) {
+  constexpr int X = E::kChunk;
+#pragma unroll
+  for (int i = 0; i < MfmaFrag<E, D>::KL; ++i)
+    f.k[i] = *reinterpret_cast<const uint4*>(kt + (i * kWave + lane) * X);
+  const int n = lane & 15, q = lane >> 4;
+#pragma unroll
+  for (int mc = 0; mc < MfmaShape<D>::MC; ++mc)
+    f.v[mc] = *reinterpret_cast<const typename MfmaFrag<E, D>::VPiece*>(
+        vt + (16 * mc + n) * kBlockTokens + 4 * q);
+}
+
 // Operand i of S = K Q^T and operand mc of O^T = V^T P^T, as bf16.
 template <typename E, int D>
 __device__ __forceinline__ bf16x8_t k_operand(const MfmaFrag<E, D>& f, int i) {

@@ -254,3 +254,34 @@ def test_chunk_write_alone_is_bit_exact(kv, d):
                                  w.num_blocks, w.k_scale, w.v_scale)
     assert np.array_equal(from_dev(dw.pool.k_cache, kv), kp)
     assert np.array_equal(from_dev(dw.pool.v_cache, kv), vp)
+
+
+def test_long_chunk_kernel_contains_bad_inputs():
+    """The same containment for the long-chunk kernel (g * max_query_len of 320
+    columns, ten column sets): n > ctx, n > max_query_len and ctx > max_nb*16
+    give NaN rows below max_query_len, a bad table entry in block 0 gives NaN
+    rows, the good sequence is unaffected."""
+    H, H_kv, d = 32, 4, 128
+    ctx = [300, 10, 200, 120, 400]
+    n = [40, 30, 45, 33, 20]
+    w = W.multi_token_workload("badc", "bf16", len(ctx), H, H_kv, d, ctx, n, seed=78, max_nb=25)
+    m = w.multi
+    w.block_tables[3, 0] = w.num_blocks + 3
+    ctx_dev = m.context_lens.copy()
+    ctx_dev[4] = 25 * 16 + 1
+    dw = upload(w, w.k_pool, w.v_pool)
+    qs = m.query_start
+    T = int(qs[-1])
+    log("[gpu] long-chunk bad-input containment")
+    m2 = W.MultiStep(context_lens=ctx_dev, query_start=qs, q=m.q, new_k=m.new_k, new_v=m.new_v)
+    _, out = _gpu_multi(dw, m2, max_query_len=40, write=False, out_fill=SENT16)
+    torch.cuda.synchronize()
+    got = from_dev(out, "bf16").reshape(T, H, d)
+    rows = lambda b: slice(int(qs[b]), int(qs[b + 1]))
+    assert np.all(np.isnan(O.bits_to_f64(got[rows(1)], "bf16")))          # n > ctx
+    assert np.all(np.isnan(O.bits_to_f64(got[rows(2)][:40], "bf16")))     # n > max_query_len
+    assert np.all(got[rows(2)][40:] == SENT16)
+    assert np.all(np.isnan(O.bits_to_f64(got[rows(3)], "bf16")))          # bad entry, block 0
+    assert np.all(np.isnan(O.bits_to_f64(got[rows(4)], "bf16")))          # ctx > max_nb * 16
+    ref = _ref_rows(w, w.k_pool, w.v_pool, seqs=[0])
+    assert_rows_close(got, ref, "good sequence next to bad ones")
