@@ -31,7 +31,6 @@ against the 8 TB/s HBM3E peak.
 from __future__ import annotations
 
 import argparse
-import glob
 import hashlib
 import json
 import math
@@ -94,11 +93,25 @@ def parse_args(argv=None):
     return ap.parse_args(argv)
 
 
-def kernel_source_hash() -> str:
+# Sources each timed kernel is compiled from (its own file and the headers it
+# includes); a counter summary stays valid while these hash the same.
+KERNEL_SOURCES = {
+    "decode_valu": ["decode_valu.hip", "device_common.h", "launch.h", "work_list.h"],
+    "decode_mfma": ["decode_mfma.hip", "mfma_tile.h", "device_common.h", "launch.h",
+                    "work_list.h"],
+    "multi_mfma": ["multi_mfma.hip", "mfma_tile.h", "device_common.h", "launch.h",
+                   "work_list.h"],
+}
+
+
+def kernel_source_hash(kernel: str = "") -> str:
+    """SHA-256 over the sources of `kernel` (all kernel sources if empty)."""
+    csrc = os.path.join(ROOT, "paged_kv_cache_33_amd", "csrc")
+    names = KERNEL_SOURCES.get(kernel) or sorted(os.listdir(csrc))
     h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(ROOT, "paged_kv_cache_33_amd", "csrc", "*"))):
-        with open(p, "rb") as f:
-            h.update(os.path.basename(p).encode() + b"\0" + f.read())
+    for name in sorted(names):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()
 
 
@@ -129,7 +142,7 @@ def traffic_from_profile(kernel: str, workload: str):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("source_sha256") != kernel_source_hash():
+    if rec.get("source_sha256") != kernel_source_hash(kernel):
         return None
     return float(rec["hbm_bytes_per_dispatch"])
 
