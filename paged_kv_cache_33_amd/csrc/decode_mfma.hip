@@ -18,12 +18,19 @@
 namespace pagedkv {
 namespace {
 
-// Waves per work-group.  Single pass: 4, so that three work-groups share a CU
-// (168 VGPRs leave room for 3 waves per SIMD) and a finishing work-group's
-// successor fetches its first blocks while two others stream.  Split: 8, as its
-// work-list loop does not fit 3 waves per SIMD without spilling.
-template <bool kSplit>
-constexpr int kWavesOf = kSplit ? 8 : 4;
+// Waves per work-group and work-groups per CU.  Single pass: 4 waves, three
+// work-groups per CU (168 VGPRs leave room for 3 waves per SIMD), so a
+// finishing work-group's successor fetches its first blocks while two others
+// stream.  Split, bf16: 8 waves, one work-group per CU (its work-list loop
+// does not fit 3 waves per SIMD without spilling).  Split, fp8: 4 waves, two
+// per CU; a 512-token item is half the bytes there, so the start of each item
+// (length, table and first tile loads in a row) weighs twice as much, and a
+// second work-group streaming meanwhile hides it (measured on the long-context
+// mix: 104 -> 86 us; bf16 is 1% slower that way).
+template <typename E, bool kSplit>
+constexpr int kWavesOf = kSplit && E::kKind != Kind::kFp8 ? 8 : 4;
+template <typename E, bool kSplit>
+constexpr int kGroupsPerCu = !kSplit ? 3 : E::kKind == Kind::kFp8 ? 2 : 1;
 // One work item: partition `part` of sequence b, head tile `tile_y` (a KV
 // head and a group of up to 16 of its query heads).
 template <typename E, int D, int kWaves>
@@ -219,9 +226,9 @@ __device__ __forceinline__ void mfma_item(const DecodeArgs& a, const int part, c
 // true): grid (resident workers, head tiles, 1) walking the work list.  Two instantiations keep each one's
 // register allocation that of a single inlined item.
 template <typename E, int D, bool kSplit>
-__global__ __launch_bounds__(kWavesOf<kSplit> * kWave, kSplit ? 1 : 3) void decode_mfma_kernel(
-    DecodeArgs a) {
-  constexpr int kWaves = kWavesOf<kSplit>;
+__global__ __launch_bounds__((kWavesOf<E, kSplit> * kWave),
+                             (kGroupsPerCu<E, kSplit>)) void decode_mfma_kernel(DecodeArgs a) {
+  constexpr int kWaves = kWavesOf<E, kSplit>;
   if constexpr (!kSplit) {
     __shared__ int sm_order[kOrderBuckets + kWaves + 1];
     const int b = a.B <= kMaxOrderedSeqs
@@ -259,7 +266,9 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, Kind kind, int head_dim, hipS
   if (!kern) return hipErrorInvalidValue;
   const int g = a.H / a.num_kv_heads;
   const int tiles = a.num_kv_heads * ((g + kHeadsPerTile - 1) / kHeadsPerTile);
-  const dim3 block((split ? kWavesOf<true> : kWavesOf<false>) * kWave);
+  const int waves = kind == Kind::kFp8 ? (split ? kWavesOf<Fp8, true> : kWavesOf<Fp8, false>)
+                                       : (split ? kWavesOf<Bf16, true> : kWavesOf<Bf16, false>);
+  const dim3 block(waves * kWave);
   dim3 grid(1, tiles, a.B);
   if (a.partition_size > 0) {
     const int64_t most = int64_t(a.B) * a.num_partitions;
