@@ -27,6 +27,9 @@ Pages cited (titles as the pages give them):
          W tokens) and Q4 (sliding-window attention: the first K tile a query
          at position q_pos needs starts at q_pos + 1 - W, rounded down to the
          tile; tiles wholly before it are skipped).
+  [QA8]  same Q&A page, Q3 item 1 (quantise the KV cache to INT8 with one
+         scale per token, the row's largest magnitude over 127; dequantise
+         before the softmax).
 
 What the oracle computes is the plain definition: decode attention over a
 paged cache equals ordinary softmax attention of one query over its
@@ -58,6 +61,14 @@ Readings taken where the pages are silent (each listed in the design notes):
     float32, ties to the even code; magnitudes beyond 448 (the largest finite
     E4M3 value; the format has no infinities) store +-448, and NaN stores
     sign | 0x7F.  Queries and outputs stay bf16.
+  * int8 cache ([QA8]): one scale per (token, KV head) row of K and of V, in
+    float32: s = a / 127 with a the row's largest finite magnitude (0 for a
+    row with none); element code = the integer nearest x / s (float32
+    division), ties to even, clamped to +-127; a non-finite element, or any
+    element of a row with s = 0, stores code 0.  A cached value is code * s.
+    Each cache buffer holds the codes (the fp8 layout: 16 codes per chunk)
+    followed by the scales, scale (p, h, t) at byte
+    codes_bytes + 4 * ((p * H_kv + h) * 16 + t).
 
 Parity status: every function below is pinned by tests/test_oracle_pins.py
 against printed page values, closed forms, library routines or invariants.
@@ -83,6 +94,12 @@ __all__ = [
     "blocks_needed",
     "slot_mapping",
     "window_first",
+    "INT8_MAX",
+    "int8_quantize_rows",
+    "int8_codes_bytes",
+    "int8_scale_offset",
+    "int8_read_scales",
+    "int8_write_scales",
     "chunk_slots",
     "reshape_and_cache",
     "gather_sequence",
@@ -119,18 +136,21 @@ def bits_to_f64(bits: np.ndarray, dtype: str) -> np.ndarray:
             return bits.astype(np.uint32).view(np.float32).astype(np.float64)
     if dtype == "fp8":
         return e4m3_value(bits)
+    if dtype == "int8":
+        return np.asarray(bits).astype(np.uint8).view(np.int8).astype(np.float64)
     raise ValueError(dtype)
 
 
 def act_dtype(dtype: str) -> str:
     """Element type of query, output and the rows handed to the cache write
-    for a cache of element type `dtype` (an fp8 cache serves bf16 activations)."""
-    return "bf16" if dtype == "fp8" else dtype
+    for a cache of element type `dtype` (fp8 and int8 caches serve bf16
+    activations)."""
+    return "bf16" if dtype in ("fp8", "int8") else dtype
 
 
 def chunk_elems(dtype: str) -> int:
     """Elements per 16-byte chunk of the K layout."""
-    return {"bf16": 8, "f32": 4, "fp8": 16}[dtype]
+    return {"bf16": 8, "f32": 4, "fp8": 16, "int8": 16}[dtype]
 
 
 # --------------------------------------------------------------------------
@@ -183,6 +203,55 @@ def e4m3_quantize(bits: np.ndarray, dtype: str, scale: float) -> np.ndarray:
     with np.errstate(invalid="ignore", divide="ignore", over="ignore"):
         q = x / np.float32(scale)
     return e4m3_encode(q)
+
+
+# --------------------------------------------------------------------------
+# int8 cache elements with per-token scales, [QA8]
+# --------------------------------------------------------------------------
+INT8_MAX = 127
+
+
+def int8_quantize_rows(bits: np.ndarray, dtype: str):
+    """Codes (uint8 bytes of int8 values) and float32 scales of rows [..., d]
+    of activation values (bit patterns of `dtype`): per row, s = a / 127 with a
+    the largest finite |x| (0 if none), code = round-half-even(x / s) clamped
+    to +-127, both divisions in float32; code 0 where x is not finite or s = 0."""
+    x = bits_to_f64(bits, dtype).astype(np.float32)          # exact: bf16/f32 values
+    finite = np.isfinite(x)
+    a = np.max(np.where(finite, np.abs(x), np.float32(0)), axis=-1)
+    s = (a / np.float32(INT8_MAX)).astype(np.float32)
+    with np.errstate(invalid="ignore", divide="ignore", over="ignore"):
+        q = (x / s[..., None]).astype(np.float32)
+    ok = finite & (s[..., None] > 0)
+    code = np.where(ok, np.clip(np.rint(np.where(ok, q, 0)), -INT8_MAX, INT8_MAX), 0)
+    return code.astype(np.int8).view(np.uint8), s
+
+
+def int8_codes_bytes(pool_len: int, d: int) -> int:
+    """Bytes of the code region of an int8 cache buffer of pool_len bytes:
+    each (block, head, slot) row holds d codes and one 4-byte scale."""
+    return pool_len // (d + 4) * d
+
+
+def int8_scale_offset(p, h, t, H_kv: int, d: int, pool_len: int):
+    """Byte offset of the scale of row (block p, kv head h, slot t)."""
+    p = np.asarray(p, dtype=np.int64)
+    return int8_codes_bytes(pool_len, d) + 4 * ((p * H_kv + h) * BLOCK + np.asarray(t))
+
+
+def int8_read_scales(pool: np.ndarray, offsets) -> np.ndarray:
+    """float32 scales stored at byte offsets (little-endian)."""
+    offsets = np.asarray(offsets, dtype=np.int64)
+    raw = np.stack([pool[offsets + k] for k in range(4)], axis=-1).astype(np.uint8)
+    return raw.reshape(-1).view(np.float32).reshape(offsets.shape)
+
+
+def int8_write_scales(pool: np.ndarray, offsets, scales) -> None:
+    """Store float32 scales at byte offsets (in place)."""
+    offsets = np.asarray(offsets, dtype=np.int64).reshape(-1)
+    raw = np.asarray(scales, dtype=np.float32).reshape(-1).view(np.uint8).reshape(-1, 4)
+    for k in range(4):
+        pool[offsets + k] = raw[:, k]
 
 
 # --------------------------------------------------------------------------
@@ -271,9 +340,13 @@ def reshape_and_cache(k_pool: np.ndarray, v_pool: np.ndarray, key: np.ndarray,
     v_pool = np.array(v_pool, copy=True)
     key = np.asarray(key).reshape(-1, H_kv, d)
     value = np.asarray(value).reshape(-1, H_kv, d)
+    ks = vs = None
     if dtype == "fp8":
         key = e4m3_quantize(key, act_dtype(dtype), k_scale)
         value = e4m3_quantize(value, act_dtype(dtype), v_scale)
+    elif dtype == "int8":
+        key, ks = int8_quantize_rows(key, act_dtype(dtype))
+        value, vs = int8_quantize_rows(value, act_dtype(dtype))
     slots = np.asarray(slots, dtype=np.int64)
     live = [int(s) for s in slots if s >= 0]
     if len(set(live)) != len(live):
@@ -289,6 +362,11 @@ def reshape_and_cache(k_pool: np.ndarray, v_pool: np.ndarray, key: np.ndarray,
             xs = np.arange(d)
             k_pool[k_offset(blk, h, off, xs, H_kv, d, dtype)] = key[i, h]
             v_pool[v_offset(blk, h, off, xs, H_kv, d, dtype)] = value[i, h]
+            if dtype == "int8":
+                int8_write_scales(k_pool, [int8_scale_offset(blk, h, off, H_kv, d, len(k_pool))],
+                                  [ks[i, h]])
+                int8_write_scales(v_pool, [int8_scale_offset(blk, h, off, H_kv, d, len(v_pool))],
+                                  [vs[i, h]])
     return k_pool, v_pool
 
 
@@ -317,6 +395,11 @@ def gather_sequence(k_pool: np.ndarray, v_pool: np.ndarray, table_row: np.ndarra
     if dtype == "fp8":
         K = K * float(np.float32(k_scale))
         V = V * float(np.float32(v_scale))
+    elif dtype == "int8":                    # [QA8]: code * the row's scale (exact in f64)
+        K = K * int8_read_scales(k_pool, int8_scale_offset(blocks, kvh, t % BLOCK, H_kv, d,
+                                                           len(k_pool))).astype(np.float64)[:, None]
+        V = V * int8_read_scales(v_pool, int8_scale_offset(blocks, kvh, t % BLOCK, H_kv, d,
+                                                           len(v_pool))).astype(np.float64)[:, None]
     return K, V
 
 

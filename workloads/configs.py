@@ -37,7 +37,7 @@ def bits_dtype(dtype: str):
         return np.uint16
     if dtype == "f32":
         return np.uint32
-    if dtype == "fp8":
+    if dtype in ("fp8", "int8"):
         return np.uint8
     raise ValueError(f"unsupported dtype {dtype!r}")
 
@@ -74,6 +74,8 @@ POOL_CHUNK = 1 << 22  # elements per independently keyed stream of a pool fill
 
 
 FP8_MAG_CODES = 0x40  # fp8 pool bytes: magnitude codes 0x00..0x3F
+INT8_CODE_SD = 40.0   # int8 pool codes: rint(40 N(0,1)) clipped to +-127
+INT8_SCALE_RANGE = (0.02, 0.03)  # int8 pool row scales: uniform on this range
 
 
 def _pool_bits(seed: int, tag: int, n: int, dtype: str, threads: int = 0) -> np.ndarray:
@@ -82,6 +84,8 @@ def _pool_bits(seed: int, tag: int, n: int, dtype: str, threads: int = 0) -> np.
     bf16 / f32: N(0,1) values.  fp8: bytes with a random sign bit and a
     magnitude code drawn uniformly from 0x00..0x3F (in the E4M3 format those
     are the values 0 to 1.875, spaced logarithmically; no NaN code is drawn).
+    int8: codes rint(40 N(0,1)) clipped to +-127 (the row scales come from
+    kv_pool, which appends them).
     Chunk i comes from its own PCG64 stream keyed by SeedSequence([seed, tag, i]),
     so the values do not depend on how many threads fill them.
     """
@@ -92,6 +96,10 @@ def _pool_bits(seed: int, tag: int, n: int, dtype: str, threads: int = 0) -> np.
         lo = i * POOL_CHUNK
         m = min(POOL_CHUNK, n - lo)
         rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, tag, i])))
+        if dtype == "int8":
+            g = rng.standard_normal(m, dtype=np.float32) * np.float32(INT8_CODE_SD)
+            out[lo:lo + m] = np.clip(np.rint(g), -127, 127).astype(np.int8).view(np.uint8)
+            return
         if dtype == "fp8":
             r = rng.integers(0, 2 * FP8_MAG_CODES, size=m, dtype=np.uint8)
             out[lo:lo + m] = (r & np.uint8(FP8_MAG_CODES - 1)) | ((r & np.uint8(FP8_MAG_CODES)) << np.uint8(1))
@@ -107,6 +115,20 @@ def _pool_bits(seed: int, tag: int, n: int, dtype: str, threads: int = 0) -> np.
         with ThreadPoolExecutor(max_workers=threads) as ex:
             list(ex.map(fill, range(nchunks)))
     return out
+
+
+def kv_pool(seed: int, tag: int, num_blocks: int, H_kv: int, d: int, dtype: str) -> np.ndarray:
+    """One cache buffer of a pool: num_blocks*H_kv*16*d elements; an int8 cache
+    also holds one float32 scale per (block, head, slot) row after its codes,
+    drawn uniformly from INT8_SCALE_RANGE (so values code * scale are near
+    N(0,1))."""
+    n = num_blocks * H_kv * BLOCK_SIZE * d
+    codes = _pool_bits(seed, tag, n, dtype)
+    if dtype != "int8":
+        return codes
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, tag, 1 << 30])))
+    scales = rng.uniform(*INT8_SCALE_RANGE, size=num_blocks * H_kv * BLOCK_SIZE).astype(np.float32)
+    return np.concatenate([codes, scales.view(np.uint8)])
 
 
 @dataclass
@@ -168,7 +190,13 @@ class Workload:
 
     @property
     def kv_elem_bytes(self) -> int:
-        return 1 if self.kv_dtype == "fp8" else self.elem_bytes
+        return 1 if self.kv_dtype in ("fp8", "int8") else self.elem_bytes
+
+    @property
+    def kv_row_extra_bytes(self) -> int:
+        """Bytes stored per cached (token, KV head) row besides its elements:
+        an int8 cache's float32 row scale."""
+        return 4 if self.kv_dtype == "int8" else 0
 
     @property
     def group(self) -> int:
@@ -218,10 +246,9 @@ def scattered_workload(name: str, dtype: str, B: int, H: int, H_kv: int, d: int,
         tables[b, :nb[b]] = perm[pos:pos + nb[b]]
         pos += nb[b]
     q = _normal_bits(rng, B * H * d, dtype).reshape(B, H, d)
-    n_pool = num_blocks * H_kv * BLOCK_SIZE * d
     kv_dtype = kv_dtype or dtype
-    k_pool = _pool_bits(seed, 1, n_pool, kv_dtype)
-    v_pool = _pool_bits(seed, 2, n_pool, kv_dtype)
+    k_pool = kv_pool(seed, 1, num_blocks, H_kv, d, kv_dtype)
+    v_pool = kv_pool(seed, 2, num_blocks, H_kv, d, kv_dtype)
     new_k = _normal_bits(rng, B * H_kv * d, dtype).reshape(B, H_kv, d)
     new_v = _normal_bits(rng, B * H_kv * d, dtype).reshape(B, H_kv, d)
     step = DecodeStep(context_lens=ctx.astype(np.int32), q=q, new_k=new_k, new_v=new_v)
@@ -264,9 +291,9 @@ def multi_token_workload(name: str, dtype: str, B: int, H: int, H_kv: int, d: in
 
 
 def _name(config: int, kv_dtype: str) -> str:
-    """Workload name; an fp8-cache variant of a bf16 workload says so."""
+    """Workload name; an fp8- or int8-cache variant of a bf16 workload says so."""
     base = CONFIG_NAMES[config]
-    return base if kv_dtype != "fp8" else base.replace("-bf16", "") + "-fp8kv"
+    return base if kv_dtype not in ("fp8", "int8") else base.replace("-bf16", "") + f"-{kv_dtype}kv"
 
 
 def _config1(seed: int) -> Workload:
@@ -345,10 +372,9 @@ def shared_prefix_workload(seed: int, B: int = 128, H: int = 32, H_kv: int = 8,
             ctx_s[b] = pos + 1
         ctx_per_step.append(ctx_s)
     dtype = "bf16"
-    n_pool = num_blocks * H_kv * BLOCK_SIZE * d
     qs = [_normal_bits(rng, B * H * d, dtype).reshape(B, H, d) for _ in range(steps)]
-    k_pool = _pool_bits(seed, 1, n_pool, kv_dtype)
-    v_pool = _pool_bits(seed, 2, n_pool, kv_dtype)
+    k_pool = kv_pool(seed, 1, num_blocks, H_kv, d, kv_dtype)
+    v_pool = kv_pool(seed, 2, num_blocks, H_kv, d, kv_dtype)
     step_list = []
     for s in range(steps):
         nk = _normal_bits(rng, B * H_kv * d, dtype).reshape(B, H_kv, d)
@@ -363,18 +389,19 @@ def shared_prefix_workload(seed: int, B: int = 128, H: int = 32, H_kv: int = 8,
 def make_workload(config: int, seed: Optional[int] = None, kv_dtype: str = "") -> Workload:
     """Build workload `config` (1..5) with its default seed (= config number).
 
-    kv_dtype "fp8" gives the same shapes, lengths, tables and activations with an
-    fp8 cache (configs 2..5; its pool bytes follow the fp8 recipe of _pool_bits,
-    scales 1.0).
+    kv_dtype "fp8" / "int8" gives the same shapes, lengths, tables and
+    activations with an fp8 cache (per-tensor scales 1.0) or an int8 cache (per
+    row scales) (configs 2..5; pool bytes follow the recipes of _pool_bits and
+    kv_pool).
     """
     seed = config if seed is None else seed
-    if kv_dtype and kv_dtype not in ("fp8", "bf16", "f32"):
+    if kv_dtype and kv_dtype not in ("fp8", "int8", "bf16", "f32"):
         raise ValueError(f"unsupported kv_dtype {kv_dtype!r}")
     if config == 1:
-        if kv_dtype == "fp8":
-            raise ValueError("workload 1 is float32; an fp8 cache serves bf16 activations")
+        if kv_dtype in ("fp8", "int8"):
+            raise ValueError("workload 1 is float32; fp8 and int8 caches serve bf16 activations")
         return _config1(seed)
-    kv = "fp8" if kv_dtype == "fp8" else "bf16"
+    kv = kv_dtype if kv_dtype in ("fp8", "int8") else "bf16"
     if config == 2:
         return _config2(seed, kv)
     if config == 3:
