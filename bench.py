@@ -59,9 +59,10 @@ def parse_args(argv=None):
     ap.add_argument("--config", type=int, default=2, help="workload 1..5 (default 2: the headline)")
     ap.add_argument("--partition", type=int, default=None,
                     help="split-KV partition size in tokens (0 = single pass)")
-    ap.add_argument("--kv-dtype", default="bf16", choices=["bf16", "fp8"],
-                    help="cache element type: bf16 (the workloads as configured) or fp8 "
-                         "(E4M3 codes, scales 1.0, bf16 activations)")
+    ap.add_argument("--kv-dtype", default="bf16", choices=["bf16", "fp8", "int8"],
+                    help="cache element type: bf16 (the workloads as configured), fp8 "
+                         "(E4M3 codes, scales 1.0) or int8 (codes with per-token row scales); "
+                         "activations stay bf16")
     ap.add_argument("--window", type=int, default=0,
                     help="sliding window in tokens (0 = whole context): each decode query "
                          "attends to its last W positions (paged_attention_decode_window)")
@@ -126,10 +127,10 @@ def step_bytes(w, step, window: int = 0) -> dict:
     first = np.maximum(ctx - window, 0) if window > 0 else np.zeros_like(ctx)
     nb = (ctx + 15) // 16 - first // 16
     ctx = ctx - first
-    kv = int(ctx.sum()) * w.H_kv * w.d * 2 * ec
+    kv = int(ctx.sum()) * w.H_kv * (w.d * ec + w.kv_row_extra_bytes) * 2
     qo = 2 * w.B * w.H * w.d * e
     decode = kv + qo + 4 * int(nb.sum()) + 4 * w.B
-    write = 2 * w.B * w.H_kv * w.d * (e + ec)              # K,V rows in, cache elements out
+    write = 2 * w.B * w.H_kv * (w.d * (e + ec) + w.kv_row_extra_bytes)  # rows in, cache out
     slots = 4 * w.B + 4 * w.B + 8 * w.B                    # lengths, table entries, slots out
     return {"decode": decode, "kv": kv, "step": decode + write + slots}
 

@@ -67,6 +67,18 @@
  * code with an even mantissa; magnitudes beyond 448 store +-448 and NaN stores
  * sign | 0x7F.  The decode converts codes to bf16 exactly and applies the
  * scales in fp32.
+ *
+ * int8 pools (KV_INT8; "MLSys Engineer - Inference Systems Q&A", Q3 item 1:
+ * INT8 with per-token scaling).  Each cached (token, KV head) row of K and of
+ * V has its own float32 scale s = a / 127, a the row's largest finite
+ * magnitude; element x is stored as the integer nearest x / s (the division
+ * in fp32), ties to even, clamped to +-127 (code 0 for a non-finite x or
+ * s = 0), and stands for code * s.  Codes use the fp8 layout (X = 16); each
+ * cache buffer continues, after its num_blocks*H_kv*16*d code bytes, with the
+ * scales: the scale of (block p, head h, slot t) is float number
+ * (p*H_kv + h)*16 + t of that region.  The desc's k_scale / v_scale are
+ * ignored.  kv_cache_append_chunk and paged_attention_multi refuse int8
+ * pools.
  */
 #ifndef PAGEDKV_H_
 #define PAGEDKV_H_
@@ -90,7 +102,8 @@ typedef enum {
 typedef enum {
   KV_F32 = 0,      /* fp32 cache, fp32 activations                          */
   KV_BF16 = 1,     /* bf16 cache, bf16 activations                          */
-  KV_FP8_E4M3 = 2  /* E4M3 cache codes with per-tensor scales, bf16 activations */
+  KV_FP8_E4M3 = 2, /* E4M3 cache codes with per-tensor scales, bf16 activations */
+  KV_INT8 = 3      /* int8 cache codes with per-token row scales, bf16 activations */
 } kv_dtype;
 
 typedef struct {
@@ -108,7 +121,8 @@ typedef struct kv_pool kv_pool; /* opaque host object; borrows the two caches */
 /* Bytes of ONE cache (K or V) for this geometry; 0 if the descriptor is
  * invalid.  The pool is num_blocks*H_kv*16*d elements (the KV-cache size
  * formula of the workbook's "The equations" with L = 1, per cache) of 4, 2 or
- * 1 byte. */
+ * 1 byte, plus 4 bytes per (block, head, slot) row for an int8 pool's row
+ * scales. */
 size_t kv_pool_bytes(const kv_pool_desc* desc);
 
 /* Wrap two caller-owned device buffers (each kv_pool_bytes(desc) bytes, 16-byte

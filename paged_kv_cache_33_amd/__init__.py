@@ -54,17 +54,19 @@ def _dtype_code(dtype) -> int:
         return _lib.KV_F32
     if dtype in ("fp8", "fp8_e4m3", torch.float8_e4m3fn, _lib.KV_FP8_E4M3):
         return _lib.KV_FP8_E4M3
+    if dtype in ("int8", torch.int8, _lib.KV_INT8):
+        return _lib.KV_INT8
     raise ValueError(f"unsupported dtype {dtype!r}")
 
 
 def _elem_size(code: int) -> int:
     """Bytes of one cache element."""
-    return {_lib.KV_BF16: 2, _lib.KV_F32: 4, _lib.KV_FP8_E4M3: 1}[code]
+    return {_lib.KV_BF16: 2, _lib.KV_F32: 4, _lib.KV_FP8_E4M3: 1, _lib.KV_INT8: 1}[code]
 
 
 def _act_code(code: int) -> int:
     """Element type of query, output and cache-write rows for a cache type."""
-    return _lib.KV_BF16 if code == _lib.KV_FP8_E4M3 else code
+    return _lib.KV_BF16 if code in (_lib.KV_FP8_E4M3, _lib.KV_INT8) else code
 
 
 def _stream_handle(stream) -> int:
@@ -104,7 +106,8 @@ class KVPool:
     """A K cache and a V cache in the documented block layout, owned by torch.
 
     dtype "fp8" holds E4M3 codes; k_scale / v_scale are its per-tensor scales
-    (ignored for bf16 / f32 pools)."""
+    (ignored for bf16 / f32 / int8 pools).  dtype "int8" holds int8 codes and,
+    after them in each buffer, one float32 scale per (block, head, slot) row."""
 
     def __init__(self, k_cache: torch.Tensor, v_cache: torch.Tensor, num_blocks: int,
                  num_kv_heads: int, head_dim: int, dtype, k_scale: float = 1.0,
@@ -134,8 +137,9 @@ class KVPool:
                  device="cuda", k_scale: float = 1.0, v_scale: float = 1.0) -> "KVPool":
         code = _dtype_code(dtype)
         tdt = {_lib.KV_BF16: torch.bfloat16, _lib.KV_F32: torch.float32,
-               _lib.KV_FP8_E4M3: torch.uint8}[code]
-        n = num_blocks * num_kv_heads * BLOCK_SIZE * head_dim
+               _lib.KV_FP8_E4M3: torch.uint8, _lib.KV_INT8: torch.uint8}[code]
+        # elements, plus an int8 pool's row scales (kv_pool_bytes counts both)
+        n = kv_pool_bytes(num_blocks, num_kv_heads, head_dim, dtype) // _elem_size(code)
         k = torch.empty(n, dtype=tdt, device=device)
         v = torch.empty(n, dtype=tdt, device=device)
         return cls(k, v, num_blocks, num_kv_heads, head_dim, dtype, k_scale, v_scale)

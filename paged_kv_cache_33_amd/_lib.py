@@ -18,6 +18,7 @@ KV_ERR_NO_BLOCKS = -5
 KV_F32 = 0
 KV_BF16 = 1
 KV_FP8_E4M3 = 2
+KV_INT8 = 3
 
 STATUS_NAMES = {
     KV_OK: "KV_OK",

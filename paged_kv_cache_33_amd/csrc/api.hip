@@ -83,10 +83,20 @@ kv_status hip_status(hipError_t e, const char* what) {
   return fail(KV_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-size_t elem_bytes(kv_dtype t) { return t == KV_FP8_E4M3 ? 1 : t == KV_BF16 ? 2 : 4; }
+size_t elem_bytes(kv_dtype t) {
+  return t == KV_FP8_E4M3 || t == KV_INT8 ? 1 : t == KV_BF16 ? 2 : 4;
+}
+
+// Bytes of the element (code) region of one cache buffer; an int8 buffer
+// continues with one float32 scale per (block, head, slot) row.
+int64_t codes_bytes(const kv_pool_desc& d) {
+  return int64_t(d.num_blocks) * d.num_kv_heads * 16 * d.head_dim * int64_t(elem_bytes(d.dtype));
+}
+int64_t scales_offset(const kv_pool_desc& d) { return d.dtype == KV_INT8 ? codes_bytes(d) : 0; }
 
 pagedkv::Kind kind_of(kv_dtype t) {
   return t == KV_FP8_E4M3 ? pagedkv::Kind::kFp8
+         : t == KV_INT8   ? pagedkv::Kind::kInt8
          : t == KV_BF16   ? pagedkv::Kind::kBf16
                           : pagedkv::Kind::kF32;
 }
@@ -98,9 +108,10 @@ constexpr int64_t kMaxPartitions = 8192;
 
 kv_status check_desc(const kv_pool_desc* d) {
   if (!d) return fail(KV_ERR_INVALID_ARG, "pool descriptor is NULL");
-  if (d->dtype != KV_F32 && d->dtype != KV_BF16 && d->dtype != KV_FP8_E4M3)
-    return fail(KV_ERR_UNSUPPORTED, "dtype %d is not supported (f32=0, bf16=1, fp8_e4m3=2)",
-                int(d->dtype));
+  if (d->dtype != KV_F32 && d->dtype != KV_BF16 && d->dtype != KV_FP8_E4M3 &&
+      d->dtype != KV_INT8)
+    return fail(KV_ERR_UNSUPPORTED,
+                "dtype %d is not supported (f32=0, bf16=1, fp8_e4m3=2, int8=3)", int(d->dtype));
   if (d->dtype == KV_FP8_E4M3 && (!positive_finite(d->k_scale) || !positive_finite(d->v_scale)))
     return fail(KV_ERR_INVALID_ARG, "fp8 pool scales must be finite and > 0 (k %g, v %g)",
                 double(d->k_scale), double(d->v_scale));
@@ -161,8 +172,9 @@ extern "C" {
 
 size_t kv_pool_bytes(const kv_pool_desc* desc) {
   if (check_desc(desc) != KV_OK) return 0;
-  return size_t(desc->num_blocks) * size_t(desc->num_kv_heads) * 16u * size_t(desc->head_dim) *
-         elem_bytes(desc->dtype);
+  const size_t rows = size_t(desc->num_blocks) * size_t(desc->num_kv_heads) * 16u;
+  return rows * size_t(desc->head_dim) * elem_bytes(desc->dtype) +
+         (desc->dtype == KV_INT8 ? rows * sizeof(float) : 0);
 }
 
 kv_status kv_pool_create(const kv_pool_desc* desc, void* k_cache, void* v_cache, kv_pool** out) {
@@ -205,7 +217,8 @@ kv_status reshape_and_cache(const kv_pool* pool, const void* key, const void* va
     return fail(KV_ERR_INVALID_ARG, "key and value must be 16-byte aligned");
   const kv_pool_desc& d = pool->desc;
   pagedkv::CacheWriteArgs a{pool->k_cache, pool->v_cache, d.num_blocks, d.num_kv_heads,
-                            d.head_dim, key, value, slot_mapping, N, d.k_scale, d.v_scale};
+                            d.head_dim, key,           value,           slot_mapping,
+                            N,           d.k_scale,     d.v_scale,       scales_offset(d)};
   return hip_status(pagedkv::launch_cache_write(a, kind_of(d.dtype),
                                                 static_cast<hipStream_t>(stream)),
                     "cache write launch");
@@ -220,7 +233,8 @@ size_t paged_attention_workspace_bytes(int32_t B, int32_t H, int32_t head_dim,
 
 int32_t kv_decode_kernel_kind(const kv_pool* pool, int32_t H) {
   if (!pool || H < 1 || H % pool->desc.num_kv_heads != 0) return -1;
-  const bool packed = pool->desc.dtype == KV_BF16 || pool->desc.dtype == KV_FP8_E4M3;
+  const bool packed = pool->desc.dtype == KV_BF16 || pool->desc.dtype == KV_FP8_E4M3 ||
+                      pool->desc.dtype == KV_INT8;
   return (packed && H > pool->desc.num_kv_heads) ? 1 : 0;
 }
 
@@ -280,6 +294,7 @@ kv_status decode_impl(const kv_pool* pool, void* out, const void* query,
   a.scale_log2 = scale * 1.4426950408889634f * (fp8 ? d.k_scale : 1.f);
   a.v_scale = fp8 ? d.v_scale : 1.f;
   a.window = window;
+  a.scales_offset = scales_offset(d);
   a.partition_size = partition_size;
   a.num_partitions = static_cast<int32_t>(P);
   a.ws_o = ws.o;
@@ -333,6 +348,7 @@ kv_status kv_cache_append(const kv_pool* pool, const void* key, const void* valu
   pagedkv::AppendArgs a{pool->k_cache, pool->v_cache, d.num_blocks, d.num_kv_heads, d.head_dim,
                         key,           value,          block_tables, max_nb,     context_lens,
                         B,             slot_mapping,   d.k_scale,    d.v_scale};
+  a.scales_offset = scales_offset(d);
   return hip_status(pagedkv::launch_append(a, kind_of(d.dtype), static_cast<hipStream_t>(stream)),
                     "append launch");
 }
@@ -353,6 +369,8 @@ kv_status kv_cache_append_chunk(const kv_pool* pool, const void* key, const void
   if (!aligned16(key) || !aligned16(value))
     return fail(KV_ERR_INVALID_ARG, "key and value must be 16-byte aligned");
   const kv_pool_desc& d = pool->desc;
+  if (d.dtype == KV_INT8)
+    return fail(KV_ERR_UNSUPPORTED, "kv_cache_append_chunk does not write int8 pools");
   pagedkv::AppendArgs a{};
   a.k_cache = pool->k_cache;
   a.v_cache = pool->v_cache;
@@ -439,10 +457,15 @@ kv_status kv_copy_blocks(const kv_pool* pool, const int32_t* src, const int32_t*
   if (n == 0) return ok();
   if (!src || !dst) return fail(KV_ERR_INVALID_ARG, "src and dst must be non-NULL");
   const kv_pool_desc& d = pool->desc;
-  pagedkv::CopyBlocksArgs a{pool->k_cache, pool->v_cache, d.num_blocks,
-                            int64_t(d.num_kv_heads) * 16 * d.head_dim *
-                                int64_t(elem_bytes(d.dtype)),
-                            src, dst, n};
+  pagedkv::CopyBlocksArgs a{pool->k_cache,
+                            pool->v_cache,
+                            d.num_blocks,
+                            int64_t(d.num_kv_heads) * 16 * d.head_dim * int64_t(elem_bytes(d.dtype)),
+                            scales_offset(d),
+                            d.dtype == KV_INT8 ? d.num_kv_heads * 16 * int32_t(sizeof(float)) : 0,
+                            src,
+                            dst,
+                            n};
   return hip_status(pagedkv::launch_copy_blocks(a, static_cast<hipStream_t>(stream)),
                     "copy_blocks launch");
 }

@@ -78,6 +78,66 @@ __device__ __forceinline__ uint4 source_chunk(const void* base, int64_t src, flo
   }
 }
 
+// Chunk c (16 values) of a source row as int8 codes; s receives the row's
+// scale, its largest finite magnitude / 127 ("MLSys Engineer - Inference
+// Systems Q&A", Q3 item 1).  The C threads of one row are C consecutive lanes
+// (C a power of two dividing 64) and all of them call this: the row maximum
+// is combined across them with lane shuffles.
+__device__ __forceinline__ uint4 int8_chunk(const void* base, int64_t src, int C, float& s) {
+  const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + src);
+  const uint4 lo = p[0], hi = p[1];
+  const uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+  float x[16];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    x[2 * k] = bf16_lo(w[k]);
+    x[2 * k + 1] = bf16_hi(w[k]);
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int k = 0; k < 16; ++k)
+    if (__builtin_isfinite(x[k])) amax = fmaxf(amax, fabsf(x[k]));
+  for (int off = 1; off < C; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off, kWave));
+  s = amax / 127.f;
+  uint32_t c[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    c[k] = int8_code(x[4 * k], s) | int8_code(x[4 * k + 1], s) << 8 |
+           int8_code(x[4 * k + 2], s) << 16 | int8_code(x[4 * k + 3], s) << 24;
+  return make_uint4(c[0], c[1], c[2], c[3]);
+}
+
+// Source chunks of one (token, head) row chunk for the cache: K and V codes
+// or bits, and for an int8 cache the two row scales.
+template <typename Tr>
+__device__ __forceinline__ void row_chunks(const void* key, const void* value, int64_t src, int C,
+                                           float k_scale, float v_scale, uint4& kc, uint4& vc,
+                                           float& ks, float& vs) {
+  if constexpr (Tr::kKind == Kind::kInt8) {
+    kc = int8_chunk(key, src, C, ks);
+    vc = int8_chunk(value, src, C, vs);
+  } else {
+    kc = source_chunk<Tr>(key, src, k_scale);
+    vc = source_chunk<Tr>(value, src, v_scale);
+  }
+}
+
+// An int8 row's two scales, stored by the thread of chunk 0 (tile = block *
+// H_kv + head, t = in-block slot).
+template <typename Tr>
+__device__ __forceinline__ void write_row_scales(void* k_cache, void* v_cache,
+                                                 int64_t scales_offset, int64_t tile, int t,
+                                                 int c, float ks, float vs) {
+  if constexpr (Tr::kKind == Kind::kInt8) {
+    if (c != 0) return;
+    const int64_t i = tile * kBlockTokens + t;
+    __builtin_nontemporal_store(ks, reinterpret_cast<float*>(static_cast<char*>(k_cache) +
+                                                             scales_offset) + i);
+    __builtin_nontemporal_store(vs, reinterpret_cast<float*>(static_cast<char*>(v_cache) +
+                                                             scales_offset) + i);
+  }
+}
+
 // One thread per (token, kv head, 16-byte chunk of the head's cached row).  K
 // chunks land as one 16-byte store ([d/X][16][X] tile); V elements land one by
 // one in the token-minor [d][16] tile.  bf16 / fp32: pure bit moves.
@@ -94,14 +154,16 @@ __global__ __launch_bounds__(256) void cache_write_kernel(CacheWriteArgs a) {
   // The source chunk does not depend on the slot: load it first, so its
   // latency overlaps that of the slot load.
   const int64_t src = (i * a.num_kv_heads + h) * a.head_dim + int64_t(c) * X;
-  const uint4 kc = source_chunk<Tr>(a.key, src, a.k_scale);
-  const uint4 vc = source_chunk<Tr>(a.value, src, a.v_scale);
+  uint4 kc, vc;
+  float ks = 0.f, vs = 0.f;
+  row_chunks<Tr>(a.key, a.value, src, C, a.k_scale, a.v_scale, kc, vc, ks, vs);
   const int64_t slot = a.slot_mapping[i];
   if (slot < 0 || slot >= int64_t(a.num_blocks) * kBlockTokens) return;
   const int64_t p = slot / kBlockTokens;
   const int t = int(slot % kBlockTokens);
   const int64_t tile = p * a.num_kv_heads + h;
   write_token_chunk<Tr>(a.k_cache, a.v_cache, tile, C, a.head_dim, c, t, kc, vc);
+  write_row_scales<Tr>(a.k_cache, a.v_cache, a.scales_offset, tile, t, c, ks, vs);
 }
 
 // One new token per sequence, slot mapping and write in one launch: one thread
@@ -120,8 +182,9 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   const int b = int(idx / (int64_t(C) * a.num_kv_heads));
   // Source chunk first: it overlaps the dependent length -> table loads.
   const int64_t src = (int64_t(b) * a.num_kv_heads + h) * a.head_dim + int64_t(c) * X;
-  const uint4 kc = source_chunk<Tr>(a.key, src, a.k_scale);
-  const uint4 vc = source_chunk<Tr>(a.value, src, a.v_scale);
+  uint4 kc, vc;
+  float ks = 0.f, vs = 0.f;
+  row_chunks<Tr>(a.key, a.value, src, C, a.k_scale, a.v_scale, kc, vc, ks, vs);
   const int32_t n = a.context_lens[b];
   int64_t slot = -1;
   if (n > 0 && n <= a.max_nb * kBlockTokens) {
@@ -134,6 +197,8 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   const int64_t tile = (slot / kBlockTokens) * a.num_kv_heads + h;
   write_token_chunk<Tr>(a.k_cache, a.v_cache, tile, C, a.head_dim, c, int(slot % kBlockTokens), kc,
                         vc);
+  write_row_scales<Tr>(a.k_cache, a.v_cache, a.scales_offset, tile, int(slot % kBlockTokens), c,
+                       ks, vs);
 }
 
 // Several new tokens per sequence (a prefill chunk, draft tokens).  Row
@@ -260,6 +325,13 @@ __global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(CopyBlocksArg
   char* base = static_cast<char*>(blockIdx.y == 0 ? a.k_cache : a.v_cache);
   const int64_t lo = int64_t(blockIdx.z) * kCopySlice;
   const int64_t hi = min(lo + kCopySlice, a.block_bytes);
+  if (a.scale_block_bytes > 0 && blockIdx.z == 0) {  // int8: the block's row scales
+    const int n4 = a.scale_block_bytes / 4;
+    const float* fs = reinterpret_cast<const float*>(base + a.scales_offset) + int64_t(s) * n4;
+    float* fd = reinterpret_cast<float*>(base + a.scales_offset) + int64_t(d) * n4;
+    for (int k = threadIdx.x; k < n4; k += kCopyThreads)
+      __builtin_nontemporal_store(__builtin_nontemporal_load(fs + k), fd + k);
+  }
   const u32x4_t* from = reinterpret_cast<const u32x4_t*>(base + int64_t(s) * a.block_bytes + lo);
   u32x4_t* to = reinterpret_cast<u32x4_t*>(base + int64_t(d) * a.block_bytes + lo);
   const int n16 = int((hi - lo) / 16);
@@ -285,7 +357,8 @@ hipError_t launch_copy_blocks(const CopyBlocksArgs& a, hipStream_t s) {
 }
 
 static int chunk_elems(Kind kind) {
-  return kind == Kind::kFp8 ? Fp8::kChunk : kind == Kind::kBf16 ? Bf16::kChunk : F32::kChunk;
+  return kind == Kind::kFp8 || kind == Kind::kInt8 ? 16 : kind == Kind::kBf16 ? Bf16::kChunk
+                                                                             : F32::kChunk;
 }
 
 hipError_t launch_cache_write(const CacheWriteArgs& a, Kind kind, hipStream_t s) {
@@ -303,6 +376,9 @@ hipError_t launch_cache_write(const CacheWriteArgs& a, Kind kind, hipStream_t s)
     case Kind::kFp8:
       hipLaunchKernelGGL(cache_write_kernel<Fp8>, dim3(blocks), dim3(threads), 0, s, a);
       break;
+    case Kind::kInt8:
+      hipLaunchKernelGGL(cache_write_kernel<Int8>, dim3(blocks), dim3(threads), 0, s, a);
+      break;
   }
   return hipGetLastError();
 }
@@ -314,9 +390,11 @@ static void (*append_kernel_for(bool chunk))(AppendArgs) {
 
 hipError_t launch_append(const AppendArgs& a, Kind kind, hipStream_t s) {
   const bool chunk = a.query_start != nullptr;
-  void (*kern)(AppendArgs) = kind == Kind::kBf16  ? append_kernel_for<Bf16>(chunk)
-                             : kind == Kind::kFp8 ? append_kernel_for<Fp8>(chunk)
-                                                  : append_kernel_for<F32>(chunk);
+  void (*kern)(AppendArgs) = kind == Kind::kBf16   ? append_kernel_for<Bf16>(chunk)
+                             : kind == Kind::kFp8  ? append_kernel_for<Fp8>(chunk)
+                             : kind == Kind::kInt8 ? (chunk ? nullptr : append_kernel<Int8>)
+                                                   : append_kernel_for<F32>(chunk);
+  if (!kern) return hipErrorInvalidValue;
   if (chunk) {
     // blocks the rows of one sequence may touch: ceil(max_query_len / 16) + 1
     if (a.B == 0 || a.max_query_len == 0) return hipSuccess;

@@ -22,15 +22,16 @@ namespace {
 // work-groups per CU (168 VGPRs leave room for 3 waves per SIMD), so a
 // finishing work-group's successor fetches its first blocks while two others
 // stream.  Split, bf16: 8 waves, one work-group per CU (its work-list loop
-// does not fit 3 waves per SIMD without spilling).  Split, fp8: 4 waves, two
-// per CU; a 512-token item is half the bytes there, so the start of each item
-// (length, table and first tile loads in a row) weighs twice as much, and a
-// second work-group streaming meanwhile hides it (measured on the long-context
-// mix: 104 -> 86 us; bf16 is 1% slower that way).
+// does not fit 3 waves per SIMD without spilling).  Split, one-byte codes (fp8,
+// int8): 4 waves, two per CU; a 512-token item is half the bytes there, so
+// the start of each item (length, table and first tile loads in a row) weighs
+// twice as much, and a second work-group streaming meanwhile hides it
+// (measured on the long-context mix with fp8: 104 -> 86 us; bf16 is 1% slower
+// that way).
 template <typename E, bool kSplit>
-constexpr int kWavesOf = kSplit && E::kKind != Kind::kFp8 ? 8 : 4;
+constexpr int kWavesOf = kSplit && !kByteCodes<E> ? 8 : 4;
 template <typename E, bool kSplit>
-constexpr int kGroupsPerCu = !kSplit ? 3 : E::kKind == Kind::kFp8 ? 2 : 1;
+constexpr int kGroupsPerCu = !kSplit ? 3 : kByteCodes<E> ? 2 : 1;
 // One work item: partition `part` of sequence b, head tile `tile_y` (a KV
 // head and a group of up to 16 of its query heads).
 template <typename E, int D, int kWaves>
@@ -140,7 +141,13 @@ __device__ __forceinline__ void mfma_item(const DecodeArgs& a, const int part, c
     const int p = __builtin_amdgcn_readlane(win, n - n0);
     const bool ok = p >= 0 && p < a.num_blocks;
     const int64_t tile = (int64_t(ok ? p : 0) * a.num_kv_heads + kvh) * tile_elems;
-    load_block<E, D>(f, kc + tile, vc + tile, lane);
+    if constexpr (E::kKind == Kind::kInt8) {
+      const int64_t row0 = tile / D;  // the tile's first (block, head, slot) row
+      load_block<E, D>(f, kc + tile, vc + tile, lane, row_scales(a.k_cache, a.scales_offset) + row0,
+                        row_scales(a.v_cache, a.scales_offset) + row0);
+    } else {
+      load_block<E, D>(f, kc + tile, vc + tile, lane);
+    }
     return ok ? tile : -1;
   };
   auto consume = [&](int j, int64_t tile, const MfmaFrag<E, D>& f) {
@@ -260,14 +267,16 @@ void (*mfma_kernel(int head_dim, bool split))(DecodeArgs) {
 
 hipError_t launch_decode_mfma(const DecodeArgs& a, Kind kind, int head_dim, hipStream_t s) {
   const bool split = a.partition_size > 0;
-  void (*kern)(DecodeArgs) = kind == Kind::kBf16  ? mfma_kernel<Bf16>(head_dim, split)
-                             : kind == Kind::kFp8 ? mfma_kernel<Fp8>(head_dim, split)
-                                                  : nullptr;
+  void (*kern)(DecodeArgs) = kind == Kind::kBf16   ? mfma_kernel<Bf16>(head_dim, split)
+                             : kind == Kind::kFp8  ? mfma_kernel<Fp8>(head_dim, split)
+                             : kind == Kind::kInt8 ? mfma_kernel<Int8>(head_dim, split)
+                                                   : nullptr;
   if (!kern) return hipErrorInvalidValue;
   const int g = a.H / a.num_kv_heads;
   const int tiles = a.num_kv_heads * ((g + kHeadsPerTile - 1) / kHeadsPerTile);
-  const int waves = kind == Kind::kFp8 ? (split ? kWavesOf<Fp8, true> : kWavesOf<Fp8, false>)
-                                       : (split ? kWavesOf<Bf16, true> : kWavesOf<Bf16, false>);
+  const bool bytes = kind == Kind::kFp8 || kind == Kind::kInt8;
+  const int waves = bytes ? (split ? kWavesOf<Fp8, true> : kWavesOf<Fp8, false>)
+                          : (split ? kWavesOf<Bf16, true> : kWavesOf<Bf16, false>);
   const dim3 block(waves * kWave);
   dim3 grid(1, tiles, a.B);
   if (a.partition_size > 0) {

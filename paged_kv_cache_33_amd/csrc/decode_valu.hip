@@ -39,16 +39,31 @@ struct ValuShape {
   static constexpr int VL = XK * R;     // V loads per lane per block
 };
 
+// int8 caches also carry the K and V scales of the lane's token (l % 16).
+template <typename Tr, bool kScaled = Tr::kKind == Kind::kInt8>
+struct RowScales {
+  float ks, vs;
+};
+template <typename Tr>
+struct RowScales<Tr, false> {};
+
 template <typename Tr, int D>
-struct BlockFrag {
+struct BlockFrag : RowScales<Tr> {
   uint4 k[ValuShape<Tr, D>::KL];
   uint4 v[ValuShape<Tr, D>::VL];
 };
 
+// ksr / vsr: the tile's 16 row scales (int8 caches only).
 template <typename Tr, int D>
 __device__ __forceinline__ void load_block(BlockFrag<Tr, D>& f, const typename Tr::storage* kt,
-                                           const typename Tr::storage* vt, int lane) {
+                                           const typename Tr::storage* vt, int lane,
+                                           const float* ksr = nullptr,
+                                           const float* vsr = nullptr) {
   using Sh = ValuShape<Tr, D>;
+  if constexpr (Tr::kKind == Kind::kInt8) {
+    f.ks = __builtin_nontemporal_load(ksr + (lane & 15));
+    f.vs = __builtin_nontemporal_load(vsr + (lane & 15));
+  }
 #pragma unroll
   for (int i = 0; i < Sh::KL; ++i)
     f.k[i] = load_tile16(kt + (i * kWave + lane) * Sh::X);
@@ -71,17 +86,18 @@ struct WaveState {
 // 16 bf16 query values, two 16-byte pieces.
 template <typename Tr, int D>
 struct QueryFrag {
-  static constexpr int kPieces = Tr::kKind == Kind::kFp8 ? 2 : 1;
+  static constexpr int kPieces = kByteCodes<Tr> ? 2 : 1;
   uint4 c[ValuShape<Tr, D>::KL][kPieces];
 };
 
-// One 16-byte piece of 16 E4M3 codes as 8 bf16 pairs (lo: codes 0..7, hi:
-// codes 8..15), exact.
-__device__ __forceinline__ void e4m3x16_to_bf16(const uint4& v, uint4& lo, uint4& hi) {
-  lo = make_uint4(e4m3x2_to_bf16x2<false>(v.x), e4m3x2_to_bf16x2<true>(v.x),
-                  e4m3x2_to_bf16x2<false>(v.y), e4m3x2_to_bf16x2<true>(v.y));
-  hi = make_uint4(e4m3x2_to_bf16x2<false>(v.z), e4m3x2_to_bf16x2<true>(v.z),
-                  e4m3x2_to_bf16x2<false>(v.w), e4m3x2_to_bf16x2<true>(v.w));
+// One 16-byte piece of 16 one-byte codes (E4M3 or int8) as 8 bf16 pairs (lo:
+// codes 0..7, hi: codes 8..15), exact.
+template <Kind kK>
+__device__ __forceinline__ void codes16_to_bf16(const uint4& v, uint4& lo, uint4& hi) {
+  lo = make_uint4(code2_to_bf16x2<kK, false>(v.x), code2_to_bf16x2<kK, true>(v.x),
+                  code2_to_bf16x2<kK, false>(v.y), code2_to_bf16x2<kK, true>(v.y));
+  hi = make_uint4(code2_to_bf16x2<kK, false>(v.z), code2_to_bf16x2<kK, true>(v.z),
+                  code2_to_bf16x2<kK, false>(v.w), code2_to_bf16x2<kK, true>(v.w));
 }
 
 // Zero the bf16 V values of tokens outside [nfirst, nvalid) inside one 16-byte
@@ -107,15 +123,16 @@ __device__ __forceinline__ void compute_block(const BlockFrag<Tr, D>& f, const Q
                                               float (&o)[ValuShape<Tr, D>::XK], WaveState& st,
                                               int nfirst, int nvalid, float scale_log2, int lane) {
   using Sh = ValuShape<Tr, D>;
-  constexpr bool kFp8 = Tr::kKind == Kind::kFp8;
+  constexpr bool kBytes = kByteCodes<Tr>;             // one-byte codes, converted to bf16
+  constexpr bool kInt8 = Tr::kKind == Kind::kInt8;    // per-token row scales
   constexpr bool kPacked = Tr::kKind != Kind::kF32;  // bf16 pairs into dot2
   // ---- scores: this lane's chunks of token lane%16, then the 4 rows combined
   float dot = 0.f;
 #pragma unroll
   for (int i = 0; i < Sh::KL; ++i) {
-    if constexpr (kFp8) {
+    if constexpr (kBytes) {
       uint4 klo, khi;
-      e4m3x16_to_bf16(f.k[i], klo, khi);
+      codes16_to_bf16<Tr::kKind>(f.k[i], klo, khi);
       dot = dot2_bf16(klo.x, qf.c[i][0].x, dot);
       dot = dot2_bf16(klo.y, qf.c[i][0].y, dot);
       dot = dot2_bf16(klo.z, qf.c[i][0].z, dot);
@@ -139,7 +156,9 @@ __device__ __forceinline__ void compute_block(const BlockFrag<Tr, D>& f, const Q
   dot = cross_row_sum(dot);
   const int t = lane & 15;
   float s = dot * scale_log2;
-  if (kTail && (t >= nvalid || t < nfirst)) s = -INFINITY;  // select: the slot may hold NaN
+  if constexpr (kInt8) s *= f.ks;  // the token's K row scale
+  const bool masked = kTail && (t >= nvalid || t < nfirst);
+  if (masked) s = -INFINITY;  // select: the slot may hold NaN
   // ---- online softmax over the block's 16 tokens (one per lane of a row)
   const float m_new = fmaxf(st.m, row16_max(s));
   const float alpha = fast_exp2(st.m - m_new);
@@ -149,13 +168,20 @@ __device__ __forceinline__ void compute_block(const BlockFrag<Tr, D>& f, const Q
   for (int xk = 0; xk < Sh::XK; ++xk) o[xk] *= alpha;
   if constexpr (kPacked) {
     // weights rounded to bf16 pairs (tokens 2k, 2k+1); the denominator sums
-    // the same rounded values
+    // the same rounded values.  int8: the values the products take are p
+    // times the token's V row scale (0 where masked: the scale may be NaN),
+    // the denominator sums p alone.
     const uint32_t packed = pack_bf16x2(p, dpp_mov<kDppQuadXor1>(p));
     st.l = fmaf(st.l, alpha, __uint_as_float(packed << 16));
+    uint32_t packed_v = packed;
+    if constexpr (kInt8) {
+      const float pv = masked ? 0.f : p * f.vs;
+      packed_v = pack_bf16x2(pv, dpp_mov<kDppQuadXor1>(pv));
+    }
     uint32_t pp[kBlockTokens / 2];
 #pragma unroll
     for (int k = 0; k < kBlockTokens / 2; ++k)
-      pp[k] = __builtin_amdgcn_readlane(packed, 2 * k);
+      pp[k] = __builtin_amdgcn_readlane(packed_v, 2 * k);
     auto accumulate = [&](uint4 v, int th, float& acc) {  // tokens 8th .. 8th+7
       if (kTail) v = mask_tokens(v, th * 8, nfirst, nvalid);
       acc = dot2_bf16(v.x, pp[th * 4 + 0], acc);
@@ -165,9 +191,9 @@ __device__ __forceinline__ void compute_block(const BlockFrag<Tr, D>& f, const Q
     };
 #pragma unroll
     for (int xk = 0; xk < Sh::XK; ++xk) {
-      if constexpr (kFp8) {
+      if constexpr (kBytes) {
         uint4 vlo, vhi;
-        e4m3x16_to_bf16(f.v[xk], vlo, vhi);
+        codes16_to_bf16<Tr::kKind>(f.v[xk], vlo, vhi);
         accumulate(vlo, 0, o[xk]);
         accumulate(vhi, 1, o[xk]);
       } else {
@@ -290,7 +316,13 @@ __device__ __forceinline__ void valu_item(const DecodeArgs& a, const int part, c
     const int p = __builtin_amdgcn_readlane(win, n - n0);
     const bool ok = p >= 0 && p < a.num_blocks;
     const int64_t tile = (int64_t(ok ? p : 0) * a.num_kv_heads + kvh) * tile_elems;
-    load_block<Tr, D>(f, kc + tile, vc + tile, lane);
+    if constexpr (Tr::kKind == Kind::kInt8) {
+      const int64_t row0 = tile / D;  // the tile's first (block, head, slot) row
+      load_block<Tr, D>(f, kc + tile, vc + tile, lane, row_scales(a.k_cache, a.scales_offset) + row0,
+                        row_scales(a.v_cache, a.scales_offset) + row0);
+    } else {
+      load_block<Tr, D>(f, kc + tile, vc + tile, lane);
+    }
     return ok ? tile : -1;
   };
   auto consume = [&](int j, int64_t tile, const BlockFrag<Tr, D>& f) {
@@ -408,9 +440,10 @@ void (*valu_kernel(int head_dim, bool split))(DecodeArgs) {
 
 hipError_t launch_decode_valu(const DecodeArgs& a, Kind kind, int head_dim, hipStream_t s) {
   const bool split = a.partition_size > 0;
-  void (*kern)(DecodeArgs) = kind == Kind::kBf16  ? valu_kernel<Bf16>(head_dim, split)
-                             : kind == Kind::kF32 ? valu_kernel<F32>(head_dim, split)
-                                                  : valu_kernel<Fp8>(head_dim, split);
+  void (*kern)(DecodeArgs) = kind == Kind::kBf16   ? valu_kernel<Bf16>(head_dim, split)
+                             : kind == Kind::kF32  ? valu_kernel<F32>(head_dim, split)
+                             : kind == Kind::kInt8 ? valu_kernel<Int8>(head_dim, split)
+                                                   : valu_kernel<Fp8>(head_dim, split);
   if (!kern) return hipErrorInvalidValue;
   const dim3 block(kWaves * kWave);
   dim3 grid(1, a.H, a.B);

@@ -151,12 +151,71 @@ struct Fp8 {
   __device__ __forceinline__ static act from_f32(float f) { return f32_to_bf16_rne(f); }
 };
 
+// int8 cache ("MLSys Engineer - Inference Systems Q&A", Q3 item 1): codes with
+// one float32 scale per (token, KV head) row, stored after the codes of each
+// cache buffer; bf16 activations.
+struct Int8 {
+  using storage = uint8_t;
+  using act = uint16_t;
+  static constexpr Kind kKind = Kind::kInt8;
+  static constexpr int kChunk = 16;
+  __device__ __forceinline__ static act from_f32(float f) { return f32_to_bf16_rne(f); }
+};
+
+// Elements stored as one-byte codes (fp8 and int8 caches).
+template <typename Tr>
+constexpr bool kByteCodes = Tr::kKind == Kind::kFp8 || Tr::kKind == Kind::kInt8;
+
+// Two int8 codes (bytes 0, 1 of `w`, or bytes 2, 3 when `hi`) as a bf16 pair:
+// exact, since |code| <= 127 needs 7 significant bits.
+template <bool kHi>
+__device__ __forceinline__ uint32_t i8x2_to_bf16x2(uint32_t w) {
+  const float lo = float(int(w << (kHi ? 8 : 24)) >> 24);
+  const float hi = float(int(w << (kHi ? 0 : 16)) >> 24);
+  return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
+}
+
+// The row scales of an int8 cache buffer (after its codes).
+__device__ __forceinline__ const float* row_scales(const void* cache, int64_t scales_offset) {
+  return reinterpret_cast<const float*>(static_cast<const char*>(cache) + scales_offset);
+}
+
+// Two one-byte codes of a cache type as a bf16 pair.
+template <Kind kK, bool kHi>
+__device__ __forceinline__ uint32_t code2_to_bf16x2(uint32_t w);
+
 // Two E4M3 codes (bytes 0, 1 of `w`, or bytes 2, 3 when `hi`) as a bf16 pair:
 // exact, since every E4M3 value is a bf16 value.
 template <bool kHi>
 __device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
   typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, kHi));
+}
+
+template <>
+__device__ __forceinline__ uint32_t code2_to_bf16x2<Kind::kFp8, false>(uint32_t w) {
+  return e4m3x2_to_bf16x2<false>(w);
+}
+template <>
+__device__ __forceinline__ uint32_t code2_to_bf16x2<Kind::kFp8, true>(uint32_t w) {
+  return e4m3x2_to_bf16x2<true>(w);
+}
+template <>
+__device__ __forceinline__ uint32_t code2_to_bf16x2<Kind::kInt8, false>(uint32_t w) {
+  return i8x2_to_bf16x2<false>(w);
+}
+template <>
+__device__ __forceinline__ uint32_t code2_to_bf16x2<Kind::kInt8, true>(uint32_t w) {
+  return i8x2_to_bf16x2<true>(w);
+}
+
+// int8 code of x under the row scale s (s = the row's largest finite
+// magnitude / 127): round half to even of x / s, the division correctly
+// rounded in fp32, clamped to +-127; 0 for a non-finite x or s = 0.
+__device__ __forceinline__ uint32_t int8_code(float x, float s) {
+  if (!(s > 0.f) || !__builtin_isfinite(x)) return 0u;
+  const float q = fminf(fmaxf(__builtin_rintf(x / s), -127.f), 127.f);
+  return uint32_t(int(q)) & 0xFFu;
 }
 
 // E4M3 code of x: the nearest value, ties to the even code (the hardware

@@ -11,7 +11,7 @@ namespace pagedkv {
 constexpr int kMaxSplitSeqs = 4096;
 
 // Cache element type of a pool (see the traits in device_common.h).
-enum class Kind { kF32, kBf16, kFp8 };
+enum class Kind { kF32, kBf16, kFp8, kInt8 };
 
 // Work-groups of `kernel` (block size `threads`) the current GPU keeps
 // resident at once, divided among `tiles` head tiles (at least 1 each).
@@ -39,6 +39,7 @@ struct DecodeArgs {
   float* ws_o;                 // [B][H][P][d]   (split mode only)
   float* ws_m;                 // [B][H][P]
   float* ws_l;                 // [B][H][P]
+  int64_t scales_offset;       // int8: bytes from a cache buffer to its row scales
 };
 
 // Several new query tokens per sequence (a prefill chunk or draft tokens to
@@ -92,6 +93,7 @@ struct CacheWriteArgs {
   int32_t N;
   float k_scale;                // fp8: stored code = e4m3(x / scale)
   float v_scale;
+  int64_t scales_offset;        // int8: bytes from a cache buffer to its row scales
 };
 
 // One new token per sequence: slot mapping and cache write in one launch.
@@ -116,6 +118,7 @@ struct AppendArgs {
   const int32_t* query_start;
   int32_t max_query_len;
   int32_t num_rows;
+  int64_t scales_offset;        // int8: bytes from a cache buffer to its row scales
 };
 
 // Whole-block copies (copy-on-write): block src[i] -> dst[i] in both caches.
@@ -124,6 +127,8 @@ struct CopyBlocksArgs {
   void* v_cache;
   int32_t num_blocks;
   int64_t block_bytes;          // bytes of one block in one cache (a multiple of 16)
+  int64_t scales_offset;        // int8: bytes to the row scales (0: none)
+  int32_t scale_block_bytes;    // int8: bytes of one block's row scales
   const int32_t* src;
   const int32_t* dst;
   int32_t n;

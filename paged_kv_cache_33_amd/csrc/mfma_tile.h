@@ -36,23 +36,39 @@ struct MfmaShape {
 
 // One block's K and V as loaded by one lane.  bf16: 16-byte K chunk 4i + q of
 // token n is operand i of S = K Q^T as stored; 8 bytes of V (tokens 4q..4q+3
-// of dim 16mc + n) are operand mc of O^T = V^T P^T.  fp8 (E4M3 codes): one
-// 16-byte load holds chunk q + 4j (16 dims) and becomes operands 2j, 2j+1
-// (dims 8 and 8 more); 4 bytes of V become operand mc.  The codes convert to
-// bf16 exactly, so both caches feed the same bf16 products.
+// of dim 16mc + n) are operand mc of O^T = V^T P^T.  One-byte codes (fp8 E4M3
+// or int8): one 16-byte load holds chunk q + 4j (16 dims) and becomes operands
+// 2j, 2j+1 (dims 8 and 8 more); 4 bytes of V become operand mc.  The codes
+// convert to bf16 exactly, so every cache feeds the same bf16 products.  An
+// int8 cache adds the K and V row scales of tokens 4q..4q+3 (the rows of S
+// this lane holds).
+template <typename E, bool kScaled = E::kKind == Kind::kInt8>
+struct MfmaScales {
+  uint4 ks, vs;  // float bits
+};
+template <typename E>
+struct MfmaScales<E, false> {};
+
 template <typename E, int D>
-struct MfmaFrag {
-  static constexpr bool kFp8 = E::kKind == Kind::kFp8;
+struct MfmaFrag : MfmaScales<E> {
+  static constexpr bool kFp8 = kByteCodes<E>;  // one-byte codes
   static constexpr int KL = kFp8 ? D / 64 : D / 32;  // 16-byte K loads per lane
   using VPiece = std::conditional_t<kFp8, uint32_t, uint2>;
   uint4 k[KL];
   VPiece v[MfmaShape<D>::MC];
 };
 
+// ksr / vsr: the tile's 16 row scales (int8 caches only).
 template <typename E, int D>
 __device__ __forceinline__ void load_block(MfmaFrag<E, D>& f, const typename E::storage* kt,
-                                           const typename E::storage* vt, int lane) {
+                                           const typename E::storage* vt, int lane,
+                                           const float* ksr = nullptr,
+                                           const float* vsr = nullptr) {
   constexpr int X = E::kChunk;
+  if constexpr (E::kKind == Kind::kInt8) {
+    f.ks = load_tile16(ksr + 4 * (lane >> 4));
+    f.vs = load_tile16(vsr + 4 * (lane >> 4));
+  }
 #pragma unroll
   for (int i = 0; i < MfmaFrag<E, D>::KL; ++i)
     f.k[i] = load_tile16(kt + (i * kWave + lane) * X);
@@ -85,12 +101,13 @@ __device__ __forceinline__ void load_block_lds(MfmaFrag<E, D>& f, const typename
 template <typename E, int D>
 __device__ __forceinline__ bf16x8_t k_operand(const MfmaFrag<E, D>& f, int i) {
   if constexpr (MfmaFrag<E, D>::kFp8) {
+    constexpr Kind kK = E::kKind;
     const uint4 c = f.k[i >> 1];
     const uint32_t w0 = (i & 1) ? c.z : c.x, w1 = (i & 1) ? c.w : c.y;
-    return __builtin_bit_cast(bf16x8_t, make_uint4(e4m3x2_to_bf16x2<false>(w0),
-                                                   e4m3x2_to_bf16x2<true>(w0),
-                                                   e4m3x2_to_bf16x2<false>(w1),
-                                                   e4m3x2_to_bf16x2<true>(w1)));
+    return __builtin_bit_cast(bf16x8_t, make_uint4(code2_to_bf16x2<kK, false>(w0),
+                                                   code2_to_bf16x2<kK, true>(w0),
+                                                   code2_to_bf16x2<kK, false>(w1),
+                                                   code2_to_bf16x2<kK, true>(w1)));
   } else {
     return __builtin_bit_cast(bf16x8_t, f.k[i]);
   }
@@ -98,7 +115,8 @@ __device__ __forceinline__ bf16x8_t k_operand(const MfmaFrag<E, D>& f, int i) {
 template <typename E, int D>
 __device__ __forceinline__ uint2 v_operand(const MfmaFrag<E, D>& f, int mc) {
   if constexpr (MfmaFrag<E, D>::kFp8)
-    return make_uint2(e4m3x2_to_bf16x2<false>(f.v[mc]), e4m3x2_to_bf16x2<true>(f.v[mc]));
+    return make_uint2(code2_to_bf16x2<E::kKind, false>(f.v[mc]),
+                      code2_to_bf16x2<E::kKind, true>(f.v[mc]));
   else
     return f.v[mc];
 }
@@ -106,7 +124,7 @@ __device__ __forceinline__ uint2 v_operand(const MfmaFrag<E, D>& f, int mc) {
 // First query dim of the 8 that pair with K operand i in lane quarter q.
 template <typename E>
 __device__ __forceinline__ int query_dim0(int i, int q) {
-  if constexpr (E::kKind == Kind::kFp8)
+  if constexpr (kByteCodes<E>)
     return (q + 4 * (i >> 1)) * 16 + (i & 1) * 8;
   else
     return (4 * i + q) * 8;
@@ -139,13 +157,19 @@ __device__ __forceinline__ void compute_block(const MfmaFrag<E, D>& f,
 #pragma unroll
   for (int i = 0; i < MfmaShape<D>::KI; ++i)
     s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand<E, D>(f, i), qop[i], s, 0, 0, 0);
+  constexpr bool kInt8 = E::kKind == Kind::kInt8;
   float sc[4];
+  bool masked[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     sc[j] = s[j] * scale_log2;
-    if (kTail && (4 * q + j >= nvalid || 4 * q + j < nfirst))
-      sc[j] = -INFINITY;  // select: the slot may hold NaN
-    if (kCausal && (key0 + 4 * q + j > limit || key0 + 4 * q + j < lo)) sc[j] = -INFINITY;
+    if constexpr (kInt8) {  // token 4q + j's K row scale
+      const uint32_t ks[4] = {f.ks.x, f.ks.y, f.ks.z, f.ks.w};
+      sc[j] *= __uint_as_float(ks[j]);
+    }
+    masked[j] = (kTail && (4 * q + j >= nvalid || 4 * q + j < nfirst)) ||
+                (kCausal && (key0 + 4 * q + j > limit || key0 + 4 * q + j < lo));
+    if (masked[j]) sc[j] = -INFINITY;  // select: the slot may hold NaN
   }
   const float mx = cross_row_max(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
   // The reference max st.m moves only when a head's block max exceeds it by
@@ -167,12 +191,26 @@ __device__ __forceinline__ void compute_block(const MfmaFrag<E, D>& f,
   // same rounded values.  Causal: a column that has seen no position yet
   // (every score -inf) takes weight 0, not 2^(-inf - -inf).
   const float mref = (kCausal && st.m == -INFINITY) ? 0.f : st.m;
-  const uint32_t p01 = pack_bf16x2(fast_exp2(sc[0] - mref), fast_exp2(sc[1] - mref));
-  const uint32_t p23 = pack_bf16x2(fast_exp2(sc[2] - mref), fast_exp2(sc[3] - mref));
+  float pw[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) pw[j] = fast_exp2(sc[j] - mref);
+  const uint32_t p01 = pack_bf16x2(pw[0], pw[1]);
+  const uint32_t p23 = pack_bf16x2(pw[2], pw[3]);
   const float psum = (__uint_as_float(p01 << 16) + __uint_as_float(p01 & 0xffff0000u)) +
                      (__uint_as_float(p23 << 16) + __uint_as_float(p23 & 0xffff0000u));
   st.l += psum;
-  const short4_t pop = __builtin_bit_cast(short4_t, make_uint2(p01, p23));
+  uint32_t q01 = p01, q23 = p23;
+  if constexpr (kInt8) {
+    // the products take p times the token's V row scale (0 where masked: the
+    // scale may be NaN there); the denominator above sums p alone
+    const uint32_t vs[4] = {f.vs.x, f.vs.y, f.vs.z, f.vs.w};
+    float pv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) pv[j] = masked[j] ? 0.f : pw[j] * __uint_as_float(vs[j]);
+    q01 = pack_bf16x2(pv[0], pv[1]);
+    q23 = pack_bf16x2(pv[2], pv[3]);
+  }
+  const short4_t pop = __builtin_bit_cast(short4_t, make_uint2(q01, q23));
 #pragma unroll
   for (int mc = 0; mc < MfmaShape<D>::MC; ++mc) {
     uint2 v = v_operand<E, D>(f, mc);

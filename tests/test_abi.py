@@ -220,6 +220,19 @@ def test_append_chunk_argument_errors(lib, pool):
         assert f(key=None, **nothing) == _lib.KV_OK
 
 
+def test_int8_pools(lib):
+    st, h = _create(lib, desc(8, 16, 2, 128, _lib.KV_INT8, 0.0, float("nan")))  # scales ignored
+    assert st == _lib.KV_OK
+    # codes plus one float32 scale per (block, head, slot) row
+    assert lib.kv_pool_bytes(C.byref(desc(8, 16, 2, 128, _lib.KV_INT8))) == 8 * 2 * 16 * (128 + 4)
+    assert lib.kv_decode_kernel_kind(h, 2) == 0 and lib.kv_decode_kernel_kind(h, 8) == 1
+    f = lib.kv_cache_append_chunk
+    assert f(h, FAKE_K, FAKE_V, 6, FAKE_K, 4, FAKE_K, 4, FAKE_V, 2, None, None) \
+        == _lib.KV_ERR_UNSUPPORTED
+    assert _multi(lib, h) == _lib.KV_ERR_UNSUPPORTED
+    lib.kv_pool_destroy(h)
+
+
 def test_window_argument_errors(lib, pool):
     f = lib.paged_attention_decode_window
     assert f(pool, FAKE_K, FAKE_V, FAKE_K, 4, FAKE_V, 2, 4, 64, 0.1, -1, 0, None, 0, None) \
