@@ -167,12 +167,14 @@ template <typename Tr>
 constexpr bool kByteCodes = Tr::kKind == Kind::kFp8 || Tr::kKind == Kind::kInt8;
 
 // Two int8 codes (bytes 0, 1 of `w`, or bytes 2, 3 when `hi`) as a bf16 pair:
-// exact, since |code| <= 127 needs 7 significant bits.
+// exact, since |code| <= 127 needs 7 significant bits, so each float's upper
+// half is its bf16 value.  The two halves are joined with one byte permute.
 template <bool kHi>
 __device__ __forceinline__ uint32_t i8x2_to_bf16x2(uint32_t w) {
   const float lo = float(int(w << (kHi ? 8 : 24)) >> 24);
   const float hi = float(int(w << (kHi ? 0 : 16)) >> 24);
-  return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
+  // bytes 2, 3 of lo, then bytes 2, 3 of hi
+  return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
 }
 
 // The row scales of an int8 cache buffer (after its codes).
