@@ -19,7 +19,10 @@ Order of work:
   4. W warm-up steps, then the timed region: exactly K steps between two
      events, nothing else inside -> ms_per_step and `value`;
   5. K more steps with events around every kernel -> the decode kernel's
-     average duration (`roofline`) and the step-time distribution.
+     average duration (`roofline`) and the step-time distribution;
+  6. the read ceiling: kv_read_tiles over exactly the tiles the first step's
+     decode reads (same loads, no arithmetic), timed over 10 launches; the
+     decode's rate as a fraction of it is `roofline.frac_of_read_ceiling`.
 With --cold every step is instead preceded by a 512 MiB write that evicts the
 caches (outside the timed range) and timed alone.
 
@@ -133,6 +136,69 @@ def step_bytes(w, step, window: int = 0) -> dict:
     write = 2 * w.B * w.H_kv * (w.d * (e + ec) + w.kv_row_extra_bytes)  # rows in, cache out
     slots = 4 * w.B + 4 * w.B + 8 * w.B                    # lengths, table entries, slots out
     return {"decode": decode, "kv": kv, "step": decode + write + slots}
+
+
+def visible_tiles(w, step, window: int = 0) -> np.ndarray:
+    """The (block, KV head) tiles a decode step reads, as tile indices
+    p * H_kv + h, sequence by sequence in table order (each once per
+    sequence, so a block shared by several sequences appears once for each)."""
+    out = []
+    hs = np.arange(w.H_kv, dtype=np.int64)
+    for b, c in enumerate(step.context_lens.astype(np.int64)):
+        if c <= 0:
+            continue
+        first = max(int(c) - window, 0) if window > 0 else 0
+        blocks = w.block_tables[b][first // 16:(int(c) + 15) // 16].astype(np.int64)
+        out.append((blocks[:, None] * w.H_kv + hs[None, :]).reshape(-1))
+    return np.concatenate(out).astype(np.int32) if out else np.zeros(0, np.int32)
+
+
+def read_ceiling(P, torch, pool, w, step, window, stream, launches: int = 10) -> dict:
+    """Time kv_read_tiles over exactly the tiles the decode reads: the rate
+    that access pattern reaches with no arithmetic (the decode's own ceiling)."""
+    tiles = visible_tiles(w, step, window)
+    tile_bytes = 16 * w.d * w.kv_elem_bytes
+    groups = 8 * torch.cuda.get_device_properties(0).multi_processor_count
+    t = torch.from_numpy(tiles).cuda()
+    sink = torch.empty(groups, dtype=torch.int32, device="cuda")
+    for _ in range(3):
+        P.kv_read_tiles(pool, t, sink, stream)
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(launches):
+        P.kv_read_tiles(pool, t, sink, stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / launches
+    nbytes = 2 * int(tiles.size) * tile_bytes
+    unique = 2 * int(np.unique(tiles).size) * (tile_bytes + 16 * w.kv_row_extra_bytes)
+    return {"kernel": "read_tiles", "achieved": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "unit": "GB/s", "frac_of_peak": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "bytes_per_launch": nbytes, "avg_launch_ms": round(ms, 5),
+            "tiles": int(tiles.size), "unique_kv_bytes": unique}
+
+
+def gpu_clocks(torch) -> dict:
+    """Current shader and memory clock levels of device 0 from sysfs (the
+    lines marked '*' of pp_dpm_sclk / pp_dpm_mclk), when the files are
+    readable; empty otherwise."""
+    try:
+        p = torch.cuda.get_device_properties(0)
+        base = "/sys/bus/pci/devices/%04x:%02x:%02x.0" % (
+            int(getattr(p, "pci_domain_id", 0)), int(p.pci_bus_id), int(p.pci_device_id))
+        out = {}
+        for name in ("pp_dpm_sclk", "pp_dpm_mclk", "pp_dpm_fclk"):
+            path = os.path.join(base, name)
+            if os.path.exists(path):
+                with open(path) as f:
+                    cur = [l.split(":", 1)[1].replace("*", "").strip()
+                           for l in f.read().splitlines() if l.strip().endswith("*")]
+                if cur:
+                    out[name[7:]] = cur[0]
+        return out
+    except Exception:  # best effort: the clocks are context, not a result
+        return {}
 
 
 def traffic_from_profile(kernel: str, workload: str):
@@ -724,6 +790,8 @@ def main(argv=None) -> int:
     dec_gbs = dec_b / (dec_avg * 1e-3) / 1e9
     wname = w.name + (f"-window{args.window}" if args.window else "")
     traffic = traffic_from_profile(kernel, wname)
+    ceiling = read_ceiling(P, torch, pool, w, w.steps[0], args.window, stream)
+    clocks = gpu_clocks(torch)
 
     def pct(a, q):
         return round(float(np.percentile(a, q)), 5)
@@ -778,7 +846,13 @@ def main(argv=None) -> int:
             "bytes_per_launch": int(dec_b),
             "avg_launch_ms": round(dec_avg, 5),
             "launch_ms_p10_median_p90": [pct(dec_ms, 10), pct(dec_ms, 50), pct(dec_ms, 90)],
+            "frac_of_read_ceiling": round(dec_gbs / ceiling["achieved"], 4),
         },
+        "read_ceiling": ceiling,
+        "kv_bytes_logical": int(np.mean([u["kv"] for u in used])),
+        "kv_bytes_unique": ceiling["unique_kv_bytes"],
+        "decode_gbps_unique_kv": round(ceiling["unique_kv_bytes"] / (dec_avg * 1e-3) / 1e9, 1),
+        "gpu_clocks": clocks,
     }
     if cpu_rec is not None:
         cpu_rec["parity"] = parity

@@ -307,6 +307,19 @@ kv_status paged_attention_multi(const kv_pool* pool, void* out, const void* quer
 kv_status kv_copy_blocks(const kv_pool* pool, const int32_t* src, const int32_t* dst, int32_t n,
                          void* stream);
 
+/* Measurement helper, not a step of the decode: read tiles[i] (a tile index
+ * p * H_kv + h, naming the 16-slot tile of block p and KV head h) of both
+ * caches once, as the decode kernels read a tile (non-temporal 16-byte loads),
+ * with no arithmetic.  Timed over the tiles a decode step visits, it gives the
+ * bandwidth that access pattern can reach on the device (the decode's own
+ * ceiling, below the published peak).  Entries outside [0, num_blocks*H_kv)
+ * are skipped.  An int8 pool's row scales are not read.  groups work-groups
+ * (1 .. 2^20) share the entries; work-group i stores into sink[i] (device
+ * uint32 [groups]) the XOR of every 32-bit word it read, so the XOR over sink
+ * is the XOR of all listed tiles' words (a checksum the caller can verify). */
+kv_status kv_read_tiles(const kv_pool* pool, const int32_t* tiles, int64_t n, uint32_t* sink,
+                        int32_t groups, void* stream);
+
 /* ---------------------------------------------------------------------------
  * Host block manager ("Forward Deployed Engineering Interview", Ch.2 section 8,
  * the block-manager teaching model; "Anthropic Interview: Design an LLM

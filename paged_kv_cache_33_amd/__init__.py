@@ -35,6 +35,7 @@ __all__ = [
     "paged_attention_multi",
     "kv_decode_kernel_kind",
     "kv_copy_blocks",
+    "kv_read_tiles",
     "BlockManager",
     "NoBlocks",
     "library_path",
@@ -353,6 +354,18 @@ def kv_copy_blocks(pool: KVPool, src: torch.Tensor, dst: torch.Tensor, stream=No
     sp = _buf(src, "src", 4 * n, dtype=torch.int32)
     dp = _buf(dst, "dst", 4 * n, dtype=torch.int32)
     _lib.check(_lib.load().kv_copy_blocks(pool.handle, sp, dp, n, _stream_handle(stream)))
+
+
+def kv_read_tiles(pool: KVPool, tiles: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
+    """Read the listed K/V tiles (device int32 tile indices p * H_kv + h) once,
+    with no arithmetic: the bandwidth ceiling of that access pattern.  One
+    work-group per element of sink (device int32/uint32 [groups]); each stores
+    the XOR of the 32-bit words it read."""
+    n = int(tiles.numel())
+    tp = _buf(tiles, "tiles", 4 * n, dtype=torch.int32)
+    groups = int(sink.numel())
+    sp = _buf(sink, "sink", 4 * groups, elem_size=4)
+    _lib.check(_lib.load().kv_read_tiles(pool.handle, tp, n, sp, groups, _stream_handle(stream)))
 
 
 class BlockManager:

@@ -45,6 +45,7 @@ EXPORTED = (
     "paged_attention_reduce_window",
     "paged_attention_multi",
     "kv_copy_blocks",
+    "kv_read_tiles",
     "kv_bm_create",
     "kv_bm_destroy",
     "kv_bm_admit",
@@ -117,6 +118,7 @@ def load() -> C.CDLL:
         "paged_attention_reduce_window": (C.c_int, [vp, vp, i32p, i32, i32, i32, i32, i32, i32,
                                                     C.c_int, vp]),
         "kv_copy_blocks": (C.c_int, [vp, i32p, i32p, i32, vp]),
+        "kv_read_tiles": (C.c_int, [vp, i32p, C.c_int64, vp, i32, vp]),
         "kv_bm_create": (C.c_int, [i32, C.POINTER(vp)]),
         "kv_bm_destroy": (None, [vp]),
         "kv_bm_admit": (C.c_int, [vp, C.c_int64, vp, i32, C.c_char_p, i32, C.POINTER(C.c_int32)]),

@@ -23,6 +23,7 @@ BUILD = os.path.join(ROOT, "_build", "pagedkv")
 LIB = os.path.join(PKG, "libpagedkv.so")
 
 SOURCES = ["api.hip", "cache_write.hip", "decode_valu.hip", "decode_mfma.hip", "multi_mfma.hip",
+           "read_tiles.hip",
            "reduce.hip"]
 HOST_SOURCES = ["block_manager.cpp"]  # host-only C++ (the block manager)
 ARCH = "gfx950"

@@ -470,6 +470,26 @@ kv_status kv_copy_blocks(const kv_pool* pool, const int32_t* src, const int32_t*
                     "copy_blocks launch");
 }
 
+kv_status kv_read_tiles(const kv_pool* pool, const int32_t* tiles, int64_t n, uint32_t* sink,
+                        int32_t groups, void* stream) {
+  if (!pool) return fail(KV_ERR_INVALID_ARG, "pool is NULL");
+  if (n < 0) return fail(KV_ERR_INVALID_ARG, "n must be >= 0");
+  if (groups < 1 || groups > (1 << 20))
+    return fail(KV_ERR_INVALID_ARG, "groups must be in 1 .. 2^20 (got %d)", int(groups));
+  if (!sink) return fail(KV_ERR_INVALID_ARG, "sink must be non-NULL");
+  if (n > 0 && !tiles) return fail(KV_ERR_INVALID_ARG, "tiles must be non-NULL");
+  const kv_pool_desc& d = pool->desc;
+  pagedkv::ReadTilesArgs a{pool->k_cache,
+                           pool->v_cache,
+                           tiles,
+                           n,
+                           int64_t(16) * d.head_dim * int64_t(elem_bytes(d.dtype)),
+                           int64_t(d.num_blocks) * d.num_kv_heads,
+                           sink};
+  return hip_status(pagedkv::launch_read_tiles(a, groups, static_cast<hipStream_t>(stream)),
+                    "read_tiles launch");
+}
+
 static kv_status reduce_impl(void* out, const void* workspace, const int32_t* context_lens,
                              int32_t B, int32_t H, int32_t head_dim, int32_t max_context_len,
                              int32_t window, int32_t partition_size, kv_dtype out_dtype,

@@ -134,6 +134,16 @@ struct CopyBlocksArgs {
   int32_t n;
 };
 
+struct ReadTilesArgs {
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* tiles;         // tile indices p * H_kv + h; others skipped
+  int64_t n;
+  int64_t tile_bytes;           // one tile of one cache (a multiple of 1 KiB)
+  int64_t pool_tiles;           // num_blocks * H_kv
+  uint32_t* sink;               // [groups]
+};
+
 struct SlotMappingArgs {
   const int32_t* block_tables;
   int32_t max_nb;
@@ -147,6 +157,7 @@ hipError_t launch_slot_mapping(const SlotMappingArgs& a, hipStream_t s);
 hipError_t launch_cache_write(const CacheWriteArgs& a, Kind kind, hipStream_t s);
 hipError_t launch_append(const AppendArgs& a, Kind kind, hipStream_t s);
 hipError_t launch_copy_blocks(const CopyBlocksArgs& a, hipStream_t s);
+hipError_t launch_read_tiles(const ReadTilesArgs& a, int groups, hipStream_t s);
 hipError_t launch_decode_valu(const DecodeArgs& a, Kind kind, int head_dim, hipStream_t s);
 hipError_t launch_decode_mfma(const DecodeArgs& a, Kind kind, int head_dim, hipStream_t s);
 hipError_t launch_multi_mfma(const MultiArgs& a, Kind kind, int head_dim, hipStream_t s);

@@ -144,6 +144,16 @@ def test_append_argument_errors(lib, pool):
     assert f(pool, None, None, None, 4, None, 0, None, None) == _lib.KV_OK   # nothing to do
 
 
+def test_read_tiles_argument_errors(lib, pool):
+    f = lib.kv_read_tiles
+    assert f(None, FAKE_K, 4, FAKE_V, 8, None) == _lib.KV_ERR_INVALID_ARG
+    assert f(pool, FAKE_K, -1, FAKE_V, 8, None) == _lib.KV_ERR_INVALID_ARG
+    assert f(pool, FAKE_K, 4, FAKE_V, 0, None) == _lib.KV_ERR_INVALID_ARG      # no work-group
+    assert f(pool, FAKE_K, 4, FAKE_V, (1 << 20) + 1, None) == _lib.KV_ERR_INVALID_ARG
+    assert f(pool, FAKE_K, 4, None, 8, None) == _lib.KV_ERR_INVALID_ARG        # no sink
+    assert f(pool, None, 4, FAKE_V, 8, None) == _lib.KV_ERR_INVALID_ARG        # no tiles
+
+
 def test_slot_mapping_argument_errors(lib):
     assert lib.kv_slot_mapping(None, 4, None, -1, None, None) == _lib.KV_ERR_INVALID_ARG
     assert lib.kv_slot_mapping(FAKE_K, 0, FAKE_K, 1, FAKE_V, None) == _lib.KV_ERR_INVALID_ARG
