@@ -474,14 +474,22 @@ __global__ __launch_bounds__(kMultiWaves* kWave, 2) void chunk_mfma_kernel(Multi
         const int nfirst = klo - key0;
         const bool open =
             nvalid >= kBlockTokens && key0 + kBlockTokens - 1 <= kmin && key0 >= klo_max;
+        // The branch encloses the tile loop, so the masked path's work (the V
+        // operands' masking, shared by the tiles) stays inside it instead of
+        // being computed ahead of the branch for every block.
+        if (open) {
 #pragma unroll
-        for (int tt = 0; tt < kTiles; ++tt) {
-          if (tt > 0 && tt >= ntiles) break;
-          if (open)
+          for (int tt = 0; tt < kTiles; ++tt) {
+            if (tt > 0 && tt >= ntiles) break;
             compute_block<E, D, false>(f, qop[tt], st[tt], 0, nvalid, a.scale_log2, lane);
-          else
+          }
+        } else {
+#pragma unroll
+          for (int tt = 0; tt < kTiles; ++tt) {
+            if (tt > 0 && tt >= ntiles) break;
             compute_block<E, D, true, true>(f, qop[tt], st[tt], nfirst, nvalid, a.scale_log2,
                                             lane, key0, lo[tt], limit[tt]);
+          }
         }
       }
     }
@@ -508,9 +516,10 @@ __global__ __launch_bounds__(kMultiWaves* kWave, 2) void chunk_mfma_kernel(Multi
   }
 }
 
+template <typename E>
 void (*chunk_kernel(int head_dim))(MultiArgs) {
-  if (head_dim == 128) return chunk_mfma_kernel<Bf16, 128>;
-  if (head_dim == 64) return chunk_mfma_kernel<Bf16, 64>;
+  if (head_dim == 128) return chunk_mfma_kernel<E, 128>;
+  if (head_dim == 64) return chunk_mfma_kernel<E, 64>;
   return nullptr;
 }
 
@@ -535,13 +544,13 @@ hipError_t launch_multi_mfma(const MultiArgs& a, Kind kind, int head_dim, hipStr
   const int g = a.H / a.num_kv_heads;
   const int64_t set_cols = int64_t(kHeadsPerTile) * a.tiles_per_set;
   const int64_t sets = (int64_t(a.max_query_len) * g + set_cols - 1) / set_cols;
-  // four or more two-tile sets of a bf16 pool: the LDS-staged long-chunk
-  // kernel (measured on 512-token prefill chunks: 15% faster than the
-  // per-wave kernel for bf16, 10% slower for fp8, whose blocks are half the
-  // bytes, so the shared loads save less than the barriers cost)
-  const bool chunk = a.tiles_per_set == 2 && sets >= kMultiWaves && kind == Kind::kBf16;
+  // four or more two-tile sets: the LDS-staged long-chunk kernel (measured
+  // on 512-token prefill chunks: 21% faster than the per-wave kernel for a
+  // bf16 pool, 11% for fp8)
+  const bool chunk = a.tiles_per_set == 2 && sets >= kMultiWaves &&
+                     (kind == Kind::kBf16 || kind == Kind::kFp8);
   void (*kern)(MultiArgs) =
-      chunk ? chunk_kernel(head_dim)
+      chunk ? (kind == Kind::kBf16 ? chunk_kernel<Bf16>(head_dim) : chunk_kernel<Fp8>(head_dim))
             : (kind == Kind::kBf16 ? multi_kernel<Bf16>(head_dim, a.tiles_per_set)
                : kind == Kind::kFp8 ? multi_kernel<Fp8>(head_dim, a.tiles_per_set)
                                     : nullptr);

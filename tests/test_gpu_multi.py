@@ -256,7 +256,8 @@ def test_chunk_write_alone_is_bit_exact(kv, d):
     assert np.array_equal(from_dev(dw.pool.v_cache, kv), vp)
 
 
-def test_long_chunk_kernel_contains_bad_inputs():
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
+def test_long_chunk_kernel_contains_bad_inputs(kv_dtype):
     """The same containment for the long-chunk kernel (g * max_query_len of 320
     columns, ten column sets): n > ctx, n > max_query_len and ctx > max_nb*16
     give NaN rows below max_query_len, a bad table entry in block 0 gives NaN
@@ -264,7 +265,8 @@ def test_long_chunk_kernel_contains_bad_inputs():
     H, H_kv, d = 32, 4, 128
     ctx = [300, 10, 200, 120, 400]
     n = [40, 30, 45, 33, 20]
-    w = W.multi_token_workload("badc", "bf16", len(ctx), H, H_kv, d, ctx, n, seed=78, max_nb=25)
+    w = W.multi_token_workload("badc", "bf16", len(ctx), H, H_kv, d, ctx, n, seed=78, max_nb=25,
+                               kv_dtype=kv_dtype)
     m = w.multi
     w.block_tables[3, 0] = w.num_blocks + 3
     ctx_dev = m.context_lens.copy()
@@ -272,7 +274,7 @@ def test_long_chunk_kernel_contains_bad_inputs():
     dw = upload(w, w.k_pool, w.v_pool)
     qs = m.query_start
     T = int(qs[-1])
-    log("[gpu] long-chunk bad-input containment")
+    log(f"[gpu] long-chunk bad-input containment ({kv_dtype})")
     m2 = W.MultiStep(context_lens=ctx_dev, query_start=qs, q=m.q, new_k=m.new_k, new_v=m.new_v)
     _, out = _gpu_multi(dw, m2, max_query_len=40, write=False, out_fill=SENT16)
     torch.cuda.synchronize()
