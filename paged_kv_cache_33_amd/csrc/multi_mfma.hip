@@ -298,15 +298,16 @@ __device__ __forceinline__ void lds_barrier() {
   __asm__ volatile("" ::: "memory");
 }
 
-// Long chunks (a prefill chunk: four or more column sets per sequence and KV
-// head).  Each wave owns one 32-column set and walks every block its columns
-// see; the four waves of a work-group need nearly the same blocks (their
-// positions differ by at most 128 / g tokens), so the work-group loads each
-// block once, cooperatively, into LDS (two buffers; each block's global loads
-// are issued two blocks ahead into registers), and every wave reads its
-// operands there.  The K/V of a
-// sequence is read by all of its work-groups, so these loads are ordinary
-// (cached) ones.  No partial results meet: a wave finishes its own columns.
+// Several column sets per sequence and KV head (a prefill chunk, or draft
+// verification with two sets of a bf16 pool).  Each wave owns one 32-column
+// set and walks every block its columns see; the waves of a work-group need
+// nearly the same blocks (their positions differ by at most 128 / g tokens),
+// so the work-group loads each block once, cooperatively, into a 4-stage LDS
+// ring (direct global-to-LDS loads, three blocks ahead), and every wave reads
+// its operands there; with fewer than four sets the idle waves only load.
+// The K/V of a sequence is read by all of its work-groups, so these loads are
+// ordinary (cached) ones.  No partial results meet: a wave finishes its own
+// columns.
 template <typename E, int D>
 __global__ __launch_bounds__(kMultiWaves* kWave, 2) void chunk_mfma_kernel(MultiArgs a) {
   using S = typename E::storage;
@@ -544,11 +545,15 @@ hipError_t launch_multi_mfma(const MultiArgs& a, Kind kind, int head_dim, hipStr
   const int g = a.H / a.num_kv_heads;
   const int64_t set_cols = int64_t(kHeadsPerTile) * a.tiles_per_set;
   const int64_t sets = (int64_t(a.max_query_len) * g + set_cols - 1) / set_cols;
-  // four or more two-tile sets: the LDS-staged long-chunk kernel (measured
-  // on 512-token prefill chunks: 21% faster than the per-wave kernel for a
-  // bf16 pool, 11% for fp8)
-  const bool chunk = a.tiles_per_set == 2 && sets >= kMultiWaves &&
-                     (kind == Kind::kBf16 || kind == Kind::kFp8);
+  // The LDS-staged long-chunk kernel loads each block once for all sets of a
+  // work-group.  Measured against the per-wave kernel: 21% faster on
+  // 512-token prefill chunks of a bf16 pool and 11% for fp8; with two sets
+  // (draft verification, g * K of 33..64 columns) 7-25% faster for bf16 but
+  // 50% slower for fp8, whose conversions make the two computing waves the
+  // bottleneck, so fp8 takes it from four sets on.
+  const bool chunk = a.tiles_per_set == 2 &&
+                     ((kind == Kind::kBf16 && sets >= 2) ||
+                      (kind == Kind::kFp8 && sets >= kMultiWaves));
   void (*kern)(MultiArgs) =
       chunk ? (kind == Kind::kBf16 ? chunk_kernel<Bf16>(head_dim) : chunk_kernel<Fp8>(head_dim))
             : (kind == Kind::kBf16 ? multi_kernel<Bf16>(head_dim, a.tiles_per_set)
