@@ -508,10 +508,10 @@ def multi_bytes_flops(w) -> dict:
     n = np.diff(m.query_start).astype(np.int64)
     T = int(n.sum())
     e, ec = w.elem_bytes, w.kv_elem_bytes
-    kv = int(ctx.sum()) * w.H_kv * w.d * 2 * ec          # every cached K/V row once
+    kv = int(ctx.sum()) * w.H_kv * (w.d * ec + w.kv_row_extra_bytes) * 2  # every cached row once
     nb = (ctx + 15) // 16
     attn = kv + 2 * T * w.H * w.d * e + 4 * int(nb.sum()) + 4 * (2 * w.B + 1)
-    write = 2 * T * w.H_kv * w.d * (e + ec) + 8 * T
+    write = 2 * T * w.H_kv * (w.d * (e + ec) + w.kv_row_extra_bytes) + 8 * T
     # row at position p: q.k and p.v over p + 1 keys, per query head
     seen = sum(int(((c - k + 1) + c) * k // 2) for c, k in zip(ctx, n))
     flops = 4 * w.H * w.d * seen

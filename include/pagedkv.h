@@ -77,8 +77,9 @@
  * cache buffer continues, after its num_blocks*H_kv*16*d code bytes, with the
  * scales: the scale of (block p, head h, slot t) is float number
  * (p*H_kv + h)*16 + t of that region.  The desc's k_scale / v_scale are
- * ignored.  kv_cache_append_chunk and paged_attention_multi refuse int8
- * pools.
+ * ignored.  Every write (reshape_and_cache, kv_cache_append,
+ * kv_cache_append_chunk) quantises this way and every attention call reads
+ * code * s.
  */
 #ifndef PAGEDKV_H_
 #define PAGEDKV_H_
@@ -282,8 +283,8 @@ kv_status paged_attention_reduce_window(void* out, const void* workspace,
  *   out[row][h][:] = softmax_t(scale * q[row][h] . K_b[t]) V_b[t], t <= p,
  * with K_b, V_b read through the block table as in paged_attention_decode;
  * out: device [num_rows][H][d], bf16 (rounded to nearest-even).  n_b = 1 is
- * the decode step.  Matrix-core kernel for every H / H_kv, bf16 or fp8 pools
- * (KV_F32 is refused).  max_query_len: a host bound on every n_b.  Rows of a
+ * the decode step.  Matrix-core kernel for every H / H_kv, bf16, fp8 or int8
+ * pools (KV_F32 is refused).  max_query_len: a host bound on every n_b.  Rows of a
  * sequence with n_b > ctx_b, n_b > max_query_len or ctx_b > max_nb*16 are NaN
  * (those below max_query_len; nothing is written past it).  A table entry
  * outside the pool that a row's range reaches makes that row NaN (and may make

@@ -369,8 +369,6 @@ kv_status kv_cache_append_chunk(const kv_pool* pool, const void* key, const void
   if (!aligned16(key) || !aligned16(value))
     return fail(KV_ERR_INVALID_ARG, "key and value must be 16-byte aligned");
   const kv_pool_desc& d = pool->desc;
-  if (d.dtype == KV_INT8)
-    return fail(KV_ERR_UNSUPPORTED, "kv_cache_append_chunk does not write int8 pools");
   pagedkv::AppendArgs a{};
   a.k_cache = pool->k_cache;
   a.v_cache = pool->v_cache;
@@ -389,6 +387,7 @@ kv_status kv_cache_append_chunk(const kv_pool* pool, const void* key, const void
   a.query_start = query_start;
   a.max_query_len = max_query_len;
   a.num_rows = num_rows;
+  a.scales_offset = scales_offset(d);
   return hip_status(pagedkv::launch_append(a, kind_of(d.dtype), static_cast<hipStream_t>(stream)),
                     "chunk append launch");
 }
@@ -401,9 +400,8 @@ kv_status paged_attention_multi(const kv_pool* pool, void* out, const void* quer
   if (!pool) return fail(KV_ERR_INVALID_ARG, "pool is NULL");
   if (window < 0) return fail(KV_ERR_INVALID_ARG, "window must be >= 0 (0 = whole context)");
   const kv_pool_desc& d = pool->desc;
-  if (d.dtype != KV_BF16 && d.dtype != KV_FP8_E4M3)
-    return fail(KV_ERR_UNSUPPORTED, "multi-token attention needs a bf16 or fp8 pool (dtype %d)",
-                int(d.dtype));
+  if (d.dtype == KV_F32)
+    return fail(KV_ERR_UNSUPPORTED, "multi-token attention needs a bf16, fp8 or int8 pool");
   if (B < 0 || num_rows < 0 || max_query_len < 0)
     return fail(KV_ERR_INVALID_ARG, "B, num_rows and max_query_len must be >= 0");
   if (H < 1 || H % d.num_kv_heads != 0)
@@ -440,6 +438,7 @@ kv_status paged_attention_multi(const kv_pool* pool, void* out, const void* quer
   a.scale_log2 = scale * 1.4426950408889634f * (fp8 ? d.k_scale : 1.f);
   a.v_scale = fp8 ? d.v_scale : 1.f;
   a.window = window;
+  a.scales_offset = scales_offset(d);
   // one tile per wave when one tile holds every column; else two per wave,
   // and up to four such sets per work-group
   a.tiles_per_set = tiles > 1 ? 2 : 1;

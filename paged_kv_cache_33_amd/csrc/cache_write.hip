@@ -264,14 +264,31 @@ __global__ __launch_bounds__(kChunkThreads) void append_chunk_kernel(AppendArgs 
   S* vt = static_cast<S*>(a.v_cache) + tile * int64_t(kBlockTokens) * D;
 
   // K straight to the tile; V chunks into LDS
-  for (int idx = threadIdx.x; idx < C * kBlockTokens; idx += blockDim.x) {
-    const int c = idx / kBlockTokens, s = idx % kBlockTokens;
-    if (s < s_lo || s >= s_hi) continue;
-    const int64_t src = ((row0 + s) * a.num_kv_heads + h) * D + int64_t(c) * X;
-    const uint4 kc = source_chunk<Tr>(a.key, src, a.k_scale);
-    const u32x4_t ku = {kc.x, kc.y, kc.z, kc.w};
-    __builtin_nontemporal_store(ku, reinterpret_cast<u32x4_t*>(kt + (int64_t(c) * kBlockTokens + s) * X));
-    sv[s][c] = source_chunk<Tr>(a.value, src, a.v_scale);
+  if constexpr (Tr::kKind == Kind::kInt8) {
+    // A row's C chunks sit in C consecutive lanes (C divides 64), which
+    // reduce its largest magnitude together; the lane of chunk 0 stores the
+    // row's two scales.
+    for (int idx = threadIdx.x; idx < C * kBlockTokens; idx += blockDim.x) {
+      const int s = idx / C, c = idx % C;
+      if (s < s_lo || s >= s_hi) continue;  // uniform over the row's lanes
+      const int64_t src = ((row0 + s) * a.num_kv_heads + h) * D + int64_t(c) * X;
+      float ks, vs;
+      const uint4 kc = int8_chunk(a.key, src, C, ks);
+      const u32x4_t ku = {kc.x, kc.y, kc.z, kc.w};
+      __builtin_nontemporal_store(ku, reinterpret_cast<u32x4_t*>(kt + (int64_t(c) * kBlockTokens + s) * X));
+      sv[s][c] = int8_chunk(a.value, src, C, vs);
+      write_row_scales<Tr>(a.k_cache, a.v_cache, a.scales_offset, tile, s, c, ks, vs);
+    }
+  } else {
+    for (int idx = threadIdx.x; idx < C * kBlockTokens; idx += blockDim.x) {
+      const int c = idx / kBlockTokens, s = idx % kBlockTokens;
+      if (s < s_lo || s >= s_hi) continue;
+      const int64_t src = ((row0 + s) * a.num_kv_heads + h) * D + int64_t(c) * X;
+      const uint4 kc = source_chunk<Tr>(a.key, src, a.k_scale);
+      const u32x4_t ku = {kc.x, kc.y, kc.z, kc.w};
+      __builtin_nontemporal_store(ku, reinterpret_cast<u32x4_t*>(kt + (int64_t(c) * kBlockTokens + s) * X));
+      sv[s][c] = source_chunk<Tr>(a.value, src, a.v_scale);
+    }
   }
   __syncthreads();
 
@@ -392,7 +409,7 @@ hipError_t launch_append(const AppendArgs& a, Kind kind, hipStream_t s) {
   const bool chunk = a.query_start != nullptr;
   void (*kern)(AppendArgs) = kind == Kind::kBf16   ? append_kernel_for<Bf16>(chunk)
                              : kind == Kind::kFp8  ? append_kernel_for<Fp8>(chunk)
-                             : kind == Kind::kInt8 ? (chunk ? nullptr : append_kernel<Int8>)
+                             : kind == Kind::kInt8 ? append_kernel_for<Int8>(chunk)
                                                    : append_kernel_for<F32>(chunk);
   if (!kern) return hipErrorInvalidValue;
   if (chunk) {

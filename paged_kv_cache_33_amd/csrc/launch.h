@@ -65,6 +65,7 @@ struct MultiArgs {
   int32_t window;               // sliding window per row; 0 = whole context
   int32_t tiles_per_set;        // 16-column tiles one wave carries (1 or 2)
   int32_t sets_per_group;       // column sets one work-group takes (1..4)
+  int64_t scales_offset;        // int8: bytes from a cache buffer to its row scales
 };
 
 struct ReduceArgs {

@@ -159,7 +159,13 @@ __global__ __launch_bounds__(kMultiWaves* kWave, 2) void multi_mfma_kernel(
   auto fetch = [&](int p, MfmaFrag<E, D>& f) -> int64_t {
     const bool ok = p >= 0 && p < a.num_blocks;
     const int64_t tile = (int64_t(ok ? p : 0) * a.num_kv_heads + kvh) * tile_elems;
-    load_block<E, D>(f, kc + tile, vc + tile, lane);
+    if constexpr (E::kKind == Kind::kInt8) {
+      const int64_t row0 = tile / D;  // the tile's first (block, head, slot) row
+      load_block<E, D>(f, kc + tile, vc + tile, lane, row_scales(a.k_cache, a.scales_offset) + row0,
+                        row_scales(a.v_cache, a.scales_offset) + row0);
+    } else {
+      load_block<E, D>(f, kc + tile, vc + tile, lane);
+    }
     return ok ? tile : -1;
   };
   auto consume = [&](int j, int64_t tile, const MfmaFrag<E, D>& f) {
@@ -556,9 +562,10 @@ hipError_t launch_multi_mfma(const MultiArgs& a, Kind kind, int head_dim, hipStr
                       (kind == Kind::kFp8 && sets >= kMultiWaves));
   void (*kern)(MultiArgs) =
       chunk ? (kind == Kind::kBf16 ? chunk_kernel<Bf16>(head_dim) : chunk_kernel<Fp8>(head_dim))
-            : (kind == Kind::kBf16 ? multi_kernel<Bf16>(head_dim, a.tiles_per_set)
-               : kind == Kind::kFp8 ? multi_kernel<Fp8>(head_dim, a.tiles_per_set)
-                                    : nullptr);
+            : (kind == Kind::kBf16   ? multi_kernel<Bf16>(head_dim, a.tiles_per_set)
+               : kind == Kind::kFp8  ? multi_kernel<Fp8>(head_dim, a.tiles_per_set)
+               : kind == Kind::kInt8 ? multi_kernel<Int8>(head_dim, a.tiles_per_set)
+                                     : nullptr);
   if (!kern) return hipErrorInvalidValue;
   if (a.B == 0 || a.max_query_len == 0) return hipSuccess;
   const int64_t per_group = chunk ? kMultiWaves : a.sets_per_group;

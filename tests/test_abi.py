@@ -210,7 +210,7 @@ def test_multi_argument_errors(lib, pool):
         assert _multi(lib, pool, out=None, **nothing) == _lib.KV_OK        # nothing to launch
     st, hf = _create(lib, desc(8, 16, 2, 64, _lib.KV_F32))
     assert _multi(lib, hf) == _lib.KV_ERR_UNSUPPORTED                       # no fp32 kernel
-    assert b"bf16 or fp8" in lib.kv_last_error()
+    assert b"bf16, fp8 or int8" in lib.kv_last_error()
     lib.kv_pool_destroy(hf)
 
 
@@ -236,10 +236,12 @@ def test_int8_pools(lib):
     # codes plus one float32 scale per (block, head, slot) row
     assert lib.kv_pool_bytes(C.byref(desc(8, 16, 2, 128, _lib.KV_INT8))) == 8 * 2 * 16 * (128 + 4)
     assert lib.kv_decode_kernel_kind(h, 2) == 0 and lib.kv_decode_kernel_kind(h, 8) == 1
+    # multi-token calls take int8 pools; argument checks still come first
     f = lib.kv_cache_append_chunk
-    assert f(h, FAKE_K, FAKE_V, 6, FAKE_K, 4, FAKE_K, 4, FAKE_V, 2, None, None) \
-        == _lib.KV_ERR_UNSUPPORTED
-    assert _multi(lib, h) == _lib.KV_ERR_UNSUPPORTED
+    assert f(h, FAKE_K + 2, FAKE_V, 6, FAKE_K, 4, FAKE_K, 4, FAKE_V, 2, None, None) \
+        == _lib.KV_ERR_INVALID_ARG
+    assert f(h, None, None, 0, None, 4, None, 4, None, 0, None, None) == _lib.KV_OK
+    assert _multi(lib, h, q=FAKE_V + 2) == _lib.KV_ERR_INVALID_ARG    # past the dtype check
     lib.kv_pool_destroy(h)
 
 

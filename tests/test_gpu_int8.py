@@ -15,6 +15,9 @@ Inference Systems Q&A", Q3 item 1).
   carries that rounding and the output's, together a few ulps of its own
   magnitude, not of 1.
 - kv_copy_blocks copies a block's row scales with its codes.
+- The multi-token calls (chunk write, causal attention) take int8 pools: their
+  parity cases live with the bf16 and fp8 ones in test_gpu_multi.py and
+  test_gpu_window.py; the chunk write of extreme rows is checked here.
 """
 import numpy as np
 import pytest
@@ -149,3 +152,30 @@ def test_copy_blocks_copies_codes_and_row_scales():
                 e[codes + t * srow:codes + (t + 1) * srow] = o[codes + s * srow:codes + (s + 1) * srow]
     assert np.array_equal(from_dev(pool.k_cache, "int8"), ek)
     assert np.array_equal(from_dev(pool.v_cache, "int8"), ev)
+
+
+def test_chunk_write_quantises_rows_of_every_magnitude():
+    """kv_cache_append_chunk on an int8 pool: rows of magnitudes 2^-20..2^20,
+    zero rows and rows holding +-inf and NaN, chunks that start and end inside
+    blocks; codes and scales equal the oracle's bit for bit."""
+    ctx, n = [40, 100, 7, 33], [13, 70, 7, 20]
+    w = W.multi_token_workload("i8-chunk", "bf16", len(ctx), 8, 2, 128, ctx, n, seed=331,
+                               kv_dtype="int8")
+    m = w.multi
+    T = int(m.query_start[-1])
+    new_k, new_v = _rows(T, 2, 128, 4), _rows(T, 2, 128, 5)
+    kp0, vp0 = poison(w, np.zeros(w.B, dtype=np.int64))
+    dw = upload(w, kp0, vp0)
+    log("[gpu] int8 chunk write, extreme rows")
+    slots = torch.empty(T, dtype=torch.int64, device="cuda")
+    P.kv_cache_append_chunk(dw.pool, to_dev(new_k), to_dev(new_v),
+                            torch.from_numpy(m.query_start).cuda(), int(max(n)), dw.tables,
+                            torch.from_numpy(m.context_lens).cuda(), slots)
+    torch.cuda.synchronize()
+    want = O.chunk_slots(w.block_tables, m.context_lens, m.query_start)
+    np.testing.assert_array_equal(slots.cpu().numpy(), want)
+    kp, vp = O.reshape_and_cache(kp0, vp0, new_k, new_v, want, 2, 128, "int8", w.num_blocks)
+    for name, got, exp in (("K", from_dev(dw.pool.k_cache, "int8"), kp),
+                           ("V", from_dev(dw.pool.v_cache, "int8"), vp)):
+        bad = np.flatnonzero(got != exp)
+        assert bad.size == 0, f"{name} bytes differ at {bad[:8]}"

@@ -115,7 +115,7 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8", "int8"])
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
 def test_multi_matches_oracle(case, kv_dtype):
     name, H, H_kv, d, ctx, n = case
@@ -125,7 +125,7 @@ def test_multi_matches_oracle(case, kv_dtype):
     multi_case(w, f"{name}-{kv_dtype}")
 
 
-@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8", "int8"])
 def test_prefill_chunk_of_512_tokens(kv_dtype):
     """Chunked prefill: a 512-token chunk on top of earlier ones, a first chunk
     (the whole context is new), and a short tail chunk, batched with decodes."""
@@ -218,7 +218,7 @@ def test_full_size_draft_verification(config, K, kv_dtype):
     multi_case(w, f"config{config}-K{K}-{w.kv_dtype}", seqs=seqs)
 
 
-@pytest.mark.parametrize("kv", ["f32", "bf16", "fp8"])
+@pytest.mark.parametrize("kv", ["f32", "bf16", "fp8", "int8"])
 @pytest.mark.parametrize("d", [64, 128])
 def test_chunk_write_alone_is_bit_exact(kv, d):
     """kv_cache_append_chunk for every pool dtype: chunks that start and end

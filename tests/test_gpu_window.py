@@ -28,9 +28,9 @@ WINDOWS = [1, 7, 16, 17, 128, 1000]
 
 
 def _hide_before(w, kp, vp, tables, first):
-    """NaN in every position < first[b]; table entries of blocks wholly before
-    it set outside the pool (GPU copies only)."""
-    nan = NAN_BITS[w.kv_dtype]
+    """NaN in every position < first[b] (an int8 pool: NaN row scales, its
+    codes cannot be NaN); table entries of blocks wholly before it set outside
+    the pool (GPU copies only)."""
     xs = np.arange(w.d)
     tables = tables.copy()
     for b in range(w.B):
@@ -38,6 +38,12 @@ def _hide_before(w, kp, vp, tables, first):
         for pos in range((f // 16) * 16, f):          # the window's first block, before it
             blk = int(w.block_tables[b][pos // 16])
             for h in range(w.H_kv):
+                if w.kv_dtype == "int8":
+                    for pool in (kp, vp):
+                        O.int8_write_scales(pool, O.int8_scale_offset(blk, h, pos % 16, w.H_kv,
+                                                                      w.d, len(pool)), [np.nan])
+                    continue
+                nan = NAN_BITS[w.kv_dtype]
                 kp[O.k_offset(blk, h, pos % 16, xs, w.H_kv, w.d, w.kv_dtype)] = nan
                 vp[O.v_offset(blk, h, pos % 16, xs, w.H_kv, w.d, w.kv_dtype)] = nan
         tables[b, :f // 16] = w.num_blocks + 1000
@@ -108,7 +114,7 @@ MULTI = [
 
 
 @pytest.mark.parametrize("window", [1, 5, 16, 33, 128])
-@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+@pytest.mark.parametrize("kv", ["bf16", "fp8", "int8"])
 @pytest.mark.parametrize("case", MULTI, ids=[c[0] for c in MULTI])
 def test_windowed_multi_matches_oracle(case, kv, window):
     name, H, H_kv, d, ctx, n = case
