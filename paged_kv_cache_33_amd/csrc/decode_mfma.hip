@@ -32,20 +32,28 @@ template <typename E, bool kSplit>
 constexpr int kWavesOf = kSplit && !kByteCodes<E> ? 8 : 4;
 template <typename E, bool kSplit>
 constexpr int kGroupsPerCu = !kSplit ? 3 : kByteCodes<E> ? 2 : 1;
+// LDS where a work-group's waves merge their (m, l, O): one padded row of O
+// per wave and head of the tile.
+template <int kWaves, int D>
+struct MergeLds {
+  __attribute__((aligned(16))) float o[kWaves][kHeadsPerTile][D + 4];
+  float m[kWaves][kHeadsPerTile];
+  float l[kWaves][kHeadsPerTile];
+  int bad[kWaves];
+};
+
 // One work item: partition `part` of sequence b, head tile `tile_y` (a KV
 // head and a group of up to 16 of its query heads).
 template <typename E, int D, int kWaves>
 __device__ __forceinline__ void mfma_item(const DecodeArgs& a, const int part, const int tile_y,
-                                          const int b) {
+                                          const int b, MergeLds<kWaves, D>& sm) {
   using S = typename E::storage;
   constexpr int KI = MfmaShape<D>::KI;
   constexpr int MC = MfmaShape<D>::MC;
-  constexpr int kRow = D + 4;  // padded LDS row (floats)
-
-  __shared__ __attribute__((aligned(16))) float sm_o[kWaves][kHeadsPerTile][kRow];
-  __shared__ float sm_m[kWaves][kHeadsPerTile];
-  __shared__ float sm_l[kWaves][kHeadsPerTile];
-  __shared__ int sm_bad[kWaves];
+  auto& sm_o = sm.o;
+  auto& sm_m = sm.m;
+  auto& sm_l = sm.l;
+  auto& sm_bad = sm.bad;
 
   const int g = a.H / a.num_kv_heads;
   const int ngroups = (g + kHeadsPerTile - 1) / kHeadsPerTile;
@@ -228,6 +236,210 @@ __device__ __forceinline__ void mfma_item(const DecodeArgs& a, const int part, c
   }
 }
 
+// Split mode: a worker (work-group) takes items i = i0, i0 + G, ... of the
+// work list (G workers per head tile) and streams them back to back.  Each
+// wave's blocks of one 512-token item are few (4 at 8 waves), so an item that
+// only started loading once the previous one had merged its waves' results
+// would spend part of its time filling the pipeline.  Here the next item's
+// table window is requested when an item starts, and its first block and
+// query operand as soon as the item's last block is computed, so the LDS
+// merge and the partial's write-out overlap those loads.  Three things keep
+// them in flight: the merge's barriers wait for LDS only, none of those loads
+// sits behind a branch (the compiler waits for every load in flight where a
+// branch holding one rejoins), and the merge loop's stride is a constant
+// (blockDim.x is itself a load from the dispatch packet, and waiting for it
+// would wait for all the others).  Partitions of more than 64 blocks per wave,
+// and fp8 pools, take mfma_item item by item instead.
+template <typename E, int D, int kWaves>
+__device__ __forceinline__ void mfma_split_worker(const DecodeArgs& a, const int tile_y,
+                                                  const int* starts, const int n_items,
+                                                  MergeLds<kWaves, D>& sm) {
+  constexpr int KI = MfmaShape<D>::KI;
+  constexpr int MC = MfmaShape<D>::MC;
+  using S = typename E::storage;
+  auto& sm_o = sm.o;
+  auto& sm_m = sm.m;
+  auto& sm_l = sm.l;
+  auto& sm_bad = sm.bad;
+
+  const int g = a.H / a.num_kv_heads;
+  const int ngroups = (g + kHeadsPerTile - 1) / kHeadsPerTile;
+  const int kvh = tile_y / ngroups;
+  const int hg = tile_y % ngroups;
+  const int head0 = kvh * g + hg * kHeadsPerTile;
+  const int nh = min(kHeadsPerTile, g - hg * kHeadsPerTile);
+  const int lane = threadIdx.x % kWave;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int n = lane & 15, q = lane >> 4;
+  const S* kc = static_cast<const S*>(a.k_cache);
+  const S* vc = static_cast<const S*>(a.v_cache);
+  const int64_t tile_elems = int64_t(kBlockTokens) * D;
+  const int stride = gridDim.x;
+
+  // An item's uniform description: its sequence, token range and this wave's
+  // block count; valid = false past the end of the list.
+  struct Item {
+    int b, part, ctx, first, nparts, te, jb, nblk;
+    bool valid, bad_len;
+  };
+  auto describe = [&](int i) -> Item {
+    Item it{};
+    it.valid = i < n_items;
+    if (!it.valid) return it;
+    locate_item(starts, a.B, i, it.b, it.part);
+    it.b = __builtin_amdgcn_readfirstlane(it.b);
+    it.part = __builtin_amdgcn_readfirstlane(it.part);
+    it.ctx = a.context_lens[it.b];
+    it.first = it.ctx > 0 ? window_first(it.ctx - 1, a.window) : 0;
+    const int rs = range_start(it.ctx, a.window);
+    it.nparts = it.ctx > 0 ? (it.ctx - rs + a.partition_size - 1) / a.partition_size : 0;
+    it.bad_len = it.ctx > a.max_nb * kBlockTokens || it.nparts > a.num_partitions;
+    const int tb = rs + it.part * a.partition_size;
+    it.te = min(tb + a.partition_size, it.ctx);
+    it.jb = tb / kBlockTokens;
+    const int je = (it.te + kBlockTokens - 1) / kBlockTokens;
+    it.nblk = !it.bad_len && je - it.jb - w > 0 ? (je - it.jb - w + kWaves - 1) / kWaves : 0;
+    return it;
+  };
+  // lane i of the window: the table entry of this wave's block i of the item
+  // (always loaded, from a clamped index: a load behind a branch makes the
+  // compiler wait for every load in flight where the branch rejoins)
+  auto load_window = [&](const Item& it) -> int {
+    const int jj = min(max(it.jb + w + kWaves * lane, 0), a.max_nb - 1);
+    const int e = a.block_tables[int64_t(it.valid ? it.b : 0) * a.max_nb + jj];
+    return it.valid && !it.bad_len && lane < it.nblk ? e : -1;
+  };
+  auto load_query = [&](const Item& it, bf16x8_t (&qop)[KI]) {
+    const int bb = it.valid ? it.b : 0;
+    const uint16_t* qrow =
+        static_cast<const uint16_t*>(a.query) + (size_t(bb) * a.H + head0 + min(n, nh - 1)) * D;
+#pragma unroll
+    for (int i = 0; i < KI; ++i) {
+      uint4 raw = *reinterpret_cast<const uint4*>(qrow + query_dim0<E>(i, q));
+      if (n >= nh) raw = make_uint4(0u, 0u, 0u, 0u);
+      qop[i] = __builtin_bit_cast(bf16x8_t, raw);
+    }
+  };
+  // Block i of the wave's walk through `win`; an entry outside the pool loads
+  // tile 0 (valid memory) and is reported as -1.
+  auto fetch = [&](int win, int i, MfmaFrag<E, D>& f) -> int64_t {
+    const int p = __builtin_amdgcn_readlane(win, i);
+    const bool ok = p >= 0 && p < a.num_blocks;
+    const int64_t tile = (int64_t(ok ? p : 0) * a.num_kv_heads + kvh) * tile_elems;
+    if constexpr (E::kKind == Kind::kInt8) {
+      const int64_t row0 = tile / D;
+      load_block<E, D>(f, kc + tile, vc + tile, lane, row_scales(a.k_cache, a.scales_offset) + row0,
+                        row_scales(a.v_cache, a.scales_offset) + row0);
+    } else {
+      load_block<E, D>(f, kc + tile, vc + tile, lane);
+    }
+    return ok ? tile : -1;
+  };
+
+  Item cur = describe(blockIdx.x);
+  int win = load_window(cur);
+  bf16x8_t qop[KI];
+  load_query(cur, qop);
+  MfmaFrag<E, D> fa, fb;
+  int64_t tile_a = fetch(win, 0, fa), tile_b;
+  if (cur.nblk == 0) tile_a = -1;
+
+  for (int i = blockIdx.x; i < n_items; i += stride) {
+    // the next item's table window, in flight while this item streams
+    const Item nxt = describe(i + stride);
+    const int win_next = load_window(nxt);
+
+    MfmaState<D> st;
+#pragma unroll
+    for (int mc = 0; mc < MC; ++mc) st.o[mc] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    st.m = -INFINITY;
+    st.l = 0.f;
+    int bad_blk = 0;
+    auto consume = [&](int k, int64_t tile, const MfmaFrag<E, D>& f) {
+      bad_blk |= tile < 0;
+      const int j = cur.jb + w + kWaves * k;
+      const int nvalid = cur.te - j * kBlockTokens;
+      const int nfirst = cur.first - j * kBlockTokens;
+      if (nvalid >= kBlockTokens && nfirst <= 0)
+        compute_block<E, D, false>(f, qop, st, 0, nvalid, a.scale_log2, lane);
+      else
+        compute_block<E, D, true>(f, qop, st, nfirst, nvalid, a.scale_log2, lane);
+    };
+    // Ping-pong; block 0 is already in flight in fa.  Once the last block is
+    // computed the next item's block 0 and query are requested (requesting
+    // them one block earlier needed more registers than the 256 a wave has
+    // here and spilled).
+    const int cnt = cur.nblk;
+    if (cnt > 0) {
+      int k = 0;
+      for (; k + 2 < cnt; k += 2) {
+        tile_b = fetch(win, k + 1, fb);
+        consume(k, tile_a, fa);
+        tile_a = fetch(win, k + 2, fa);
+        consume(k + 1, tile_b, fb);
+      }
+      if (k + 1 < cnt) {
+        tile_b = fetch(win, k + 1, fb);
+        consume(k, tile_a, fa);
+        consume(k + 1, tile_b, fb);
+      } else {
+        consume(k, tile_a, fa);
+      }
+    }
+    // unconditional (an entry outside the pool loads tile 0); see load_window
+    tile_a = fetch(win_next, 0, fa);
+    if (nxt.nblk == 0) tile_a = -1;
+    load_query(nxt, qop);
+
+    // merge the waves' (m, l, O) through LDS; the barriers leave the next
+    // item's loads in flight
+    const float lsum = cross_row_sum(st.l);
+    if (q == 0) {
+      sm_m[w][n] = st.m;
+      sm_l[w][n] = lsum;
+    }
+    if (lane == 0) sm_bad[w] = bad_blk;
+#pragma unroll
+    for (int mc = 0; mc < MC; ++mc)
+      *reinterpret_cast<floatx4_t*>(&sm_o[w][n][16 * mc + 4 * q]) = st.o[mc];
+    lds_barrier();
+    int bad = cur.bad_len ? 1 : 0;
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww) bad |= sm_bad[ww];
+    uint16_t* out = static_cast<uint16_t*>(a.out);
+    for (int idx = threadIdx.x; idx < nh * D; idx += kWaves * kWave) {
+      const int hh = idx / D, x = idx % D;
+      float M = -INFINITY;
+#pragma unroll
+      for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, sm_m[ww][hh]);
+      float L = 0.f, acc = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < kWaves; ++ww) {
+        if (sm_m[ww][hh] == -INFINITY) continue;
+        const float sc = fast_exp2(sm_m[ww][hh] - M);
+        L = fmaf(sm_l[ww][hh], sc, L);
+        acc = fmaf(sm_o[ww][hh][x], sc, acc);
+      }
+      float res = acc / L * a.v_scale;
+      if (bad) res = __int_as_float(0x7fc00000);
+      if (cur.nparts == 1) {
+        out[(size_t(cur.b) * a.H + head0 + hh) * D + x] = f32_to_bf16_rne(res);
+      } else {
+        const size_t row = (size_t(cur.b) * a.H + head0 + hh) * a.num_partitions + cur.part;
+        a.ws_o[row * D + x] = res;
+        if (x == 0) {
+          a.ws_m[row] = bad ? 0.f : M;
+          a.ws_l[row] = bad ? 1.f : L;
+        }
+      }
+    }
+    lds_barrier();  // the next item reuses the merge buffers
+
+    cur = nxt;
+    win = win_next;
+  }
+}
+
 // Single pass (kSplit = false): grid (1, head tiles, B), one work-group per
 // sequence and head tile, sequences taken longest first.  Split (kSplit =
 // true): grid (resident workers, head tiles, 1) walking the work list.  Two instantiations keep each one's
@@ -236,19 +448,26 @@ template <typename E, int D, bool kSplit>
 __global__ __launch_bounds__((kWavesOf<E, kSplit> * kWave),
                              (kGroupsPerCu<E, kSplit>)) void decode_mfma_kernel(DecodeArgs a) {
   constexpr int kWaves = kWavesOf<E, kSplit>;
+  __shared__ MergeLds<kWaves, D> sm_merge;
   if constexpr (!kSplit) {
     __shared__ int sm_order[kOrderBuckets + kWaves + 1];
     const int b = a.B <= kMaxOrderedSeqs
         ? sequence_of_rank<kWaves * kWave>(a.context_lens, a.B, a.max_nb, blockIdx.z, sm_order)
         : int(blockIdx.z);
-    mfma_item<E, D, kWaves>(a, 0, blockIdx.y, b);
+    mfma_item<E, D, kWaves>(a, 0, blockIdx.y, b, sm_merge);
   } else {
     __shared__ int sm_starts[kMaxSplitSeqs + 1];
     const int n_items = build_work_list(a, sm_starts);
+    // fp8: the streamed worker measured 2.5% slower on the long-context mix
+    // (its items are half the bytes); bf16 2.8% and int8 1.5% faster
+    if (E::kKind != Kind::kFp8 && a.partition_size <= kWaves * kWave * kBlockTokens) {
+      mfma_split_worker<E, D, kWaves>(a, blockIdx.y, sm_starts, n_items, sm_merge);
+      return;
+    }
     for (int i = blockIdx.x; i < n_items; i += gridDim.x) {
       int b, part;
       locate_item(sm_starts, a.B, i, b, part);
-      mfma_item<E, D, kWaves>(a, part, blockIdx.y, b);
+      mfma_item<E, D, kWaves>(a, part, blockIdx.y, b, sm_merge);
       __syncthreads();  // the next item reuses the merge buffers
     }
   }

@@ -226,6 +226,19 @@ __device__ __forceinline__ void compute_block(const MfmaFrag<E, D>& f,
 }
 
 
+// Work-group barrier for data exchanged through LDS only: this wave's LDS
+// operations complete (lgkmcnt 0; the gfx9 s_waitcnt encoding with vmcnt and
+// expcnt at their maxima, i.e. not waited for), then s_barrier.  Unlike
+// __syncthreads it leaves global loads in flight.  The empty asm statements
+// keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  constexpr int kLgkm0 = 0xF | (3 << 14) | (7 << 4);
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(kLgkm0);
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+}
+
 // Walk a wave's blocks j = first, first + stride, ... < je.  Table entries are
 // read 64 at a time into one register (lane i holds the entry of the wave's
 // block n0 + i) so no tile load waits on a dependent table load.

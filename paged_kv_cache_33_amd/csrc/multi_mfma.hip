@@ -291,19 +291,6 @@ __device__ __forceinline__ void load_block_lds_asm(MfmaFrag<E, D>& f, uint32_t b
   }
 }
 
-// Work-group barrier for data exchanged through LDS only: this wave's LDS
-// operations complete (lgkmcnt 0; the gfx9 s_waitcnt encoding with vmcnt and
-// expcnt at their maxima, i.e. not waited for), then s_barrier.  Unlike
-// __syncthreads it leaves global loads in flight.  The empty asm statements
-// keep the compiler from moving memory accesses across it.
-__device__ __forceinline__ void lds_barrier() {
-  constexpr int kLgkm0 = 0xF | (3 << 14) | (7 << 4);
-  __asm__ volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(kLgkm0);
-  __builtin_amdgcn_s_barrier();
-  __asm__ volatile("" ::: "memory");
-}
-
 // Several column sets per sequence and KV head (a prefill chunk, or draft
 // verification with two sets of a bf16 pool).  Each wave owns one 32-column
 // set and walks every block its columns see; the waves of a work-group need
