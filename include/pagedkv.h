@@ -219,8 +219,10 @@ size_t paged_attention_workspace_bytes(int32_t B, int32_t H, int32_t head_dim,
  * a reference value with max(s) - 8 <= m <= max(s), l = sum of 2^(s - m), o =
  * normalised partial output); sequences with a single partition write out
  * directly.  Follow with paged_attention_reduce.
- * H must be a multiple of H_kv.  Kernel choice: H_kv < H with a bf16 or fp8
- * pool uses the matrix-core kernel; otherwise the vector-ALU kernel. */
+ * scale: finite and > 0 (a softmax temperature; the pages use 1/sqrt(d)),
+ * else KV_ERR_INVALID_ARG.
+ * H must be a multiple of H_kv.  Kernel choice: H_kv < H with a bf16, fp8 or
+ * int8 pool uses the matrix-core kernel; otherwise the vector-ALU kernel. */
 kv_status paged_attention_decode(const kv_pool* pool, void* out, const void* query,
                                  const int32_t* block_tables, int32_t max_nb,
                                  const int32_t* context_lens, int32_t B, int32_t H,
@@ -284,7 +286,7 @@ kv_status paged_attention_reduce_window(void* out, const void* workspace,
  * with K_b, V_b read through the block table as in paged_attention_decode;
  * out: device [num_rows][H][d], bf16 (rounded to nearest-even).  n_b = 1 is
  * the decode step.  Matrix-core kernel for every H / H_kv, bf16, fp8 or int8
- * pools (KV_F32 is refused).  max_query_len: a host bound on every n_b.  Rows of a
+ * pools (KV_F32 is refused).  scale: finite and > 0, as for the decode.  max_query_len: a host bound on every n_b.  Rows of a
  * sequence with n_b > ctx_b, n_b > max_query_len or ctx_b > max_nb*16 are NaN
  * (those below max_query_len; nothing is written past it).  A table entry
  * outside the pool that a row's range reaches makes that row NaN (and may make

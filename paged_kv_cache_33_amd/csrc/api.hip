@@ -2,6 +2,7 @@
 // The operation and every convention are documented in include/pagedkv.h.
 #include <hip/hip_runtime.h>
 
+#include <cfloat>
 #include <cstdarg>
 #include <cstdio>
 #include <mutex>
@@ -256,7 +257,8 @@ kv_status decode_impl(const kv_pool* pool, void* out, const void* query,
                 d.num_kv_heads);
   if (max_nb < 1) return fail(KV_ERR_INVALID_ARG, "max_nb must be >= 1");
   if (kv_status s = check_partition(max_context_len, partition_size); s != KV_OK) return s;
-  if (!(scale == scale)) return fail(KV_ERR_INVALID_ARG, "scale is NaN");
+  if (!(scale > 0.f && scale <= FLT_MAX))
+    return fail(KV_ERR_INVALID_ARG, "scale must be finite and > 0 (got %g)", double(scale));
   if (B == 0) return ok();
   if (partition_size > 0 && B > pagedkv::kMaxSplitSeqs)
     return fail(KV_ERR_UNSUPPORTED, "split mode holds at most %d sequences per call (got %d)",
@@ -408,7 +410,8 @@ kv_status paged_attention_multi(const kv_pool* pool, void* out, const void* quer
     return fail(KV_ERR_INVALID_ARG, "H (%d) must be a positive multiple of num_kv_heads (%d)", H,
                 d.num_kv_heads);
   if (max_nb < 1) return fail(KV_ERR_INVALID_ARG, "max_nb must be >= 1");
-  if (!(scale == scale)) return fail(KV_ERR_INVALID_ARG, "scale is NaN");
+  if (!(scale > 0.f && scale <= FLT_MAX))
+    return fail(KV_ERR_INVALID_ARG, "scale must be finite and > 0 (got %g)", double(scale));
   if (B > 65535) return fail(KV_ERR_UNSUPPORTED, "at most 65535 sequences per call (got %d)", B);
   const int64_t tiles = (int64_t(max_query_len) * (H / d.num_kv_heads) + 15) / 16;
   if (tiles > (int64_t(1) << 30))

@@ -158,26 +158,34 @@ __device__ __forceinline__ void compute_block(const MfmaFrag<E, D>& f,
   for (int i = 0; i < MfmaShape<D>::KI; ++i)
     s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand<E, D>(f, i), qop[i], s, 0, 0, 0);
   constexpr bool kInt8 = E::kKind == Kind::kInt8;
+  // sc[j]: the score of token 4q + j in base 2, -inf where masked (by select:
+  // the slot may hold NaN).  Without per-token scales the multiply by
+  // scale_log2 is folded into the exponent's argument below, and the block
+  // maximum scaled once (scale_log2 > 0, so max and rounding commute).
   float sc[4];
   bool masked[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    sc[j] = s[j] * scale_log2;
+    sc[j] = s[j];
     if constexpr (kInt8) {  // token 4q + j's K row scale
       const uint32_t ks[4] = {f.ks.x, f.ks.y, f.ks.z, f.ks.w};
-      sc[j] *= __uint_as_float(ks[j]);
+      sc[j] = sc[j] * scale_log2 * __uint_as_float(ks[j]);
     }
     masked[j] = (kTail && (4 * q + j >= nvalid || 4 * q + j < nfirst)) ||
                 (kCausal && (key0 + 4 * q + j > limit || key0 + 4 * q + j < lo));
-    if (masked[j]) sc[j] = -INFINITY;  // select: the slot may hold NaN
+    if (masked[j]) sc[j] = -INFINITY;
   }
-  const float mx = cross_row_max(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
+  float lmax = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+  if constexpr (!kInt8) lmax *= scale_log2;
   // The reference max st.m moves only when a head's block max exceeds it by
   // more than kRescaleSlack (base-2 units), so weights 2^(s - m) stay below 2^8
   // and most blocks skip rescaling O (32 multiplies at d = 128).  Softmax does
-  // not depend on the reference, so only rounding changes.
-  const bool grow = mx > st.m + kRescaleSlack;
-  if (__builtin_amdgcn_ballot_w64(grow) != 0) {  // wave-uniform branch
+  // not depend on the reference, so only rounding changes.  The column's max
+  // over its four lanes is needed only when one of them exceeds the reference
+  // by that much, so the wave first asks whether any lane's own max does.
+  if (__builtin_amdgcn_ballot_w64(lmax > st.m + kRescaleSlack) != 0) {  // wave-uniform
+    const float mx = cross_row_max(lmax);
+    const bool grow = mx > st.m + kRescaleSlack;
     // Only growing columns rescale.  The others keep factor 1: a column that
     // has seen no key yet (m = -inf, possible under causal and window masks)
     // would otherwise get 2^(-inf - -inf) = NaN.
@@ -193,7 +201,8 @@ __device__ __forceinline__ void compute_block(const MfmaFrag<E, D>& f,
   const float mref = (kCausal && st.m == -INFINITY) ? 0.f : st.m;
   float pw[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) pw[j] = fast_exp2(sc[j] - mref);
+  for (int j = 0; j < 4; ++j)
+    pw[j] = kInt8 ? fast_exp2(sc[j] - mref) : fast_exp2(__builtin_fmaf(sc[j], scale_log2, -mref));
   const uint32_t p01 = pack_bf16x2(pw[0], pw[1]);
   const uint32_t p23 = pack_bf16x2(pw[2], pw[3]);
   const float psum = (__uint_as_float(p01 << 16) + __uint_as_float(p01 & 0xffff0000u)) +

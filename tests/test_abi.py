@@ -173,7 +173,8 @@ def test_decode_argument_errors(lib, pool):
     assert _decode(lib, pool, max_nb=0) == _lib.KV_ERR_INVALID_ARG
     assert _decode(lib, pool, P=24) == _lib.KV_ERR_INVALID_ARG
     assert _decode(lib, pool, P=-16) == _lib.KV_ERR_INVALID_ARG
-    assert _decode(lib, pool, scale=float("nan")) == _lib.KV_ERR_INVALID_ARG
+    for bad in (float("nan"), 0.0, -0.1, float("inf")):     # scale: finite and > 0
+        assert _decode(lib, pool, scale=bad) == _lib.KV_ERR_INVALID_ARG
     assert _decode(lib, pool, out=None) == _lib.KV_ERR_INVALID_ARG
     assert _decode(lib, pool, q=FAKE_V + 8) == _lib.KV_ERR_INVALID_ARG
     assert _decode(lib, pool, P=16, ws=None) == _lib.KV_ERR_WORKSPACE
@@ -199,7 +200,8 @@ def test_multi_argument_errors(lib, pool):
     assert _multi(lib, pool, T=-1) == _lib.KV_ERR_INVALID_ARG
     assert _multi(lib, pool, mq=-1) == _lib.KV_ERR_INVALID_ARG
     assert _multi(lib, pool, max_nb=0) == _lib.KV_ERR_INVALID_ARG
-    assert _multi(lib, pool, scale=float("nan")) == _lib.KV_ERR_INVALID_ARG
+    for bad in (float("nan"), 0.0, -0.1, float("inf")):
+        assert _multi(lib, pool, scale=bad) == _lib.KV_ERR_INVALID_ARG
     assert _multi(lib, pool, window=-1) == _lib.KV_ERR_INVALID_ARG
     assert _multi(lib, pool, qs=None) == _lib.KV_ERR_INVALID_ARG
     assert _multi(lib, pool, out=None) == _lib.KV_ERR_INVALID_ARG
