@@ -205,9 +205,10 @@ __device__ __forceinline__ void compute_block(const MfmaFrag<E, D>& f,
     pw[j] = kInt8 ? fast_exp2(sc[j] - mref) : fast_exp2(__builtin_fmaf(sc[j], scale_log2, -mref));
   const uint32_t p01 = pack_bf16x2(pw[0], pw[1]);
   const uint32_t p23 = pack_bf16x2(pw[2], pw[3]);
-  const float psum = (__uint_as_float(p01 << 16) + __uint_as_float(p01 & 0xffff0000u)) +
-                     (__uint_as_float(p23 << 16) + __uint_as_float(p23 & 0xffff0000u));
-  st.l += psum;
+  // the rounded weights summed by two packed dot products with ones (the
+  // bf16 products are exact in fp32)
+  constexpr uint32_t kOnes = 0x3F803F80u;  // two bf16 1.0
+  st.l = dot2_bf16(p23, kOnes, dot2_bf16(p01, kOnes, st.l));
   uint32_t q01 = p01, q23 = p23;
   if constexpr (kInt8) {
     // the products take p times the token's V row scale (0 where masked: the
