@@ -175,7 +175,10 @@ __device__ __forceinline__ void compute_block(const MfmaFrag<E, D>& f,
                 (kCausal && (key0 + 4 * q + j > limit || key0 + 4 * q + j < lo));
     if (masked[j]) sc[j] = -INFINITY;
   }
-  float lmax = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+  // (maximum, not fmaxf: gfx950's v_maximum3_f32 needs no NaN quieting of
+  // the matrix-core results; a NaN score makes its column NaN either way)
+  float lmax = __builtin_elementwise_maximum(__builtin_elementwise_maximum(sc[0], sc[1]),
+                                             __builtin_elementwise_maximum(sc[2], sc[3]));
   if constexpr (!kInt8) lmax *= scale_log2;
   // The reference max st.m moves only when a head's block max exceeds it by
   // more than kRescaleSlack (base-2 units), so weights 2^(s - m) stay below 2^8
