@@ -141,89 +141,112 @@ __device__ __forceinline__ uint32_t zero_masked_pair(uint32_t w, bool keep_lo, b
   return (keep_lo ? (w & 0x0000ffffu) : 0u) | (keep_hi ? (w & 0xffff0000u) : 0u);
 }
 
-// One 16-token block: S = K Q^T, the online softmax per column, O^T += V^T P^T.
+// One 16-token block for kT column tiles that share its K/V operands: S =
+// K Q^T, the online softmax per column, O^T += V^T P^T.  The work runs phase
+// by phase over the tiles (every tile's score products, then every tile's
+// softmax, then the PV products), so the tiles' dependent chains interleave.
 // With kTail only tokens nfirst .. nvalid-1 of the block (uniform bounds) are
 // inside the range; the rest get no weight and their V is zeroed (their slots
 // may hold NaN).  kCausal: the block's first token is at key position key0 and
-// this lane's column may see positions lo .. limit only.
-template <typename E, int D, bool kTail, bool kCausal = false>
-__device__ __forceinline__ void compute_block(const MfmaFrag<E, D>& f,
-                                              const bf16x8_t (&qop)[MfmaShape<D>::KI],
-                                              MfmaState<D>& st, int nfirst, int nvalid,
-                                              float scale_log2, int lane, int key0 = 0,
-                                              int lo = 0, int limit = 0) {
+// tile tt's lane column may see positions lo[tt] .. limit[tt] only.
+template <typename E, int D, bool kTail, bool kCausal, int kT>
+__device__ __forceinline__ void compute_block_tiles(const MfmaFrag<E, D>& f,
+                                                    const bf16x8_t (*qop)[MfmaShape<D>::KI],
+                                                    MfmaState<D>* st, int nfirst, int nvalid,
+                                                    float scale_log2, int lane, int key0,
+                                                    const int* lo, const int* limit) {
   const int q = lane >> 4;
-  floatx4_t s = {0.f, 0.f, 0.f, 0.f};
+  floatx4_t s[kT];
 #pragma unroll
-  for (int i = 0; i < MfmaShape<D>::KI; ++i)
-    s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand<E, D>(f, i), qop[i], s, 0, 0, 0);
+  for (int tt = 0; tt < kT; ++tt) s[tt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < MfmaShape<D>::KI; ++i) {
+    const bf16x8_t kop = k_operand<E, D>(f, i);
+#pragma unroll
+    for (int tt = 0; tt < kT; ++tt)
+      s[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[tt][i], s[tt], 0, 0, 0);
+  }
   constexpr bool kInt8 = E::kKind == Kind::kInt8;
   // sc[j]: the score of token 4q + j in base 2, -inf where masked (by select:
   // the slot may hold NaN).  Without per-token scales the multiply by
   // scale_log2 is folded into the exponent's argument below, and the block
   // maximum scaled once (scale_log2 > 0, so max and rounding commute).
-  float sc[4];
-  bool masked[4];
+  float sc[kT][4];
+  bool masked[kT][4];
+  float lmax[kT];
+  bool exceeds = false;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    sc[j] = s[j];
-    if constexpr (kInt8) {  // token 4q + j's K row scale
-      const uint32_t ks[4] = {f.ks.x, f.ks.y, f.ks.z, f.ks.w};
-      sc[j] = sc[j] * scale_log2 * __uint_as_float(ks[j]);
+  for (int tt = 0; tt < kT; ++tt) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      sc[tt][j] = s[tt][j];
+      if constexpr (kInt8) {  // token 4q + j's K row scale
+        const uint32_t ks[4] = {f.ks.x, f.ks.y, f.ks.z, f.ks.w};
+        sc[tt][j] = sc[tt][j] * scale_log2 * __uint_as_float(ks[j]);
+      }
+      masked[tt][j] = (kTail && (4 * q + j >= nvalid || 4 * q + j < nfirst)) ||
+                      (kCausal && (key0 + 4 * q + j > limit[tt] || key0 + 4 * q + j < lo[tt]));
+      if (masked[tt][j]) sc[tt][j] = -INFINITY;
     }
-    masked[j] = (kTail && (4 * q + j >= nvalid || 4 * q + j < nfirst)) ||
-                (kCausal && (key0 + 4 * q + j > limit || key0 + 4 * q + j < lo));
-    if (masked[j]) sc[j] = -INFINITY;
+    // (maximum, not fmaxf: gfx950's v_maximum3_f32 needs no NaN quieting of
+    // the matrix-core results; a NaN score makes its column NaN either way)
+    lmax[tt] = __builtin_elementwise_maximum(__builtin_elementwise_maximum(sc[tt][0], sc[tt][1]),
+                                             __builtin_elementwise_maximum(sc[tt][2], sc[tt][3]));
+    if constexpr (!kInt8) lmax[tt] *= scale_log2;
+    exceeds = exceeds || lmax[tt] > st[tt].m + kRescaleSlack;
   }
-  // (maximum, not fmaxf: gfx950's v_maximum3_f32 needs no NaN quieting of
-  // the matrix-core results; a NaN score makes its column NaN either way)
-  float lmax = __builtin_elementwise_maximum(__builtin_elementwise_maximum(sc[0], sc[1]),
-                                             __builtin_elementwise_maximum(sc[2], sc[3]));
-  if constexpr (!kInt8) lmax *= scale_log2;
   // The reference max st.m moves only when a head's block max exceeds it by
   // more than kRescaleSlack (base-2 units), so weights 2^(s - m) stay below 2^8
   // and most blocks skip rescaling O (32 multiplies at d = 128).  Softmax does
   // not depend on the reference, so only rounding changes.  The column's max
   // over its four lanes is needed only when one of them exceeds the reference
   // by that much, so the wave first asks whether any lane's own max does.
-  if (__builtin_amdgcn_ballot_w64(lmax > st.m + kRescaleSlack) != 0) {  // wave-uniform
-    const float mx = cross_row_max(lmax);
-    const bool grow = mx > st.m + kRescaleSlack;
-    // Only growing columns rescale.  The others keep factor 1: a column that
-    // has seen no key yet (m = -inf, possible under causal and window masks)
-    // would otherwise get 2^(-inf - -inf) = NaN.
-    const float alpha = grow ? fast_exp2(st.m - mx) : 1.f;
-    st.l *= alpha;
+  if (__builtin_amdgcn_ballot_w64(exceeds) != 0) {  // wave-uniform
 #pragma unroll
-    for (int mc = 0; mc < MfmaShape<D>::MC; ++mc) st.o[mc] *= alpha;
-    st.m = grow ? mx : st.m;
+    for (int tt = 0; tt < kT; ++tt) {
+      const float mx = cross_row_max(lmax[tt]);
+      const bool grow = mx > st[tt].m + kRescaleSlack;
+      // Only growing columns rescale.  The others keep factor 1 (exact): a
+      // column that has seen no key yet (m = -inf, possible under causal and
+      // window masks) would otherwise get 2^(-inf - -inf) = NaN.
+      const float alpha = grow ? fast_exp2(st[tt].m - mx) : 1.f;
+      st[tt].l *= alpha;
+#pragma unroll
+      for (int mc = 0; mc < MfmaShape<D>::MC; ++mc) st[tt].o[mc] *= alpha;
+      st[tt].m = grow ? mx : st[tt].m;
+    }
   }
   // weights rounded to bf16 for the matrix core; the denominator sums the
   // same rounded values.  Causal: a column that has seen no position yet
   // (every score -inf) takes weight 0, not 2^(-inf - -inf).
-  const float mref = (kCausal && st.m == -INFINITY) ? 0.f : st.m;
-  float pw[4];
+  short4_t pop[kT];
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
-    pw[j] = kInt8 ? fast_exp2(sc[j] - mref) : fast_exp2(__builtin_fmaf(sc[j], scale_log2, -mref));
-  const uint32_t p01 = pack_bf16x2(pw[0], pw[1]);
-  const uint32_t p23 = pack_bf16x2(pw[2], pw[3]);
-  // the rounded weights summed by two packed dot products with ones (the
-  // bf16 products are exact in fp32)
-  constexpr uint32_t kOnes = 0x3F803F80u;  // two bf16 1.0
-  st.l = dot2_bf16(p23, kOnes, dot2_bf16(p01, kOnes, st.l));
-  uint32_t q01 = p01, q23 = p23;
-  if constexpr (kInt8) {
-    // the products take p times the token's V row scale (0 where masked: the
-    // scale may be NaN there); the denominator above sums p alone
-    const uint32_t vs[4] = {f.vs.x, f.vs.y, f.vs.z, f.vs.w};
-    float pv[4];
+  for (int tt = 0; tt < kT; ++tt) {
+    const float mref = (kCausal && st[tt].m == -INFINITY) ? 0.f : st[tt].m;
+    float pw[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) pv[j] = masked[j] ? 0.f : pw[j] * __uint_as_float(vs[j]);
-    q01 = pack_bf16x2(pv[0], pv[1]);
-    q23 = pack_bf16x2(pv[2], pv[3]);
+    for (int j = 0; j < 4; ++j)
+      pw[j] = kInt8 ? fast_exp2(sc[tt][j] - mref)
+                    : fast_exp2(__builtin_fmaf(sc[tt][j], scale_log2, -mref));
+    const uint32_t p01 = pack_bf16x2(pw[0], pw[1]);
+    const uint32_t p23 = pack_bf16x2(pw[2], pw[3]);
+    // the rounded weights summed by two packed dot products with ones (the
+    // bf16 products are exact in fp32)
+    constexpr uint32_t kOnes = 0x3F803F80u;  // two bf16 1.0
+    st[tt].l = dot2_bf16(p23, kOnes, dot2_bf16(p01, kOnes, st[tt].l));
+    uint32_t q01 = p01, q23 = p23;
+    if constexpr (kInt8) {
+      // the products take p times the token's V row scale (0 where masked:
+      // the scale may be NaN there); the denominator above sums p alone
+      const uint32_t vs[4] = {f.vs.x, f.vs.y, f.vs.z, f.vs.w};
+      float pv[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) pv[j] = masked[tt][j] ? 0.f : pw[j] * __uint_as_float(vs[j]);
+      q01 = pack_bf16x2(pv[0], pv[1]);
+      q23 = pack_bf16x2(pv[2], pv[3]);
+    }
+    pop[tt] = __builtin_bit_cast(short4_t, make_uint2(q01, q23));
   }
-  const short4_t pop = __builtin_bit_cast(short4_t, make_uint2(q01, q23));
 #pragma unroll
   for (int mc = 0; mc < MfmaShape<D>::MC; ++mc) {
     uint2 v = v_operand<E, D>(f, mc);
@@ -233,11 +256,23 @@ __device__ __forceinline__ void compute_block(const MfmaFrag<E, D>& f,
       v.y = zero_masked_pair(v.y, t + 2 >= nfirst && t + 2 < nvalid,
                              t + 3 >= nfirst && t + 3 < nvalid);
     }
-    st.o[mc] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(short4_t, v), pop,
-                                                        st.o[mc], 0, 0, 0);
+#pragma unroll
+    for (int tt = 0; tt < kT; ++tt)
+      st[tt].o[mc] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+          __builtin_bit_cast(short4_t, v), pop[tt], st[tt].o[mc], 0, 0, 0);
   }
 }
 
+// compute_block_tiles for one column tile.
+template <typename E, int D, bool kTail, bool kCausal = false>
+__device__ __forceinline__ void compute_block(const MfmaFrag<E, D>& f,
+                                              const bf16x8_t (&qop)[MfmaShape<D>::KI],
+                                              MfmaState<D>& st, int nfirst, int nvalid,
+                                              float scale_log2, int lane, int key0 = 0,
+                                              int lo = 0, int limit = 0) {
+  compute_block_tiles<E, D, kTail, kCausal, 1>(f, &qop, &st, nfirst, nvalid, scale_log2, lane,
+                                               key0, &lo, &limit);
+}
 
 // Work-group barrier for data exchanged through LDS only: this wave's LDS
 // operations complete (lgkmcnt 0; the gfx9 s_waitcnt encoding with vmcnt and

@@ -232,6 +232,19 @@ constexpr int vm_wait_imm(int n) {
   return (n & 0xF) | (((n >> 4) & 3) << 14) | (7 << 4) | (0xF << 8);
 }
 
+// Wait until at most min(later, L) blocks of kPer loads each are still in
+// flight (later is uniform; s_waitcnt takes only an immediate count).
+template <int L, int kPer>
+__device__ __forceinline__ void wait_vm_later(int later) {
+  if constexpr (L == 0) {
+    __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
+  } else {
+    static_assert(L * kPer < 64, "vmcnt holds 6 bits");
+    if (later >= L) __builtin_amdgcn_s_waitcnt(vm_wait_imm(L * kPer));
+    else wait_vm_later<L - 1, kPer>(later);
+  }
+}
+
 // Byte offset of an LDS object (the low 32 bits of its generic address).
 __device__ __forceinline__ uint32_t lds_offset(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
@@ -425,9 +438,7 @@ __global__ __launch_bounds__(kMultiWaves* kWave, 2) void chunk_mfma_kernel(Multi
   // vector-memory operations of this wave per block
   constexpr int kPerWave = kPer;
   auto wait_block = [&](int later_blocks) {  // block j landed: later blocks may still run
-    if (later_blocks >= 2) __builtin_amdgcn_s_waitcnt(vm_wait_imm(2 * kPerWave));
-    else if (later_blocks == 1) __builtin_amdgcn_s_waitcnt(vm_wait_imm(kPerWave));
-    else __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
+    wait_vm_later<kStages - 2, kPerWave>(later_blocks);
   };
 
   // the query operands are in registers before any block load is issued
@@ -468,22 +479,24 @@ __global__ __launch_bounds__(kMultiWaves* kWave, 2) void chunk_mfma_kernel(Multi
         const int nfirst = klo - key0;
         const bool open =
             nvalid >= kBlockTokens && key0 + kBlockTokens - 1 <= kmin && key0 >= klo_max;
-        // The branch encloses the tile loop, so the masked path's work (the V
+        // The branch encloses the tiles' work, so the masked path's (the V
         // operands' masking, shared by the tiles) stays inside it instead of
-        // being computed ahead of the branch for every block.
-        if (open) {
-#pragma unroll
-          for (int tt = 0; tt < kTiles; ++tt) {
-            if (tt > 0 && tt >= ntiles) break;
-            compute_block<E, D, false>(f, qop[tt], st[tt], 0, nvalid, a.scale_log2, lane);
-          }
+        // being computed ahead of the branch for every block.  Both tiles run
+        // phase by phase in one pass; a set with one tile of columns runs one.
+        if (ntiles == kTiles) {
+          if (open)
+            compute_block_tiles<E, D, false, false, kTiles>(f, qop, st, 0, nvalid, a.scale_log2,
+                                                            lane, 0, lo, limit);
+          else
+            compute_block_tiles<E, D, true, true, kTiles>(f, qop, st, nfirst, nvalid,
+                                                          a.scale_log2, lane, key0, lo, limit);
         } else {
-#pragma unroll
-          for (int tt = 0; tt < kTiles; ++tt) {
-            if (tt > 0 && tt >= ntiles) break;
-            compute_block<E, D, true, true>(f, qop[tt], st[tt], nfirst, nvalid, a.scale_log2,
-                                            lane, key0, lo[tt], limit[tt]);
-          }
+          if (open)
+            compute_block_tiles<E, D, false, false, 1>(f, qop, st, 0, nvalid, a.scale_log2, lane,
+                                                       0, lo, limit);
+          else
+            compute_block_tiles<E, D, true, true, 1>(f, qop, st, nfirst, nvalid, a.scale_log2,
+                                                     lane, key0, lo, limit);
         }
       }
     }
