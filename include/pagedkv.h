@@ -286,8 +286,9 @@ kv_status paged_attention_reduce_window(void* out, const void* workspace,
  * with K_b, V_b read through the block table as in paged_attention_decode;
  * out: device [num_rows][H][d], bf16 (rounded to nearest-even).  n_b = 1 is
  * the decode step.  Matrix-core kernel for every H / H_kv, bf16, fp8 or int8
- * pools (KV_F32 is refused).  scale: finite and > 0, as for the decode.  max_query_len: a host bound on every n_b.  Rows of a
- * sequence with n_b > ctx_b, n_b > max_query_len or ctx_b > max_nb*16 are NaN
+ * pools (KV_F32 is refused).  scale: finite and > 0, as for the decode.
+ * max_query_len: a host bound on every n_b.  Rows of a sequence with
+ * n_b > ctx_b, n_b > max_query_len or ctx_b > max_nb*16 are NaN
  * (those below max_query_len; nothing is written past it).  A table entry
  * outside the pool that a row's range reaches makes that row NaN (and may make
  * other rows of its sequence NaN).  n_b <= 0 writes nothing, and a sequence

@@ -250,6 +250,22 @@ __device__ __forceinline__ uint32_t lds_offset(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
 }
 
+// An int8 block's row scales from its LDS stage, where they follow the two
+// tiles (K's 16, then V's); lane q takes those of tokens 4q..4q+3.
+template <typename E, int D>
+__device__ __forceinline__ void load_scales_lds_asm(MfmaFrag<E, D>& f, uint32_t base, int lane) {
+  constexpr int kTileBytes = kBlockTokens * D;
+  const uint32_t sa = base + 2 * kTileBytes + uint32_t(lane >> 4) * 16;
+  u32x4_t ks, vs;
+  __asm__ volatile("ds_read_b128 %0, %1" : "=v"(ks) : "v"(sa));
+  __asm__ volatile("ds_read_b128 %0, %1 offset:64" : "=v"(vs) : "v"(sa));
+  __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __asm__ volatile("" : "+v"(ks));
+  __asm__ volatile("" : "+v"(vs));
+  f.ks = make_uint4(ks.x, ks.y, ks.z, ks.w);
+  f.vs = make_uint4(vs.x, vs.y, vs.z, vs.w);
+}
+
 // load_block_lds with the LDS reads written out, then one wait for all of
 // them.  The compiler does not see these reads as LDS accesses, so it does
 // not order them after the in-flight global-to-LDS loads of later blocks
@@ -305,8 +321,10 @@ __device__ __forceinline__ void load_block_lds_asm(MfmaFrag<E, D>& f, uint32_t b
 }
 
 // Several column sets per sequence and KV head (a prefill chunk, or draft
-// verification with two sets of a bf16 pool).  Each wave owns one 32-column
-// set and walks every block its columns see; the waves of a work-group need
+// verification with 33..64 columns).  Each wave owns one set of 16 * kTiles
+// columns (kTiles = 2 for prefill chunks, 1 for verification: three
+// work-groups per CU) and walks every block its columns see; the waves of a
+// work-group need
 // nearly the same blocks (their positions differ by at most 128 / g tokens),
 // so the work-group loads each block once, cooperatively, into a 4-stage LDS
 // ring (direct global-to-LDS loads, three blocks ahead), and every wave reads
@@ -314,17 +332,29 @@ __device__ __forceinline__ void load_block_lds_asm(MfmaFrag<E, D>& f, uint32_t b
 // The K/V of a sequence is read by all of its work-groups, so these loads are
 // ordinary (cached) ones.  No partial results meet: a wave finishes its own
 // columns.
-template <typename E, int D>
-__global__ __launch_bounds__(kMultiWaves* kWave, 2) void chunk_mfma_kernel(MultiArgs a) {
+template <typename E, int D, int kTiles>
+__global__ __launch_bounds__(kMultiWaves* kWave, kTiles == 1 ? 3 : 2) void chunk_mfma_kernel(
+    MultiArgs a) {
   using S = typename E::storage;
   constexpr int KI = MfmaShape<D>::KI;
   constexpr int MC = MfmaShape<D>::MC;
-  constexpr int kTiles = 2;
   constexpr int kSetCols = kHeadsPerTile * kTiles;
   constexpr int kThreads = kMultiWaves * kWave;
   constexpr int kTileElems = kBlockTokens * D;
-  constexpr int kUnits = 2 * kTileElems * int(sizeof(S)) / 16;  // 16-byte units: K tile, V tile
-  constexpr int kPer = (kUnits + kThreads - 1) / kThreads;        // loads per thread per block
+  constexpr bool kInt8 = E::kKind == Kind::kInt8;
+  constexpr int kTileUnits = kTileElems * int(sizeof(S)) / 16;    // 16-byte units of one tile
+  // a stage: K tile, V tile, and for int8 the 16 K then 16 V row scales
+  constexpr int kScaleUnits = kBlockTokens * int(sizeof(float)) / 16;  // per tile
+  constexpr int kUnits = 2 * kTileUnits + (kInt8 ? 2 * kScaleUnits : 0);
+  // bf16 / fp8: wave w loads units 64w + kThreads k.  int8: wave w loads
+  // code units kCodeUnits w .. + kCodeUnits - 1 (all K or all V), then two of
+  // the eight scale units (waves 0, 1 K's, waves 2, 3 V's), so every wave
+  // issues the same number of loads per block.
+  constexpr int kCodeUnits = 2 * kTileUnits / kMultiWaves;
+  static_assert(kTileUnits % kCodeUnits == 0 && kScaleUnits == kMultiWaves, "int8 stage split");
+  static_assert(!kInt8 || kTiles == 1, "int8: one tile per wave (two do not fit 256 VGPRs)");
+  constexpr int kPer = kInt8 ? (kCodeUnits + kWave - 1) / kWave + 1
+                             : (kUnits + kThreads - 1) / kThreads;  // loads per thread per block
   constexpr int kStages = 4;
   constexpr int kTabWin = 1024;
   __shared__ uint4 sm_kv[kStages][kUnits];
@@ -415,22 +445,45 @@ __global__ __launch_bounds__(kMultiWaves* kWave, 2) void chunk_mfma_kernel(Multi
   // Block j's two tiles arrive in LDS by direct global-to-LDS loads
   // (global_load_lds_dwordx4: lane i of a wave writes 16 bytes at the wave's
   // LDS address + 16 i), kStages - 1 blocks ahead of the block computing, so
-  // several blocks are in flight without holding registers.  Unit u = 64 w +
-  // lane + kThreads k of a block: K tile units first, then V (uniform per
-  // wave).
+  // several blocks are in flight without holding registers.  A stage holds
+  // the K tile's units, then V's (then, for int8, the row scales); the units
+  // of one wave-wide load are all K, all V or all scales of one tile.
   auto issue = [&](int j, int p) -> bool {
     const bool ok = p >= 0 && p < a.num_blocks;
     const int64_t tile = (int64_t(ok ? p : 0) * a.num_kv_heads + kvh) * kTileBytes;
     uint4* ring = &sm_kv[j % kStages][0];
+    if constexpr (kInt8) {
+      // the tile's 16 row scales: floats 16 (p H_kv + kvh) .. of the scale region
+      const int64_t pt = int64_t(ok ? p : 0) * a.num_kv_heads + kvh;
+      const int cu0 = w * kCodeUnits;  // uniform: all K or all V
+      const char* src = (cu0 < kTileUnits ? kc : vc) + pt * kTileBytes +
+                        int64_t((cu0 % kTileUnits) + lane) * 16;
 #pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-      const int u0 = w * kWave + k * kThreads;  // uniform
-      if (u0 < kUnits) {
-        const int u = u0 + lane;
-        const char* src = u0 < kUnits / 2 ? kc + tile + int64_t(u) * 16
-                                          : vc + tile + int64_t(u - kUnits / 2) * 16;
-        __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(ring + u0),
-                                         16, 0, 0);
+      for (int k = 0; k < kPer - 1; ++k)
+        if (lane < kCodeUnits - k * kWave)  // d = 64: half a wave-load
+          __builtin_amdgcn_global_load_lds(
+              src + k * kWave * 16,
+              (__attribute__((address_space(3))) void*)(ring + cu0 + k * kWave), 16, 0, 0);
+      const int su0 = 2 * w;  // scale units su0, su0 + 1: 0..3 K's, 4..7 V's
+      const char* ssrc = (w < kMultiWaves / 2 ? kc : vc) + a.scales_offset +
+                         pt * kBlockTokens * int64_t(sizeof(float)) +
+                         ((su0 % kScaleUnits) + lane) * 16;
+      if (lane < 2)
+        __builtin_amdgcn_global_load_lds(
+            ssrc, (__attribute__((address_space(3))) void*)(ring + 2 * kTileUnits + su0), 16, 0,
+            0);
+    } else {
+#pragma unroll
+      for (int k = 0; k < kPer; ++k) {
+        const int u0 = w * kWave + k * kThreads;  // uniform
+        if (u0 < kUnits) {
+          const int u = u0 + lane;
+          const char* src = u0 < kUnits / 2 ? kc + tile + int64_t(u) * 16
+                                            : vc + tile + int64_t(u - kUnits / 2) * 16;
+          __builtin_amdgcn_global_load_lds(src,
+                                           (__attribute__((address_space(3))) void*)(ring + u0),
+                                           16, 0, 0);
+        }
       }
     }
     return ok;
@@ -474,7 +527,9 @@ __global__ __launch_bounds__(kMultiWaves* kWave, 2) void chunk_mfma_kernel(Multi
         bad = 1;
       } else {
         MfmaFrag<E, D> f;
-        load_block_lds_asm<E, D>(f, lds_offset(&sm_kv[j % kStages][0]), lane);
+        const uint32_t stage = lds_offset(&sm_kv[j % kStages][0]);
+        load_block_lds_asm<E, D>(f, stage, lane);
+        if constexpr (kInt8) load_scales_lds_asm<E, D>(f, stage, lane);
         const int nvalid = kend - key0;
         const int nfirst = klo - key0;
         const bool open =
@@ -483,7 +538,7 @@ __global__ __launch_bounds__(kMultiWaves* kWave, 2) void chunk_mfma_kernel(Multi
         // operands' masking, shared by the tiles) stays inside it instead of
         // being computed ahead of the branch for every block.  Both tiles run
         // phase by phase in one pass; a set with one tile of columns runs one.
-        if (ntiles == kTiles) {
+        if (kTiles == 1 || ntiles == kTiles) {
           if (open)
             compute_block_tiles<E, D, false, false, kTiles>(f, qop, st, 0, nvalid, a.scale_log2,
                                                             lane, 0, lo, limit);
@@ -523,10 +578,10 @@ __global__ __launch_bounds__(kMultiWaves* kWave, 2) void chunk_mfma_kernel(Multi
   }
 }
 
-template <typename E>
+template <typename E, int kTiles>
 void (*chunk_kernel(int head_dim))(MultiArgs) {
-  if (head_dim == 128) return chunk_mfma_kernel<E, 128>;
-  if (head_dim == 64) return chunk_mfma_kernel<E, 64>;
+  if (head_dim == 128) return chunk_mfma_kernel<E, 128, kTiles>;
+  if (head_dim == 64) return chunk_mfma_kernel<E, 64, kTiles>;
   return nullptr;
 }
 
@@ -551,25 +606,37 @@ hipError_t launch_multi_mfma(const MultiArgs& a, Kind kind, int head_dim, hipStr
   const int g = a.H / a.num_kv_heads;
   const int64_t set_cols = int64_t(kHeadsPerTile) * a.tiles_per_set;
   const int64_t sets = (int64_t(a.max_query_len) * g + set_cols - 1) / set_cols;
-  // The LDS-staged long-chunk kernel loads each block once for all sets of a
-  // work-group.  Measured against the per-wave kernel: 21% faster on
-  // 512-token prefill chunks of a bf16 pool and 11% for fp8; with two sets
-  // (draft verification, g * K of 33..64 columns) 7-25% faster for bf16 but
-  // 50% slower for fp8, whose conversions make the two computing waves the
-  // bottleneck, so fp8 takes it from four sets on.
-  const bool chunk = a.tiles_per_set == 2 &&
+  // The LDS-staged kernel loads each block once for all columns of a
+  // work-group.  Measured against the per-wave kernel: 21% faster on 512-token
+  // prefill chunks of a bf16 pool and 11% for fp8 (two tiles per wave, four
+  // sets).  With 3 or 4 tiles of columns (draft verification with g * K of
+  // 33..64) each of the four waves takes one tile (148 VGPRs: three
+  // work-groups per CU): against two waves with two tiles each, 12% faster for
+  // bf16 at K = 8, g = 8, and against the per-wave kernel 11-22% faster for
+  // fp8 and 2-10% for int8 (whose stages add the row scales).  One tile per
+  // wave measured slower with two tiles of columns (8%, bf16) and on fp8
+  // prefill chunks (2.5%), and equal on bf16 and int8 prefill chunks.
+  const int64_t tiles = (int64_t(a.max_query_len) * g + kHeadsPerTile - 1) / kHeadsPerTile;
+  const bool chunk1 = tiles >= 3 && tiles <= kMultiWaves;
+  const bool chunk = !chunk1 && a.tiles_per_set == 2 &&
                      ((kind == Kind::kBf16 && sets >= 2) ||
                       (kind == Kind::kFp8 && sets >= kMultiWaves));
+  const bool bf16 = kind == Kind::kBf16;
   void (*kern)(MultiArgs) =
-      chunk ? (kind == Kind::kBf16 ? chunk_kernel<Bf16>(head_dim) : chunk_kernel<Fp8>(head_dim))
-            : (kind == Kind::kBf16   ? multi_kernel<Bf16>(head_dim, a.tiles_per_set)
-               : kind == Kind::kFp8  ? multi_kernel<Fp8>(head_dim, a.tiles_per_set)
-               : kind == Kind::kInt8 ? multi_kernel<Int8>(head_dim, a.tiles_per_set)
-                                     : nullptr);
+      chunk1  ? (bf16                 ? chunk_kernel<Bf16, 1>(head_dim)
+                 : kind == Kind::kFp8 ? chunk_kernel<Fp8, 1>(head_dim)
+                 : kind == Kind::kInt8 ? chunk_kernel<Int8, 1>(head_dim)
+                                       : nullptr)
+      : chunk ? (bf16 ? chunk_kernel<Bf16, 2>(head_dim) : chunk_kernel<Fp8, 2>(head_dim))
+              : (bf16                  ? multi_kernel<Bf16>(head_dim, a.tiles_per_set)
+                 : kind == Kind::kFp8  ? multi_kernel<Fp8>(head_dim, a.tiles_per_set)
+                 : kind == Kind::kInt8 ? multi_kernel<Int8>(head_dim, a.tiles_per_set)
+                                       : nullptr);
   if (!kern) return hipErrorInvalidValue;
   if (a.B == 0 || a.max_query_len == 0) return hipSuccess;
-  const int64_t per_group = chunk ? kMultiWaves : a.sets_per_group;
-  const int64_t groups = (sets + per_group - 1) / per_group;
+  const int64_t per_group = chunk1 || chunk ? kMultiWaves : a.sets_per_group;
+  const int64_t groups =
+      chunk1 ? (tiles + kMultiWaves - 1) / kMultiWaves : (sets + per_group - 1) / per_group;
   hipLaunchKernelGGL(kern, dim3(unsigned(groups), unsigned(a.num_kv_heads), unsigned(a.B)),
                      dim3(kMultiWaves * kWave), 0, s, a);
   return hipGetLastError();
