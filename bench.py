@@ -650,7 +650,7 @@ def multi(args) -> int:
 def main(argv=None) -> int:
     args = parse_args(argv)
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+        print(f"bench.py: the benchmark runs on one GPU; --gpus {args.gpus} is not supported "
               "(sequences, KV heads and context partitions shard without exchange, but no "
               "multi-GPU path is built)", file=sys.stderr)
         return 2

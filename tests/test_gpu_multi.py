@@ -202,7 +202,7 @@ def test_bad_lengths_tables_and_rows_are_contained():
     assert np.all(np.isfinite(O.bits_to_f64(got[rows(0)], "bf16")))
 
 
-@pytest.mark.parametrize("kv_dtype", ["", "fp8"])
+@pytest.mark.parametrize("kv_dtype", ["", "fp8", "int8"])
 @pytest.mark.parametrize("config,K", [(2, 4), (3, 4), (3, 8)])
 def test_full_size_draft_verification(config, K, kv_dtype):
     """Draft verification at the full shapes of the 7B-like batch-64 and the GQA
