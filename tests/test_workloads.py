@@ -1,6 +1,7 @@
 """The seeded input generators: determinism, shapes and the recipes' structure."""
 import numpy as np
 import pytest
+import torch
 
 from workloads import configs as W
 
@@ -8,7 +9,7 @@ from workloads import configs as W
 def test_bf16_rounding_is_nearest_even():
     x = np.array([1.0, 1.00390625, 1.005859375, 1.0078125 + 2**-8, -2.5], dtype=np.float32)
     bits = W.f32_to_bf16_bits(x)
-    back = (bits.astype(np.uint32) << 16).view(np.float32)
+    back = torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16).float().numpy()
     # 1 + 2^-8 and 1 + 3*2^-8 are ties: the even mantissa wins (1.0, then 1 + 2^-6)
     np.testing.assert_array_equal(back, np.array([1.0, 1.0, 1.0078125, 1.015625, -2.5], np.float32))
 
