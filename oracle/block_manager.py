@@ -17,15 +17,24 @@ stack, reference counts):
     from the start of the prompt and takes fresh blocks for the rest; a cached
     block that was released but not yet reused is taken back out of the free
     queue;
-  * taking a block pops the front of the free queue (the least recently freed)
-    and drops the cache entry the block still carried;
+  * taking a block takes the least recently freed one and drops the cache
+    entry the block still carried;
   * appending a token opens a fresh block when the last one is full, and copies
     the last block first when it is shared (copy-on-write): a shared block is
     never written;
   * forking gives the child the parent's table, every block's count + 1;
   * releasing drops one reference from each block, last block first; a block
-    whose count reaches zero joins the back of the free queue and keeps its
+    whose count reaches zero becomes the most recently freed one and keeps its
     cache entry until it is taken again.
+
+Form.  The state is a set of plain arrays indexed by block id (reference
+count, contents, key, and the time at which a block was last freed, absent
+while it is referenced) plus the prefix index and the tables.  The free queue
+is not stored as a list: the free blocks are those with a free-time, taken in
+increasing free-time order.  Every operation first derives the complete change
+it would make (which blocks it revives, takes, and what it writes), checks it
+against the free count, and only then applies it, so a failed operation
+leaves the state untouched by construction.
 
 Readings where the page is silent: an operation that needs more free blocks
 than there are fails with NoBlocks and changes nothing (the page's model raises
@@ -38,8 +47,7 @@ bookkeeping invariants (tests/test_block_manager.py).
 from __future__ import annotations
 
 import hashlib
-from collections import deque
-from typing import Dict, List, Optional, Tuple
+from typing import Dict, List, Optional, Sequence, Tuple
 
 BLOCK = 16
 
@@ -48,17 +56,7 @@ class NoBlocks(Exception):
     """Not enough free blocks for the operation (nothing was changed)."""
 
 
-class _Block:
-    __slots__ = ("id", "refs", "tokens", "key")
-
-    def __init__(self, bid: int):
-        self.id = bid
-        self.refs = 0
-        self.tokens: List[int] = []
-        self.key: Optional[bytes] = None
-
-
-def prefix_key(parent: Optional[bytes], tokens: List[int], salt: str) -> bytes:
+def prefix_key(parent: Optional[bytes], tokens: Sequence[int], salt: str) -> bytes:
     """Key of a full block: SHA-256 of the parent's key (the salt for a first
     block) followed by the block's token ids."""
     h = hashlib.sha256()
@@ -72,114 +70,136 @@ def prefix_key(parent: Optional[bytes], tokens: List[int], salt: str) -> bytes:
 
 class BlockManagerModel:
     def __init__(self, num_blocks: int):
-        self.blocks = [_Block(i) for i in range(num_blocks)]
-        self.free: deque = deque(self.blocks)         # front = taken first
-        self.cache: Dict[bytes, _Block] = {}
-        self.seqs: Dict[int, Tuple[List[_Block], str]] = {}
+        n = num_blocks
+        self.refcount: List[int] = [0] * n
+        self.content: List[Tuple[int, ...]] = [()] * n
+        self.key: List[Optional[bytes]] = [None] * n
+        # free-time of every unreferenced block (block i starts free at time i)
+        self.freed_at: Dict[int, int] = {i: i for i in range(n)}
+        self.clock = n
+        self.index: Dict[bytes, int] = {}          # prefix key -> block id
+        self.tables: Dict[int, List[int]] = {}
+        self.salt: Dict[int, str] = {}
 
-    # ---------------------------------------------------------------- helpers
-    def _take(self, tokens: List[int]) -> _Block:
-        b = self.free.popleft()
-        if b.key is not None and self.cache.get(b.key) is b:
-            del self.cache[b.key]
-        b.refs, b.tokens, b.key = 1, list(tokens), None
-        return b
+    # ------------------------------------------------------------ derived facts
+    def _key_of(self, table: List[int], pos: int, salt: str) -> Optional[bytes]:
+        """Key the block at table position `pos` gets if it is full."""
+        b = table[pos]
+        if len(self.content[b]) != BLOCK:
+            return None
+        parent = self.key[table[pos - 1]] if pos > 0 else None
+        return prefix_key(parent, self.content[b], salt)
 
-    def _seal(self, b: _Block, parent: Optional[bytes], salt: str) -> None:
-        if len(b.tokens) == BLOCK:
-            b.key = prefix_key(parent, b.tokens, salt)
-            self.cache.setdefault(b.key, b)
+    def _oldest_free(self, count: int, excluded=()) -> List[int]:
+        """The `count` least recently freed blocks, skipping `excluded`."""
+        order = sorted((t, b) for b, t in self.freed_at.items() if b not in excluded)
+        if len(order) < count:
+            raise NoBlocks
+        return [b for _, b in order[:count]]
 
-    def _plan_admit(self, prompt: List[int], salt: str):
-        """Cached blocks an admit would reuse (in order) and fresh blocks it needs."""
-        reuse: List[_Block] = []
-        parent = None
-        n_chunks = -(-len(prompt) // BLOCK)
-        for c in range(n_chunks):
-            chunk = prompt[c * BLOCK:(c + 1) * BLOCK]
-            if len(chunk) < BLOCK:
-                break
-            b = self.cache.get(prefix_key(parent, chunk, salt))
-            if b is None:
-                break
-            reuse.append(b)
-            parent = b.key
-        return reuse, n_chunks - len(reuse)
+    # ------------------------------------------------------------ state changes
+    def _reference(self, b: int) -> None:
+        self.freed_at.pop(b, None)
+        self.refcount[b] += 1
 
-    # ---------------------------------------------------------------- operations
+    def _unreference(self, b: int) -> None:
+        self.refcount[b] -= 1
+        if self.refcount[b] == 0:
+            self.freed_at[b] = self.clock
+            self.clock += 1
+
+    def _recycle(self, b: int, tokens: Tuple[int, ...]) -> None:
+        """Give free block b new contents: its old cache entry goes, it is held once."""
+        old = self.key[b]
+        if old is not None and self.index.get(old) == b:
+            del self.index[old]
+        self.key[b] = None
+        self.content[b] = tuple(tokens)
+        self._reference(b)
+
+    def _publish(self, table: List[int], pos: int, salt: str) -> None:
+        """Key a block that has just become full and enter it in the prefix index
+        (an existing entry for the same key is kept)."""
+        k = self._key_of(table, pos, salt)
+        if k is not None:
+            self.key[table[pos]] = k
+            self.index.setdefault(k, table[pos])
+
+    # ------------------------------------------------------------ operations
     def admit(self, seq: int, prompt: List[int], salt: str = "") -> int:
         """Build seq's table for a new prompt; return the prompt tokens found cached."""
-        if seq in self.seqs:
+        if seq in self.tables:
             raise ValueError(f"sequence {seq} exists")
-        reuse, fresh = self._plan_admit(prompt, salt)
-        revived = sum(1 for b in reuse if b.refs == 0)
-        if fresh > len(self.free) - revived:
-            raise NoBlocks
-        table: List[_Block] = []
-        for b in reuse:
-            if b.refs == 0:
-                self.free.remove(b)
-            b.refs += 1
+        chunks = [tuple(int(t) for t in prompt[i:i + BLOCK]) for i in range(0, len(prompt), BLOCK)]
+        # longest run of full leading chunks already in the prefix index
+        hits: List[int] = []
+        parent: Optional[bytes] = None
+        for chunk in chunks:
+            b = self.index.get(prefix_key(parent, chunk, salt)) if len(chunk) == BLOCK else None
+            if b is None:
+                break
+            hits.append(b)
+            parent = self.key[b]
+        fresh = self._oldest_free(len(chunks) - len(hits), excluded=set(hits))
+        # apply
+        for b in hits:
+            self._reference(b)
+        table = list(hits)
+        for chunk, b in zip(chunks[len(hits):], fresh):
+            self._recycle(b, chunk)
             table.append(b)
-        for c in range(len(reuse), len(reuse) + fresh):
-            chunk = prompt[c * BLOCK:(c + 1) * BLOCK]
-            b = self._take(chunk)
-            self._seal(b, table[-1].key if table else None, salt)
-            table.append(b)
-        self.seqs[seq] = (table, salt)
-        return len(reuse) * BLOCK
+            self._publish(table, len(table) - 1, salt)
+        self.tables[seq] = table
+        self.salt[seq] = salt
+        return len(hits) * BLOCK
 
     def append(self, seq: int, token: int):
         """Write one token.  Returns (slot, copy) where copy is (src, dst) when the
         shared last block was copied first, else None."""
-        table, salt = self.seqs[seq]
-        copy = None
+        table = self.tables[seq]
         last = table[-1] if table else None
-        if last is None or len(last.tokens) == BLOCK:
-            if not self.free:
-                raise NoBlocks
-            table.append(self._take([]))
-        elif last.refs > 1:
-            if not self.free:
-                raise NoBlocks
-            last.refs -= 1
-            nb = self._take(last.tokens)
-            copy = (last.id, nb.id)
-            table[-1] = nb
-        b = table[-1]
-        b.tokens.append(int(token))
-        self._seal(b, table[-2].key if len(table) > 1 else None, salt)
-        slot = b.id * BLOCK + len(b.tokens) - 1
-        return slot, copy
+        opens = last is None or len(self.content[last]) == BLOCK
+        copies = not opens and self.refcount[last] > 1
+        target = self._oldest_free(1)[0] if (opens or copies) else last
+        copy = None
+        if opens:
+            self._recycle(target, ())
+            table.append(target)
+        elif copies:
+            self._unreference(last)
+            self._recycle(target, self.content[last])
+            table[-1] = target
+            copy = (last, target)
+        self.content[target] = self.content[target] + (int(token),)
+        self._publish(table, len(table) - 1, self.salt[seq])
+        return target * BLOCK + len(self.content[target]) - 1, copy
 
     def fork(self, seq: int, child: int) -> None:
-        if child in self.seqs:
+        if child in self.tables:
             raise ValueError(f"sequence {child} exists")
-        table, salt = self.seqs[seq]
-        for b in table:
-            b.refs += 1
-        self.seqs[child] = (list(table), salt)
+        for b in self.tables[seq]:
+            self._reference(b)
+        self.tables[child] = list(self.tables[seq])
+        self.salt[child] = self.salt[seq]
 
     def release(self, seq: int) -> None:
-        table, _ = self.seqs.pop(seq)
-        for b in reversed(table):
-            b.refs -= 1
-            if b.refs == 0:
-                self.free.append(b)
+        table = self.tables.pop(seq)
+        self.salt.pop(seq)
+        for pos in range(len(table) - 1, -1, -1):
+            self._unreference(table[pos])
 
-    # ---------------------------------------------------------------- views
+    # ------------------------------------------------------------ views
     def num_free(self) -> int:
-        return len(self.free)
+        return len(self.freed_at)
 
     def table(self, seq: int) -> List[int]:
-        return [b.id for b in self.seqs[seq][0]]
+        return list(self.tables[seq])
 
     def num_tokens(self, seq: int) -> int:
-        t = self.seqs[seq][0]
-        return 0 if not t else (len(t) - 1) * BLOCK + len(t[-1].tokens)
+        return sum(len(self.content[b]) for b in self.tables[seq])
 
     def refs(self) -> List[int]:
-        return [b.refs for b in self.blocks]
+        return list(self.refcount)
 
     def free_order(self) -> List[int]:
-        return [b.id for b in self.free]
+        return [b for _, b in sorted((t, b) for b, t in self.freed_at.items())]

@@ -18,21 +18,21 @@ def test_demo_prints_the_page_values():
 
 
 def _check_invariants(m: BlockManagerModel, history):
-    refs = np.zeros(len(m.blocks), dtype=int)
-    for seq, (table, _) in m.seqs.items():
+    refs = np.zeros(len(m.refcount), dtype=int)
+    for seq, table in m.tables.items():
         for b in table:
-            refs[b.id] += 1
+            refs[b] += 1
         # the table holds exactly the sequence's tokens, in order
-        toks = [t for b in table for t in b.tokens]
+        toks = [t for b in table for t in m.content[b]]
         assert toks == history[seq], seq
         # every block but the last is full
-        assert all(len(b.tokens) == BLOCK for b in table[:-1])
+        assert all(len(m.content[b]) == BLOCK for b in table[:-1])
     assert refs.tolist() == m.refs()                 # counts = table references
     free = m.free_order()
     assert len(set(free)) == len(free)
     assert sorted(free) == [i for i, r in enumerate(refs) if r == 0]
-    for key, b in m.cache.items():                   # cache entries point at full blocks
-        assert b.key == key and len(b.tokens) == BLOCK
+    for key, b in m.index.items():                   # index entries point at full blocks
+        assert m.key[b] == key and len(m.content[b]) == BLOCK
 
 
 @pytest.mark.parametrize("seed", range(6))
@@ -42,7 +42,7 @@ def test_random_operations_keep_the_bookkeeping_consistent(seed, num_blocks):
     history = {}
     for op in random_ops(seed, 300):
         kind = op[0]
-        if kind == "admit" and op[1] not in m.seqs:
+        if kind == "admit" and op[1] not in m.tables:
             before = (m.free_order(), m.refs())
             try:
                 hits = m.admit(op[1], op[2], op[3])
@@ -51,9 +51,10 @@ def test_random_operations_keep_the_bookkeeping_consistent(seed, num_blocks):
                 continue
             assert hits % BLOCK == 0 and hits <= len(op[2])
             history[op[1]] = list(op[2])
-        elif kind == "append" and op[1] in m.seqs:
-            last = m.seqs[op[1]][0][-1] if m.seqs[op[1]][0] else None
-            shared = last is not None and last.refs > 1 and len(last.tokens) < BLOCK
+        elif kind == "append" and op[1] in m.tables:
+            table = m.tables[op[1]]
+            last = table[-1] if table else None
+            shared = last is not None and m.refcount[last] > 1 and len(m.content[last]) < BLOCK
             before = (m.free_order(), m.refs())
             try:
                 slot, copy = m.append(op[1], op[2])
@@ -68,10 +69,10 @@ def test_random_operations_keep_the_bookkeeping_consistent(seed, num_blocks):
             assert m.table(op[1])[-1] == slot // BLOCK
             if copy:
                 assert copy[1] == slot // BLOCK
-        elif kind == "fork" and op[1] in m.seqs and op[2] not in m.seqs:
+        elif kind == "fork" and op[1] in m.tables and op[2] not in m.tables:
             m.fork(op[1], op[2])
             history[op[2]] = list(history[op[1]])
-        elif kind == "release" and op[1] in m.seqs:
+        elif kind == "release" and op[1] in m.tables:
             m.release(op[1])
             history.pop(op[1])
         _check_invariants(m, history)
