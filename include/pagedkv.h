@@ -127,8 +127,15 @@ typedef struct kv_pool kv_pool; /* opaque host object; borrows the two caches */
 size_t kv_pool_bytes(const kv_pool_desc* desc);
 
 /* Wrap two caller-owned device buffers (each kv_pool_bytes(desc) bytes, 16-byte
- * aligned) as a pool.  Host metadata only; nothing is copied or cleared.
- * Returns KV_OK and *out on success. */
+ * aligned) as a pool: the fixed pool of 16-token blocks that every sequence's
+ * block table points into ("MLSys Engineer - Inference Systems Q&A", Q1: the
+ * cache is one pool of fixed blocks; "Anthropic Interview: Design an LLM
+ * Inference API with GPU Batching", Key concepts (Paged KV memory) and 4.1:
+ * the physical blocks are a preallocated pool, handed out by the host).  Host
+ * metadata only; nothing is copied or cleared.  Returns KV_OK and *out on
+ * success; a NULL pointer, an invalid descriptor (see kv_pool_desc) or a cache
+ * pointer not 16-byte aligned gives KV_ERR_INVALID_ARG or KV_ERR_UNSUPPORTED
+ * and leaves *out unchanged. */
 kv_status kv_pool_create(const kv_pool_desc* desc, void* k_cache, void* v_cache,
                          kv_pool** out);
 
@@ -195,14 +202,23 @@ kv_status kv_cache_append_chunk(const kv_pool* pool, const void* key, const void
                                 int32_t max_nb, const int32_t* context_lens, int32_t B,
                                 int64_t* slot_mapping, void* stream);
 
-/* Workspace bytes paged_attention_decode needs in split mode: with
+/* Workspace bytes paged_attention_decode needs in split mode, i.e. room for
+ * one partial result (o, m, l) per partition and query head: the running
+ * output, max and denominator that the Q&A page's Q4 keeps per query while it
+ * walks K/V tiles, here kept per partition so that partitions can run in
+ * parallel and be merged afterwards by the same rescale rule.  With
  * P = ceil(max_context_len / partition_size) partitions per sequence,
  *   o: float [B][H][P][d], then m: float [B][H][P], then l: float [B][H][P]
  * (each region 256-byte aligned).  0 when partition_size == 0. */
 size_t paged_attention_workspace_bytes(int32_t B, int32_t H, int32_t head_dim,
                                        int32_t max_context_len, int32_t partition_size);
 
-/* Decode attention for one new query token per sequence.
+/* Decode attention for one new query token per sequence: the attention half
+ * of the workbook's decode step ("LLM inference and serving", Code from
+ * memory: softmax(K q / sqrt(d)) V over every cached row, the new one
+ * included), with the rows read through the block table as the Q&A page's Q1
+ * describes, and computed as Q4's fused kernel computes it (online softmax,
+ * fp32 accumulation; scores never leave the chip):
  *   out[b][h][:] = softmax_t(scale * q[b][h] . K_b[t]) V_b[t], t < ctx_b,
  * where K_b[t], V_b[t] are read from block block_tables[b*max_nb + t/16],
  * slot t % 16 (ctx_b = context_lens[b], which includes the token written this
@@ -397,7 +413,12 @@ kv_status kv_bm_batch_tables(kv_block_manager* bm, const int64_t* seqs, int32_t 
  * 0 = vector-ALU kernel, 1 = matrix-core (MFMA) kernel, < 0 = unsupported. */
 int32_t kv_decode_kernel_kind(const kv_pool* pool, int32_t H);
 
-/* Message of the last failed call on this thread ("" if none). */
+/* Message of the last failed call on this thread ("" if none).  Argument
+ * errors are refused before anything is enqueued, rather than left to fail in
+ * the middle of a step ("Ch.29 Building a Production LLM Serving Stack",
+ * 29.1.2: admission refuses what the pool cannot hold instead of running out
+ * mid-step); this call says which check failed.  The string belongs to the
+ * library and stays valid until the thread's next failing call. */
 const char* kv_last_error(void);
 
 #ifdef __cplusplus

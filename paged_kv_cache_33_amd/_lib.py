@@ -95,7 +95,14 @@ def load() -> C.CDLL:
         raise RuntimeError(
             f"{LIB_PATH} is missing: build it with `python -m paged_kv_cache_33_amd.build` "
             "(there is no fallback implementation)")
-    lib = C.CDLL(LIB_PATH)
+    _lib = declare(C.CDLL(LIB_PATH))
+    return _lib
+
+
+def declare(lib: C.CDLL, names=None) -> C.CDLL:
+    """Set result and argument types of the C ABI's symbols on `lib` (all of
+    them, or only `names`: a host-only build of part of the library, such as
+    the block manager built with sanitizers, exports just those)."""
     vp, i32, i64p, i32p, sz = C.c_void_p, C.c_int32, C.POINTER(C.c_int64), C.c_void_p, C.c_size_t
     desc_p = C.POINTER(KVPoolDesc)
     sig = {
@@ -136,10 +143,11 @@ def load() -> C.CDLL:
         "kv_last_error": (C.c_char_p, []),
     }
     for name, (res, args) in sig.items():
+        if names is not None and name not in names:
+            continue
         fn = getattr(lib, name)
         fn.restype = res
         fn.argtypes = args
-    _lib = lib
     return lib
 
 

@@ -25,7 +25,7 @@ LIB = os.path.join(PKG, "libpagedkv.so")
 SOURCES = ["api.hip", "cache_write.hip", "decode_valu.hip", "decode_mfma.hip", "multi_mfma.hip",
            "read_tiles.hip",
            "reduce.hip"]
-HOST_SOURCES = ["block_manager.cpp"]  # host-only C++ (the block manager)
+HOST_SOURCES = ["block_manager.cpp", "errors.cpp"]  # host-only C++ (block manager, errors)
 ARCH = "gfx950"
 
 # Packed-fp32 instructions are kept out of every kernel: the compiler may not
@@ -88,6 +88,26 @@ def build(jobs: int = 0, verbose: bool = False) -> str:
     _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)
     return LIB
+
+
+SANITIZED_LIB = os.path.join(ROOT, "_build", "sanitize", "libpagedkv_host_asan.so")
+
+
+def build_sanitized(verbose: bool = False) -> str:
+    """The host-only part of the library (block manager and error reporting)
+    built by g++ with AddressSanitizer and UndefinedBehaviorSanitizer, for CPU
+    tests: load it in a process that preloads the ASan runtime."""
+    gxx = shutil.which("g++")
+    if gxx is None:
+        raise RuntimeError("g++ not found")
+    os.makedirs(os.path.dirname(SANITIZED_LIB), exist_ok=True)
+    tmp = SANITIZED_LIB + ".tmp"
+    _run([gxx, "-std=c++17", "-O1", "-g", "-fPIC", "-shared", "-Wall",
+          "-fsanitize=address,undefined", "-fno-omit-frame-pointer", "-fno-sanitize-recover=all",
+          f"-I{INCLUDE}", f"-I{CSRC}",
+          *[os.path.join(CSRC, s) for s in HOST_SOURCES], "-o", tmp], verbose)
+    os.replace(tmp, SANITIZED_LIB)
+    return SANITIZED_LIB
 
 
 def main(argv=None) -> int:

@@ -3,7 +3,6 @@
 #include <hip/hip_runtime.h>
 
 #include <cfloat>
-#include <cstdarg>
 #include <cstdio>
 #include <mutex>
 #include <new>
@@ -46,29 +45,6 @@ int resident_workers(const void* kernel, int threads, int tiles) {
   }
   const int per_tile = total / (tiles > 0 ? tiles : 1);
   return per_tile > 0 ? per_tile : 1;
-}
-
-}  // namespace pagedkv
-
-namespace {
-thread_local std::string g_last_error;
-}  // namespace
-
-namespace pagedkv {
-
-kv_status report(kv_status code, const char* fmt, ...) {
-  char buf[512];
-  va_list ap;
-  va_start(ap, fmt);
-  std::vsnprintf(buf, sizeof(buf), fmt, ap);
-  va_end(ap);
-  g_last_error = buf;
-  return code;
-}
-
-kv_status report_ok() {
-  g_last_error.clear();
-  return KV_OK;
 }
 
 }  // namespace pagedkv
@@ -532,7 +508,5 @@ kv_status paged_attention_reduce_window(void* out, const void* workspace,
   return reduce_impl(out, workspace, context_lens, B, H, head_dim, max_context_len, window,
                      partition_size, out_dtype, stream);
 }
-
-const char* kv_last_error(void) { return g_last_error.c_str(); }
 
 }  // extern "C"
