@@ -734,8 +734,13 @@ def main(argv=None) -> int:
             ev[3].record(stream)
 
     if args.decode_only:
+        # decode launches alone (for counter runs); with --cold each one follows
+        # a write of twice the last-level cache, so it starts from HBM
         s = steps_dev[0]
-        for _ in range(args.warmup + args.steps):
+        flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda") if args.cold else None
+        for i in range(args.warmup + args.steps):
+            if flush is not None:
+                flush.fill_(i & 0xFF)
             P.paged_attention_decode(pool, out, s["q"], tables, s["ctx"], L_max, w.scale, part,
                                      ws, stream, window=args.window)
         torch.cuda.synchronize()
@@ -789,7 +794,7 @@ def main(argv=None) -> int:
     gbs = step_b / (ms_step * 1e-3) / 1e9
     dec_gbs = dec_b / (dec_avg * 1e-3) / 1e9
     wname = w.name + (f"-window{args.window}" if args.window else "")
-    traffic = traffic_from_profile(kernel, wname)
+    traffic = traffic_from_profile(kernel, wname + ("-cold" if args.cold else ""))
     ceiling = read_ceiling(P, torch, pool, w, w.steps[0], args.window, stream)
     clocks = gpu_clocks(torch)
 
