@@ -409,6 +409,31 @@ kv_status kv_bm_table(kv_block_manager* bm, int64_t seq, int32_t* blocks, int32_
 kv_status kv_bm_batch_tables(kv_block_manager* bm, const int64_t* seqs, int32_t B, int32_t max_nb,
                              int32_t* tables, int32_t* context_lens);
 
+/* Bytes of device scratch the allocation-free decode below holds per GPU. */
+#define KV_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+/* paged_attention_decode followed by paged_attention_reduce, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): the split partials go to a
+ * library-held scratch array of KV_NOALLOC_SCRATCH_BYTES bytes per GPU (held
+ * from the first call on that GPU until the process ends) instead of a
+ * caller workspace.  The caller still passes inputs and outputs; the
+ * arguments mean what they mean for paged_attention_decode, and out receives
+ * the merged result.  partition_size == 0 is the single pass (no scratch
+ * used).  Split sizes whose partials exceed the scratch
+ * (paged_attention_workspace_bytes(B, H, head_dim, max_context_len,
+ * partition_size) > KV_NOALLOC_SCRATCH_BYTES) return KV_ERR_WORKSPACE before
+ * anything is enqueued.  No device memory is allocated or freed; nothing in
+ * the scratch needs to start cleared (every partial is written before it is
+ * read).  Every call on one GPU shares that GPU's scratch and leaves its
+ * partials there: calls that overlap on one GPU (other streams, other
+ * threads) race and give undefined results; calls in stream order do not. */
+kv_status paged_attention_decode_noalloc(const kv_pool* pool, void* out, const void* query,
+                                         const int32_t* block_tables, int32_t max_nb,
+                                         const int32_t* context_lens, int32_t B, int32_t H,
+                                         int32_t max_context_len, float scale,
+                                         int32_t partition_size, void* stream);
+
 /* Which decode kernel paged_attention_decode launches for this pool and H:
  * 0 = vector-ALU kernel, 1 = matrix-core (MFMA) kernel, < 0 = unsupported. */
 int32_t kv_decode_kernel_kind(const kv_pool* pool, int32_t H);

@@ -32,6 +32,7 @@ __all__ = [
     "paged_attention_workspace_bytes",
     "paged_attention_decode",
     "paged_attention_reduce",
+    "paged_attention_decode_noalloc",
     "paged_attention_multi",
     "kv_decode_kernel_kind",
     "kv_copy_blocks",
@@ -314,6 +315,27 @@ def paged_attention_decode(pool: KVPool, out: torch.Tensor, query: torch.Tensor,
         _lib.check(lib.paged_attention_decode(
             pool.handle, op, qp, tp, max_nb, cp, B, H, int(max_context_len), float(scale),
             int(partition_size), wp, wbytes, _stream_handle(stream)))
+
+
+def paged_attention_decode_noalloc(pool: KVPool, out: torch.Tensor, query: torch.Tensor,
+                                   block_tables: torch.Tensor, context_lens: torch.Tensor,
+                                   max_context_len: int, scale: float, partition_size: int = 0,
+                                   stream=None) -> None:
+    """Split decode and merge with the partials in the library's scratch (no
+    workspace, nothing allocated); see pagedkv.h."""
+    if query.dim() != 3 or query.shape[2] != pool.head_dim:
+        raise ValueError("query must be [B, H, head_dim]")
+    B, H, d = query.shape
+    if block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be [B, max_nb]")
+    es = pool.act_size
+    qp = _buf(query, "query", B * H * d * es, elem_size=es)
+    op = _buf(out, "out", B * H * d * es, elem_size=es)
+    tp = _buf(block_tables, "block_tables", dtype=torch.int32)
+    cp = _buf(context_lens, "context_lens", 4 * B, dtype=torch.int32)
+    _lib.check(_lib.load().paged_attention_decode_noalloc(
+        pool.handle, op, qp, tp, int(block_tables.shape[1]), cp, B, H, int(max_context_len),
+        float(scale), int(partition_size), _stream_handle(stream)))
 
 
 def paged_attention_reduce(out: torch.Tensor, workspace: torch.Tensor, context_lens: torch.Tensor,

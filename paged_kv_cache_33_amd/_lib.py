@@ -56,6 +56,7 @@ EXPORTED = (
     "kv_bm_num_free",
     "kv_bm_table",
     "kv_bm_batch_tables",
+    "paged_attention_decode_noalloc",
     "kv_decode_kernel_kind",
     "kv_last_error",
 )
@@ -139,6 +140,8 @@ def declare(lib: C.CDLL, names=None) -> C.CDLL:
         "kv_bm_table": (C.c_int, [vp, C.c_int64, vp, i32, C.POINTER(C.c_int32),
                                   C.POINTER(C.c_int32)]),
         "kv_bm_batch_tables": (C.c_int, [vp, vp, i32, i32, vp, vp]),
+        "paged_attention_decode_noalloc": (C.c_int, [vp, vp, vp, i32p, i32, i32p, i32, i32, i32,
+                                                     C.c_float, i32, vp]),
         "kv_decode_kernel_kind": (C.c_int32, [vp, i32]),
         "kv_last_error": (C.c_char_p, []),
     }

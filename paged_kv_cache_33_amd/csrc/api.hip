@@ -510,3 +510,72 @@ kv_status paged_attention_reduce_window(void* out, const void* workspace,
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Allocation-free split decode.  The split partials live in `scratch`, a
+// file-scope device array, instead of a caller workspace; each GPU holds its
+// own copy until the process ends.  In host code `scratch` names a host-side
+// stand-in, so its device address is looked up once per device (with that
+// device current) and only that address is handed to the kernels.
+namespace {
+
+static_assert(KV_NOALLOC_SCRATCH_BYTES % 256 == 0, "scratch size");
+static __device__ __align__(256) unsigned char scratch[KV_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+
+kv_status scratch_address(void** out) {
+  static std::mutex mu;
+  static void* ptr[kMaxDevices] = {};
+  int dev = -1;
+  if (hipError_t e = hipGetDevice(&dev); e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(KV_ERR_UNSUPPORTED, "device %d is beyond the %d the library tracks", dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptr[dev]) {
+    void* p = nullptr;
+    if (hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)); e != hipSuccess || !p)
+      return e != hipSuccess ? hip_status(e, "hipGetSymbolAddress(scratch)")
+                             : fail(KV_ERR_HIP, "hipGetSymbolAddress(scratch) gave NULL");
+    ptr[dev] = p;
+  }
+  *out = ptr[dev];
+  return KV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kv_status paged_attention_decode_noalloc(const kv_pool* pool, void* out, const void* query,
+                                         const int32_t* block_tables, int32_t max_nb,
+                                         const int32_t* context_lens, int32_t B, int32_t H,
+                                         int32_t max_context_len, float scale,
+                                         int32_t partition_size, void* stream) {
+  if (!pool) return fail(KV_ERR_INVALID_ARG, "pool is NULL");
+  if (partition_size == 0)  // single pass: nothing to keep between kernels
+    return decode_impl(pool, out, query, block_tables, max_nb, context_lens, B, H,
+                       max_context_len, scale, 0, 0, nullptr, 0, stream);
+  if (kv_status s = check_partition(max_context_len, partition_size); s != KV_OK) return s;
+  const kv_pool_desc& d = pool->desc;
+  const size_t need = paged_attention_workspace_bytes(B, H, d.head_dim, max_context_len,
+                                                      partition_size);
+  if (need > size_t(KV_NOALLOC_SCRATCH_BYTES))
+    return fail(KV_ERR_WORKSPACE,
+                "split partials need %zu bytes; the allocation-free call holds at most %zu "
+                "(use paged_attention_decode with a workspace)",
+                need, size_t(KV_NOALLOC_SCRATCH_BYTES));
+  void* ws = nullptr;
+  if (kv_status s = scratch_address(&ws); s != KV_OK) return s;
+  if (kv_status s = decode_impl(pool, out, query, block_tables, max_nb, context_lens, B, H,
+                                max_context_len, scale, 0, partition_size, ws,
+                                size_t(KV_NOALLOC_SCRATCH_BYTES), stream);
+      s != KV_OK)
+    return s;
+  if (B == 0) return ok();
+  return reduce_impl(out, ws, context_lens, B, H, d.head_dim, max_context_len, 0, partition_size,
+                     d.dtype == KV_F32 ? KV_F32 : KV_BF16, stream);
+}
+
+}  // extern "C"
