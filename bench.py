@@ -92,8 +92,11 @@ def parse_args(argv=None):
                     help="chunked prefill: a 512-token chunk for each of 16 sequences "
                          "(64 query heads over 8 KV heads); prints its own JSON line")
     ap.add_argument("--unfused", action="store_true",
-                    help="run the step's cache write as two calls (kv_slot_mapping + "
-                         "reshape_and_cache) instead of kv_cache_append")
+                    help="run the step as kv_slot_mapping + reshape_and_cache + the decode "
+                         "instead of one kv_decode_step launch")
+    ap.add_argument("--two-launch", action="store_true",
+                    help="run the step as kv_cache_append + the decode instead of one "
+                         "kv_decode_step launch")
     return ap.parse_args(argv)
 
 
@@ -711,20 +714,33 @@ def main(argv=None) -> int:
     stream = torch.cuda.current_stream()
     kernel = "decode_mfma" if P.kv_decode_kernel_kind(pool, w.H) == 1 else "decode_valu"
 
+    # The step: one kv_decode_step launch (the write on extra work-groups, the
+    # attention taking the newest position from the new rows), or the write and
+    # the decode as separate launches.  fp8 and int8 pools write with
+    # kv_cache_append (their write quantises), then decode.
+    one_launch = not (args.unfused or args.two_launch) and w.kv_dtype in ("bf16", "f32")
+
     def run_step(i, ev=None):
-        """One step; ev = (before write, before decode, after decode, after step) events."""
+        """One step; ev = (before write, before decode, after decode, after step)
+        events (with one launch the first two coincide)."""
         s = steps_dev[i % len(steps_dev)]
         if ev is not None:
             ev[0].record(stream)
-        if args.unfused:
-            P.kv_slot_mapping(tables, s["ctx"], s["slots"], stream)
-            P.reshape_and_cache(pool, s["k"], s["v"], s["slots"], stream)
+        if one_launch:
+            if ev is not None:
+                ev[1].record(stream)
+            P.kv_decode_step(pool, out, s["q"], s["k"], s["v"], tables, s["ctx"], L_max, w.scale,
+                             part, ws, s["slots"], stream, window=args.window)
         else:
-            P.kv_cache_append(pool, s["k"], s["v"], tables, s["ctx"], s["slots"], stream)
-        if ev is not None:
-            ev[1].record(stream)
-        P.paged_attention_decode(pool, out, s["q"], tables, s["ctx"], L_max, w.scale, part, ws,
-                                 stream, window=args.window)
+            if args.unfused:
+                P.kv_slot_mapping(tables, s["ctx"], s["slots"], stream)
+                P.reshape_and_cache(pool, s["k"], s["v"], s["slots"], stream)
+            else:
+                P.kv_cache_append(pool, s["k"], s["v"], tables, s["ctx"], s["slots"], stream)
+            if ev is not None:
+                ev[1].record(stream)
+            P.paged_attention_decode(pool, out, s["q"], tables, s["ctx"], L_max, w.scale, part,
+                                     ws, stream, window=args.window)
         if ev is not None:
             ev[2].record(stream)
         if part:
@@ -741,8 +757,12 @@ def main(argv=None) -> int:
         for i in range(args.warmup + args.steps):
             if flush is not None:
                 flush.fill_(i & 0xFF)
-            P.paged_attention_decode(pool, out, s["q"], tables, s["ctx"], L_max, w.scale, part,
-                                     ws, stream, window=args.window)
+            if one_launch:
+                P.kv_decode_step(pool, out, s["q"], s["k"], s["v"], tables, s["ctx"], L_max,
+                                 w.scale, part, ws, s["slots"], stream, window=args.window)
+            else:
+                P.paged_attention_decode(pool, out, s["q"], tables, s["ctx"], L_max, w.scale,
+                                         part, ws, stream, window=args.window)
         torch.cuda.synchronize()
         print(json.dumps({"decode_only_launches": args.warmup + args.steps}), flush=True)
         return 0
@@ -790,7 +810,8 @@ def main(argv=None) -> int:
     by = [step_bytes(w, st, args.window) for st in w.steps]
     used = [by[i % len(by)] for i in range(args.steps)]
     step_b = float(np.mean([u["step"] for u in used]))
-    dec_b = float(np.mean([u["decode"] for u in used]))
+    # the timed kernel: the decode, or with one launch the decode and the write
+    dec_b = float(np.mean([u["step"] if one_launch else u["decode"] for u in used]))
     gbs = step_b / (ms_step * 1e-3) / 1e9
     dec_gbs = dec_b / (dec_avg * 1e-3) / 1e9
     wname = w.name + (f"-window{args.window}" if args.window else "")
@@ -827,9 +848,11 @@ def main(argv=None) -> int:
             "window": args.window,
             "seed": w.seed,
             "kv_cache": w.kv_dtype,
-            "step": ("kv_slot_mapping + reshape_and_cache" if args.unfused else "kv_cache_append")
-                    + (" + paged_attention_decode_window" if args.window else
-                       " + paged_attention_decode")
+            "step": ("kv_decode_step (cache write and attention in one launch)" if one_launch
+                     else ("kv_slot_mapping + reshape_and_cache" if args.unfused
+                           else "kv_cache_append")
+                     + (" + paged_attention_decode_window" if args.window else
+                        " + paged_attention_decode"))
                     + ((" + paged_attention_reduce_window" if args.window else
                         " + paged_attention_reduce") if part else ""),
             "caches": "evicted before every step" if args.cold else "warm (steps back to back)",
@@ -842,7 +865,7 @@ def main(argv=None) -> int:
         "write_ms_avg": round(float(write_ms.mean()), 5),
         "roofline": {
             "bound": "hbm",
-            "kernel": kernel,
+            "kernel": kernel + (" (with the cache write: kv_decode_step)" if one_launch else ""),
             "achieved": round(dec_gbs, 1),
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",

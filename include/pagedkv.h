@@ -266,6 +266,32 @@ kv_status paged_attention_decode_window(const kv_pool* pool, void* out, const vo
                                         int32_t partition_size, void* workspace,
                                         size_t workspace_bytes, void* stream);
 
+/* One whole decode step in one launch: the cache write of kv_cache_append
+ * and the attention of paged_attention_decode_window, i.e. the workbook's
+ * decode step ("LLM inference and serving", Code from memory: append the new
+ * token's K and V rows, then attend over every cached row, the new one
+ * included).  key, value: device [B][H_kv][d] (the pool's activation type),
+ * the rows of each sequence's newest position ctx_b - 1; they are stored as
+ * kv_cache_append stores them (slot_mapping, optional device int64 [B],
+ * receives the slots as there), and out gets what paged_attention_decode_window
+ * gives after that write.  The attention takes position ctx_b - 1 from key and
+ * value themselves, so it does not wait for the write: both run in the same
+ * launch, the write on a few extra work-groups.  The arithmetic order differs
+ * from the two calls in a row (the newest position joins the softmax last),
+ * so results agree within rounding, not bit for bit.  Every other argument is
+ * as for paged_attention_decode_window (window = 0: the whole context); in
+ * split mode follow with paged_attention_reduce(_window) as usual.  A table
+ * entry outside the pool for the newest position's block gives NaN for that
+ * sequence (and no write).  Pools: KV_BF16 and KV_F32 (KV_ERR_UNSUPPORTED for
+ * fp8 and int8 pools, whose write quantises: use kv_cache_append, then the
+ * decode). */
+kv_status kv_decode_step(const kv_pool* pool, void* out, const void* query, const void* key,
+                         const void* value, const int32_t* block_tables, int32_t max_nb,
+                         const int32_t* context_lens, int32_t B, int32_t H,
+                         int32_t max_context_len, float scale, int32_t window,
+                         int32_t partition_size, void* workspace, size_t workspace_bytes,
+                         int64_t* slot_mapping, void* stream);
+
 /* Merge split partials (the workspace paged_attention_decode wrote with the
  * same B, H, head_dim, max_context_len and partition_size) by log-sum-exp:
  * with M = max_k m_k and w_k = l_k * 2^(m_k - M),

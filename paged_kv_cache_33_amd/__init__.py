@@ -31,6 +31,7 @@ __all__ = [
     "kv_cache_append_chunk",
     "paged_attention_workspace_bytes",
     "paged_attention_decode",
+    "kv_decode_step",
     "paged_attention_reduce",
     "paged_attention_decode_noalloc",
     "paged_attention_multi",
@@ -315,6 +316,42 @@ def paged_attention_decode(pool: KVPool, out: torch.Tensor, query: torch.Tensor,
         _lib.check(lib.paged_attention_decode(
             pool.handle, op, qp, tp, max_nb, cp, B, H, int(max_context_len), float(scale),
             int(partition_size), wp, wbytes, _stream_handle(stream)))
+
+
+def kv_decode_step(pool: KVPool, out: torch.Tensor, query: torch.Tensor, key: torch.Tensor,
+                   value: torch.Tensor, block_tables: torch.Tensor, context_lens: torch.Tensor,
+                   max_context_len: int, scale: float, partition_size: int = 0,
+                   workspace: Optional[torch.Tensor] = None,
+                   slot_mapping: Optional[torch.Tensor] = None, stream=None,
+                   window: int = 0) -> None:
+    """One decode step in one launch: the cache write of the newest rows (key,
+    value [B, H_kv, d]) and the attention, which takes the newest position from
+    those rows; see pagedkv.h."""
+    if query.dim() != 3 or query.shape[2] != pool.head_dim:
+        raise ValueError("query must be [B, H, head_dim]")
+    B, H, d = query.shape
+    if block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be [B, max_nb]")
+    es = pool.act_size
+    row = B * pool.num_kv_heads * d * es
+    qp = _buf(query, "query", B * H * d * es, elem_size=es)
+    op = _buf(out, "out", B * H * d * es, elem_size=es)
+    kp = _buf(key, "key", row, elem_size=es)
+    vp = _buf(value, "value", row, elem_size=es)
+    tp = _buf(block_tables, "block_tables", dtype=torch.int32)
+    cp = _buf(context_lens, "context_lens", 4 * B, dtype=torch.int32)
+    sp = None if slot_mapping is None else _buf(slot_mapping, "slot_mapping", 8 * B,
+                                                dtype=torch.int64)
+    wp, wbytes = None, 0
+    if partition_size:
+        if workspace is None:
+            raise ValueError("split mode (partition_size > 0) needs a workspace")
+        wp = _buf(workspace, "workspace")
+        wbytes = workspace.numel() * workspace.element_size()
+    _lib.check(_lib.load().kv_decode_step(
+        pool.handle, op, qp, kp, vp, tp, int(block_tables.shape[1]), cp, B, H,
+        int(max_context_len), float(scale), int(window), int(partition_size), wp, wbytes, sp,
+        _stream_handle(stream)))
 
 
 def paged_attention_decode_noalloc(pool: KVPool, out: torch.Tensor, query: torch.Tensor,

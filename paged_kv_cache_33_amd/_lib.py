@@ -41,6 +41,7 @@ EXPORTED = (
     "paged_attention_workspace_bytes",
     "paged_attention_decode",
     "paged_attention_decode_window",
+    "kv_decode_step",
     "paged_attention_reduce",
     "paged_attention_reduce_window",
     "paged_attention_multi",
@@ -123,6 +124,8 @@ def declare(lib: C.CDLL, names=None) -> C.CDLL:
                                             i32, C.c_float, i32, vp]),
         "paged_attention_decode_window": (C.c_int, [vp, vp, vp, i32p, i32, i32p, i32, i32, i32,
                                                     C.c_float, i32, i32, vp, sz, vp]),
+        "kv_decode_step": (C.c_int, [vp, vp, vp, vp, vp, i32p, i32, i32p, i32, i32, i32,
+                                     C.c_float, i32, i32, vp, sz, vp, vp]),
         "paged_attention_reduce_window": (C.c_int, [vp, vp, i32p, i32, i32, i32, i32, i32, i32,
                                                     C.c_int, vp]),
         "kv_copy_blocks": (C.c_int, [vp, i32p, i32p, i32, vp]),

@@ -219,12 +219,20 @@ int32_t kv_decode_kernel_kind(const kv_pool* pool, int32_t H) {
 
 namespace {
 
+// key / value non-NULL: the fused step (kv_decode_step), which also writes
+// those rows and takes the newest position from them.
 kv_status decode_impl(const kv_pool* pool, void* out, const void* query,
                       const int32_t* block_tables, int32_t max_nb, const int32_t* context_lens,
                       int32_t B, int32_t H, int32_t max_context_len, float scale, int32_t window,
                       int32_t partition_size, void* workspace, size_t workspace_bytes,
-                      void* stream) {
+                      void* stream, const void* key = nullptr, const void* value = nullptr,
+                      int64_t* slot_mapping = nullptr) {
   if (!pool) return fail(KV_ERR_INVALID_ARG, "pool is NULL");
+  const bool fused = key != nullptr || value != nullptr;
+  if (fused && pool->desc.dtype != KV_BF16 && pool->desc.dtype != KV_F32)
+    return fail(KV_ERR_UNSUPPORTED,
+                "the fused step takes bf16 and fp32 pools; for fp8 and int8 pools call "
+                "kv_cache_append, then the decode");
   if (window < 0) return fail(KV_ERR_INVALID_ARG, "window must be >= 0 (0 = whole context)");
   const kv_pool_desc& d = pool->desc;
   if (B < 0) return fail(KV_ERR_INVALID_ARG, "B must be >= 0");
@@ -243,6 +251,8 @@ kv_status decode_impl(const kv_pool* pool, void* out, const void* query,
     return fail(KV_ERR_INVALID_ARG, "out, query, block_tables and context_lens must be non-NULL");
   if (!aligned16(query) || !aligned16(out))
     return fail(KV_ERR_INVALID_ARG, "query and out must be 16-byte aligned");
+  if (fused && (!key || !value || !aligned16(key) || !aligned16(value)))
+    return fail(KV_ERR_INVALID_ARG, "key and value must both be non-NULL and 16-byte aligned");
   const int64_t P = num_partitions(max_context_len, partition_size);
   WorkspaceView ws{nullptr, nullptr, nullptr, 0};
   if (partition_size > 0) {
@@ -278,6 +288,15 @@ kv_status decode_impl(const kv_pool* pool, void* out, const void* query,
   a.ws_o = ws.o;
   a.ws_m = ws.m;
   a.ws_l = ws.l;
+  if (fused) {
+    a.fresh_key = key;
+    a.fresh_value = value;
+    a.append = pagedkv::AppendArgs{pool->k_cache, pool->v_cache, d.num_blocks, d.num_kv_heads,
+                                   d.head_dim,    key,           value,        block_tables,
+                                   max_nb,        context_lens,  B,            slot_mapping,
+                                   d.k_scale,     d.v_scale};
+    a.append.scales_offset = scales_offset(d);
+  }
   const hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
   if (kv_decode_kernel_kind(pool, H) == 1)
@@ -308,6 +327,19 @@ kv_status paged_attention_decode_window(const kv_pool* pool, void* out, const vo
                                         size_t workspace_bytes, void* stream) {
   return decode_impl(pool, out, query, block_tables, max_nb, context_lens, B, H, max_context_len,
                      scale, window, partition_size, workspace, workspace_bytes, stream);
+}
+
+kv_status kv_decode_step(const kv_pool* pool, void* out, const void* query, const void* key,
+                         const void* value, const int32_t* block_tables, int32_t max_nb,
+                         const int32_t* context_lens, int32_t B, int32_t H,
+                         int32_t max_context_len, float scale, int32_t window,
+                         int32_t partition_size, void* workspace, size_t workspace_bytes,
+                         int64_t* slot_mapping, void* stream) {
+  if (B > 0 && (!key || !value))
+    return fail(KV_ERR_INVALID_ARG, "key and value must be non-NULL");
+  return decode_impl(pool, out, query, block_tables, max_nb, context_lens, B, H, max_context_len,
+                     scale, window, partition_size, workspace, workspace_bytes, stream, key, value,
+                     slot_mapping);
 }
 
 kv_status kv_cache_append(const kv_pool* pool, const void* key, const void* value,

@@ -9,16 +9,13 @@
 //
 // An fp8 pool stores each element as an E4M3 code of x / scale (see
 // source_chunk); bf16 and fp32 pools store the bits unchanged.
-//
-// Stores are non-temporal.  A decode step writes a few bytes into many cache
-// lines (one token of each K chunk row and of each V dim row); left dirty in the
-// caches, those lines would be evicted one by one in the middle of the next
-// decode's read stream and cost it far more than their size.  Streamed out
-// here, they are gone before the decode starts.
+// The row writes themselves (and why their stores are non-temporal) are in
+// row_write.h.
 #include <type_traits>
 
 #include "device_common.h"
 #include "launch.h"
+#include "row_write.h"
 
 namespace pagedkv {
 
@@ -34,108 +31,6 @@ __global__ __launch_bounds__(256) void slot_mapping_kernel(SlotMappingArgs a) {
     if (blk >= 0) slot = int64_t(blk) * kBlockTokens + pos % kBlockTokens;
   }
   a.slot_mapping[b] = slot;
-}
-
-// Write chunk c (X elements) of one token's K and V rows, already in cache
-// storage as kc and vc, into in-block slot t of tile `tile`: one 16-byte store
-// for K ([d/X][16][X] tile), X element stores for V ([d][16] tile).
-template <typename Tr>
-__device__ __forceinline__ void write_token_chunk(void* k_cache, void* v_cache, int64_t tile, int C,
-                                                  int head_dim, int c, int t, const uint4 kc,
-                                                  const uint4 vc) {
-  using S = typename Tr::storage;
-  constexpr int X = Tr::kChunk;
-  S* kdst = static_cast<S*>(k_cache) + ((tile * C + c) * kBlockTokens + t) * X;
-  const u32x4_t ku = {kc.x, kc.y, kc.z, kc.w};
-  __builtin_nontemporal_store(ku, reinterpret_cast<u32x4_t*>(kdst));
-  S ve[X];
-  __builtin_memcpy(ve, &vc, sizeof(vc));
-  S* vdst = static_cast<S*>(v_cache) + (tile * head_dim + int64_t(c) * X) * kBlockTokens + t;
-#pragma unroll
-  for (int e = 0; e < X; ++e) __builtin_nontemporal_store(ve[e], vdst + e * kBlockTokens);
-}
-
-// Chunk c of a source row (key or value), whose first element is at element
-// offset src, in cache storage.  bf16 / fp32: the row's own 16 bytes.  fp8: the
-// row's 16 bf16 values (32 bytes), each stored as e4m3_code(x / scale), the
-// division in fp32 (correctly rounded) - "Forward Deployed Engineering
-// Interview", Ch.2 section 9: a per-tensor scale, 1.0 when uncalibrated.
-template <typename Tr>
-__device__ __forceinline__ uint4 source_chunk(const void* base, int64_t src, float scale) {
-  if constexpr (Tr::kKind == Kind::kFp8) {
-    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + src);
-    const uint4 lo = p[0], hi = p[1];
-    const uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-    uint32_t c[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-      c[k] = e4m3_code(bf16_lo(w[2 * k]) / scale) | e4m3_code(bf16_hi(w[2 * k]) / scale) << 8 |
-             e4m3_code(bf16_lo(w[2 * k + 1]) / scale) << 16 |
-             e4m3_code(bf16_hi(w[2 * k + 1]) / scale) << 24;
-    return make_uint4(c[0], c[1], c[2], c[3]);
-  } else {
-    return *reinterpret_cast<const uint4*>(static_cast<const typename Tr::storage*>(base) + src);
-  }
-}
-
-// Chunk c (16 values) of a source row as int8 codes; s receives the row's
-// scale, its largest finite magnitude / 127 ("MLSys Engineer - Inference
-// Systems Q&A", Q3 item 1).  The C threads of one row are C consecutive lanes
-// (C a power of two dividing 64) and all of them call this: the row maximum
-// is combined across them with lane shuffles.
-__device__ __forceinline__ uint4 int8_chunk(const void* base, int64_t src, int C, float& s) {
-  const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + src);
-  const uint4 lo = p[0], hi = p[1];
-  const uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-  float x[16];
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    x[2 * k] = bf16_lo(w[k]);
-    x[2 * k + 1] = bf16_hi(w[k]);
-  }
-  float amax = 0.f;
-#pragma unroll
-  for (int k = 0; k < 16; ++k)
-    if (__builtin_isfinite(x[k])) amax = fmaxf(amax, fabsf(x[k]));
-  for (int off = 1; off < C; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off, kWave));
-  s = amax / 127.f;
-  uint32_t c[4];
-#pragma unroll
-  for (int k = 0; k < 4; ++k)
-    c[k] = int8_code(x[4 * k], s) | int8_code(x[4 * k + 1], s) << 8 |
-           int8_code(x[4 * k + 2], s) << 16 | int8_code(x[4 * k + 3], s) << 24;
-  return make_uint4(c[0], c[1], c[2], c[3]);
-}
-
-// Source chunks of one (token, head) row chunk for the cache: K and V codes
-// or bits, and for an int8 cache the two row scales.
-template <typename Tr>
-__device__ __forceinline__ void row_chunks(const void* key, const void* value, int64_t src, int C,
-                                           float k_scale, float v_scale, uint4& kc, uint4& vc,
-                                           float& ks, float& vs) {
-  if constexpr (Tr::kKind == Kind::kInt8) {
-    kc = int8_chunk(key, src, C, ks);
-    vc = int8_chunk(value, src, C, vs);
-  } else {
-    kc = source_chunk<Tr>(key, src, k_scale);
-    vc = source_chunk<Tr>(value, src, v_scale);
-  }
-}
-
-// An int8 row's two scales, stored by the thread of chunk 0 (tile = block *
-// H_kv + head, t = in-block slot).
-template <typename Tr>
-__device__ __forceinline__ void write_row_scales(void* k_cache, void* v_cache,
-                                                 int64_t scales_offset, int64_t tile, int t,
-                                                 int c, float ks, float vs) {
-  if constexpr (Tr::kKind == Kind::kInt8) {
-    if (c != 0) return;
-    const int64_t i = tile * kBlockTokens + t;
-    __builtin_nontemporal_store(ks, reinterpret_cast<float*>(static_cast<char*>(k_cache) +
-                                                             scales_offset) + i);
-    __builtin_nontemporal_store(vs, reinterpret_cast<float*>(static_cast<char*>(v_cache) +
-                                                             scales_offset) + i);
-  }
 }
 
 // One thread per (token, kv head, 16-byte chunk of the head's cached row).  K
@@ -167,38 +62,12 @@ __global__ __launch_bounds__(256) void cache_write_kernel(CacheWriteArgs a) {
 }
 
 // One new token per sequence, slot mapping and write in one launch: one thread
-// per (sequence, kv head, 16-byte chunk).  The slot is that of position
-// ctx - 1; -1 (nothing written) for ctx <= 0, ctx > max_nb*16 or a table entry
-// outside the pool.
+// per (sequence, kv head, 16-byte chunk).
 template <typename Tr>
 __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
-  constexpr int X = Tr::kChunk;
-  const int C = a.head_dim / X;
-  const int64_t total = int64_t(a.B) * a.num_kv_heads * C;
   const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (idx >= total) return;
-  const int c = int(idx % C);
-  const int h = int((idx / C) % a.num_kv_heads);
-  const int b = int(idx / (int64_t(C) * a.num_kv_heads));
-  // Source chunk first: it overlaps the dependent length -> table loads.
-  const int64_t src = (int64_t(b) * a.num_kv_heads + h) * a.head_dim + int64_t(c) * X;
-  uint4 kc, vc;
-  float ks = 0.f, vs = 0.f;
-  row_chunks<Tr>(a.key, a.value, src, C, a.k_scale, a.v_scale, kc, vc, ks, vs);
-  const int32_t n = a.context_lens[b];
-  int64_t slot = -1;
-  if (n > 0 && n <= a.max_nb * kBlockTokens) {
-    const int32_t pos = n - 1;
-    const int32_t blk = a.block_tables[int64_t(b) * a.max_nb + pos / kBlockTokens];
-    if (blk >= 0 && blk < a.num_blocks) slot = int64_t(blk) * kBlockTokens + pos % kBlockTokens;
-  }
-  if (a.slot_mapping && h == 0 && c == 0) a.slot_mapping[b] = slot;
-  if (slot < 0) return;
-  const int64_t tile = (slot / kBlockTokens) * a.num_kv_heads + h;
-  write_token_chunk<Tr>(a.k_cache, a.v_cache, tile, C, a.head_dim, c, int(slot % kBlockTokens), kc,
-                        vc);
-  write_row_scales<Tr>(a.k_cache, a.v_cache, a.scales_offset, tile, int(slot % kBlockTokens), c,
-                       ks, vs);
+  if (idx >= append_threads(a, Tr::kKind)) return;
+  append_token_chunk<Tr>(a, idx);
 }
 
 // Several new tokens per sequence (a prefill chunk, draft tokens).  Row

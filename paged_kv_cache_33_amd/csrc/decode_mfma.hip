@@ -13,6 +13,7 @@
 #include "device_common.h"
 #include "launch.h"
 #include "mfma_tile.h"
+#include "row_write.h"
 #include "work_list.h"
 
 namespace pagedkv {
@@ -33,14 +34,37 @@ constexpr int kWavesOf = kSplit && !kByteCodes<E> ? 8 : 4;
 template <typename E, bool kSplit>
 constexpr int kGroupsPerCu = !kSplit ? 3 : kByteCodes<E> ? 2 : 1;
 // LDS where a work-group's waves merge their (m, l, O): one padded row of O
-// per wave and head of the tile.
+// per wave and head of the tile.  Fused step: the newest position's K and V
+// rows (bf16), its score per head of the tile, and whether its block's table
+// entry lies outside the pool.
 template <int kWaves, int D>
 struct MergeLds {
   __attribute__((aligned(16))) float o[kWaves][kHeadsPerTile][D + 4];
   float m[kWaves][kHeadsPerTile];
   float l[kWaves][kHeadsPerTile];
   int bad[kWaves];
+  __attribute__((aligned(16))) uint16_t fresh[2][D];
+  float fresh_s[kHeadsPerTile];
+  int fresh_bad;
 };
+
+// q_n . k of the newest position's key (operand order: lane quarter q holds
+// the dims that pair with K operand i), the four quarters combined: head n's
+// raw score in every lane of column n.
+template <typename E, int D>
+__device__ __forceinline__ float fresh_score(const uint4 (&krow)[MfmaShape<D>::KI],
+                                             const bf16x8_t (&qop)[MfmaShape<D>::KI]) {
+  float dot = 0.f;
+#pragma unroll
+  for (int i = 0; i < MfmaShape<D>::KI; ++i) {
+    const uint4 qq = __builtin_bit_cast(uint4, qop[i]);
+    dot = dot2_bf16(krow[i].x, qq.x, dot);
+    dot = dot2_bf16(krow[i].y, qq.y, dot);
+    dot = dot2_bf16(krow[i].z, qq.z, dot);
+    dot = dot2_bf16(krow[i].w, qq.w, dot);
+  }
+  return cross_row_sum(dot);
+}
 
 // One work item: partition `part` of sequence b, head tile `tile_y` (a KV
 // head and a group of up to 16 of its query heads).
@@ -100,7 +124,11 @@ __device__ __forceinline__ void mfma_item(const DecodeArgs& a, const int part, c
   if (split && part >= nparts) return;
 
   const int tb = rs + (split ? part * a.partition_size : 0);
-  const int te = split ? min(tb + a.partition_size, ctx) : ctx;
+  int te = split ? min(tb + a.partition_size, ctx) : ctx;
+  // Fused step: the item holding position ctx - 1 takes it from the fresh rows
+  // (folded in at the merge) and walks the cache up to ctx - 2 only.
+  const bool fold = kFoldable<E> && a.fresh_key != nullptr && (!split || part == nparts - 1);
+  if (fold) te = ctx - 1 > max(tb, first) ? ctx - 1 : tb;
   const int jb = tb / kBlockTokens;
   const int je = (te + kBlockTokens - 1) / kBlockTokens;
 
@@ -127,6 +155,7 @@ __device__ __forceinline__ void mfma_item(const DecodeArgs& a, const int part, c
       qop[i] = __builtin_bit_cast(bf16x8_t, raw);
     }
   }
+  if (fold && w == 0) fetch_fresh<E, D>(a, b, kvh, lane, sm.fresh, sm.fresh_bad);
 
   const S* kc = static_cast<const S*>(a.k_cache);
   const S* vc = static_cast<const S*>(a.v_cache);
@@ -195,6 +224,14 @@ __device__ __forceinline__ void mfma_item(const DecodeArgs& a, const int part, c
     }
   }
 
+  if (fold && w == 0) {
+    uint4 krow[KI];
+#pragma unroll
+    for (int i = 0; i < KI; ++i)
+      krow[i] = *reinterpret_cast<const uint4*>(&sm.fresh[0][query_dim0<E>(i, q)]);
+    const float sf = fresh_score<E, D>(krow, qop);
+    if (q == 0) sm.fresh_s[n] = sf * a.scale_log2;
+  }
   const float lsum = cross_row_sum(st.l);
   if (q == 0) {
     sm_m[w][n] = st.m;
@@ -206,12 +243,12 @@ __device__ __forceinline__ void mfma_item(const DecodeArgs& a, const int part, c
     *reinterpret_cast<floatx4_t*>(&sm_o[w][n][16 * mc + 4 * q]) = st.o[mc];
   __syncthreads();
 
-  int bad = 0;
+  int bad = fold ? sm.fresh_bad : 0;
 #pragma unroll
   for (int ww = 0; ww < kWaves; ++ww) bad |= sm_bad[ww];
   for (int idx = threadIdx.x; idx < nh * D; idx += blockDim.x) {
     const int hh = idx / D, x = idx % D;
-    float M = -INFINITY;
+    float M = fold ? sm.fresh_s[hh] : -INFINITY;  // the newest position: m = its score, l = 1
 #pragma unroll
     for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, sm_m[ww][hh]);
     float L = 0.f, acc = 0.f;
@@ -221,6 +258,11 @@ __device__ __forceinline__ void mfma_item(const DecodeArgs& a, const int part, c
       const float sc = fast_exp2(sm_m[ww][hh] - M);
       L = fmaf(sm_l[ww][hh], sc, L);
       acc = fmaf(sm_o[ww][hh][x], sc, acc);
+    }
+    if (fold) {
+      const float sc = fast_exp2(sm.fresh_s[hh] - M);
+      L += sc;
+      acc = fmaf(bf16_to_f32(sm.fresh[1][x]), sc, acc);
     }
     float res = acc / L * a.v_scale;
     if (bad) res = __int_as_float(0x7fc00000);
@@ -280,7 +322,7 @@ __device__ __forceinline__ void mfma_split_worker(const DecodeArgs& a, const int
   // block count; valid = false past the end of the list.
   struct Item {
     int b, part, ctx, first, nparts, te, jb, nblk;
-    bool valid, bad_len;
+    bool valid, bad_len, fold;
   };
   auto describe = [&](int i) -> Item {
     Item it{};
@@ -296,6 +338,9 @@ __device__ __forceinline__ void mfma_split_worker(const DecodeArgs& a, const int
     it.bad_len = it.ctx > a.max_nb * kBlockTokens || it.nparts > a.num_partitions;
     const int tb = rs + it.part * a.partition_size;
     it.te = min(tb + a.partition_size, it.ctx);
+    // fused step: the last partition takes position ctx - 1 from the fresh rows
+    it.fold = kFoldable<E> && a.fresh_key != nullptr && it.part == it.nparts - 1;
+    if (it.fold) it.te = it.ctx - 1 > max(tb, it.first) ? it.ctx - 1 : tb;
     it.jb = tb / kBlockTokens;
     const int je = (it.te + kBlockTokens - 1) / kBlockTokens;
     it.nblk = !it.bad_len && je - it.jb - w > 0 ? (je - it.jb - w + kWaves - 1) / kWaves : 0;
@@ -348,7 +393,6 @@ __device__ __forceinline__ void mfma_split_worker(const DecodeArgs& a, const int
     // the next item's table window, in flight while this item streams
     const Item nxt = describe(i + stride);
     const int win_next = load_window(nxt);
-
     MfmaState<D> st;
 #pragma unroll
     for (int mc = 0; mc < MC; ++mc) st.o[mc] = floatx4_t{0.f, 0.f, 0.f, 0.f};
@@ -386,6 +430,32 @@ __device__ __forceinline__ void mfma_split_worker(const DecodeArgs& a, const int
         consume(k, tile_a, fa);
       }
     }
+    // Fused step, last partition: wave 0 loads the newest position's K row
+    // (its operand dims) and V row, scores it against the current query (qop
+    // moves on to the next item below) and leaves score, V row and the table
+    // check for the merge.  Nothing else is in flight here (this item's blocks
+    // are consumed, the next item's come after), so the loads' wait costs one
+    // latency, on the last partitions only.
+    if constexpr (kFoldable<E>) {
+      if (cur.fold && w == 0) {
+        const size_t row = (size_t(cur.b) * a.num_kv_heads + kvh) * D;
+        const uint16_t* fk = static_cast<const uint16_t*>(a.fresh_key) + row;
+        const uint16_t* fv = static_cast<const uint16_t*>(a.fresh_value) + row;
+        uint4 krow[KI];
+#pragma unroll
+        for (int k = 0; k < KI; ++k)
+          krow[k] = *reinterpret_cast<const uint4*>(fk + query_dim0<E>(k, q));
+        if (lane < D / 8)
+          *reinterpret_cast<uint4*>(&sm.fresh[1][lane * 8]) =
+              *reinterpret_cast<const uint4*>(fv + lane * 8);
+        if (lane == 0) {
+          const int p = a.block_tables[int64_t(cur.b) * a.max_nb + (cur.ctx - 1) / kBlockTokens];
+          sm.fresh_bad = p < 0 || p >= a.num_blocks;
+        }
+        const float sf = fresh_score<E, D>(krow, qop);
+        if (q == 0) sm.fresh_s[n] = sf * a.scale_log2;
+      }
+    }
     // unconditional (an entry outside the pool loads tile 0); see load_window
     tile_a = fetch(win_next, 0, fa);
     if (nxt.nblk == 0) tile_a = -1;
@@ -404,12 +474,13 @@ __device__ __forceinline__ void mfma_split_worker(const DecodeArgs& a, const int
       *reinterpret_cast<floatx4_t*>(&sm_o[w][n][16 * mc + 4 * q]) = st.o[mc];
     lds_barrier();
     int bad = cur.bad_len ? 1 : 0;
+    if (cur.fold) bad |= sm.fresh_bad;
 #pragma unroll
     for (int ww = 0; ww < kWaves; ++ww) bad |= sm_bad[ww];
     uint16_t* out = static_cast<uint16_t*>(a.out);
     for (int idx = threadIdx.x; idx < nh * D; idx += kWaves * kWave) {
       const int hh = idx / D, x = idx % D;
-      float M = -INFINITY;
+      float M = cur.fold ? sm.fresh_s[hh] : -INFINITY;  // newest position: m = its score, l = 1
 #pragma unroll
       for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, sm_m[ww][hh]);
       float L = 0.f, acc = 0.f;
@@ -419,6 +490,11 @@ __device__ __forceinline__ void mfma_split_worker(const DecodeArgs& a, const int
         const float sc = fast_exp2(sm_m[ww][hh] - M);
         L = fmaf(sm_l[ww][hh], sc, L);
         acc = fmaf(sm_o[ww][hh][x], sc, acc);
+      }
+      if (cur.fold) {
+        const float sc = fast_exp2(sm.fresh_s[hh] - M);
+        L += sc;
+        acc = fmaf(bf16_to_f32(sm.fresh[1][x]), sc, acc);
       }
       float res = acc / L * a.v_scale;
       if (bad) res = __int_as_float(0x7fc00000);
@@ -444,18 +520,35 @@ __device__ __forceinline__ void mfma_split_worker(const DecodeArgs& a, const int
 // sequence and head tile, sequences taken longest first.  Split (kSplit =
 // true): grid (resident workers, head tiles, 1) walking the work list.  Two instantiations keep each one's
 // register allocation that of a single inlined item.
+//
+// Fused step: append_groups more work-groups write the new rows, placed as in
+// the vector-ALU kernel (after every decode work-group: z-slabs past the
+// sequences of a single pass, y-slabs past the head tiles of a split launch);
+// the decode takes the newest position from the fresh rows and never waits
+// for them.
 template <typename E, int D, bool kSplit>
 __global__ __launch_bounds__((kWavesOf<E, kSplit> * kWave),
                              (kGroupsPerCu<E, kSplit>)) void decode_mfma_kernel(DecodeArgs a) {
   constexpr int kWaves = kWavesOf<E, kSplit>;
   __shared__ MergeLds<kWaves, D> sm_merge;
   if constexpr (!kSplit) {
+    const int z = blockIdx.z;
+    if (a.append_groups > 0 && z >= a.B) {
+      append_group<E>(a.append, int64_t(z - a.B) * gridDim.y + blockIdx.y);
+      return;
+    }
     __shared__ int sm_order[kOrderBuckets + kWaves + 1];
     const int b = a.B <= kMaxOrderedSeqs
-        ? sequence_of_rank<kWaves * kWave>(a.context_lens, a.B, a.max_nb, blockIdx.z, sm_order)
-        : int(blockIdx.z);
+        ? sequence_of_rank<kWaves * kWave>(a.context_lens, a.B, a.max_nb, z, sm_order)
+        : z;
     mfma_item<E, D, kWaves>(a, 0, blockIdx.y, b, sm_merge);
   } else {
+    const int g = a.H / a.num_kv_heads;
+    const int tiles = a.num_kv_heads * ((g + kHeadsPerTile - 1) / kHeadsPerTile);
+    if (int(blockIdx.y) >= tiles) {
+      append_group<E>(a.append, int64_t(blockIdx.y - tiles) * gridDim.x + blockIdx.x);
+      return;
+    }
     __shared__ int sm_starts[kMaxSplitSeqs + 1];
     const int n_items = build_work_list(a, sm_starts);
     // fp8: the streamed worker measured 2.5% slower on the long-context mix
@@ -503,7 +596,23 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, Kind kind, int head_dim, hipS
     const int workers = resident_workers(reinterpret_cast<const void*>(kern), block.x, tiles);
     grid = dim3(unsigned(most < workers ? most : workers), tiles, 1);
   }
-  hipLaunchKernelGGL(kern, grid, block, 0, s, a);
+  DecodeArgs args = a;
+  args.append_groups = 0;
+  if (a.fresh_key) {  // fused step: add the work-groups of the cache write
+    const int64_t need = append_threads(a.append, kind);
+    if (a.partition_size > 0) {
+      const int64_t slab = int64_t(grid.x) * block.x;
+      const int64_t slabs = (need + slab - 1) / slab;
+      grid.y += unsigned(slabs);
+      args.append_groups = int32_t(slabs * grid.x);
+    } else {
+      const int64_t slab = int64_t(grid.y) * block.x;
+      const int64_t slabs = (need + slab - 1) / slab;
+      grid.z += unsigned(slabs);
+      args.append_groups = int32_t(slabs * grid.y);
+    }
+  }
+  hipLaunchKernelGGL(kern, grid, block, 0, s, args);
   return hipGetLastError();
 }
 

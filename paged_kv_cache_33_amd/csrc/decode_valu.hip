@@ -22,6 +22,7 @@
 //     each lane does plain fp32 FMAs.
 #include "device_common.h"
 #include "launch.h"
+#include "row_write.h"
 #include "work_list.h"
 
 namespace pagedkv {
@@ -224,6 +225,33 @@ __device__ __forceinline__ void compute_block(const BlockFrag<Tr, D>& f, const Q
   }
 }
 
+// q . k of the newest position's key row (in LDS) over this lane's query
+// chunks, the four 16-lane rows combined: the same value in every lane.
+template <typename Tr, int D>
+__device__ __forceinline__ float fresh_score(const typename Tr::act* krow,
+                                             const QueryFrag<Tr, D>& qf, int lane) {
+  using Sh = ValuShape<Tr, D>;
+  float dot = 0.f;
+  if constexpr (kFoldable<Tr>) {
+#pragma unroll
+    for (int i = 0; i < Sh::KL; ++i) {
+      const uint4 k = *reinterpret_cast<const uint4*>(krow + (4 * i + lane / 16) * Sh::X);
+      if constexpr (Tr::kKind == Kind::kBf16) {
+        dot = dot2_bf16(k.x, qf.c[i][0].x, dot);
+        dot = dot2_bf16(k.y, qf.c[i][0].y, dot);
+        dot = dot2_bf16(k.z, qf.c[i][0].z, dot);
+        dot = dot2_bf16(k.w, qf.c[i][0].w, dot);
+      } else {
+        dot = fmaf(__uint_as_float(k.x), __uint_as_float(qf.c[i][0].x), dot);
+        dot = fmaf(__uint_as_float(k.y), __uint_as_float(qf.c[i][0].y), dot);
+        dot = fmaf(__uint_as_float(k.z), __uint_as_float(qf.c[i][0].z), dot);
+        dot = fmaf(__uint_as_float(k.w), __uint_as_float(qf.c[i][0].w), dot);
+      }
+    }
+  }
+  return cross_row_sum(dot);
+}
+
 // One work item: partition `part` of sequence b, query head h.
 template <typename Tr, int D>
 __device__ __forceinline__ void valu_item(const DecodeArgs& a, const int part, const int h,
@@ -237,6 +265,11 @@ __device__ __forceinline__ void valu_item(const DecodeArgs& a, const int part, c
   __shared__ float sm_m[kWaves];
   __shared__ float sm_l[kWaves];
   __shared__ int sm_bad[kWaves];
+  // fused step: the newest position's K and V rows, its score, and whether its
+  // block's table entry lies outside the pool
+  __shared__ __attribute__((aligned(16))) A sm_fresh[2][D];
+  __shared__ float sm_fresh_s;
+  __shared__ int sm_fresh_bad;
 
   const int lane = threadIdx.x % kWave;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -270,7 +303,12 @@ __device__ __forceinline__ void valu_item(const DecodeArgs& a, const int part, c
   if (split && part >= nparts) return;
 
   const int tb = rs + (split ? part * a.partition_size : 0);
-  const int te = split ? min(tb + a.partition_size, ctx) : ctx;
+  int te = split ? min(tb + a.partition_size, ctx) : ctx;
+  // Fused step: the item holding position ctx - 1 takes that position from
+  // the fresh rows (folded in at the merge) and walks the cache up to ctx - 2
+  // only; with no cached position left in its range it walks nothing.
+  const bool fold = kFoldable<Tr> && a.fresh_key != nullptr && (!split || part == nparts - 1);
+  if (fold) te = ctx - 1 > max(tb, first) ? ctx - 1 : tb;
   const int jb = tb / kBlockTokens;
   const int je = (te + kBlockTokens - 1) / kBlockTokens;
 
@@ -295,6 +333,7 @@ __device__ __forceinline__ void valu_item(const DecodeArgs& a, const int part, c
       for (int pc = 0; pc < QueryFrag<Tr, D>::kPieces; ++pc)
         qf.c[i][pc] = *reinterpret_cast<const uint4*>(qrow + (4 * i + lane / 16) * X + pc * 8);
   }
+  if (fold && w == 0) fetch_fresh<Tr, D>(a, b, kvh, lane, sm_fresh, sm_fresh_bad);
 
   const S* kc = static_cast<const S*>(a.k_cache);
   const S* vc = static_cast<const S*>(a.v_cache);
@@ -362,6 +401,10 @@ __device__ __forceinline__ void valu_item(const DecodeArgs& a, const int part, c
     }
   }
 
+  if (fold && w == 0) {
+    const float sf = fresh_score<Tr, D>(sm_fresh[0], qf, lane);
+    if (lane == 0) sm_fresh_s = sf * a.scale_log2;
+  }
   // Wave totals: the denominator is spread over the 16 token lanes of a row.
   const float lsum = row16_sum(st.l);
   if (lane == 0) {
@@ -381,6 +424,10 @@ __device__ __forceinline__ void valu_item(const DecodeArgs& a, const int part, c
       M = fmaxf(M, sm_m[ww]);
       bad |= sm_bad[ww];
     }
+    if (fold) {  // the newest position joins as one more partial: m = its score, l = 1
+      M = fmaxf(M, sm_fresh_s);
+      bad |= sm_fresh_bad;
+    }
     float L = 0.f, acc = 0.f;
 #pragma unroll
     for (int ww = 0; ww < kWaves; ++ww) {
@@ -388,6 +435,11 @@ __device__ __forceinline__ void valu_item(const DecodeArgs& a, const int part, c
       const float sc = fast_exp2(sm_m[ww] - M);
       L = fmaf(sm_l[ww], sc, L);
       acc = fmaf(sm_o[ww][x], sc, acc);
+    }
+    if (fold) {
+      const float sc = fast_exp2(sm_fresh_s - M);
+      L += sc;
+      acc = fmaf(act_to_f32<Tr>(sm_fresh[1][x]), sc, acc);
     }
     float res = acc / L * a.v_scale;
     if (bad) res = __int_as_float(0x7fc00000);
@@ -407,15 +459,32 @@ __device__ __forceinline__ void valu_item(const DecodeArgs& a, const int part, c
 // sequence and head tile, sequences taken longest first.  Split (kSplit = true): grid (resident workers, head
 // tiles, 1) walking the work list.  Two instantiations keep each one's
 // register allocation that of a single inlined item.
+//
+// Fused step: append_groups more work-groups write the new rows, dispatched
+// after every decode work-group (single pass: z-slabs past the sequences;
+// split: y-slabs past the heads), so their stores meet the end of the read
+// stream.  The decode never waits for them: it takes the newest position from
+// the fresh rows.  (The scattered partial-line stores of a write slow a read
+// stream they overlap: placed first, or spread over the decode work-groups,
+// they cost the 7B-shape step 20-24 us; placed last, 8 us.)
 template <typename Tr, int D, bool kSplit>
 __global__ __launch_bounds__(kWaves * kWave) void decode_valu_kernel(DecodeArgs a) {
   if constexpr (!kSplit) {
+    const int z = blockIdx.z;
+    if (a.append_groups > 0 && z >= a.B) {
+      append_group<Tr>(a.append, int64_t(z - a.B) * gridDim.y + blockIdx.y);
+      return;
+    }
     __shared__ int sm_order[kOrderBuckets + kWaves + 1];
     const int b = a.B <= kMaxOrderedSeqs
-        ? sequence_of_rank<kWaves * kWave>(a.context_lens, a.B, a.max_nb, blockIdx.z, sm_order)
-        : int(blockIdx.z);
+        ? sequence_of_rank<kWaves * kWave>(a.context_lens, a.B, a.max_nb, z, sm_order)
+        : z;
     valu_item<Tr, D>(a, 0, blockIdx.y, b);
   } else {
+    if (int(blockIdx.y) >= a.H) {
+      append_group<Tr>(a.append, int64_t(blockIdx.y - a.H) * gridDim.x + blockIdx.x);
+      return;
+    }
     __shared__ int sm_starts[kMaxSplitSeqs + 1];
     const int n_items = build_work_list(a, sm_starts);
     for (int i = blockIdx.x; i < n_items; i += gridDim.x) {
@@ -452,7 +521,23 @@ hipError_t launch_decode_valu(const DecodeArgs& a, Kind kind, int head_dim, hipS
     const int workers = resident_workers(reinterpret_cast<const void*>(kern), block.x, a.H);
     grid = dim3(unsigned(most < workers ? most : workers), a.H, 1);
   }
-  hipLaunchKernelGGL(kern, grid, block, 0, s, a);
+  DecodeArgs args = a;
+  args.append_groups = 0;
+  if (a.fresh_key) {  // fused step: add the work-groups of the cache write
+    const int64_t need = append_threads(a.append, kind);
+    if (a.partition_size > 0) {
+      const int64_t slab = int64_t(grid.x) * block.x;
+      const int64_t slabs = (need + slab - 1) / slab;
+      grid.y += unsigned(slabs);
+      args.append_groups = int32_t(slabs * grid.x);
+    } else {
+      const int64_t slab = int64_t(grid.y) * block.x;
+      const int64_t slabs = (need + slab - 1) / slab;
+      grid.z += unsigned(slabs);
+      args.append_groups = int32_t(slabs * grid.y);
+    }
+  }
+  hipLaunchKernelGGL(kern, grid, block, 0, s, args);
   return hipGetLastError();
 }
 

@@ -17,6 +17,31 @@ enum class Kind { kF32, kBf16, kFp8, kInt8 };
 // resident at once, divided among `tiles` head tiles (at least 1 each).
 int resident_workers(const void* kernel, int threads, int tiles);
 
+// One new token per sequence: slot mapping and cache write in one launch.
+struct AppendArgs {
+  void* k_cache;
+  void* v_cache;
+  int32_t num_blocks;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  const void* key;              // [B][H_kv][d]
+  const void* value;
+  const int32_t* block_tables;  // [B][max_nb]
+  int32_t max_nb;
+  const int32_t* context_lens;  // [B]
+  int32_t B;
+  int64_t* slot_mapping;        // optional [B] out ([num_rows] with query_start)
+  float k_scale;                // fp8: stored code = e4m3(x / scale)
+  float v_scale;
+  // Several rows per sequence: with query_start non-NULL, key/value are
+  // [num_rows][H_kv][d] and sequence b's rows query_start[b] .. [b+1]-1 sit at
+  // positions ctx_b - n_b .. ctx_b - 1 (n_b <= max_query_len).
+  const int32_t* query_start;
+  int32_t max_query_len;
+  int32_t num_rows;
+  int64_t scales_offset;        // int8: bytes from a cache buffer to its row scales
+};
+
 // Everything a decode kernel needs; passed by value as the kernel argument.
 struct DecodeArgs {
   const void* k_cache;
@@ -40,6 +65,14 @@ struct DecodeArgs {
   float* ws_m;                 // [B][H][P]
   float* ws_l;                 // [B][H][P]
   int64_t scales_offset;       // int8: bytes from a cache buffer to its row scales
+  // Fused decode step (kv_decode_step): the K/V rows of each sequence's newest
+  // position ctx - 1 ([B][H_kv][d] activations), which the decode takes from
+  // here instead of the cache; NULL otherwise.  `append` is the cache write of
+  // those rows, done by `append_groups` extra work-groups of the same launch.
+  const void* fresh_key;
+  const void* fresh_value;
+  int32_t append_groups;
+  AppendArgs append;
 };
 
 // Several new query tokens per sequence (a prefill chunk or draft tokens to
@@ -94,31 +127,6 @@ struct CacheWriteArgs {
   int32_t N;
   float k_scale;                // fp8: stored code = e4m3(x / scale)
   float v_scale;
-  int64_t scales_offset;        // int8: bytes from a cache buffer to its row scales
-};
-
-// One new token per sequence: slot mapping and cache write in one launch.
-struct AppendArgs {
-  void* k_cache;
-  void* v_cache;
-  int32_t num_blocks;
-  int32_t num_kv_heads;
-  int32_t head_dim;
-  const void* key;              // [B][H_kv][d]
-  const void* value;
-  const int32_t* block_tables;  // [B][max_nb]
-  int32_t max_nb;
-  const int32_t* context_lens;  // [B]
-  int32_t B;
-  int64_t* slot_mapping;        // optional [B] out ([num_rows] with query_start)
-  float k_scale;                // fp8: stored code = e4m3(x / scale)
-  float v_scale;
-  // Several rows per sequence: with query_start non-NULL, key/value are
-  // [num_rows][H_kv][d] and sequence b's rows query_start[b] .. [b+1]-1 sit at
-  // positions ctx_b - n_b .. ctx_b - 1 (n_b <= max_query_len).
-  const int32_t* query_start;
-  int32_t max_query_len;
-  int32_t num_rows;
   int64_t scales_offset;        // int8: bytes from a cache buffer to its row scales
 };
 

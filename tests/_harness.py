@@ -106,9 +106,11 @@ def upload(w: W.Workload, k_pool: np.ndarray, v_pool: np.ndarray) -> DevWorkload
 
 
 def gpu_step(dw: DevWorkload, step: W.DecodeStep, partition_size: int = 0,
-             max_context_len: Optional[int] = None, write: bool = True, fused: bool = False):
+             max_context_len: Optional[int] = None, write: bool = True, fused: bool = False,
+             one_launch: bool = False, window: int = 0):
     """One decode step on the GPU: slot mapping, cache write, decode (+ reduce);
-    the first two as separate calls or (fused) as one kv_cache_append.
+    the first two as separate calls or (fused) as one kv_cache_append, or
+    (one_launch) the whole step as kv_decode_step.
     Returns (slots, out) as device tensors."""
     w = dw.w
     ctx = torch.from_numpy(step.context_lens).cuda()
@@ -119,6 +121,13 @@ def gpu_step(dw: DevWorkload, step: W.DecodeStep, partition_size: int = 0,
     if partition_size:
         n = P.paged_attention_workspace_bytes(w.B, w.H, w.d, L, partition_size)
         ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    if one_launch:
+        slots = torch.full((w.B,), -7, dtype=torch.int64, device="cuda")
+        P.kv_decode_step(dw.pool, out, q, to_dev(step.new_k), to_dev(step.new_v), dw.tables, ctx,
+                         L, w.scale, partition_size, ws, slots, window=window)
+        if partition_size:
+            P.paged_attention_reduce(out, ws, ctx, L, partition_size, w.dtype, window=window)
+        return slots, out
     if fused:
         slots = torch.full((w.B,), -7, dtype=torch.int64, device="cuda")
         P.kv_cache_append(dw.pool, to_dev(step.new_k), to_dev(step.new_v), dw.tables, ctx, slots)
@@ -126,20 +135,22 @@ def gpu_step(dw: DevWorkload, step: W.DecodeStep, partition_size: int = 0,
         slots = P.kv_slot_mapping(dw.tables, ctx)
         if write:
             P.reshape_and_cache(dw.pool, to_dev(step.new_k), to_dev(step.new_v), slots)
-    P.paged_attention_decode(dw.pool, out, q, dw.tables, ctx, L, w.scale, partition_size, ws)
+    P.paged_attention_decode(dw.pool, out, q, dw.tables, ctx, L, w.scale, partition_size, ws,
+                             window=window)
     if partition_size:
-        P.paged_attention_reduce(out, ws, ctx, L, partition_size, w.dtype)
+        P.paged_attention_reduce(out, ws, ctx, L, partition_size, w.dtype, window=window)
     return slots, out
 
 
-def oracle_step(w: W.Workload, k_pool, v_pool, step: W.DecodeStep, seqs=None):
+def oracle_step(w: W.Workload, k_pool, v_pool, step: W.DecodeStep, seqs=None, window: int = 0):
     """Oracle slot mapping, cache write and decode (optionally for some sequences)."""
     slots = O.slot_mapping(w.block_tables, step.context_lens)
     kp, vp = O.reshape_and_cache(k_pool, v_pool, step.new_k, step.new_v, slots, w.H_kv, w.d,
                                  w.kv_dtype, w.num_blocks, w.k_scale, w.v_scale)
     seqs = range(w.B) if seqs is None else seqs
     ref = {b: O.decode_sequence(kp, vp, step.q[b], w.block_tables[b], int(step.context_lens[b]),
-                                w.H, w.H_kv, w.d, w.kv_dtype, w.scale, w.k_scale, w.v_scale)
+                                w.H, w.H_kv, w.d, w.kv_dtype, w.scale, w.k_scale, w.v_scale,
+                                window=window)
            for b in seqs}
     return slots, kp, vp, ref
 
@@ -176,17 +187,20 @@ def assert_close(got_bits: np.ndarray, ref: dict, dtype: str, label: str = "",
 
 
 def single_step_case(w: W.Workload, partition_size: int = 0, seqs=None, label: str = "",
-                     amplitude: float = 1.0, fused: bool = False, per_row: bool = False):
+                     amplitude: float = 1.0, fused: bool = False, per_row: bool = False,
+                     one_launch: bool = False, window: int = 0):
     """Full parity check of one step: slots and pool bit-exact, outputs in tolerance."""
     step = w.steps[0]
     first_unwritten = step.context_lens.astype(np.int64) - 1
     kp0, vp0 = poison(w, np.maximum(first_unwritten, 0))
     dw = upload(w, kp0, vp0)
     log(f"[gpu] {label} B={w.B} H={w.H} H_kv={w.H_kv} d={w.d} {w.kv_dtype} P={partition_size}"
-        f"{' fused' if fused else ''}")
-    slots, out = gpu_step(dw, step, partition_size, fused=fused)
+        f"{' fused' if fused else ''}{' one-launch' if one_launch else ''}"
+        f"{f' window={window}' if window else ''}")
+    slots, out = gpu_step(dw, step, partition_size, fused=fused, one_launch=one_launch,
+                          window=window)
     torch.cuda.synchronize()
-    oslots, kp, vp, ref = oracle_step(w, kp0, vp0, step, seqs)
+    oslots, kp, vp, ref = oracle_step(w, kp0, vp0, step, seqs, window=window)
     np.testing.assert_array_equal(slots.cpu().numpy(), oslots, err_msg=f"{label}: slots")
     assert np.array_equal(from_dev(dw.pool.k_cache, w.kv_dtype), kp), f"{label}: K pool bits"
     assert np.array_equal(from_dev(dw.pool.v_cache, w.kv_dtype), vp), f"{label}: V pool bits"
