@@ -251,19 +251,20 @@ __device__ __forceinline__ uint32_t lds_offset(const void* p) {
 }
 
 // An int8 block's row scales from its LDS stage, where they follow the two
-// tiles (K's 16, then V's); lane q takes those of tokens 4q..4q+3.
+// tiles (K's 16, then V's); lane (n, q) takes those of token 4q + n % 4 (see
+// MfmaScales).
 template <typename E, int D>
 __device__ __forceinline__ void load_scales_lds_asm(MfmaFrag<E, D>& f, uint32_t base, int lane) {
   constexpr int kTileBytes = kBlockTokens * D;
-  const uint32_t sa = base + 2 * kTileBytes + uint32_t(lane >> 4) * 16;
-  u32x4_t ks, vs;
-  __asm__ volatile("ds_read_b128 %0, %1" : "=v"(ks) : "v"(sa));
-  __asm__ volatile("ds_read_b128 %0, %1 offset:64" : "=v"(vs) : "v"(sa));
+  const uint32_t sa = base + 2 * kTileBytes + uint32_t(4 * (lane >> 4) + (lane & 3)) * 4;
+  float ks, vs;
+  __asm__ volatile("ds_read_b32 %0, %1" : "=v"(ks) : "v"(sa));
+  __asm__ volatile("ds_read_b32 %0, %1 offset:64" : "=v"(vs) : "v"(sa));
   __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   __asm__ volatile("" : "+v"(ks));
   __asm__ volatile("" : "+v"(vs));
-  f.ks = make_uint4(ks.x, ks.y, ks.z, ks.w);
-  f.vs = make_uint4(vs.x, vs.y, vs.z, vs.w);
+  f.ks = ks;
+  f.vs = vs;
 }
 
 // load_block_lds with the LDS reads written out, then one wait for all of

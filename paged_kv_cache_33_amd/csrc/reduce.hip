@@ -6,51 +6,31 @@
 // "MLSys Engineer - Inference Systems Q&A", Q4 (multiply by exp(m_old - m_new)),
 // applied to whole partitions:
 //   w_k = l_k * 2^(m_k - M),   out = sum_k w_k o_k / sum_k w_k.
-// One work-group per (query head, sequence); the weights are computed once into
-// LDS, then the threads split the partitions and the output dims.
 #include "device_common.h"
 #include "launch.h"
 
 namespace pagedkv {
 namespace {
 
-constexpr int kReduceThreads = 256;
+constexpr int kReduceThreads = 512;
 
-// Block-wide max / sum of one value per thread (256 threads = 4 waves).
-__device__ __forceinline__ float block_max(float v, float* scratch) {
-  v = cross_row_max(row16_max(v));
-  const int w = threadIdx.x / kWave;
-  __syncthreads();
-  if (threadIdx.x % kWave == 0) scratch[w] = v;
-  __syncthreads();
-  float r = scratch[0];
-#pragma unroll
-  for (int i = 1; i < kReduceThreads / kWave; ++i) r = fmaxf(r, scratch[i]);
-  return r;
-}
-__device__ __forceinline__ float block_sum(float v, float* scratch) {
-  v = cross_row_sum(row16_sum(v));
-  const int w = threadIdx.x / kWave;
-  __syncthreads();
-  if (threadIdx.x % kWave == 0) scratch[w] = v;
-  __syncthreads();
-  float r = 0.f;
-#pragma unroll
-  for (int i = 0; i < kReduceThreads / kWave; ++i) r += scratch[i];
-  return r;
-}
-
-// Thread t owns the four output dims 4*(t % R) .. +3 (one 16-byte load per
-// partition row, R = D / 4 threads per row) and partitions k = t / R,
-// t / R + G, ... with G = 256 / R groups; four independent accumulators keep
-// four partition rows in flight per thread, and the G group sums meet in LDS.
+// One work-group per (query head, sequence).  Thread t owns the four output
+// dims 4*(t % R) .. +3 (one 16-byte load per partition row, R = D / 4
+// threads per row) and partitions k = t / R, t / R + G, ... (G = 512 / R
+// groups).  Each thread merges its partitions as it loads them (the same
+// rule, one partition at a time: a running max, the denominator and the sum
+// rescaled whenever the max rises), four partitions' loads in flight at a
+// time, so one pass over the partials suffices; the G group results meet in
+// LDS, merged by the same rule.  A sequence of 196 partitions (100,000
+// tokens in 512-token partitions) is 7 partitions per thread.
 template <typename Tr, int D>
 __global__ __launch_bounds__(kReduceThreads) void lse_reduce_kernel(ReduceArgs a) {
   constexpr int R = D / 4;
   constexpr int G = kReduceThreads / R;
-  extern __shared__ float sm_w[];  // [num_partitions] weights
-  __shared__ float sm_red[kReduceThreads / kWave];
-  __shared__ __attribute__((aligned(16))) float sm_part[G][D];
+  constexpr int U = 4;  // partitions in flight per thread
+  __shared__ float sm_m[G];
+  __shared__ float sm_l[G];
+  __shared__ __attribute__((aligned(16))) float sm_o[G][D];
   using S = typename Tr::storage;
 
   const int h = blockIdx.x;
@@ -71,50 +51,55 @@ __global__ __launch_bounds__(kReduceThreads) void lse_reduce_kernel(ReduceArgs a
   const float* l = a.ws_l + base;
   const float4* o = reinterpret_cast<const float4*>(a.ws_o + base * D);
 
-  float mx = -INFINITY;
-  for (int k = threadIdx.x; k < nparts; k += kReduceThreads) mx = fmaxf(mx, m[k]);
-  const float M = block_max(mx, sm_red);
-
-  float tot = 0.f;
-  for (int k = threadIdx.x; k < nparts; k += kReduceThreads) {
-    const float wk = l[k] * fast_exp2(m[k] - M);
-    sm_w[k] = wk;
-    tot += wk;
-  }
-  const float total = block_sum(tot, sm_red);  // its barriers also publish sm_w
-
   const int xv = threadIdx.x % R;
   const int kg = threadIdx.x / R;
-  float4 acc[4];
-#pragma unroll
-  for (int u = 0; u < 4; ++u) acc[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-  auto fma4 = [](float w, const float4 v, float4& c) {
-    c.x = fmaf(w, v.x, c.x);
-    c.y = fmaf(w, v.y, c.y);
-    c.z = fmaf(w, v.z, c.z);
-    c.w = fmaf(w, v.w, c.w);
+  float M = -INFINITY, L = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  auto merge = [&](float mk, float lk, float4 ok) {
+    const float Mn = fmaxf(M, mk);
+    const float so = fast_exp2(M - Mn);   // 0 while nothing is merged (M = -inf)
+    const float wk = lk * fast_exp2(mk - Mn);
+    L = fmaf(L, so, wk);
+    acc.x = fmaf(acc.x, so, wk * ok.x);
+    acc.y = fmaf(acc.y, so, wk * ok.y);
+    acc.z = fmaf(acc.z, so, wk * ok.z);
+    acc.w = fmaf(acc.w, so, wk * ok.w);
+    M = Mn;
   };
   int k = kg;
-  for (; k + 3 * G < nparts; k += 4 * G) {
-    float4 v[4];
+  for (; k + (U - 1) * G < nparts; k += U * G) {
+    float mk[U], lk[U];
+    float4 ok[U];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) v[u] = o[size_t(k + u * G) * R + xv];
+    for (int u = 0; u < U; ++u) {
+      mk[u] = m[k + u * G];
+      lk[u] = l[k + u * G];
+      ok[u] = o[size_t(k + u * G) * R + xv];
+    }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) fma4(sm_w[k + u * G], v[u], acc[u]);
+    for (int u = 0; u < U; ++u) merge(mk[u], lk[u], ok[u]);
   }
-  for (; k < nparts; k += G) fma4(sm_w[k], o[size_t(k) * R + xv], acc[0]);
-  float4 r;
-  r.x = (acc[0].x + acc[1].x) + (acc[2].x + acc[3].x);
-  r.y = (acc[0].y + acc[1].y) + (acc[2].y + acc[3].y);
-  r.z = (acc[0].z + acc[1].z) + (acc[2].z + acc[3].z);
-  r.w = (acc[0].w + acc[1].w) + (acc[2].w + acc[3].w);
-  *reinterpret_cast<float4*>(&sm_part[kg][4 * xv]) = r;
+  for (; k < nparts; k += G) merge(m[k], l[k], o[size_t(k) * R + xv]);
+
+  if (xv == 0) {
+    sm_m[kg] = M;
+    sm_l[kg] = L;
+  }
+  *reinterpret_cast<float4*>(&sm_o[kg][4 * xv]) = acc;
   __syncthreads();
-  for (int x = threadIdx.x; x < D; x += kReduceThreads) {
-    float sum = 0.f;
+  for (int x = threadIdx.x; x < D; x += blockDim.x) {
+    float Mx = -INFINITY;
 #pragma unroll
-    for (int g = 0; g < G; ++g) sum += sm_part[g][x];
-    out[x] = Tr::from_f32(sum / total);
+    for (int g = 0; g < G; ++g) Mx = fmaxf(Mx, sm_m[g]);
+    float tot = 0.f, sum = 0.f;
+#pragma unroll 8
+    for (int g = 0; g < G; ++g) {
+      if (sm_m[g] == -INFINITY) continue;  // a group with no partition
+      const float sc = fast_exp2(sm_m[g] - Mx);
+      tot = fmaf(sm_l[g], sc, tot);
+      sum = fmaf(sm_o[g][x], sc, sum);
+    }
+    out[x] = Tr::from_f32(sum / tot);
   }
 }
 
@@ -124,7 +109,7 @@ hipError_t launch_reduce(const ReduceArgs& a, bool bf16_out, hipStream_t s) {
   if (a.B == 0 || a.H == 0) return hipSuccess;
   const dim3 grid(a.H, a.B);
   const dim3 block(kReduceThreads);
-  const size_t shmem = size_t(a.num_partitions) * sizeof(float);
+  const size_t shmem = 0;
   if (bf16_out && a.head_dim == 128)
     hipLaunchKernelGGL((lse_reduce_kernel<Bf16, 128>), grid, block, shmem, s, a);
   else if (bf16_out && a.head_dim == 64)
