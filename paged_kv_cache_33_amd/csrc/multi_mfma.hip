@@ -267,57 +267,196 @@ __device__ __forceinline__ void load_scales_lds_asm(MfmaFrag<E, D>& f, uint32_t 
   f.vs = vs;
 }
 
-// load_block_lds with the LDS reads written out, then one wait for all of
-// them.  The compiler does not see these reads as LDS accesses, so it does
-// not order them after the in-flight global-to-LDS loads of later blocks
-// (it cannot tell the ring's buffers apart); the explicit block waits and
-// the barrier provide that order.  It also takes an asm result as ready at
-// once, so after the wait every loaded register passes through an empty
-// volatile statement: volatile statements keep their order, so no use can
-// move above the wait.
+// The K half and the V half of load_block_lds_asm, each with its own wait.
 template <typename E, int D>
-__device__ __forceinline__ void load_block_lds_asm(MfmaFrag<E, D>& f, uint32_t base, int lane) {
-  using S = typename E::storage;
-  constexpr int X = E::kChunk;
+__device__ __forceinline__ void load_k_lds_asm(MfmaFrag<E, D>& f, uint32_t base, int lane) {
   constexpr int KL = MfmaFrag<E, D>::KL;
-  constexpr int MC = MfmaShape<D>::MC;
-  constexpr int kTileBytes = kBlockTokens * D * int(sizeof(S));
-  constexpr int kRowStep = 16 * kBlockTokens * int(sizeof(S));  // 16 dims of V
-  static_assert(X * int(sizeof(S)) == 16, "16-byte K chunks");
-  const int n = lane & 15, q = lane >> 4;
+  static_assert(E::kChunk * int(sizeof(typename E::storage)) == 16, "16-byte K chunks");
   const uint32_t ka = base + uint32_t(lane) * 16;
-  const uint32_t va = base + kTileBytes + uint32_t(n * kBlockTokens + 4 * q) * uint32_t(sizeof(S));
   u32x4_t k[KL];
 #pragma unroll
   for (int i = 0; i < KL; ++i)
     __asm__ volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(k[i]) : "v"(ka), "i"(i * kWave * 16));
+  __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int i = 0; i < KL; ++i) {
+    __asm__ volatile("" : "+v"(k[i]));
+    f.k[i] = make_uint4(k[i].x, k[i].y, k[i].z, k[i].w);
+  }
+}
+// V operands mc0 .. mc0 + MC - 1 (all of them by default).
+template <typename E, int D, int MC = MfmaShape<D>::MC, int mc0 = 0>
+__device__ __forceinline__ void load_v_lds_asm(MfmaFrag<E, D>& f, uint32_t base, int lane) {
+  using S = typename E::storage;
+  constexpr int kTileBytes = kBlockTokens * D * int(sizeof(S));
+  constexpr int kRowStep = 16 * kBlockTokens * int(sizeof(S));  // 16 dims of V
+  const int n = lane & 15, q = lane >> 4;
+  const uint32_t va = base + kTileBytes + uint32_t(n * kBlockTokens + 4 * q) * uint32_t(sizeof(S));
   if constexpr (MfmaFrag<E, D>::kFp8) {
     uint32_t v[MC];
 #pragma unroll
     for (int mc = 0; mc < MC; ++mc)
-      __asm__ volatile("ds_read_b32 %0, %1 offset:%2" : "=v"(v[mc]) : "v"(va), "i"(mc * kRowStep));
+      __asm__ volatile("ds_read_b32 %0, %1 offset:%2"
+                       : "=v"(v[mc]) : "v"(va), "i"((mc0 + mc) * kRowStep));
     __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
     for (int mc = 0; mc < MC; ++mc) {
       __asm__ volatile("" : "+v"(v[mc]));
-      f.v[mc] = v[mc];
+      f.v[mc0 + mc] = v[mc];
     }
   } else {
     u32x2_t v[MC];
 #pragma unroll
     for (int mc = 0; mc < MC; ++mc)
-      __asm__ volatile("ds_read_b64 %0, %1 offset:%2" : "=v"(v[mc]) : "v"(va), "i"(mc * kRowStep));
+      __asm__ volatile("ds_read_b64 %0, %1 offset:%2"
+                       : "=v"(v[mc]) : "v"(va), "i"((mc0 + mc) * kRowStep));
     __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
     for (int mc = 0; mc < MC; ++mc) {
       __asm__ volatile("" : "+v"(v[mc]));
-      f.v[mc] = make_uint2(v[mc].x, v[mc].y);
+      f.v[mc0 + mc] = make_uint2(v[mc].x, v[mc].y);
     }
   }
+}
+
+// load_block_lds with the LDS reads written out, then a wait for them.  The
+// compiler does not see these reads as LDS accesses, so it does not order
+// them after the in-flight global-to-LDS loads of later blocks (it cannot tell
+// the ring's buffers apart); the explicit block waits and the barrier provide
+// that order.  It also takes an asm result as ready at once, so after the wait
+// every loaded register passes through an empty volatile statement: volatile
+// statements keep their order, so no use can move above the wait.
+template <typename E, int D>
+__device__ __forceinline__ void load_block_lds_asm(MfmaFrag<E, D>& f, uint32_t base, int lane) {
+  load_k_lds_asm<E, D>(f, base, lane);
+  load_v_lds_asm<E, D>(f, base, lane);
+}
+
+// Two consecutive 16-token blocks a, b (keys key0 .. key0 + 31), read from
+// their LDS stages sa, sb, for kT column tiles, with one 32-deep product per
+// output tile for P V.  The contraction runs over the 32 keys in the order
+// lane quarter q holds them: tokens 4q..4q+3 of a, then tokens 4q..4q+3 of b.
+// That is where the score accumulators of S_a = K_a Q^T and S_b = K_b Q^T
+// already put them (register j: token 4q + j), and where the V^T operand
+// takes them from the two token-minor V tiles (8 bytes of each for bf16), so
+// a pair needs no lane exchange and half the P V instructions of two 16-deep
+// products.  The softmax runs once over both blocks (one reference max for
+// the pair).  Masks as in compute_block_tiles, with nfirst / nvalid relative
+// to the pair's first token.  To stay within 256 VGPRs at two waves per SIMD,
+// the operands are read in stages: K of a, its products; K of b, its
+// products; then V in two halves of the dims, each followed by its products.
+// bf16 and fp8 pools.
+template <typename E, int D, bool kTail, bool kCausal, int kT>
+__device__ __forceinline__ void compute_pair_lds(uint32_t sa, uint32_t sb,
+                                                 const bf16x8_t (*qop)[MfmaShape<D>::KI],
+                                                 MfmaState<D>* st, int nfirst, int nvalid,
+                                                 float scale_log2, int lane, int key0,
+                                                 const int* lo, const int* limit) {
+  static_assert(E::kKind != Kind::kInt8, "pairs take pools without row scales");
+  constexpr int MC = MfmaShape<D>::MC;
+  const int q = lane >> 4;
+  floatx4_t s[2][kT];
 #pragma unroll
-  for (int i = 0; i < KL; ++i) {
-    __asm__ volatile("" : "+v"(k[i]));
-    f.k[i] = make_uint4(k[i].x, k[i].y, k[i].z, k[i].w);
+  for (int h = 0; h < 2; ++h) {
+    MfmaFrag<E, D> f;
+    load_k_lds_asm<E, D>(f, h ? sb : sa, lane);
+#pragma unroll
+    for (int tt = 0; tt < kT; ++tt) s[h][tt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < MfmaShape<D>::KI; ++i) {
+      const bf16x8_t kop = k_operand<E, D>(f, i);
+#pragma unroll
+      for (int tt = 0; tt < kT; ++tt)
+        s[h][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[tt][i], s[h][tt], 0, 0, 0);
+    }
+  }
+  // raw scores, -inf where masked (by select: the slot may hold NaN)
+  float lmax[kT];
+  bool exceeds = false;
+#pragma unroll
+  for (int tt = 0; tt < kT; ++tt) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int t = 16 * h + 4 * q + j;  // token within the pair
+        const bool masked = (kTail && (t >= nvalid || t < nfirst)) ||
+                            (kCausal && (key0 + t > limit[tt] || key0 + t < lo[tt]));
+        if (masked) s[h][tt][j] = -INFINITY;
+      }
+    lmax[tt] = __builtin_elementwise_maximum(
+        __builtin_elementwise_maximum(
+            __builtin_elementwise_maximum(s[0][tt][0], s[0][tt][1]),
+            __builtin_elementwise_maximum(s[0][tt][2], s[0][tt][3])),
+        __builtin_elementwise_maximum(
+            __builtin_elementwise_maximum(s[1][tt][0], s[1][tt][1]),
+            __builtin_elementwise_maximum(s[1][tt][2], s[1][tt][3])));
+    lmax[tt] *= scale_log2;
+    exceeds = exceeds || lmax[tt] > st[tt].m + kRescaleSlack;
+  }
+  if (__builtin_amdgcn_ballot_w64(exceeds) != 0) {  // wave-uniform; as in compute_block_tiles
+#pragma unroll
+    for (int tt = 0; tt < kT; ++tt) {
+      const float mx = cross_row_max(lmax[tt]);
+      const bool grow = mx > st[tt].m + kRescaleSlack;
+      const float alpha = grow ? fast_exp2(st[tt].m - mx) : 1.f;
+      st[tt].l *= alpha;
+#pragma unroll
+      for (int mc = 0; mc < MC; ++mc) st[tt].o[mc] *= alpha;
+      st[tt].m = grow ? mx : st[tt].m;
+    }
+  }
+  bf16x8_t pop[kT];
+#pragma unroll
+  for (int tt = 0; tt < kT; ++tt) {
+    const float mref = (kCausal && st[tt].m == -INFINITY) ? 0.f : st[tt].m;
+    uint32_t pk[4];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      float pw[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        pw[j] = fast_exp2(__builtin_fmaf(s[h][tt][j], scale_log2, -mref));
+      pk[2 * h] = pack_bf16x2(pw[0], pw[1]);
+      pk[2 * h + 1] = pack_bf16x2(pw[2], pw[3]);
+    }
+    constexpr uint32_t kOnes = 0x3F803F80u;  // two bf16 1.0
+    float l = st[tt].l;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) l = dot2_bf16(pk[k], kOnes, l);
+    st[tt].l = l;
+    pop[tt] = __builtin_bit_cast(bf16x8_t, make_uint4(pk[0], pk[1], pk[2], pk[3]));
+  }
+  auto pv = [&](const MfmaFrag<E, D>& fa, const MfmaFrag<E, D>& fb, int mc) {
+    uint2 va = v_operand<E, D>(fa, mc), vb = v_operand<E, D>(fb, mc);
+    if (kTail) {  // tokens outside the range get weight 0; their V must be 0, not NaN
+      const int t = 4 * q;
+      va.x = zero_masked_pair(va.x, t >= nfirst && t < nvalid, t + 1 >= nfirst && t + 1 < nvalid);
+      va.y = zero_masked_pair(va.y, t + 2 >= nfirst && t + 2 < nvalid,
+                              t + 3 >= nfirst && t + 3 < nvalid);
+      const int u = 16 + 4 * q;
+      vb.x = zero_masked_pair(vb.x, u >= nfirst && u < nvalid, u + 1 >= nfirst && u + 1 < nvalid);
+      vb.y = zero_masked_pair(vb.y, u + 2 >= nfirst && u + 2 < nvalid,
+                              u + 3 >= nfirst && u + 3 < nvalid);
+    }
+    const bf16x8_t vop = __builtin_bit_cast(bf16x8_t, make_uint4(va.x, va.y, vb.x, vb.y));
+#pragma unroll
+    for (int tt = 0; tt < kT; ++tt)
+      st[tt].o[mc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop[tt], st[tt].o[mc], 0, 0, 0);
+  };
+  {
+    MfmaFrag<E, D> fa, fb;
+    load_v_lds_asm<E, D, MC / 2, 0>(fa, sa, lane);
+    load_v_lds_asm<E, D, MC / 2, 0>(fb, sb, lane);
+#pragma unroll
+    for (int mc = 0; mc < MC / 2; ++mc) pv(fa, fb, mc);
+  }
+  {
+    MfmaFrag<E, D> fa, fb;
+    load_v_lds_asm<E, D, MC / 2, MC / 2>(fa, sa, lane);
+    load_v_lds_asm<E, D, MC / 2, MC / 2>(fb, sb, lane);
+#pragma unroll
+    for (int mc = MC / 2; mc < MC; ++mc) pv(fa, fb, mc);
   }
 }
 
@@ -356,7 +495,11 @@ __global__ __launch_bounds__(kMultiWaves* kWave, kTiles == 1 ? 3 : 2) void chunk
   static_assert(!kInt8 || kTiles == 1, "int8: one tile per wave (two do not fit 256 VGPRs)");
   constexpr int kPer = kInt8 ? (kCodeUnits + kWave - 1) / kWave + 1
                              : (kUnits + kThreads - 1) / kThreads;  // loads per thread per block
-  constexpr int kStages = 4;
+  // Prefill chunks of bf16 and fp8 pools compute blocks in pairs (one
+  // 32-deep P V product per pair; compute_pair_lds), six ring stages: the
+  // pair computing and two pairs in flight.
+  constexpr bool kPairs = kTiles == 2 && !kInt8;
+  constexpr int kStages = kPairs ? 6 : 4;
   constexpr int kTabWin = 1024;
   __shared__ uint4 sm_kv[kStages][kUnits];
   __shared__ int sm_tab[kTabWin];
@@ -508,53 +651,103 @@ __global__ __launch_bounds__(kMultiWaves* kWave, kTiles == 1 ? 3 : 2) void chunk
   };
   fill_tab();
   uint32_t ok_bits = 0;  // bit j % 32: block j's entry was inside the pool
-  for (int t = 0; t < kStages - 1 && wjb + t < wje; ++t) {
-    if (wjb + t - tb >= kTabWin) { tb = wjb + t; fill_tab(); }
-    ok_bits |= uint32_t(issue(wjb + t, sm_tab[wjb + t - tb])) << ((wjb + t) & 31);
-  }
-  for (int j = wjb; j < wje; ++j) {
-    wait_block(min(kStages - 2, wje - 1 - j));
-    // block j is in LDS for every wave, and every wave is done with block
-    // j - 1, whose buffer the next issue reuses
-    lds_barrier();
-    const int jn = j + kStages - 1;
-    if (jn < wje) {
-      if (jn - tb >= kTabWin) { tb = jn; fill_tab(); }  // uniform
-      ok_bits = (ok_bits & ~(1u << (jn & 31))) | (uint32_t(issue(jn, sm_tab[jn - tb])) << (jn & 31));
-    }
+  // Block j of the wave's range, alone: the per-block arithmetic.
+  auto single = [&](int j) {
     const int key0 = j * kBlockTokens;
-    if (active && key0 < kend && key0 + kBlockTokens > klo) {  // uniform per wave
-      if (!((ok_bits >> (j & 31)) & 1u)) {
-        bad = 1;
-      } else {
-        MfmaFrag<E, D> f;
-        const uint32_t stage = lds_offset(&sm_kv[j % kStages][0]);
-        load_block_lds_asm<E, D>(f, stage, lane);
-        if constexpr (kInt8) load_scales_lds_asm<E, D>(f, stage, lane);
+    if (!(active && key0 < kend && key0 + kBlockTokens > klo)) return;  // uniform per wave
+    if (!((ok_bits >> (j & 31)) & 1u)) {
+      bad = 1;
+      return;
+    }
+    MfmaFrag<E, D> f;
+    const uint32_t stage = lds_offset(&sm_kv[j % kStages][0]);
+    load_block_lds_asm<E, D>(f, stage, lane);
+    if constexpr (kInt8) load_scales_lds_asm<E, D>(f, stage, lane);
+    const int nvalid = kend - key0;
+    const int nfirst = klo - key0;
+    const bool open =
+        nvalid >= kBlockTokens && key0 + kBlockTokens - 1 <= kmin && key0 >= klo_max;
+    // The branch encloses the tiles' work, so the masked path's (the V
+    // operands' masking, shared by the tiles) stays inside it instead of
+    // being computed ahead of the branch for every block.  Both tiles run
+    // phase by phase in one pass; a set with one tile of columns runs one.
+    if (kTiles == 1 || ntiles == kTiles) {
+      if (open)
+        compute_block_tiles<E, D, false, false, kTiles>(f, qop, st, 0, nvalid, a.scale_log2, lane,
+                                                        0, lo, limit);
+      else
+        compute_block_tiles<E, D, true, true, kTiles>(f, qop, st, nfirst, nvalid, a.scale_log2,
+                                                      lane, key0, lo, limit);
+    } else {
+      if (open)
+        compute_block_tiles<E, D, false, false, 1>(f, qop, st, 0, nvalid, a.scale_log2, lane, 0,
+                                                   lo, limit);
+      else
+        compute_block_tiles<E, D, true, true, 1>(f, qop, st, nfirst, nvalid, a.scale_log2, lane,
+                                                 key0, lo, limit);
+    }
+  };
+  auto issue_at = [&](int jn) {  // uniform
+    if (jn - tb >= kTabWin) { tb = jn; fill_tab(); }
+    ok_bits = (ok_bits & ~(1u << (jn & 31))) | (uint32_t(issue(jn, sm_tab[jn - tb])) << (jn & 31));
+  };
+  if constexpr (kPairs) {
+    // blocks wjb .. wjb + 3 in flight; at pair (j, j + 1) the two after it
+    // may still be loading
+    for (int t = 0; t < kStages - 2 && wjb + t < wje; ++t) issue_at(wjb + t);
+    for (int j = wjb; j < wje; j += 2) {
+      wait_vm_later<kStages - 4, kPer>(min(kStages - 4, max(wje - 2 - j, 0)));
+      // blocks j, j + 1 are in LDS for every wave, and every wave is done with
+      // the previous pair, whose buffers the next issues reuse
+      lds_barrier();
+      if (j + kStages - 2 < wje) issue_at(j + kStages - 2);
+      if (j + kStages - 1 < wje) issue_at(j + kStages - 1);
+      const int key0 = j * kBlockTokens;
+      const bool in_a = active && key0 < kend && key0 + kBlockTokens > klo;
+      const bool in_b = j + 1 < wje && active && key0 + kBlockTokens < kend &&
+                        key0 + 2 * kBlockTokens > klo;
+      if (in_a && in_b) {  // uniform per wave
+        if (!((ok_bits >> (j & 31)) & (ok_bits >> ((j + 1) & 31)) & 1u)) {
+          bad = 1;
+          continue;
+        }
+        const uint32_t sa = lds_offset(&sm_kv[j % kStages][0]);
+        const uint32_t sb = lds_offset(&sm_kv[(j + 1) % kStages][0]);
         const int nvalid = kend - key0;
         const int nfirst = klo - key0;
         const bool open =
-            nvalid >= kBlockTokens && key0 + kBlockTokens - 1 <= kmin && key0 >= klo_max;
-        // The branch encloses the tiles' work, so the masked path's (the V
-        // operands' masking, shared by the tiles) stays inside it instead of
-        // being computed ahead of the branch for every block.  Both tiles run
-        // phase by phase in one pass; a set with one tile of columns runs one.
-        if (kTiles == 1 || ntiles == kTiles) {
+            nvalid >= 2 * kBlockTokens && key0 + 2 * kBlockTokens - 1 <= kmin && key0 >= klo_max;
+        if (ntiles == kTiles) {
           if (open)
-            compute_block_tiles<E, D, false, false, kTiles>(f, qop, st, 0, nvalid, a.scale_log2,
-                                                            lane, 0, lo, limit);
+            compute_pair_lds<E, D, false, false, kTiles>(sa, sb, qop, st, 0, nvalid,
+                                                         a.scale_log2, lane, 0, lo, limit);
           else
-            compute_block_tiles<E, D, true, true, kTiles>(f, qop, st, nfirst, nvalid,
-                                                          a.scale_log2, lane, key0, lo, limit);
+            compute_pair_lds<E, D, true, true, kTiles>(sa, sb, qop, st, nfirst, nvalid,
+                                                       a.scale_log2, lane, key0, lo, limit);
         } else {
           if (open)
-            compute_block_tiles<E, D, false, false, 1>(f, qop, st, 0, nvalid, a.scale_log2, lane,
-                                                       0, lo, limit);
+            compute_pair_lds<E, D, false, false, 1>(sa, sb, qop, st, 0, nvalid, a.scale_log2,
+                                                    lane, 0, lo, limit);
           else
-            compute_block_tiles<E, D, true, true, 1>(f, qop, st, nfirst, nvalid, a.scale_log2,
-                                                     lane, key0, lo, limit);
+            compute_pair_lds<E, D, true, true, 1>(sa, sb, qop, st, nfirst, nvalid, a.scale_log2,
+                                                  lane, key0, lo, limit);
         }
+      } else if (in_a) {
+        single(j);
+      } else if (in_b) {
+        single(j + 1);
       }
+    }
+  } else {
+    for (int t = 0; t < kStages - 1 && wjb + t < wje; ++t) issue_at(wjb + t);
+    for (int j = wjb; j < wje; ++j) {
+      wait_block(min(kStages - 2, wje - 1 - j));
+      // block j is in LDS for every wave, and every wave is done with block
+      // j - 1, whose buffer the next issue reuses
+      lds_barrier();
+      const int jn = j + kStages - 1;
+      if (jn < wje) issue_at(jn);
+      single(j);
     }
   }
 
