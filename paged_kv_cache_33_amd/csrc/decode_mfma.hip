@@ -66,6 +66,22 @@ __device__ __forceinline__ float fresh_score(const uint4 (&krow)[MfmaShape<D>::K
   return cross_row_sum(dot);
 }
 
+// Split mode with several work-groups per CU (one-byte caches): the work-groups
+// sharing a CU are not served alike (the instruction arbiter of each SIMD
+// prefers the oldest wave, so the oldest work-group's loads go first), and
+// with items dealt round-robin the starved worker finishes last: on the
+// long-context mix with an fp8 cache, first items took 9 to 31 us and workers
+// ended between 45 and 78 us.  Each worker therefore raises its waves'
+// priority with the number of items it still has, so one that has fallen
+// behind is served first (fp8 84.7 -> 80.5 us, int8 92.7 -> 90.8 us; with
+// one work-group per CU there is nothing to balance).  p: 0..3, wave-uniform.
+__device__ __forceinline__ void set_priority(int p) {
+  if (p >= 3) __builtin_amdgcn_s_setprio(3);
+  else if (p == 2) __builtin_amdgcn_s_setprio(2);
+  else if (p == 1) __builtin_amdgcn_s_setprio(1);
+  else __builtin_amdgcn_s_setprio(0);
+}
+
 // One work item: partition `part` of sequence b, head tile `tile_y` (a KV
 // head and a group of up to 16 of its query heads).
 template <typename E, int D, int kWaves>
@@ -390,6 +406,7 @@ __device__ __forceinline__ void mfma_split_worker(const DecodeArgs& a, const int
   if (cur.nblk == 0) tile_a = -1;
 
   for (int i = blockIdx.x; i < n_items; i += stride) {
+    if constexpr (kGroupsPerCu<E, true> > 1) set_priority((n_items - i + stride - 1) / stride - 1);
     // the next item's table window, in flight while this item streams
     const Item nxt = describe(i + stride);
     const int win_next = load_window(nxt);
@@ -558,6 +575,8 @@ __global__ __launch_bounds__((kWavesOf<E, kSplit> * kWave),
       return;
     }
     for (int i = blockIdx.x; i < n_items; i += gridDim.x) {
+      if constexpr (kGroupsPerCu<E, kSplit> > 1)
+        set_priority((n_items - i + int(gridDim.x) - 1) / int(gridDim.x) - 1);
       int b, part;
       locate_item(sm_starts, a.B, i, b, part);
       mfma_item<E, D, kWaves>(a, part, blockIdx.y, b, sm_merge);
