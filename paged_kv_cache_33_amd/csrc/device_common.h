@@ -162,9 +162,18 @@ struct Int8 {
   __device__ __forceinline__ static act from_f32(float f) { return f32_to_bf16_rne(f); }
 };
 
+// int8 codes already rewritten as bf16 values (exact; see i8x2_to_bf16x2), in
+// the bf16 tile layout, with the int8 cache's row scales still to apply.
+struct Int8AsBf16 {
+  using storage = uint16_t;
+  using act = uint16_t;
+  static constexpr Kind kKind = Kind::kInt8;
+  static constexpr int kChunk = 8;
+};
+
 // Elements stored as one-byte codes (fp8 and int8 caches).
 template <typename Tr>
-constexpr bool kByteCodes = Tr::kKind == Kind::kFp8 || Tr::kKind == Kind::kInt8;
+constexpr bool kByteCodes = sizeof(typename Tr::storage) == 1;
 
 // Two int8 codes (bytes 0, 1 of `w`, or bytes 2, 3 when `hi`) as a bf16 pair:
 // exact, since |code| <= 127 needs 7 significant bits, so each float's upper

@@ -253,8 +253,8 @@ __device__ __forceinline__ uint32_t lds_offset(const void* p) {
 // An int8 block's row scales from its LDS stage, where they follow the two
 // tiles (K's 16, then V's); lane (n, q) takes those of token 4q + n % 4 (see
 // MfmaScales).
-template <typename E, int D>
-__device__ __forceinline__ void load_scales_lds_asm(MfmaFrag<E, D>& f, uint32_t base, int lane) {
+template <typename E, int D, typename F>
+__device__ __forceinline__ void load_scales_lds_asm(F& f, uint32_t base, int lane) {
   constexpr int kTileBytes = kBlockTokens * D;
   const uint32_t sa = base + 2 * kTileBytes + uint32_t(4 * (lane >> 4) + (lane & 3)) * 4;
   float ks, vs;
@@ -330,6 +330,37 @@ template <typename E, int D>
 __device__ __forceinline__ void load_block_lds_asm(MfmaFrag<E, D>& f, uint32_t base, int lane) {
   load_k_lds_asm<E, D>(f, base, lane);
   load_v_lds_asm<E, D>(f, base, lane);
+}
+
+// One 16-byte unit of an int8 block's LDS stage (K units first: chunk u / 16
+// of token u % 16, 16 dims; then V rows, 16 tokens each) rewritten as bf16
+// into the bf16 layout of the same block at cv (K [d/8][16][8], then V
+// [d][16]): two 16-byte units.  int8 codes are bf16 values, so the operands
+// the products see are exactly those of converting in registers.  The LDS
+// accesses are written out: the compiler would otherwise order them after
+// the stage ring's global-to-LDS loads in flight (see load_block_lds_asm).
+template <int D>
+__device__ __forceinline__ void convert_int8_unit_lds(uint32_t stage, uint32_t cv, int u) {
+  constexpr int kKUnits = kBlockTokens * D / 16;  // int8 K units; bf16 has twice as many
+  u32x4_t c;
+  __asm__ volatile("ds_read_b128 %0, %1" : "=v"(c) : "v"(stage + uint32_t(u) * 16));
+  __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __asm__ volatile("" : "+v"(c));
+  const u32x4_t lo = {i8x2_to_bf16x2<false>(c.x), i8x2_to_bf16x2<true>(c.x),
+                      i8x2_to_bf16x2<false>(c.y), i8x2_to_bf16x2<true>(c.y)};
+  const u32x4_t hi = {i8x2_to_bf16x2<false>(c.z), i8x2_to_bf16x2<true>(c.z),
+                      i8x2_to_bf16x2<false>(c.w), i8x2_to_bf16x2<true>(c.w)};
+  uint32_t a0, a1;  // destination units
+  if (u < kKUnits) {
+    const int c16 = u / kBlockTokens, t = u % kBlockTokens;
+    a0 = uint32_t((2 * c16) * kBlockTokens + t);
+    a1 = a0 + kBlockTokens;
+  } else {
+    a0 = uint32_t(2 * kKUnits + 2 * (u - kKUnits));
+    a1 = a0 + 1;
+  }
+  __asm__ volatile("ds_write_b128 %0, %1" ::"v"(cv + a0 * 16), "v"(lo) : "memory");
+  __asm__ volatile("ds_write_b128 %0, %1" ::"v"(cv + a1 * 16), "v"(hi) : "memory");
 }
 
 // Two consecutive 16-token blocks a, b (keys key0 .. key0 + 31), read from
@@ -506,6 +537,13 @@ __global__ __launch_bounds__(kMultiWaves* kWave, kTiles == 1 ? 3 : 2) void chunk
   constexpr int kTabWin = 1024;
   __shared__ uint4 sm_kv[kStages][kUnits];
   __shared__ int sm_tab[kTabWin];
+  // int8: each block is converted to bf16 once per work-group (every thread
+  // one 16-byte unit) into sm_cv, and the waves take their operands from
+  // there (C, the compute type, keeps the row scales).
+  constexpr bool kConvert = kInt8;
+  using C = std::conditional_t<kConvert, Int8AsBf16, E>;
+  constexpr int kCvUnits = 2 * kTileElems * 2 / 16;  // one bf16 block, K and V
+  __shared__ uint4 sm_cv[kConvert ? kCvUnits : 1];
 
   __shared__ int sm_order[kOrderBuckets + kMultiWaves + 1];
   const int b = __builtin_amdgcn_readfirstlane(
@@ -570,7 +608,7 @@ __global__ __launch_bounds__(kMultiWaves* kWave, kTiles == 1 ? 3 : 2) void chunk
 #pragma unroll
     for (int i = 0; i < KI; ++i) {
       uint4 raw = make_uint4(0u, 0u, 0u, 0u);
-      if (col_ok[tt]) raw = *reinterpret_cast<const uint4*>(qrow + query_dim0<E>(i, q));
+      if (col_ok[tt]) raw = *reinterpret_cast<const uint4*>(qrow + query_dim0<C>(i, q));
       qop[tt][i] = __builtin_bit_cast(bf16x8_t, raw);
     }
   }
@@ -655,16 +693,17 @@ __global__ __launch_bounds__(kMultiWaves* kWave, kTiles == 1 ? 3 : 2) void chunk
   fill_tab();
   uint32_t ok_bits = 0;  // bit j % 32: block j's entry was inside the pool
   // Block j of the wave's range, alone: the per-block arithmetic.
-  auto single = [&](int j) {
+  // (operands: where block j's K and V are, in the layout of C)
+  auto single = [&](int j, uint32_t operands) {
     const int key0 = j * kBlockTokens;
     if (!(active && key0 < kend && key0 + kBlockTokens > klo)) return;  // uniform per wave
     if (!((ok_bits >> (j & 31)) & 1u)) {
       bad = 1;
       return;
     }
-    MfmaFrag<E, D> f;
+    MfmaFrag<C, D> f;
     const uint32_t stage = lds_offset(&sm_kv[j % kStages][0]);
-    load_block_lds_asm<E, D>(f, stage, lane);
+    load_block_lds_asm<C, D>(f, operands, lane);
     if constexpr (kInt8) load_scales_lds_asm<E, D>(f, stage, lane);
     const int nvalid = kend - key0;
     const int nfirst = klo - key0;
@@ -676,17 +715,17 @@ __global__ __launch_bounds__(kMultiWaves* kWave, kTiles == 1 ? 3 : 2) void chunk
     // phase by phase in one pass; a set with one tile of columns runs one.
     if (kTiles == 1 || ntiles == kTiles) {
       if (open)
-        compute_block_tiles<E, D, false, false, kTiles>(f, qop, st, 0, nvalid, a.scale_log2, lane,
+        compute_block_tiles<C, D, false, false, kTiles>(f, qop, st, 0, nvalid, a.scale_log2, lane,
                                                         0, lo, limit);
       else
-        compute_block_tiles<E, D, true, true, kTiles>(f, qop, st, nfirst, nvalid, a.scale_log2,
+        compute_block_tiles<C, D, true, true, kTiles>(f, qop, st, nfirst, nvalid, a.scale_log2,
                                                       lane, key0, lo, limit);
     } else {
       if (open)
-        compute_block_tiles<E, D, false, false, 1>(f, qop, st, 0, nvalid, a.scale_log2, lane, 0,
+        compute_block_tiles<C, D, false, false, 1>(f, qop, st, 0, nvalid, a.scale_log2, lane, 0,
                                                    lo, limit);
       else
-        compute_block_tiles<E, D, true, true, 1>(f, qop, st, nfirst, nvalid, a.scale_log2, lane,
+        compute_block_tiles<C, D, true, true, 1>(f, qop, st, nfirst, nvalid, a.scale_log2, lane,
                                                  key0, lo, limit);
     }
   };
@@ -705,6 +744,8 @@ __global__ __launch_bounds__(kMultiWaves* kWave, kTiles == 1 ? 3 : 2) void chunk
       lds_barrier();
       if (j + kStages - 2 < wje) issue_at(j + kStages - 2);
       if (j + kStages - 1 < wje) issue_at(j + kStages - 1);
+      const uint32_t sa = lds_offset(&sm_kv[j % kStages][0]);
+      const uint32_t sb = lds_offset(&sm_kv[(j + 1) % kStages][0]);
       const int key0 = j * kBlockTokens;
       const bool in_a = active && key0 < kend && key0 + kBlockTokens > klo;
       const bool in_b = j + 1 < wje && active && key0 + kBlockTokens < kend &&
@@ -714,8 +755,6 @@ __global__ __launch_bounds__(kMultiWaves* kWave, kTiles == 1 ? 3 : 2) void chunk
           bad = 1;
           continue;
         }
-        const uint32_t sa = lds_offset(&sm_kv[j % kStages][0]);
-        const uint32_t sb = lds_offset(&sm_kv[(j + 1) % kStages][0]);
         const int nvalid = kend - key0;
         const int nfirst = klo - key0;
         const bool open =
@@ -736,9 +775,9 @@ __global__ __launch_bounds__(kMultiWaves* kWave, kTiles == 1 ? 3 : 2) void chunk
                                                   lane, key0, lo, limit);
         }
       } else if (in_a) {
-        single(j);
+        single(j, sa);
       } else if (in_b) {
-        single(j + 1);
+        single(j + 1, sb);
       }
     }
   } else {
@@ -750,7 +789,14 @@ __global__ __launch_bounds__(kMultiWaves* kWave, kTiles == 1 ? 3 : 2) void chunk
       lds_barrier();
       const int jn = j + kStages - 1;
       if (jn < wje) issue_at(jn);
-      single(j);
+      uint32_t operands = lds_offset(&sm_kv[j % kStages][0]);
+      if constexpr (kConvert) {
+        const uint32_t cv = lds_offset(&sm_cv[0]);
+        if (tid < 2 * kTileUnits) convert_int8_unit_lds<D>(operands, cv, tid);
+        lds_barrier();  // the bf16 block is complete
+        operands = cv;
+      }
+      single(j, operands);
     }
   }
 
