@@ -60,6 +60,22 @@ __device__ __forceinline__ float quad_bcast(float v) {
       __builtin_amdgcn_update_dpp(0, __float_as_int(v), J * 0x55, 0xF, 0xF, false));
 }
 
+// The four row scales of a quad's tokens 4q .. 4q + 3 (lane n % 4 of the quad
+// holds token 4q + n % 4's, see MfmaScales), for every lane, where a lane uses
+// them under a mask.  A broadcast reads another lane, so it must run with the
+// whole wave active: left to itself the compiler may compute it under the
+// mask, where only the lanes that use it are on, and a broadcast from a lane
+// that is off returns 0 (seen in an int8 kernel: the weights of some causally
+// masked columns came out 0).  The empty asm statement makes the values exist
+// here, before any masking.
+__device__ __forceinline__ void quad_scales(float v, float (&out)[4]) {
+  out[0] = quad_bcast<0>(v);
+  out[1] = quad_bcast<1>(v);
+  out[2] = quad_bcast<2>(v);
+  out[3] = quad_bcast<3>(v);
+  __asm__ volatile("" : "+v"(out[0]), "+v"(out[1]), "+v"(out[2]), "+v"(out[3]));
+}
+
 template <typename E, int D>
 struct MfmaFrag : MfmaScales<E> {
   static constexpr bool kFp8 = kByteCodes<E>;  // one-byte codes
@@ -192,7 +208,7 @@ __device__ __forceinline__ void compute_block_tiles(const MfmaFrag<E, D>& f,
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       sc[tt][j] = s[tt][j];
-      if constexpr (kInt8) {  // token 4q + j's K row scale
+      if constexpr (kInt8) {  // token 4q + j's K row scale (used by every lane)
         const float ks[4] = {quad_bcast<0>(f.ks), quad_bcast<1>(f.ks), quad_bcast<2>(f.ks),
                              quad_bcast<3>(f.ks)};
         sc[tt][j] = sc[tt][j] * scale_log2 * ks[j];
@@ -232,6 +248,8 @@ __device__ __forceinline__ void compute_block_tiles(const MfmaFrag<E, D>& f,
   // weights rounded to bf16 for the matrix core; the denominator sums the
   // same rounded values.  Causal: a column that has seen no position yet
   // (every score -inf) takes weight 0, not 2^(-inf - -inf).
+  float vs[4];  // int8: the V row scales of tokens 4q + j
+  if constexpr (kInt8) quad_scales(f.vs, vs);
   short4_t pop[kT];
 #pragma unroll
   for (int tt = 0; tt < kT; ++tt) {
@@ -251,8 +269,6 @@ __device__ __forceinline__ void compute_block_tiles(const MfmaFrag<E, D>& f,
     if constexpr (kInt8) {
       // the products take p times the token's V row scale (0 where masked:
       // the scale may be NaN there); the denominator above sums p alone
-      const float vs[4] = {quad_bcast<0>(f.vs), quad_bcast<1>(f.vs), quad_bcast<2>(f.vs),
-                           quad_bcast<3>(f.vs)};
       float pv[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) pv[j] = masked[tt][j] ? 0.f : pw[j] * vs[j];
