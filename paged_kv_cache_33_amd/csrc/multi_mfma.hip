@@ -523,7 +523,6 @@ __global__ __launch_bounds__(kMultiWaves* kWave, kTiles == 1 ? 3 : 2) void chunk
   // issues the same number of loads per block.
   constexpr int kCodeUnits = 2 * kTileUnits / kMultiWaves;
   static_assert(kTileUnits % kCodeUnits == 0 && kScaleUnits == kMultiWaves, "int8 stage split");
-  static_assert(!kInt8 || kTiles == 1, "int8: one tile per wave (two do not fit 256 VGPRs)");
   constexpr int kPer = kInt8 ? (kCodeUnits + kWave - 1) / kWave + 1
                              : (kUnits + kThreads - 1) / kThreads;  // loads per thread per block
   // bf16 and fp8 pools compute blocks in pairs (one 32-deep P V product per
@@ -858,19 +857,24 @@ hipError_t launch_multi_mfma(const MultiArgs& a, Kind kind, int head_dim, hipStr
   // bf16 at K = 8, g = 8, and against the per-wave kernel 11-22% faster for
   // fp8 and 2-10% for int8 (whose stages add the row scales).  One tile per
   // wave measured slower with two tiles of columns (8%, bf16) and on fp8
-  // prefill chunks (2.5%), and equal on bf16 and int8 prefill chunks.
+  // prefill chunks (2.5%), and equal on bf16 prefill chunks.  int8 pools take
+  // it since their blocks are converted to bf16 once per work-group (two tiles
+  // per wave then fit 256 VGPRs): 512-token prefill chunks 1.456 -> 1.298 ms
+  // against the per-wave kernel.
   const int64_t tiles = (int64_t(a.max_query_len) * g + kHeadsPerTile - 1) / kHeadsPerTile;
   const bool chunk1 = tiles >= 3 && tiles <= kMultiWaves;
   const bool chunk = !chunk1 && a.tiles_per_set == 2 &&
                      ((kind == Kind::kBf16 && sets >= 2) ||
-                      (kind == Kind::kFp8 && sets >= kMultiWaves));
+                      ((kind == Kind::kFp8 || kind == Kind::kInt8) && sets >= kMultiWaves));
   const bool bf16 = kind == Kind::kBf16;
   void (*kern)(MultiArgs) =
       chunk1  ? (bf16                 ? chunk_kernel<Bf16, 1>(head_dim)
                  : kind == Kind::kFp8 ? chunk_kernel<Fp8, 1>(head_dim)
                  : kind == Kind::kInt8 ? chunk_kernel<Int8, 1>(head_dim)
                                        : nullptr)
-      : chunk ? (bf16 ? chunk_kernel<Bf16, 2>(head_dim) : chunk_kernel<Fp8, 2>(head_dim))
+      : chunk ? (bf16                 ? chunk_kernel<Bf16, 2>(head_dim)
+                 : kind == Kind::kFp8 ? chunk_kernel<Fp8, 2>(head_dim)
+                                      : chunk_kernel<Int8, 2>(head_dim))
               : (bf16                  ? multi_kernel<Bf16>(head_dim, a.tiles_per_set)
                  : kind == Kind::kFp8  ? multi_kernel<Fp8>(head_dim, a.tiles_per_set)
                  : kind == Kind::kInt8 ? multi_kernel<Int8>(head_dim, a.tiles_per_set)
