@@ -738,28 +738,38 @@ __global__ __launch_bounds__(kMultiWaves* kWave, kTiles == 1 ? 3 : 2) void chunk
     for (int t = 0; t < kStages - 2 && wjb + t < wje; ++t) issue_at(wjb + t);
     int j = wjb;
     // First the pairs every column of the work-group sees whole (all of a
-    // prefill chunk's blocks but those on its diagonal): one straight path,
-    // every wave computing all its tiles (an inactive wave or a partial set
-    // computes on zero queries and writes nothing; a block whose entry lies
-    // outside the pool computes on tile 0 and turns the columns NaN).  With
-    // the branches of the general loop below (open or masked pair, a single
+    // prefill chunk's or a verification's blocks but those on its diagonal):
+    // one straight path, an active wave computing all its tiles (a partial
+    // set computes on zero queries and writes nothing; a block whose entry
+    // lies outside the pool computes on tile 0 and turns the columns NaN), an
+    // inactive one only keeping the loads and barriers in step.  With the
+    // branches of the general loop below (open or masked pair, a single
     // block, nothing) the compiler moved the output accumulators between
     // registers at every join: about 100 moves per pair.
-    if constexpr (kTiles == 2) {
+    {
       const int kmin_wg = pos0 + cbeg / g;                                // first column's position
       const int klo_wg = window_first(pos0 + (cend - 1) / g, a.window);  // last column's first key
-      for (; j + 1 < wje && j * kBlockTokens >= klo_wg &&
-             j * kBlockTokens + 2 * kBlockTokens - 1 <= kmin_wg;
-           j += 2) {
-        wait_vm_later<kStages - 4, kPer>(min(kStages - 4, max(wje - 2 - j, 0)));
+      auto open = [&](int jj) {
+        return jj + 1 < wje && jj * kBlockTokens >= klo_wg &&
+               jj * kBlockTokens + 2 * kBlockTokens - 1 <= kmin_wg;
+      };
+      auto step = [&](int jj) {
+        wait_vm_later<kStages - 4, kPer>(min(kStages - 4, max(wje - 2 - jj, 0)));
         lds_barrier();
-        if (j + kStages - 2 < wje) issue_at(j + kStages - 2);
-        if (j + kStages - 1 < wje) issue_at(j + kStages - 1);
-        bad |= int(~(ok_bits >> (j & 31)) & 1u) | int(~(ok_bits >> ((j + 1) & 31)) & 1u);
-        compute_pair_lds<C, D, false, false, kTiles>(lds_offset(&sm_kv[j % kStages][0]),
-                                                     lds_offset(&sm_kv[(j + 1) % kStages][0]),
-                                                     qop, st, 0, 2 * kBlockTokens,
-                                                     a.scale_log2, lane, 0, lo, limit);
+        if (jj + kStages - 2 < wje) issue_at(jj + kStages - 2);
+        if (jj + kStages - 1 < wje) issue_at(jj + kStages - 1);
+      };
+      if (active) {
+        for (; open(j); j += 2) {
+          step(j);
+          bad |= int(~(ok_bits >> (j & 31)) & 1u) | int(~(ok_bits >> ((j + 1) & 31)) & 1u);
+          compute_pair_lds<C, D, false, false, kTiles>(lds_offset(&sm_kv[j % kStages][0]),
+                                                       lds_offset(&sm_kv[(j + 1) % kStages][0]),
+                                                       qop, st, 0, 2 * kBlockTokens,
+                                                       a.scale_log2, lane, 0, lo, limit);
+        }
+      } else {
+        for (; open(j); j += 2) step(j);
       }
     }
     for (; j < wje; j += 2) {
