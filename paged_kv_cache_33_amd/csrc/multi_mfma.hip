@@ -817,22 +817,47 @@ __global__ __launch_bounds__(kMultiWaves* kWave, kTiles == 1 ? 3 : 2) void chunk
     }
   } else {
     for (int t = 0; t < kStages - 1 && wjb + t < wje; ++t) issue_at(wjb + t);
-    for (int j = wjb; j < wje; ++j) {
-      wait_block(min(kStages - 2, wje - 1 - j));
-      // block j is in LDS for every wave, and every wave is done with block
-      // j - 1, whose buffer the next issue reuses
+    // block j is in LDS for every wave, and every wave is done with block
+    // j - 1, whose buffer the next issue reuses; then (int8) the block in bf16
+    auto step = [&](int jj) -> uint32_t {
+      wait_block(min(kStages - 2, wje - 1 - jj));
       lds_barrier();
-      const int jn = j + kStages - 1;
+      const int jn = jj + kStages - 1;
       if (jn < wje) issue_at(jn);
-      uint32_t operands = lds_offset(&sm_kv[j % kStages][0]);
+      uint32_t operands = lds_offset(&sm_kv[jj % kStages][0]);
       if constexpr (kConvert) {
         const uint32_t cv = lds_offset(&sm_cv[0]);
         if (tid < 2 * kTileUnits) convert_int8_unit_lds<D>(operands, cv, tid);
         lds_barrier();  // the bf16 block is complete
         operands = cv;
       }
-      single(j, operands);
+      return operands;
+    };
+    int j = wjb;
+    {
+      // the blocks every column of the work-group sees whole, on a straight
+      // path (as for pairs above)
+      const int kmin_wg = pos0 + cbeg / g;
+      const int klo_wg = window_first(pos0 + (cend - 1) / g, a.window);
+      auto open = [&](int jj) {
+        return jj < wje && jj * kBlockTokens >= klo_wg &&
+               jj * kBlockTokens + kBlockTokens - 1 <= kmin_wg;
+      };
+      if (active) {
+        for (; open(j); ++j) {
+          const uint32_t operands = step(j);
+          bad |= int(~(ok_bits >> (j & 31)) & 1u);
+          MfmaFrag<C, D> f;
+          load_block_lds_asm<C, D>(f, operands, lane);
+          if constexpr (kInt8) load_scales_lds_asm<E, D>(f, lds_offset(&sm_kv[j % kStages][0]), lane);
+          compute_block_tiles<C, D, false, false, kTiles>(f, qop, st, 0, kBlockTokens,
+                                                          a.scale_log2, lane, 0, lo, limit);
+        }
+      } else {
+        for (; open(j); ++j) step(j);
+      }
     }
+    for (; j < wje; ++j) single(j, step(j));
   }
 
   // Each wave finishes its own columns: lane (q, n) holds dims 16mc + 4q .. +3
