@@ -245,6 +245,11 @@ __device__ __forceinline__ void wait_vm_later(int later) {
   }
 }
 
+// Fourth word of a raw buffer resource (stride 0, byte-addressed range): the
+// 32-bit data format, without which the gfx9 family treats every access as
+// out of range.
+constexpr int kRawBufferWord3 = 0x00020000;
+
 // Byte offset of an LDS object (the low 32 bits of its generic address).
 __device__ __forceinline__ uint32_t lds_offset(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
@@ -372,21 +377,18 @@ __device__ __forceinline__ void convert_int8_unit_lds(uint32_t stage, uint32_t c
 // takes them from the two token-minor V tiles (8 bytes of each for bf16), so
 // a pair needs no lane exchange and half the P V instructions of two 16-deep
 // products.  The softmax runs once over both blocks (one reference max for
-// the pair).  Masks as in compute_block_tiles, with nfirst / nvalid relative
-// to the pair's first token.  To stay within 256 VGPRs at two waves per SIMD,
-// the operands are read in stages: K of a, its products; K of b, its
-// products; then V in two halves of the dims, each followed by its products.
-// bf16 and fp8 pools.
-template <typename E, int D, bool kTail, bool kCausal, int kT>
-__device__ __forceinline__ void compute_pair_lds(uint32_t sa, uint32_t sb,
-                                                 const bf16x8_t (*qop)[MfmaShape<D>::KI],
-                                                 MfmaState<D>* st, int nfirst, int nvalid,
-                                                 float scale_log2, int lane, int key0,
-                                                 const int* lo, const int* limit) {
+// the pair).  bf16 and fp8 pools.  The work comes in three parts, so a
+// caller can compute the next pair's scores while this pair's weights and
+// products run: pair_scores, pair_rescale, pair_pv.
+//
+// pair_scores: the raw scores s[h][tt] (h = 0: block a, 1: block b).  To
+// stay within 256 VGPRs at two waves per SIMD the operands are read in
+// stages: K of a, its products; K of b, its products.
+template <typename E, int D, int kT>
+__device__ __forceinline__ void pair_scores(uint32_t sa, uint32_t sb,
+                                            const bf16x8_t (*qop)[MfmaShape<D>::KI],
+                                            floatx4_t (*s)[kT], int lane) {
   static_assert(E::kKind != Kind::kInt8, "pairs take pools without row scales");
-  constexpr int MC = MfmaShape<D>::MC;
-  const int q = lane >> 4;
-  floatx4_t s[2][kT];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     MfmaFrag<E, D> f;
@@ -401,7 +403,18 @@ __device__ __forceinline__ void compute_pair_lds(uint32_t sa, uint32_t sb,
         s[h][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[tt][i], s[h][tt], 0, 0, 0);
     }
   }
-  // raw scores, -inf where masked (by select: the slot may hold NaN)
+}
+
+// pair_rescale: masks (as in compute_block_tiles, with nfirst / nvalid
+// relative to the pair's first token: -inf by select, the slot may hold NaN),
+// then the reference max: when some score exceeds it by more than the slack,
+// the state is rescaled (wave-uniform branch, as in compute_block_tiles).
+template <int D, bool kTail, bool kCausal, int kT>
+__device__ __forceinline__ void pair_rescale(floatx4_t (*s)[kT], MfmaState<D>* st, int nfirst,
+                                             int nvalid, float scale_log2, int lane, int key0,
+                                             const int* lo, const int* limit) {
+  constexpr int MC = MfmaShape<D>::MC;
+  const int q = lane >> 4;
   float lmax[kT];
   bool exceeds = false;
 #pragma unroll
@@ -425,7 +438,7 @@ __device__ __forceinline__ void compute_pair_lds(uint32_t sa, uint32_t sb,
     lmax[tt] *= scale_log2;
     exceeds = exceeds || lmax[tt] > st[tt].m + kRescaleSlack;
   }
-  if (__builtin_amdgcn_ballot_w64(exceeds) != 0) {  // wave-uniform; as in compute_block_tiles
+  if (__builtin_amdgcn_ballot_w64(exceeds) != 0) {
 #pragma unroll
     for (int tt = 0; tt < kT; ++tt) {
       const float mx = cross_row_max(lmax[tt]);
@@ -437,6 +450,18 @@ __device__ __forceinline__ void compute_pair_lds(uint32_t sa, uint32_t sb,
       st[tt].m = grow ? mx : st[tt].m;
     }
   }
+}
+
+// pair_pv: the weights 2^(s scale - m) as bf16, their row sums, and
+// O^T += V^T P^T, the V operands read in two halves of the dims, each
+// followed by its products.  With kTail the V of tokens outside the range
+// is zeroed (weight 0 times NaN would be NaN).
+template <typename E, int D, bool kTail, bool kCausal, int kT>
+__device__ __forceinline__ void pair_pv(uint32_t sa, uint32_t sb, const floatx4_t (*s)[kT],
+                                        MfmaState<D>* st, int nfirst, int nvalid,
+                                        float scale_log2, int lane) {
+  constexpr int MC = MfmaShape<D>::MC;
+  const int q = lane >> 4;
   bf16x8_t pop[kT];
 #pragma unroll
   for (int tt = 0; tt < kT; ++tt) {
@@ -460,7 +485,7 @@ __device__ __forceinline__ void compute_pair_lds(uint32_t sa, uint32_t sb,
   }
   auto pv = [&](const MfmaFrag<E, D>& fa, const MfmaFrag<E, D>& fb, int mc) {
     uint2 va = v_operand<E, D>(fa, mc), vb = v_operand<E, D>(fb, mc);
-    if (kTail) {  // tokens outside the range get weight 0; their V must be 0, not NaN
+    if (kTail) {
       const int t = 4 * q;
       va.x = zero_masked_pair(va.x, t >= nfirst && t < nvalid, t + 1 >= nfirst && t + 1 < nvalid);
       va.y = zero_masked_pair(va.y, t + 2 >= nfirst && t + 2 < nvalid,
@@ -489,6 +514,159 @@ __device__ __forceinline__ void compute_pair_lds(uint32_t sa, uint32_t sb,
 #pragma unroll
     for (int mc = MC / 2; mc < MC; ++mc) pv(fa, fb, mc);
   }
+}
+
+// LDS reads written out without their wait: the K pieces of a block's stage
+// (as load_k_lds_asm), and V pieces mc0 .. mc0 + H - 1 (as load_v_lds_asm).
+// wait_lds<N> then waits until at most N of this wave's LDS operations are
+// outstanding (they complete in order); the registers a wait covers pass
+// through an empty volatile statement after it, so no use moves above it.
+template <typename E, int D>
+using VRaw = std::conditional_t<MfmaFrag<E, D>::kFp8, uint32_t, u32x2_t>;
+template <int KL>
+__device__ __forceinline__ void issue_k_lds(u32x4_t (&k)[KL], uint32_t base, int lane) {
+  const uint32_t ka = base + uint32_t(lane) * 16;
+#pragma unroll
+  for (int i = 0; i < KL; ++i)
+    __asm__ volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(k[i]) : "v"(ka), "i"(i * kWave * 16));
+}
+template <typename E, int D, int H, int mc0>
+__device__ __forceinline__ void issue_v_lds(VRaw<E, D> (&v)[H], uint32_t base, int lane) {
+  using S = typename E::storage;
+  constexpr int kTileBytes = kBlockTokens * D * int(sizeof(S));
+  constexpr int kRowStep = 16 * kBlockTokens * int(sizeof(S));
+  const int n = lane & 15, q = lane >> 4;
+  const uint32_t va = base + kTileBytes + uint32_t(n * kBlockTokens + 4 * q) * uint32_t(sizeof(S));
+#pragma unroll
+  for (int mc = 0; mc < H; ++mc) {
+    if constexpr (MfmaFrag<E, D>::kFp8)
+      __asm__ volatile("ds_read_b32 %0, %1 offset:%2"
+                       : "=v"(v[mc]) : "v"(va), "i"((mc0 + mc) * kRowStep));
+    else
+      __asm__ volatile("ds_read_b64 %0, %1 offset:%2"
+                       : "=v"(v[mc]) : "v"(va), "i"((mc0 + mc) * kRowStep));
+  }
+}
+template <int N>
+__device__ __forceinline__ void wait_lds() {
+  static_assert(N >= 0 && N < 16, "lgkmcnt holds 4 bits");
+  __asm__ volatile("s_waitcnt lgkmcnt(%0)" ::"n"(N) : "memory");
+}
+template <typename T, int N>
+__device__ __forceinline__ void pin(T (&r)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) __asm__ volatile("" : "+v"(r[i]));
+}
+
+// One step of the software-pipelined pair loop, for pairs every column sees
+// whole (no masks): the scores of the next pair (stages na, nb) into sn, and
+// the weights and P V products of the current pair (scores sc, already
+// rescaled for; stages ca, cb).  All LDS reads of the step are issued at its
+// start (K of the next pair, then the first half of the current pair's V;
+// the second half once the first K has landed), so the waits find them
+// mostly done, and the exponentials of the current weights have no
+// dependence on any of them.
+template <typename E, int D, int kT>
+__device__ __forceinline__ void pair_pipelined(uint32_t na, uint32_t nb, uint32_t ca, uint32_t cb,
+                                               const bf16x8_t (*qop)[MfmaShape<D>::KI],
+                                               const floatx4_t (*sc)[kT], floatx4_t (*sn)[kT],
+                                               MfmaState<D>* st, float scale_log2, int lane) {
+  constexpr int KL = MfmaFrag<E, D>::KL;
+  constexpr int MC = MfmaShape<D>::MC;
+  constexpr int H = MC / 2;
+  static_assert(KL + 2 * H < 16, "outstanding LDS reads fit lgkmcnt");
+  u32x4_t kr[2][KL];
+  VRaw<E, D> v1[2][H], v2[2][H];
+  issue_k_lds(kr[0], na, lane);
+  issue_k_lds(kr[1], nb, lane);
+  issue_v_lds<E, D, H, 0>(v1[0], ca, lane);
+  issue_v_lds<E, D, H, 0>(v1[1], cb, lane);
+  // the current pair's weights and their row sums
+  bf16x8_t pop[kT];
+#pragma unroll
+  for (int tt = 0; tt < kT; ++tt) {
+    const float mref = st[tt].m;
+    uint32_t pk[4];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      float pw[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        pw[j] = fast_exp2(__builtin_fmaf(sc[h][tt][j], scale_log2, -mref));
+      pk[2 * h] = pack_bf16x2(pw[0], pw[1]);
+      pk[2 * h + 1] = pack_bf16x2(pw[2], pw[3]);
+    }
+    constexpr uint32_t kOnes = 0x3F803F80u;  // two bf16 1.0
+    float l = st[tt].l;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) l = dot2_bf16(pk[k], kOnes, l);
+    st[tt].l = l;
+    pop[tt] = __builtin_bit_cast(bf16x8_t, make_uint4(pk[0], pk[1], pk[2], pk[3]));
+  }
+  // the next pair's scores, block by block as its K lands
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    if (h == 0) wait_lds<KL + 2 * H>();
+    else wait_lds<2 * H>();
+    pin(kr[h]);
+    MfmaFrag<E, D> f;
+#pragma unroll
+    for (int i = 0; i < KL; ++i) f.k[i] = make_uint4(kr[h][i].x, kr[h][i].y, kr[h][i].z, kr[h][i].w);
+#pragma unroll
+    for (int tt = 0; tt < kT; ++tt) sn[h][tt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < MfmaShape<D>::KI; ++i) {
+      const bf16x8_t kop = k_operand<E, D>(f, i);
+#pragma unroll
+      for (int tt = 0; tt < kT; ++tt)
+        sn[h][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[tt][i], sn[h][tt], 0, 0, 0);
+    }
+  }
+  // the current pair's products, the V halves in turn
+  auto pv = [&](const VRaw<E, D>& ra, const VRaw<E, D>& rb, int mc) {
+    MfmaFrag<E, D> fa, fb;
+    if constexpr (MfmaFrag<E, D>::kFp8) {
+      fa.v[mc] = ra;
+      fb.v[mc] = rb;
+    } else {
+      fa.v[mc] = make_uint2(ra.x, ra.y);
+      fb.v[mc] = make_uint2(rb.x, rb.y);
+    }
+    const uint2 va = v_operand<E, D>(fa, mc), vb = v_operand<E, D>(fb, mc);
+    const bf16x8_t vop = __builtin_bit_cast(bf16x8_t, make_uint4(va.x, va.y, vb.x, vb.y));
+#pragma unroll
+    for (int tt = 0; tt < kT; ++tt)
+      st[tt].o[mc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop[tt], st[tt].o[mc], 0, 0, 0);
+  };
+  // The compiler checks no hazard against registers an asm statement writes,
+  // and the score products above may still be reading their accumulator
+  // operands from registers these reads reuse: 16 wait states first.
+  __asm__ volatile("s_nop 7\n\ts_nop 7" ::: "memory");
+  issue_v_lds<E, D, H, H>(v2[0], ca, lane);
+  issue_v_lds<E, D, H, H>(v2[1], cb, lane);
+  wait_lds<2 * H>();
+  pin(v1[0]);
+  pin(v1[1]);
+#pragma unroll
+  for (int mc = 0; mc < H; ++mc) pv(v1[0][mc], v1[1][mc], mc);
+  wait_lds<0>();
+  pin(v2[0]);
+  pin(v2[1]);
+#pragma unroll
+  for (int mc = 0; mc < H; ++mc) pv(v2[0][mc], v2[1][mc], H + mc);
+}
+
+// The whole pair: scores, masks and rescale, weights and products.
+template <typename E, int D, bool kTail, bool kCausal, int kT>
+__device__ __forceinline__ void compute_pair_lds(uint32_t sa, uint32_t sb,
+                                                 const bf16x8_t (*qop)[MfmaShape<D>::KI],
+                                                 MfmaState<D>* st, int nfirst, int nvalid,
+                                                 float scale_log2, int lane, int key0,
+                                                 const int* lo, const int* limit) {
+  floatx4_t s[2][kT];
+  pair_scores<E, D, kT>(sa, sb, qop, s, lane);
+  pair_rescale<D, kTail, kCausal, kT>(s, st, nfirst, nvalid, scale_log2, lane, key0, lo, limit);
+  pair_pv<E, D, kTail, kCausal, kT>(sa, sb, s, st, nfirst, nvalid, scale_log2, lane);
 }
 
 // Several column sets per sequence and KV head (a prefill chunk, or draft
@@ -532,8 +710,14 @@ __global__ __launch_bounds__(kMultiWaves* kWave, kTiles == 1 ? 3 : 2) void chunk
   // draft tokens at g = 8, 528 -> 518 us (bf16), 416 -> 380 us (fp8).  One
   // tile per wave stays at three work-groups per CU (164 VGPRs, 52 KiB LDS).
   constexpr bool kPairs = !kInt8;
-  constexpr int kStages = kPairs ? 6 : 4;
   constexpr int kTabWin = 1024;
+  // Pairs on the software-pipelined path (see below) take eight stages where
+  // the work-groups of a CU still fit its 160 KiB of LDS (two with two tiles
+  // per wave, three with one).
+  constexpr int kStageBytes = kUnits * 16;
+  constexpr bool kPipe =
+      kPairs && (kTiles == 2 ? 2 : 3) * (8 * kStageBytes + 4 * kTabWin + 1024) <= 160 * 1024;
+  constexpr int kStages = kPipe ? 8 : kPairs ? 6 : 4;
   __shared__ uint4 sm_kv[kStages][kUnits];
   __shared__ int sm_tab[kTabWin];
   // int8: each block is converted to bf16 once per work-group (every thread
@@ -553,6 +737,7 @@ __global__ __launch_bounds__(kMultiWaves* kWave, kTiles == 1 ? 3 : 2) void chunk
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
   const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
+  __builtin_assume(w >= 0 && w < kMultiWaves);
   const int n = lane & 15, q = lane >> 4;
   const int g = a.H / a.num_kv_heads;
 
@@ -632,13 +817,15 @@ __global__ __launch_bounds__(kMultiWaves* kWave, kTiles == 1 ? 3 : 2) void chunk
   // several blocks are in flight without holding registers.  A stage holds
   // the K tile's units, then V's (then, for int8, the row scales); the units
   // of one wave-wide load are all K, all V or all scales of one tile.
-  auto issue = [&](int j, int p) -> bool {
-    const bool ok = p >= 0 && p < a.num_blocks;
-    const int64_t tile = (int64_t(ok ? p : 0) * a.num_kv_heads + kvh) * kTileBytes;
-    uint4* ring = &sm_kv[j % kStages][0];
+  // e: the block's table word as staged (see fill_tab): its tile's index, bit
+  // 31 set for an entry outside the pool (whose tile index is then kvh's in
+  // block 0, loaded but never used).
+  auto issue = [&](int j, int e) {
+    const int64_t pt = int64_t(e & 0x7fffffff);  // tile index p H_kv + kvh
+    const int64_t tile = pt * kTileBytes;
+    uint4* ring = &sm_kv[unsigned(j) % kStages][0];
     if constexpr (kInt8) {
       // the tile's 16 row scales: floats 16 (p H_kv + kvh) .. of the scale region
-      const int64_t pt = int64_t(ok ? p : 0) * a.num_kv_heads + kvh;
       const int cu0 = w * kCodeUnits;  // uniform: all K or all V
       const char* src = (cu0 < kTileUnits ? kc : vc) + pt * kTileBytes +
                         int64_t((cu0 % kTileUnits) + lane) * 16;
@@ -657,20 +844,22 @@ __global__ __launch_bounds__(kMultiWaves* kWave, kTiles == 1 ? 3 : 2) void chunk
             ssrc, (__attribute__((address_space(3))) void*)(ring + 2 * kTileUnits + su0), 16, 0,
             0);
     } else {
+      // Buffer loads: the tile's address in a resource (scalar registers), the
+      // wave's first unit a scalar offset and the lane's 16 bytes a vector
+      // offset that never changes, so no lane holds a 64-bit address.
 #pragma unroll
       for (int k = 0; k < kPer; ++k) {
         const int u0 = w * kWave + k * kThreads;  // uniform
         if (u0 < kUnits) {
-          const int u = u0 + lane;
-          const char* src = u0 < kUnits / 2 ? kc + tile + int64_t(u) * 16
-                                            : vc + tile + int64_t(u - kUnits / 2) * 16;
-          __builtin_amdgcn_global_load_lds(src,
-                                           (__attribute__((address_space(3))) void*)(ring + u0),
-                                           16, 0, 0);
+          const bool is_k = u0 < kUnits / 2;
+          const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+              const_cast<char*>((is_k ? kc : vc) + tile), 0, int(kTileBytes), kRawBufferWord3);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              rsrc, (__attribute__((address_space(3))) void*)(ring + u0), 16, lane * 16,
+              (is_k ? u0 : u0 - kUnits / 2) * 16, 0, 0);
         }
       }
     }
-    return ok;
   };
   // vector-memory operations of this wave per block
   constexpr int kPerWave = kPer;
@@ -684,12 +873,39 @@ __global__ __launch_bounds__(kMultiWaves* kWave, kTiles == 1 ? 3 : 2) void chunk
   // a time, so the loop below consumes no vector-load result (the compiler
   // would wait for every load in flight before one); a refill (one barrier
   // that drains the loads in flight) comes once per kTabWin blocks.
+  // Each word is validated as it is staged: the tile index p H_kv + kvh of
+  // the entry p, or kvh's tile of block 0 with bit 31 set where p lies outside
+  // the pool (the launch checks that tile indices fit 31 bits).
   int tb = wjb;
   auto fill_tab = [&]() {
-    for (int i = tid; i < kTabWin && tb + i < wje; i += kThreads) sm_tab[i] = table[tb + i];
+    // (the first block through readfirstlane: the compiler then keeps no
+    // pointer per call site stepping along with the loops that call it)
+    const int32_t* row = table + __builtin_amdgcn_readfirstlane(tb);
+    for (int i = tid; i < kTabWin && tb + i < wje; i += kThreads) {
+      const int p = row[i];
+      const bool ok = p >= 0 && p < a.num_blocks;
+      sm_tab[i] = ((ok ? p : 0) * a.num_kv_heads + kvh) | (ok ? 0 : int(0x80000000u));
+    }
     __syncthreads();
   };
   fill_tab();
+  // The words of blocks wb .. wb + 63 in a register (lane i: block wb + i),
+  // read from sm_tab once per 64 blocks; a block's word is then one lane read,
+  // with no LDS wait.
+  int wb = -(1 << 30), win = 0;
+  auto table_word = [&](int jn) -> int {  // uniform
+    if (jn - tb >= kTabWin) {
+      tb = jn;
+      fill_tab();
+      wb = -(1 << 30);
+    }
+    if (jn - wb >= kWave) {
+      wb = jn;
+      const int i = jn - tb + lane;
+      win = i < kTabWin ? sm_tab[i] : 0;
+    }
+    return __builtin_amdgcn_readlane(win, jn - wb);
+  };
   uint32_t ok_bits = 0;  // bit j % 32: block j's entry was inside the pool
   // Block j of the wave's range, alone: the per-block arithmetic.
   // (operands: where block j's K and V are, in the layout of C)
@@ -729,8 +945,10 @@ __global__ __launch_bounds__(kMultiWaves* kWave, kTiles == 1 ? 3 : 2) void chunk
     }
   };
   auto issue_at = [&](int jn) {  // uniform
-    if (jn - tb >= kTabWin) { tb = jn; fill_tab(); }
-    ok_bits = (ok_bits & ~(1u << (jn & 31))) | (uint32_t(issue(jn, sm_tab[jn - tb])) << (jn & 31));
+    const int e = table_word(jn);
+    issue(jn, e);
+    const uint32_t ok = (uint32_t(e) >> 31) ^ 1u;
+    ok_bits = (ok_bits & ~(1u << (jn & 31))) | (ok << (jn & 31));
   };
   if constexpr (kPairs) {
     // blocks wjb .. wjb + 3 in flight; at pair (j, j + 1) the two after it
@@ -753,23 +971,94 @@ __global__ __launch_bounds__(kMultiWaves* kWave, kTiles == 1 ? 3 : 2) void chunk
         return jj + 1 < wje && jj * kBlockTokens >= klo_wg &&
                jj * kBlockTokens + 2 * kBlockTokens - 1 <= kmin_wg;
       };
-      auto step = [&](int jj) {
-        wait_vm_later<kStages - 4, kPer>(min(kStages - 4, max(wje - 2 - jj, 0)));
-        lds_barrier();
-        if (jj + kStages - 2 < wje) issue_at(jj + kStages - 2);
-        if (jj + kStages - 1 < wje) issue_at(jj + kStages - 1);
+      auto slot = [&](int jj) { return lds_offset(&sm_kv[unsigned(jj) % kStages][0]); };
+      auto mark_bad = [&](int jj) {  // blocks jj, jj + 1 (jj even: one 2-bit field)
+        bad |= int(((ok_bits >> (jj & 31)) & 3u) ^ 3u);
       };
-      if (active) {
-        for (; open(j); j += 2) {
-          step(j);
-          bad |= int(~(ok_bits >> (j & 31)) & 1u) | int(~(ok_bits >> ((j + 1) & 31)) & 1u);
-          compute_pair_lds<C, D, false, false, kTiles>(lds_offset(&sm_kv[j % kStages][0]),
-                                                       lds_offset(&sm_kv[(j + 1) % kStages][0]),
-                                                       qop, st, 0, 2 * kBlockTokens,
-                                                       a.scale_log2, lane, 0, lo, limit);
+      if constexpr (kPipe) {
+        // Software-pipelined: while pair j's weights and P V products run, the
+        // scores of pair j + 2 are computed, so a wave has matrix products
+        // independent of its exponentials.  Eight stages (four pairs): at pair
+        // j the scores need pair j + 2 in LDS, pair j's V is still read, and
+        // the pair issued (j + 6, j + 7) reuses the stages of pair j - 2,
+        // which every wave has finished once past the barrier.  Invariant at
+        // the top of an iteration: blocks below j + kStages - 2 are issued.
+        if (open(j)) {
+          auto run = [&](auto act) {
+            constexpr bool kAct = decltype(act)::value;
+            auto rescale = [&](floatx4_t (*sc)[kTiles]) {
+              pair_rescale<D, false, false, kTiles>(sc, st, 0, 2 * kBlockTokens, a.scale_log2,
+                                                    lane, 0, lo, limit);
+            };
+            // pair j landed; the blocks after it may still be loading
+            wait_vm_later<kStages - 4, kPer>(min(kStages - 4, max(wje - 2 - j, 0)));
+            lds_barrier();
+            floatx4_t s0[2][kTiles], s1[2][kTiles];
+            if constexpr (kAct) {
+              pair_scores<C, D, kTiles>(slot(j), slot(j + 1), qop, s0, lane);
+              rescale(s0);
+            }
+            // one iteration: pair j's scores (rescaled for) in sc; pair j + 2
+            // whole, and the pair after it issued, so exactly its two blocks
+            // load after pair j + 2's: a fixed count to wait for.  The rescale
+            // for pair j + 2 comes last, after pair j's products, as the
+            // output accumulators then pass one branch per pair, in place.
+            auto cont = [&](int jj) { return open(jj + 2) && jj + 5 < wje; };
+            auto iter = [&](floatx4_t (*sc)[kTiles], floatx4_t (*sn)[kTiles]) {
+              __builtin_amdgcn_s_waitcnt(vm_wait_imm((kStages - 6) * kPer));
+              lds_barrier();
+              if (j + kStages - 2 < wje) issue_at(j + kStages - 2);
+              if (j + kStages - 1 < wje) issue_at(j + kStages - 1);
+              if constexpr (kAct) {
+                mark_bad(j);
+                pair_pipelined<C, D, kTiles>(slot(j + 2), slot(j + 3), slot(j), slot(j + 1), qop,
+                                             sc, sn, st, a.scale_log2, lane);
+                rescale(sn);
+              }
+              j += 2;
+            };
+            // the last pair of the path: its weights and products, and the
+            // issue that keeps the invariant of the general loop below
+            auto last = [&](floatx4_t (*sc)[kTiles]) {
+              lds_barrier();
+              if (j + kStages - 2 < wje) issue_at(j + kStages - 2);
+              if (j + kStages - 1 < wje) issue_at(j + kStages - 1);
+              if constexpr (kAct) {
+                mark_bad(j);
+                pair_pv<C, D, false, false, kTiles>(slot(j), slot(j + 1), sc, st, 0,
+                                                    2 * kBlockTokens, a.scale_log2, lane);
+              }
+              j += 2;
+            };
+            // two iterations per trip so the score buffers swap roles without copies
+            for (;;) {
+              if (!cont(j)) { last(s0); break; }
+              iter(s0, s1);
+              if (!cont(j)) { last(s1); break; }
+              iter(s1, s0);
+            }
+          };
+          if (active) run(std::true_type{});
+          else run(std::false_type{});
         }
       } else {
-        for (; open(j); j += 2) step(j);
+        auto step = [&](int jj) {
+          wait_vm_later<kStages - 4, kPer>(min(kStages - 4, max(wje - 2 - jj, 0)));
+          lds_barrier();
+          if (jj + kStages - 2 < wje) issue_at(jj + kStages - 2);
+          if (jj + kStages - 1 < wje) issue_at(jj + kStages - 1);
+        };
+        if (active) {
+          for (; open(j); j += 2) {
+            step(j);
+            mark_bad(j);
+            compute_pair_lds<C, D, false, false, kTiles>(slot(j), slot(j + 1), qop, st, 0,
+                                                         2 * kBlockTokens, a.scale_log2, lane, 0,
+                                                         lo, limit);
+          }
+        } else {
+          for (; open(j); j += 2) step(j);
+        }
       }
     }
     for (; j < wje; j += 2) {
@@ -906,6 +1195,8 @@ hipError_t launch_multi_mfma(const MultiArgs& a, Kind kind, int head_dim, hipStr
   if (a.tiles_per_set < 1 || a.tiles_per_set > 2 || a.sets_per_group < 1 ||
       a.sets_per_group > kMaxSetsPerGroup)
     return hipErrorInvalidValue;
+  // tile indices p H_kv + kvh are staged as 31-bit words
+  if (int64_t(a.num_blocks) * a.num_kv_heads > (int64_t(1) << 31)) return hipErrorInvalidValue;
   const int g = a.H / a.num_kv_heads;
   const int64_t set_cols = int64_t(kHeadsPerTile) * a.tiles_per_set;
   const int64_t sets = (int64_t(a.max_query_len) * g + set_cols - 1) / set_cols;
