@@ -518,33 +518,31 @@ __device__ __forceinline__ void pair_pv(uint32_t sa, uint32_t sb, const floatx4_
 
 // LDS reads written out without their wait: the K pieces of a block's stage
 // (as load_k_lds_asm), and V pieces mc0 .. mc0 + H - 1 (as load_v_lds_asm).
-// wait_lds<N> then waits until at most N of this wave's LDS operations are
-// outstanding (they complete in order); the registers a wait covers pass
-// through an empty volatile statement after it, so no use moves above it.
+// kl / vl: the lane's K / V address in stage 0, kOff the stage's byte offset
+// (an immediate of the read).  wait_lds<N> then waits until at most N of this
+// wave's LDS operations are outstanding (they complete in order); the
+// registers a wait covers pass through an empty volatile statement after it,
+// so no use moves above it.
 template <typename E, int D>
 using VRaw = std::conditional_t<MfmaFrag<E, D>::kFp8, uint32_t, u32x2_t>;
-template <int KL>
-__device__ __forceinline__ void issue_k_lds(u32x4_t (&k)[KL], uint32_t base, int lane) {
-  const uint32_t ka = base + uint32_t(lane) * 16;
+template <int KL, uint32_t kOff>
+__device__ __forceinline__ void issue_k_lds(u32x4_t (&k)[KL], uint32_t kl) {
 #pragma unroll
   for (int i = 0; i < KL; ++i)
-    __asm__ volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(k[i]) : "v"(ka), "i"(i * kWave * 16));
+    __asm__ volatile("ds_read_b128 %0, %1 offset:%2"
+                     : "=v"(k[i]) : "v"(kl), "i"(kOff + i * kWave * 16));
 }
-template <typename E, int D, int H, int mc0>
-__device__ __forceinline__ void issue_v_lds(VRaw<E, D> (&v)[H], uint32_t base, int lane) {
-  using S = typename E::storage;
-  constexpr int kTileBytes = kBlockTokens * D * int(sizeof(S));
-  constexpr int kRowStep = 16 * kBlockTokens * int(sizeof(S));
-  const int n = lane & 15, q = lane >> 4;
-  const uint32_t va = base + kTileBytes + uint32_t(n * kBlockTokens + 4 * q) * uint32_t(sizeof(S));
+template <typename E, int D, int H, int mc0, uint32_t kOff>
+__device__ __forceinline__ void issue_v_lds(VRaw<E, D> (&v)[H], uint32_t vl) {
+  constexpr int kRowStep = 16 * kBlockTokens * int(sizeof(typename E::storage));  // 16 dims
 #pragma unroll
   for (int mc = 0; mc < H; ++mc) {
     if constexpr (MfmaFrag<E, D>::kFp8)
       __asm__ volatile("ds_read_b32 %0, %1 offset:%2"
-                       : "=v"(v[mc]) : "v"(va), "i"((mc0 + mc) * kRowStep));
+                       : "=v"(v[mc]) : "v"(vl), "i"(kOff + (mc0 + mc) * kRowStep));
     else
       __asm__ volatile("ds_read_b64 %0, %1 offset:%2"
-                       : "=v"(v[mc]) : "v"(va), "i"((mc0 + mc) * kRowStep));
+                       : "=v"(v[mc]) : "v"(vl), "i"(kOff + (mc0 + mc) * kRowStep));
   }
 }
 template <int N>
@@ -559,28 +557,28 @@ __device__ __forceinline__ void pin(T (&r)[N]) {
 }
 
 // One step of the software-pipelined pair loop, for pairs every column sees
-// whole (no masks): the scores of the next pair (stages na, nb) into sn, and
-// the weights and P V products of the current pair (scores sc, already
-// rescaled for; stages ca, cb).  All LDS reads of the step are issued at its
-// start (K of the next pair, then the first half of the current pair's V;
-// the second half once the first K has landed), so the waits find them
-// mostly done, and the exponentials of the current weights have no
-// dependence on any of them.
-template <typename E, int D, int kT>
-__device__ __forceinline__ void pair_pipelined(uint32_t na, uint32_t nb, uint32_t ca, uint32_t cb,
+// whole (no masks): the scores of the next pair (stages at byte offsets kNa,
+// kNb) into sn, and the weights and P V products of the current pair (scores
+// sc, already rescaled for; stages kCa, kCb).  All LDS reads of the step are
+// issued at its start (K of the next pair, then the first half of the
+// current pair's V; the second half once the first K has landed), so the
+// waits find them mostly done, and the exponentials of the current weights
+// have no dependence on any of them.
+template <typename E, int D, int kT, uint32_t kNa, uint32_t kNb, uint32_t kCa, uint32_t kCb>
+__device__ __forceinline__ void pair_pipelined(uint32_t kl, uint32_t vl,
                                                const bf16x8_t (*qop)[MfmaShape<D>::KI],
                                                const floatx4_t (*sc)[kT], floatx4_t (*sn)[kT],
-                                               MfmaState<D>* st, float scale_log2, int lane) {
+                                               MfmaState<D>* st, float scale_log2) {
   constexpr int KL = MfmaFrag<E, D>::KL;
   constexpr int MC = MfmaShape<D>::MC;
   constexpr int H = MC / 2;
   static_assert(KL + 2 * H < 16, "outstanding LDS reads fit lgkmcnt");
   u32x4_t kr[2][KL];
   VRaw<E, D> v1[2][H], v2[2][H];
-  issue_k_lds(kr[0], na, lane);
-  issue_k_lds(kr[1], nb, lane);
-  issue_v_lds<E, D, H, 0>(v1[0], ca, lane);
-  issue_v_lds<E, D, H, 0>(v1[1], cb, lane);
+  issue_k_lds<KL, kNa>(kr[0], kl);
+  issue_k_lds<KL, kNb>(kr[1], kl);
+  issue_v_lds<E, D, H, 0, kCa>(v1[0], vl);
+  issue_v_lds<E, D, H, 0, kCb>(v1[1], vl);
   // the current pair's weights and their row sums
   bf16x8_t pop[kT];
 #pragma unroll
@@ -642,8 +640,8 @@ __device__ __forceinline__ void pair_pipelined(uint32_t na, uint32_t nb, uint32_
   // and the score products above may still be reading their accumulator
   // operands from registers these reads reuse: 16 wait states first.
   __asm__ volatile("s_nop 7\n\ts_nop 7" ::: "memory");
-  issue_v_lds<E, D, H, H>(v2[0], ca, lane);
-  issue_v_lds<E, D, H, H>(v2[1], cb, lane);
+  issue_v_lds<E, D, H, H, kCa>(v2[0], vl);
+  issue_v_lds<E, D, H, H, kCb>(v2[1], vl);
   wait_lds<2 * H>();
   pin(v1[0]);
   pin(v1[1]);
@@ -817,13 +815,17 @@ __global__ __launch_bounds__(kMultiWaves* kWave, kTiles == 1 ? 3 : 2) void chunk
   // several blocks are in flight without holding registers.  A stage holds
   // the K tile's units, then V's (then, for int8, the row scales); the units
   // of one wave-wide load are all K, all V or all scales of one tile.
+  // Block j's ring stage, counted from the work-group's first block (so a
+  // loop that advances eight blocks per trip sees the same stages every trip).
+  auto stage_of = [&](int jj) { return unsigned(jj - wjb) % kStages; };
+  auto stage_addr = [&](int jj) { return lds_offset(&sm_kv[stage_of(jj)][0]); };
   // e: the block's table word as staged (see fill_tab): its tile's index, bit
   // 31 set for an entry outside the pool (whose tile index is then kvh's in
   // block 0, loaded but never used).
-  auto issue = [&](int j, int e) {
+  auto issue = [&](unsigned stage, int e) {
     const int64_t pt = int64_t(e & 0x7fffffff);  // tile index p H_kv + kvh
     const int64_t tile = pt * kTileBytes;
-    uint4* ring = &sm_kv[unsigned(j) % kStages][0];
+    uint4* ring = &sm_kv[stage][0];
     if constexpr (kInt8) {
       // the tile's 16 row scales: floats 16 (p H_kv + kvh) .. of the scale region
       const int cu0 = w * kCodeUnits;  // uniform: all K or all V
@@ -877,16 +879,19 @@ __global__ __launch_bounds__(kMultiWaves* kWave, kTiles == 1 ? 3 : 2) void chunk
   // the entry p, or kvh's tile of block 0 with bit 31 set where p lies outside
   // the pool (the launch checks that tile indices fit 31 bits).
   int tb = wjb;
+  int any_bad = 0;  // some word staged so far lay outside the pool
   auto fill_tab = [&]() {
     // (the first block through readfirstlane: the compiler then keeps no
     // pointer per call site stepping along with the loops that call it)
     const int32_t* row = table + __builtin_amdgcn_readfirstlane(tb);
+    int inval = 0;
     for (int i = tid; i < kTabWin && tb + i < wje; i += kThreads) {
       const int p = row[i];
       const bool ok = p >= 0 && p < a.num_blocks;
       sm_tab[i] = ((ok ? p : 0) * a.num_kv_heads + kvh) | (ok ? 0 : int(0x80000000u));
+      inval |= ok ? 0 : 1;
     }
-    __syncthreads();
+    any_bad |= __syncthreads_or(inval);
   };
   fill_tab();
   // The words of blocks wb .. wb + 63 in a register (lane i: block wb + i),
@@ -906,18 +911,13 @@ __global__ __launch_bounds__(kMultiWaves* kWave, kTiles == 1 ? 3 : 2) void chunk
     }
     return __builtin_amdgcn_readlane(win, jn - wb);
   };
-  uint32_t ok_bits = 0;  // bit j % 32: block j's entry was inside the pool
   // Block j of the wave's range, alone: the per-block arithmetic.
   // (operands: where block j's K and V are, in the layout of C)
   auto single = [&](int j, uint32_t operands) {
     const int key0 = j * kBlockTokens;
     if (!(active && key0 < kend && key0 + kBlockTokens > klo)) return;  // uniform per wave
-    if (!((ok_bits >> (j & 31)) & 1u)) {
-      bad = 1;
-      return;
-    }
     MfmaFrag<C, D> f;
-    const uint32_t stage = lds_offset(&sm_kv[j % kStages][0]);
+    const uint32_t stage = stage_addr(j);
     load_block_lds_asm<C, D>(f, operands, lane);
     if constexpr (kInt8) load_scales_lds_asm<E, D>(f, stage, lane);
     const int nvalid = kend - key0;
@@ -945,10 +945,7 @@ __global__ __launch_bounds__(kMultiWaves* kWave, kTiles == 1 ? 3 : 2) void chunk
     }
   };
   auto issue_at = [&](int jn) {  // uniform
-    const int e = table_word(jn);
-    issue(jn, e);
-    const uint32_t ok = (uint32_t(e) >> 31) ^ 1u;
-    ok_bits = (ok_bits & ~(1u << (jn & 31))) | (ok << (jn & 31));
+    issue(stage_of(jn), table_word(jn));
   };
   if constexpr (kPairs) {
     // blocks wjb .. wjb + 3 in flight; at pair (j, j + 1) the two after it
@@ -971,10 +968,6 @@ __global__ __launch_bounds__(kMultiWaves* kWave, kTiles == 1 ? 3 : 2) void chunk
         return jj + 1 < wje && jj * kBlockTokens >= klo_wg &&
                jj * kBlockTokens + 2 * kBlockTokens - 1 <= kmin_wg;
       };
-      auto slot = [&](int jj) { return lds_offset(&sm_kv[unsigned(jj) % kStages][0]); };
-      auto mark_bad = [&](int jj) {  // blocks jj, jj + 1 (jj even: one 2-bit field)
-        bad |= int(((ok_bits >> (jj & 31)) & 3u) ^ 3u);
-      };
       if constexpr (kPipe) {
         // Software-pipelined: while pair j's weights and P V products run, the
         // scores of pair j + 2 are computed, so a wave has matrix products
@@ -984,6 +977,36 @@ __global__ __launch_bounds__(kMultiWaves* kWave, kTiles == 1 ? 3 : 2) void chunk
         // which every wave has finished once past the barrier.  Invariant at
         // the top of an iteration: blocks below j + kStages - 2 are issued.
         if (open(j)) {
+          // Iterations: pairs j = wjb, wjb + 2, ... while pair j + 2 is whole
+          // for every column and blocks j + 6, j + 7 exist (so both issues
+          // happen and exactly two blocks load after pair j + 2's: a fixed
+          // count to wait for).  open(wjb) already holds the window bound.
+          const int jmax = min(wje - 8, ((kmin_wg - (2 * kBlockTokens - 1)) >> 4) - 2);
+          const int n_iter = jmax >= j ? (jmax - j) / 2 + 1 : 0;
+          // stage byte offsets and the lane's addresses in stage 0
+          const uint32_t ring0 = lds_offset(&sm_kv[0][0]);
+          const uint32_t kl = ring0 + uint32_t(lane) * 16;
+          const uint32_t vl = ring0 + uint32_t(kTileBytes) +
+                              uint32_t((n * kBlockTokens + 4 * q) * int(sizeof(S)));
+          // blocks jn, jn + 1 (both in the range) into stages kS, kS + 1: one
+          // window check for the two table words
+          auto issue_pair = [&](int jn, auto stag) {
+            constexpr unsigned kS = decltype(stag)::value;
+            if (jn + 1 - tb >= kTabWin) {
+              tb = jn;
+              fill_tab();
+              wb = -(1 << 30);
+            }
+            if (jn + 1 - wb >= kWave) {
+              wb = jn;
+              const int i = jn - tb + lane;
+              win = i < kTabWin ? sm_tab[i] : 0;
+            }
+            const int e0 = __builtin_amdgcn_readlane(win, jn - wb);
+            const int e1 = __builtin_amdgcn_readlane(win, jn + 1 - wb);
+            issue(kS, e0);
+            issue(kS + 1, e1);
+          };
           auto run = [&](auto act) {
             constexpr bool kAct = decltype(act)::value;
             auto rescale = [&](floatx4_t (*sc)[kTiles]) {
@@ -995,24 +1018,24 @@ __global__ __launch_bounds__(kMultiWaves* kWave, kTiles == 1 ? 3 : 2) void chunk
             lds_barrier();
             floatx4_t s0[2][kTiles], s1[2][kTiles];
             if constexpr (kAct) {
-              pair_scores<C, D, kTiles>(slot(j), slot(j + 1), qop, s0, lane);
+              pair_scores<C, D, kTiles>(stage_addr(j), stage_addr(j + 1), qop, s0, lane);
               rescale(s0);
             }
-            // one iteration: pair j's scores (rescaled for) in sc; pair j + 2
-            // whole, and the pair after it issued, so exactly its two blocks
-            // load after pair j + 2's: a fixed count to wait for.  The rescale
-            // for pair j + 2 comes last, after pair j's products, as the
-            // output accumulators then pass one branch per pair, in place.
-            auto cont = [&](int jj) { return open(jj + 2) && jj + 5 < wje; };
-            auto iter = [&](floatx4_t (*sc)[kTiles], floatx4_t (*sn)[kTiles]) {
+            // Iteration M (mod 4) of the path: pair j (stages 2M, 2M + 1 of
+            // the ring, counted from wjb) has its scores, rescaled for, in sc.
+            // The rescale for pair j + 2 comes last, after pair j's products,
+            // as the output accumulators then pass one branch per pair, in
+            // place.
+            auto iter = [&](auto mtag, floatx4_t (*sc)[kTiles], floatx4_t (*sn)[kTiles]) {
+              constexpr unsigned M = decltype(mtag)::value;
+              constexpr unsigned kStage = kStageBytes;
               __builtin_amdgcn_s_waitcnt(vm_wait_imm((kStages - 6) * kPer));
               lds_barrier();
-              if (j + kStages - 2 < wje) issue_at(j + kStages - 2);
-              if (j + kStages - 1 < wje) issue_at(j + kStages - 1);
+              issue_pair(j + kStages - 2, std::integral_constant<unsigned, (2 * M + 6) % 8>{});
               if constexpr (kAct) {
-                mark_bad(j);
-                pair_pipelined<C, D, kTiles>(slot(j + 2), slot(j + 3), slot(j), slot(j + 1), qop,
-                                             sc, sn, st, a.scale_log2, lane);
+                pair_pipelined<C, D, kTiles, ((2 * M + 2) % 8) * kStage, ((2 * M + 3) % 8) * kStage,
+                               (2 * M) * kStage, (2 * M + 1) * kStage>(kl, vl, qop, sc, sn, st,
+                                                                       a.scale_log2);
                 rescale(sn);
               }
               j += 2;
@@ -1024,19 +1047,27 @@ __global__ __launch_bounds__(kMultiWaves* kWave, kTiles == 1 ? 3 : 2) void chunk
               if (j + kStages - 2 < wje) issue_at(j + kStages - 2);
               if (j + kStages - 1 < wje) issue_at(j + kStages - 1);
               if constexpr (kAct) {
-                mark_bad(j);
-                pair_pv<C, D, false, false, kTiles>(slot(j), slot(j + 1), sc, st, 0,
+                pair_pv<C, D, false, false, kTiles>(stage_addr(j), stage_addr(j + 1), sc, st, 0,
                                                     2 * kBlockTokens, a.scale_log2, lane);
               }
               j += 2;
             };
-            // two iterations per trip so the score buffers swap roles without copies
-            for (;;) {
-              if (!cont(j)) { last(s0); break; }
-              iter(s0, s1);
-              if (!cont(j)) { last(s1); break; }
-              iter(s1, s0);
+            using I0 = std::integral_constant<unsigned, 0>;
+            using I1 = std::integral_constant<unsigned, 1>;
+            using I2 = std::integral_constant<unsigned, 2>;
+            using I3 = std::integral_constant<unsigned, 3>;
+            // Four iterations per trip: the stages repeat, and the score
+            // buffers swap roles without copies.  Whole trips only (the up to
+            // three pairs left go through the general loop below): a
+            // remainder taken here put the accumulators through four joins,
+            // and the compiler spilled.
+            for (int it = 0; it + 4 <= n_iter; it += 4) {
+              iter(I0{}, s0, s1);
+              iter(I1{}, s1, s0);
+              iter(I2{}, s0, s1);
+              iter(I3{}, s1, s0);
             }
+            last(s0);
           };
           if (active) run(std::true_type{});
           else run(std::false_type{});
@@ -1051,8 +1082,7 @@ __global__ __launch_bounds__(kMultiWaves* kWave, kTiles == 1 ? 3 : 2) void chunk
         if (active) {
           for (; open(j); j += 2) {
             step(j);
-            mark_bad(j);
-            compute_pair_lds<C, D, false, false, kTiles>(slot(j), slot(j + 1), qop, st, 0,
+            compute_pair_lds<C, D, false, false, kTiles>(stage_addr(j), stage_addr(j + 1), qop, st, 0,
                                                          2 * kBlockTokens, a.scale_log2, lane, 0,
                                                          lo, limit);
           }
@@ -1068,17 +1098,13 @@ __global__ __launch_bounds__(kMultiWaves* kWave, kTiles == 1 ? 3 : 2) void chunk
       lds_barrier();
       if (j + kStages - 2 < wje) issue_at(j + kStages - 2);
       if (j + kStages - 1 < wje) issue_at(j + kStages - 1);
-      const uint32_t sa = lds_offset(&sm_kv[j % kStages][0]);
-      const uint32_t sb = lds_offset(&sm_kv[(j + 1) % kStages][0]);
+      const uint32_t sa = stage_addr(j);
+      const uint32_t sb = stage_addr(j + 1);
       const int key0 = j * kBlockTokens;
       const bool in_a = active && key0 < kend && key0 + kBlockTokens > klo;
       const bool in_b = j + 1 < wje && active && key0 + kBlockTokens < kend &&
                         key0 + 2 * kBlockTokens > klo;
       if (in_a && in_b) {  // uniform per wave
-        if (!((ok_bits >> (j & 31)) & (ok_bits >> ((j + 1) & 31)) & 1u)) {
-          bad = 1;
-          continue;
-        }
         const int nvalid = kend - key0;
         const int nfirst = klo - key0;
         const bool open =
@@ -1113,7 +1139,7 @@ __global__ __launch_bounds__(kMultiWaves* kWave, kTiles == 1 ? 3 : 2) void chunk
       lds_barrier();
       const int jn = jj + kStages - 1;
       if (jn < wje) issue_at(jn);
-      uint32_t operands = lds_offset(&sm_kv[jj % kStages][0]);
+      uint32_t operands = stage_addr(jj);
       if constexpr (kConvert) {
         const uint32_t cv = lds_offset(&sm_cv[0]);
         if (tid < 2 * kTileUnits) convert_int8_unit_lds<D>(operands, cv, tid);
@@ -1135,10 +1161,9 @@ __global__ __launch_bounds__(kMultiWaves* kWave, kTiles == 1 ? 3 : 2) void chunk
       if (active) {
         for (; open(j); ++j) {
           const uint32_t operands = step(j);
-          bad |= int(~(ok_bits >> (j & 31)) & 1u);
           MfmaFrag<C, D> f;
           load_block_lds_asm<C, D>(f, operands, lane);
-          if constexpr (kInt8) load_scales_lds_asm<E, D>(f, lds_offset(&sm_kv[j % kStages][0]), lane);
+          if constexpr (kInt8) load_scales_lds_asm<E, D>(f, stage_addr(j), lane);
           compute_block_tiles<C, D, false, false, kTiles>(f, qop, st, 0, kBlockTokens,
                                                           a.scale_log2, lane, 0, lo, limit);
         }
@@ -1147,6 +1172,19 @@ __global__ __launch_bounds__(kMultiWaves* kWave, kTiles == 1 ? 3 : 2) void chunk
       }
     }
     for (; j < wje; ++j) single(j, step(j));
+  }
+
+  // A staged table word lay outside the pool: the wave's columns turn NaN if
+  // their keys reach such a block (the blocks of positions klo .. kend - 1,
+  // all of which the loops above computed, a bad one on tile 0).  Rare, so
+  // the entries are read again here instead of tracked block by block.
+  if (any_bad && active) {
+    int inval = 0;
+    for (int jj = klo / kBlockTokens + lane; jj * kBlockTokens < kend; jj += kWave) {
+      const int p = table[jj];
+      inval |= (p >= 0 && p < a.num_blocks) ? 0 : 1;
+    }
+    bad = __builtin_amdgcn_ballot_w64(inval != 0) != 0 ? 1 : 0;
   }
 
   // Each wave finishes its own columns: lane (q, n) holds dims 16mc + 4q .. +3

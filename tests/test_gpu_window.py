@@ -117,6 +117,19 @@ MULTI = [
 @pytest.mark.parametrize("kv", ["bf16", "fp8", "int8"])
 @pytest.mark.parametrize("case", MULTI, ids=[c[0] for c in MULTI])
 def test_windowed_multi_matches_oracle(case, kv, window):
+    windowed_multi_case(case, kv, window)
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8", "int8"])
+def test_windowed_long_chunk_matches_oracle(kv):
+    # g = 8 with 64 and 40 rows (the LDS-staged kernel, two tiles per wave)
+    # and a 1,000-token window: the work-groups' first blocks are odd and
+    # even in turn, and each walks more than 32 blocks, past the wrap of the
+    # per-block validity bits
+    windowed_multi_case(("g8-long", 64, 8, 128, [1500, 2100], [64, 40]), kv, 1000)
+
+
+def windowed_multi_case(case, kv, window):
     name, H, H_kv, d, ctx, n = case
     w = W.multi_token_workload(name, "bf16", len(ctx), H, H_kv, d, ctx, n, seed=500 + H,
                                kv_dtype=kv, k_scale=0.5 if kv == "fp8" else 1.0,
