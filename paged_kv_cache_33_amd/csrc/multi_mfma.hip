@@ -1057,15 +1057,22 @@ __global__ __launch_bounds__(kMultiWaves* kWave, kTiles == 1 ? 3 : 2) void chunk
             using I2 = std::integral_constant<unsigned, 2>;
             using I3 = std::integral_constant<unsigned, 3>;
             // Four iterations per trip: the stages repeat, and the score
-            // buffers swap roles without copies.  Whole trips only (the up to
-            // three pairs left go through the general loop below): a
-            // remainder taken here put the accumulators through four joins,
-            // and the compiler spilled.
-            for (int it = 0; it + 4 <= n_iter; it += 4) {
+            // buffers swap roles without copies.  Then two more if at least
+            // two are left (the stages of a trip's first half); the one pair
+            // that may remain goes through the general loop below.  Every path
+            // ends on the same score buffer: a remainder of one or three taken
+            // here put the accumulators through joins the compiler resolved
+            // by spilling.
+            int it = 0;
+            for (; it + 4 <= n_iter; it += 4) {
               iter(I0{}, s0, s1);
               iter(I1{}, s1, s0);
               iter(I2{}, s0, s1);
               iter(I3{}, s1, s0);
+            }
+            if (it + 2 <= n_iter) {
+              iter(I0{}, s0, s1);
+              iter(I1{}, s1, s0);
             }
             last(s0);
           };
@@ -1195,16 +1202,13 @@ __global__ __launch_bounds__(kMultiWaves* kWave, kTiles == 1 ? 3 : 2) void chunk
     if (!active || !col_ok[tt]) continue;
     uint16_t* orow = out + row_at(scb + tt * kHeadsPerTile + n);
     const float inv = a.v_scale / L;
+    // (the hardware's conversion rounds to nearest even, as f32_to_bf16_rne)
 #pragma unroll
-    for (int mc = 0; mc < MC; ++mc) {
-      uint16_t h4[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        h4[e] = bad ? uint16_t(0x7fc0) : f32_to_bf16_rne(st[tt].o[mc][e] * inv);
-      uint2 v;
-      __builtin_memcpy(&v, h4, sizeof(v));
-      *reinterpret_cast<uint2*>(orow + 16 * mc + 4 * q) = v;
-    }
+    for (int mc = 0; mc < MC; ++mc)
+      *reinterpret_cast<uint2*>(orow + 16 * mc + 4 * q) =
+          bad ? make_uint2(0x7fc07fc0u, 0x7fc07fc0u)
+              : make_uint2(pack_bf16x2(st[tt].o[mc][0] * inv, st[tt].o[mc][1] * inv),
+                           pack_bf16x2(st[tt].o[mc][2] * inv, st[tt].o[mc][3] * inv));
   }
 }
 

@@ -98,7 +98,11 @@ __device__ __forceinline__ int sequence_of_rank(const int32_t* __restrict__ cont
     if (it < iters && j < B) {
       const int n = context_lens[j];
       const int64_t nb = n > 0 ? min((int64_t(n) + kBlockTokens - 1) / kBlockTokens, int64_t(max_nb)) : 0;
-      key[it] = int(nb * kOrderBuckets / (int64_t(max_nb) + 1));
+      // (32-bit arithmetic where it cannot overflow: far cheaper than 64-bit
+      // division)
+      key[it] = max_nb < (1 << 26)
+                    ? int(unsigned(nb) * unsigned(kOrderBuckets) / unsigned(max_nb + 1))
+                    : int(nb * kOrderBuckets / (int64_t(max_nb) + 1));
     }
   }
   __syncthreads();
