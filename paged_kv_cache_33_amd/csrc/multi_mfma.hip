@@ -388,7 +388,7 @@ template <typename E, int D, int kT>
 __device__ __forceinline__ void pair_scores(uint32_t sa, uint32_t sb,
                                             const bf16x8_t (*qop)[MfmaShape<D>::KI],
                                             floatx4_t (*s)[kT], int lane) {
-  static_assert(E::kKind != Kind::kInt8, "pairs take pools without row scales");
+  static_assert(!(E::kKind == Kind::kInt8 && kByteCodes<E>), "int8 codes are converted first");
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     MfmaFrag<E, D> f;
@@ -405,14 +405,17 @@ __device__ __forceinline__ void pair_scores(uint32_t sa, uint32_t sb,
   }
 }
 
-// pair_rescale: masks (as in compute_block_tiles, with nfirst / nvalid
-// relative to the pair's first token: -inf by select, the slot may hold NaN),
-// then the reference max: when some score exceeds it by more than the slack,
-// the state is rescaled (wave-uniform branch, as in compute_block_tiles).
-template <int D, bool kTail, bool kCausal, int kT>
+// pair_rescale: with kScaled (int8 pools) each score times its key row's
+// scale ks[h][j] (token 4q + j of block h); masks (as in compute_block_tiles,
+// with nfirst / nvalid relative to the pair's first token: -inf by select, the
+// slot may hold NaN), then the reference max: when some score exceeds it by
+// more than the slack, the state is rescaled (wave-uniform branch, as in
+// compute_block_tiles).
+template <int D, bool kTail, bool kCausal, int kT, bool kScaled = false>
 __device__ __forceinline__ void pair_rescale(floatx4_t (*s)[kT], MfmaState<D>* st, int nfirst,
                                              int nvalid, float scale_log2, int lane, int key0,
-                                             const int* lo, const int* limit) {
+                                             const int* lo, const int* limit,
+                                             const float (*ks)[4] = nullptr) {
   constexpr int MC = MfmaShape<D>::MC;
   const int q = lane >> 4;
   float lmax[kT];
@@ -424,6 +427,7 @@ __device__ __forceinline__ void pair_rescale(floatx4_t (*s)[kT], MfmaState<D>* s
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int t = 16 * h + 4 * q + j;  // token within the pair
+        if constexpr (kScaled) s[h][tt][j] *= ks[h][j];
         const bool masked = (kTail && (t >= nvalid || t < nfirst)) ||
                             (kCausal && (key0 + t > limit[tt] || key0 + t < lo[tt]));
         if (masked) s[h][tt][j] = -INFINITY;
@@ -455,18 +459,21 @@ __device__ __forceinline__ void pair_rescale(floatx4_t (*s)[kT], MfmaState<D>* s
 // pair_pv: the weights 2^(s scale - m) as bf16, their row sums, and
 // O^T += V^T P^T, the V operands read in two halves of the dims, each
 // followed by its products.  With kTail the V of tokens outside the range
-// is zeroed (weight 0 times NaN would be NaN).
-template <typename E, int D, bool kTail, bool kCausal, int kT>
+// is zeroed (weight 0 times NaN would be NaN).  kScaled (int8 pools): the
+// products take each weight times its token's V row scale vs[h][j] (0 where
+// masked, as the scale may be NaN there); the row sums take the weights alone.
+template <typename E, int D, bool kTail, bool kCausal, int kT, bool kScaled = false>
 __device__ __forceinline__ void pair_pv(uint32_t sa, uint32_t sb, const floatx4_t (*s)[kT],
                                         MfmaState<D>* st, int nfirst, int nvalid,
-                                        float scale_log2, int lane) {
+                                        float scale_log2, int lane,
+                                        const float (*vs)[4] = nullptr) {
   constexpr int MC = MfmaShape<D>::MC;
   const int q = lane >> 4;
   bf16x8_t pop[kT];
 #pragma unroll
   for (int tt = 0; tt < kT; ++tt) {
     const float mref = (kCausal && st[tt].m == -INFINITY) ? 0.f : st[tt].m;
-    uint32_t pk[4];
+    uint32_t pk[4], pkv[4];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       float pw[4];
@@ -475,13 +482,24 @@ __device__ __forceinline__ void pair_pv(uint32_t sa, uint32_t sb, const floatx4_
         pw[j] = fast_exp2(__builtin_fmaf(s[h][tt][j], scale_log2, -mref));
       pk[2 * h] = pack_bf16x2(pw[0], pw[1]);
       pk[2 * h + 1] = pack_bf16x2(pw[2], pw[3]);
+      if constexpr (kScaled) {
+        float pv[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          pv[j] = ((kTail || kCausal) && s[h][tt][j] == -INFINITY) ? 0.f : pw[j] * vs[h][j];
+        pkv[2 * h] = pack_bf16x2(pv[0], pv[1]);
+        pkv[2 * h + 1] = pack_bf16x2(pv[2], pv[3]);
+      }
     }
     constexpr uint32_t kOnes = 0x3F803F80u;  // two bf16 1.0
     float l = st[tt].l;
 #pragma unroll
     for (int k = 0; k < 4; ++k) l = dot2_bf16(pk[k], kOnes, l);
     st[tt].l = l;
-    pop[tt] = __builtin_bit_cast(bf16x8_t, make_uint4(pk[0], pk[1], pk[2], pk[3]));
+    if constexpr (kScaled)
+      pop[tt] = __builtin_bit_cast(bf16x8_t, make_uint4(pkv[0], pkv[1], pkv[2], pkv[3]));
+    else
+      pop[tt] = __builtin_bit_cast(bf16x8_t, make_uint4(pk[0], pk[1], pk[2], pk[3]));
   }
   auto pv = [&](const MfmaFrag<E, D>& fa, const MfmaFrag<E, D>& fb, int mc) {
     uint2 va = v_operand<E, D>(fa, mc), vb = v_operand<E, D>(fb, mc);
@@ -654,17 +672,49 @@ __device__ __forceinline__ void pair_pipelined(uint32_t kl, uint32_t vl,
   for (int mc = 0; mc < H; ++mc) pv(v2[0][mc], v2[1][mc], H + mc);
 }
 
-// The whole pair: scores, masks and rescale, weights and products.
+// The whole pair: scores, masks and rescale, weights and products.  int8
+// pools (E = Int8AsBf16: the blocks converted to bf16 at sa, sb): the row
+// scales come from the blocks' ring stages ra, rb, where they follow the two
+// code tiles (K's 16, then V's); lane quarter q reads tokens 4q..4q+3 of each.
 template <typename E, int D, bool kTail, bool kCausal, int kT>
 __device__ __forceinline__ void compute_pair_lds(uint32_t sa, uint32_t sb,
                                                  const bf16x8_t (*qop)[MfmaShape<D>::KI],
                                                  MfmaState<D>* st, int nfirst, int nvalid,
                                                  float scale_log2, int lane, int key0,
-                                                 const int* lo, const int* limit) {
+                                                 const int* lo, const int* limit,
+                                                 uint32_t ra = 0, uint32_t rb = 0) {
+  constexpr bool kScaled = E::kKind == Kind::kInt8;
   floatx4_t s[2][kT];
   pair_scores<E, D, kT>(sa, sb, qop, s, lane);
-  pair_rescale<D, kTail, kCausal, kT>(s, st, nfirst, nvalid, scale_log2, lane, key0, lo, limit);
-  pair_pv<E, D, kTail, kCausal, kT>(sa, sb, s, st, nfirst, nvalid, scale_log2, lane);
+  if constexpr (kScaled) {
+    constexpr uint32_t kCodes = 2 * kBlockTokens * D;  // both int8 code tiles
+    const uint32_t off = kCodes + uint32_t(lane >> 4) * 16;
+    // four scales of each block, K's before the rescale, V's before the
+    // products (so they are not held at once)
+    auto read4 = [&](uint32_t addr, float (*x)[4]) {
+      u32x4_t r[2];
+      __asm__ volatile("ds_read_b128 %0, %1" : "=v"(r[0]) : "v"(ra + addr));
+      __asm__ volatile("ds_read_b128 %0, %1" : "=v"(r[1]) : "v"(rb + addr));
+      __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      pin(r);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        x[h][0] = __uint_as_float(r[h].x);
+        x[h][1] = __uint_as_float(r[h].y);
+        x[h][2] = __uint_as_float(r[h].z);
+        x[h][3] = __uint_as_float(r[h].w);
+      }
+    };
+    float ks[2][4], vs[2][4];
+    read4(off, ks);
+    pair_rescale<D, kTail, kCausal, kT, true>(s, st, nfirst, nvalid, scale_log2, lane, key0, lo,
+                                              limit, ks);
+    read4(off + 64, vs);
+    pair_pv<E, D, kTail, kCausal, kT, true>(sa, sb, s, st, nfirst, nvalid, scale_log2, lane, vs);
+  } else {
+    pair_rescale<D, kTail, kCausal, kT>(s, st, nfirst, nvalid, scale_log2, lane, key0, lo, limit);
+    pair_pv<E, D, kTail, kCausal, kT>(sa, sb, s, st, nfirst, nvalid, scale_log2, lane);
+  }
 }
 
 // Several column sets per sequence and KV head (a prefill chunk, or draft
@@ -701,30 +751,34 @@ __global__ __launch_bounds__(kMultiWaves* kWave, kTiles == 1 ? 3 : 2) void chunk
   static_assert(kTileUnits % kCodeUnits == 0 && kScaleUnits == kMultiWaves, "int8 stage split");
   constexpr int kPer = kInt8 ? (kCodeUnits + kWave - 1) / kWave + 1
                              : (kUnits + kThreads - 1) / kThreads;  // loads per thread per block
-  // bf16 and fp8 pools compute blocks in pairs (one 32-deep P V product per
-  // pair; compute_pair_lds), six ring stages: the pair computing and two pairs
-  // in flight.  Measured against single blocks: 512-token prefill chunks
-  // 0.975 -> 0.866 ms (bf16), 1.052 -> 0.957 ms (fp8); verification of 8
-  // draft tokens at g = 8, 528 -> 518 us (bf16), 416 -> 380 us (fp8).  One
-  // tile per wave stays at three work-groups per CU (164 VGPRs, 52 KiB LDS).
-  constexpr bool kPairs = !kInt8;
+  // Blocks are computed in pairs (one 32-deep P V product per pair;
+  // compute_pair_lds).  Measured against single blocks: 512-token prefill
+  // chunks 0.975 -> 0.866 ms (bf16), 1.052 -> 0.957 ms (fp8); verification of
+  // 8 draft tokens at g = 8, 528 -> 518 us (bf16), 416 -> 380 us (fp8).  One
+  // tile per wave stays at three work-groups per CU.
+  // int8 pools with one tile per wave (draft verification) keep single
+  // blocks: pairs measured 1.5-3.5% slower there (and 6% faster with two
+  // tiles per wave, on prefill chunks).
+  constexpr bool kPairs = !(kInt8 && kTiles == 1);
   constexpr int kTabWin = 1024;
-  // Pairs on the software-pipelined path (see below) take eight stages where
-  // the work-groups of a CU still fit its 160 KiB of LDS (two with two tiles
-  // per wave, three with one).
+  // bf16 and fp8 pairs on the software-pipelined path (see below) take eight
+  // stages where the work-groups of a CU still fit its 160 KiB of LDS (two
+  // with two tiles per wave, three with one); the other pairs six, single
+  // blocks four.
   constexpr int kStageBytes = kUnits * 16;
   constexpr bool kPipe =
-      kPairs && (kTiles == 2 ? 2 : 3) * (8 * kStageBytes + 4 * kTabWin + 1024) <= 160 * 1024;
+      !kInt8 && (kTiles == 2 ? 2 : 3) * (8 * kStageBytes + 4 * kTabWin + 1024) <= 160 * 1024;
   constexpr int kStages = kPipe ? 8 : kPairs ? 6 : 4;
   __shared__ uint4 sm_kv[kStages][kUnits];
   __shared__ int sm_tab[kTabWin];
-  // int8: each block is converted to bf16 once per work-group (every thread
-  // one 16-byte unit) into sm_cv, and the waves take their operands from
-  // there (C, the compute type, keeps the row scales).
+  // int8: each pair of blocks is converted to bf16 once per work-group
+  // (every thread two 16-byte units) into sm_cv, and the waves take their
+  // operands from there and the row scales from the ring stages (C, the
+  // compute type, keeps the row scales).
   constexpr bool kConvert = kInt8;
   using C = std::conditional_t<kConvert, Int8AsBf16, E>;
   constexpr int kCvUnits = 2 * kTileElems * 2 / 16;  // one bf16 block, K and V
-  __shared__ uint4 sm_cv[kConvert ? kCvUnits : 1];
+  __shared__ uint4 sm_cv[kConvert ? (kPairs ? 2 : 1) * kCvUnits : 1];
 
   __shared__ int sm_order[kOrderBuckets + kMultiWaves + 1];
   const int b = __builtin_amdgcn_readfirstlane(
@@ -947,6 +1001,23 @@ __global__ __launch_bounds__(kMultiWaves* kWave, kTiles == 1 ? 3 : 2) void chunk
   auto issue_at = [&](int jn) {  // uniform
     issue(stage_of(jn), table_word(jn));
   };
+  // int8: blocks jj and jj + 1 (if in the range) in bf16 into sm_cv (after
+  // the barrier that makes them visible, before the one that hands them to
+  // the waves); where each one's operands are
+  const uint32_t cv0 = lds_offset(&sm_cv[0]);
+  auto convert_pair = [&](int jj) {
+    if constexpr (kConvert) {
+      const int units = (jj + 1 < wje ? 2 : 1) * 2 * kTileUnits;
+      for (int u = tid; u < units; u += kThreads) {
+        const int h = u / (2 * kTileUnits);
+        convert_int8_unit_lds<D>(stage_addr(jj + h), cv0 + uint32_t(h) * kCvUnits * 16,
+                                 u - h * 2 * kTileUnits);
+      }
+    }
+  };
+  auto operands_of = [&](int jj, int h) {  // block jj + h (h = 0, 1)
+    return kConvert ? cv0 + uint32_t(h) * kCvUnits * 16 : stage_addr(jj + h);
+  };
   if constexpr (kPairs) {
     // blocks wjb .. wjb + 3 in flight; at pair (j, j + 1) the two after it
     // may still be loading
@@ -1086,15 +1157,25 @@ __global__ __launch_bounds__(kMultiWaves* kWave, kTiles == 1 ? 3 : 2) void chunk
           if (jj + kStages - 2 < wje) issue_at(jj + kStages - 2);
           if (jj + kStages - 1 < wje) issue_at(jj + kStages - 1);
         };
+        auto convert_step = [&](int jj) {
+          if constexpr (kConvert) {
+            convert_pair(jj);
+            lds_barrier();  // the bf16 blocks are complete
+          }
+        };
         if (active) {
           for (; open(j); j += 2) {
             step(j);
-            compute_pair_lds<C, D, false, false, kTiles>(stage_addr(j), stage_addr(j + 1), qop, st, 0,
-                                                         2 * kBlockTokens, a.scale_log2, lane, 0,
-                                                         lo, limit);
+            convert_step(j);
+            compute_pair_lds<C, D, false, false, kTiles>(
+                operands_of(j, 0), operands_of(j, 1), qop, st, 0, 2 * kBlockTokens, a.scale_log2,
+                lane, 0, lo, limit, stage_addr(j), stage_addr(j + 1));
           }
         } else {
-          for (; open(j); j += 2) step(j);
+          for (; open(j); j += 2) {
+            step(j);
+            convert_step(j);
+          }
         }
       }
     }
@@ -1105,8 +1186,13 @@ __global__ __launch_bounds__(kMultiWaves* kWave, kTiles == 1 ? 3 : 2) void chunk
       lds_barrier();
       if (j + kStages - 2 < wje) issue_at(j + kStages - 2);
       if (j + kStages - 1 < wje) issue_at(j + kStages - 1);
-      const uint32_t sa = stage_addr(j);
-      const uint32_t sb = stage_addr(j + 1);
+      if constexpr (kConvert) {
+        convert_pair(j);
+        lds_barrier();  // the bf16 blocks are complete
+      }
+      const uint32_t sa = operands_of(j, 0);
+      const uint32_t sb = operands_of(j, 1);
+      const uint32_t ra = stage_addr(j), rb = stage_addr(j + 1);
       const int key0 = j * kBlockTokens;
       const bool in_a = active && key0 < kend && key0 + kBlockTokens > klo;
       const bool in_b = j + 1 < wje && active && key0 + kBlockTokens < kend &&
@@ -1118,18 +1204,19 @@ __global__ __launch_bounds__(kMultiWaves* kWave, kTiles == 1 ? 3 : 2) void chunk
             nvalid >= 2 * kBlockTokens && key0 + 2 * kBlockTokens - 1 <= kmin && key0 >= klo_max;
         if (ntiles == kTiles) {
           if (open)
-            compute_pair_lds<E, D, false, false, kTiles>(sa, sb, qop, st, 0, nvalid,
-                                                         a.scale_log2, lane, 0, lo, limit);
+            compute_pair_lds<C, D, false, false, kTiles>(sa, sb, qop, st, 0, nvalid,
+                                                         a.scale_log2, lane, 0, lo, limit, ra, rb);
           else
-            compute_pair_lds<E, D, true, true, kTiles>(sa, sb, qop, st, nfirst, nvalid,
-                                                       a.scale_log2, lane, key0, lo, limit);
+            compute_pair_lds<C, D, true, true, kTiles>(sa, sb, qop, st, nfirst, nvalid,
+                                                       a.scale_log2, lane, key0, lo, limit, ra,
+                                                       rb);
         } else {
           if (open)
-            compute_pair_lds<E, D, false, false, 1>(sa, sb, qop, st, 0, nvalid, a.scale_log2,
-                                                    lane, 0, lo, limit);
+            compute_pair_lds<C, D, false, false, 1>(sa, sb, qop, st, 0, nvalid, a.scale_log2,
+                                                    lane, 0, lo, limit, ra, rb);
           else
-            compute_pair_lds<E, D, true, true, 1>(sa, sb, qop, st, nfirst, nvalid, a.scale_log2,
-                                                  lane, key0, lo, limit);
+            compute_pair_lds<C, D, true, true, 1>(sa, sb, qop, st, nfirst, nvalid, a.scale_log2,
+                                                  lane, key0, lo, limit, ra, rb);
         }
       } else if (in_a) {
         single(j, sa);
