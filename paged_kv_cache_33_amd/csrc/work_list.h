@@ -110,12 +110,25 @@ __device__ __forceinline__ int sequence_of_rank(const int32_t* __restrict__ cont
   for (int it = 0; it < kMaxIters; ++it)
     if (key[it] >= 0) atomicAdd(&total[key[it]], 1);
   __syncthreads();
-  // Bucket holding rank r, from the longest bucket down, and r's index in it.
+  // Bucket holding rank r, from the longest bucket down, and r's index in it:
+  // lane i takes bucket kOrderBuckets - 1 - i, a prefix sum over the lanes
+  // gives each bucket's last rank, and the first lane past r holds it (one
+  // LDS read and five shuffles, where a bucket-by-bucket walk waited for up
+  // to 32 dependent LDS reads).
+  static_assert(kOrderBuckets <= kWave, "one lane per bucket");
+  const int t = lane < kOrderBuckets ? total[kOrderBuckets - 1 - lane] : 0;
+  int incl = t;
+#pragma unroll
+  for (int off = 1; off < kOrderBuckets; off <<= 1) {
+    const int y = __shfl_up(incl, off, kWave);
+    if (lane >= off) incl += y;
+  }
+  const uint64_t past = __ballot(lane < kOrderBuckets && r < incl);
   int want_key = 0, before = 0;
-  for (int k = kOrderBuckets - 1; k >= 0; --k) {
-    const int t = total[k];
-    if (r < before + t) { want_key = k; break; }
-    before += t;
+  if (past != 0) {
+    const int i = __ffsll(static_cast<unsigned long long>(past)) - 1;
+    want_key = kOrderBuckets - 1 - i;
+    before = __shfl(incl - t, i, kWave);
   }
   const int want = r - before;
   int cnt = 0;
