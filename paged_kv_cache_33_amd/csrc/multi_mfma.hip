@@ -411,11 +411,16 @@ __device__ __forceinline__ void pair_scores(uint32_t sa, uint32_t sb,
 // slot may hold NaN), then the reference max: when some score exceeds it by
 // more than the slack, the state is rescaled (wave-uniform branch, as in
 // compute_block_tiles).
+//
+// thr (optional): per column tile, (m + slack) / scale_log2, the reference in
+// raw score units, kept up to date here; the test then compares raw maxima
+// (two fewer instructions per tile, as m changes only in the rare rescale).
 template <int D, bool kTail, bool kCausal, int kT, bool kScaled = false>
 __device__ __forceinline__ void pair_rescale(floatx4_t (*s)[kT], MfmaState<D>* st, int nfirst,
                                              int nvalid, float scale_log2, int lane, int key0,
                                              const int* lo, const int* limit,
-                                             const float (*ks)[4] = nullptr) {
+                                             const float (*ks)[4] = nullptr,
+                                             float* thr = nullptr) {
   constexpr int MC = MfmaShape<D>::MC;
   const int q = lane >> 4;
   float lmax[kT];
@@ -439,19 +444,24 @@ __device__ __forceinline__ void pair_rescale(floatx4_t (*s)[kT], MfmaState<D>* s
         __builtin_elementwise_maximum(
             __builtin_elementwise_maximum(s[1][tt][0], s[1][tt][1]),
             __builtin_elementwise_maximum(s[1][tt][2], s[1][tt][3])));
-    lmax[tt] *= scale_log2;
-    exceeds = exceeds || lmax[tt] > st[tt].m + kRescaleSlack;
+    if (thr) {
+      exceeds = exceeds || lmax[tt] > thr[tt];
+    } else {
+      lmax[tt] *= scale_log2;
+      exceeds = exceeds || lmax[tt] > st[tt].m + kRescaleSlack;
+    }
   }
   if (__builtin_amdgcn_ballot_w64(exceeds) != 0) {
 #pragma unroll
     for (int tt = 0; tt < kT; ++tt) {
-      const float mx = cross_row_max(lmax[tt]);
+      const float mx = cross_row_max(lmax[tt]) * (thr ? scale_log2 : 1.f);
       const bool grow = mx > st[tt].m + kRescaleSlack;
       const float alpha = grow ? fast_exp2(st[tt].m - mx) : 1.f;
       st[tt].l *= alpha;
 #pragma unroll
       for (int mc = 0; mc < MC; ++mc) st[tt].o[mc] *= alpha;
       st[tt].m = grow ? mx : st[tt].m;
+      if (thr) thr[tt] = (st[tt].m + kRescaleSlack) / scale_log2;
     }
   }
 }
@@ -1080,9 +1090,14 @@ __global__ __launch_bounds__(kMultiWaves* kWave, kTiles == 1 ? 3 : 2) void chunk
           };
           auto run = [&](auto act) {
             constexpr bool kAct = decltype(act)::value;
+            // the state's reference in raw score units (the state is fresh:
+            // m = -inf)
+            float thr[kTiles];
+#pragma unroll
+            for (int tt = 0; tt < kTiles; ++tt) thr[tt] = (st[tt].m + kRescaleSlack) / a.scale_log2;
             auto rescale = [&](floatx4_t (*sc)[kTiles]) {
               pair_rescale<D, false, false, kTiles>(sc, st, 0, 2 * kBlockTokens, a.scale_log2,
-                                                    lane, 0, lo, limit);
+                                                    lane, 0, lo, limit, nullptr, thr);
             };
             // pair j landed; the blocks after it may still be loading
             wait_vm_later<kStages - 4, kPer>(min(kStages - 4, max(wje - 2 - j, 0)));
