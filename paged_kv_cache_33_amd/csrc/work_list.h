@@ -80,6 +80,8 @@ template <int kThreads>
 __device__ __forceinline__ int sequence_of_rank(const int32_t* __restrict__ context_lens, int B,
                                                 int max_nb, int r, int* sh) {
   constexpr int kW = kThreads / kWave;
+  // each thread keys kMaxIters sequences: the work-group must cover all of them
+  static_assert(kMaxOrderedSeqs % kThreads == 0, "kMaxIters * kThreads == kMaxOrderedSeqs");
   constexpr int kMaxIters = kMaxOrderedSeqs / kThreads;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
   int* total = sh;                      // [kOrderBuckets] members per bucket

@@ -185,6 +185,10 @@ def test_decode_argument_errors(lib, pool):
     assert _decode(lib, pool, max_ctx=16 * 8193, P=16, ws=FAKE_K, ws_bytes=1 << 40) \
         == _lib.KV_ERR_INVALID_ARG
     assert _decode(lib, pool, B=0) == _lib.KV_OK  # nothing to launch
+    # split mode keeps one work-list entry per sequence in LDS: 4,096 at most
+    assert _decode(lib, pool, B=4097, P=16, ws=FAKE_K, ws_bytes=1 << 40) \
+        == _lib.KV_ERR_UNSUPPORTED
+    assert b"4096" in lib.kv_last_error()
 
 
 def _multi(lib, pool, B=2, H=4, T=6, mq=4, max_nb=4, scale=0.1, out=FAKE_K, q=FAKE_V,
