@@ -729,10 +729,9 @@ def main(argv=None) -> int:
     kernel = "decode_mfma" if P.kv_decode_kernel_kind(pool, w.H) == 1 else "decode_valu"
 
     # The step: one kv_decode_step launch (the write on extra work-groups, the
-    # attention taking the newest position from the new rows), or the write and
-    # the decode as separate launches.  fp8 and int8 pools write with
-    # kv_cache_append (their write quantises), then decode.
-    one_launch = not (args.unfused or args.two_launch) and w.kv_dtype in ("bf16", "f32")
+    # attention taking the newest position from the new rows, as the write
+    # stores them), or the write and the decode as separate launches.
+    one_launch = not (args.unfused or args.two_launch)
 
     def run_step(i, ev=None):
         """One step; ev = (before write, before decode, after decode, after step)

@@ -282,9 +282,10 @@ kv_status paged_attention_decode_window(const kv_pool* pool, void* out, const vo
  * as for paged_attention_decode_window (window = 0: the whole context); in
  * split mode follow with paged_attention_reduce(_window) as usual.  A table
  * entry outside the pool for the newest position's block gives NaN for that
- * sequence (and no write).  Pools: KV_BF16 and KV_F32 (KV_ERR_UNSUPPORTED for
- * fp8 and int8 pools, whose write quantises: use kv_cache_append, then the
- * decode). */
+ * sequence (and no write).  Every pool type: for fp8 and int8 pools the
+ * newest position enters the attention as the codes (and, int8, the row
+ * scales) the write stores, computed from key and value by the write's own
+ * rules, so it is the value the cache holds after the step. */
 kv_status kv_decode_step(const kv_pool* pool, void* out, const void* query, const void* key,
                          const void* value, const int32_t* block_tables, int32_t max_nb,
                          const int32_t* context_lens, int32_t B, int32_t H,

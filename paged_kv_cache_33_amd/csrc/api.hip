@@ -229,10 +229,6 @@ kv_status decode_impl(const kv_pool* pool, void* out, const void* query,
                       int64_t* slot_mapping = nullptr) {
   if (!pool) return fail(KV_ERR_INVALID_ARG, "pool is NULL");
   const bool fused = key != nullptr || value != nullptr;
-  if (fused && pool->desc.dtype != KV_BF16 && pool->desc.dtype != KV_F32)
-    return fail(KV_ERR_UNSUPPORTED,
-                "the fused step takes bf16 and fp32 pools; for fp8 and int8 pools call "
-                "kv_cache_append, then the decode");
   if (window < 0) return fail(KV_ERR_INVALID_ARG, "window must be >= 0 (0 = whole context)");
   const kv_pool_desc& d = pool->desc;
   if (B < 0) return fail(KV_ERR_INVALID_ARG, "B must be >= 0");

@@ -44,6 +44,7 @@ struct MergeLds {
   float l[kWaves][kHeadsPerTile];
   int bad[kWaves];
   __attribute__((aligned(16))) uint16_t fresh[2][D];
+  float fresh_scale[2];  // int8: the newest rows' scales (K, V)
   float fresh_s[kHeadsPerTile];
   int fresh_bad;
 };
@@ -143,7 +144,7 @@ __device__ __forceinline__ void mfma_item(const DecodeArgs& a, const int part, c
   int te = split ? min(tb + a.partition_size, ctx) : ctx;
   // Fused step: the item holding position ctx - 1 takes it from the fresh rows
   // (folded in at the merge) and walks the cache up to ctx - 2 only.
-  const bool fold = kFoldable<E> && a.fresh_key != nullptr && (!split || part == nparts - 1);
+  const bool fold = a.fresh_key != nullptr && (!split || part == nparts - 1);
   if (fold) te = ctx - 1 > max(tb, first) ? ctx - 1 : tb;
   const int jb = tb / kBlockTokens;
   const int je = (te + kBlockTokens - 1) / kBlockTokens;
@@ -171,7 +172,7 @@ __device__ __forceinline__ void mfma_item(const DecodeArgs& a, const int part, c
       qop[i] = __builtin_bit_cast(bf16x8_t, raw);
     }
   }
-  if (fold && w == 0) fetch_fresh<E, D>(a, b, kvh, lane, sm.fresh, sm.fresh_bad);
+  if (fold && w == 0) fetch_fresh<E, D>(a, b, kvh, lane, sm.fresh, sm.fresh_bad, sm.fresh_scale);
 
   const S* kc = static_cast<const S*>(a.k_cache);
   const S* vc = static_cast<const S*>(a.v_cache);
@@ -245,8 +246,9 @@ __device__ __forceinline__ void mfma_item(const DecodeArgs& a, const int part, c
 #pragma unroll
     for (int i = 0; i < KI; ++i)
       krow[i] = *reinterpret_cast<const uint4*>(&sm.fresh[0][query_dim0<E>(i, q)]);
-    const float sf = fresh_score<E, D>(krow, qop);
-    if (q == 0) sm.fresh_s[n] = sf * a.scale_log2;
+    float sf = fresh_score<E, D>(krow, qop) * a.scale_log2;
+    if constexpr (E::kKind == Kind::kInt8) sf *= sm.fresh_scale[0];  // as the blocks' ks
+    if (q == 0) sm.fresh_s[n] = sf;
   }
   const float lsum = cross_row_sum(st.l);
   if (q == 0) {
@@ -278,7 +280,9 @@ __device__ __forceinline__ void mfma_item(const DecodeArgs& a, const int part, c
     if (fold) {
       const float sc = fast_exp2(sm.fresh_s[hh] - M);
       L += sc;
-      acc = fmaf(bf16_to_f32(sm.fresh[1][x]), sc, acc);
+      float v = bf16_to_f32(sm.fresh[1][x]);
+      if constexpr (E::kKind == Kind::kInt8) v *= sm.fresh_scale[1];  // as the blocks' vs
+      acc = fmaf(v, sc, acc);
     }
     float res = acc / L * a.v_scale;
     if (bad) res = __int_as_float(0x7fc00000);
@@ -355,7 +359,7 @@ __device__ __forceinline__ void mfma_split_worker(const DecodeArgs& a, const int
     const int tb = rs + it.part * a.partition_size;
     it.te = min(tb + a.partition_size, it.ctx);
     // fused step: the last partition takes position ctx - 1 from the fresh rows
-    it.fold = kFoldable<E> && a.fresh_key != nullptr && it.part == it.nparts - 1;
+    it.fold = a.fresh_key != nullptr && it.part == it.nparts - 1;
     if (it.fold) it.te = it.ctx - 1 > max(tb, it.first) ? it.ctx - 1 : tb;
     it.jb = tb / kBlockTokens;
     const int je = (it.te + kBlockTokens - 1) / kBlockTokens;
@@ -447,31 +451,22 @@ __device__ __forceinline__ void mfma_split_worker(const DecodeArgs& a, const int
         consume(k, tile_a, fa);
       }
     }
-    // Fused step, last partition: wave 0 loads the newest position's K row
-    // (its operand dims) and V row, scores it against the current query (qop
-    // moves on to the next item below) and leaves score, V row and the table
-    // check for the merge.  Nothing else is in flight here (this item's blocks
-    // are consumed, the next item's come after), so the loads' wait costs one
-    // latency, on the last partitions only.
-    if constexpr (kFoldable<E>) {
-      if (cur.fold && w == 0) {
-        const size_t row = (size_t(cur.b) * a.num_kv_heads + kvh) * D;
-        const uint16_t* fk = static_cast<const uint16_t*>(a.fresh_key) + row;
-        const uint16_t* fv = static_cast<const uint16_t*>(a.fresh_value) + row;
-        uint4 krow[KI];
+    // Fused step, last partition: wave 0 puts the newest position's K and V
+    // rows into LDS as the cache will hold them (fetch_fresh), scores the K row
+    // against the current query (qop moves on to the next item below) and
+    // leaves score, V row and the table check for the merge.  Nothing else is
+    // in flight here (this item's blocks are consumed, the next item's come
+    // after), so the loads' wait costs one latency, on the last partitions
+    // only.
+    if (cur.fold && w == 0) {
+      fetch_fresh<E, D>(a, cur.b, kvh, lane, sm.fresh, sm.fresh_bad, sm.fresh_scale);
+      uint4 krow[KI];
 #pragma unroll
-        for (int k = 0; k < KI; ++k)
-          krow[k] = *reinterpret_cast<const uint4*>(fk + query_dim0<E>(k, q));
-        if (lane < D / 8)
-          *reinterpret_cast<uint4*>(&sm.fresh[1][lane * 8]) =
-              *reinterpret_cast<const uint4*>(fv + lane * 8);
-        if (lane == 0) {
-          const int p = a.block_tables[int64_t(cur.b) * a.max_nb + (cur.ctx - 1) / kBlockTokens];
-          sm.fresh_bad = p < 0 || p >= a.num_blocks;
-        }
-        const float sf = fresh_score<E, D>(krow, qop);
-        if (q == 0) sm.fresh_s[n] = sf * a.scale_log2;
-      }
+      for (int k = 0; k < KI; ++k)
+        krow[k] = *reinterpret_cast<const uint4*>(&sm.fresh[0][query_dim0<E>(k, q)]);
+      float sf = fresh_score<E, D>(krow, qop) * a.scale_log2;
+      if constexpr (E::kKind == Kind::kInt8) sf *= sm.fresh_scale[0];  // as the blocks' ks
+      if (q == 0) sm.fresh_s[n] = sf;
     }
     // unconditional (an entry outside the pool loads tile 0); see load_window
     tile_a = fetch(win_next, 0, fa);
@@ -511,7 +506,9 @@ __device__ __forceinline__ void mfma_split_worker(const DecodeArgs& a, const int
       if (cur.fold) {
         const float sc = fast_exp2(sm.fresh_s[hh] - M);
         L += sc;
-        acc = fmaf(bf16_to_f32(sm.fresh[1][x]), sc, acc);
+        float v = bf16_to_f32(sm.fresh[1][x]);
+        if constexpr (E::kKind == Kind::kInt8) v *= sm.fresh_scale[1];  // as the blocks' vs
+        acc = fmaf(v, sc, acc);
       }
       float res = acc / L * a.v_scale;
       if (bad) res = __int_as_float(0x7fc00000);

@@ -225,27 +225,30 @@ __device__ __forceinline__ void compute_block(const BlockFrag<Tr, D>& f, const Q
   }
 }
 
-// q . k of the newest position's key row (in LDS) over this lane's query
-// chunks, the four 16-lane rows combined: the same value in every lane.
+// q . k of the newest position's key row (in LDS, as the cache holds it: for
+// one-byte caches the codes' bf16 values, in dim order) over this lane's
+// query chunks, the four 16-lane rows combined: the same value in every lane.
 template <typename Tr, int D>
 __device__ __forceinline__ float fresh_score(const typename Tr::act* krow,
                                              const QueryFrag<Tr, D>& qf, int lane) {
   using Sh = ValuShape<Tr, D>;
   float dot = 0.f;
-  if constexpr (kFoldable<Tr>) {
 #pragma unroll
-    for (int i = 0; i < Sh::KL; ++i) {
-      const uint4 k = *reinterpret_cast<const uint4*>(krow + (4 * i + lane / 16) * Sh::X);
-      if constexpr (Tr::kKind == Kind::kBf16) {
-        dot = dot2_bf16(k.x, qf.c[i][0].x, dot);
-        dot = dot2_bf16(k.y, qf.c[i][0].y, dot);
-        dot = dot2_bf16(k.z, qf.c[i][0].z, dot);
-        dot = dot2_bf16(k.w, qf.c[i][0].w, dot);
+  for (int i = 0; i < Sh::KL; ++i) {
+#pragma unroll
+    for (int pc = 0; pc < QueryFrag<Tr, D>::kPieces; ++pc) {
+      const uint4 k =
+          *reinterpret_cast<const uint4*>(krow + (4 * i + lane / 16) * Sh::X + pc * 8);
+      if constexpr (Tr::kKind == Kind::kF32) {
+        dot = fmaf(__uint_as_float(k.x), __uint_as_float(qf.c[i][pc].x), dot);
+        dot = fmaf(__uint_as_float(k.y), __uint_as_float(qf.c[i][pc].y), dot);
+        dot = fmaf(__uint_as_float(k.z), __uint_as_float(qf.c[i][pc].z), dot);
+        dot = fmaf(__uint_as_float(k.w), __uint_as_float(qf.c[i][pc].w), dot);
       } else {
-        dot = fmaf(__uint_as_float(k.x), __uint_as_float(qf.c[i][0].x), dot);
-        dot = fmaf(__uint_as_float(k.y), __uint_as_float(qf.c[i][0].y), dot);
-        dot = fmaf(__uint_as_float(k.z), __uint_as_float(qf.c[i][0].z), dot);
-        dot = fmaf(__uint_as_float(k.w), __uint_as_float(qf.c[i][0].w), dot);
+        dot = dot2_bf16(k.x, qf.c[i][pc].x, dot);
+        dot = dot2_bf16(k.y, qf.c[i][pc].y, dot);
+        dot = dot2_bf16(k.z, qf.c[i][pc].z, dot);
+        dot = dot2_bf16(k.w, qf.c[i][pc].w, dot);
       }
     }
   }
@@ -268,6 +271,7 @@ __device__ __forceinline__ void valu_item(const DecodeArgs& a, const int part, c
   // fused step: the newest position's K and V rows, its score, and whether its
   // block's table entry lies outside the pool
   __shared__ __attribute__((aligned(16))) A sm_fresh[2][D];
+  __shared__ float sm_fresh_scale[2];  // int8: the rows' scales (K, V)
   __shared__ float sm_fresh_s;
   __shared__ int sm_fresh_bad;
 
@@ -307,7 +311,7 @@ __device__ __forceinline__ void valu_item(const DecodeArgs& a, const int part, c
   // Fused step: the item holding position ctx - 1 takes that position from
   // the fresh rows (folded in at the merge) and walks the cache up to ctx - 2
   // only; with no cached position left in its range it walks nothing.
-  const bool fold = kFoldable<Tr> && a.fresh_key != nullptr && (!split || part == nparts - 1);
+  const bool fold = a.fresh_key != nullptr && (!split || part == nparts - 1);
   if (fold) te = ctx - 1 > max(tb, first) ? ctx - 1 : tb;
   const int jb = tb / kBlockTokens;
   const int je = (te + kBlockTokens - 1) / kBlockTokens;
@@ -333,7 +337,7 @@ __device__ __forceinline__ void valu_item(const DecodeArgs& a, const int part, c
       for (int pc = 0; pc < QueryFrag<Tr, D>::kPieces; ++pc)
         qf.c[i][pc] = *reinterpret_cast<const uint4*>(qrow + (4 * i + lane / 16) * X + pc * 8);
   }
-  if (fold && w == 0) fetch_fresh<Tr, D>(a, b, kvh, lane, sm_fresh, sm_fresh_bad);
+  if (fold && w == 0) fetch_fresh<Tr, D>(a, b, kvh, lane, sm_fresh, sm_fresh_bad, sm_fresh_scale);
 
   const S* kc = static_cast<const S*>(a.k_cache);
   const S* vc = static_cast<const S*>(a.v_cache);
@@ -402,8 +406,9 @@ __device__ __forceinline__ void valu_item(const DecodeArgs& a, const int part, c
   }
 
   if (fold && w == 0) {
-    const float sf = fresh_score<Tr, D>(sm_fresh[0], qf, lane);
-    if (lane == 0) sm_fresh_s = sf * a.scale_log2;
+    float sf = fresh_score<Tr, D>(sm_fresh[0], qf, lane) * a.scale_log2;
+    if constexpr (Tr::kKind == Kind::kInt8) sf *= sm_fresh_scale[0];  // as the blocks' ks
+    if (lane == 0) sm_fresh_s = sf;
   }
   // Wave totals: the denominator is spread over the 16 token lanes of a row.
   const float lsum = row16_sum(st.l);
@@ -439,7 +444,9 @@ __device__ __forceinline__ void valu_item(const DecodeArgs& a, const int part, c
     if (fold) {
       const float sc = fast_exp2(sm_fresh_s - M);
       L += sc;
-      acc = fmaf(act_to_f32<Tr>(sm_fresh[1][x]), sc, acc);
+      float v = act_to_f32<Tr>(sm_fresh[1][x]);
+      if constexpr (Tr::kKind == Kind::kInt8) v *= sm_fresh_scale[1];  // as the blocks' vs
+      acc = fmaf(v, sc, acc);
     }
     float res = acc / L * a.v_scale;
     if (bad) res = __int_as_float(0x7fc00000);

@@ -239,12 +239,6 @@ __device__ __forceinline__ uint32_t e4m3_code(float x) {
   return uint32_t(__builtin_amdgcn_cvt_pk_fp8_f32(c, c, 0, false)) & 0xFFu;
 }
 
-// Fused decode step (fresh rows): caches whose stored value is the input's
-// own bits.  fp8 and int8 pools store a quantised value the fold would have
-// to reproduce, and are not taken by the fused step.
-template <typename Tr>
-constexpr bool kFoldable = !kByteCodes<Tr>;
-
 template <typename Tr>
 __device__ __forceinline__ float act_to_f32(typename Tr::act v) {
   if constexpr (Tr::kKind == Kind::kF32) return v; else return bf16_to_f32(v);

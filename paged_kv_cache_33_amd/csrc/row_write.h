@@ -161,23 +161,73 @@ __host__ __device__ inline int64_t append_threads(const AppendArgs& a, Kind kind
   return int64_t(a.B) * a.num_kv_heads * (a.head_dim / X);
 }
 
-// Wave 0 of an item holding the newest position copies that position's K and
-// V rows (sequence b, KV head kvh) from the fused step's inputs into LDS, and
-// notes whether the table entry of its block lies outside the pool (the cache
-// write skips such a row, so the step's result is NaN as when the decode meets
-// such a block).  LDS operations of one wave complete in order, so the same
+// Wave 0 of an item holding the newest position puts that position's K and V
+// rows (sequence b, KV head kvh) into LDS as the cache will hold them once the
+// step's write has run, and notes whether the table entry of its block lies
+// outside the pool (the cache write skips such a row, so the step's result is
+// NaN as when the decode meets such a block).  bf16 and fp32 caches store the
+// rows' own bits, copied as they are.  One-byte caches store codes: the rows
+// are quantised here with the write's own functions on the same inputs, so
+// the codes are the ones the write stores, and each code goes to LDS as its
+// bf16 value (exact), in dim order, where the decode reads its operands
+// (an fp8 code without its scale, which the decode applies where it applies
+// it to cached codes; an int8 code with its row scale in fresh_scale[0] (K)
+// and [1] (V)).  LDS operations of one wave complete in order, so the same
 // wave reads them back after its walk without a barrier; the other waves read
 // them after the merge barrier.
 template <typename Tr, int D>
 __device__ __forceinline__ void fetch_fresh(const DecodeArgs& a, int b, int kvh, int lane,
-                                            typename Tr::act (*sm_fresh)[D], int& sm_fresh_bad) {
+                                            typename Tr::act (*sm_fresh)[D], int& sm_fresh_bad,
+                                            float* sm_fresh_scale) {
   using A = typename Tr::act;
   constexpr int CH = D * int(sizeof(A)) / 16;  // 16-byte chunks per row (<= 32)
-  if (lane < 2 * CH) {
-    const char* src = static_cast<const char*>(lane < CH ? a.fresh_key : a.fresh_value) +
-                      ((size_t(b) * a.num_kv_heads + kvh) * D) * sizeof(A) + (lane % CH) * 16;
-    const uint4 r = *reinterpret_cast<const uint4*>(src);
-    *reinterpret_cast<uint4*>(reinterpret_cast<char*>(&sm_fresh[lane / CH][0]) + (lane % CH) * 16) = r;
+  const size_t row = (size_t(b) * a.num_kv_heads + kvh) * D;
+  if constexpr (!kByteCodes<Tr>) {
+    if (lane < 2 * CH) {
+      const char* src = static_cast<const char*>(lane < CH ? a.fresh_key : a.fresh_value) +
+                        row * sizeof(A) + (lane % CH) * 16;
+      const uint4 r = *reinterpret_cast<const uint4*>(src);
+      *reinterpret_cast<uint4*>(reinterpret_cast<char*>(&sm_fresh[lane / CH][0]) + (lane % CH) * 16) = r;
+    }
+  } else {
+    // lanes r * CH + c: row r (0 = K, 1 = V), bf16 values 8c .. 8c + 7; the CH
+    // lanes of a row are consecutive and CH divides 64 (row maxima by shuffles)
+    static_assert(2 * CH <= kWave && (kWave % CH) == 0, "fresh rows in one wave");
+    const int r = (lane / CH) & 1, c = lane % CH;
+    const uint16_t* src = static_cast<const uint16_t*>(r ? a.fresh_value : a.fresh_key) + row + 8 * c;
+    const uint4 raw = *reinterpret_cast<const uint4*>(src);  // every lane: in bounds, unused past 2 CH
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+    float x[8];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      x[2 * k] = bf16_lo(w[k]);
+      x[2 * k + 1] = bf16_hi(w[k]);
+    }
+    uint32_t o[4];
+    if constexpr (Tr::kKind == Kind::kFp8) {
+      // the code source_chunk<Fp8> stores, decoded as the block path decodes it
+      const float scale = r ? a.append.v_scale : a.append.k_scale;
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        o[k] = code2_to_bf16x2<Kind::kFp8, false>(e4m3_code(x[2 * k] / scale) |
+                                                  (e4m3_code(x[2 * k + 1] / scale) << 8));
+    } else {
+      // int8_chunk's scale: the row's largest finite magnitude / 127 (a max,
+      // so the grouping of the lanes does not matter), then its codes
+      float amax = 0.f;
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (__builtin_isfinite(x[k])) amax = fmaxf(amax, fabsf(x[k]));
+      for (int off = 1; off < CH; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off, kWave));
+      const float s = amax / 127.f;
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        o[k] = code2_to_bf16x2<Kind::kInt8, false>(int8_code(x[2 * k], s) |
+                                                   (int8_code(x[2 * k + 1], s) << 8));
+      if (c == 0 && lane < 2 * CH) sm_fresh_scale[r] = s;
+    }
+    if (lane < 2 * CH)
+      *reinterpret_cast<uint4*>(&sm_fresh[r][8 * c]) = make_uint4(o[0], o[1], o[2], o[3]);
   }
   if (lane == 0) {
     const int pos = a.context_lens[b] - 1;
