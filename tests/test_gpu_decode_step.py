@@ -59,10 +59,12 @@ def test_gqa_bf16(d, H, H_kv, P_):
 @pytest.mark.parametrize("H,H_kv", [(4, 4), (32, 8)])
 @pytest.mark.parametrize("window", [1, 7, 16, 100])
 @pytest.mark.parametrize("P_", [0, 32])
-def test_windows(H, H_kv, window, P_):
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8", "int8"])
+def test_windows(H, H_kv, window, P_, kv_dtype):
     w = W.scattered_workload("step-win", "bf16", B=len(LENS), H=H, H_kv=H_kv, d=128,
-                             context_lens=LENS, seed=231 + window)
-    single_step_case(w, P_, label=f"step-window{window}", one_launch=True, window=window)
+                             context_lens=LENS, seed=231 + window, kv_dtype=kv_dtype)
+    single_step_case(w, P_, label=f"step-window{window}-{kv_dtype}", one_launch=True,
+                     window=window, per_row=kv_dtype == "int8")
 
 
 @pytest.mark.parametrize("H,H_kv,dtype", [(4, 4, "bf16"), (16, 2, "bf16"), (2, 2, "f32")])
@@ -81,12 +83,13 @@ def test_single_token_context_returns_the_new_value_row(H, H_kv, dtype, P_):
 
 @pytest.mark.parametrize("H,H_kv", [(4, 4), (16, 2)])
 @pytest.mark.parametrize("P_", [0, 32])
-def test_bad_entry_for_the_newest_block(H, H_kv, P_):
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8", "int8"])
+def test_bad_entry_for_the_newest_block(H, H_kv, P_, kv_dtype):
     # sequence 1's newest position opens block 2 (ctx 33); sequence 2's sits
     # inside block 1 (ctx 30); both blocks' entries point outside the pool
     lens = [40, 33, 30, 17]
     w = W.scattered_workload("step-bad", "bf16", B=4, H=H, H_kv=H_kv, d=128,
-                             context_lens=lens, seed=251)
+                             context_lens=lens, seed=251, kv_dtype=kv_dtype)
     step = w.steps[0]
     kp, vp = poison(w, step.context_lens.astype(np.int64) - 1)
     good_tables = w.block_tables.copy()
@@ -102,15 +105,16 @@ def test_bad_entry_for_the_newest_block(H, H_kv, P_):
     # tables gives their outputs
     w.block_tables[:] = good_tables
     _, _, _, ref = oracle_step(w, kp, vp, step, seqs=[0, 3])
-    assert_close(got, ref, "bf16", "step-bad-entry")
+    assert_close(got, ref, "bf16", f"step-bad-entry-{kv_dtype}", per_row=kv_dtype == "int8")
 
 
 @pytest.mark.parametrize("H,H_kv", [(4, 4), (8, 2)])
 @pytest.mark.parametrize("P_", [0, 16])
-def test_empty_contexts(H, H_kv, P_):
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8", "int8"])
+def test_empty_contexts(H, H_kv, P_, kv_dtype):
     lens = [0, 20, 0, 33]
     w = W.scattered_workload("step-empty", "bf16", B=4, H=H, H_kv=H_kv, d=128,
-                             context_lens=lens, seed=261)
+                             context_lens=lens, seed=261, kv_dtype=kv_dtype)
     step = w.steps[0]
     kp, vp = poison(w, np.maximum(step.context_lens.astype(np.int64) - 1, 0))
     dw = upload(w, kp, vp)
@@ -119,7 +123,7 @@ def test_empty_contexts(H, H_kv, P_):
     assert list(slots.cpu().numpy()[[0, 2]]) == [-1, -1]
     assert np.all(got[[0, 2]] == 0)
     _, _, _, ref = oracle_step(w, kp, vp, step, seqs=[1, 3])
-    assert_close(got, ref, "bf16", "step-empty")
+    assert_close(got, ref, "bf16", f"step-empty-{kv_dtype}", per_row=kv_dtype == "int8")
 
 
 @pytest.mark.parametrize("kv_dtype", ["bf16", "fp8", "int8"])
