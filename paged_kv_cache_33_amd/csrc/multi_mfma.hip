@@ -339,13 +339,15 @@ __device__ __forceinline__ void load_block_lds_asm(MfmaFrag<E, D>& f, uint32_t b
 
 // One 16-byte unit of an int8 block's LDS stage (K units first: chunk u / 16
 // of token u % 16, 16 dims; then V rows, 16 tokens each) rewritten as bf16
-// into the bf16 layout of the same block at cv (K [d/8][16][8], then V
-// [d][16]): two 16-byte units.  int8 codes are bf16 values, so the operands
-// the products see are exactly those of converting in registers.  The LDS
-// accesses are written out: the compiler would otherwise order them after
-// the stage ring's global-to-LDS loads in flight (see load_block_lds_asm).
+// into the bf16 tile layouts of the same block, K [d/8][16][8] at cvk and V
+// [d][16] at cvv: two 16-byte units.  int8 codes are bf16 values, so the
+// operands the products see are exactly those of converting in registers.
+// The LDS accesses are written out: the compiler would otherwise order them
+// after the stage ring's global-to-LDS loads in flight (see
+// load_block_lds_asm).
 template <int D>
-__device__ __forceinline__ void convert_int8_unit_lds(uint32_t stage, uint32_t cv, int u) {
+__device__ __forceinline__ void convert_int8_unit_lds(uint32_t stage, uint32_t cvk, uint32_t cvv,
+                                                      int u) {
   constexpr int kKUnits = kBlockTokens * D / 16;  // int8 K units; bf16 has twice as many
   u32x4_t c;
   __asm__ volatile("ds_read_b128 %0, %1" : "=v"(c) : "v"(stage + uint32_t(u) * 16));
@@ -355,17 +357,45 @@ __device__ __forceinline__ void convert_int8_unit_lds(uint32_t stage, uint32_t c
                       i8x2_to_bf16x2<false>(c.y), i8x2_to_bf16x2<true>(c.y)};
   const u32x4_t hi = {i8x2_to_bf16x2<false>(c.z), i8x2_to_bf16x2<true>(c.z),
                       i8x2_to_bf16x2<false>(c.w), i8x2_to_bf16x2<true>(c.w)};
-  uint32_t a0, a1;  // destination units
+  uint32_t a0, a1;  // destination addresses
   if (u < kKUnits) {
     const int c16 = u / kBlockTokens, t = u % kBlockTokens;
-    a0 = uint32_t((2 * c16) * kBlockTokens + t);
-    a1 = a0 + kBlockTokens;
+    a0 = cvk + uint32_t((2 * c16) * kBlockTokens + t) * 16;
+    a1 = a0 + kBlockTokens * 16;
   } else {
-    a0 = uint32_t(2 * kKUnits + 2 * (u - kKUnits));
-    a1 = a0 + 1;
+    a0 = cvv + uint32_t(2 * (u - kKUnits)) * 16;
+    a1 = a0 + 16;
   }
-  __asm__ volatile("ds_write_b128 %0, %1" ::"v"(cv + a0 * 16), "v"(lo) : "memory");
-  __asm__ volatile("ds_write_b128 %0, %1" ::"v"(cv + a1 * 16), "v"(hi) : "memory");
+  __asm__ volatile("ds_write_b128 %0, %1" ::"v"(a0), "v"(lo) : "memory");
+  __asm__ volatile("ds_write_b128 %0, %1" ::"v"(a1), "v"(hi) : "memory");
+}
+
+// One 16-byte unit (four row scales) copied between LDS addresses.
+__device__ __forceinline__ void copy_unit_lds(uint32_t from, uint32_t to) {
+  u32x4_t c;
+  __asm__ volatile("ds_read_b128 %0, %1" : "=v"(c) : "v"(from));
+  __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __asm__ volatile("" : "+v"(c));
+  __asm__ volatile("ds_write_b128 %0, %1" ::"v"(to), "v"(c) : "memory");
+}
+
+// The four row scales of tokens 4q .. 4q + 3 of two blocks, at a and b
+// (16 floats each), for lane quarter q.
+__device__ __forceinline__ void read_scales4_lds(uint32_t a, uint32_t b, int lane,
+                                                 float (*x)[4]) {
+  const uint32_t off = uint32_t(lane >> 4) * 16;
+  u32x4_t r[2];
+  __asm__ volatile("ds_read_b128 %0, %1" : "=v"(r[0]) : "v"(a + off));
+  __asm__ volatile("ds_read_b128 %0, %1" : "=v"(r[1]) : "v"(b + off));
+  __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __asm__ volatile("" : "+v"(r[0]), "+v"(r[1]));
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    x[h][0] = __uint_as_float(r[h].x);
+    x[h][1] = __uint_as_float(r[h].y);
+    x[h][2] = __uint_as_float(r[h].z);
+    x[h][3] = __uint_as_float(r[h].w);
+  }
 }
 
 // Two consecutive 16-token blocks a, b (keys key0 .. key0 + 31), read from
@@ -591,12 +621,16 @@ __device__ __forceinline__ void pin(T (&r)[N]) {
 // issued at its start (K of the next pair, then the first half of the
 // current pair's V; the second half once the first K has landed), so the
 // waits find them mostly done, and the exponentials of the current weights
-// have no dependence on any of them.
-template <typename E, int D, int kT, uint32_t kNa, uint32_t kNb, uint32_t kCa, uint32_t kCb>
+// have no dependence on any of them.  kScaled (int8 pools, the blocks
+// converted to bf16): the products take each weight times its token's V row
+// scale vs[h][j], the row sums the weights alone (as pair_pv).
+template <typename E, int D, int kT, uint32_t kNa, uint32_t kNb, uint32_t kCa, uint32_t kCb,
+          bool kScaled = false>
 __device__ __forceinline__ void pair_pipelined(uint32_t kl, uint32_t vl,
                                                const bf16x8_t (*qop)[MfmaShape<D>::KI],
                                                const floatx4_t (*sc)[kT], floatx4_t (*sn)[kT],
-                                               MfmaState<D>* st, float scale_log2) {
+                                               MfmaState<D>* st, float scale_log2,
+                                               const float (*vs)[4] = nullptr) {
   constexpr int KL = MfmaFrag<E, D>::KL;
   constexpr int MC = MfmaShape<D>::MC;
   constexpr int H = MC / 2;
@@ -612,7 +646,7 @@ __device__ __forceinline__ void pair_pipelined(uint32_t kl, uint32_t vl,
 #pragma unroll
   for (int tt = 0; tt < kT; ++tt) {
     const float mref = st[tt].m;
-    uint32_t pk[4];
+    uint32_t pk[4], pkv[4];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       float pw[4];
@@ -621,13 +655,20 @@ __device__ __forceinline__ void pair_pipelined(uint32_t kl, uint32_t vl,
         pw[j] = fast_exp2(__builtin_fmaf(sc[h][tt][j], scale_log2, -mref));
       pk[2 * h] = pack_bf16x2(pw[0], pw[1]);
       pk[2 * h + 1] = pack_bf16x2(pw[2], pw[3]);
+      if constexpr (kScaled) {
+        pkv[2 * h] = pack_bf16x2(pw[0] * vs[h][0], pw[1] * vs[h][1]);
+        pkv[2 * h + 1] = pack_bf16x2(pw[2] * vs[h][2], pw[3] * vs[h][3]);
+      }
     }
     constexpr uint32_t kOnes = 0x3F803F80u;  // two bf16 1.0
     float l = st[tt].l;
 #pragma unroll
     for (int k = 0; k < 4; ++k) l = dot2_bf16(pk[k], kOnes, l);
     st[tt].l = l;
-    pop[tt] = __builtin_bit_cast(bf16x8_t, make_uint4(pk[0], pk[1], pk[2], pk[3]));
+    if constexpr (kScaled)
+      pop[tt] = __builtin_bit_cast(bf16x8_t, make_uint4(pkv[0], pkv[1], pkv[2], pkv[3]));
+    else
+      pop[tt] = __builtin_bit_cast(bf16x8_t, make_uint4(pk[0], pk[1], pk[2], pk[3]));
   }
   // the next pair's scores, block by block as its K lands
 #pragma unroll
@@ -766,29 +807,35 @@ __global__ __launch_bounds__(kMultiWaves* kWave, kTiles == 1 ? 3 : 2) void chunk
   // chunks 0.975 -> 0.866 ms (bf16), 1.052 -> 0.957 ms (fp8); verification of
   // 8 draft tokens at g = 8, 528 -> 518 us (bf16), 416 -> 380 us (fp8).  One
   // tile per wave stays at three work-groups per CU.
-  // int8 pools with one tile per wave (draft verification) keep single
-  // blocks: pairs measured 1.5-3.5% slower there (and 6% faster with two
-  // tiles per wave, on prefill chunks).
-  constexpr bool kPairs = !(kInt8 && kTiles == 1);
-  constexpr int kTabWin = 1024;
+  // The table window: int8 pools take a smaller one, so three work-groups
+  // with one tile per wave fit a CU with their bf16 buffers (below).
+  constexpr int kTabWin = kInt8 ? 512 : 1024;
   // bf16 and fp8 pairs on the software-pipelined path (see below) take eight
   // stages where the work-groups of a CU still fit its 160 KiB of LDS (two
-  // with two tiles per wave, three with one); the other pairs six, single
-  // blocks four.
+  // with two tiles per wave, three with one); the others six.
   constexpr int kStageBytes = kUnits * 16;
   constexpr bool kPipe =
       !kInt8 && (kTiles == 2 ? 2 : 3) * (8 * kStageBytes + 4 * kTabWin + 1024) <= 160 * 1024;
-  constexpr int kStages = kPipe ? 8 : kPairs ? 6 : 4;
+  constexpr int kStages = kPipe ? 8 : 6;
   __shared__ uint4 sm_kv[kStages][kUnits];
   __shared__ int sm_tab[kTabWin];
-  // int8: each pair of blocks is converted to bf16 once per work-group
-  // (every thread two 16-byte units) into sm_cv, and the waves take their
-  // operands from there and the row scales from the ring stages (C, the
-  // compute type, keeps the row scales).
+  // int8: the blocks are converted to bf16 once per work-group (each
+  // thread one or two 16-byte units of codes per block) into sm_cv, and the
+  // waves take their operands from there (C, the compute type, keeps the row
+  // scales).  sm_cv holds six bf16 tiles, with kBT the bytes of one:
+  //   [K a][V a, slot 0][K b][V b, slot 0][V a, slot 1][V b, slot 1]
+  // then the row scales: K's of a, b (16 floats each), V's of slot 0, V's of
+  // slot 1.  A pair converted for the general loop below takes the first four
+  // tiles (block a's K and V adjacent, as is b's) and keeps its row scales in
+  // the ring stages; the pipelined path converts each pair one pair ahead, K
+  // into the K tiles and V into the slot the pair being computed does not
+  // read, with the row scales beside them.
   constexpr bool kConvert = kInt8;
   using C = std::conditional_t<kConvert, Int8AsBf16, E>;
   constexpr int kCvUnits = 2 * kTileElems * 2 / 16;  // one bf16 block, K and V
-  __shared__ uint4 sm_cv[kConvert ? (kPairs ? 2 : 1) * kCvUnits : 1];
+  constexpr uint32_t kBT = kTileElems * 2;            // one bf16 tile
+  constexpr int kCvScaleUnits = 3 * 2 * kScaleUnits;   // K's, V's of two slots
+  __shared__ uint4 sm_cv[kConvert ? 3 * kCvUnits + kCvScaleUnits : 1];
 
   __shared__ int sm_order[kOrderBuckets + kMultiWaves + 1];
   const int b = __builtin_amdgcn_readfirstlane(
@@ -927,11 +974,6 @@ __global__ __launch_bounds__(kMultiWaves* kWave, kTiles == 1 ? 3 : 2) void chunk
       }
     }
   };
-  // vector-memory operations of this wave per block
-  constexpr int kPerWave = kPer;
-  auto wait_block = [&](int later_blocks) {  // block j landed: later blocks may still run
-    wait_vm_later<kStages - 2, kPerWave>(later_blocks);
-  };
 
   // the query operands are in registers before any block load is issued
   __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
@@ -1020,15 +1062,15 @@ __global__ __launch_bounds__(kMultiWaves* kWave, kTiles == 1 ? 3 : 2) void chunk
       const int units = (jj + 1 < wje ? 2 : 1) * 2 * kTileUnits;
       for (int u = tid; u < units; u += kThreads) {
         const int h = u / (2 * kTileUnits);
-        convert_int8_unit_lds<D>(stage_addr(jj + h), cv0 + uint32_t(h) * kCvUnits * 16,
-                                 u - h * 2 * kTileUnits);
+        const uint32_t cvk = cv0 + uint32_t(h) * kCvUnits * 16;
+        convert_int8_unit_lds<D>(stage_addr(jj + h), cvk, cvk + kBT, u - h * 2 * kTileUnits);
       }
     }
   };
   auto operands_of = [&](int jj, int h) {  // block jj + h (h = 0, 1)
     return kConvert ? cv0 + uint32_t(h) * kCvUnits * 16 : stage_addr(jj + h);
   };
-  if constexpr (kPairs) {
+  {
     // blocks wjb .. wjb + 3 in flight; at pair (j, j + 1) the two after it
     // may still be loading
     for (int t = 0; t < kStages - 2 && wjb + t < wje; ++t) issue_at(wjb + t);
@@ -1165,6 +1207,106 @@ __global__ __launch_bounds__(kMultiWaves* kWave, kTiles == 1 ? 3 : 2) void chunk
           if (active) run(std::true_type{});
           else run(std::false_type{});
         }
+      } else if constexpr (kConvert) {
+        // int8, software-pipelined as above on the bf16 copies: at pair j the
+        // work-group converts pair j + 2 (K into the K tiles, V into the slot
+        // pair j does not read, the row scales beside them), then each wave
+        // computes pair j + 2's scores and pair j's weights and products.
+        // Six ring stages: pair j + 2 converting, pair j + 4 loading, and the
+        // pair issued, j + 6, takes the stages of pair j, converted one pair
+        // earlier.  Invariant at the top of an iteration: blocks below j + 6
+        // are issued.  Two barriers per pair: one before the conversion (pair
+        // j + 2 landed for every wave, every wave done with what the
+        // conversion overwrites), one after it.
+        if (open(j)) {
+          // Iterations: pairs j = wjb, wjb + 2, ... while pair j + 2 is whole
+          // for every column and blocks j + 6, j + 7 exist; an even count, so
+          // that every path ends on the same score buffer and V slot.
+          const int jmax = min(wje - 8, ((kmin_wg - (2 * kBlockTokens - 1)) >> 4) - 2);
+          const int n_iter = jmax >= j ? ((jmax - j) / 2 + 1) & ~1 : 0;
+          const uint32_t kl = cv0 + uint32_t(lane) * 16;
+          const uint32_t vl = cv0 + uint32_t((n * kBlockTokens + 4 * q) * 2);
+          constexpr uint32_t kScaleBytes = kBlockTokens * sizeof(float);  // one tile's
+          const uint32_t ks0 = cv0 + 6 * kBT;  // K row scales of a, then b
+          auto vs_at = [&](int slot) { return ks0 + uint32_t(1 + slot) * 2 * kScaleBytes; };
+          auto convert_ahead = [&](int jn, int slot) {
+            constexpr int kBlockUnits = 2 * kTileUnits;  // code units of one block
+#pragma unroll
+            for (int k = 0; k < (2 * kBlockUnits + kThreads - 1) / kThreads; ++k) {
+              const int u = tid + k * kThreads;
+              if (u < 2 * kBlockUnits) {
+                const int h = u / kBlockUnits;
+                const uint32_t vt = cv0 + uint32_t(slot ? 4 + h : 1 + 2 * h) * kBT;
+                convert_int8_unit_lds<D>(stage_addr(jn + h), cv0 + uint32_t(2 * h) * kBT, vt,
+                                         u - h * kBlockUnits);
+              }
+            }
+            if (tid < 4 * kScaleUnits) {  // (block h, unit r: K's, then V's)
+              const int h = tid / (2 * kScaleUnits), r = tid % (2 * kScaleUnits);
+              const uint32_t to = (r < kScaleUnits ? ks0 : vs_at(slot)) + uint32_t(h) * kScaleBytes +
+                                  uint32_t(r % kScaleUnits) * 16;
+              copy_unit_lds(stage_addr(jn + h) + uint32_t(2 * kTileUnits + r) * 16, to);
+            }
+          };
+          auto run = [&](auto act) {
+            constexpr bool kAct = decltype(act)::value;
+            float thr[kTiles];
+#pragma unroll
+            for (int tt = 0; tt < kTiles; ++tt) thr[tt] = (st[tt].m + kRescaleSlack) / a.scale_log2;
+            auto rescale = [&](floatx4_t (*sc)[kTiles]) {  // K row scales of the pair converted last
+              float ks[2][4];
+              read_scales4_lds(ks0, ks0 + kScaleBytes, lane, ks);
+              pair_rescale<D, false, false, kTiles, true>(sc, st, 0, 2 * kBlockTokens,
+                                                          a.scale_log2, lane, 0, lo, limit, ks, thr);
+            };
+            // pair j landed (the two blocks after it may still be loading)
+            wait_vm_later<kStages - 4, kPer>(min(kStages - 4, max(wje - 2 - j, 0)));
+            lds_barrier();
+            convert_ahead(j, 0);
+            if (j + 4 < wje) issue_at(j + 4);
+            if (j + 5 < wje) issue_at(j + 5);
+            lds_barrier();
+            floatx4_t s0[2][kTiles], s1[2][kTiles];
+            if constexpr (kAct) {
+              pair_scores<C, D, kTiles>(cv0, cv0 + 2 * kBT, qop, s0, lane);
+              rescale(s0);
+            }
+            // iteration M (mod 2): pair j's V in slot M, its scores in sc
+            auto iter = [&](auto mtag, floatx4_t (*sc)[kTiles], floatx4_t (*sn)[kTiles]) {
+              constexpr unsigned M = decltype(mtag)::value;
+              __builtin_amdgcn_s_waitcnt(vm_wait_imm(2 * kPer));  // pair j + 2 landed
+              lds_barrier();
+              issue_at(j + 6);
+              issue_at(j + 7);
+              convert_ahead(j + 2, 1 - M);
+              lds_barrier();
+              if constexpr (kAct) {
+                float vs[2][4];
+                read_scales4_lds(vs_at(M), vs_at(M) + kScaleBytes, lane, vs);
+                pair_pipelined<C, D, kTiles, 0, 2 * kBT, (M ? 4 : 1) * kBT, (M ? 5 : 3) * kBT,
+                               true>(kl, vl, qop, sc, sn, st, a.scale_log2, vs);
+                rescale(sn);
+              }
+              j += 2;
+            };
+            using I0 = std::integral_constant<unsigned, 0>;
+            using I1 = std::integral_constant<unsigned, 1>;
+            for (int it = 0; it < n_iter; it += 2) {
+              iter(I0{}, s0, s1);
+              iter(I1{}, s1, s0);
+            }
+            // the last pair of the path (V in slot 0): its weights and products
+            if constexpr (kAct) {
+              float vs[2][4];
+              read_scales4_lds(vs_at(0), vs_at(0) + kScaleBytes, lane, vs);
+              pair_pv<C, D, false, false, kTiles, true>(cv0, cv0 + 2 * kBT, s0, st, 0,
+                                                        2 * kBlockTokens, a.scale_log2, lane, vs);
+            }
+            j += 2;
+          };
+          if (active) run(std::true_type{});
+          else run(std::false_type{});
+        }
       } else {
         auto step = [&](int jj) {
           wait_vm_later<kStages - 4, kPer>(min(kStages - 4, max(wje - 2 - jj, 0)));
@@ -1172,25 +1314,15 @@ __global__ __launch_bounds__(kMultiWaves* kWave, kTiles == 1 ? 3 : 2) void chunk
           if (jj + kStages - 2 < wje) issue_at(jj + kStages - 2);
           if (jj + kStages - 1 < wje) issue_at(jj + kStages - 1);
         };
-        auto convert_step = [&](int jj) {
-          if constexpr (kConvert) {
-            convert_pair(jj);
-            lds_barrier();  // the bf16 blocks are complete
-          }
-        };
         if (active) {
           for (; open(j); j += 2) {
             step(j);
-            convert_step(j);
-            compute_pair_lds<C, D, false, false, kTiles>(
-                operands_of(j, 0), operands_of(j, 1), qop, st, 0, 2 * kBlockTokens, a.scale_log2,
-                lane, 0, lo, limit, stage_addr(j), stage_addr(j + 1));
+            compute_pair_lds<C, D, false, false, kTiles>(stage_addr(j), stage_addr(j + 1), qop, st,
+                                                         0, 2 * kBlockTokens, a.scale_log2, lane,
+                                                         0, lo, limit);
           }
         } else {
-          for (; open(j); j += 2) {
-            step(j);
-            convert_step(j);
-          }
+          for (; open(j); j += 2) step(j);
         }
       }
     }
@@ -1239,48 +1371,6 @@ __global__ __launch_bounds__(kMultiWaves* kWave, kTiles == 1 ? 3 : 2) void chunk
         single(j + 1, sb);
       }
     }
-  } else {
-    for (int t = 0; t < kStages - 1 && wjb + t < wje; ++t) issue_at(wjb + t);
-    // block j is in LDS for every wave, and every wave is done with block
-    // j - 1, whose buffer the next issue reuses; then (int8) the block in bf16
-    auto step = [&](int jj) -> uint32_t {
-      wait_block(min(kStages - 2, wje - 1 - jj));
-      lds_barrier();
-      const int jn = jj + kStages - 1;
-      if (jn < wje) issue_at(jn);
-      uint32_t operands = stage_addr(jj);
-      if constexpr (kConvert) {
-        const uint32_t cv = lds_offset(&sm_cv[0]);
-        if (tid < 2 * kTileUnits) convert_int8_unit_lds<D>(operands, cv, tid);
-        lds_barrier();  // the bf16 block is complete
-        operands = cv;
-      }
-      return operands;
-    };
-    int j = wjb;
-    {
-      // the blocks every column of the work-group sees whole, on a straight
-      // path (as for pairs above)
-      const int kmin_wg = pos0 + cbeg / g;
-      const int klo_wg = window_first(pos0 + (cend - 1) / g, a.window);
-      auto open = [&](int jj) {
-        return jj < wje && jj * kBlockTokens >= klo_wg &&
-               jj * kBlockTokens + kBlockTokens - 1 <= kmin_wg;
-      };
-      if (active) {
-        for (; open(j); ++j) {
-          const uint32_t operands = step(j);
-          MfmaFrag<C, D> f;
-          load_block_lds_asm<C, D>(f, operands, lane);
-          if constexpr (kInt8) load_scales_lds_asm<E, D>(f, stage_addr(j), lane);
-          compute_block_tiles<C, D, false, false, kTiles>(f, qop, st, 0, kBlockTokens,
-                                                          a.scale_log2, lane, 0, lo, limit);
-        }
-      } else {
-        for (; open(j); ++j) step(j);
-      }
-    }
-    for (; j < wje; ++j) single(j, step(j));
   }
 
   // A staged table word lay outside the pool: the wave's columns turn NaN if
