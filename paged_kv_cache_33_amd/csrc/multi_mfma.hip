@@ -345,14 +345,11 @@ __device__ __forceinline__ void load_block_lds_asm(MfmaFrag<E, D>& f, uint32_t b
 // The LDS accesses are written out: the compiler would otherwise order them
 // after the stage ring's global-to-LDS loads in flight (see
 // load_block_lds_asm).
+// (write_int8_unit_lds: the second half, for codes c already read.)
 template <int D>
-__device__ __forceinline__ void convert_int8_unit_lds(uint32_t stage, uint32_t cvk, uint32_t cvv,
-                                                      int u) {
+__device__ __forceinline__ void write_int8_unit_lds(u32x4_t c, uint32_t cvk, uint32_t cvv,
+                                                    int u) {
   constexpr int kKUnits = kBlockTokens * D / 16;  // int8 K units; bf16 has twice as many
-  u32x4_t c;
-  __asm__ volatile("ds_read_b128 %0, %1" : "=v"(c) : "v"(stage + uint32_t(u) * 16));
-  __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  __asm__ volatile("" : "+v"(c));
   const u32x4_t lo = {i8x2_to_bf16x2<false>(c.x), i8x2_to_bf16x2<true>(c.x),
                       i8x2_to_bf16x2<false>(c.y), i8x2_to_bf16x2<true>(c.y)};
   const u32x4_t hi = {i8x2_to_bf16x2<false>(c.z), i8x2_to_bf16x2<true>(c.z),
@@ -369,32 +366,39 @@ __device__ __forceinline__ void convert_int8_unit_lds(uint32_t stage, uint32_t c
   __asm__ volatile("ds_write_b128 %0, %1" ::"v"(a0), "v"(lo) : "memory");
   __asm__ volatile("ds_write_b128 %0, %1" ::"v"(a1), "v"(hi) : "memory");
 }
-
-// One 16-byte unit (four row scales) copied between LDS addresses.
-__device__ __forceinline__ void copy_unit_lds(uint32_t from, uint32_t to) {
+template <int D>
+__device__ __forceinline__ void convert_int8_unit_lds(uint32_t stage, uint32_t cvk, uint32_t cvv,
+                                                      int u) {
   u32x4_t c;
-  __asm__ volatile("ds_read_b128 %0, %1" : "=v"(c) : "v"(from));
+  __asm__ volatile("ds_read_b128 %0, %1" : "=v"(c) : "v"(stage + uint32_t(u) * 16));
   __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   __asm__ volatile("" : "+v"(c));
-  __asm__ volatile("ds_write_b128 %0, %1" ::"v"(to), "v"(c) : "memory");
+  write_int8_unit_lds<D>(c, cvk, cvv, u);
 }
 
-// The four row scales of tokens 4q .. 4q + 3 of two blocks, at a and b
-// (16 floats each), for lane quarter q.
-__device__ __forceinline__ void read_scales4_lds(uint32_t a, uint32_t b, int lane,
-                                                 float (*x)[4]) {
+// The four row scales of tokens 4q .. 4q + 3 (lane quarter q) of two blocks'
+// K rows, at ka and ka + 64 (16 floats each), and of their V rows, at va and
+// va + 64; one wait for the four reads.
+__device__ __forceinline__ void read_pair_scales_lds(uint32_t ka, uint32_t va, int lane,
+                                                     float (*ks)[4], float (*vs)[4]) {
   const uint32_t off = uint32_t(lane >> 4) * 16;
-  u32x4_t r[2];
-  __asm__ volatile("ds_read_b128 %0, %1" : "=v"(r[0]) : "v"(a + off));
-  __asm__ volatile("ds_read_b128 %0, %1" : "=v"(r[1]) : "v"(b + off));
+  u32x4_t r[4];
+  __asm__ volatile("ds_read_b128 %0, %1" : "=v"(r[0]) : "v"(ka + off));
+  __asm__ volatile("ds_read_b128 %0, %1 offset:64" : "=v"(r[1]) : "v"(ka + off));
+  __asm__ volatile("ds_read_b128 %0, %1" : "=v"(r[2]) : "v"(va + off));
+  __asm__ volatile("ds_read_b128 %0, %1 offset:64" : "=v"(r[3]) : "v"(va + off));
   __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  __asm__ volatile("" : "+v"(r[0]), "+v"(r[1]));
+  __asm__ volatile("" : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]));
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    x[h][0] = __uint_as_float(r[h].x);
-    x[h][1] = __uint_as_float(r[h].y);
-    x[h][2] = __uint_as_float(r[h].z);
-    x[h][3] = __uint_as_float(r[h].w);
+    ks[h][0] = __uint_as_float(r[h].x);
+    ks[h][1] = __uint_as_float(r[h].y);
+    ks[h][2] = __uint_as_float(r[h].z);
+    ks[h][3] = __uint_as_float(r[h].w);
+    vs[h][0] = __uint_as_float(r[2 + h].x);
+    vs[h][1] = __uint_as_float(r[2 + h].y);
+    vs[h][2] = __uint_as_float(r[2 + h].z);
+    vs[h][3] = __uint_as_float(r[2 + h].w);
   }
 }
 
@@ -1229,23 +1233,39 @@ __global__ __launch_bounds__(kMultiWaves* kWave, kTiles == 1 ? 3 : 2) void chunk
           constexpr uint32_t kScaleBytes = kBlockTokens * sizeof(float);  // one tile's
           const uint32_t ks0 = cv0 + 6 * kBT;  // K row scales of a, then b
           auto vs_at = [&](int slot) { return ks0 + uint32_t(1 + slot) * 2 * kScaleBytes; };
+          // All LDS reads of a thread's share first (its code units, and for
+          // threads 0..15 one unit of row scales), one wait, then the writes.
           auto convert_ahead = [&](int jn, int slot) {
             constexpr int kBlockUnits = 2 * kTileUnits;  // code units of one block
+            constexpr int kU = (2 * kBlockUnits + kThreads - 1) / kThreads;
+            static_assert(2 * kBlockUnits % kThreads == 0, "every thread converts kU units");
+            u32x4_t c[kU], sc;
 #pragma unroll
-            for (int k = 0; k < (2 * kBlockUnits + kThreads - 1) / kThreads; ++k) {
-              const int u = tid + k * kThreads;
-              if (u < 2 * kBlockUnits) {
-                const int h = u / kBlockUnits;
-                const uint32_t vt = cv0 + uint32_t(slot ? 4 + h : 1 + 2 * h) * kBT;
-                convert_int8_unit_lds<D>(stage_addr(jn + h), cv0 + uint32_t(2 * h) * kBT, vt,
-                                         u - h * kBlockUnits);
-              }
+            for (int k = 0; k < kU; ++k) {
+              const int u = tid + k * kThreads, h = u / kBlockUnits;
+              __asm__ volatile("ds_read_b128 %0, %1"
+                               : "=v"(c[k])
+                               : "v"(stage_addr(jn + h) + uint32_t(u - h * kBlockUnits) * 16));
             }
-            if (tid < 4 * kScaleUnits) {  // (block h, unit r: K's, then V's)
-              const int h = tid / (2 * kScaleUnits), r = tid % (2 * kScaleUnits);
-              const uint32_t to = (r < kScaleUnits ? ks0 : vs_at(slot)) + uint32_t(h) * kScaleBytes +
-                                  uint32_t(r % kScaleUnits) * 16;
-              copy_unit_lds(stage_addr(jn + h) + uint32_t(2 * kTileUnits + r) * 16, to);
+            const bool copies = tid < 4 * kScaleUnits;  // (block h, unit r: K's, then V's)
+            const int sh = tid / (2 * kScaleUnits), sr = tid % (2 * kScaleUnits);
+            if (copies)
+              __asm__ volatile("ds_read_b128 %0, %1"
+                               : "=v"(sc)
+                               : "v"(stage_addr(jn + sh) + uint32_t(2 * kTileUnits + sr) * 16));
+            __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+            for (int k = 0; k < kU; ++k) {
+              __asm__ volatile("" : "+v"(c[k]));
+              const int u = tid + k * kThreads, h = u / kBlockUnits;
+              const uint32_t vt = cv0 + uint32_t(slot ? 4 + h : 1 + 2 * h) * kBT;
+              write_int8_unit_lds<D>(c[k], cv0 + uint32_t(2 * h) * kBT, vt, u - h * kBlockUnits);
+            }
+            if (copies) {
+              __asm__ volatile("" : "+v"(sc));
+              const uint32_t to = (sr < kScaleUnits ? ks0 : vs_at(slot)) +
+                                  uint32_t(sh) * kScaleBytes + uint32_t(sr % kScaleUnits) * 16;
+              __asm__ volatile("ds_write_b128 %0, %1" ::"v"(to), "v"(sc) : "memory");
             }
           };
           auto run = [&](auto act) {
@@ -1253,9 +1273,13 @@ __global__ __launch_bounds__(kMultiWaves* kWave, kTiles == 1 ? 3 : 2) void chunk
             float thr[kTiles];
 #pragma unroll
             for (int tt = 0; tt < kTiles; ++tt) thr[tt] = (st[tt].m + kRescaleSlack) / a.scale_log2;
-            auto rescale = [&](floatx4_t (*sc)[kTiles]) {  // K row scales of the pair converted last
+            // vcur: the V row scales of the pair whose products come next
+            float vcur[2][4];
+            // the pair converted last (its V in `slot`): its scores' rescale,
+            // and its V row scales into vcur
+            auto rescale = [&](floatx4_t (*sc)[kTiles], int slot) {
               float ks[2][4];
-              read_scales4_lds(ks0, ks0 + kScaleBytes, lane, ks);
+              read_pair_scales_lds(ks0, vs_at(slot), lane, ks, vcur);
               pair_rescale<D, false, false, kTiles, true>(sc, st, 0, 2 * kBlockTokens,
                                                           a.scale_log2, lane, 0, lo, limit, ks, thr);
             };
@@ -1269,7 +1293,7 @@ __global__ __launch_bounds__(kMultiWaves* kWave, kTiles == 1 ? 3 : 2) void chunk
             floatx4_t s0[2][kTiles], s1[2][kTiles];
             if constexpr (kAct) {
               pair_scores<C, D, kTiles>(cv0, cv0 + 2 * kBT, qop, s0, lane);
-              rescale(s0);
+              rescale(s0, 0);
             }
             // iteration M (mod 2): pair j's V in slot M, its scores in sc
             auto iter = [&](auto mtag, floatx4_t (*sc)[kTiles], floatx4_t (*sn)[kTiles]) {
@@ -1281,11 +1305,9 @@ __global__ __launch_bounds__(kMultiWaves* kWave, kTiles == 1 ? 3 : 2) void chunk
               convert_ahead(j + 2, 1 - M);
               lds_barrier();
               if constexpr (kAct) {
-                float vs[2][4];
-                read_scales4_lds(vs_at(M), vs_at(M) + kScaleBytes, lane, vs);
                 pair_pipelined<C, D, kTiles, 0, 2 * kBT, (M ? 4 : 1) * kBT, (M ? 5 : 3) * kBT,
-                               true>(kl, vl, qop, sc, sn, st, a.scale_log2, vs);
-                rescale(sn);
+                               true>(kl, vl, qop, sc, sn, st, a.scale_log2, vcur);
+                rescale(sn, 1 - M);
               }
               j += 2;
             };
@@ -1296,12 +1318,9 @@ __global__ __launch_bounds__(kMultiWaves* kWave, kTiles == 1 ? 3 : 2) void chunk
               iter(I1{}, s1, s0);
             }
             // the last pair of the path (V in slot 0): its weights and products
-            if constexpr (kAct) {
-              float vs[2][4];
-              read_scales4_lds(vs_at(0), vs_at(0) + kScaleBytes, lane, vs);
+            if constexpr (kAct)
               pair_pv<C, D, false, false, kTiles, true>(cv0, cv0 + 2 * kBT, s0, st, 0,
-                                                        2 * kBlockTokens, a.scale_log2, lane, vs);
-            }
+                                                        2 * kBlockTokens, a.scale_log2, lane, vcur);
             j += 2;
           };
           if (active) run(std::true_type{});
