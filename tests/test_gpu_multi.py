@@ -112,6 +112,10 @@ CASES = [
     ("g24", 48, 2, 128, [60, 33], [5, 2]),
     # sequences with no new token this step next to others
     ("idle-rows", 16, 2, 128, [30, 64, 65, 10], [0, 8, 0, 3]),
+    # 6 to 8 draft tokens at g = 8 (3 or 4 tiles, one per wave) over contexts
+    # long enough for the pipelined pairs, d 64 and 128
+    ("g8-verify8", 32, 4, 64, [900, 450, 1300], [8, 6, 7]),
+    ("g8-verify8-d128", 16, 2, 128, [700, 260], [8, 8]),
 ]
 
 
@@ -256,7 +260,7 @@ def test_chunk_write_alone_is_bit_exact(kv, d):
     assert np.array_equal(from_dev(dw.pool.v_cache, kv), vp)
 
 
-@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8", "int8"])
 def test_long_chunk_kernel_contains_bad_inputs(kv_dtype):
     """The same containment for the long-chunk kernel (g * max_query_len of 320
     columns, ten column sets): n > ctx, n > max_query_len and ctx > max_nb*16

@@ -110,6 +110,7 @@ MULTI = [
     ("g8-verify", 32, 4, 128, [700, 33, 129, 1500, 20, 260], [2, 4, 5, 4, 1, 3]),
     ("g4-chunk", 16, 4, 64, [40, 90, 200, 31], [40, 17, 32, 31]),
     ("mha", 4, 4, 128, [5, 40, 300, 17, 64, 1000], [5, 4, 16, 17, 33, 1]),
+    ("g8-verify8", 32, 4, 64, [900, 450, 1300], [8, 6, 7]),
 ]
 
 
@@ -121,12 +122,17 @@ def test_windowed_multi_matches_oracle(case, kv, window):
 
 
 @pytest.mark.parametrize("kv", ["bf16", "fp8", "int8"])
-def test_windowed_long_chunk_matches_oracle(kv):
-    # g = 8 with 64 and 40 rows (the LDS-staged kernel, two tiles per wave)
-    # and a 1,000-token window: the work-groups' first blocks are odd and
-    # even in turn, and each walks more than 32 blocks, past the wrap of the
-    # per-block validity bits
-    windowed_multi_case(("g8-long", 64, 8, 128, [1500, 2100], [64, 40]), kv, 1000)
+@pytest.mark.parametrize("case", [
+    # g = 8 with 64 and 40 rows (the LDS-staged kernel, two tiles per wave):
+    # the work-groups' first blocks are odd and even in turn, and each walks
+    # more than 32 blocks, past the wrap of the per-block validity bits
+    ("g8-long", 64, 8, 128, [1500, 2100], [64, 40]),
+    # 8 and 6 draft tokens at g = 8 (one tile per wave): the pipelined pairs
+    # start inside the window
+    ("g8-verify-long", 32, 4, 128, [1500, 2100], [8, 6]),
+], ids=["two-tiles", "one-tile"])
+def test_windowed_long_chunk_matches_oracle(case, kv):
+    windowed_multi_case(case, kv, 1000)
 
 
 def windowed_multi_case(case, kv, window):
