@@ -411,9 +411,10 @@ __device__ __forceinline__ void read_pair_scales_lds(uint32_t ka, uint32_t va, i
 // takes them from the two token-minor V tiles (8 bytes of each for bf16), so
 // a pair needs no lane exchange and half the P V instructions of two 16-deep
 // products.  The softmax runs once over both blocks (one reference max for
-// the pair).  bf16 and fp8 pools.  The work comes in three parts, so a
-// caller can compute the next pair's scores while this pair's weights and
-// products run: pair_scores, pair_rescale, pair_pv.
+// the pair).  bf16 and fp8 pools, and int8 pools converted to bf16.  The
+// work comes in three parts, so a caller can compute the next pair's scores
+// while this pair's weights and products run: pair_scores, pair_rescale,
+// pair_pv.
 //
 // pair_scores: the raw scores s[h][tt] (h = 0: block a, 1: block b).  To
 // stay within 256 VGPRs at two waves per SIMD the operands are read in
@@ -775,12 +776,13 @@ __device__ __forceinline__ void compute_pair_lds(uint32_t sa, uint32_t sb,
 // Several column sets per sequence and KV head (a prefill chunk, or draft
 // verification with 33..64 columns).  Each wave owns one set of 16 * kTiles
 // columns (kTiles = 2 for prefill chunks, 1 for verification: three
-// work-groups per CU) and walks every block its columns see; the waves of a
-// work-group need
-// nearly the same blocks (their positions differ by at most 128 / g tokens),
-// so the work-group loads each block once, cooperatively, into a 4-stage LDS
-// ring (direct global-to-LDS loads, three blocks ahead), and every wave reads
-// its operands there; with fewer than four sets the idle waves only load.
+// work-groups per CU) and walks every block its columns see, two blocks at a
+// time; the waves of a work-group need nearly the same blocks (their
+// positions differ by at most 128 / g tokens), so the work-group loads each
+// block once, cooperatively, into an LDS ring of six or eight stages (direct
+// global-to-LDS loads, two pairs ahead), and every wave reads its operands
+// there; with fewer than four sets the idle waves only load (and, for int8
+// pools, convert).
 // The K/V of a sequence is read by all of its work-groups, so these loads are
 // ordinary (cached) ones.  No partial results meet: a wave finishes its own
 // columns.
