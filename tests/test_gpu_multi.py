@@ -116,6 +116,9 @@ CASES = [
     # long enough for the pipelined pairs, d 64 and 128
     ("g8-verify8", 32, 4, 64, [900, 450, 1300], [8, 6, 7]),
     ("g8-verify8-d128", 16, 2, 128, [700, 260], [8, 8]),
+    # group 4, d 64, chunks of 33-40 rows (two tiles per wave) over long
+    # contexts: many pipelined pairs per work-group
+    ("g4-chunk-long", 16, 4, 64, [700, 1000], [40, 33]),
 ]
 
 
@@ -291,3 +294,34 @@ def test_long_chunk_kernel_contains_bad_inputs(kv_dtype):
     assert np.all(np.isnan(O.bits_to_f64(got[rows(4)], "bf16")))          # ctx > max_nb * 16
     ref = _ref_rows(w, w.k_pool, w.v_pool, seqs=[0])
     assert_rows_close(got, ref, "good sequence next to bad ones")
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8", "int8"])
+@pytest.mark.parametrize("shape", [
+    # (H, H_kv, d, context lengths, rows per sequence)
+    (64, 8, 128, [1500, 2100, 900, 3000], [8, 8, 8, 8]),      # one tile per wave
+    (64, 8, 128, [1200, 2600], [64, 48]),                      # two tiles per wave
+], ids=["verify", "chunk"])
+def test_repeated_calls_are_bit_identical(kv_dtype, shape):
+    """The LDS-staged kernel's pipelined pairs share each block between waves
+    through barriers; the same call repeated on the same pool gives the same
+    bits every time (a wave reading a stage before it is complete, or after
+    it is reused, would show as run-to-run differences), and the rows agree
+    with the oracle."""
+    H, H_kv, d, ctx, n = shape
+    w = W.multi_token_workload("rep", "bf16", len(ctx), H, H_kv, d, ctx, n, seed=91 + n[0],
+                               kv_dtype=kv_dtype)
+    m = w.multi
+    dw = upload(w, w.k_pool, w.v_pool)
+    log(f"[gpu] repeated multi {kv_dtype} rows={n}")
+    _, out0 = _gpu_multi(dw, m, write=True)
+    first = from_dev(out0, "bf16").copy()
+    for rep in range(4):
+        _, out = _gpu_multi(dw, m, write=False)
+        torch.cuda.synchronize()
+        got = from_dev(out, "bf16")
+        assert np.array_equal(got, first), f"call {rep + 2} differs from the first"
+    sl = O.chunk_slots(w.block_tables, m.context_lens, m.query_start)
+    kp, vp = O.reshape_and_cache(w.k_pool, w.v_pool, m.new_k, m.new_v, sl, w.H_kv, w.d,
+                                 w.kv_dtype, w.num_blocks, w.k_scale, w.v_scale)
+    assert_rows_close(first, _ref_rows(w, kp, vp, seqs=[0, len(ctx) - 1]), "repeated calls")
