@@ -9,7 +9,9 @@ taken per partition; the oracle's `partials` computes them in natural units
 (m_k = max s, l_k = sum e^(s - m_k)).  Converted, l * 2^m must equal
 l_k * e^(m_k), and o must equal o_k element by element.
 
-Also covered: the vector-ALU kernel's refill of its 64-entry table window (a
+Also covered: repeated split steps give the same bits (the work list's
+dealing and the streamed worker's prefetch of its next item), the vector-ALU
+kernel's refill of its 64-entry table window (a
 wave walks more than 64 blocks: contexts beyond 8,192 tokens in one pass) and
 the item-by-item split path taken by partitions longer than one streamed
 item (partition_size beyond 64 blocks per wave).
@@ -24,7 +26,7 @@ import oracle as O
 import paged_kv_cache_33_amd as P
 from workloads import configs as W
 
-from _harness import from_dev, log, poison, single_step_case, to_dev, upload
+from _harness import from_dev, gpu_step, log, poison, single_step_case, to_dev, upload
 
 pytestmark = pytest.mark.gpu
 
@@ -122,3 +124,28 @@ def test_long_partitions_take_the_item_by_item_path(kvd, Ps):
                              context_lens=lens, seed=83,
                              kv_dtype=None if kvd == "bf16" else kvd)
     single_step_case(w, Ps, label=f"long-partitions-{kvd}-P{Ps}", per_row=kvd == "int8")
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8", "int8"])
+@pytest.mark.parametrize("one_launch", [False, True], ids=["two-calls", "one-launch"])
+def test_repeated_split_steps_are_bit_identical(kv_dtype, one_launch):
+    """Resident workers deal the (sequence, partition) items among themselves
+    (bf16 and int8 pools: each streams its items back to back, requesting the
+    next item's table window and first tiles while it merges; fp8: item by
+    item), and the reduce merges the partials.  The same step repeated on the
+    same pool (its write stores the same rows again) gives the same output
+    bits every time."""
+    ctx = [20000, 9000, 3000, 700, 17]
+    w = W.scattered_workload("rep-split", "bf16", B=len(ctx), H=32, H_kv=8, d=128,
+                             context_lens=ctx, seed=123, kv_dtype=kv_dtype)
+    dw = upload(w, w.k_pool, w.v_pool)
+    log(f"[gpu] repeated split steps {kv_dtype} one_launch={one_launch}")
+    outs = []
+    for _ in range(4):
+        _, out = gpu_step(dw, w.steps[0], partition_size=512, fused=not one_launch,
+                          one_launch=one_launch)
+        torch.cuda.synchronize()
+        outs.append(from_dev(out, "bf16").copy())
+    assert np.all(np.isfinite(O.bits_to_f64(outs[0], "bf16")))
+    for rep, o in enumerate(outs[1:]):
+        assert np.array_equal(o, outs[0]), f"step {rep + 2} differs from the first"
